@@ -1,0 +1,332 @@
+"""Workload generators: seeded, synthetic, shaped like the pages' video workloads.
+
+Five named configurations are built here (see ``CONFIG_NAMES``); ``make_custom`` builds
+smaller cases for tests (ragged clusters, tiny sequences, edge cases).
+
+Value recipes
+-------------
+* ``clustered`` -- 16 centres ~ N(0, 1)^D per (batch, head, tensor); token i is the centre
+  of its label plus ``noise * N(0, 1)``.
+* ``field`` -- a token grid T x H x W in raster order (t slowest).  Each channel d of each
+  (batch, head, tensor) is a sum of 8 random sinusoids
+  ``sum_m a_m sin(2 pi (nu_t t/T + nu_y y/H + nu_x x/W) + phi_m)`` with
+  ``a_m ~ N(0, 1/8)``, ``nu ~ U[0, 2)`` per axis and ``phi ~ U[0, 2 pi)``, multiplied by an
+  amplitude, plus noise (Gaussian, or Student-t with 3 degrees of freedom).
+
+Everything is drawn in float64 from ``numpy.random.Generator(PCG64(SeedSequence(seed)))``
+with one spawned sub-stream per role in the order Q, K, V, mask, tau, then rounded once to
+float32 and, for bf16 workloads, once more to bfloat16 with round-to-nearest-even.  The
+arrays returned hold float32 values that are exactly representable in the workload's
+dtype, so both sides of a parity test read identical bits.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+CONFIG_NAMES = {
+    0: "tiny_f32_S1024_H2_D64_given_mask",
+    1: "grid4x32x32_bf16_S4096_H8_D128_scored",
+    2: "wan_video_21x30x52_bf16_S32760_H40_D128_scored_compensated",
+    3: "wan_video_21x30x52_bf16_S32760_H40_D128_scored_harddrop_probe_repair",
+    4: "wan_video_gqa40x8_bf16_B2_S32760_D128_scored_compensated_probe_repair",
+}
+
+# Field amplitudes for the video configurations.  Each was chosen once, by running the
+# oracle's scoring and top-p on heads of the generated inputs (synthetic/calibrate.py),
+# so that the mean block density lands in the band the workload asks for (about 22%
+# for the Wan-shaped case, about 26% for the grouped-query case).
+AMPLITUDE_CFG2 = 1.0
+AMPLITUDE_CFG4 = 1.0
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bf16_bits(x32))
+    return x32
+
+
+def grid_tile_labels(T: int, H: int, W: int, tile: Tuple[int, int, int], chunk: int) -> np.ndarray:
+    """Input labels for a T x H x W token grid stored in raster order.
+
+    Tokens are ranked tile-major: tiles of ``tile`` = (tt, th, tw) in raster order of tiles
+    (edge tiles may be partial), and raster order inside a tile.  ``chunk == 0`` labels
+    each token with its tile id; ``chunk > 0`` labels it ``rank // chunk``.
+    """
+    tt, th, tw = tile
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    t, y, x = t.ravel(), y.ravel(), x.ravel()
+    ny, nx = -(-H // th), -(-W // tw)
+    tile_id = ((t // tt) * ny + (y // th)) * nx + (x // tw)
+    if chunk == 0:
+        return tile_id.astype(np.int32)
+    order = np.lexsort((x, y, t, tile_id))  # primary key: tile id, then raster inside
+    rank = np.empty(T * H * W, dtype=np.int64)
+    rank[order] = np.arange(T * H * W)
+    return (rank // chunk).astype(np.int32)
+
+
+def _field(rng: np.random.Generator, D: int, grid: Tuple[int, int, int], amplitude: float) -> np.ndarray:
+    """One (head, tensor) field: [T*H*W, D] float64, raster order, 8 sinusoids per channel."""
+    T, H, W = grid
+    n_sin = 8
+    a = rng.normal(0.0, math.sqrt(1.0 / n_sin), size=(D, n_sin))
+    nu = rng.uniform(0.0, 2.0, size=(D, n_sin, 3))
+    phi = rng.uniform(0.0, 2.0 * math.pi, size=(D, n_sin))
+    # sin(sum of phases) = Im(prod of unit phasors); the grid is an outer product per term.
+    et = np.exp(2j * math.pi * nu[:, :, 0, None] * (np.arange(T) / T))  # [D, m, T]
+    ey = np.exp(2j * math.pi * nu[:, :, 1, None] * (np.arange(H) / H))  # [D, m, H]
+    ex = np.exp(2j * math.pi * nu[:, :, 2, None] * (np.arange(W) / W))  # [D, m, W]
+    coef = a * np.exp(1j * phi)  # [D, m]
+    g = (coef[:, :, None, None] * et[:, :, :, None] * ey[:, :, None, :]).reshape(D, n_sin, T * H)
+    f = np.matmul(g.transpose(0, 2, 1), ex)  # [D, T*H, W]
+    return amplitude * f.imag.reshape(D, T * H * W).T
+
+
+def _noise(rng: np.random.Generator, shape, kind: str, scale: float) -> np.ndarray:
+    if kind == "gauss":
+        return scale * rng.standard_normal(shape)
+    if kind == "t3":
+        return scale * rng.standard_t(3.0, size=shape)
+    raise ValueError(kind)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One synthetic problem instance (all arrays on the host)."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: str  # "f32" or "bf16": the element type the kernels read
+    q: np.ndarray  # [B, Hq, S, D] float32 (values exactly representable in dtype)
+    k: np.ndarray  # [B, Hkv, S, D]
+    v: np.ndarray  # [B, Hkv, S, D]
+    labels: np.ndarray  # [S] int32, shared by queries and keys
+    C: int  # number of clusters (labels lie in [0, C))
+    scale: float  # attention scale
+    mask_mode: str  # "given" or "scored"
+    mask: Optional[np.ndarray] = None  # given mode: uint8 keep bits [B, Hm, C, C]
+    block: int = 128
+    stride: int = 16
+    score_scale: float = 0.0
+    tau: Optional[np.ndarray] = None  # scored mode: float32 [Hm] thresholds
+    pool_gqa: bool = False  # scored mode: mask per K/V group from pooled query-head scores
+    compensate: bool = True
+    probes: int = 0  # M; 0 = no repair
+    lam: float = 0.1
+    rank: int = 16
+    grid: Optional[Tuple[int, int, int]] = None
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def Hm(self) -> int:
+        """Number of distinct block masks per batch entry."""
+        if self.mask_mode == "given":
+            return int(self.mask.shape[1])
+        return self.Hkv if self.pool_gqa else self.Hq
+
+
+def _given_random_mask(rng: np.random.Generator, C: int, p_off: float) -> np.ndarray:
+    u = rng.uniform(size=(C, C))
+    keep = (u < p_off).astype(np.uint8)
+    np.fill_diagonal(keep, 1)
+    return keep
+
+
+def _cfg0() -> Workload:
+    ss = np.random.SeedSequence(1000)
+    sq, sk, sv, sm, _ = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
+    B, H, S, D, C = 1, 2, 1024, 64, 16
+    labels = (np.arange(S) // 64).astype(np.int32)
+
+    def clustered(rng):
+        out = np.empty((B, H, S, D), dtype=np.float32)
+        for b in range(B):
+            for h in range(H):
+                centres = rng.standard_normal((C, D))
+                out[b, h] = centres[labels] + 0.3 * rng.standard_normal((S, D))
+        return out
+
+    q, k, v = clustered(sq), clustered(sk), clustered(sv)
+    mask = _given_random_mask(sm, C, 0.25)[None, None]
+    return Workload(CONFIG_NAMES[0], B, H, H, S, D, "f32", q, k, v, labels, C, 1.0 / math.sqrt(D),
+                    "given", mask=mask, compensate=True, probes=0)
+
+
+def _video(cfg: int, B: int, Hq: int, Hkv: int, grid, amplitude: float, noise_kind: str,
+           v_kind: str, tau_choices, labels: np.ndarray, C: int, heads: Optional[Sequence[int]] = None,
+           batches: Optional[Sequence[int]] = None) -> dict:
+    """Fields for Q (per query head) and K (per K/V head), V noise, per-mask-head tau."""
+    T, Hg, Wg = grid
+    S, D = T * Hg * Wg, 128
+    ss = np.random.SeedSequence(1000 + cfg)
+    sq, sk, sv, _, st = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
+    bsel = list(range(B)) if batches is None else list(batches)
+    hsel = list(range(Hq)) if heads is None else list(heads)
+    kvsel = sorted({h // (Hq // Hkv) for h in hsel})
+    q = np.empty((len(bsel), len(hsel), S, D), dtype=np.float32)
+    k = np.empty((len(bsel), len(kvsel), S, D), dtype=np.float32)
+    v = np.empty((len(bsel), len(kvsel), S, D), dtype=np.float32)
+    # Draws always run over every (b, h) in order, so a head subset has the same bits as
+    # the corresponding heads of the full workload.
+    for b in range(B):
+        for h in range(Hq):
+            x = _field(sq, D, grid, amplitude) + _noise(sq, (S, D), noise_kind, 0.2)
+            if b in bsel and h in hsel:
+                q[bsel.index(b), hsel.index(h)] = _round_to(x, "bf16")
+        for h in range(Hkv):
+            x = _field(sk, D, grid, amplitude) + _noise(sk, (S, D), noise_kind, 0.2)
+            xv = _noise(sv, (S, D), v_kind, 1.0)
+            if b in bsel and h in kvsel:
+                k[bsel.index(b), kvsel.index(h)] = _round_to(x, "bf16")
+                v[bsel.index(b), kvsel.index(h)] = _round_to(xv, "bf16")
+    n_tau = Hkv if Hq != Hkv else Hq
+    tau = np.asarray(tau_choices, dtype=np.float64)[st.integers(0, len(tau_choices), size=n_tau)]
+    return dict(q=q, k=k, v=v, tau=tau.astype(np.float32), hsel=hsel, kvsel=kvsel, bsel=bsel)
+
+
+def make_config(cfg: int, heads: Optional[Sequence[int]] = None,
+                batches: Optional[Sequence[int]] = None) -> Workload:
+    """Build one of the five named configurations.
+
+    ``heads`` / ``batches`` restrict the returned tensors to a subset of query heads (and
+    the K/V heads they read) and batch entries; the values are identical to those of the
+    full workload.
+    """
+    if cfg == 0:
+        return _cfg0()
+    if cfg == 1:
+        grid = (4, 32, 32)
+        S = 4096
+        labels = (np.arange(S) // 128).astype(np.int32)
+        g = _video(1, 1, 8, 8, grid, 1.0, "gauss", "gauss", [0.9], labels, 32, heads, batches)
+        return Workload(CONFIG_NAMES[1], len(g["bsel"]), len(g["hsel"]), len(g["kvsel"]), S, 128, "bf16",
+                        g["q"], g["k"], g["v"], labels, 32, 1.0 / math.sqrt(128), "scored",
+                        block=128, stride=16, score_scale=1.0 / math.sqrt(128),
+                        tau=g["tau"][g["hsel"]], compensate=True, probes=0, grid=grid)
+    if cfg in (2, 3):
+        grid = (21, 30, 52)
+        S = 32760
+        labels = grid_tile_labels(*grid, tile=(2, 8, 8), chunk=128)
+        g = _video(2, 1, 40, 40, grid, AMPLITUDE_CFG2, "gauss", "gauss", [0.85, 0.90, 0.95], labels, 256,
+                   heads, batches)
+        return Workload(CONFIG_NAMES[cfg], len(g["bsel"]), len(g["hsel"]), len(g["kvsel"]), S, 128, "bf16",
+                        g["q"], g["k"], g["v"], labels, 256, 1.0 / math.sqrt(128), "scored",
+                        block=128, stride=16, score_scale=1.0 / math.sqrt(128),
+                        tau=g["tau"][g["hsel"]], compensate=(cfg == 2), probes=(64 if cfg == 3 else 0),
+                        lam=0.1, rank=16, grid=grid)
+    if cfg == 4:
+        grid = (21, 30, 52)
+        S = 32760
+        labels = grid_tile_labels(*grid, tile=(2, 8, 8), chunk=128)
+        g = _video(4, 2, 40, 8, grid, AMPLITUDE_CFG4, "t3", "t3", [0.85, 0.90, 0.95], labels, 256,
+                   heads, batches)
+        hq = len(g["hsel"])
+        if heads is not None and (hq % 5 != 0 or any(h // 5 != g["kvsel"][i // 5] for i, h in enumerate(g["hsel"]))):
+            raise ValueError("config 4 head subsets must be whole groups of 5 query heads")
+        return Workload(CONFIG_NAMES[4], len(g["bsel"]), hq, len(g["kvsel"]), S, 128, "bf16",
+                        g["q"], g["k"], g["v"], labels, 256, 1.0 / math.sqrt(128), "scored",
+                        block=128, stride=16, score_scale=1.0 / math.sqrt(128),
+                        tau=g["tau"][g["kvsel"]], pool_gqa=True, compensate=True, probes=64,
+                        lam=0.1, rank=16, grid=grid)
+    raise ValueError(f"unknown config {cfg}")
+
+
+def make_custom(seed: int, *, B: int = 1, Hq: int = 2, Hkv: Optional[int] = None, S: int = 1000,
+                D: int = 128, dtype: str = "bf16", cluster_sizes: Optional[Sequence[int]] = None,
+                block: int = 0, shuffle_labels: bool = True, n_centres: int = 8, noise: float = 0.5,
+                mask: str = "random", p_keep: float = 0.3, compensate: bool = True, probes: int = 0,
+                v_kind: str = "gauss", tau: float = 0.9, stride: int = 16) -> Workload:
+    """A small seeded case for tests.
+
+    Labels: if ``block > 0`` the labels are ``i // block`` (the layout scored masks use);
+    otherwise clusters of the given sizes (default: ragged sizes) are assigned to token
+    positions, shuffled when ``shuffle_labels`` so that clusters are not contiguous.
+    Values: each cluster has ``n_centres``-mixture centres plus Gaussian noise, so keys in
+    a cluster are similar but not equal.  Mask: ``random`` (diagonal kept, others kept with
+    probability ``p_keep``), ``all``, ``diag``, ``none`` (nothing kept: only meaningful for
+    compensation), or ``scored`` (mask computed from the inputs by scoring and top-p).
+    """
+    Hkv = Hq if Hkv is None else Hkv
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    if block > 0:
+        labels = (np.arange(S) // block).astype(np.int32)
+        C = -(-S // block)
+    else:
+        if cluster_sizes is None:
+            sizes = []
+            left = S
+            while left > 0:
+                n = int(min(left, rng.integers(1, 200)))
+                sizes.append(n)
+                left -= n
+        else:
+            sizes = list(cluster_sizes)
+            if sum(sizes) != S:
+                raise ValueError("cluster sizes must sum to S")
+        C = len(sizes)
+        labels = np.repeat(np.arange(C, dtype=np.int32), sizes)
+        if shuffle_labels:
+            labels = labels[rng.permutation(S)]
+    centre_of = rng.integers(0, n_centres, size=max(C, 1))
+
+    def tensor(H):
+        out = np.empty((B, H, S, D), dtype=np.float64)
+        for b in range(B):
+            for h in range(H):
+                centres = rng.standard_normal((n_centres, D))
+                base = centres[centre_of[labels]] if C > 0 else 0.0
+                out[b, h] = base + noise * rng.standard_normal((S, D))
+        return out
+
+    q = _round_to(tensor(Hq), dtype)
+    k = _round_to(tensor(Hkv), dtype)
+    if v_kind == "t3":
+        v = _round_to(rng.standard_t(3.0, size=(B, Hkv, S, D)), dtype)
+    else:
+        v = _round_to(rng.standard_normal((B, Hkv, S, D)), dtype)
+    if mask == "scored":
+        return Workload(f"custom{seed}", B, Hq, Hkv, S, D, dtype, q, k, v, labels, C, 1.0 / math.sqrt(D),
+                        "scored", block=block, stride=stride, score_scale=1.0 / math.sqrt(D),
+                        tau=np.full(Hkv if Hq != Hkv else Hq, tau, dtype=np.float32), pool_gqa=(Hq != Hkv),
+                        compensate=compensate, probes=probes)
+    Hm = Hkv
+    keep = np.empty((B, Hm, C, C), dtype=np.uint8)
+    for b in range(B):
+        for h in range(Hm):
+            if mask == "random":
+                keep[b, h] = _given_random_mask(rng, C, p_keep)
+            elif mask == "all":
+                keep[b, h] = 1
+            elif mask == "diag":
+                keep[b, h] = np.eye(C, dtype=np.uint8)
+            elif mask == "none":
+                keep[b, h] = 0
+            else:
+                raise ValueError(mask)
+    return Workload(f"custom{seed}", B, Hq, Hkv, S, D, dtype, q, k, v, labels, C, 1.0 / math.sqrt(D),
+                    "given", mask=keep, compensate=compensate, probes=probes)
