@@ -1,0 +1,28 @@
+"""Block-sparse video-DiT attention for AMD Instinct MI355X (gfx950).
+
+Antidiagonal block scoring, per-row top-p block masks, block-sparse flash attention with
+centroid compensation, and probe-fitted residual repair, as hand-written HIP kernels
+behind a C ABI (include/bsa.h, libbsa.so).  This package is the thin Python binding:
+importing it loads libbsa.so and fails if the library has not been built.
+"""
+
+from . import _lib
+
+_lib.load()
+
+from .api import (  # noqa: E402,F401
+    BlockMask,
+    ClusterLayout,
+    antidiagonal_block_scores,
+    centroid_compensated_attention,
+    centroids,
+    cluster_layout,
+    mask_from_keep,
+    probe_apply,
+    probe_attention,
+    probe_fit,
+    select_probe_rows,
+    tile_labels,
+    top_p_block_mask,
+)
+from .path import PathConfig, PathResult, SparseAttentionPath  # noqa: E402,F401

@@ -1,0 +1,86 @@
+"""ctypes view of libbsa.so: the C ABI declared in include/bsa.h, nothing more.
+
+Loading fails loudly when the library has not been built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+c_size_p = ctypes.POINTER(ctypes.c_size_t)
+
+# name -> argument types (every call returns int status unless listed in _RESTYPES)
+SIGNATURES = {
+    "bsa_status_string": [c_int],
+    "bsa_abi_version": [],
+    "bsa_cluster_layout_workspace_size": [c_int, c_int, c_size_p],
+    "bsa_cluster_layout": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                      c_void_p, c_void_p],
+    "bsa_antidiag_scores_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_antidiag_scores": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                            c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_top_p_mask": [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_mask_lists": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
+    "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
+                             c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                             c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
+                            c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_probe_fit": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, c_void_p,
+                      c_void_p],
+    "bsa_probe_apply": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_select_probe_rows": [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p],
+    "bsa_tile_labels": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
+}
+_RESTYPES = {"bsa_status_string": ctypes.c_char_p}
+
+BSA_F32, BSA_BF16 = 0, 1
+
+
+class BsaError(RuntimeError):
+    def __init__(self, name: str, status: int, text: str):
+        super().__init__(f"{name} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libbsa.so (once) and declare every exported call."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python block_sparse_attention_antidiagonal_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, c_int)
+    _lib = lib
+    return lib
+
+
+def call(name: str, *args) -> None:
+    """Call an ABI function and raise BsaError on a non-zero status."""
+    lib = load()
+    status = getattr(lib, name)(*args)
+    if status != 0:
+        raise BsaError(name, status, lib.bsa_status_string(status).decode())
+
+
+def size_query(name: str, *args) -> int:
+    out = ctypes.c_size_t(0)
+    call(name, *args, ctypes.byref(out))
+    return int(out.value)

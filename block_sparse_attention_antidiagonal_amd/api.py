@@ -1,0 +1,244 @@
+"""Torch-tensor front end of the C ABI (argument marshalling only).
+
+Every function checks shapes, dtypes and devices, allocates its outputs with torch on the
+current device, and calls the matching ``bsa_*`` entry point on torch's current stream.
+All arithmetic happens in the HIP kernels.  Names follow the pages' API (Sparse-block
+compensation, API table; Dynamic block masks and head-wise mask reuse, API table).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import BSA_BF16, BSA_F32
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class ClusterLayout:
+    """Cluster-major order of tokens: cluster c owns perm[offsets[c]:offsets[c+1]]."""
+
+    perm: torch.Tensor  # int32 [S]
+    offsets: torch.Tensor  # int32 [C+1]
+    counts: torch.Tensor  # int32 [C]
+    C: int
+
+
+def cluster_layout(labels: torch.Tensor, C: int) -> ClusterLayout:
+    """Stable counting sort of int32 labels [S] in [0, C) (bsa_cluster_layout)."""
+    _check_cuda(labels)
+    if labels.dtype != torch.int32 or labels.dim() != 1:
+        raise ValueError("labels must be int32 [S]")
+    S = labels.numel()
+    dev = labels.device
+    perm = torch.empty(S, dtype=torch.int32, device=dev)
+    offsets = torch.empty(C + 1, dtype=torch.int32, device=dev)
+    counts = torch.empty(C, dtype=torch.int32, device=dev)
+    nbytes = _lib.size_query("bsa_cluster_layout_workspace_size", S, C)
+    ws = _workspace(nbytes, dev)
+    _lib.call("bsa_cluster_layout", _ptr(labels), S, C, _ptr(perm), _ptr(offsets), _ptr(counts), _ptr(ws),
+              ws.numel(), _stream())
+    return ClusterLayout(perm, offsets, counts, C)
+
+
+def centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Key/value cluster means, float32 [B, Hkv, C, D] (bsa_centroids)."""
+    _check_cuda(k, v)
+    B, Hkv, S, D = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must match")
+    kbar = torch.empty(B, Hkv, layout.C, D, dtype=torch.float32, device=k.device)
+    vbar = torch.empty_like(kbar)
+    _lib.call("bsa_centroids", B, Hkv, S, D, _dtype_code(k), _ptr(k), _ptr(v), _ptr(layout.perm),
+              _ptr(layout.offsets), layout.C, _ptr(kbar), _ptr(vbar), _stream())
+    return kbar, vbar
+
+
+def antidiagonal_block_scores(q: torch.Tensor, k: torch.Tensor, layout: Optional[ClusterLayout] = None,
+                              block_size: int = 128, stride: int = 16, score_scale: Optional[float] = None,
+                              pool_gqa: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Normalized antidiagonal block scores [B, Hs, nb, nb] (bsa_antidiag_scores)."""
+    _check_cuda(q, k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k shapes/dtypes do not match")
+    if score_scale is None:
+        score_scale = 1.0 / math.sqrt(D)
+    nb = -(-S // block_size)
+    Hs = Hkv if pool_gqa else Hq
+    scores = torch.empty(B, Hs, nb, nb, dtype=torch.float32, device=q.device)
+    nbytes = _lib.size_query("bsa_antidiag_scores_workspace_size", B, Hq, Hkv, S, D, block_size, stride)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
+    _lib.call("bsa_antidiag_scores", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k),
+              _ptr(layout.perm) if layout is not None else None, block_size, stride, float(score_scale),
+              int(pool_gqa), _ptr(scores), _ptr(workspace), workspace.numel(), _stream())
+    return scores
+
+
+@dataclass
+class BlockMask:
+    """Keep bits [B, Hm, Cq, Ck] and the ascending kept-block list of every row."""
+
+    keep: torch.Tensor  # uint8
+    kv_count: torch.Tensor  # int32 [B, Hm, Cq]
+    kv_idx: torch.Tensor  # int16 [B, Hm, Cq, Ck]
+
+    @property
+    def Hm(self) -> int:
+        return int(self.keep.shape[1])
+
+
+def top_p_block_mask(scores: torch.Tensor, tau) -> BlockMask:
+    """Per-row top-p keep bits from scores [B, Hs, Cq, Ck]; tau scalar or [Hs] (bsa_top_p_mask)."""
+    _check_cuda(scores)
+    B, Hs, Cq, Ck = scores.shape
+    if isinstance(tau, torch.Tensor):
+        tau_t = tau.to(device=scores.device, dtype=torch.float32).reshape(-1).contiguous()
+    else:
+        tau_t = torch.as_tensor(np.asarray(tau, dtype=np.float32).reshape(-1)).to(scores.device)
+    if tau_t.numel() not in (1, Hs):
+        raise ValueError("tau must be a scalar or one value per head")
+    keep = torch.empty(B, Hs, Cq, Ck, dtype=torch.uint8, device=scores.device)
+    cnt = torch.empty(B, Hs, Cq, dtype=torch.int32, device=scores.device)
+    idx = torch.empty(B, Hs, Cq, Ck, dtype=torch.int16, device=scores.device)
+    _lib.call("bsa_top_p_mask", _ptr(scores), B * Hs, Cq, Ck, _ptr(tau_t), tau_t.numel(), Hs, _ptr(keep), _ptr(cnt),
+              _ptr(idx), _stream())
+    return BlockMask(keep, cnt, idx)
+
+
+def mask_from_keep(keep: torch.Tensor) -> BlockMask:
+    """Kept-block lists of a caller-given uint8 mask [B, Hm, Cq, Ck] (bsa_mask_lists)."""
+    keep = keep.to(torch.uint8).contiguous()
+    _check_cuda(keep)
+    B, Hm, Cq, Ck = keep.shape
+    cnt = torch.empty(B, Hm, Cq, dtype=torch.int32, device=keep.device)
+    idx = torch.empty(B, Hm, Cq, Ck, dtype=torch.int16, device=keep.device)
+    _lib.call("bsa_mask_lists", _ptr(keep), B * Hm * Cq, Ck, _ptr(cnt), _ptr(idx), _stream())
+    return BlockMask(keep, cnt, idx)
+
+
+def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: ClusterLayout, mask: BlockMask,
+                                   kbar: Optional[torch.Tensor] = None, vbar: Optional[torch.Tensor] = None,
+                                   scale: Optional[float] = None, return_lse: bool = False,
+                                   out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                                   c: Optional[torch.Tensor] = None):
+    """Block-sparse attention; compensated when kbar/vbar are given, hard drop otherwise;
+    with A, c every output row o becomes o + o A + c before rounding (bsa_sparse_attention)."""
+    _check_cuda(q, k, v, kbar, vbar, A, c)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if mask.keep.shape[0] != B or mask.keep.shape[2] != q_layout.C or mask.keep.shape[3] != k_layout.C:
+        raise ValueError("mask shape does not match batch / cluster counts")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.call("bsa_sparse_attention", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), float(scale),
+              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(k_layout.perm), _ptr(k_layout.offsets),
+              k_layout.C, _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kbar), _ptr(vbar),
+              _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _stream())
+    return (o, lse) if return_lse else o
+
+
+def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = None,
+                    q_labels: Optional[torch.Tensor] = None, k_labels: Optional[torch.Tensor] = None,
+                    k_layout: Optional[ClusterLayout] = None, mask: Optional[BlockMask] = None,
+                    kbar: Optional[torch.Tensor] = None, vbar: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Probe rows in float32 [B, Hq, M, D]: exact dense rows, and (when a mask is given) the
+    same rows under the block-sparse rule (bsa_probe_attention).  Returns (dense, sparse)."""
+    _check_cuda(q, k, v, probe_idx, q_labels, k_labels, kbar, vbar)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    M = probe_idx.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    od = torch.empty(B, Hq, M, D, dtype=torch.float32, device=q.device)
+    os_ = torch.empty_like(od) if mask is not None else None
+    nbytes = _lib.size_query("bsa_probe_attention_workspace_size", B, Hq, S, D, M)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
+    if mask is not None:
+        Hm, Cq, Ck = mask.Hm, int(mask.keep.shape[2]), int(mask.keep.shape[3])
+        args = (_ptr(q_labels), _ptr(k_labels), _ptr(mask.keep), Hm, Cq, Ck, _ptr(k_layout.offsets), _ptr(kbar),
+                _ptr(vbar))
+    else:
+        args = (None, None, None, 1, 1, 1, None, None, None)
+    _lib.call("bsa_probe_attention", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), float(scale),
+              _ptr(probe_idx), M, *args, _ptr(od), _ptr(os_), _ptr(workspace), workspace.numel(), _stream())
+    return od, os_
+
+
+def probe_fit(o_sparse_probe: torch.Tensor, o_dense_probe: torch.Tensor, weights: torch.Tensor,
+              lam: float = 0.1, rank: int = 16) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Folded correction map A [B, Hq, D, D], c [B, Hq, D] from float32 probe rows (bsa_probe_fit)."""
+    _check_cuda(o_sparse_probe, o_dense_probe, weights)
+    B, Hq, M, D = o_sparse_probe.shape
+    A = torch.empty(B, Hq, D, D, dtype=torch.float32, device=o_sparse_probe.device)
+    c = torch.empty(B, Hq, D, dtype=torch.float32, device=o_sparse_probe.device)
+    _lib.call("bsa_probe_fit", B, Hq, D, _ptr(o_sparse_probe), _ptr(o_dense_probe), _ptr(weights), M, float(lam),
+              int(rank), _ptr(A), _ptr(c), _stream())
+    return A, c
+
+
+def probe_apply(o: torch.Tensor, A: torch.Tensor, c: torch.Tensor) -> torch.Tensor:
+    """o <- o + o A + c for every row, in place (bsa_probe_apply)."""
+    _check_cuda(o, A, c)
+    B, Hq, S, D = o.shape
+    _lib.call("bsa_probe_apply", B, Hq, S, D, _dtype_code(o), _ptr(o), _ptr(A), _ptr(c), _stream())
+    return o
+
+
+def select_probe_rows(labels: np.ndarray, C: int, M: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Host helper: probe rows and normalized weights (bsa_select_probe_rows)."""
+    lab = np.ascontiguousarray(labels, dtype=np.int32)
+    idx = np.empty(M, dtype=np.int32)
+    w = np.empty(M, dtype=np.float32)
+    _lib.call("bsa_select_probe_rows", lab.ctypes.data_as(ctypes.c_void_p), lab.size, C, M,
+              idx.ctypes.data_as(ctypes.c_void_p), w.ctypes.data_as(ctypes.c_void_p))
+    return idx, w
+
+
+def tile_labels(T: int, H: int, W: int, tile, chunk: int = 0) -> np.ndarray:
+    """Host helper: sliding-tile labels of a raster T x H x W grid (bsa_tile_labels)."""
+    out = np.empty(T * H * W, dtype=np.int32)
+    _lib.call("bsa_tile_labels", T, H, W, int(tile[0]), int(tile[1]), int(tile[2]), int(chunk),
+              out.ctypes.data_as(ctypes.c_void_p))
+    return out

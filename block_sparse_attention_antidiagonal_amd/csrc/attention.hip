@@ -1,0 +1,901 @@
+// Block-sparse flash attention with centroid compensation, and exact dense probe rows.
+//
+// "Sparse-block compensation", sections "The problem" (kept blocks only; hard drop
+// renormalizes over kept keys), "SVG-EAR -- centroid compensation" (each skipped key
+// cluster adds one column with logit q.kbar_c*scale + log n_c and value vbar_c) and "No LSE
+// needed" (the result is one softmax over the extended keys).  Here that softmax is one
+// online softmax per query row: centroid columns and kept key tiles stream through the
+// same running max and sum, so no mask or log-sum-exp merge is ever materialised.
+// "Partition the Support, Reconstruct the Residual" (summary page), Probe-Fitted Residual
+// Reconstruction: probe rows attend to every key, and their block-sparse rows are computed
+// again in float32 for the fit (bsa_probe_attention); the fitted correction is applied to
+// every output row in the attention epilogue, before the output is rounded.
+//
+// Work decomposition (gfx950): a workgroup of 4 waves owns 128 query rows of one query
+// cluster (the cluster's rows are gathered through the cluster layout); each wave owns 32
+// rows.  Keys stream through LDS in tiles of 64 rows.  Products are computed transposed,
+// S^T = K Q^T and O^T += V^T P^T, with 32x32 MFMA tiles, so that in the accumulator layout
+// every lane holds one query row's values: the row max/sum need one exchange between the
+// two 32-lane halves and the P tile feeds the second product without leaving registers.
+#include "common.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int kNK = 64;        // keys per LDS tile
+constexpr int kRowsWG = 128;   // query rows per workgroup
+constexpr int kThreads = 256;  // 4 waves
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag (p <= 256)
+constexpr int kFlagBytes = 32;         // per-wave tile flags at the end of LDS (4 waves x 2 ints)
+
+template <typename T, int D>
+struct Cfg {
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                            // chunks per row
+  static constexpr int KPAD = EPC;                               // K row padding (16 B)
+  static constexpr int VPAD = sizeof(T) == 2 ? 4 : 4;            // V^T row padding (8 B bf16, 16 B fp32)
+  static constexpr int KROW = D + KPAD;
+  static constexpr int VROW = kNK + VPAD;
+  static constexpr int K_ELEMS = kNK * KROW;
+  static constexpr int V_ELEMS = D * VROW;
+  static constexpr int ZROW = D + KPAD;  // output staging row
+  static constexpr int KV_BYTES = (K_ELEMS + V_ELEMS) * static_cast<int>(sizeof(T));
+  static constexpr int Z_BYTES = kRowsWG * ZROW * static_cast<int>(sizeof(T));
+  static constexpr int LDS_BYTES = (KV_BYTES > Z_BYTES ? KV_BYTES : Z_BYTES) + kNK * 4;
+  static constexpr int DT = D / 32;  // 32-wide output tiles
+  static constexpr int KK = D / 16;  // contraction steps of Q K^T
+};
+
+// Running softmax state of one wave (32 query rows; lane l holds row l % 32).
+template <int D>
+struct RowState {
+  f32x16 o[D / 32];
+  float m;  // running max, log2 units (may lag the true max by < kRescaleSlack)
+  float l;  // this lane's partial sum (its 16 keys of every 32-key tile)
+};
+
+// ----------------------------------------------------------------- tile loaders
+
+// For bfloat16 inputs the V^T tile is stored as float16 when every value fits it (|v| < 2^15)
+// and the tile holds at least one value >= 2^-8 (so values that lose float16 precision are
+// negligible next to the tile's largest); otherwise the tile is stored as bfloat16.  Each
+// wave publishes two flags (any value too large, any value large enough) in LDS; after the
+// next barrier every wave reads the same decision.
+__device__ __forceinline__ void publish_tile_flags(int* flags, bool big, bool normal) {
+  const unsigned long long b = __ballot(big), n = __ballot(normal);
+  if ((threadIdx.x & 63) == 0) {
+    flags[2 * (threadIdx.x >> 6)] = b != 0;
+    flags[2 * (threadIdx.x >> 6) + 1] = n != 0;
+  }
+}
+__device__ __forceinline__ bool tile_fits_f16(const int* flags) {
+  const bool big = flags[0] | flags[2] | flags[4] | flags[6];
+  const bool normal = flags[1] | flags[3] | flags[5] | flags[7];
+  return !big && normal;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// V^T store of one thread's 4 keys x 8 columns (bfloat16 words w[key][pair]).
+__device__ __forceinline__ void store_vt_bf16(bf16_t* Vt, int vrow, int d0, int k0, const uint32_t (&w)[4][4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // column pair (2p, 2p+1): low halves -> 2p, high halves -> 2p+1
+    const uint32_t lo01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x05040100u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07060302u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07060302u);
+    *reinterpret_cast<uint2*>(Vt + (d0 + 2 * p) * vrow + k0) = make_uint2(lo01, lo23);
+    *reinterpret_cast<uint2*>(Vt + (d0 + 2 * p + 1) * vrow + k0) = make_uint2(hi01, hi23);
+  }
+}
+__device__ __forceinline__ void store_vt_f16(bf16_t* Vt, int vrow, int d0, int k0, const uint32_t (&w)[4][4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    *reinterpret_cast<uint2*>(Vt + (d0 + 2 * p) * vrow + k0) =
+        make_uint2(pack_f16x2(bf16_lo(w[0][p]), bf16_lo(w[1][p])), pack_f16x2(bf16_lo(w[2][p]), bf16_lo(w[3][p])));
+    *reinterpret_cast<uint2*>(Vt + (d0 + 2 * p + 1) * vrow + k0) =
+        make_uint2(pack_f16x2(bf16_hi(w[0][p]), bf16_hi(w[1][p])), pack_f16x2(bf16_hi(w[2][p]), bf16_hi(w[3][p])));
+  }
+}
+
+// K rows -> Ks[key][d] and V rows -> Vt[d][key] (transposed), zero rows past `nvalid`.
+// `row_of(key)` gives the source row offset (in elements) of tile key `key`.  Pass 1 of a
+// bfloat16 tile writes V^T as float16 and publishes the fits-float16 flags; if the tile does
+// not fit, load_kv_tile_fallback rewrites V^T as bfloat16 after the barrier.
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void load_kv_tile(T* Ks, T* Vt, int* flags, const T* __restrict__ Kh,
+                                             const T* __restrict__ Vh, int nvalid, RowFn row_of) {
+  using C = Cfg<T, D>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kNK * C::CPR / kThreads; ++i) {
+    const int idx = t + i * kThreads;
+    const int key = idx / C::CPR, ch = idx % C::CPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (key < nvalid) v = *reinterpret_cast<const uint4*>(Kh + row_of(key) + ch * C::EPC);
+    *reinterpret_cast<uint4*>(Ks + key * C::KROW + ch * C::EPC) = v;
+  }
+  // V: each thread transposes a block of 4 keys x EPC columns.
+  constexpr int kBlocks = (kNK / 4) * C::CPR;
+  uint32_t emax = 0;  // largest exponent field among this thread's bfloat16 values
+#pragma unroll
+  for (int i = 0; i < (kBlocks + kThreads - 1) / kThreads; ++i) {
+    const int idx = t + i * kThreads;
+    if (kBlocks % kThreads != 0 && idx >= kBlocks) break;
+    const int kq = idx / C::CPR, ch = idx % C::CPR;
+    uint4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int key = kq * 4 + k;
+      r[k] = key < nvalid ? *reinterpret_cast<const uint4*>(Vh + row_of(key) + ch * C::EPC) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w},
+                              {r[1].x, r[1].y, r[1].z, r[1].w},
+                              {r[2].x, r[2].y, r[2].z, r[2].w},
+                              {r[3].x, r[3].y, r[3].z, r[3].w}};
+    const int d0 = ch * C::EPC;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) emax = max(emax, max((w[k][p] >> 7) & 0xffu, (w[k][p] >> 23) & 0xffu));
+      store_vt_f16(Vt, C::VROW, d0, kq * 4, w);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<uint4*>(Vt + (d0 + p) * C::VROW + kq * 4) = make_uint4(w[0][p], w[1][p], w[2][p], w[3][p]);
+    }
+  }
+  // bfloat16 exponent 143 is 2^16 > float16 max; exponent 119 is 2^-8.
+  if constexpr (sizeof(T) == 2) publish_tile_flags(flags, emax >= 143u, emax >= 119u);
+}
+
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void load_kv_tile_fallback(T* Vt, const T* __restrict__ Vh, int nvalid, RowFn row_of) {
+  using C = Cfg<T, D>;
+  constexpr int kBlocks = (kNK / 4) * C::CPR;
+  for (int idx = threadIdx.x; idx < kBlocks; idx += kThreads) {
+    const int kq = idx / C::CPR, ch = idx % C::CPR;
+    uint4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int key = kq * 4 + k;
+      r[k] = key < nvalid ? *reinterpret_cast<const uint4*>(Vh + row_of(key) + ch * C::EPC) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w},
+                              {r[1].x, r[1].y, r[1].z, r[1].w},
+                              {r[2].x, r[2].y, r[2].z, r[2].w},
+                              {r[3].x, r[3].y, r[3].z, r[3].w}};
+    store_vt_bf16(reinterpret_cast<bf16_t*>(Vt), C::VROW, ch * C::EPC, kq * 4, w);
+  }
+}
+
+// Centroid rows (float32) -> the same LDS layout; bias[key] (log2 units) is log2 n_c for a
+// skipped non-empty cluster and -inf otherwise (keep_row == nullptr: every non-empty cluster
+// counts as skipped).  bfloat16 inputs: K-bar is rounded to bfloat16; V-bar is stored as
+// float16 when the tile fits it (flags as for token tiles), else as bfloat16 by
+// load_centroid_fallback.
+template <typename T, int D>
+__device__ __forceinline__ void load_centroid_tile(T* Ks, T* Vt, float* bias, int* flags, const float* __restrict__ Kb,
+                                                   const float* __restrict__ Vb, int c0, int Ck,
+                                                   const int32_t* __restrict__ k_offsets,
+                                                   const uint8_t* __restrict__ keep_row) {
+  using C = Cfg<T, D>;
+  const int t = threadIdx.x;
+  constexpr int kGroups = D / 8;  // 8 floats per item
+  for (int idx = t; idx < kNK * kGroups; idx += kThreads) {
+    const int key = idx / kGroups, g = idx % kGroups;
+    const int c = c0 + key;
+    float x[8];
+    if (c < Ck) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Kb + static_cast<size_t>(c) * D + g * 8);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Kb + static_cast<size_t>(c) * D + g * 8 + 4);
+      x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+      x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Ks[key * C::KROW + g * 8 + i] = from_f32<T>(x[i]);
+  }
+  float vmax = 0.0f;
+  for (int idx = t; idx < kNK * D; idx += kThreads) {
+    const int key = idx % kNK, d = idx / kNK;
+    const int c = c0 + key;
+    const float x = c < Ck ? Vb[static_cast<size_t>(c) * D + d] : 0.0f;
+    if constexpr (sizeof(T) == 2) {
+      vmax = fmaxf(vmax, fabsf(x));
+      const _Float16 hx = static_cast<_Float16>(x);
+      Vt[d * C::VROW + key].bits = __builtin_bit_cast(uint16_t, hx);
+    } else {
+      Vt[d * C::VROW + key] = from_f32<T>(x);
+    }
+  }
+  if constexpr (sizeof(T) == 2) publish_tile_flags(flags, !(vmax < 32768.0f), vmax >= 0.00390625f);
+  if (t < kNK) {
+    const int c = c0 + t;
+    float b = -INFINITY;
+    if (c < Ck) {
+      const int n = k_offsets[c + 1] - k_offsets[c];
+      if (n > 0 && (keep_row == nullptr || keep_row[c] == 0)) b = __log2f(static_cast<float>(n));
+    }
+    bias[t] = b;
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_centroid_fallback(T* Vt, const float* __restrict__ Vb, int c0, int Ck) {
+  using C = Cfg<T, D>;
+  for (int idx = threadIdx.x; idx < kNK * D; idx += kThreads) {
+    const int key = idx % kNK, d = idx / kNK;
+    const int c = c0 + key;
+    Vt[d * C::VROW + key] = from_f32<T>(c < Ck ? Vb[static_cast<size_t>(c) * D + d] : 0.0f);
+  }
+}
+
+// ----------------------------------------------------------------- tile compute
+
+// Logit bias policies for one 64-key tile (values in log2 units, added to the scaled logits).
+// `key` is the tile-local key index, `lane` the caller's lane (its query row).
+struct NoBias {
+  static constexpr bool kNone = true;
+  __device__ float operator()(int) const { return 0.0f; }
+};
+struct TailMask {  // keys at or past `nvalid` do not exist
+  static constexpr bool kNone = false;
+  int nvalid;
+  __device__ float operator()(int key) const { return key < nvalid ? 0.0f : -INFINITY; }
+};
+struct KeyBias {  // one bias per key, from LDS (centroid columns: log2 n_c or -inf)
+  static constexpr bool kNone = false;
+  const float* bias;
+  __device__ float operator()(int key) const { return bias[key]; }
+};
+
+// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// qf: this wave's Q fragments; c2 = scale * log2(e).
+template <typename T, int D, typename Bias>
+__device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
+                                          const Bias& bias, bool pv_f16) {
+  using C = Cfg<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, h = lane >> 5;
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) {
+    Frag<T> a0, a1;
+    load_frag(a0, Ks + r * C::KROW + kk * 16 + 8 * h);
+    load_frag(a1, Ks + (32 + r) * C::KROW + kk * 16 + 8 * h);
+    s0 = mma(a0, qf[kk], s0);
+    s1 = mma(a1, qf[kk], s1);
+  }
+  // Logits in log2 units.  Key of s_mt[j]: mt*32 + 8*(j/4) + 4*h + j%4.
+  float x[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    x[j] = s0[j] * c2;
+    x[16 + j] = s1[j] * c2;
+  }
+  if constexpr (!Bias::kNone) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[mt * 16 + j] += bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
+  mx = fmaxf(mx, swap_halves(mx));
+  // Raise the running max only when a row exceeds it by the slack (wave-uniform branch).
+  if (__ballot(mx > st.m + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = (st.m == -INFINITY) ? 0.0f : fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
+  }
+  const float m_use = st.m == -INFINITY ? 0.0f : st.m;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    x[j] = fast_exp2(x[j] - m_use);
+    lsum += x[j];
+  }
+  st.l += lsum;
+  // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
+  // ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
+  // bfloat16 inputs use float16 P and V^T when the tile allows it (see load_kv_tile).
+  if (sizeof(T) == 2 && pv_f16) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag16 pb;
+      frag16_from_f32(pb, x + ks * 8);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        Frag16 va;
+        load_frag_split(va, reinterpret_cast<const bf16_t*>(Vt + (dt * 32 + r) * C::VROW + ks * 16 + 4 * h));
+        st.o[dt] = mma(va, pb, st.o[dt]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag<T> pb;
+      frag_from_f32(pb, x + ks * 8);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        Frag<T> va;
+        load_frag_split(va, Vt + (dt * 32 + r) * C::VROW + ks * 16 + 4 * h);
+        st.o[dt] = mma(va, pb, st.o[dt]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_q_frags(Frag<T>* qf, const T* __restrict__ qrow) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) load_frag(qf[kk], qrow + kk * 16 + 8 * h);
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(RowState<D>& st) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.0f;
+}
+
+// Workgroup -> (kv unit, query cluster, head-in-group).  Workgroups are dispatched to the
+// 8 XCDs round-robin by linear id; consecutive K/V heads are kept on one XCD and the query
+// heads sharing a K/V head (and a mask) run back to back, so their key tiles hit that
+// XCD's L2.
+__device__ __forceinline__ void decode_block(int n_units, int Cq, int G, int& unit, int& a, int& g) {
+  const int i = blockIdx.x;
+  const int per_unit = Cq * G;
+  int s;
+  if (n_units % kXcds == 0) {
+    const int x = i % kXcds;
+    s = i / kXcds;
+    unit = x * (n_units / kXcds) + s / per_unit;
+  } else {
+    s = i;
+    unit = s / per_unit;
+  }
+  const int rem = s % per_unit;
+  a = rem / G;
+  g = rem % G;
+}
+
+// ----------------------------------------------------------------- correction epilogue
+
+// O^T <- O^T + (O A)^T + c for the wave's 32 normalized rows ("Partition the Support,
+// Reconstruct the Residual": the fitted correction applied to every row), before the output
+// is rounded.  (O A)^T = A^T O^T on MFMA: the A^T fragments come from LDS (At[j][i]); the O^T
+// fragments come straight from the accumulators, in the same permuted contraction order the
+// P V product uses.  For bfloat16 both operands are split into high and low bfloat16 parts
+// (hi*hi + hi*lo + lo*hi), keeping the product accurate to float32 rounding.
+template <typename T, int D>
+__device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __restrict__ Ah,
+                                                const float* __restrict__ ch, unsigned char* smem) {
+  constexpr int ROWA = D + 4;
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    bf16_t* AtH = reinterpret_cast<bf16_t*>(smem);
+    bf16_t* AtL = AtH + D * ROWA;
+    for (int e = threadIdx.x; e < D * D; e += kThreads) {
+      const int i = e / D, j = e % D;
+      const float a = Ah[e];
+      const __bf16 hi = static_cast<__bf16>(a);
+      const __bf16 lo = static_cast<__bf16>(a - static_cast<float>(hi));
+      AtH[j * ROWA + i].bits = __builtin_bit_cast(uint16_t, hi);
+      AtL[j * ROWA + i].bits = __builtin_bit_cast(uint16_t, lo);
+    }
+    __syncthreads();
+    Frag<bf16_t> oh[D / 16], ol[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = st.o[kk / 2][(kk % 2) * 8 + e];
+        const __bf16 hi = static_cast<__bf16>(x);
+        oh[kk].v[e] = hi;
+        ol[kk].v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+      }
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        Frag<bf16_t> ahf, alf;
+        load_frag_split(ahf, AtH + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
+        load_frag_split(alf, AtL + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
+        acc = mma(ahf, oh[kk], acc);
+        acc = mma(ahf, ol[kk], acc);
+        acc = mma(alf, oh[kk], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[j] + ch[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
+    }
+  } else {
+    float* At = reinterpret_cast<float*>(smem);
+    for (int e = threadIdx.x; e < D * D; e += kThreads) At[(e % D) * ROWA + e / D] = Ah[e];
+    __syncthreads();
+    Frag<float> of[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) of[kk].v[e] = st.o[kk / 2][(kk % 2) * 8 + e];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        Frag<float> af;
+        load_frag_split(af, At + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
+        acc = mma(af, of[kk], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[j] + ch[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
+    }
+  }
+  __syncthreads();
+}
+
+template <typename T, int D>
+constexpr int repair_lds_bytes() {
+  return (sizeof(T) == 2 ? 2 * D * (D + 4) * 2 : D * (D + 4) * 4);
+}
+
+template <typename T, int D, bool REPAIR>
+constexpr int attn_lds_bytes() {
+  using C = Cfg<T, D>;
+  const int base = C::KV_BYTES > C::Z_BYTES ? C::KV_BYTES : C::Z_BYTES;
+  const int rep = REPAIR ? repair_lds_bytes<T, D>() : 0;
+  return (base > rep ? base : rep) + kNK * 4 + kFlagBytes;
+}
+
+// ----------------------------------------------------------------- sparse attention
+
+template <typename T, int D, bool COMP, bool REPAIR>
+__global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
+    float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2, const int32_t* __restrict__ q_perm,
+    const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_perm,
+    const int32_t* __restrict__ k_off, int Ck, const uint8_t* __restrict__ keep,
+    const int32_t* __restrict__ kv_count, const int16_t* __restrict__ kv_idx, int Hm,
+    const float* __restrict__ Kbar, const float* __restrict__ Vbar, const float* __restrict__ Acorr,
+    const float* __restrict__ ccorr) {
+  using C = Cfg<T, D>;
+  constexpr int LDS = attn_lds_bytes<T, D, REPAIR>();
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vt = Ks + C::K_ELEMS;
+  T* Z = reinterpret_cast<T*>(smem);
+  float* bias = reinterpret_cast<float*>(smem + (LDS - kNK * 4 - kFlagBytes));
+  int* flags = reinterpret_cast<int*>(smem + (LDS - kFlagBytes));
+
+  const int G = Hq / Hkv;
+  int unit, a, g;
+  decode_block(B * Hkv, Cq, G, unit, a, g);
+  const int b = unit / Hkv, kvh = unit % Hkv;
+  const int hq = kvh * G + g;
+  const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+  const size_t mrow = (static_cast<size_t>(b) * Hm + hm) * Cq + a;
+  const size_t bhq = static_cast<size_t>(b) * Hq + hq;
+  const T* Qh = Q + bhq * S * D;
+  T* Oh = O + bhq * S * D;
+  const T* Kh = K + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const T* Vh = V + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const float* Kb = COMP ? Kbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D : nullptr;
+  const float* Vb = COMP ? Vbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D : nullptr;
+  const uint8_t* keep_row = keep + mrow * Ck;
+  const int16_t* list = kv_idx + mrow * Ck;
+  const int cnt = kv_count[mrow];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int q_lo = q_off[a], q_hi = q_off[a + 1];
+
+  for (int rt = q_lo; rt < q_hi; rt += kRowsWG) {
+    const int nrows = min(kRowsWG, q_hi - rt);
+    // This lane's query row; rows past the cluster reuse row 0 and are not stored.
+    const int my = wave * 32 + r;
+    const int qtok = q_perm[rt + (my < nrows ? my : 0)];
+    Frag<T> qf[C::KK];
+    load_q_frags<T, D>(qf, Qh + static_cast<size_t>(qtok) * D);
+    RowState<D> st;
+    init_state<D>(st);
+
+    if constexpr (COMP) {
+      for (int c0 = 0; c0 < Ck; c0 += kNK) {
+        load_centroid_tile<T, D>(Ks, Vt, bias, flags, Kb, Vb, c0, Ck, k_off, keep_row);
+        __syncthreads();
+        const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
+        if (sizeof(T) == 2 && !f16) {
+          load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
+          __syncthreads();
+        }
+        const bool any = __ballot(bias[lane] > -INFINITY) != 0;
+        if (any) tile_step<T, D>(Ks, Vt, qf, st, c2, KeyBias{bias}, f16);
+        __syncthreads();
+      }
+    }
+    for (int it = 0; it < cnt; ++it) {
+      const int c = list[it];
+      if (c < 0 || c >= Ck) continue;
+      const int k_lo = k_off[c], k_hi = k_off[c + 1];
+      for (int kt = k_lo; kt < k_hi; kt += kNK) {
+        const int nvalid = min(kNK, k_hi - kt);
+        auto row_of = [&](int key) { return static_cast<size_t>(k_perm[kt + key]) * D; };
+        load_kv_tile<T, D>(Ks, Vt, flags, Kh, Vh, nvalid, row_of);
+        __syncthreads();
+        const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
+        if (sizeof(T) == 2 && !f16) {
+          load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
+          __syncthreads();
+        }
+        if (nvalid == kNK)
+          tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, f16);
+        else
+          tile_step<T, D>(Ks, Vt, qf, st, c2, TailMask{nvalid}, f16);
+        __syncthreads();
+      }
+    }
+    const float l_tot = st.l + swap_halves(st.l);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[dt][j] *= inv;
+    if constexpr (REPAIR) repair_epilogue<T, D>(st, Acorr + bhq * D * D, ccorr + bhq * D, smem);
+    // Stage the tile as rows in LDS, then store rows with 16-byte writes.
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int d = dt * 32 + 8 * (j / 4) + 4 * h + (j % 4);
+        Z[my * C::ZROW + d] = from_f32<T>(st.o[dt][j]);
+      }
+    if (lse != nullptr && h == 0 && my < nrows) {
+      const float v = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+      lse[bhq * S + qtok] = v;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kRowsWG * C::CPR; idx += kThreads) {
+      const int row = idx / C::CPR, ch = idx % C::CPR;
+      if (row < nrows) {
+        const int tok = q_perm[rt + row];
+        *reinterpret_cast<uint4*>(Oh + static_cast<size_t>(tok) * D + ch * C::EPC) =
+            *reinterpret_cast<const uint4*>(Z + row * C::ZROW + ch * C::EPC);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------- probe rows
+
+// Per (query row, key) mask of a probe tile: the key's cluster must be kept for the query's
+// cluster.  Keep bits of the workgroup's probe rows are packed in LDS (one bit per key
+// cluster); the tile's key-cluster labels are in LDS too.
+struct ProbeMask {
+  static constexpr bool kNone = false;
+  const uint32_t* bits;  // this lane's row of packed keep bits
+  const int* klab;       // tile key -> key cluster
+  int nvalid;
+  __device__ float operator()(int key) const {
+    if (key >= nvalid) return -INFINITY;
+    const int c = klab[key];
+    if (c < 0) return -INFINITY;
+    return ((bits[c >> 5] >> (c & 31)) & 1u) ? 0.0f : -INFINITY;
+  }
+};
+// Centroid columns of a probe row: log2 n_c where the row's cluster skipped c, else -inf.
+struct ProbeCentroids {
+  static constexpr bool kNone = false;
+  const uint32_t* bits;
+  const float* log2n;  // tile centroid -> log2 n_c (-inf for empty / out of range)
+  int c0;
+  __device__ float operator()(int key) const {
+    const int c = c0 + key;
+    const float b = log2n[key];
+    if (b == -INFINITY) return -INFINITY;
+    return ((bits[c >> 5] >> (c & 31)) & 1u) ? -INFINITY : b;
+  }
+};
+
+constexpr int kMaxCkProbe = 2048;  // packed keep bits per probe row in LDS
+
+// Partial attention of up to 128 probe rows against one chunk of keys, written unnormalized
+// with the running max (log2 units) and sum for a later merge.  DENSE: every key.  Sparse:
+// only keys of kept clusters of the row's own query cluster, and (with centroids) one extra
+// chunk index holding the centroid columns of its skipped clusters, which is the row of the
+// block-sparse output computed in float32.
+template <typename T, int D, bool SPARSE>
+__global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int Hq, int Hkv, int S, float c2,
+    const int32_t* __restrict__ probe_idx, int M, int chunk, int ntok_chunks, int nchunks,
+    const int32_t* __restrict__ q_labels, const int32_t* __restrict__ k_labels, const uint8_t* __restrict__ keep,
+    int Hm, int Cq, int Ck, const int32_t* __restrict__ k_off, const float* __restrict__ Kbar,
+    const float* __restrict__ Vbar, float* __restrict__ Opart, float* __restrict__ mpart,
+    float* __restrict__ lpart) {
+  using C = Cfg<T, D>;
+  constexpr int LDS = attn_lds_bytes<T, D, false>();
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vt = Ks + C::K_ELEMS;
+  float* bias = reinterpret_cast<float*>(smem + (LDS - kNK * 4 - kFlagBytes));
+  int* flags = reinterpret_cast<int*>(smem + (LDS - kFlagBytes));
+  int* klab = reinterpret_cast<int*>(smem + LDS);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(smem + LDS + kNK * 4);
+  const int ci = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
+  const T* Qh = Q + static_cast<size_t>(bh) * S * D;
+  const T* Kh = K + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const T* Vh = V + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int my = qt * kRowsWG + wave * 32 + r;
+  const int qtok = probe_idx[my < M ? my : 0];
+  const int words = (Ck + 31) / 32;
+  if constexpr (SPARSE) {
+    // Pack the keep bits of every probe row of this workgroup.
+    const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+    for (int e = threadIdx.x; e < kRowsWG * words; e += kThreads) {
+      const int row = e / words, w = e % words;
+      const int pr = qt * kRowsWG + row;
+      uint32_t v = 0;
+      if (pr < M) {
+        const int a = q_labels[probe_idx[pr]];
+        if (a >= 0 && a < Cq) {
+          const uint8_t* krow = keep + ((static_cast<size_t>(b) * Hm + hm) * Cq + a) * Ck;
+          for (int k = 0; k < 32; ++k) {
+            const int c = w * 32 + k;
+            if (c < Ck && krow[c] != 0) v |= 1u << k;
+          }
+        }
+      }
+      bits[row * words + w] = v;
+    }
+    __syncthreads();
+  }
+  const uint32_t* mybits = bits + (wave * 32 + r) * words;
+  Frag<T> qf[C::KK];
+  load_q_frags<T, D>(qf, Qh + static_cast<size_t>(qtok) * D);
+  RowState<D> st;
+  init_state<D>(st);
+  if (ci < ntok_chunks) {
+    const int k_lo = ci * chunk, k_hi = min(S, k_lo + chunk);
+    for (int kt = k_lo; kt < k_hi; kt += kNK) {
+      const int nvalid = min(kNK, k_hi - kt);
+      auto row_of = [&](int key) { return static_cast<size_t>(kt + key) * D; };
+      load_kv_tile<T, D>(Ks, Vt, flags, Kh, Vh, nvalid, row_of);
+      if constexpr (SPARSE) {
+        if (threadIdx.x < kNK) {
+          const int key = kt + threadIdx.x;
+          const int c = key < k_hi ? k_labels[key] : -1;
+          klab[threadIdx.x] = (c >= 0 && c < Ck) ? c : -1;  // tokens outside every cluster stay masked
+        }
+      }
+      __syncthreads();
+      const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
+      if (sizeof(T) == 2 && !f16) {
+        load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
+        __syncthreads();
+      }
+      if constexpr (SPARSE) {
+        tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, f16);
+      } else {
+        if (nvalid == kNK)
+          tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, f16);
+        else
+          tile_step<T, D>(Ks, Vt, qf, st, c2, TailMask{nvalid}, f16);
+      }
+      __syncthreads();
+    }
+  } else if constexpr (SPARSE) {
+    // Centroid columns (the chunk past the token chunks).
+    const float* Kb = Kbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D;
+    const float* Vb = Vbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D;
+    for (int c0 = 0; c0 < Ck; c0 += kNK) {
+      // With an all-zero keep row the per-tile bias is log2 n_c for every non-empty cluster.
+      load_centroid_tile<T, D>(Ks, Vt, bias, flags, Kb, Vb, c0, Ck, k_off, nullptr);
+      __syncthreads();
+      const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
+      if (sizeof(T) == 2 && !f16) {
+        load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
+        __syncthreads();
+      }
+      tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, f16);
+      __syncthreads();
+    }
+  }
+  const float l_tot = st.l + swap_halves(st.l);
+  if (my < M) {
+    const size_t prow = (static_cast<size_t>(bh) * nchunks + ci) * M + my;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + 8 * g4 + 4 * h;
+        *reinterpret_cast<f32x4*>(Opart + prow * D + d) =
+            f32x4{st.o[dt][4 * g4], st.o[dt][4 * g4 + 1], st.o[dt][4 * g4 + 2], st.o[dt][4 * g4 + 3]};
+      }
+    if (h == 0) {
+      mpart[prow] = st.m;
+      lpart[prow] = l_tot;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ Opart,
+                                                        const float* __restrict__ mpart,
+                                                        const float* __restrict__ lpart, int M, int nchunks,
+                                                        float* __restrict__ Od) {
+  const int m = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, mpart[(static_cast<size_t>(bh) * nchunks + c) * M + m]);
+  float l = 0.0f, o = 0.0f;
+  for (int c = 0; c < nchunks; ++c) {
+    const size_t prow = (static_cast<size_t>(bh) * nchunks + c) * M + m;
+    const float mc = mpart[prow];
+    if (mc == -INFINITY) continue;
+    const float w = fast_exp2(mc - mx);
+    l += lpart[prow] * w;
+    o += Opart[prow * D + d] * w;
+  }
+  Od[(static_cast<size_t>(bh) * M + m) * D + d] = l > 0.0f ? o / l : 0.0f;
+}
+
+constexpr int kProbeChunk = 2048;
+
+template <typename T, int D, bool COMP, bool REPAIR>
+void launch_sparse_variant(dim3 grid, hipStream_t stream, const void* Q, const void* K, const void* V, void* O,
+                           float* lse, int B, int Hq, int Hkv, int S, float c2, const int32_t* q_perm,
+                           const int32_t* q_off, int Cq, const int32_t* k_perm, const int32_t* k_off, int Ck,
+                           const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                           const float* Kbar, const float* Vbar, const float* A, const float* c) {
+  constexpr int LDS = attn_lds_bytes<T, D, REPAIR>();
+  auto kern = sparse_attn_kernel<T, D, COMP, REPAIR>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<const T*>(K),
+                     static_cast<const T*>(V), static_cast<T*>(O), lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_perm,
+                     k_off, Ck, keep, kv_count, kv_idx, Hm, Kbar, Vbar, A, c);
+}
+
+template <typename T, int D>
+bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const void* V, float scale,
+                         const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_perm,
+                         const int32_t* k_off, int Ck, const uint8_t* keep, const int32_t* kv_count,
+                         const int16_t* kv_idx, int Hm, const float* Kbar, const float* Vbar, const float* A,
+                         const float* c, void* O, float* lse, hipStream_t stream) {
+  const long long nblocks = static_cast<long long>(B) * Hq * Cq;
+  if (nblocks > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  const float c2 = scale * kLog2e;
+#define BSA_LAUNCH(COMP, REP)                                                                                      \
+  launch_sparse_variant<T, D, COMP, REP>(grid, stream, Q, K, V, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_perm, \
+                                         k_off, Ck, keep, kv_count, kv_idx, Hm, Kbar, Vbar, A, c)
+  if (Kbar != nullptr) {
+    if (A != nullptr) BSA_LAUNCH(true, true); else BSA_LAUNCH(true, false);
+  } else {
+    if (A != nullptr) BSA_LAUNCH(false, true); else BSA_LAUNCH(false, false);
+  }
+#undef BSA_LAUNCH
+  return launch_status();
+}
+
+template <typename T, int D, bool SPARSE>
+void launch_probe_pass(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const void* V, float c2,
+                       const int32_t* probe_idx, int M, const int32_t* q_labels, const int32_t* k_labels,
+                       const uint8_t* keep, int Hm, int Cq, int Ck, const int32_t* k_off, const float* Kbar,
+                       const float* Vbar, float* out, float* ws, hipStream_t stream) {
+  constexpr int LDS = attn_lds_bytes<T, D, false>();
+  const int ntok = (S + kProbeChunk - 1) / kProbeChunk;
+  const int nchunks = ntok + ((SPARSE && Kbar != nullptr) ? 1 : 0);
+  const int qtiles = (M + kRowsWG - 1) / kRowsWG;
+  float* Opart = ws;
+  float* mpart = Opart + static_cast<size_t>(B) * Hq * nchunks * M * D;
+  float* lpart = mpart + static_cast<size_t>(B) * Hq * nchunks * M;
+  const int extra = SPARSE ? kNK * 4 + kRowsWG * ((Ck + 31) / 32) * 4 : 0;
+  auto kern = probe_partial_kernel<T, D, SPARSE>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS + extra);
+  hipLaunchKernelGGL(kern, dim3(nchunks, qtiles, B * Hq), dim3(kThreads), LDS + extra, stream,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V), Hq, Hkv, S, c2,
+                     probe_idx, M, kProbeChunk, ntok, nchunks, q_labels, k_labels, keep, Hm, Cq, Ck, k_off, Kbar,
+                     Vbar, Opart, mpart, lpart);
+  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks,
+                     out);
+}
+
+size_t probe_ws_floats(int B, int Hq, int S, int D, int M) {
+  const size_t nchunks = (static_cast<size_t>(S) + kProbeChunk - 1) / kProbeChunk + 1;
+  return static_cast<size_t>(B) * Hq * nchunks * M * (D + 2);
+}
+
+template <typename T, int D>
+bsa_status launch_probe(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const void* V, float scale,
+                        const int32_t* probe_idx, int M, const int32_t* q_labels, const int32_t* k_labels,
+                        const uint8_t* keep, int Hm, int Cq, int Ck, const int32_t* k_off, const float* Kbar,
+                        const float* Vbar, float* Od, float* Os, void* ws, hipStream_t stream) {
+  const float c2 = scale * kLog2e;
+  float* w = static_cast<float*>(ws);
+  launch_probe_pass<T, D, false>(B, Hq, Hkv, S, Q, K, V, c2, probe_idx, M, nullptr, nullptr, nullptr, 1, 1, 1, nullptr,
+                                 nullptr, nullptr, Od, w, stream);
+  if (Os != nullptr)
+    launch_probe_pass<T, D, true>(B, Hq, Hkv, S, Q, K, V, c2, probe_idx, M, q_labels, k_labels, keep, Hm, Cq, Ck,
+                                  k_off, Kbar, Vbar, Os, w, stream);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
+                                           const void* K, const void* V, float scale, const int32_t* q_perm,
+                                           const int32_t* q_offsets, int Cq, const int32_t* k_perm,
+                                           const int32_t* k_offsets, int Ck, const uint8_t* keep,
+                                           const int32_t* kv_count, const int16_t* kv_idx, int Hm, const float* Kbar,
+                                           const float* Vbar, const float* A, const float* c, void* O, float* lse,
+                                           hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
+  if (!Q || !K || !V || !O || !q_perm || !q_offsets || !k_perm || !k_offsets || !keep || !kv_count || !kv_idx)
+    return BSA_E_ARG;
+  if ((Kbar == nullptr) != (Vbar == nullptr)) return BSA_E_ARG;
+  if ((A == nullptr) != (c == nullptr)) return BSA_E_ARG;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  if (Ck > 32767) return BSA_E_UNSUPPORTED;
+#define BSA_ARGS B, Hq, Hkv, S, Q, K, V, scale, q_perm, q_offsets, Cq, k_perm, k_offsets, Ck, keep, kv_count, kv_idx, \
+                 Hm, Kbar, Vbar, A, c, O, lse, stream
+  if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
+  return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
+#undef BSA_ARGS
+}
+
+extern "C" bsa_status bsa_probe_attention_workspace_size(int B, int Hq, int S, int D, int M, size_t* bytes) {
+  if (!bytes || B < 1 || Hq < 1 || S < 1 || M < 1) return BSA_E_ARG;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  if (M > 1024) return BSA_E_UNSUPPORTED;
+  *bytes = probe_ws_floats(B, Hq, S, D, M) * sizeof(float);
+  return BSA_OK;
+}
+
+extern "C" bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
+                                          const void* K, const void* V, float scale, const int32_t* probe_idx, int M,
+                                          const int32_t* q_labels, const int32_t* k_labels, const uint8_t* keep,
+                                          int Hm, int Cq, int Ck, const int32_t* k_offsets, const float* Kbar,
+                                          const float* Vbar, float* O_dense_probe, float* O_sparse_probe, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+  size_t need = 0;
+  bsa_status st = bsa_probe_attention_workspace_size(B, Hq, S, D, M, &need);
+  if (st != BSA_OK) return st;
+  if (Hkv < 1 || Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (!Q || !K || !V || !probe_idx || !O_dense_probe) return BSA_E_ARG;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
+  if (O_sparse_probe != nullptr) {
+    if (!q_labels || !k_labels || !keep || !k_offsets || Cq < 1 || Ck < 1) return BSA_E_ARG;
+    if ((Kbar == nullptr) != (Vbar == nullptr)) return BSA_E_ARG;
+    if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
+    if (Ck > kMaxCkProbe) return BSA_E_UNSUPPORTED;
+  }
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+#define BSA_ARGS B, Hq, Hkv, S, Q, K, V, scale, probe_idx, M, q_labels, k_labels, keep, Hm, Cq, Ck, k_offsets, Kbar, \
+                 Vbar, O_dense_probe, O_sparse_probe, ws, stream
+  if (dtype == BSA_BF16) return D == 128 ? launch_probe<bf16_t, 128>(BSA_ARGS) : launch_probe<bf16_t, 64>(BSA_ARGS);
+  return D == 128 ? launch_probe<float, 128>(BSA_ARGS) : launch_probe<float, 64>(BSA_ARGS);
+#undef BSA_ARGS
+}

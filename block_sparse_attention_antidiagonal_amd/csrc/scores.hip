@@ -1,0 +1,338 @@
+// XAttention antidiagonal block scores.
+//
+// "Dynamic block masks and head-wise mask reuse", section "XAttention -- anti-diagonal block
+// scoring": every stride x stride sub-block of Q K^T is summarized by the sum along its
+// anti-diagonal; the strided logits are softmaxed per row and summed per block x block
+// tile; section "Deviations from the papers": rows are divided by their total; section
+// "Out of scope, and why": the sequence is zero-padded to a multiple of the block size and
+// padded keys take softmax mass.
+//
+// The anti-diagonal sum of sub-block (i', j') is the dot product of two length stride*D
+// vectors: strided query row i' lists tokens i'*s+s-1, ..., i'*s (reverse order) and strided
+// key row j' lists tokens j'*s, ..., j'*s+s-1.  So the strided logits are one GEMM with
+// contraction length stride*D, computed here with bf16 MFMA in tiles of 128 x 128 strided
+// rows.  Its epilogue keeps, per strided query row, the tile max, the tile sum of
+// exponentials and the per-block sums relative to that max; a second pass merges the
+// tiles of a row (the full-row softmax), sums the rows of a query block and normalizes.
+// Workspace: part[bh][key block][strided row], mstat/lstat[bh][key tile][strided row].
+#include "common.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int kTile = 128;  // strided rows per tile side
+constexpr int kKC = 64;     // contraction elements per LDS stage
+
+template <typename T>
+struct SCfg {
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  static constexpr int CPR = kKC / EPC;  // 16-byte chunks per stage row
+  static constexpr int ROW = kKC + EPC;  // padded LDS row (elements)
+  static constexpr int ELEMS = kTile * ROW;
+};
+
+// S^T tile: keys (A operand) x queries (B operand).  Wave w: keys 64*(w/2).., queries 64*(w%2)..
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                             const int32_t* __restrict__ perm, int Hq, int Hkv,
+                                                             int S, int stride, int Ns, int nb, int ntk, float c2,
+                                                             float* __restrict__ part, float* __restrict__ mstat,
+                                                             float* __restrict__ lstat) {
+  using C = SCfg<T>;
+  __shared__ __align__(16) T As[C::ELEMS];
+  __shared__ __align__(16) T Bs[C::ELEMS];
+  __shared__ float red[2][kTile];
+  const int kt = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
+  const T* Qh = Q + static_cast<size_t>(bh) * S * D;
+  const T* Kh = K + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int kw = wave >> 1, qw = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  for (int tt = 0; tt < stride; ++tt) {
+    for (int dc = 0; dc < D; dc += kKC) {
+      // Stage rows: key strided row j' takes token j'*s + tt; query row i' takes i'*s + s-1-tt.
+#pragma unroll
+      for (int i = 0; i < kTile * C::CPR / 256; ++i) {
+        const int idx = t + i * 256;
+        const int row = idx / C::CPR, ch = idx % C::CPR;
+        const int jk = kt * kTile + row, iq = qt * kTile + row;
+        const int pk = jk * stride + tt, pq = iq * stride + stride - 1 - tt;
+        uint4 vk = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
+        if (jk < Ns && pk < S) {
+          const int tok = perm ? perm[pk] : pk;
+          vk = *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(tok) * D + dc + ch * C::EPC);
+        }
+        if (iq < Ns && pq < S) {
+          const int tok = perm ? perm[pq] : pq;
+          vq = *reinterpret_cast<const uint4*>(Qh + static_cast<size_t>(tok) * D + dc + ch * C::EPC);
+        }
+        *reinterpret_cast<uint4*>(As + row * C::ROW + ch * C::EPC) = vk;
+        *reinterpret_cast<uint4*>(Bs + row * C::ROW + ch * C::EPC) = vq;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kKC / 16; ++ks) {
+        Frag<T> fa[2], fb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) load_frag(fa[m], As + (kw * 64 + m * 32 + r) * C::ROW + ks * 16 + 8 * h);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) load_frag(fb[n], Bs + (qw * 64 + n * 32 + r) * C::ROW + ks * 16 + 8 * h);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue.  acc[m][n][j]: key kt*128 + kw*64 + m*32 + 8*(j/4) + 4*h + j%4,
+  //                          query qt*128 + qw*64 + n*32 + r.
+  float mx[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kt * kTile + kw * 64 + m * 32 + 8 * (j / 4) + 4 * h + (j % 4);
+        const float y = key < Ns ? acc[m][n][j] * c2 : -INFINITY;
+        acc[m][n][j] = y;
+        v = fmaxf(v, y);
+      }
+    v = fmaxf(v, swap_halves(v));
+    mx[n] = v;
+  }
+  if (h == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) red[kw][qw * 64 + n * 32 + r] = mx[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < 2; ++n) mx[n] = fmaxf(red[0][qw * 64 + n * 32 + r], red[1][qw * 64 + n * 32 + r]);
+  __syncthreads();
+  float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(acc[m][n][j] - mx[n]);
+        acc[m][n][j] = e;
+        ls[n] += e;
+      }
+  // Block sums over R consecutive keys.
+  const size_t pbase = static_cast<size_t>(bh) * nb;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int query = qt * kTile + qw * 64 + n * 32 + r;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int kbase = kt * kTile + kw * 64 + m * 32;  // first key of this 32-key group
+      if constexpr (R <= 4) {
+        // Blocks lie inside one lane's 4-key runs.
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int q0 = 0; q0 < 4; q0 += R) {
+            float s = 0.0f;
+#pragma unroll
+            for (int e = 0; e < R; ++e) s += acc[m][n][4 * g + q0 + e];
+            const int key0 = kbase + 8 * g + 4 * h + q0;
+            if (query < Ns && key0 < Ns) part[(pbase + key0 / R) * Ns + query] = s;
+          }
+      } else {
+        // A block spans R/8 run pairs: runs 8*g..8*g+3 (lower half) and 8*g+4.. (upper half).
+        constexpr int kRunsPer = R / 8;
+#pragma unroll
+        for (int g0 = 0; g0 < 4; g0 += kRunsPer) {
+          float s = 0.0f;
+#pragma unroll
+          for (int g = g0; g < g0 + kRunsPer; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += acc[m][n][4 * g + e];
+          s += swap_halves(s);
+          const int key0 = kbase + 8 * g0;
+          if (h == 0 && query < Ns && key0 < Ns) part[(pbase + key0 / R) * Ns + query] = s;
+        }
+      }
+    }
+    ls[n] += swap_halves(ls[n]);
+  }
+  if (h == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) red[kw][qw * 64 + n * 32 + r] = ls[n];
+  }
+  __syncthreads();
+  if (kw == 0 && h == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int ql = qw * 64 + n * 32 + r;
+      const int query = qt * kTile + ql;
+      if (query < Ns) {
+        const size_t s_idx = (static_cast<size_t>(bh) * ntk + kt) * Ns + query;
+        mstat[s_idx] = mx[n];
+        lstat[s_idx] = red[0][ql] + red[1][ql];
+      }
+    }
+  }
+}
+
+// One workgroup per (batch, score head, query block): merge the key tiles of each strided
+// row (full-row softmax), sum the block's rows, normalize, and average over the query heads
+// of a group when pooling.
+template <int R>
+__global__ __launch_bounds__(256) void score_finalize_kernel(const float* __restrict__ part,
+                                                              const float* __restrict__ mstat,
+                                                              const float* __restrict__ lstat, int Hq, int Hs,
+                                                              int Ns, int nb, int ntk, float* __restrict__ scores) {
+  __shared__ float Mrow[R], Lrow[R];
+  __shared__ float red[256];
+  const int a = blockIdx.x, bhs = blockIdx.y;
+  const int b = bhs / Hs, hs = bhs % Hs;
+  const int G = Hq / Hs;
+  constexpr int kPerT = 4;  // blocks per thread (nb <= 1024)
+  float acc[kPerT] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int gi = 0; gi < G; ++gi) {
+    const int hq = hs * G + gi;
+    const size_t bh = static_cast<size_t>(b) * Hq + hq;
+    if (threadIdx.x < R) {
+      const int row = a * R + threadIdx.x;
+      float M = -INFINITY;
+      for (int k = 0; k < ntk; ++k) M = fmaxf(M, mstat[(bh * ntk + k) * Ns + row]);
+      float L = 0.0f;
+      for (int k = 0; k < ntk; ++k) {
+        const size_t s = (bh * ntk + k) * Ns + row;
+        L += lstat[s] * fast_exp2(mstat[s] - M);
+      }
+      Mrow[threadIdx.x] = M;
+      Lrow[threadIdx.x] = L;
+    }
+    __syncthreads();
+    float mass[kPerT];
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) {
+      const int c = threadIdx.x + e * 256;
+      mass[e] = 0.0f;
+      if (c < nb) {
+        const int k = c * R / kTile;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int row = a * R + i;
+          const float w = fast_exp2(mstat[(bh * ntk + k) * Ns + row] - Mrow[i]) / Lrow[i];
+          mass[e] += part[(bh * nb + c) * Ns + row] * w;
+        }
+      }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) tot += mass[e];
+    red[threadIdx.x] = tot;
+    __syncthreads();
+    for (int d = 128; d > 0; d >>= 1) {
+      if (threadIdx.x < static_cast<unsigned>(d)) red[threadIdx.x] += red[threadIdx.x + d];
+      __syncthreads();
+    }
+    const float inv = 1.0f / red[0];
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) acc[e] += mass[e] * inv;
+    __syncthreads();
+  }
+  const float invG = 1.0f / static_cast<float>(G);
+  float* out = scores + (static_cast<size_t>(bhs) * nb + a) * nb;
+#pragma unroll
+  for (int e = 0; e < kPerT; ++e) {
+    const int c = threadIdx.x + e * 256;
+    if (c < nb) out[c] = G == 1 ? acc[e] : acc[e] * invG;
+  }
+}
+
+struct ScoreDims {
+  int nb, Ns, ntk;
+};
+
+inline ScoreDims score_dims(int S, int block, int stride) {
+  ScoreDims d;
+  d.nb = (S + block - 1) / block;
+  d.Ns = d.nb * (block / stride);
+  d.ntk = (d.Ns + kTile - 1) / kTile;
+  return d;
+}
+
+template <typename T, int D, int R>
+void launch_scores(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const int32_t* perm, int stride,
+                   float score_scale, int pool_gqa, float* scores, void* ws, hipStream_t stream, const ScoreDims& sd) {
+  float* part = static_cast<float*>(ws);
+  float* mstat = part + static_cast<size_t>(B) * Hq * sd.nb * sd.Ns;
+  float* lstat = mstat + static_cast<size_t>(B) * Hq * sd.ntk * sd.Ns;
+  hipLaunchKernelGGL((score_gemm_kernel<T, D, R>), dim3(sd.ntk, sd.ntk, B * Hq), dim3(256), 0, stream,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), perm, Hq, Hkv, S, stride, sd.Ns, sd.nb, sd.ntk,
+                     score_scale * kLog2e, part, mstat, lstat);
+  const int Hs = pool_gqa ? Hkv : Hq;
+  hipLaunchKernelGGL((score_finalize_kernel<R>), dim3(sd.nb, B * Hs), dim3(256), 0, stream, part, mstat, lstat, Hq, Hs,
+                     sd.Ns, sd.nb, sd.ntk, scores);
+}
+
+template <typename T, int D>
+bsa_status dispatch_r(int R, int B, int Hq, int Hkv, int S, const void* Q, const void* K, const int32_t* perm,
+                      int stride, float score_scale, int pool_gqa, float* scores, void* ws, hipStream_t stream,
+                      const ScoreDims& sd) {
+  switch (R) {
+    case 2: launch_scores<T, D, 2>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
+    case 4: launch_scores<T, D, 4>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
+    case 8: launch_scores<T, D, 8>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
+    case 16: launch_scores<T, D, 16>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
+    default: return BSA_E_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" bsa_status bsa_antidiag_scores_workspace_size(int B, int Hq, int Hkv, int S, int D, int block, int stride,
+                                                         size_t* bytes) {
+  if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || S < 1 || block < 1 || stride < 1) return BSA_E_ARG;
+  if (block % stride != 0) return BSA_E_ARG;
+  const int R = block / stride;
+  if (R != 2 && R != 4 && R != 8 && R != 16) return BSA_E_UNSUPPORTED;
+  if (stride != 4 && stride != 8 && stride != 16 && stride != 32) return BSA_E_UNSUPPORTED;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  const ScoreDims sd = score_dims(S, block, stride);
+  if (sd.nb > 1024) return BSA_E_UNSUPPORTED;
+  *bytes = static_cast<size_t>(B) * Hq * sd.Ns * (static_cast<size_t>(sd.nb) + 2 * sd.ntk) * sizeof(float);
+  return BSA_OK;
+}
+
+extern "C" bsa_status bsa_antidiag_scores(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                                          const int32_t* perm, int block, int stride, float score_scale, int pool_gqa,
+                                          float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+  size_t need = 0;
+  bsa_status st = bsa_antidiag_scores_workspace_size(B, Hq, Hkv, S, D, block, stride, &need);
+  if (st != BSA_OK) return st;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (!Q || !K || !scores) return BSA_E_ARG;
+  if (!(score_scale > 0.0f) || !(score_scale < INFINITY)) return BSA_E_ARG;
+  if (pool_gqa != 0 && pool_gqa != 1) return BSA_E_ARG;
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+  const ScoreDims sd = score_dims(S, block, stride);
+  const int R = block / stride;
+  if (dtype == BSA_BF16) {
+    if (D == 128) return dispatch_r<bf16_t, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
+    return dispatch_r<bf16_t, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
+  }
+  if (D == 128) return dispatch_r<float, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
+  return dispatch_r<float, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
+}

@@ -1,0 +1,177 @@
+// Per-row top-p block selection and kept-block lists.
+//
+// "Dynamic block masks and head-wise mask reuse", section "XAttention -- anti-diagonal block
+// scoring": each query block keeps the smallest set of key blocks whose mass reaches tau of
+// the row total; section "Deviations from the papers": at least one block per row, key
+// block 0 not forced.  Equal scores are taken by lower key-block index.
+#include "common.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int kMaxCk = 1024;
+
+__device__ __forceinline__ uint32_t sortable(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads).
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int add = t >= d ? tmp[t - d] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const int incl = tmp[t];
+  *total = tmp[255];
+  __syncthreads();
+  return incl - v;
+}
+
+// One workgroup (256 threads) per score row.
+__global__ __launch_bounds__(256) void top_p_kernel(const float* __restrict__ scores, int Cq, int Ck,
+                                                     const float* __restrict__ tau, int n_tau, int Hs,
+                                                     uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
+                                                     int16_t* __restrict__ kv_idx) {
+  __shared__ uint64_t key[kMaxCk];
+  __shared__ float csum[kMaxCk];
+  __shared__ int tmpi[256];
+  __shared__ float tmpf[256];
+  __shared__ uint8_t kb[kMaxCk];
+  const size_t row = blockIdx.x;
+  const int g = static_cast<int>(row / Cq);
+  const float tau_r = n_tau == 1 ? tau[0] : tau[g % Hs];
+  const float* srow = scores + row * Ck;
+  int n2 = 1;
+  while (n2 < Ck) n2 <<= 1;
+  for (int i = threadIdx.x; i < n2; i += 256) {
+    // Descending by score, then ascending by index: the low word is the inverted index.
+    key[i] = i < Ck ? (static_cast<uint64_t>(sortable(srow[i])) << 32) | static_cast<uint32_t>(0xffffffffu - i) : 0ull;
+  }
+  __syncthreads();
+  // Bitonic sort, descending.
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 256) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t a = key[i], b = key[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            key[i] = b;
+            key[p] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Inclusive prefix sum of the sorted scores: 4 consecutive entries per thread, then a
+  // scan over the thread totals.
+  float loc[4];
+  float run = 0.0f;
+  const int b0 = threadIdx.x * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = b0 + e;
+    float s = 0.0f;
+    if (i < Ck) s = srow[0xffffffffu - static_cast<uint32_t>(key[i])];
+    run += s;
+    loc[e] = run;
+  }
+  tmpf[threadIdx.x] = run;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const float add = threadIdx.x >= static_cast<unsigned>(d) ? tmpf[threadIdx.x - d] : 0.0f;
+    __syncthreads();
+    tmpf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const float before = tmpf[threadIdx.x] - run;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (b0 + e < kMaxCk) csum[b0 + e] = before + loc[e];
+  __syncthreads();
+  const float target = tau_r * csum[Ck - 1];
+  // Shortest prefix reaching the target: the first rank whose cumulative mass >= target.
+  int first = Ck - 1;
+  for (int i = threadIdx.x; i < Ck; i += 256)
+    if (csum[i] >= target) first = min(first, i);
+  tmpi[threadIdx.x] = first;
+  __syncthreads();
+  for (int d = 128; d > 0; d >>= 1) {
+    if (threadIdx.x < static_cast<unsigned>(d)) tmpi[threadIdx.x] = min(tmpi[threadIdx.x], tmpi[threadIdx.x + d]);
+    __syncthreads();
+  }
+  const int last = tmpi[0];
+  __syncthreads();
+  for (int i = threadIdx.x; i < Ck; i += 256) kb[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i <= last; i += 256) kb[0xffffffffu - static_cast<uint32_t>(key[i])] = 1;
+  __syncthreads();
+  uint8_t* krow = keep + row * Ck;
+  for (int i = threadIdx.x; i < Ck; i += 256) krow[i] = kb[i];
+  // Ascending kept list.
+  int16_t* lrow = kv_idx + row * Ck;
+  int offset = 0;
+  for (int c0 = 0; c0 < Ck; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int bit = c < Ck ? kb[c] : 0;
+    int total;
+    const int pos = block_excl_scan(bit, tmpi, &total);
+    if (bit) lrow[offset + pos] = static_cast<int16_t>(c);
+    offset += total;
+  }
+  if (threadIdx.x == 0) kv_count[row] = offset;
+}
+
+__global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restrict__ keep, int Ck,
+                                                          int32_t* __restrict__ kv_count,
+                                                          int16_t* __restrict__ kv_idx) {
+  __shared__ int tmpi[256];
+  const size_t row = blockIdx.x;
+  const uint8_t* krow = keep + row * Ck;
+  int16_t* lrow = kv_idx + row * Ck;
+  int offset = 0;
+  for (int c0 = 0; c0 < Ck; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int bit = (c < Ck && krow[c] != 0) ? 1 : 0;
+    int total;
+    const int pos = block_excl_scan(bit, tmpi, &total);
+    if (bit) lrow[offset + pos] = static_cast<int16_t>(c);
+    offset += total;
+  }
+  if (threadIdx.x == 0) kv_count[row] = offset;
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" bsa_status bsa_top_p_mask(const float* scores, int G, int Cq, int Ck, const float* tau, int n_tau, int Hs,
+                                     uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream) {
+  if (!scores || !tau || !keep || !kv_count || !kv_idx) return BSA_E_ARG;
+  if (G < 1 || Cq < 1 || Ck < 1 || Hs < 1) return BSA_E_ARG;
+  if (n_tau != 1 && n_tau != Hs) return BSA_E_SHAPE;
+  if (G % Hs != 0) return BSA_E_SHAPE;
+  if (Ck > kMaxCk) return BSA_E_UNSUPPORTED;
+  const long long rows = static_cast<long long>(G) * Cq;
+  if (rows > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
+  hipLaunchKernelGGL(top_p_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, scores, Cq, Ck, tau, n_tau,
+                     Hs, keep, kv_count, kv_idx);
+  return launch_status();
+}
+
+extern "C" bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_count, int16_t* kv_idx,
+                                     hipStream_t stream) {
+  if (!keep || !kv_count || !kv_idx || rows < 1 || Ck < 1) return BSA_E_ARG;
+  if (Ck > 32767) return BSA_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mask_lists_kernel, dim3(rows), dim3(256), 0, stream, keep, Ck, kv_count, kv_idx);
+  return launch_status();
+}

@@ -1,0 +1,116 @@
+"""The whole path as one call: layout -> centroids -> scores -> top-p -> sparse attention
+-> probe rows -> fit -> correction.
+
+Order of stages: "Dynamic block masks and head-wise mask reuse", section "Recipe" (scores,
+top-p mask, labels, compensated attention) and "Sparse-block compensation", section
+"Recipe: STA with both repairs" (compensated attention, probe selection, dense probe rows,
+residual correction).  Every stage is one or two kernel launches on the current stream;
+nothing is computed on the host except the probe selection, which depends only on the
+labels and is done once.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import api
+
+
+@dataclass
+class PathConfig:
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    labels: np.ndarray  # int32 [S] (host)
+    C: int
+    scale: float
+    mask_mode: str  # "given" or "scored"
+    keep: Optional[np.ndarray] = None  # given mode: uint8 [B or 1, Hm, C, C]
+    block: int = 128
+    stride: int = 16
+    score_scale: Optional[float] = None
+    tau: Optional[np.ndarray] = None  # scored mode: [Hs]
+    pool_gqa: bool = False
+    compensate: bool = True
+    probes: int = 0
+    lam: float = 0.1
+    rank: int = 16
+
+    @classmethod
+    def from_workload(cls, wl) -> "PathConfig":
+        return cls(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, S=wl.S, D=wl.D, labels=wl.labels, C=wl.C, scale=wl.scale,
+                   mask_mode=wl.mask_mode, keep=wl.mask, block=wl.block, stride=wl.stride,
+                   score_scale=wl.score_scale or None, tau=wl.tau, pool_gqa=wl.pool_gqa, compensate=wl.compensate,
+                   probes=wl.probes, lam=wl.lam, rank=wl.rank)
+
+
+@dataclass
+class PathResult:
+    out: torch.Tensor
+    layout: api.ClusterLayout
+    mask: api.BlockMask
+    scores: Optional[torch.Tensor] = None
+    kbar: Optional[torch.Tensor] = None
+    vbar: Optional[torch.Tensor] = None
+    out_sparse: Optional[torch.Tensor] = None  # before the correction (copy; only if requested)
+    o_dense_probe: Optional[torch.Tensor] = None
+    o_sparse_probe: Optional[torch.Tensor] = None
+    A: Optional[torch.Tensor] = None
+    c: Optional[torch.Tensor] = None
+    extras: dict = field(default_factory=dict)
+
+
+class SparseAttentionPath:
+    """Holds the per-call constants (labels, probe rows, thresholds) on the device."""
+
+    def __init__(self, cfg: PathConfig, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
+        if cfg.mask_mode == "given":
+            keep = np.asarray(cfg.keep, dtype=np.uint8)
+            if keep.shape[0] == 1 and cfg.B > 1:
+                keep = np.broadcast_to(keep, (cfg.B,) + keep.shape[1:])
+            self.given_keep = torch.as_tensor(np.ascontiguousarray(keep)).to(self.device)
+        else:
+            self.tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(self.device)
+        if cfg.probes:
+            idx, w = api.select_probe_rows(cfg.labels, cfg.C, cfg.probes)
+            self.probe_idx = torch.as_tensor(idx).to(self.device)
+            self.probe_w = torch.as_tensor(w).to(self.device)
+
+    def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False) -> PathResult:
+        """Run the path.  With probes the fit runs before the attention, whose epilogue
+        applies the correction to every row; keep_sparse additionally returns the output
+        without correction (one more attention launch, for inspection)."""
+        cfg = self.cfg
+        layout = api.cluster_layout(self.labels, cfg.C)
+        kbar = vbar = None
+        if cfg.compensate:
+            kbar, vbar = api.centroids(k, v, layout)
+        scores = None
+        if cfg.mask_mode == "scored":
+            scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
+                                                   cfg.score_scale or 1.0 / math.sqrt(cfg.D), cfg.pool_gqa)
+            mask = api.top_p_block_mask(scores, self.tau)
+        else:
+            mask = api.mask_from_keep(self.given_keep)
+        res = PathResult(out=None, layout=layout, mask=mask, scores=scores, kbar=kbar, vbar=vbar)
+        A = c = None
+        if cfg.probes:
+            od, os_ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale, self.labels, self.labels, layout, mask,
+                                          kbar, vbar)
+            A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
+            res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
+            if keep_sparse:
+                res.out_sparse = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar,
+                                                                    cfg.scale)
+        res.out = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar, cfg.scale, A=A, c=c)
+        return res

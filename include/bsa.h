@@ -1,0 +1,230 @@
+/*
+ * bsa.h -- block-sparse video-DiT attention on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The library computes one path, stage by stage:
+ *   cluster layout -> centroids -> antidiagonal block scores -> per-row top-p block mask
+ *   -> block-sparse flash attention with centroid compensation (or hard drop)
+ *   -> exact dense probe rows -> weighted ridge fit -> correction of every row.
+ *
+ * Sources (cited by page title and section):
+ *   [SBC] "Sparse-block compensation" (mlx-arsenal research note)
+ *   [HMR] "Dynamic block masks and head-wise mask reuse" (mlx-arsenal research note)
+ *   [SPR] "Partition the Support, Reconstruct the Residual" (paper summary page)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors.  Q is [B, Hq, S, D]; K and V are [B, Hkv, S, D]; O has Q's shape.  All are
+ *   dense row-major (the innermost dimension D is contiguous) and hold `dtype`
+ *   elements (BSA_F32 = float, BSA_BF16 = bfloat16 bit patterns).  Hq must be a multiple
+ *   of Hkv; query head h reads K/V head h / (Hq / Hkv) (grouped-query attention).
+ *   D must be 64 or 128.
+ * Labels.  Cluster labels are int32 [S] in [0, C), shared by every batch entry and head
+ *   ([SBC] "Deviations from the papers": clusters are caller inputs).  A cluster layout
+ *   (perm, offsets) lists token positions cluster by cluster: cluster c owns
+ *   perm[offsets[c] .. offsets[c+1]).
+ * Block masks.  keep is uint8 [B, Hm, Cq, Ck] (nonzero = block kept), with Hm one of
+ *   1 (shared by all heads), Hkv (shared by the query heads of a K/V group, [SPR]
+ *   grouped-query sharing) or Hq.  The kept-block list of a mask row is kv_count int32
+ *   [B, Hm, Cq] and kv_idx int16 [B, Hm, Cq, Ck]: row r lists its kept key clusters in
+ *   ascending order in kv_idx[r][0 .. kv_count[r]); the rest of the row is unused.
+ * Memory.  Every pointer argument is caller-owned.  Pointers named "host" point to host
+ *   memory; all others are device pointers on the current HIP device.  The library never
+ *   allocates result memory; calls that need scratch memory take a caller-provided
+ *   workspace of at least the size the matching *_workspace_size call reports.
+ * Streams.  Device calls are asynchronous and ordered on the given stream (0 = the null
+ *   stream).  They keep no state between calls and may be called from several threads.
+ * Errors.  Every call validates its scalar arguments and pointers on the host before any
+ *   launch; an invalid call returns an error and enqueues nothing.  BSA_E_HIP reports a
+ *   failed launch (hipGetLastError).  Device-side data (labels, kv lists) is not checked:
+ *   out-of-range values are skipped by the kernels rather than read or written out of
+ *   bounds, and they make the result undefined.  No C++ exception crosses this ABI.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_E_ARG = 1,         /* null pointer or scalar out of range */
+  BSA_E_SHAPE = 2,       /* sizes inconsistent with each other */
+  BSA_E_DTYPE = 3,       /* unknown element type */
+  BSA_E_UNSUPPORTED = 4, /* valid request this library does not implement (e.g. D = 96) */
+  BSA_E_WORKSPACE = 5,   /* workspace missing or too small */
+  BSA_E_HIP = 6          /* a kernel launch failed */
+} bsa_status;
+
+typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype;
+
+/* Text for a status code (static storage). */
+const char* bsa_status_string(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int bsa_abi_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * Cluster layout.  [SPR] group-major permutation: tokens are ordered cluster by cluster,
+ * keeping their given order inside a cluster (a stable counting sort of the labels).
+ *   labels  int32 [S] in [0, C)            (tokens with other labels are left out)
+ *   perm    int32 [S]   out: token positions in cluster-major order
+ *   offsets int32 [C+1] out: exclusive prefix sum of counts
+ *   counts  int32 [C]   out: tokens per cluster
+ * Needs S >= 1, 1 <= C <= 8192 and workspace of bsa_cluster_layout_workspace_size bytes.
+ */
+bsa_status bsa_cluster_layout_workspace_size(int S, int C, size_t* bytes_host);
+bsa_status bsa_cluster_layout(const int32_t* labels, int S, int C, int32_t* perm, int32_t* offsets,
+                              int32_t* counts, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Centroids.  [SBC] "SVG-EAR -- centroid compensation": kbar_c and vbar_c are the means of
+ * the keys and values of key cluster c, per (batch, K/V head); n_c = offsets[c+1]-offsets[c].
+ *   K, V   [B, Hkv, S, D] dtype;  perm/offsets: key cluster layout with C clusters
+ *   Kbar, Vbar float [B, Hkv, C, D] out (float32 sums; an empty cluster gives zeros)
+ */
+bsa_status bsa_centroids(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
+                         const int32_t* perm, const int32_t* offsets, int C, float* Kbar, float* Vbar,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Antidiagonal block scores.  [HMR] "XAttention -- anti-diagonal block scoring": over the
+ * cluster-major token order (perm; NULL = identity), zero-padded to Sp = nb*block tokens
+ * with nb = ceil(S / block) ([HMR] "Out of scope, and why": padding, padded keys take
+ * mass), the strided logit of strided rows (i', j') is
+ *     score_scale * sum_{t<stride} q[i'*stride + stride-1-t] . k[j'*stride + t],
+ * each strided row is softmaxed over all Sp/stride columns, block x block tiles are summed,
+ * and each row of block sums is divided by its total ([HMR] "Deviations from the papers").
+ * With pool_gqa = 1 the scores of the query heads of each K/V group are averaged (the
+ * group shares one mask, [SPR] grouped-query sharing).
+ *   Q [B, Hq, S, D], K [B, Hkv, S, D] dtype; perm int32 [S] or NULL
+ *   scores float [B, Hs, nb, nb] out, Hs = pool_gqa ? Hkv : Hq
+ * Needs stride in {4, 8, 16, 32}, block % stride == 0, block / stride in {2, 4, 8, 16},
+ * D in {64, 128}, and workspace of bsa_antidiag_scores_workspace_size bytes.
+ */
+bsa_status bsa_antidiag_scores_workspace_size(int B, int Hq, int Hkv, int S, int D, int block, int stride,
+                                              size_t* bytes_host);
+bsa_status bsa_antidiag_scores(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                               const int32_t* perm, int block, int stride, float score_scale, int pool_gqa,
+                               float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Per-row top-p block mask.  [HMR] "XAttention -- anti-diagonal block scoring": each row
+ * keeps the smallest set of key blocks whose mass reaches tau of the row total (blocks
+ * taken by descending score, equal scores by lower index); [HMR] "Deviations from the
+ * papers": at least one block per row, block 0 not forced.
+ *   scores float [G, Cq, Ck] with G = B * Hs row groups (one per batch entry and mask head)
+ *   tau    float [n_tau]: n_tau == 1 (one value) or n_tau == Hs (row group g uses tau[g % Hs])
+ *   keep   uint8 [G, Cq, Ck] out;  kv_count int32 [G, Cq] out;  kv_idx int16 [G, Cq, Ck] out
+ * Needs 1 <= Ck <= 1024 and 0 < tau <= 1.
+ */
+bsa_status bsa_top_p_mask(const float* scores, int G, int Cq, int Ck, const float* tau, int n_tau, int Hs,
+                          uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream);
+
+/* Kept-block lists of a caller-given mask: keep uint8 [rows, Ck] -> kv_count int32 [rows],
+ * kv_idx int16 [rows, Ck] (ascending).  Needs 1 <= Ck <= 32767. */
+bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_count, int16_t* kv_idx,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Block-sparse attention with centroid compensation.  [SBC] "The problem", "SVG-EAR --
+ * centroid compensation" and "No LSE needed": query row i of cluster a attends to every
+ * key of every kept key cluster (kv list of its mask row) and, when Kbar/Vbar are given,
+ * to one extra column per skipped non-empty key cluster c with logit
+ * q_i . kbar_c * scale + log n_c and value vbar_c, all inside one softmax.  With
+ * Kbar == Vbar == NULL skipped blocks are dropped (hard drop; the softmax renormalizes over
+ * kept keys).  A row with no column at all gets O = 0 and lse = -inf.
+ * With A and c given (from bsa_probe_fit), every output row o is replaced by o + o A + c
+ * before it is rounded to dtype ([SPR]: the correction is applied to all rows).
+ *   Q [B, Hq, S, D], K, V [B, Hkv, S, D], O [B, Hq, S, D] out, all dtype
+ *   q_perm/q_offsets (Cq clusters) and k_perm/k_offsets (Ck clusters): cluster layouts
+ *   keep/kv_count/kv_idx: block mask with Hm in {1, Hkv, Hq}
+ *   Kbar, Vbar float [B, Hkv, Ck, D] (from bsa_centroids) or both NULL
+ *   A float [B, Hq, D, D], c float [B, Hq, D] (correction) or both NULL
+ *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
+ */
+bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                                const void* V, float scale, const int32_t* q_perm, const int32_t* q_offsets,
+                                int Cq, const int32_t* k_perm, const int32_t* k_offsets, int Ck,
+                                const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                                const float* Kbar, const float* Vbar, const float* A, const float* c, void* O,
+                                float* lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)
+ * get exact dense attention over all S keys, O_dense[p] = softmax(q_p K^T scale) V ([SBC]
+ * "Recipe: STA with both repairs" computes them the same way).  When O_sparse_probe is given
+ * the same rows are also computed under the block-sparse rule of bsa_sparse_attention
+ * (their cluster's kept blocks, plus centroid columns when Kbar/Vbar are given), in float32,
+ * so the fit sees unrounded sparse outputs.
+ *   probe_idx int32 [M] token positions (shared by all heads, [SBC] API table)
+ *   q_labels, k_labels int32 [S]: query / key cluster labels (the layouts' labels)
+ *   keep [B, Hm, Cq, Ck], k_offsets [Ck+1], Kbar/Vbar: as for bsa_sparse_attention
+ *   O_dense_probe, O_sparse_probe float [B, Hq, M, D] out (O_sparse_probe may be NULL: then
+ *   the label, mask and centroid arguments are ignored)
+ * Needs 1 <= M <= 1024, Ck <= 2048 and workspace of bsa_probe_attention_workspace_size bytes.
+ */
+bsa_status bsa_probe_attention_workspace_size(int B, int Hq, int S, int D, int M, size_t* bytes_host);
+bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                               const void* V, float scale, const int32_t* probe_idx, int M, const int32_t* q_labels,
+                               const int32_t* k_labels, const uint8_t* keep, int Hm, int Cq, int Ck,
+                               const int32_t* k_offsets, const float* Kbar, const float* Vbar, float* O_dense_probe,
+                               float* O_sparse_probe, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Ridge fit.  [SPR] Probe-Fitted Residual Reconstruction and [SBC] "Deviations from the
+ * papers".  Per (batch, head), from the sparse rows X0 = O_sparse_probe and the exact rows
+ * O_dense_probe of the M probes:
+ *   w = weights / sum(weights); R = O_dense_probe - X0;
+ *   mu = sum w X0; sigma = sqrt(sum w (X0 - mu)^2) (below 1e-6 -> 1); X = (X0 - mu) / sigma;
+ *   rbar = sum w R; Rc = R - rbar;  W = (X^T W X + lambda I)^-1 X^T W Rc   (W = diag(w));
+ *   P = V_r V_r^T with V_r the top min(rank, #eigenvalues > 1e-12 * max) eigenvectors of
+ *   Rc^T diag(w) Rc;  A = diag(1/sigma) W P;  c = rbar - mu A.
+ * The correction of any row o is then o A + c.  Computed in float64 on the device.
+ *   O_sparse_probe, O_dense_probe float [B, Hq, M, D]; weights float [M] > 0
+ *   A float [B, Hq, D, D] out (row-major: correction_j = sum_i o_i A[i][j] + c_j); c float [B, Hq, D] out
+ * Needs 2 <= M <= 64, lambda > 0 and 1 <= rank <= 16 (rank <= D).
+ */
+bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_probe, const float* O_dense_probe,
+                         const float* weights, int M, float lambda, int rank, float* A, float* c, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Correction of an existing output ([SPR]: the correction is applied to all rows; probe rows
+ * are corrected too, not overwritten):  O <- O + O A + c, in place, per (batch, head).
+ * bsa_sparse_attention applies the same correction in its epilogue; this call serves
+ * outputs computed elsewhere.
+ */
+bsa_status bsa_probe_apply(int B, int Hq, int S, int D, int dtype, void* O, const float* A, const float* c,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Host helpers (host pointers only).
+ *
+ * Probe rows.  [SBC] API table and "Deviations from the papers": probes are shared by all
+ * heads; each query cluster's members are taken middle-out (positions in ascending order,
+ * member floor(n/2) first, then n/2-1, n/2+1, n/2-2, ...), round-robin over clusters; each
+ * probe of cluster a weighs |G_a| / m_a (cluster size over probes taken from it) and the
+ * weights are normalized to sum to 1.  When M is below the number of non-empty clusters the
+ * single round visits clusters floor((j + 1/2) * C_nonempty / M), j < M, spreading the
+ * probes over the sequence ([SPR]: probes are stratified across query groups).
+ *   labels_host int32 [S]; probe_idx_host int32 [M] out; weights_host float [M] out
+ */
+bsa_status bsa_select_probe_rows(const int32_t* labels_host, int S, int C, int M, int32_t* probe_idx_host,
+                                 float* weights_host);
+
+/* Sliding-tile labels of a T x H x W raster-order grid ([SBC] API table: tile_labels).
+ * chunk == 0: the id of the (tt, th, tw) tile holding each token (tiles in raster order,
+ * edge tiles partial).  chunk > 0: tokens ranked tile-major (raster order inside a tile),
+ * label = rank / chunk.   labels_host int32 [T*H*W] out. */
+bsa_status bsa_tile_labels(int T, int H, int W, int tt, int th, int tw, int chunk, int32_t* labels_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

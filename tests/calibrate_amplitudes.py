@@ -49,5 +49,5 @@ def bisect(cfg, target, lo, hi, heads, iters=7):
 
 if __name__ == "__main__":
     a2 = bisect(2, 0.22, 0.55, 0.9, heads=list(range(8)))
-    a4 = bisect(4, 0.26, 0.45, 0.9, heads=list(range(10)))
+    a4 = bisect(4, 0.26, 0.85, 1.8, heads=list(range(10)))
     print(f"AMPLITUDE_CFG2 = {a2:.4f}\nAMPLITUDE_CFG4 = {a4:.4f}")

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point,
+its host helpers agree with the oracle, and invalid calls are rejected on the host before
+any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_attention_antidiagonal_amd import _lib
+
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for must in ("bsa_cluster_layout", "bsa_centroids", "bsa_antidiag_scores", "bsa_top_p_mask",
+                 "bsa_sparse_attention", "bsa_probe_attention", "bsa_probe_fit", "bsa_probe_apply",
+                 "bsa_select_probe_rows", "bsa_tile_labels"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from block_sparse_attention_antidiagonal_amd import _lib
+
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_status_string(0) == b"ok"
+    assert b"workspace" in lib.bsa_status_string(5)
+
+
+def test_probe_selection_matches_oracle():
+    from block_sparse_attention_antidiagonal_amd import api
+    from oracle import repair
+
+    rng = np.random.default_rng(0)
+    for C, S, M in ((9, 400, 64), (256, 32760, 64), (3, 10, 5), (40, 500, 40), (7, 30, 30)):
+        labels = rng.integers(0, C, size=S).astype(np.int32)
+        idx, w = api.select_probe_rows(labels, C, M)
+        ridx, rw = repair.select_probe_rows(labels, C, M)
+        assert np.array_equal(idx, ridx)
+        assert np.allclose(w, rw, rtol=1e-6, atol=0)
+
+
+def test_probe_selection_on_video_labels_matches_oracle():
+    from block_sparse_attention_antidiagonal_amd import api
+    from oracle import repair
+    from synthetic import grid_tile_labels
+
+    labels = grid_tile_labels(21, 30, 52, (2, 8, 8), 128)
+    idx, w = api.select_probe_rows(labels, 256, 64)
+    ridx, rw = repair.select_probe_rows(labels, 256, 64)
+    assert np.array_equal(idx, ridx) and np.allclose(w, rw, rtol=1e-6)
+
+
+def test_tile_labels_match_oracle_and_inputs():
+    from block_sparse_attention_antidiagonal_amd import api
+    from oracle import layout
+    from synthetic import grid_tile_labels
+
+    for T, H, W, tile, chunk in ((2, 3, 4, (1, 2, 2), 0), (2, 3, 4, (1, 2, 2), 3), (5, 7, 9, (2, 3, 4), 11),
+                                 (21, 30, 52, (2, 8, 8), 128)):
+        got = api.tile_labels(T, H, W, tile, chunk)
+        assert np.array_equal(got, layout.tile_labels(T, H, W, tile, chunk))
+        assert np.array_equal(got, grid_tile_labels(T, H, W, tile, chunk))
+
+
+def test_video_labels_are_256_clusters_of_128():
+    from synthetic import grid_tile_labels
+
+    lab = grid_tile_labels(21, 30, 52, (2, 8, 8), 128)
+    counts = np.bincount(lab)
+    assert counts.size == 256 and np.all(counts[:-1] == 128) and counts[-1] == 120
+
+
+def test_host_validation_rejects_before_launch(lib):
+    dummy = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    size = ctypes.c_size_t(0)
+    # unknown dtype
+    assert lib.bsa_centroids(1, 1, 8, 128, 7, dummy, dummy, dummy, dummy, 1, dummy, dummy, None) == 3
+    # unsupported head dim
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
+                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, None, None, dummy, None,
+                                    None) == 4
+    # Hq not a multiple of Hkv
+    assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
+                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, None, None, dummy, None,
+                                    None) == 2
+    # only one of Kbar / Vbar; only one of A / c
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
+                                    dummy, dummy, 1, dummy, dummy, dummy, 1, dummy, None, None, None, dummy, None,
+                                    None) == 1
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
+                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, dummy, None, dummy, None,
+                                    None) == 1
+    # probe rows: sparse rows need the mask; too many key clusters
+    assert lib.bsa_probe_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, 4, None,
+                                   None, None, 1, 1, 1, None, None, None, dummy, dummy, dummy, 1 << 30, None) == 1
+    assert lib.bsa_probe_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, 4, dummy,
+                                   dummy, dummy, 1, 1, 4096, dummy, None, None, dummy, dummy, dummy, 1 << 30,
+                                   None) == 4
+    # null output
+    assert lib.bsa_probe_apply(1, 1, 8, 128, 1, None, dummy, dummy, None) == 1
+    # block not a multiple of stride
+    assert lib.bsa_antidiag_scores_workspace_size(1, 1, 1, 1024, 128, 100, 16, ctypes.byref(size)) == 1
+    # workspace too small
+    assert lib.bsa_cluster_layout(dummy, 100, 4, dummy, dummy, dummy, dummy, 0, None) == 5
+    # too many probes for the fit; bad lambda
+    assert lib.bsa_probe_fit(1, 1, 128, dummy, dummy, dummy, 65, ctypes.c_float(0.1), 16, dummy, dummy, None) == 4
+    assert lib.bsa_probe_fit(1, 1, 128, dummy, dummy, dummy, 64, ctypes.c_float(0.0), 16, dummy, dummy, None) == 1
+    assert lib.bsa_probe_fit(1, 1, 128, dummy, dummy, dummy, 64, ctypes.c_float(0.1), 17, dummy, dummy, None) == 4
+    # tau count must be 1 or one per head
+    assert lib.bsa_top_p_mask(dummy, 4, 8, 8, dummy, 3, 4, dummy, dummy, dummy, None) == 2
+
+
+def test_workspace_sizes(lib):
+    from block_sparse_attention_antidiagonal_amd import _lib
+
+    assert _lib.size_query("bsa_cluster_layout_workspace_size", 32760, 256) == 32 * 256 * 4
+    nb, ns, ntk = 256, 2048, 16
+    assert _lib.size_query("bsa_antidiag_scores_workspace_size", 1, 40, 40, 32760, 128, 128, 16) == \
+        40 * ns * (nb + 2 * ntk) * 4
+    assert _lib.size_query("bsa_probe_attention_workspace_size", 1, 40, 32760, 128, 64) == 40 * 17 * 64 * 130 * 4

@@ -1,0 +1,115 @@
+"""GPU parity of the whole path on the five named workloads.
+
+Configs 0 and 1 are checked on every row of every head.  The video-shaped configs 2-4
+run at full size in the same launch configuration the benchmark times; the oracle then
+checks the masks of sampled heads (bit-exact outside fragile blocks) and the outputs of
+sampled rows (the ragged last cluster and the probe rows always included), using the GPU's
+own mask so that mask rounding cannot leak into output parity.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle import pipeline as opipe
+from oracle import repair as orep
+from synthetic import make_config
+
+from gpu_common import check_output, compare_masks, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import block_sparse_attention_antidiagonal_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run_gpu(bsa, wl):
+    path = bsa.SparseAttentionPath(bsa.PathConfig.from_workload(wl))
+    q, k, v = dev(wl.q, wl.dtype), dev(wl.k, wl.dtype), dev(wl.v, wl.dtype)
+    res = path(q, k, v, keep_sparse=True)
+    torch.cuda.synchronize()
+    return path, res
+
+
+def check_masks(wl, res, pairs):
+    keep = res.mask.keep.cpu().numpy()
+    cnt = res.mask.kv_count.cpu().numpy()
+    idx = res.mask.kv_idx.cpu().numpy()
+    frag = 0
+    for b, hm in pairs:
+        if wl.mask_mode == "given":
+            want = wl.mask[b if wl.mask.shape[0] > 1 else 0, hm if wl.mask.shape[1] > 1 else 0]
+            assert np.array_equal(keep[b, hm], want)
+            continue
+        ref = opipe.mask_scores(wl, b, hm)
+        frag += compare_masks(keep[b, hm], cnt[b, hm], idx[b, hm], ref, float(wl.tau[hm]),
+                              f"mask b{b} head{hm}")["fragile_rows"]
+    return frag
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_small_config_every_row(bsa, cfg):
+    say(f"config {cfg} full")
+    wl = make_config(cfg)
+    path, res = run_gpu(bsa, wl)
+    Hm = res.mask.Hm
+    check_masks(wl, res, [(b, h) for b in range(wl.B) for h in range(Hm)])
+    keep = res.mask.keep.cpu().numpy()
+    out = host(res.out)
+    for b in range(wl.B):
+        for hq in range(wl.Hq):
+            r = opipe.run_head(wl, b, hq, keep=keep[b, opipe.mask_head_of(wl, hq)])
+            e = check_output(out[b, hq], r["out"], wl.dtype, f"config {cfg} b{b} h{hq}")
+            say(f"config {cfg} b{b} h{hq} error {e:.3e}")
+
+
+def sample_rows(wl, probe_idx, n=320, seed=0):
+    rng = np.random.default_rng(seed)
+    last = np.nonzero(wl.labels == wl.labels.max())[0]
+    rows = np.concatenate([rng.choice(wl.S, size=n, replace=False), last[:64], probe_idx if probe_idx is not None else []])
+    return np.unique(rows.astype(np.int64))
+
+
+@pytest.mark.parametrize("cfg,heads", [(2, [(0, 0), (0, 17), (0, 39)]), (3, [(0, 5), (0, 38)]),
+                                       (4, [(0, 0), (0, 4), (1, 17), (1, 39)])])
+def test_video_config_sampled(bsa, cfg, heads):
+    say(f"config {cfg} generate")
+    wl = make_config(cfg)
+    say(f"config {cfg} gpu path")
+    path, res = run_gpu(bsa, wl)
+    keep = res.mask.keep.cpu().numpy()
+    mask_pairs = sorted({(b, opipe.mask_head_of(wl, h)) for b, h in heads})
+    say(f"config {cfg} masks {mask_pairs}")
+    check_masks(wl, res, mask_pairs)
+    density = float(keep.mean())
+    say(f"config {cfg} mask density {density:.4f}")
+    probe_idx = path.probe_idx.cpu().numpy() if wl.probes else None
+    rows = sample_rows(wl, probe_idx)
+    out = host(res.out)
+    out_sparse = host(res.out_sparse) if res.out_sparse is not None else out
+    for b, hq in heads:
+        say(f"config {cfg} b{b} h{hq} rows {rows.size}")
+        hm = opipe.mask_head_of(wl, hq)
+        r = opipe.run_head(wl, b, hq, rows=rows, keep=keep[b, hm])
+        e1 = check_output(out_sparse[b, hq][rows], r["out_sparse"], wl.dtype, f"sparse b{b} h{hq}")
+        e2 = check_output(out[b, hq][rows], r["out"], wl.dtype, f"final b{b} h{hq}")
+        say(f"config {cfg} b{b} h{hq} error sparse {e1:.3e} final {e2:.3e}")
+        if wl.probes:
+            # Probe invariant on the GPU's own numbers: repaired probe rows differ from the
+            # exact rows by the fit residual of the oracle's fit on the same inputs.
+            od = host(res.o_dense_probe)[b, hq]
+            check_output(od, r["o_dense_p"], wl.dtype, f"dense probe rows b{b} h{hq}")
+            xs = host(res.o_sparse_probe)[b, hq]
+            check_output(xs, r["o_sparse_p"], wl.dtype, f"sparse probe rows b{b} h{hq}")
+            fit = orep.ridge_fit(xs, od, path.probe_w.cpu().numpy(), wl.lam, wl.rank)
+            resid = fit["X"] @ fit["W"] @ fit["P"] - fit["Rc"]
+            got = out[b, hq][probe_idx] - od
+            err = np.linalg.norm(got - resid) / np.linalg.norm(od)
+            say(f"config {cfg} b{b} h{hq} probe invariant rel err {err:.3e}")
+            assert err < 5e-3, f"probe invariant b{b} h{hq}: {err:.3e}"

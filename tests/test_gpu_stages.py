@@ -1,0 +1,309 @@
+"""GPU parity, stage by stage: every kernel against the oracle on the same seeded inputs,
+at sizes the oracle finishes in seconds that still span several tiles and ragged tails."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle import centroids as ocen
+from oracle import layout as olay
+from oracle import repair as orep
+from oracle import scoring as osco
+from synthetic import make_custom
+
+from gpu_common import check_output, compare_masks, dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import block_sparse_attention_antidiagonal_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+# ------------------------------------------------------------------ layout
+
+
+@pytest.mark.parametrize("S,C,seed", [(1, 1, 0), (1000, 7, 1), (4096, 300, 2), (32760, 256, 3), (5000, 8192, 4)])
+def test_cluster_layout_bit_exact(bsa, S, C, seed):
+    say(f"layout S={S} C={C}")
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, C, size=S).astype(np.int32)
+    if C > 2:
+        labels[labels == 1] = 2  # an empty cluster
+    lay = bsa.cluster_layout(torch.from_numpy(labels).cuda(), C)
+    perm, off, cnt = olay.cluster_layout(labels, C)
+    assert np.array_equal(lay.perm.cpu().numpy(), perm)
+    assert np.array_equal(lay.offsets.cpu().numpy(), off)
+    assert np.array_equal(lay.counts.cpu().numpy(), cnt)
+
+
+# ------------------------------------------------------------------ centroids
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_centroids(bsa, dtype, D):
+    say(f"centroids {dtype} D={D}")
+    wl = make_custom(11, B=2, Hq=2, Hkv=2, S=1500, D=D, dtype=dtype)
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, wl.C)
+    kbar, vbar = bsa.centroids(dev(wl.k, dtype), dev(wl.v, dtype), lay)
+    for b in range(2):
+        for h in range(2):
+            kb, vb, n = ocen.centroids(wl.k[b, h], wl.v[b, h], wl.labels, wl.C)
+            assert np.allclose(host(kbar[b, h]), kb, rtol=1e-5, atol=1e-6)
+            assert np.allclose(host(vbar[b, h]), vb, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------------ top-p
+
+
+@pytest.mark.parametrize("Ck,seed", [(1, 0), (16, 1), (32, 2), (256, 3), (1000, 4)])
+def test_top_p(bsa, Ck, seed):
+    say(f"top-p Ck={Ck}")
+    rng = np.random.default_rng(seed)
+    B, Hs, Cq = 2, 3, 40
+    scores = rng.dirichlet(np.full(Ck, 0.3), size=(B, Hs, Cq)).astype(np.float32)
+    scores[0, 0, 0] = 1.0 / Ck  # an all-equal row: ties by lower index
+    taus = np.array([0.85, 0.9, 0.95], dtype=np.float32)
+    mask = bsa.top_p_block_mask(torch.from_numpy(scores).cuda(), taus)
+    keep, cnt, idx = mask.keep.cpu().numpy(), mask.kv_count.cpu().numpy(), mask.kv_idx.cpu().numpy()
+    for b in range(B):
+        for h in range(Hs):
+            compare_masks(keep[b, h], cnt[b, h], idx[b, h], scores[b, h].astype(np.float64), float(taus[h]),
+                          f"top-p b{b} h{h}")
+    assert cnt.min() >= 1
+
+
+def test_mask_lists(bsa):
+    say("mask lists")
+    rng = np.random.default_rng(5)
+    keep = (rng.uniform(size=(2, 3, 17, 300)) < 0.3).astype(np.uint8)
+    m = bsa.mask_from_keep(torch.from_numpy(keep).cuda())
+    cnt, idx = m.kv_count.cpu().numpy(), m.kv_idx.cpu().numpy()
+    for r, row in enumerate(keep.reshape(-1, 300)):
+        want = np.nonzero(row)[0]
+        assert cnt.reshape(-1)[r] == want.size
+        assert np.array_equal(idx.reshape(-1, 300)[r, : want.size], want)
+
+
+# ------------------------------------------------------------------ scores
+
+
+@pytest.mark.parametrize(
+    "S,D,block,stride,dtype,Hq,Hkv,shuffle",
+    [
+        (1000, 128, 128, 16, "bf16", 2, 2, True),    # ragged tail, padded keys, gathered order
+        (4096, 128, 128, 16, "bf16", 2, 1, False),   # two 128-row tiles of strided rows
+        (2048, 64, 64, 8, "f32", 2, 2, True),        # R = 8, D = 64, float32
+        (777, 128, 64, 16, "bf16", 2, 2, False),     # R = 4
+        (900, 64, 32, 16, "bf16", 1, 1, True),       # R = 2
+        (3000, 128, 256, 16, "bf16", 1, 1, False),   # R = 16
+    ],
+)
+def test_antidiagonal_scores_and_mask(bsa, S, D, block, stride, dtype, Hq, Hkv, shuffle):
+    say(f"scores S={S} D={D} block={block} stride={stride} {dtype}")
+    wl = make_custom(21 + S, B=1, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype=dtype, block=block, mask="scored", noise=0.8)
+    labels = wl.labels.copy()
+    perm_np = None
+    if shuffle:
+        # Cluster-major order of shuffled positions: label = rank // block of a random order.
+        order = np.random.default_rng(S).permutation(S)
+        labels = np.empty(S, dtype=np.int32)
+        labels[order] = np.arange(S) // block
+    C = -(-S // block)
+    lay = bsa.cluster_layout(torch.from_numpy(labels.astype(np.int32)).cuda(), C)
+    perm_np = olay.cluster_layout(labels, C)[0]
+    q, k = dev(wl.q, dtype), dev(wl.k, dtype)
+    pool = Hq != Hkv
+    scores = bsa.antidiagonal_block_scores(q, k, lay, block, stride, 1 / math.sqrt(D), pool_gqa=pool)
+    got = host(scores)
+    taus = np.array([0.9] * scores.shape[1], dtype=np.float32)
+    mask = bsa.top_p_block_mask(scores, taus)
+    keep, cnt, idx = mask.keep.cpu().numpy(), mask.kv_count.cpu().numpy(), mask.kv_idx.cpu().numpy()
+    for hs in range(scores.shape[1]):
+        if pool:
+            g = Hq // Hkv
+            ref = np.mean([osco.antidiagonal_block_scores(wl.q[0, h], wl.k[0, hs], perm_np, block, stride,
+                                                          1 / math.sqrt(D)) for h in range(hs * g, (hs + 1) * g)], 0)
+        else:
+            ref = osco.antidiagonal_block_scores(wl.q[0, hs], wl.k[0, hs * Hkv // Hq], perm_np, block, stride,
+                                                 1 / math.sqrt(D))
+        assert np.allclose(got[0, hs], ref, rtol=1e-4, atol=1e-6), np.max(np.abs(got[0, hs] - ref))
+        compare_masks(keep[0, hs], cnt[0, hs], idx[0, hs], ref, 0.9, f"scores head {hs}")
+
+
+# ------------------------------------------------------------------ attention
+
+
+def run_attention(bsa, wl, keep_np, compensate, lse=False):
+    dtype = wl.dtype
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, wl.C)
+    q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
+    mask = bsa.mask_from_keep(torch.from_numpy(np.ascontiguousarray(keep_np)).cuda())
+    kbar = vbar = None
+    if compensate:
+        kbar, vbar = bsa.centroids(k, v, lay)
+    return bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, kbar, vbar, wl.scale, return_lse=lse)
+
+
+def oracle_attention(wl, keep_np, compensate, b, hq):
+    Hm = keep_np.shape[1]
+    hm = 0 if Hm == 1 else (hq if Hm == wl.Hq else hq // (wl.Hq // wl.Hkv))
+    kvh = hq // (wl.Hq // wl.Hkv)
+    return oatt.compensated_attention(wl.q[b, hq], wl.k[b, kvh], wl.v[b, kvh], wl.labels, wl.labels,
+                                      keep_np[b, hm], wl.scale, compensate)
+
+
+@pytest.mark.parametrize(
+    "name,kw,compensate",
+    [
+        ("ragged_bf16_d128", dict(S=1500, D=128, dtype="bf16"), True),
+        ("ragged_bf16_d128_harddrop", dict(S=1500, D=128, dtype="bf16"), False),
+        ("ragged_f32_d64", dict(S=900, D=64, dtype="f32"), True),
+        ("ragged_f32_d128", dict(S=700, D=128, dtype="f32"), True),
+        ("ragged_bf16_d64", dict(S=1100, D=64, dtype="bf16"), True),
+        ("gqa_bf16", dict(S=1200, D=128, dtype="bf16", Hq=4, Hkv=2, B=2), True),
+        ("big_clusters", dict(S=1000, D=128, dtype="bf16", cluster_sizes=[300, 5, 129, 64, 1, 257, 244]), True),
+        ("all_kept", dict(S=1000, D=128, dtype="bf16", mask="all"), True),
+        ("nothing_kept_compensated", dict(S=1000, D=128, dtype="bf16", mask="none"), True),
+        ("student_t_values", dict(S=1300, D=128, dtype="bf16", v_kind="t3"), True),
+    ],
+)
+def test_sparse_attention(bsa, name, kw, compensate):
+    say(f"attention {name}")
+    wl = make_custom(100 + len(name), **kw)
+    out, lse = run_attention(bsa, wl, wl.mask, compensate, lse=True)
+    got = host(out)
+    got_lse = lse.cpu().numpy()
+    for b in range(wl.B):
+        for hq in range(wl.Hq):
+            ref, ref_lse = oracle_attention(wl, wl.mask, compensate, b, hq)
+            check_output(got[b, hq], ref, wl.dtype, f"{name} b{b} h{hq}")
+            fin = np.isfinite(ref_lse)
+            assert np.array_equal(np.isfinite(got_lse[b, hq]), fin)
+            # bf16: centroids enter the MFMA rounded to bf16, which moves centroid logits by
+            # up to ~1e-3; float32 keeps them exact to rounding.
+            lse_tol = 1e-4 if wl.dtype == "f32" else 1e-2
+            assert np.max(np.abs(got_lse[b, hq][fin] - ref_lse[fin])) < lse_tol
+
+
+def test_hard_drop_empty_rows_are_zero(bsa):
+    say("attention empty rows")
+    wl = make_custom(7, S=600, D=128, dtype="bf16", mask="random", p_keep=0.2)
+    keep = wl.mask.copy()
+    keep[0, 0, 0] = 0  # cluster 0 keeps nothing
+    out, lse = run_attention(bsa, wl, keep, compensate=False, lse=True)
+    rows = wl.labels == 0
+    assert np.all(host(out)[0, 0][rows] == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()[0, 0][rows]))
+    ref, _ = oracle_attention(wl, keep, False, 0, 0)
+    check_output(host(out)[0, 0], ref, "bf16", "empty rows")
+
+
+def test_identical_keys_compensation_equals_dense(bsa):
+    say("attention identical keys")
+    wl = make_custom(8, S=1024, D=128, dtype="f32", noise=0.0, mask="random", p_keep=0.2)
+    # keys identical within each cluster: compensation is exact
+    for c in range(wl.C):
+        rows = wl.labels == c
+        wl.k[0, 0][rows] = wl.k[0, 0][rows][0]
+    out = host(run_attention(bsa, wl, wl.mask, compensate=True))
+    dense = oatt.dense_attention_rows(wl.q[0, 0], wl.k[0, 0], wl.v[0, 0], wl.scale)
+    check_output(out[0, 0], dense, "f32", "identical keys vs dense")
+
+
+# ------------------------------------------------------------------ probes, fit, apply
+
+
+@pytest.mark.parametrize("dtype,D,M,compensate,Hkv", [("bf16", 128, 64, True, 1), ("f32", 64, 20, True, 2),
+                                                      ("bf16", 128, 130, False, 1), ("bf16", 64, 33, True, 2)])
+def test_probe_attention(bsa, dtype, D, M, compensate, Hkv):
+    say(f"probe rows {dtype} D={D} M={M} compensate={compensate}")
+    wl = make_custom(31 + M, B=1, Hq=2, Hkv=Hkv, S=5000, D=D, dtype=dtype, p_keep=0.25)
+    idx = np.random.default_rng(0).choice(wl.S, size=M, replace=False).astype(np.int32)
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, wl.C)
+    q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
+    mask = bsa.mask_from_keep(torch.from_numpy(wl.mask).cuda())
+    kbar = vbar = None
+    if compensate:
+        kbar, vbar = bsa.centroids(k, v, lay)
+    od, os_ = bsa.probe_attention(q, k, v, torch.from_numpy(idx).cuda(), wl.scale, lab, lab, lay, mask, kbar, vbar)
+    od, os_ = host(od), host(os_)
+    for h in range(2):
+        kvh = h // (2 // Hkv)
+        ref = oatt.dense_attention_rows(wl.q[0, h][idx], wl.k[0, kvh], wl.v[0, kvh], wl.scale)
+        check_output(od[0, h], ref, dtype, f"dense probe rows h{h}")
+        ref_s, _ = oatt.compensated_attention(wl.q[0, h], wl.k[0, kvh], wl.v[0, kvh], wl.labels, wl.labels,
+                                              wl.mask[0, kvh if Hkv > 1 else 0], wl.scale, compensate, rows=idx)
+        check_output(os_[0, h], ref_s, dtype, f"sparse probe rows h{h}")
+
+
+def fit_inputs(M, D, H=3, seed=0):
+    rng = np.random.default_rng(seed)
+    xs = rng.standard_normal((1, H, M, D)) * rng.uniform(0.3, 2.0, size=D)
+    mix = rng.standard_normal((D, D)) * 0.05
+    xd = xs + xs @ mix + 0.05 * rng.standard_normal((1, H, M, D)) + 0.1
+    _, w = orep.select_probe_rows(np.arange(50 * 12) // 50, 12, M)
+    return xs.astype(np.float32), xd.astype(np.float32), w.astype(np.float32)
+
+
+@pytest.mark.parametrize("D,M,rank", [(128, 64, 16), (64, 16, 4), (128, 2, 16), (128, 33, 16), (64, 64, 16)])
+def test_probe_fit(bsa, D, M, rank):
+    say(f"probe fit D={D} M={M} r={rank}")
+    xs, xd, w = fit_inputs(M, D, seed=M + D)
+    A, c = bsa.probe_fit(torch.from_numpy(xs).cuda(), torch.from_numpy(xd).cuda(), torch.from_numpy(w).cuda(),
+                         0.1, rank)
+    A_h, c_h = host(A), host(c)
+    for h in range(xs.shape[1]):
+        fit = orep.ridge_fit(xs[0, h], xd[0, h], w, 0.1, rank)
+        scale = np.max(np.abs(fit["A"])) + 1e-30
+        assert np.max(np.abs(A_h[0, h] - fit["A"])) <= 1e-4 * scale + 1e-6, np.max(np.abs(A_h[0, h] - fit["A"]))
+        assert np.max(np.abs(c_h[0, h] - fit["c"])) <= 1e-4 * (np.max(np.abs(fit["c"])) + scale) + 1e-6
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_probe_apply(bsa, dtype, D):
+    say(f"probe apply {dtype} D={D}")
+    rng = np.random.default_rng(D)
+    B, H, S = 1, 2, 700
+    o = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    A = (rng.standard_normal((B, H, D, D)) * 0.3).astype(np.float32)
+    c = rng.standard_normal((B, H, D)).astype(np.float32)
+    o_t = dev(o, dtype)
+    before = host(o_t)
+    bsa.probe_apply(o_t, torch.from_numpy(A).cuda(), torch.from_numpy(c).cuda())
+    after = host(o_t)
+    for h in range(H):
+        check_output(after[0, h], orep.apply_correction(before[0, h], A[0, h], c[0, h]), dtype, f"apply h{h}")
+
+
+@pytest.mark.parametrize("dtype,D,compensate", [("bf16", 128, True), ("f32", 64, True), ("bf16", 64, False)])
+def test_attention_with_correction_epilogue(bsa, dtype, D, compensate):
+    """The correction applied inside the attention epilogue equals the oracle's
+    o + o A + c on the exact attention output (one rounding, at the end)."""
+    say(f"attention epilogue {dtype} D={D}")
+    wl = make_custom(77, B=1, Hq=2, Hkv=1, S=1200, D=D, dtype=dtype)
+    rng = np.random.default_rng(3)
+    A = (rng.standard_normal((1, 2, D, D)) * 0.5).astype(np.float32)
+    c = (rng.standard_normal((1, 2, D)) * 0.1).astype(np.float32)
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, wl.C)
+    q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
+    mask = bsa.mask_from_keep(torch.from_numpy(wl.mask).cuda())
+    kbar = vbar = None
+    if compensate:
+        kbar, vbar = bsa.centroids(k, v, lay)
+    out = host(bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, kbar, vbar, wl.scale,
+                                                  A=torch.from_numpy(A).cuda(), c=torch.from_numpy(c).cuda()))
+    for h in range(2):
+        ref, _ = oracle_attention(wl, wl.mask, compensate, 0, h)
+        check_output(out[0, h], orep.apply_correction(ref, A[0, h], c[0, h]), dtype, f"epilogue h{h}")
