@@ -155,6 +155,7 @@ template <typename T, int D, typename RowFn>
 __device__ __forceinline__ void load_kv_tile_fallback(T* Vt, const T* __restrict__ Vh, int nvalid, RowFn row_of) {
   using C = Cfg<T, D>;
   constexpr int kBlocks = (kNK / 4) * C::CPR;
+#pragma unroll 1
   for (int idx = threadIdx.x; idx < kBlocks; idx += kThreads) {
     const int kq = idx / C::CPR, ch = idx % C::CPR;
     uint4 r[4];
@@ -184,6 +185,7 @@ __device__ __forceinline__ void load_centroid_tile(T* Ks, T* Vt, float* bias, in
   using C = Cfg<T, D>;
   const int t = threadIdx.x;
   constexpr int kGroups = D / 8;  // 8 floats per item
+#pragma unroll 1
   for (int idx = t; idx < kNK * kGroups; idx += kThreads) {
     const int key = idx / kGroups, g = idx % kGroups;
     const int c = c0 + key;
@@ -201,6 +203,7 @@ __device__ __forceinline__ void load_centroid_tile(T* Ks, T* Vt, float* bias, in
     for (int i = 0; i < 8; ++i) Ks[key * C::KROW + g * 8 + i] = from_f32<T>(x[i]);
   }
   float vmax = 0.0f;
+#pragma unroll 2
   for (int idx = t; idx < kNK * D; idx += kThreads) {
     const int key = idx % kNK, d = idx / kNK;
     const int c = c0 + key;
@@ -228,6 +231,7 @@ __device__ __forceinline__ void load_centroid_tile(T* Ks, T* Vt, float* bias, in
 template <typename T, int D>
 __device__ __forceinline__ void load_centroid_fallback(T* Vt, const float* __restrict__ Vb, int c0, int Ck) {
   using C = Cfg<T, D>;
+#pragma unroll 2
   for (int idx = threadIdx.x; idx < kNK * D; idx += kThreads) {
     const int key = idx % kNK, d = idx / kNK;
     const int c = c0 + key;
@@ -243,11 +247,6 @@ struct NoBias {
   static constexpr bool kNone = true;
   __device__ float operator()(int) const { return 0.0f; }
 };
-struct TailMask {  // keys at or past `nvalid` do not exist
-  static constexpr bool kNone = false;
-  int nvalid;
-  __device__ float operator()(int key) const { return key < nvalid ? 0.0f : -INFINITY; }
-};
 struct KeyBias {  // one bias per key, from LDS (centroid columns: log2 n_c or -inf)
   static constexpr bool kNone = false;
   const float* bias;
@@ -255,10 +254,11 @@ struct KeyBias {  // one bias per key, from LDS (centroid columns: log2 n_c or -
 };
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// qf: this wave's Q fragments; c2 = scale * log2(e).
-template <typename T, int D, typename Bias>
+// qf: this wave's Q fragments; c2 = scale * log2(e); keys at or past `nvalid` do not exist.
+// PV16: bfloat16 inputs take the P V product in float16 (the tile's V^T is float16 in LDS).
+template <typename T, int D, bool PV16, typename Bias>
 __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
-                                          const Bias& bias, bool pv_f16) {
+                                          const Bias& bias, int nvalid) {
   using C = Cfg<T, D>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
@@ -271,23 +271,34 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
     s0 = mma(a0, qf[kk], s0);
     s1 = mma(a1, qf[kk], s1);
   }
-  // Logits in log2 units.  Key of s_mt[j]: mt*32 + 8*(j/4) + 4*h + j%4.
+  // Logits in log2 units.  Key of s_mt[j]: mt*32 + 8*(j/4) + 4*h + j%4.  Without a bias the
+  // max is taken on the raw products (c2 > 0) and the scale folds into the exponent's FMA.
   float x[32];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    x[j] = s0[j] * c2;
-    x[16 + j] = s1[j] * c2;
+    x[j] = s0[j];
+    x[16 + j] = s1[j];
   }
+  float xs = c2;  // scale still to apply to x
   if constexpr (!Bias::kNone) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[mt * 16 + j] += bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
+      for (int j = 0; j < 16; ++j)
+        x[mt * 16 + j] = x[mt * 16 + j] * c2 + bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
+    xs = 1.0f;
   }
-  float mx = x[0];
+  if (nvalid < kNK) {  // ragged last tile of a cluster (uniform branch)
 #pragma unroll
-  for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
-  mx = fmaxf(mx, swap_halves(mx));
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (mt * 32 + 8 * (j / 4) + 4 * h + (j % 4) >= nvalid) x[mt * 16 + j] = -INFINITY;
+  }
+  float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+  for (int j = 2; j < 32; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+  mx = fmaxf(mx, swap_halves(mx)) * xs;
   // Raise the running max only when a row exceeds it by the slack (wave-uniform branch).
   if (__ballot(mx > st.m + kRescaleSlack) != 0) {
     const float m_new = fmaxf(st.m, mx);
@@ -303,14 +314,13 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
   float lsum = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    x[j] = fast_exp2(x[j] - m_use);
+    x[j] = fast_exp2(__builtin_fmaf(x[j], xs, -m_use));
     lsum += x[j];
   }
   st.l += lsum;
   // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
   // ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
-  // bfloat16 inputs use float16 P and V^T when the tile allows it (see load_kv_tile).
-  if (sizeof(T) == 2 && pv_f16) {
+  if constexpr (sizeof(T) == 2 && PV16) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       Frag16 pb;
@@ -389,13 +399,29 @@ __device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __
   if constexpr (sizeof(T) == 2) {
     bf16_t* AtH = reinterpret_cast<bf16_t*>(smem);
     bf16_t* AtL = AtH + D * ROWA;
-    for (int e = threadIdx.x; e < D * D; e += kThreads) {
-      const int i = e / D, j = e % D;
-      const float a = Ah[e];
-      const __bf16 hi = static_cast<__bf16>(a);
-      const __bf16 lo = static_cast<__bf16>(a - static_cast<float>(hi));
-      AtH[j * ROWA + i].bits = __builtin_bit_cast(uint16_t, hi);
-      AtL[j * ROWA + i].bits = __builtin_bit_cast(uint16_t, lo);
+    // 4 x 4 blocks: four coalesced float4 row loads, transposed in registers, written as
+    // 8-byte runs of A^T rows (high and low bfloat16 parts).
+    constexpr int kBlk = (D / 4) * (D / 4);
+#pragma unroll 1
+    for (int blk = threadIdx.x; blk < kBlk; blk += kThreads) {
+      const int i0 = (blk / (D / 4)) * 4, j0 = (blk % (D / 4)) * 4;
+      f32x4 rowv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rowv[k] = *reinterpret_cast<const f32x4*>(Ah + (i0 + k) * D + j0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const __bf16 hb = static_cast<__bf16>(rowv[k][jj]);
+          hi[k] = static_cast<float>(hb);
+          lo[k] = rowv[k][jj] - hi[k];
+        }
+        *reinterpret_cast<uint2*>(AtH + (j0 + jj) * ROWA + i0) =
+            make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+        *reinterpret_cast<uint2*>(AtL + (j0 + jj) * ROWA + i0) =
+            make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+      }
     }
     __syncthreads();
     Frag<bf16_t> oh[D / 16], ol[D / 16];
@@ -425,6 +451,7 @@ __device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __
     }
   } else {
     float* At = reinterpret_cast<float*>(smem);
+#pragma unroll 2
     for (int e = threadIdx.x; e < D * D; e += kThreads) At[(e % D) * ROWA + e / D] = Ah[e];
     __syncthreads();
     Frag<float> of[D / 16];
@@ -463,8 +490,136 @@ constexpr int attn_lds_bytes() {
 
 // ----------------------------------------------------------------- sparse attention
 
+// One thread's share of a 64-key tile held in registers between its global loads and its
+// LDS stores: NB blocks of 4 keys x 16 bytes of K and of V.  The 4 keys of a block share
+// their gathered row indices.
+template <typename T, int D>
+struct KVRegs {
+  using C = Cfg<T, D>;
+  static constexpr int kBlocks = (kNK / 4) * C::CPR;
+  static constexpr int NB = (kBlocks + kThreads - 1) / kThreads;
+  uint4 k[NB][4];
+  uint4 v[NB][4];
+};
+
+// Walks the kept key clusters of a mask row as a sequence of <= 64-key tiles.
+struct TileCursor {
+  int it;  // position in the kept list
+  int kt;  // first cluster-major key position of the tile
+  int hi;  // end of the current cluster
+};
+__device__ __forceinline__ bool cursor_next(TileCursor& c, const int16_t* __restrict__ list, int cnt,
+                                            const int32_t* __restrict__ k_off, int Ck) {
+  c.kt += kNK;
+  while (c.kt >= c.hi) {
+    ++c.it;
+    if (c.it >= cnt) return false;
+    const int cl = list[c.it];
+    if (cl < 0 || cl >= Ck) {
+      c.kt = 0;
+      c.hi = 0;
+      continue;
+    }
+    c.kt = k_off[cl];
+    c.hi = k_off[cl + 1];
+  }
+  return true;
+}
+
+// Gathered row indices of one thread's keys in a tile (loaded one tile ahead of the rows).
+template <typename T, int D>
+struct TileRows {
+  int tok[KVRegs<T, D>::NB][4];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void prefetch_rows(TileRows<T, D>& tr, const int32_t* __restrict__ k_perm, int kt,
+                                              int nvalid) {
+  using C = Cfg<T, D>;
+  // Keys past the tile end re-read its last row (zeroed when stored): no branches, so the
+  // loads issue back to back.
+#pragma unroll
+  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
+    const int idx = min(static_cast<int>(threadIdx.x) + bi * kThreads, KVRegs<T, D>::kBlocks - 1);
+    const int kq = idx / C::CPR;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tr.tok[bi][k] = k_perm[kt + min(kq * 4 + k, nvalid - 1)];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void prefetch_tile(KVRegs<T, D>& r, const TileRows<T, D>& tr, const T* __restrict__ Kh,
+                                              const T* __restrict__ Vh) {
+  using C = Cfg<T, D>;
+#pragma unroll
+  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
+    const int idx = min(static_cast<int>(threadIdx.x) + bi * kThreads, KVRegs<T, D>::kBlocks - 1);
+    const int ch = idx % C::CPR;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t row = static_cast<size_t>(tr.tok[bi][k]) * D + ch * C::EPC;
+      r.k[bi][k] = *reinterpret_cast<const uint4*>(Kh + row);
+      r.v[bi][k] = *reinterpret_cast<const uint4*>(Vh + row);
+    }
+  }
+}
+
+// Registers -> LDS: K rows as they are, V transposed (float16 for bfloat16 inputs, with the
+// fits-float16 flags published for the barrier that follows).
+template <typename T, int D>
+__device__ __forceinline__ void store_tile(KVRegs<T, D>& r, T* Ks, T* Vt, int* flags, int nvalid) {
+  using C = Cfg<T, D>;
+  uint32_t emax = 0;
+#pragma unroll
+  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
+    const int idx = threadIdx.x + bi * kThreads;
+    if (idx >= KVRegs<T, D>::kBlocks) break;
+    const int kq = idx / C::CPR, ch = idx % C::CPR;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (kq * 4 + k >= nvalid) {
+        r.k[bi][k] = make_uint4(0, 0, 0, 0);
+        r.v[bi][k] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(Ks + (kq * 4 + k) * C::KROW + ch * C::EPC) = r.k[bi][k];
+    const uint32_t w[4][4] = {{r.v[bi][0].x, r.v[bi][0].y, r.v[bi][0].z, r.v[bi][0].w},
+                              {r.v[bi][1].x, r.v[bi][1].y, r.v[bi][1].z, r.v[bi][1].w},
+                              {r.v[bi][2].x, r.v[bi][2].y, r.v[bi][2].z, r.v[bi][2].w},
+                              {r.v[bi][3].x, r.v[bi][3].y, r.v[bi][3].z, r.v[bi][3].w}};
+    const int d0 = ch * C::EPC;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) emax = max(emax, max((w[k][p] >> 7) & 0xffu, (w[k][p] >> 23) & 0xffu));
+      store_vt_f16(Vt, C::VROW, d0, kq * 4, w);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<uint4*>(Vt + (d0 + p) * C::VROW + kq * 4) = make_uint4(w[0][p], w[1][p], w[2][p], w[3][p]);
+    }
+  }
+  if constexpr (sizeof(T) == 2) publish_tile_flags(flags, emax >= 143u, emax >= 119u);
+}
+
+template <typename T, int D, bool REPAIR>
+struct AttnLds {
+  using C = Cfg<T, D>;
+  static constexpr int BUF_BYTES = C::KV_BYTES;  // one K + V^T tile
+  static constexpr int TILES = 2 * BUF_BYTES;
+  static constexpr int REP = REPAIR ? repair_lds_bytes<T, D>() : 0;
+  static constexpr int MAIN0 = TILES > C::Z_BYTES ? TILES : C::Z_BYTES;
+  static constexpr int MAIN = MAIN0 > REP ? MAIN0 : REP;
+  static constexpr int BIAS = MAIN;                      // float[kNK]
+  static constexpr int FLAGS = BIAS + kNK * 4;           // int[2 buffers][8]
+  static constexpr int TOTAL = FLAGS + 2 * kFlagBytes;
+};
+
+// One workgroup per CU with the whole register file per wave (launch bound 1): the loads of
+// the next tile, the LDS fragment reads and both MFMA chains stay in flight without spills.
 template <typename T, int D, bool COMP, bool REPAIR>
-__global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2, const int32_t* __restrict__ q_perm,
     const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_perm,
@@ -473,13 +628,12 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
     const float* __restrict__ Kbar, const float* __restrict__ Vbar, const float* __restrict__ Acorr,
     const float* __restrict__ ccorr) {
   using C = Cfg<T, D>;
-  constexpr int LDS = attn_lds_bytes<T, D, REPAIR>();
+  using L = AttnLds<T, D, REPAIR>;
   extern __shared__ __align__(16) unsigned char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vt = Ks + C::K_ELEMS;
+  T* Ks0 = reinterpret_cast<T*>(smem);
   T* Z = reinterpret_cast<T*>(smem);
-  float* bias = reinterpret_cast<float*>(smem + (LDS - kNK * 4 - kFlagBytes));
-  int* flags = reinterpret_cast<int*>(smem + (LDS - kFlagBytes));
+  float* bias = reinterpret_cast<float*>(smem + L::BIAS);
+  int* flags0 = reinterpret_cast<int*>(smem + L::FLAGS);
 
   const int G = Hq / Hkv;
   int unit, a, g;
@@ -509,44 +663,108 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
     const int qtok = q_perm[rt + (my < nrows ? my : 0)];
     Frag<T> qf[C::KK];
     load_q_frags<T, D>(qf, Qh + static_cast<size_t>(qtok) * D);
+    // Wait for Q here: otherwise the loop's wait counters, merged over the loop entry, make
+    // every tile wait for its own prefetch before the first MFMA.
+    __builtin_amdgcn_s_waitcnt(0);
     RowState<D> st;
     init_state<D>(st);
 
     if constexpr (COMP) {
+      // Centroid columns: one tile per 64 key clusters, bias log2 n_c where skipped.
+      T* Ks = Ks0;
+      T* Vt = Ks0 + C::K_ELEMS;
       for (int c0 = 0; c0 < Ck; c0 += kNK) {
-        load_centroid_tile<T, D>(Ks, Vt, bias, flags, Kb, Vb, c0, Ck, k_off, keep_row);
+        load_centroid_tile<T, D>(Ks, Vt, bias, flags0, Kb, Vb, c0, Ck, k_off, keep_row);
         __syncthreads();
-        const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
-        if (sizeof(T) == 2 && !f16) {
+        const bool f16 = sizeof(T) != 2 || tile_fits_f16(flags0);
+        if (!f16) {
           load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
           __syncthreads();
         }
-        const bool any = __ballot(bias[lane] > -INFINITY) != 0;
-        if (any) tile_step<T, D>(Ks, Vt, qf, st, c2, KeyBias{bias}, f16);
+        if (__ballot(bias[lane] > -INFINITY) != 0) {
+          if (f16)
+            tile_step<T, D, true>(Ks, Vt, qf, st, c2, KeyBias{bias}, kNK);
+          else
+            tile_step<T, D, false>(Ks, Vt, qf, st, c2, KeyBias{bias}, kNK);
+        }
         __syncthreads();
       }
     }
-    for (int it = 0; it < cnt; ++it) {
-      const int c = list[it];
-      if (c < 0 || c >= Ck) continue;
-      const int k_lo = k_off[c], k_hi = k_off[c + 1];
-      for (int kt = k_lo; kt < k_hi; kt += kNK) {
-        const int nvalid = min(kNK, k_hi - kt);
-        auto row_of = [&](int key) { return static_cast<size_t>(k_perm[kt + key]) * D; };
-        load_kv_tile<T, D>(Ks, Vt, flags, Kh, Vh, nvalid, row_of);
-        __syncthreads();
-        const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
-        if (sizeof(T) == 2 && !f16) {
-          load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
+
+    // Kept key tiles, software pipelined: while tile i is computed from LDS, the rows of
+    // tile i+1 are in flight into registers and the row indices of tile i+2 are in flight
+    // too; two LDS buffers, one barrier per tile.
+    TileCursor cur{-1, 0, 0};
+    bool have = cursor_next(cur, list, cnt, k_off, Ck);
+    KVRegs<T, D> regs;
+    TileRows<T, D> rows_next;
+    TileCursor nxt = cur;
+    bool have_next = false;
+    if (have) {
+      TileRows<T, D> rows0;
+      prefetch_rows<T, D>(rows0, k_perm, cur.kt, min(kNK, cur.hi - cur.kt));
+      prefetch_tile<T, D>(regs, rows0, Kh, Vh);
+      have_next = cursor_next(nxt, list, cnt, k_off, Ck);
+      if (have_next) prefetch_rows<T, D>(rows_next, k_perm, nxt.kt, min(kNK, nxt.hi - nxt.kt));
+      store_tile<T, D>(regs, Ks0, Ks0 + C::K_ELEMS, flags0, min(kNK, cur.hi - cur.kt));
+    }
+    __syncthreads();
+    int buf = 0;
+    bool deferred = false;
+    while (have) {
+      // Issue the rows of tile i+1 (indices arrived during the previous tile) and the
+      // indices of tile i+2.
+      TileCursor nn = nxt;
+      bool have_nn = false;
+      if (have_next) {
+        prefetch_tile<T, D>(regs, rows_next, Kh, Vh);
+        have_nn = cursor_next(nn, list, cnt, k_off, Ck);
+        if (have_nn) prefetch_rows<T, D>(rows_next, k_perm, nn.kt, min(kNK, nn.hi - nn.kt));
+      }
+      T* Ks = reinterpret_cast<T*>(smem + buf * L::BUF_BYTES);
+      T* Vt = Ks + C::K_ELEMS;
+      int* flags = flags0 + buf * (kFlagBytes / 4);
+      const int nvalid = min(kNK, cur.hi - cur.kt);
+      // Tiles whose values do not fit float16 are left to the second pass below.
+      if (sizeof(T) != 2 || tile_fits_f16(flags))
+        tile_step<T, D, true>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
+      else
+        deferred = true;
+      if (have_next) {
+        T* Kn = reinterpret_cast<T*>(smem + (buf ^ 1) * L::BUF_BYTES);
+        store_tile<T, D>(regs, Kn, Kn + C::K_ELEMS, flags0 + (buf ^ 1) * (kFlagBytes / 4),
+                         min(kNK, nxt.hi - nxt.kt));
+      }
+      __syncthreads();
+      cur = nxt;
+      have = have_next;
+      nxt = nn;
+      have_next = have_nn;
+      buf ^= 1;
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (deferred) {
+        // Second pass (normally empty): the tiles the first pass skipped, with a bfloat16
+        // P V product.  The same range test picks exactly those tiles again.
+        T* Ks = Ks0;
+        T* Vt = Ks0 + C::K_ELEMS;
+        TileCursor c2c{-1, 0, 0};
+        while (cursor_next(c2c, list, cnt, k_off, Ck)) {
+          const int nvalid = min(kNK, c2c.hi - c2c.kt);
+          const int kt = c2c.kt;
+          auto row_of = [&](int key) { return static_cast<size_t>(k_perm[kt + key]) * D; };
+          load_kv_tile<T, D>(Ks, Vt, flags0, Kh, Vh, nvalid, row_of);
+          __syncthreads();
+          if (!tile_fits_f16(flags0)) {
+            load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
+            __syncthreads();
+            tile_step<T, D, false>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
+          }
           __syncthreads();
         }
-        if (nvalid == kNK)
-          tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, f16);
-        else
-          tile_step<T, D>(Ks, Vt, qf, st, c2, TailMask{nvalid}, f16);
-        __syncthreads();
       }
     }
+
     const float l_tot = st.l + swap_halves(st.l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
@@ -567,6 +785,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
       lse[bhq * S + qtok] = v;
     }
     __syncthreads();
+#pragma unroll 2
     for (int idx = threadIdx.x; idx < kRowsWG * C::CPR; idx += kThreads) {
       const int row = idx / C::CPR, ch = idx % C::CPR;
       if (row < nrows) {
@@ -683,18 +902,21 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
         }
       }
       __syncthreads();
-      const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
-      if (sizeof(T) == 2 && !f16) {
+      const bool f16 = sizeof(T) != 2 || tile_fits_f16(flags);
+      if (!f16) {
         load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
         __syncthreads();
       }
       if constexpr (SPARSE) {
-        tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, f16);
-      } else {
-        if (nvalid == kNK)
-          tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, f16);
+        if (f16)
+          tile_step<T, D, true>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid);
         else
-          tile_step<T, D>(Ks, Vt, qf, st, c2, TailMask{nvalid}, f16);
+          tile_step<T, D, false>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid);
+      } else {
+        if (f16)
+          tile_step<T, D, true>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
+        else
+          tile_step<T, D, false>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
       }
       __syncthreads();
     }
@@ -706,12 +928,15 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
       // With an all-zero keep row the per-tile bias is log2 n_c for every non-empty cluster.
       load_centroid_tile<T, D>(Ks, Vt, bias, flags, Kb, Vb, c0, Ck, k_off, nullptr);
       __syncthreads();
-      const bool f16 = sizeof(T) == 2 && tile_fits_f16(flags);
-      if (sizeof(T) == 2 && !f16) {
+      const bool f16 = sizeof(T) != 2 || tile_fits_f16(flags);
+      if (!f16) {
         load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
         __syncthreads();
       }
-      tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, f16);
+      if (f16)
+        tile_step<T, D, true>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK);
+      else
+        tile_step<T, D, false>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK);
       __syncthreads();
     }
   }
@@ -761,7 +986,7 @@ void launch_sparse_variant(dim3 grid, hipStream_t stream, const void* Q, const v
                            const int32_t* q_off, int Cq, const int32_t* k_perm, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
                            const float* Kbar, const float* Vbar, const float* A, const float* c) {
-  constexpr int LDS = attn_lds_bytes<T, D, REPAIR>();
+  constexpr int LDS = AttnLds<T, D, REPAIR>::TOTAL;
   auto kern = sparse_attn_kernel<T, D, COMP, REPAIR>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<const T*>(K),

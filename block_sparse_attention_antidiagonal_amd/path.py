@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import Optional
+from typing import Callable, Optional
 
 import numpy as np
 import torch
@@ -86,31 +86,43 @@ class SparseAttentionPath:
             self.probe_idx = torch.as_tensor(idx).to(self.device)
             self.probe_w = torch.as_tensor(w).to(self.device)
 
-    def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False) -> PathResult:
+    def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False,
+                 mark: Optional[Callable[[str], None]] = None) -> PathResult:
         """Run the path.  With probes the fit runs before the attention, whose epilogue
         applies the correction to every row; keep_sparse additionally returns the output
-        without correction (one more attention launch, for inspection)."""
+        without correction (one more attention launch, for inspection).  ``mark(stage)`` is
+        called after each stage's launches (for stream-ordered timing events)."""
         cfg = self.cfg
+        mark = mark or (lambda name: None)
+        mark("start")
         layout = api.cluster_layout(self.labels, cfg.C)
+        mark("layout")
         kbar = vbar = None
         if cfg.compensate:
             kbar, vbar = api.centroids(k, v, layout)
+            mark("centroids")
         scores = None
         if cfg.mask_mode == "scored":
             scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
                                                    cfg.score_scale or 1.0 / math.sqrt(cfg.D), cfg.pool_gqa)
+            mark("scores")
             mask = api.top_p_block_mask(scores, self.tau)
+            mark("top_p")
         else:
             mask = api.mask_from_keep(self.given_keep)
+            mark("mask_lists")
         res = PathResult(out=None, layout=layout, mask=mask, scores=scores, kbar=kbar, vbar=vbar)
         A = c = None
         if cfg.probes:
             od, os_ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale, self.labels, self.labels, layout, mask,
                                           kbar, vbar)
+            mark("probe_rows")
             A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
+            mark("fit")
             res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
             if keep_sparse:
                 res.out_sparse = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar,
                                                                     cfg.scale)
         res.out = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar, cfg.scale, A=A, c=c)
+        mark("attention")
         return res
