@@ -13,10 +13,13 @@ _lib.load()
 from .api import (  # noqa: E402,F401
     BlockMask,
     ClusterLayout,
+    PackedKV,
     antidiagonal_block_scores,
+    block_sparse_attention,
     centroid_compensated_attention,
     centroids,
     cluster_layout,
+    kv_pack,
     mask_from_keep,
     probe_apply,
     probe_attention,

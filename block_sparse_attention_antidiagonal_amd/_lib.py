@@ -27,9 +27,12 @@ SIGNATURES = {
                             c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_top_p_mask": [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_mask_lists": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
-    "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
-                             c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
-                             c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_kv_pack_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_kv_pack": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                    c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_int,
+                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,

@@ -89,6 +89,40 @@ def centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout) -> Tuple[
     return kbar, vbar
 
 
+@dataclass
+class PackedKV:
+    """Keys and values in cluster-major 64-key tiles plus the centroid tiles (bsa_kv_pack).
+    ``buffer`` is opaque; it belongs to ``layout`` and the K/V shape it was packed from."""
+
+    buffer: torch.Tensor  # uint8
+    kbar: torch.Tensor  # float32 [B, Hkv, C, D]
+    vbar: torch.Tensor  # float32 [B, Hkv, C, D]
+    layout: ClusterLayout
+    B: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: torch.dtype
+
+
+def kv_pack(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout,
+            buffer: Optional[torch.Tensor] = None) -> PackedKV:
+    """Pack K/V into cluster tiles and compute the cluster means (bsa_kv_pack)."""
+    _check_cuda(k, v)
+    B, Hkv, S, D = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must match")
+    code = _dtype_code(k)
+    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C)
+    if buffer is None or buffer.numel() < nbytes:
+        buffer = _workspace(nbytes, k.device)
+    kbar = torch.empty(B, Hkv, layout.C, D, dtype=torch.float32, device=k.device)
+    vbar = torch.empty_like(kbar)
+    _lib.call("bsa_kv_pack", B, Hkv, S, D, code, _ptr(k), _ptr(v), _ptr(layout.perm), _ptr(layout.offsets),
+              layout.C, _ptr(kbar), _ptr(vbar), _ptr(buffer), buffer.numel(), _stream())
+    return PackedKV(buffer, kbar, vbar, layout, B, Hkv, S, D, k.dtype)
+
+
 def antidiagonal_block_scores(q: torch.Tensor, k: torch.Tensor, layout: Optional[ClusterLayout] = None,
                               block_size: int = 128, stride: int = 16, score_scale: Optional[float] = None,
                               pool_gqa: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -154,27 +188,38 @@ def mask_from_keep(keep: torch.Tensor) -> BlockMask:
     return BlockMask(keep, cnt, idx)
 
 
-def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: ClusterLayout, mask: BlockMask,
-                                   kbar: Optional[torch.Tensor] = None, vbar: Optional[torch.Tensor] = None,
-                                   scale: Optional[float] = None, return_lse: bool = False,
-                                   out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
-                                   c: Optional[torch.Tensor] = None):
-    """Block-sparse attention; compensated when kbar/vbar are given, hard drop otherwise;
-    with A, c every output row o becomes o + o A + c before rounding (bsa_sparse_attention)."""
-    _check_cuda(q, k, v, kbar, vbar, A, c)
+def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
+                           compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
+                           out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                           c: Optional[torch.Tensor] = None):
+    """Block-sparse attention over packed K/V; compensated by the skipped clusters'
+    centroids, or hard drop with compensate=False; with A, c every output row o becomes
+    o + o A + c before rounding (bsa_sparse_attention)."""
+    _check_cuda(q, A, c)
     B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
+        raise ValueError("q does not match the packed K/V")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if mask.keep.shape[0] != B or mask.keep.shape[2] != q_layout.C or mask.keep.shape[3] != k_layout.C:
+    Ck = kv.layout.C
+    if mask.keep.shape[0] != B or mask.keep.shape[2] != q_layout.C or mask.keep.shape[3] != Ck:
         raise ValueError("mask shape does not match batch / cluster counts")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device) if return_lse else None
-    _lib.call("bsa_sparse_attention", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), float(scale),
-              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(k_layout.perm), _ptr(k_layout.offsets),
-              k_layout.C, _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kbar), _ptr(vbar),
-              _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _stream())
+    _lib.call("bsa_sparse_attention", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
+              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
+              _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
+              int(bool(compensate)), _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _stream())
     return (o, lse) if return_lse else o
+
+
+def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: ClusterLayout, mask: BlockMask,
+                                   compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
+                                   out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                                   c: Optional[torch.Tensor] = None):
+    """kv_pack followed by block_sparse_attention, for callers holding plain K/V."""
+    kv = kv_pack(k, v, k_layout)
+    return block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out, A, c)
 
 
 def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = None,

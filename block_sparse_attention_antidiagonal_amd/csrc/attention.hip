@@ -18,6 +18,7 @@
 // every lane holds one query row's values: the row max/sum need one exchange between the
 // two 32-lane halves and the P tile feeds the second product without leaving registers.
 #include "common.hpp"
+#include "pack.hpp"
 
 namespace bsa {
 namespace {
@@ -244,21 +245,23 @@ __device__ __forceinline__ void load_centroid_fallback(T* Vt, const float* __res
 // Logit bias policies for one 64-key tile (values in log2 units, added to the scaled logits).
 // `key` is the tile-local key index, `lane` the caller's lane (its query row).
 struct NoBias {
-  static constexpr bool kNone = true;
+  __device__ bool active() const { return false; }
   __device__ float operator()(int) const { return 0.0f; }
 };
-struct KeyBias {  // one bias per key, from LDS (centroid columns: log2 n_c or -inf)
-  static constexpr bool kNone = false;
+struct KeyBias {  // one bias per key from LDS (centroid columns: log2 n_c or -inf); null = none
   const float* bias;
+  __device__ bool active() const { return bias != nullptr; }
   __device__ float operator()(int key) const { return bias[key]; }
 };
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // qf: this wave's Q fragments; c2 = scale * log2(e); keys at or past `nvalid` do not exist.
-// PV16: bfloat16 inputs take the P V product in float16 (the tile's V^T is float16 in LDS).
-template <typename T, int D, bool PV16, typename Bias>
+// pv16: for bfloat16 inputs the tile's V^T in LDS is float16 and P is rounded to float16
+// (else both are bfloat16).  Bias, nvalid and pv16 are uniform over the workgroup, so the
+// branches on them cost no divergence and the tile step is instantiated once per call site.
+template <typename T, int D, typename Bias>
 __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
-                                          const Bias& bias, int nvalid) {
+                                          const Bias& bias, int nvalid, bool pv16) {
   using C = Cfg<T, D>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
@@ -280,7 +283,7 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
     x[16 + j] = s1[j];
   }
   float xs = c2;  // scale still to apply to x
-  if constexpr (!Bias::kNone) {
+  if (bias.active()) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -320,7 +323,7 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
   st.l += lsum;
   // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
   // ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
-  if constexpr (sizeof(T) == 2 && PV16) {
+  if (sizeof(T) == 2 && pv16) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       Frag16 pb;
@@ -490,117 +493,109 @@ constexpr int attn_lds_bytes() {
 
 // ----------------------------------------------------------------- sparse attention
 
-// One thread's share of a 64-key tile held in registers between its global loads and its
-// LDS stores: NB blocks of 4 keys x 16 bytes of K and of V.  The 4 keys of a block share
-// their gathered row indices.
+// One thread's share of a packed tile between its global loads and its LDS stores: NK
+// 16-byte chunks of the K tile and NV of the V^T tile.
 template <typename T, int D>
-struct KVRegs {
-  using C = Cfg<T, D>;
-  static constexpr int kBlocks = (kNK / 4) * C::CPR;
-  static constexpr int NB = (kBlocks + kThreads - 1) / kThreads;
-  uint4 k[NB][4];
-  uint4 v[NB][4];
-};
-
-// Walks the kept key clusters of a mask row as a sequence of <= 64-key tiles.
-struct TileCursor {
-  int it;  // position in the kept list
-  int kt;  // first cluster-major key position of the tile
-  int hi;  // end of the current cluster
-};
-__device__ __forceinline__ bool cursor_next(TileCursor& c, const int16_t* __restrict__ list, int cnt,
-                                            const int32_t* __restrict__ k_off, int Ck) {
-  c.kt += kNK;
-  while (c.kt >= c.hi) {
-    ++c.it;
-    if (c.it >= cnt) return false;
-    const int cl = list[c.it];
-    if (cl < 0 || cl >= Ck) {
-      c.kt = 0;
-      c.hi = 0;
-      continue;
-    }
-    c.kt = k_off[cl];
-    c.hi = k_off[cl + 1];
-  }
-  return true;
-}
-
-// Gathered row indices of one thread's keys in a tile (loaded one tile ahead of the rows).
-template <typename T, int D>
-struct TileRows {
-  int tok[KVRegs<T, D>::NB][4];
+struct TileRegs {
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  static constexpr int K_CHUNKS = kNK * D / EPC;
+  static constexpr int V_EPC = sizeof(T) == 2 ? 8 : 4;  // V^T chunk: 8 x 16-bit or 4 x float32
+  static constexpr int V_CHUNKS = D * kNK / V_EPC;
+  static constexpr int NK = K_CHUNKS / kThreads;
+  static constexpr int NV = V_CHUNKS / kThreads;
+  static_assert(K_CHUNKS % kThreads == 0 && V_CHUNKS % kThreads == 0, "tile chunks must split evenly");
+  uint4 k[NK];
+  uint4 v[NV];
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void prefetch_rows(TileRows<T, D>& tr, const int32_t* __restrict__ k_perm, int kt,
-                                              int nvalid) {
-  using C = Cfg<T, D>;
-  // Keys past the tile end re-read its last row (zeroed when stored): no branches, so the
-  // loads issue back to back.
+__device__ __forceinline__ void prefetch_packed(TileRegs<T, D>& r, const T* __restrict__ ktile,
+                                                const void* __restrict__ vtile) {
+  using R = TileRegs<T, D>;
 #pragma unroll
-  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
-    const int idx = min(static_cast<int>(threadIdx.x) + bi * kThreads, KVRegs<T, D>::kBlocks - 1);
-    const int kq = idx / C::CPR;
+  for (int i = 0; i < R::NK; ++i)
+    r.k[i] = reinterpret_cast<const uint4*>(ktile)[threadIdx.x + i * kThreads];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) tr.tok[bi][k] = k_perm[kt + min(kq * 4 + k, nvalid - 1)];
-  }
+  for (int i = 0; i < R::NV; ++i)
+    r.v[i] = reinterpret_cast<const uint4*>(vtile)[threadIdx.x + i * kThreads];
 }
 
 template <typename T, int D>
-__device__ __forceinline__ void prefetch_tile(KVRegs<T, D>& r, const TileRows<T, D>& tr, const T* __restrict__ Kh,
-                                              const T* __restrict__ Vh) {
+__device__ __forceinline__ void store_packed(const TileRegs<T, D>& r, T* Ks, T* Vt) {
   using C = Cfg<T, D>;
+  using R = TileRegs<T, D>;
 #pragma unroll
-  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
-    const int idx = min(static_cast<int>(threadIdx.x) + bi * kThreads, KVRegs<T, D>::kBlocks - 1);
-    const int ch = idx % C::CPR;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const size_t row = static_cast<size_t>(tr.tok[bi][k]) * D + ch * C::EPC;
-      r.k[bi][k] = *reinterpret_cast<const uint4*>(Kh + row);
-      r.v[bi][k] = *reinterpret_cast<const uint4*>(Vh + row);
-    }
+  for (int i = 0; i < R::NK; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    const int row = q / C::CPR, ch = q % C::CPR;
+    *reinterpret_cast<uint4*>(Ks + row * C::KROW + ch * C::EPC) = r.k[i];
   }
-}
-
-// Registers -> LDS: K rows as they are, V transposed (float16 for bfloat16 inputs, with the
-// fits-float16 flags published for the barrier that follows).
-template <typename T, int D>
-__device__ __forceinline__ void store_tile(KVRegs<T, D>& r, T* Ks, T* Vt, int* flags, int nvalid) {
-  using C = Cfg<T, D>;
-  uint32_t emax = 0;
+  constexpr int VCPR = kNK / R::V_EPC;  // chunks per V^T row
 #pragma unroll
-  for (int bi = 0; bi < KVRegs<T, D>::NB; ++bi) {
-    const int idx = threadIdx.x + bi * kThreads;
-    if (idx >= KVRegs<T, D>::kBlocks) break;
-    const int kq = idx / C::CPR, ch = idx % C::CPR;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (kq * 4 + k >= nvalid) {
-        r.k[bi][k] = make_uint4(0, 0, 0, 0);
-        r.v[bi][k] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(Ks + (kq * 4 + k) * C::KROW + ch * C::EPC) = r.k[bi][k];
-    const uint32_t w[4][4] = {{r.v[bi][0].x, r.v[bi][0].y, r.v[bi][0].z, r.v[bi][0].w},
-                              {r.v[bi][1].x, r.v[bi][1].y, r.v[bi][1].z, r.v[bi][1].w},
-                              {r.v[bi][2].x, r.v[bi][2].y, r.v[bi][2].z, r.v[bi][2].w},
-                              {r.v[bi][3].x, r.v[bi][3].y, r.v[bi][3].z, r.v[bi][3].w}};
-    const int d0 = ch * C::EPC;
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) emax = max(emax, max((w[k][p] >> 7) & 0xffu, (w[k][p] >> 23) & 0xffu));
-      store_vt_f16(Vt, C::VROW, d0, kq * 4, w);
+  for (int i = 0; i < R::NV; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    const int d = q / VCPR, k0 = (q % VCPR) * R::V_EPC;
+    if constexpr (sizeof(T) == 2) {  // 136-byte rows: two 8-byte halves keep the alignment
+      uint2* dst = reinterpret_cast<uint2*>(Vt + d * C::VROW + k0);
+      dst[0] = make_uint2(r.v[i].x, r.v[i].y);
+      dst[1] = make_uint2(r.v[i].z, r.v[i].w);
     } else {
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        *reinterpret_cast<uint4*>(Vt + (d0 + p) * C::VROW + kq * 4) = make_uint4(w[0][p], w[1][p], w[2][p], w[3][p]);
+      *reinterpret_cast<uint4*>(Vt + d * C::VROW + k0) = r.v[i];
     }
   }
-  if constexpr (sizeof(T) == 2) publish_tile_flags(flags, emax >= 143u, emax >= 119u);
+}
+
+// Walks the tiles of one workgroup: the centroid tiles (compensation), then the tiles of
+// every kept key cluster in list order.  A cluster's tile count is clamped to the tiles the
+// packed buffer gives it, so keys past it are never read.
+struct PackCursor {
+  int phase;   // 0: centroid tiles, 1: kept clusters
+  int it;      // centroid tile index, or position in the kept list
+  int j;       // tile within the cluster
+  int nt;      // tiles of the current cluster
+  int n;       // keys of the current cluster
+  int t0;      // first tile of the current cluster
+  int tile;    // packed tile index within the head
+  int nvalid;  // keys of the tile
+};
+__device__ __forceinline__ bool pack_next(PackCursor& c, bool comp, int ctiles, int first_ctile,
+                                          const int16_t* __restrict__ list, int cnt,
+                                          const int32_t* __restrict__ k_off, const int32_t* __restrict__ tile_off,
+                                          int Ck) {
+  if (c.phase == 0) {
+    if (comp && c.it + 1 < ctiles) {
+      ++c.it;
+      c.tile = first_ctile + c.it;
+      c.nvalid = kNK;
+      return true;
+    }
+    c.phase = 1;
+    c.it = -1;
+    c.j = 0;
+    c.nt = 0;
+  }
+  if (c.j + 1 < c.nt) {  // next tile of the current cluster
+    ++c.j;
+    c.tile = c.t0 + c.j;
+    c.nvalid = min(kNK, c.n - c.j * kNK);
+    return true;
+  }
+  while (++c.it < cnt) {  // first tile of the next non-empty kept cluster
+    const int cl = list[c.it];
+    if (cl < 0 || cl >= Ck) continue;
+    const int n = k_off[cl + 1] - k_off[cl];
+    const int t0 = tile_off[cl];
+    const int nt = min((n + kNK - 1) / kNK, min(tile_off[cl + 1], first_ctile) - t0);
+    if (n <= 0 || t0 < 0 || nt <= 0) continue;
+    c.j = 0;
+    c.nt = nt;
+    c.n = n;
+    c.t0 = t0;
+    c.tile = t0;
+    c.nvalid = min(kNK, n);
+    return true;
+  }
+  return false;
 }
 
 template <typename T, int D, bool REPAIR>
@@ -611,29 +606,33 @@ struct AttnLds {
   static constexpr int REP = REPAIR ? repair_lds_bytes<T, D>() : 0;
   static constexpr int MAIN0 = TILES > C::Z_BYTES ? TILES : C::Z_BYTES;
   static constexpr int MAIN = MAIN0 > REP ? MAIN0 : REP;
-  static constexpr int BIAS = MAIN;                      // float[kNK]
-  static constexpr int FLAGS = BIAS + kNK * 4;           // int[2 buffers][8]
-  static constexpr int TOTAL = FLAGS + 2 * kFlagBytes;
+  static constexpr int BIAS = MAIN;  // float[2 buffers][kNK]
+  static constexpr int TOTAL = BIAS + 2 * kNK * 4;
 };
 
-// One workgroup per CU with the whole register file per wave (launch bound 1): the loads of
-// the next tile, the LDS fragment reads and both MFMA chains stay in flight without spills.
+// Workgroups resident per CU: bfloat16 kernels keep two (eight waves, two per SIMD, so
+// one wave's softmax overlaps the other's MFMAs); float32 tiles need the LDS of one.
+template <typename T>
+constexpr int attn_occupancy() {
+  return sizeof(T) == 2 ? 2 : 1;
+}
+
 template <typename T, int D, bool COMP, bool REPAIR>
-__global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2, const int32_t* __restrict__ q_perm,
-    const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_perm,
-    const int32_t* __restrict__ k_off, int Ck, const uint8_t* __restrict__ keep,
-    const int32_t* __restrict__ kv_count, const int16_t* __restrict__ kv_idx, int Hm,
-    const float* __restrict__ Kbar, const float* __restrict__ Vbar, const float* __restrict__ Acorr,
+__global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_kernel(
+    const T* __restrict__ Q, T* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
+    const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
+    int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ kv_count,
+    const int16_t* __restrict__ kv_idx, int Hm, const int32_t* __restrict__ tile_off,
+    const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
+    int tiles_per_head, int first_ctile, int ctiles, const float* __restrict__ Acorr,
     const float* __restrict__ ccorr) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, REPAIR>;
+  using R = TileRegs<T, D>;
+  constexpr size_t kTileElems = static_cast<size_t>(kNK) * D;
   extern __shared__ __align__(16) unsigned char smem[];
-  T* Ks0 = reinterpret_cast<T*>(smem);
   T* Z = reinterpret_cast<T*>(smem);
-  float* bias = reinterpret_cast<float*>(smem + L::BIAS);
-  int* flags0 = reinterpret_cast<int*>(smem + L::FLAGS);
+  float* bias0 = reinterpret_cast<float*>(smem + L::BIAS);
 
   const int G = Hq / Hkv;
   int unit, a, g;
@@ -643,18 +642,31 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
   const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
   const size_t mrow = (static_cast<size_t>(b) * Hm + hm) * Cq + a;
   const size_t bhq = static_cast<size_t>(b) * Hq + hq;
+  const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
   const T* Qh = Q + bhq * S * D;
   T* Oh = O + bhq * S * D;
-  const T* Kh = K + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
-  const T* Vh = V + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
-  const float* Kb = COMP ? Kbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D : nullptr;
-  const float* Vb = COMP ? Vbar + (static_cast<size_t>(b) * Hkv + kvh) * Ck * D : nullptr;
+  const T* Kph = Kp + bkv * tiles_per_head * kTileElems;
+  const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileElems * sizeof(T);
+  const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
   const uint8_t* keep_row = keep + mrow * Ck;
   const int16_t* list = kv_idx + mrow * Ck;
   const int cnt = kv_count[mrow];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int q_lo = q_off[a], q_hi = q_off[a + 1];
+
+  // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise).
+  auto write_bias = [&](float* dst, int ct) {
+    if (threadIdx.x < kNK) {
+      const int cc = ct * kNK + static_cast<int>(threadIdx.x);
+      float bv = -INFINITY;
+      if (cc < Ck) {
+        const int n = k_off[cc + 1] - k_off[cc];
+        if (n > 0 && keep_row[cc] == 0) bv = __log2f(static_cast<float>(n));
+      }
+      dst[threadIdx.x] = bv;
+    }
+  };
 
   for (int rt = q_lo; rt < q_hi; rt += kRowsWG) {
     const int nrows = min(kRowsWG, q_hi - rt);
@@ -669,100 +681,37 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     RowState<D> st;
     init_state<D>(st);
 
-    if constexpr (COMP) {
-      // Centroid columns: one tile per 64 key clusters, bias log2 n_c where skipped.
-      T* Ks = Ks0;
-      T* Vt = Ks0 + C::K_ELEMS;
-      for (int c0 = 0; c0 < Ck; c0 += kNK) {
-        load_centroid_tile<T, D>(Ks, Vt, bias, flags0, Kb, Vb, c0, Ck, k_off, keep_row);
-        __syncthreads();
-        const bool f16 = sizeof(T) != 2 || tile_fits_f16(flags0);
-        if (!f16) {
-          load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
-          __syncthreads();
-        }
-        if (__ballot(bias[lane] > -INFINITY) != 0) {
-          if (f16)
-            tile_step<T, D, true>(Ks, Vt, qf, st, c2, KeyBias{bias}, kNK);
-          else
-            tile_step<T, D, false>(Ks, Vt, qf, st, c2, KeyBias{bias}, kNK);
-        }
-        __syncthreads();
-      }
-    }
-
-    // Kept key tiles, software pipelined: while tile i is computed from LDS, the rows of
-    // tile i+1 are in flight into registers and the row indices of tile i+2 are in flight
-    // too; two LDS buffers, one barrier per tile.
-    TileCursor cur{-1, 0, 0};
-    bool have = cursor_next(cur, list, cnt, k_off, Ck);
-    KVRegs<T, D> regs;
-    TileRows<T, D> rows_next;
-    TileCursor nxt = cur;
-    bool have_next = false;
+    // Tiles stream through two LDS buffers: while tile i is computed, tile i+1 is in flight
+    // from global memory into registers, then stored; one barrier per tile.
+    PackCursor cur{0, -1, 0, 0, 0, 0, 0, 0};
+    bool have = pack_next(cur, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
+    TileRegs<T, D> regs;
     if (have) {
-      TileRows<T, D> rows0;
-      prefetch_rows<T, D>(rows0, k_perm, cur.kt, min(kNK, cur.hi - cur.kt));
-      prefetch_tile<T, D>(regs, rows0, Kh, Vh);
-      have_next = cursor_next(nxt, list, cnt, k_off, Ck);
-      if (have_next) prefetch_rows<T, D>(rows_next, k_perm, nxt.kt, min(kNK, nxt.hi - nxt.kt));
-      store_tile<T, D>(regs, Ks0, Ks0 + C::K_ELEMS, flags0, min(kNK, cur.hi - cur.kt));
+      prefetch_packed<T, D>(regs, Kph + cur.tile * kTileElems, Vph + cur.tile * kTileElems * sizeof(T));
+      store_packed<T, D>(regs, reinterpret_cast<T*>(smem), reinterpret_cast<T*>(smem) + C::K_ELEMS);
+      if (cur.phase == 0) write_bias(bias0, cur.it);
     }
     __syncthreads();
     int buf = 0;
-    bool deferred = false;
     while (have) {
-      // Issue the rows of tile i+1 (indices arrived during the previous tile) and the
-      // indices of tile i+2.
-      TileCursor nn = nxt;
-      bool have_nn = false;
-      if (have_next) {
-        prefetch_tile<T, D>(regs, rows_next, Kh, Vh);
-        have_nn = cursor_next(nn, list, cnt, k_off, Ck);
-        if (have_nn) prefetch_rows<T, D>(rows_next, k_perm, nn.kt, min(kNK, nn.hi - nn.kt));
-      }
+      PackCursor nxt = cur;
+      const bool have_next = pack_next(nxt, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
+      if (have_next)
+        prefetch_packed<T, D>(regs, Kph + nxt.tile * kTileElems, Vph + nxt.tile * kTileElems * sizeof(T));
       T* Ks = reinterpret_cast<T*>(smem + buf * L::BUF_BYTES);
       T* Vt = Ks + C::K_ELEMS;
-      int* flags = flags0 + buf * (kFlagBytes / 4);
-      const int nvalid = min(kNK, cur.hi - cur.kt);
-      // Tiles whose values do not fit float16 are left to the second pass below.
-      if (sizeof(T) != 2 || tile_fits_f16(flags))
-        tile_step<T, D, true>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
-      else
-        deferred = true;
+      float* bias = bias0 + buf * kNK;
+      const bool pv16 = flags_h[cur.tile] != 0;
+      tile_step<T, D>(Ks, Vt, qf, st, c2, KeyBias{cur.phase == 0 ? bias : nullptr}, cur.nvalid, pv16);
       if (have_next) {
         T* Kn = reinterpret_cast<T*>(smem + (buf ^ 1) * L::BUF_BYTES);
-        store_tile<T, D>(regs, Kn, Kn + C::K_ELEMS, flags0 + (buf ^ 1) * (kFlagBytes / 4),
-                         min(kNK, nxt.hi - nxt.kt));
+        store_packed<T, D>(regs, Kn, Kn + C::K_ELEMS);
+        if (nxt.phase == 0) write_bias(bias0 + (buf ^ 1) * kNK, nxt.it);
       }
       __syncthreads();
       cur = nxt;
       have = have_next;
-      nxt = nn;
-      have_next = have_nn;
       buf ^= 1;
-    }
-    if constexpr (sizeof(T) == 2) {
-      if (deferred) {
-        // Second pass (normally empty): the tiles the first pass skipped, with a bfloat16
-        // P V product.  The same range test picks exactly those tiles again.
-        T* Ks = Ks0;
-        T* Vt = Ks0 + C::K_ELEMS;
-        TileCursor c2c{-1, 0, 0};
-        while (cursor_next(c2c, list, cnt, k_off, Ck)) {
-          const int nvalid = min(kNK, c2c.hi - c2c.kt);
-          const int kt = c2c.kt;
-          auto row_of = [&](int key) { return static_cast<size_t>(k_perm[kt + key]) * D; };
-          load_kv_tile<T, D>(Ks, Vt, flags0, Kh, Vh, nvalid, row_of);
-          __syncthreads();
-          if (!tile_fits_f16(flags0)) {
-            load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
-            __syncthreads();
-            tile_step<T, D, false>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
-          }
-          __syncthreads();
-        }
-      }
     }
 
     const float l_tot = st.l + swap_halves(st.l);
@@ -804,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 // cluster.  Keep bits of the workgroup's probe rows are packed in LDS (one bit per key
 // cluster); the tile's key-cluster labels are in LDS too.
 struct ProbeMask {
-  static constexpr bool kNone = false;
+  __device__ bool active() const { return true; }
   const uint32_t* bits;  // this lane's row of packed keep bits
   const int* klab;       // tile key -> key cluster
   int nvalid;
@@ -817,7 +766,7 @@ struct ProbeMask {
 };
 // Centroid columns of a probe row: log2 n_c where the row's cluster skipped c, else -inf.
 struct ProbeCentroids {
-  static constexpr bool kNone = false;
+  __device__ bool active() const { return true; }
   const uint32_t* bits;
   const float* log2n;  // tile centroid -> log2 n_c (-inf for empty / out of range)
   int c0;
@@ -907,17 +856,10 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
         load_kv_tile_fallback<T, D>(Vt, Vh, nvalid, row_of);
         __syncthreads();
       }
-      if constexpr (SPARSE) {
-        if (f16)
-          tile_step<T, D, true>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid);
-        else
-          tile_step<T, D, false>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid);
-      } else {
-        if (f16)
-          tile_step<T, D, true>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
-        else
-          tile_step<T, D, false>(Ks, Vt, qf, st, c2, NoBias{}, nvalid);
-      }
+      if constexpr (SPARSE)
+        tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid, f16);
+      else
+        tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, nvalid, f16);
       __syncthreads();
     }
   } else if constexpr (SPARSE) {
@@ -933,10 +875,7 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
         load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
         __syncthreads();
       }
-      if (f16)
-        tile_step<T, D, true>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK);
-      else
-        tile_step<T, D, false>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK);
+      tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK, f16);
       __syncthreads();
     }
   }
@@ -980,34 +919,44 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
 
 constexpr int kProbeChunk = 2048;
 
+struct PackedKV {
+  const int32_t* tile_off;
+  const uint8_t* flags;
+  const void* k;
+  const void* v;
+  int tiles_per_head, first_ctile, ctiles;
+};
+
 template <typename T, int D, bool COMP, bool REPAIR>
-void launch_sparse_variant(dim3 grid, hipStream_t stream, const void* Q, const void* K, const void* V, void* O,
-                           float* lse, int B, int Hq, int Hkv, int S, float c2, const int32_t* q_perm,
-                           const int32_t* q_off, int Cq, const int32_t* k_perm, const int32_t* k_off, int Ck,
-                           const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                           const float* Kbar, const float* Vbar, const float* A, const float* c) {
+void launch_sparse_variant(dim3 grid, hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv,
+                           int S, float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off,
+                           int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                           const PackedKV& P, const float* A, const float* c) {
   constexpr int LDS = AttnLds<T, D, REPAIR>::TOTAL;
   auto kern = sparse_attn_kernel<T, D, COMP, REPAIR>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<const T*>(K),
-                     static_cast<const T*>(V), static_cast<T*>(O), lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_perm,
-                     k_off, Ck, keep, kv_count, kv_idx, Hm, Kbar, Vbar, A, c);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<T*>(O), lse, B,
+                     Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, kv_count, kv_idx, Hm, P.tile_off, P.flags,
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, P.ctiles, A, c);
 }
 
 template <typename T, int D>
-bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const void* V, float scale,
-                         const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_perm,
-                         const int32_t* k_off, int Ck, const uint8_t* keep, const int32_t* kv_count,
-                         const int16_t* kv_idx, int Hm, const float* Kbar, const float* Vbar, const float* A,
-                         const float* c, void* O, float* lse, hipStream_t stream) {
+bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* q_perm,
+                         const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const uint8_t* keep,
+                         const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed, bool comp,
+                         const float* A, const float* c, void* O, float* lse, hipStream_t stream) {
   const long long nblocks = static_cast<long long>(B) * Hq * Cq;
   if (nblocks > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(nblocks));
   const float c2 = scale * kLog2e;
-#define BSA_LAUNCH(COMP, REP)                                                                                      \
-  launch_sparse_variant<T, D, COMP, REP>(grid, stream, Q, K, V, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_perm, \
-                                         k_off, Ck, keep, kv_count, kv_idx, Hm, Kbar, Vbar, A, c)
-  if (Kbar != nullptr) {
+  const PackLayout L = pack_layout(B, Hkv, S, D, Ck, sizeof(T));
+  const unsigned char* base = static_cast<const unsigned char*>(packed);
+  const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off), base + L.flags, base + L.k, base + L.v,
+                   L.tiles_per_head, L.first_centroid_tile, L.centroid_tiles};
+#define BSA_LAUNCH(COMP, REP)                                                                                  \
+  launch_sparse_variant<T, D, COMP, REP>(grid, stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, \
+                                         keep, kv_count, kv_idx, Hm, P, A, c)
+  if (comp) {
     if (A != nullptr) BSA_LAUNCH(true, true); else BSA_LAUNCH(true, false);
   } else {
     if (A != nullptr) BSA_LAUNCH(false, true); else BSA_LAUNCH(false, false);
@@ -1065,25 +1014,23 @@ bsa_status launch_probe(int B, int Hq, int Hkv, int S, const void* Q, const void
 using namespace bsa;
 
 extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
-                                           const void* K, const void* V, float scale, const int32_t* q_perm,
-                                           const int32_t* q_offsets, int Cq, const int32_t* k_perm,
+                                           float scale, const int32_t* q_perm, const int32_t* q_offsets, int Cq,
                                            const int32_t* k_offsets, int Ck, const uint8_t* keep,
-                                           const int32_t* kv_count, const int16_t* kv_idx, int Hm, const float* Kbar,
-                                           const float* Vbar, const float* A, const float* c, void* O, float* lse,
-                                           hipStream_t stream) {
+                                           const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                                           const void* packed, size_t packed_bytes, int compensate, const float* A,
+                                           const float* c, void* O, float* lse, hipStream_t stream) {
   if (!valid_dtype(dtype)) return BSA_E_DTYPE;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
-  if (!Q || !K || !V || !O || !q_perm || !q_offsets || !k_perm || !k_offsets || !keep || !kv_count || !kv_idx)
-    return BSA_E_ARG;
-  if ((Kbar == nullptr) != (Vbar == nullptr)) return BSA_E_ARG;
+  if (!Q || !O || !q_perm || !q_offsets || !k_offsets || !keep || !kv_count || !kv_idx || !packed) return BSA_E_ARG;
   if ((A == nullptr) != (c == nullptr)) return BSA_E_ARG;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   if (Ck > 32767) return BSA_E_UNSUPPORTED;
-#define BSA_ARGS B, Hq, Hkv, S, Q, K, V, scale, q_perm, q_offsets, Cq, k_perm, k_offsets, Ck, keep, kv_count, kv_idx, \
-                 Hm, Kbar, Vbar, A, c, O, lse, stream
+  if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype)).total) return BSA_E_WORKSPACE;
+#define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
+                 compensate != 0, A, c, O, lse, stream
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS

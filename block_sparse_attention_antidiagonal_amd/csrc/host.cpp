@@ -19,7 +19,7 @@ extern "C" const char* bsa_status_string(int status) {
   }
 }
 
-extern "C" int bsa_abi_version(void) { return 1; }
+extern "C" int bsa_abi_version(void) { return 2; }
 
 // "Sparse-block compensation", API table (select_probe_rows: head-agnostic, round-robin over
 // query clusters, weights |G_a| / m_a) and "Deviations from the papers" (middle-out member;

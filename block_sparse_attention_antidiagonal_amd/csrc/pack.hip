@@ -1,0 +1,239 @@
+// Key/value packing for block-sparse attention, fused with the cluster centroids.
+//
+// "Partition the Support, Reconstruct the Residual" (summary page): keys and values are
+// permuted into group-major order before the sparse kernel.  "Sparse-block compensation",
+// section "SVG-EAR -- centroid compensation": each key cluster's key and value means and its
+// size.
+//
+// One pass over K and V per (batch, K/V head) writes, for every key cluster, its keys in
+// tiles of 64 (the last tile of a cluster zero-filled), in the layout the attention kernel
+// copies straight into LDS:
+//   K tile   [64 keys][D]   (input element type)
+//   V^T tile [D][64 keys]   (bfloat16 inputs: float16 when every value of the tile is
+//                            below 2^16 in magnitude -- bfloat16 values there are at most
+//                            65280, inside the float16 range -- and some is at least 2^-8,
+//                            so that values losing float16 precision are negligible next to
+//                            the tile's largest; else bfloat16.  float32 inputs: float32)
+// and the per-tile format flag.  The same pass sums each cluster's keys and values for the
+// centroids, which are packed afterwards as extra tiles (K-bar rounded to the input type,
+// V-bar like V).
+#include "pack.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int kPackThreads = 256;
+
+// tile_off[c] = first tile of cluster c (exclusive prefix of ceil(n_c / 64)); one workgroup.
+__global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __restrict__ offsets, int C,
+                                                             int32_t* __restrict__ tile_off) {
+  __shared__ int32_t part[1024];
+  const int per = (C + blockDim.x - 1) / blockDim.x;
+  const int c0 = threadIdx.x * per;
+  int32_t run = 0;
+  for (int c = c0; c < c0 + per && c < C; ++c) run += (offsets[c + 1] - offsets[c] + kPackTile - 1) / kPackTile;
+  part[threadIdx.x] = run;
+  __syncthreads();
+  for (int d = 1; d < static_cast<int>(blockDim.x); d <<= 1) {
+    const int32_t add = threadIdx.x >= static_cast<unsigned>(d) ? part[threadIdx.x - d] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int32_t off = part[threadIdx.x] - run;
+  for (int c = c0; c < c0 + per && c < C; ++c) {
+    tile_off[c] = off;
+    off += (offsets[c + 1] - offsets[c] + kPackTile - 1) / kPackTile;
+  }
+  if (threadIdx.x == blockDim.x - 1) tile_off[C] = part[blockDim.x - 1];
+}
+
+__device__ __forceinline__ uint32_t bf16_exp(uint16_t b) { return (b >> 7) & 0xffu; }
+
+// One workgroup per (key cluster, batch x K/V head).
+template <typename T, int D>
+__global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, int S, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, int C, const int32_t* __restrict__ tile_off, int tiles_per_head,
+    T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
+    float* __restrict__ Kbar, float* __restrict__ Vbar) {
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;                            // chunks per row
+  constexpr int kItems = kPackTile * CPR / kPackThreads;  // (key, chunk) items per thread
+  constexpr int kKeyGroups = kPackThreads / CPR;          // keys covered in one pass
+  __shared__ float vt[kPackTile][D + 1];                  // the tile's V as float32
+  __shared__ float red[2][kKeyGroups][D];
+  __shared__ uint32_t emax_s;
+  const int c = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int lo = offsets[c], n = offsets[c + 1] - lo;
+  const int t = threadIdx.x, ch = t % CPR, kg = t / CPR;
+  const T* Kh = K + bh * static_cast<size_t>(S) * D;
+  const T* Vh = V + bh * static_cast<size_t>(S) * D;
+  float ks[EPC], vs[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) ks[e] = vs[e] = 0.0f;
+  const int ntiles = (n + kPackTile - 1) / kPackTile;
+  for (int j = 0; j < ntiles; ++j) {
+    const size_t tile = bh * tiles_per_head + tile_off[c] + j;
+    if (t == 0) emax_s = 0;
+    __syncthreads();
+    uint32_t emax = 0;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int key = kg + i * kKeyGroups;
+      const int r = j * kPackTile + key;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (r < n) {
+        const size_t row = static_cast<size_t>(perm[lo + r]) * D + ch * EPC;
+        kv = *reinterpret_cast<const uint4*>(Kh + row);
+        vv = *reinterpret_cast<const uint4*>(Vh + row);
+      }
+      *reinterpret_cast<uint4*>(Kp + (tile * kPackTile + key) * D + ch * EPC) = kv;
+      const T* ke = reinterpret_cast<const T*>(&kv);
+      const T* ve = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float kf = to_f32(ke[e]), vf = to_f32(ve[e]);
+        ks[e] += kf;
+        vs[e] += vf;
+        vt[key][ch * EPC + e] = vf;
+        if constexpr (sizeof(T) == 2) emax = max(emax, bf16_exp(ve[e].bits));
+      }
+    }
+    if constexpr (sizeof(T) == 2) atomicMax(&emax_s, emax);
+    __syncthreads();
+    // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).
+    if constexpr (sizeof(T) == 2) {
+      const bool f16 = emax_s <= 142u && emax_s >= 119u;  // bfloat16 exponent 142: [2^15, 2^16); 119: 2^-8
+      if (t == 0) flags[tile] = f16 ? 1 : 0;
+      for (int idx = t; idx < D * (kPackTile / 8); idx += kPackThreads) {
+        const int d = idx / (kPackTile / 8), k0 = (idx % (kPackTile / 8)) * 8;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float a = vt[k0 + 2 * p][d], b = vt[k0 + 2 * p + 1][d];
+          w[p] = f16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+        }
+        *reinterpret_cast<uint4*>(Vtp16 + (tile * D + d) * kPackTile + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      if (t == 0) flags[tile] = 1;
+      for (int idx = t; idx < D * (kPackTile / 4); idx += kPackThreads) {
+        const int d = idx / (kPackTile / 4), k0 = (idx % (kPackTile / 4)) * 4;
+        *reinterpret_cast<f32x4*>(Vtp32 + (tile * D + d) * kPackTile + k0) =
+            f32x4{vt[k0][d], vt[k0 + 1][d], vt[k0 + 2][d], vt[k0 + 3][d]};
+      }
+    }
+    __syncthreads();
+  }
+  // Centroid means: reduce the per-thread column sums over the key groups.
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+    red[0][kg][ch * EPC + e] = ks[e];
+    red[1][kg][ch * EPC + e] = vs[e];
+  }
+  __syncthreads();
+  const float inv = n > 0 ? 1.0f / static_cast<float>(n) : 0.0f;
+  for (int e = t; e < 2 * D; e += kPackThreads) {
+    const int which = e / D, d = e % D;
+    float s = 0.0f;
+    for (int g = 0; g < kKeyGroups; ++g) s += red[which][g][d];
+    (which == 0 ? Kbar : Vbar)[(bh * C + c) * D + d] = s * inv;
+  }
+}
+
+// Centroid tiles: K-bar rounded to the input type, V-bar^T like value tiles.  One workgroup
+// per (64-centroid tile, batch x K/V head).
+template <typename T, int D>
+__global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
+    const float* __restrict__ Kbar, const float* __restrict__ Vbar, int C, int tiles_per_head, int first_tile,
+    T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags) {
+  __shared__ float vmax_s;
+  const int j = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const size_t tile = bh * tiles_per_head + first_tile + j;
+  const float* Kb = Kbar + bh * C * D;
+  const float* Vb = Vbar + bh * C * D;
+  const int t = threadIdx.x;
+  if (t == 0) vmax_s = 0.0f;
+  __syncthreads();
+  float vmax = 0.0f;
+  for (int idx = t; idx < kPackTile * D; idx += kPackThreads) {
+    const int key = idx / D, d = idx % D;
+    const int cc = j * kPackTile + key;
+    Kp[(tile * kPackTile + key) * D + d] = from_f32<T>(cc < C ? Kb[static_cast<size_t>(cc) * D + d] : 0.0f);
+    if (cc < C) vmax = fmaxf(vmax, fabsf(Vb[static_cast<size_t>(cc) * D + d]));
+  }
+  // The range test is on float values here: every |v| at most the float16 maximum, some
+  // |v| >= 2^-8.
+  atomicMax(reinterpret_cast<unsigned int*>(&vmax_s), __float_as_uint(vmax));  // non-negative floats order as uints
+  __syncthreads();
+  if constexpr (sizeof(T) == 2) {
+    const bool f16 = vmax_s <= 65504.0f && vmax_s >= 0.00390625f;
+    if (t == 0) flags[tile] = f16 ? 1 : 0;
+    for (int idx = t; idx < D * kPackTile; idx += kPackThreads) {
+      const int d = idx / kPackTile, key = idx % kPackTile;
+      const int cc = j * kPackTile + key;
+      const float x = cc < C ? Vb[static_cast<size_t>(cc) * D + d] : 0.0f;
+      Vtp16[(tile * D + d) * kPackTile + key] =
+          f16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)) : f32_to_bf16(x);
+    }
+  } else {
+    if (t == 0) flags[tile] = 1;
+    for (int idx = t; idx < D * kPackTile; idx += kPackThreads) {
+      const int d = idx / kPackTile, key = idx % kPackTile;
+      const int cc = j * kPackTile + key;
+      Vtp32[(tile * D + d) * kPackTile + key] = cc < C ? Vb[static_cast<size_t>(cc) * D + d] : 0.0f;
+    }
+  }
+}
+
+template <typename T, int D>
+bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, const int32_t* perm,
+                       const int32_t* offsets, int C, float* Kbar, float* Vbar, void* packed, hipStream_t stream) {
+  const PackLayout L = pack_layout(B, Hkv, S, D, C, sizeof(T));
+  unsigned char* base = static_cast<unsigned char*>(packed);
+  int32_t* tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
+  uint8_t* flags = base + L.flags;
+  T* Kp = reinterpret_cast<T*>(base + L.k);
+  uint16_t* V16 = reinterpret_cast<uint16_t*>(base + L.v);
+  float* V32 = reinterpret_cast<float*>(base + L.v);
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, tile_off);
+  hipLaunchKernelGGL((pack_cluster_kernel<T, D>), dim3(C, B * Hkv), dim3(kPackThreads), 0, stream,
+                     static_cast<const T*>(K), static_cast<const T*>(V), S, perm, offsets, C, tile_off, L.tiles_per_head,
+                     Kp, V16, V32, flags, Kbar, Vbar);
+  hipLaunchKernelGGL((pack_centroid_kernel<T, D>), dim3(L.centroid_tiles, B * Hkv), dim3(kPackThreads), 0, stream,
+                     Kbar, Vbar, C, L.tiles_per_head, L.first_centroid_tile, Kp, V16, V32, flags);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, size_t* bytes) {
+  if (!bytes || B < 1 || Hkv < 1 || S < 1 || C < 1) return BSA_E_ARG;
+  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  if (C > 32767) return BSA_E_UNSUPPORTED;
+  *bytes = pack_layout(B, Hkv, S, D, C, dtype_size(dtype)).total;
+  return BSA_OK;
+}
+
+extern "C" bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
+                                  const int32_t* perm, const int32_t* offsets, int C, float* Kbar, float* Vbar,
+                                  void* packed, size_t packed_bytes, hipStream_t stream) {
+  size_t need = 0;
+  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, &need);
+  if (st != BSA_OK) return st;
+  if (!K || !V || !perm || !offsets || !Kbar || !Vbar) return BSA_E_ARG;
+  if (!packed || packed_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hkv > 65535) return BSA_E_UNSUPPORTED;
+  if (dtype == BSA_BF16)
+    return D == 128 ? launch_pack<bf16_t, 128>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream)
+                    : launch_pack<bf16_t, 64>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream);
+  return D == 128 ? launch_pack<float, 128>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream)
+                  : launch_pack<float, 64>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream);
+}

@@ -1,0 +1,45 @@
+// Layout of the packed key/value buffer written by bsa_kv_pack and read by
+// bsa_sparse_attention.
+#pragma once
+
+#include "common.hpp"
+
+namespace bsa {
+
+constexpr int kPackTile = 64;  // keys per packed tile
+
+// Byte offsets of the packed buffer's sections, and its tile counts.
+//   tile_off  int32 [C + 1]            first tile of each key cluster (shared by all heads)
+//   flags     uint8 [B*Hkv][tiles]     V^T tile format: 1 = float16 / float32, 0 = bfloat16
+//   k         T     [B*Hkv][tiles][64][D]
+//   v         [B*Hkv][tiles][D][64]    16-bit for bfloat16 inputs, float32 for float32 inputs
+// Per head, token tiles come first (sum over clusters of ceil(n_c / 64) <= ceil(S/64) + C of
+// them), then ceil(C / 64) centroid tiles starting at first_centroid_tile.
+struct PackLayout {
+  size_t tile_off, flags, k, v, total;
+  int tiles_per_head, first_centroid_tile, centroid_tiles;
+};
+
+inline size_t pack_align(size_t x) { return (x + 255) / 256 * 256; }
+
+inline PackLayout pack_layout(int B, int Hkv, int S, int D, int C, size_t elem) {
+  PackLayout L;
+  const int tok_tiles = (S + kPackTile - 1) / kPackTile + C;
+  L.centroid_tiles = (C + kPackTile - 1) / kPackTile;
+  L.first_centroid_tile = tok_tiles;
+  L.tiles_per_head = tok_tiles + L.centroid_tiles;
+  const size_t nt = static_cast<size_t>(B) * Hkv * L.tiles_per_head;
+  size_t off = 0;
+  L.tile_off = off;
+  off = pack_align(off + (static_cast<size_t>(C) + 1) * 4);
+  L.flags = off;
+  off = pack_align(off + nt);
+  L.k = off;
+  off = pack_align(off + nt * kPackTile * D * elem);
+  L.v = off;
+  off = pack_align(off + nt * kPackTile * D * elem);
+  L.total = off;
+  return L;
+}
+
+}  // namespace bsa

@@ -73,6 +73,7 @@ class SparseAttentionPath:
     def __init__(self, cfg: PathConfig, device="cuda"):
         self.cfg = cfg
         self.device = torch.device(device)
+        self._pack_buffer = None  # reused across calls
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -97,10 +98,11 @@ class SparseAttentionPath:
         mark("start")
         layout = api.cluster_layout(self.labels, cfg.C)
         mark("layout")
-        kbar = vbar = None
-        if cfg.compensate:
-            kbar, vbar = api.centroids(k, v, layout)
-            mark("centroids")
+        # One pass over K/V: cluster tiles for the attention kernel and the centroids.
+        kv = api.kv_pack(k, v, layout, self._pack_buffer)
+        self._pack_buffer = kv.buffer
+        kbar, vbar = (kv.kbar, kv.vbar) if cfg.compensate else (None, None)
+        mark("pack")
         scores = None
         if cfg.mask_mode == "scored":
             scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
@@ -121,8 +123,7 @@ class SparseAttentionPath:
             mark("fit")
             res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
             if keep_sparse:
-                res.out_sparse = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar,
-                                                                    cfg.scale)
-        res.out = api.centroid_compensated_attention(q, k, v, layout, layout, mask, kbar, vbar, cfg.scale, A=A, c=c)
+                res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale)
+        res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, A=A, c=c)
         mark("attention")
         return res

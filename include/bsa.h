@@ -93,6 +93,30 @@ bsa_status bsa_centroids(int B, int Hkv, int S, int D, int dtype, const void* K,
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Key/value packing, fused with the centroids.  [SPR] (summary page): keys and values are
+ * permuted into group-major order before the sparse kernel; [SBC] "SVG-EAR -- centroid
+ * compensation": kbar_c, vbar_c and n_c as for bsa_centroids.  One pass over K and V writes
+ * every key cluster's keys in tiles of 64 (a cluster's last tile zero-filled) in the form
+ * bsa_sparse_attention copies into on-chip memory, then the centroid tiles:
+ *   K tile    [64 keys][D]  dtype
+ *   V^T tile  [D][64 keys]  float32 inputs: float32.  bfloat16 inputs: float16 when every
+ *             value of the tile is below 2^16 in magnitude and some is at least 2^-8, else
+ *             bfloat16 (a per-tile flag records which)
+ * plus the first tile of every cluster.  The buffer is opaque to callers: its size comes
+ * from bsa_kv_pack_workspace_size, it is valid for the key layout (perm, offsets, C) it was
+ * packed with, and bsa_sparse_attention must be given the same offsets.
+ *   K, V [B, Hkv, S, D] dtype;  perm int32 [S], offsets int32 [C+1]: key cluster layout
+ *   Kbar, Vbar float [B, Hkv, C, D] out (cluster means; an empty cluster gives zeros)
+ *   packed: device buffer of at least bsa_kv_pack_workspace_size bytes, packed_bytes its size
+ * Needs D in {64, 128}, 1 <= C <= 32767, B * Hkv <= 65535.  BSA_E_WORKSPACE if the buffer
+ * is missing or too small.
+ */
+bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, size_t* bytes_host);
+bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V, const int32_t* perm,
+                       const int32_t* offsets, int C, float* Kbar, float* Vbar, void* packed, size_t packed_bytes,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Antidiagonal block scores.  [HMR] "XAttention -- anti-diagonal block scoring": over the
  * cluster-major token order (perm; NULL = identity), zero-padded to Sp = nb*block tokens
  * with nb = ceil(S / block) ([HMR] "Out of scope, and why": padding, padded keys take
@@ -134,26 +158,26 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
 /* ------------------------------------------------------------------------------------
  * Block-sparse attention with centroid compensation.  [SBC] "The problem", "SVG-EAR --
  * centroid compensation" and "No LSE needed": query row i of cluster a attends to every
- * key of every kept key cluster (kv list of its mask row) and, when Kbar/Vbar are given,
- * to one extra column per skipped non-empty key cluster c with logit
- * q_i . kbar_c * scale + log n_c and value vbar_c, all inside one softmax.  With
- * Kbar == Vbar == NULL skipped blocks are dropped (hard drop; the softmax renormalizes over
- * kept keys).  A row with no column at all gets O = 0 and lse = -inf.
- * With A and c given (from bsa_probe_fit), every output row o is replaced by o + o A + c
- * before it is rounded to dtype ([SPR]: the correction is applied to all rows).
- *   Q [B, Hq, S, D], K, V [B, Hkv, S, D], O [B, Hq, S, D] out, all dtype
- *   q_perm/q_offsets (Cq clusters) and k_perm/k_offsets (Ck clusters): cluster layouts
+ * key of every kept key cluster (kv list of its mask row) and, with compensate != 0, to one
+ * extra column per skipped non-empty key cluster c with logit q_i . kbar_c * scale + log n_c
+ * and value vbar_c, all inside one softmax.  With compensate == 0 skipped blocks are dropped
+ * (hard drop; the softmax renormalizes over kept keys).  A row with no column at all gets
+ * O = 0 and lse = -inf.  With A and c given (from bsa_probe_fit), every output row o is
+ * replaced by o + o A + c before it is rounded to dtype ([SPR]: the correction is applied to
+ * all rows).  Keys, values and centroids are read from the buffer bsa_kv_pack wrote.
+ *   Q [B, Hq, S, D], O [B, Hq, S, D] out, both dtype
+ *   q_perm/q_offsets (Cq clusters): query cluster layout; k_offsets [Ck+1]: the key layout
+ *     the buffer was packed with
  *   keep/kv_count/kv_idx: block mask with Hm in {1, Hkv, Hq}
- *   Kbar, Vbar float [B, Hkv, Ck, D] (from bsa_centroids) or both NULL
+ *   packed, packed_bytes: the bsa_kv_pack buffer (BSA_E_WORKSPACE if smaller than its size)
  *   A float [B, Hq, D, D], c float [B, Hq, D] (correction) or both NULL
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
  */
-bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
-                                const void* V, float scale, const int32_t* q_perm, const int32_t* q_offsets,
-                                int Cq, const int32_t* k_perm, const int32_t* k_offsets, int Ck,
-                                const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                const float* Kbar, const float* Vbar, const float* A, const float* c, void* O,
-                                float* lse, hipStream_t stream);
+bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
+                                const int32_t* q_perm, const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
+                                int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                                const void* packed, size_t packed_bytes, int compensate, const float* A,
+                                const float* c, void* O, float* lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)

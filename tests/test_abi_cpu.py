@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
     assert lib.bsa_status_string(0) == b"ok"
     assert b"workspace" in lib.bsa_status_string(5)
 
@@ -97,21 +97,27 @@ def test_host_validation_rejects_before_launch(lib):
     size = ctypes.c_size_t(0)
     # unknown dtype
     assert lib.bsa_centroids(1, 1, 8, 128, 7, dummy, dummy, dummy, dummy, 1, dummy, dummy, None) == 3
+    # sparse attention: (B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
+    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, O, lse, stream)
+    f = ctypes.c_float(0.1)
+    big = 1 << 40
     # unsupported head dim
-    assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
-                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, None, None, dummy, None,
-                                    None) == 4
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, None, None, dummy, None, None) == 4
     # Hq not a multiple of Hkv
-    assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
-                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, None, None, dummy, None,
-                                    None) == 2
-    # only one of Kbar / Vbar; only one of A / c
-    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
-                                    dummy, dummy, 1, dummy, dummy, dummy, 1, dummy, None, None, None, dummy, None,
-                                    None) == 1
-    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, dummy, 1,
-                                    dummy, dummy, 1, dummy, dummy, dummy, 1, None, None, dummy, None, dummy, None,
-                                    None) == 1
+    assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, None, None, dummy, None, None) == 2
+    # only one of A / c; no packed buffer; packed buffer too small
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, dummy, None, dummy, None, None) == 1
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    None, big, 1, None, None, dummy, None, None) == 1
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, 1024, 1, None, None, dummy, None, None) == 5
+    # K/V packing: centroid outputs are required; buffer too small; unsupported head dim
+    assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, None, None, dummy, big, None) == 1
+    assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, 64, None) == 5
+    assert lib.bsa_kv_pack(1, 1, 8, 80, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, big, None) == 4
     # probe rows: sparse rows need the mask; too many key clusters
     assert lib.bsa_probe_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, 4, None,
                                    None, None, 1, 1, 1, None, None, None, dummy, dummy, dummy, 1 << 30, None) == 1
@@ -140,3 +146,9 @@ def test_workspace_sizes(lib):
     assert _lib.size_query("bsa_antidiag_scores_workspace_size", 1, 40, 40, 32760, 128, 128, 16) == \
         40 * ns * (nb + 2 * ntk) * 4
     assert _lib.size_query("bsa_probe_attention_workspace_size", 1, 40, 32760, 128, 64) == 40 * 17 * 64 * 130 * 4
+    # packed K/V: per head ceil(S/64) + C token tiles and ceil(C/64) centroid tiles of 64 x D
+    # keys and 64 x D values; sections (cluster tile offsets, tile flags, K, V) 256-byte aligned
+    tiles = 40 * (512 + 256 + 4)
+    tile_bytes = 64 * 128 * 2
+    expect = 1280 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
+    assert _lib.size_query("bsa_kv_pack_workspace_size", 1, 40, 32760, 128, 1, 256) == expect

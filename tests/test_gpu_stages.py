@@ -12,7 +12,7 @@ from oracle import centroids as ocen
 from oracle import layout as olay
 from oracle import repair as orep
 from oracle import scoring as osco
-from synthetic import make_custom
+from synthetic import bf16_bits, make_custom
 
 from gpu_common import check_output, compare_masks, dev, host, rel_l2, say
 
@@ -59,6 +59,98 @@ def test_centroids(bsa, dtype, D):
             kb, vb, n = ocen.centroids(wl.k[b, h], wl.v[b, h], wl.labels, wl.C)
             assert np.allclose(host(kbar[b, h]), kb, rtol=1e-5, atol=1e-6)
             assert np.allclose(host(vbar[b, h]), vb, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------------ K/V packing
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem):
+    """Sections of the packed buffer as documented for bsa_kv_pack (test-side decoding)."""
+    tok = -(-S // 64) + C
+    ctiles = -(-C // 64)
+    tph = tok + ctiles
+    nt = B * Hkv * tph
+    off_flags = _align(4 * (C + 1))
+    off_k = off_flags + _align(nt)
+    off_v = off_k + _align(nt * 64 * D * elem)
+    tile_off = buf[: 4 * (C + 1)].view(np.int32)
+    flags = buf[off_flags: off_flags + nt].reshape(B * Hkv, tph)
+    kdt = np.uint16 if elem == 2 else np.float32
+    kt = buf[off_k: off_k + nt * 64 * D * elem].view(kdt).reshape(B * Hkv, tph, 64, D)
+    vt = buf[off_v: off_v + nt * 64 * D * elem].view(kdt).reshape(B * Hkv, tph, D, 64)
+    return tile_off, flags, kt, vt, tok
+
+
+def _as_f16_bits(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype,D,sizes", [("bf16", 128, None), ("f32", 64, None), ("bf16", 64, [0, 1, 63, 64, 65, 130, 7])])
+def test_kv_pack(bsa, dtype, D, sizes):
+    """Packed tiles hold every cluster's keys in layout order, zero-padded to 64, V^T as float16
+    exactly when the tile's values fit (else bfloat16), and the centroid tiles; bit-exact."""
+    say(f"kv pack {dtype} D={D} sizes={sizes}")
+    if sizes is None:
+        wl = make_custom(13, B=2, Hq=2, Hkv=2, S=1500, D=D, dtype=dtype)
+    else:
+        wl = make_custom(14, B=1, Hq=1, Hkv=1, S=sum(sizes), D=D, dtype=dtype, cluster_sizes=sizes,
+                         shuffle_labels=True)
+    B, Hkv, S, C = wl.B, wl.Hkv, wl.S, wl.C
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, C)
+    kv = bsa.kv_pack(dev(wl.k, dtype), dev(wl.v, dtype), lay)
+    elem = 2 if dtype == "bf16" else 4
+    tile_off, flags, kt, vt, tok = decode_packed(kv.buffer.cpu().numpy(), B, Hkv, S, D, C, elem)
+    perm, off, cnt = olay.cluster_layout(wl.labels, C)
+    ntiles = -(-cnt // 64)
+    assert np.array_equal(tile_off, np.concatenate([[0], np.cumsum(ntiles)]))
+    kbar, vbar = host(kv.kbar), host(kv.vbar)
+    for b in range(B):
+        for h in range(Hkv):
+            u = b * Hkv + h
+            kb, vb, _ = ocen.centroids(wl.k[b, h], wl.v[b, h], wl.labels, C)
+            assert np.allclose(kbar[b, h], kb, rtol=1e-5, atol=1e-6)
+            assert np.allclose(vbar[b, h], vb, rtol=1e-5, atol=1e-6)
+            kbits = bf16_bits(wl.k[b, h]) if elem == 2 else wl.k[b, h].astype(np.float32)
+            for c in range(C):
+                rows = perm[off[c]: off[c + 1]]
+                for j in range(ntiles[c]):
+                    t = tile_off[c] + j
+                    r = rows[j * 64: (j + 1) * 64]
+                    n = r.size
+                    assert np.array_equal(kt[u, t, :n], kbits[r]), (c, j)
+                    assert not kt[u, t, n:].any()
+                    vals = wl.v[b, h][r].astype(np.float64)  # [n, D], exact in the input type
+                    if elem == 4:
+                        assert flags[u, t] == 1
+                        assert np.array_equal(vt[u, t, :, :n], vals.T.astype(np.float32))
+                    else:
+                        mx = np.max(np.abs(vals)) if n else 0.0
+                        fits = mx < 65536.0 and mx >= 2.0 ** -8
+                        assert flags[u, t] == int(fits), (c, j, mx)
+                        want = _as_f16_bits(vals.T) if fits else bf16_bits(vals.T)
+                        assert np.array_equal(vt[u, t, :, :n], want), (c, j)
+                    assert not vt[u, t, :, n:].any()
+            # centroid tiles: K-bar rounded to the input type, V-bar^T like value tiles
+            for j in range(-(-C // 64)):
+                t = tok + j
+                cs = slice(j * 64, min(C, (j + 1) * 64))
+                n = cs.stop - cs.start
+                want_k = bf16_bits(kbar[b, h][cs]) if elem == 2 else kbar[b, h][cs].astype(np.float32)
+                assert np.array_equal(kt[u, t, :n], want_k)
+                vv = vbar[b, h][cs]
+                if elem == 2:
+                    mx = np.max(np.abs(vv))
+                    fits = mx <= 65504.0 and mx >= 2.0 ** -8
+                    assert flags[u, t] == int(fits)
+                    want_v = _as_f16_bits(vv.T) if fits else bf16_bits(vv.T)
+                else:
+                    want_v = vv.T.astype(np.float32)
+                assert np.array_equal(vt[u, t, :, :n], want_v)
 
 
 # ------------------------------------------------------------------ top-p
@@ -148,10 +240,7 @@ def run_attention(bsa, wl, keep_np, compensate, lse=False):
     lay = bsa.cluster_layout(lab, wl.C)
     q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
     mask = bsa.mask_from_keep(torch.from_numpy(np.ascontiguousarray(keep_np)).cuda())
-    kbar = vbar = None
-    if compensate:
-        kbar, vbar = bsa.centroids(k, v, lay)
-    return bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, kbar, vbar, wl.scale, return_lse=lse)
+    return bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, compensate, wl.scale, return_lse=lse)
 
 
 def oracle_attention(wl, keep_np, compensate, b, hq):
@@ -299,10 +388,7 @@ def test_attention_with_correction_epilogue(bsa, dtype, D, compensate):
     lay = bsa.cluster_layout(lab, wl.C)
     q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
     mask = bsa.mask_from_keep(torch.from_numpy(wl.mask).cuda())
-    kbar = vbar = None
-    if compensate:
-        kbar, vbar = bsa.centroids(k, v, lay)
-    out = host(bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, kbar, vbar, wl.scale,
+    out = host(bsa.centroid_compensated_attention(q, k, v, lay, lay, mask, compensate, wl.scale,
                                                   A=torch.from_numpy(A).cuda(), c=torch.from_numpy(c).cuda()))
     for h in range(2):
         ref, _ = oracle_attention(wl, wl.mask, compensate, 0, h)
