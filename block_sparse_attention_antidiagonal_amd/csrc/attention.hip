@@ -240,6 +240,70 @@ __device__ __forceinline__ void load_centroid_fallback(T* Vt, const float* __res
   }
 }
 
+// ----------------------------------------------------------------- LDS tile layouts
+
+// Padded rows (tiles stored by the threads themselves): K rows of D + 16 B, V^T rows of
+// 64 keys + 8 B (bfloat16) or 16 B (float32), keys in natural order.
+template <typename T, int D>
+struct PaddedLds {
+  using C = Cfg<T, D>;
+  static __device__ __forceinline__ void kfrag(Frag<T>& f, const T* Ks, int row, int kk, int h) {
+    load_frag(f, Ks + row * C::KROW + kk * 16 + 8 * h);
+  }
+  static __device__ __forceinline__ void vfrag(Frag<T>& f, const T* Vt, int d, int ks, int h) {
+    load_frag_split(f, Vt + d * C::VROW + ks * 16 + 4 * h);
+  }
+  static __device__ __forceinline__ void vfrag16(Frag16& f, const T* Vt, int d, int ks, int h) {
+    load_frag_split(f, reinterpret_cast<const bf16_t*>(Vt + d * C::VROW + ks * 16 + 4 * h));
+  }
+};
+
+// Unpadded rows with an XOR swizzle of 16-byte chunks (tiles copied from the packed buffer
+// straight into LDS).  Chunk c of row r sits at chunk position c ^ ((r / RP) & MASK), where
+// RP rows share one 256-byte bank line; the 16 lanes of a read then hit 16 distinct chunks.
+// V^T rows hold the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15, so the
+// eight keys one lane needs in a P V step are one contiguous 16 bytes.
+template <int ROWB>
+struct Swz {
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;
+  static constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+  static __device__ __forceinline__ int pos(int r, int c) { return c ^ ((r / RP) & MASK); }
+  static __device__ __forceinline__ const uint4* chunk(const void* base, int r, int c) {
+    return reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(base) + r * ROWB + pos(r, c) * 16);
+  }
+};
+
+template <typename T, int D>
+struct SwzLds {
+  static constexpr int KROWB = D * static_cast<int>(sizeof(T));
+  static constexpr int VROWB = kNK * static_cast<int>(sizeof(T));
+  static constexpr int K_BYTES = kNK * KROWB;
+  static constexpr int V_BYTES = D * VROWB;
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  using SK = Swz<KROWB>;
+  using SV = Swz<VROWB>;
+  template <typename S, typename F>
+  static __device__ __forceinline__ void frag(F& f, const void* base, int row, int e0) {
+    if constexpr (sizeof(T) == 2) {
+      f.v = __builtin_bit_cast(decltype(f.v), *S::chunk(base, row, e0 / EPC));
+    } else {
+      const f32x4 lo = __builtin_bit_cast(f32x4, *S::chunk(base, row, e0 / EPC));
+      const f32x4 hi = __builtin_bit_cast(f32x4, *S::chunk(base, row, e0 / EPC + 1));
+      f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  static __device__ __forceinline__ void kfrag(Frag<T>& f, const T* Ks, int row, int kk, int h) {
+    frag<SK>(f, Ks, row, kk * 16 + 8 * h);
+  }
+  static __device__ __forceinline__ void vfrag(Frag<T>& f, const T* Vt, int d, int ks, int h) {
+    frag<SV>(f, Vt, d, ks * 16 + 8 * h);
+  }
+  static __device__ __forceinline__ void vfrag16(Frag16& f, const T* Vt, int d, int ks, int h) {
+    f.v = __builtin_bit_cast(f16x8, *SV::chunk(Vt, d, (ks * 16 + 8 * h) / EPC));
+  }
+};
+
 // ----------------------------------------------------------------- tile compute
 
 // Logit bias policies for one 64-key tile (values in log2 units, added to the scaled logits).
@@ -259,7 +323,7 @@ struct KeyBias {  // one bias per key from LDS (centroid columns: log2 n_c or -i
 // pv16: for bfloat16 inputs the tile's V^T in LDS is float16 and P is rounded to float16
 // (else both are bfloat16).  Bias, nvalid and pv16 are uniform over the workgroup, so the
 // branches on them cost no divergence and the tile step is instantiated once per call site.
-template <typename T, int D, typename Bias>
+template <typename T, int D, typename Lds, typename Bias>
 __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
                                           const Bias& bias, int nvalid, bool pv16) {
   using C = Cfg<T, D>;
@@ -269,8 +333,8 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk) {
     Frag<T> a0, a1;
-    load_frag(a0, Ks + r * C::KROW + kk * 16 + 8 * h);
-    load_frag(a1, Ks + (32 + r) * C::KROW + kk * 16 + 8 * h);
+    Lds::kfrag(a0, Ks, r, kk, h);
+    Lds::kfrag(a1, Ks, 32 + r, kk, h);
     s0 = mma(a0, qf[kk], s0);
     s1 = mma(a1, qf[kk], s1);
   }
@@ -331,7 +395,7 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         Frag16 va;
-        load_frag_split(va, reinterpret_cast<const bf16_t*>(Vt + (dt * 32 + r) * C::VROW + ks * 16 + 4 * h));
+        Lds::vfrag16(va, Vt, dt * 32 + r, ks, h);
         st.o[dt] = mma(va, pb, st.o[dt]);
       }
     }
@@ -343,7 +407,7 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         Frag<T> va;
-        load_frag_split(va, Vt + (dt * 32 + r) * C::VROW + ks * 16 + 4 * h);
+        Lds::vfrag(va, Vt, dt * 32 + r, ks, h);
         st.o[dt] = mma(va, pb, st.o[dt]);
       }
     }
@@ -493,57 +557,51 @@ constexpr int attn_lds_bytes() {
 
 // ----------------------------------------------------------------- sparse attention
 
-// One thread's share of a packed tile between its global loads and its LDS stores: NK
-// 16-byte chunks of the K tile and NV of the V^T tile.
+// Packed tiles go from global memory straight into LDS (16 bytes per lane, no registers):
+// one wave instruction fills 1 KB of LDS, lane l writing bytes [16 l, 16 l + 16).  Each lane
+// fetches the global chunk that the swizzle puts in its LDS slot; these per-lane byte offsets
+// are the same for every tile.
 template <typename T, int D>
-struct TileRegs {
-  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
-  static constexpr int K_CHUNKS = kNK * D / EPC;
-  static constexpr int V_EPC = sizeof(T) == 2 ? 8 : 4;  // V^T chunk: 8 x 16-bit or 4 x float32
-  static constexpr int V_CHUNKS = D * kNK / V_EPC;
-  static constexpr int NK = K_CHUNKS / kThreads;
-  static constexpr int NV = V_CHUNKS / kThreads;
-  static_assert(K_CHUNKS % kThreads == 0 && V_CHUNKS % kThreads == 0, "tile chunks must split evenly");
-  uint4 k[NK];
-  uint4 v[NV];
-};
-
-template <typename T, int D>
-__device__ __forceinline__ void prefetch_packed(TileRegs<T, D>& r, const T* __restrict__ ktile,
-                                                const void* __restrict__ vtile) {
-  using R = TileRegs<T, D>;
+struct TileDma {
+  using S = SwzLds<T, D>;
+  static constexpr int NK = S::K_BYTES / 16 / kThreads;  // K chunks per thread
+  static constexpr int NV = S::V_BYTES / 16 / kThreads;  // V^T chunks per thread
+  static_assert(S::K_BYTES % (16 * kThreads) == 0 && S::V_BYTES % (16 * kThreads) == 0, "tile split");
+  int koff[NK];
+  int voff[NV];
+  __device__ __forceinline__ void init() {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < R::NK; ++i)
-    r.k[i] = reinterpret_cast<const uint4*>(ktile)[threadIdx.x + i * kThreads];
+    for (int j = 0; j < NK; ++j) {
+      const int slot = (j * 4 + wave) * 64 + lane;
+      const int r = slot / S::SK::CPR, p = slot % S::SK::CPR;
+      koff[j] = r * S::KROWB + S::SK::pos(r, p) * 16;
+    }
 #pragma unroll
-  for (int i = 0; i < R::NV; ++i)
-    r.v[i] = reinterpret_cast<const uint4*>(vtile)[threadIdx.x + i * kThreads];
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void store_packed(const TileRegs<T, D>& r, T* Ks, T* Vt) {
-  using C = Cfg<T, D>;
-  using R = TileRegs<T, D>;
-#pragma unroll
-  for (int i = 0; i < R::NK; ++i) {
-    const int q = threadIdx.x + i * kThreads;
-    const int row = q / C::CPR, ch = q % C::CPR;
-    *reinterpret_cast<uint4*>(Ks + row * C::KROW + ch * C::EPC) = r.k[i];
-  }
-  constexpr int VCPR = kNK / R::V_EPC;  // chunks per V^T row
-#pragma unroll
-  for (int i = 0; i < R::NV; ++i) {
-    const int q = threadIdx.x + i * kThreads;
-    const int d = q / VCPR, k0 = (q % VCPR) * R::V_EPC;
-    if constexpr (sizeof(T) == 2) {  // 136-byte rows: two 8-byte halves keep the alignment
-      uint2* dst = reinterpret_cast<uint2*>(Vt + d * C::VROW + k0);
-      dst[0] = make_uint2(r.v[i].x, r.v[i].y);
-      dst[1] = make_uint2(r.v[i].z, r.v[i].w);
-    } else {
-      *reinterpret_cast<uint4*>(Vt + d * C::VROW + k0) = r.v[i];
+    for (int j = 0; j < NV; ++j) {
+      const int slot = (j * 4 + wave) * 64 + lane;
+      const int r = slot / S::SV::CPR, p = slot % S::SV::CPR;
+      voff[j] = r * S::VROWB + S::SV::pos(r, p) * 16;
     }
   }
-}
+  // Start copying the tile at gk (K) / gv (V^T) into LDS at Ks / Vt.
+  __device__ __forceinline__ void issue(const unsigned char* gk, const unsigned char* gv, T* Ks, T* Vt) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's launch stub
+    const int wave = threadIdx.x >> 6;
+    unsigned char* lk = reinterpret_cast<unsigned char*>(Ks);
+    unsigned char* lv = reinterpret_cast<unsigned char*>(Vt);
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      __builtin_amdgcn_global_load_lds(gk + koff[j], lk + (j * 4 + wave) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      __builtin_amdgcn_global_load_lds(gv + voff[j], lv + (j * 4 + wave) * 1024, 16, 0, 0);
+#endif
+  }
+};
+
+// Wait for this wave's outstanding global memory operations, tile copies included.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Walks the tiles of one workgroup: the centroid tiles (compensation), then the tiles of
 // every kept key cluster in list order.  A cluster's tile count is clamped to the tiles the
@@ -601,7 +659,7 @@ __device__ __forceinline__ bool pack_next(PackCursor& c, bool comp, int ctiles, 
 template <typename T, int D, bool REPAIR>
 struct AttnLds {
   using C = Cfg<T, D>;
-  static constexpr int BUF_BYTES = C::KV_BYTES;  // one K + V^T tile
+  static constexpr int BUF_BYTES = SwzLds<T, D>::K_BYTES + SwzLds<T, D>::V_BYTES;  // one K + V^T tile
   static constexpr int TILES = 2 * BUF_BYTES;
   static constexpr int REP = REPAIR ? repair_lds_bytes<T, D>() : 0;
   static constexpr int MAIN0 = TILES > C::Z_BYTES ? TILES : C::Z_BYTES;
@@ -628,8 +686,7 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     const float* __restrict__ ccorr) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, REPAIR>;
-  using R = TileRegs<T, D>;
-  constexpr size_t kTileElems = static_cast<size_t>(kNK) * D;
+  constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
   T* Z = reinterpret_cast<T*>(smem);
   float* bias0 = reinterpret_cast<float*>(smem + L::BIAS);
@@ -645,8 +702,8 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
   const T* Qh = Q + bhq * S * D;
   T* Oh = O + bhq * S * D;
-  const T* Kph = Kp + bkv * tiles_per_head * kTileElems;
-  const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileElems * sizeof(T);
+  const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
+  const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
   const uint8_t* keep_row = keep + mrow * Ck;
   const int16_t* list = kv_idx + mrow * Ck;
@@ -654,6 +711,8 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int q_lo = q_off[a], q_hi = q_off[a + 1];
+  TileDma<T, D> dma;
+  dma.init();
 
   // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise).
   auto write_bias = [&](float* dst, int ct) {
@@ -681,33 +740,34 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     RowState<D> st;
     init_state<D>(st);
 
-    // Tiles stream through two LDS buffers: while tile i is computed, tile i+1 is in flight
-    // from global memory into registers, then stored; one barrier per tile.
+    // Tiles stream through two LDS buffers: while tile i is computed, tile i+1 is copied
+    // from global memory into the other buffer; one wait and one barrier per tile.
     PackCursor cur{0, -1, 0, 0, 0, 0, 0, 0};
     bool have = pack_next(cur, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
-    TileRegs<T, D> regs;
     if (have) {
-      prefetch_packed<T, D>(regs, Kph + cur.tile * kTileElems, Vph + cur.tile * kTileElems * sizeof(T));
-      store_packed<T, D>(regs, reinterpret_cast<T*>(smem), reinterpret_cast<T*>(smem) + C::K_ELEMS);
+      T* K0 = reinterpret_cast<T*>(smem);
+      dma.issue(Kph + cur.tile * kTileBytes, Vph + cur.tile * kTileBytes, K0,
+                reinterpret_cast<T*>(smem + SwzLds<T, D>::K_BYTES));
       if (cur.phase == 0) write_bias(bias0, cur.it);
     }
+    wait_vmem();
     __syncthreads();
     int buf = 0;
     while (have) {
       PackCursor nxt = cur;
       const bool have_next = pack_next(nxt, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
-      if (have_next)
-        prefetch_packed<T, D>(regs, Kph + nxt.tile * kTileElems, Vph + nxt.tile * kTileElems * sizeof(T));
-      T* Ks = reinterpret_cast<T*>(smem + buf * L::BUF_BYTES);
-      T* Vt = Ks + C::K_ELEMS;
-      float* bias = bias0 + buf * kNK;
-      const bool pv16 = flags_h[cur.tile] != 0;
-      tile_step<T, D>(Ks, Vt, qf, st, c2, KeyBias{cur.phase == 0 ? bias : nullptr}, cur.nvalid, pv16);
       if (have_next) {
-        T* Kn = reinterpret_cast<T*>(smem + (buf ^ 1) * L::BUF_BYTES);
-        store_packed<T, D>(regs, Kn, Kn + C::K_ELEMS);
+        unsigned char* nb = smem + (buf ^ 1) * L::BUF_BYTES;
+        dma.issue(Kph + nxt.tile * kTileBytes, Vph + nxt.tile * kTileBytes, reinterpret_cast<T*>(nb),
+                  reinterpret_cast<T*>(nb + SwzLds<T, D>::K_BYTES));
         if (nxt.phase == 0) write_bias(bias0 + (buf ^ 1) * kNK, nxt.it);
       }
+      const unsigned char* cb = smem + buf * L::BUF_BYTES;
+      const bool pv16 = flags_h[cur.tile] != 0;
+      tile_step<T, D, SwzLds<T, D>>(reinterpret_cast<const T*>(cb),
+                                    reinterpret_cast<const T*>(cb + SwzLds<T, D>::K_BYTES), qf, st, c2,
+                                    KeyBias{cur.phase == 0 ? bias0 + buf * kNK : nullptr}, cur.nvalid, pv16);
+      wait_vmem();
       __syncthreads();
       cur = nxt;
       have = have_next;
@@ -857,9 +917,9 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
         __syncthreads();
       }
       if constexpr (SPARSE)
-        tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid, f16);
+        tile_step<T, D, PaddedLds<T, D>>(Ks, Vt, qf, st, c2, ProbeMask{mybits, klab, nvalid}, nvalid, f16);
       else
-        tile_step<T, D>(Ks, Vt, qf, st, c2, NoBias{}, nvalid, f16);
+        tile_step<T, D, PaddedLds<T, D>>(Ks, Vt, qf, st, c2, NoBias{}, nvalid, f16);
       __syncthreads();
     }
   } else if constexpr (SPARSE) {
@@ -875,7 +935,7 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
         load_centroid_fallback<T, D>(Vt, Vb, c0, Ck);
         __syncthreads();
       }
-      tile_step<T, D>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK, f16);
+      tile_step<T, D, PaddedLds<T, D>>(Ks, Vt, qf, st, c2, ProbeCentroids{mybits, bias, c0}, kNK, f16);
       __syncthreads();
     }
   }

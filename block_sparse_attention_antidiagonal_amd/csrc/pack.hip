@@ -9,7 +9,9 @@
 // tiles of 64 (the last tile of a cluster zero-filled), in the layout the attention kernel
 // copies straight into LDS:
 //   K tile   [64 keys][D]   (input element type)
-//   V^T tile [D][64 keys]   (bfloat16 inputs: float16 when every value of the tile is
+//   V^T tile [D][64 keys]   (keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15,
+//                            the order in which the attention kernel's P V product takes
+//                            them; bfloat16 inputs: float16 when every value of the tile is
 //                            below 2^16 in magnitude -- bfloat16 values there are at most
 //                            65280, inside the float16 range -- and some is at least 2^-8,
 //                            so that values losing float16 precision are negligible next to
@@ -49,6 +51,10 @@ __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __res
 }
 
 __device__ __forceinline__ uint32_t bf16_exp(uint16_t b) { return (b >> 7) & 0xffu; }
+
+// Key held at position `pos` of a V^T row: positions 4-7 and 8-11 of each 16-key group are
+// swapped (order 0-3, 8-11, 4-7, 12-15), an involution.
+__device__ __forceinline__ int vt_key(int pos) { return (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1); }
 
 // One workgroup per (key cluster, batch x K/V head).
 template <typename T, int D>
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float a = vt[k0 + 2 * p][d], b = vt[k0 + 2 * p + 1][d];
+          const float a = vt[vt_key(k0 + 2 * p)][d], b = vt[vt_key(k0 + 2 * p + 1)][d];
           w[p] = f16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
         }
         *reinterpret_cast<uint4*>(Vtp16 + (tile * D + d) * kPackTile + k0) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
       for (int idx = t; idx < D * (kPackTile / 4); idx += kPackThreads) {
         const int d = idx / (kPackTile / 4), k0 = (idx % (kPackTile / 4)) * 4;
         *reinterpret_cast<f32x4*>(Vtp32 + (tile * D + d) * kPackTile + k0) =
-            f32x4{vt[k0][d], vt[k0 + 1][d], vt[k0 + 2][d], vt[k0 + 3][d]};
+            f32x4{vt[vt_key(k0)][d], vt[vt_key(k0 + 1)][d], vt[vt_key(k0 + 2)][d], vt[vt_key(k0 + 3)][d]};
       }
     }
     __syncthreads();
@@ -173,18 +179,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
     const bool f16 = vmax_s <= 65504.0f && vmax_s >= 0.00390625f;
     if (t == 0) flags[tile] = f16 ? 1 : 0;
     for (int idx = t; idx < D * kPackTile; idx += kPackThreads) {
-      const int d = idx / kPackTile, key = idx % kPackTile;
-      const int cc = j * kPackTile + key;
+      const int d = idx / kPackTile, pos = idx % kPackTile;
+      const int cc = j * kPackTile + vt_key(pos);
       const float x = cc < C ? Vb[static_cast<size_t>(cc) * D + d] : 0.0f;
-      Vtp16[(tile * D + d) * kPackTile + key] =
+      Vtp16[(tile * D + d) * kPackTile + pos] =
           f16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)) : f32_to_bf16(x);
     }
   } else {
     if (t == 0) flags[tile] = 1;
     for (int idx = t; idx < D * kPackTile; idx += kPackThreads) {
-      const int d = idx / kPackTile, key = idx % kPackTile;
-      const int cc = j * kPackTile + key;
-      Vtp32[(tile * D + d) * kPackTile + key] = cc < C ? Vb[static_cast<size_t>(cc) * D + d] : 0.0f;
+      const int d = idx / kPackTile, pos = idx % kPackTile;
+      const int cc = j * kPackTile + vt_key(pos);
+      Vtp32[(tile * D + d) * kPackTile + pos] = cc < C ? Vb[static_cast<size_t>(cc) * D + d] : 0.0f;
     }
   }
 }

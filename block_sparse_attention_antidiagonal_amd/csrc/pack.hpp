@@ -12,7 +12,9 @@ constexpr int kPackTile = 64;  // keys per packed tile
 //   tile_off  int32 [C + 1]            first tile of each key cluster (shared by all heads)
 //   flags     uint8 [B*Hkv][tiles]     V^T tile format: 1 = float16 / float32, 0 = bfloat16
 //   k         T     [B*Hkv][tiles][64][D]
-//   v         [B*Hkv][tiles][D][64]    16-bit for bfloat16 inputs, float32 for float32 inputs
+//   v         [B*Hkv][tiles][D][64]    16-bit for bfloat16 inputs, float32 for float32 inputs;
+//                                      within each group of 16 keys the positions hold keys
+//                                      0-3, 8-11, 4-7, 12-15
 // Per head, token tiles come first (sum over clusters of ceil(n_c / 64) <= ceil(S/64) + C of
 // them), then ceil(C / 64) centroid tiles starting at first_centroid_tile.
 struct PackLayout {

@@ -99,7 +99,8 @@ bsa_status bsa_centroids(int B, int Hkv, int S, int D, int dtype, const void* K,
  * every key cluster's keys in tiles of 64 (a cluster's last tile zero-filled) in the form
  * bsa_sparse_attention copies into on-chip memory, then the centroid tiles:
  *   K tile    [64 keys][D]  dtype
- *   V^T tile  [D][64 keys]  float32 inputs: float32.  bfloat16 inputs: float16 when every
+ *   V^T tile  [D][64 keys]  (keys of each 16-key group stored in the order 0-3, 8-11, 4-7,
+ *             12-15) float32 inputs: float32.  bfloat16 inputs: float16 when every
  *             value of the tile is below 2^16 in magnitude and some is at least 2^-8, else
  *             bfloat16 (a per-tile flag records which)
  * plus the first tile of every cluster.  The buffer is opaque to callers: its size comes

@@ -82,7 +82,12 @@ def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem):
     kdt = np.uint16 if elem == 2 else np.float32
     kt = buf[off_k: off_k + nt * 64 * D * elem].view(kdt).reshape(B * Hkv, tph, 64, D)
     vt = buf[off_v: off_v + nt * 64 * D * elem].view(kdt).reshape(B * Hkv, tph, D, 64)
-    return tile_off, flags, kt, vt, tok
+    # V^T positions hold the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15
+    pos = np.arange(64)
+    key_at = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)
+    vt_nat = np.empty_like(vt)
+    vt_nat[..., key_at] = vt
+    return tile_off, flags, kt, vt_nat, tok
 
 
 def _as_f16_bits(x):
