@@ -3,7 +3,8 @@
 
 Workload: the Wan-shaped video case -- B=1, 40 heads, S=32760 tokens (a 21x30x52 latent
 grid), D=128, bfloat16, 256 tile-major clusters of 128 tokens (the last holds 120) --
-run through every stage of the path in one call: cluster layout, centroids, antidiagonal
+run through every stage of the path in one call: cluster layout, K/V packing with the
+centroids, antidiagonal
 block scores (block 128, stride 16), per-head top-p masks (tau per head from
 {0.85, 0.90, 0.95}), 64 probe rows (dense and block-sparse), the ridge fit (lambda 0.1,
 rank 16), and the compensated block-sparse attention whose epilogue applies the fitted
@@ -15,15 +16,20 @@ Printed: one JSON line.  ``value`` is the executed-pair throughput of the whole 
 over the measured time per call); ``ms_per_step`` is the time per call.  ``roofline``
 covers the dominant kernel (the sparse attention): its algorithmic flops (4*D per kept
 token pair) over its average launch time, measured with events on the stream it runs on,
-against the bf16 dense MFMA peak.  ``cpu_baseline`` is the float64 CPU oracle timed on a
-bounded sample of the same workload (one head, a subset of query clusters).
+against the bf16 dense MFMA peak; ``traffic`` is the kernel's HBM bytes per launch from the
+rocprofv3 counter summary in profiles/ when that summary was taken on the current kernel
+sources (else null).  ``cpu_baseline`` is the float64 CPU oracle timed on a bounded sample
+of the same workload (one head, a subset of query clusters).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --profile-kernels K   # for rocprofv3: K launches of each kernel alone,
+                                          # then one plain copy of a known size
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -42,6 +48,30 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PROBES, LAMBDA, RANK = 64, 0.1, 16
 WORKLOAD = ("wan_video_21x30x52_S32760_H40_D128_bf16: scored top-p masks + compensated block-sparse "
             "attention + 64-probe ridge repair")
+COPY_BYTES = 1 << 30  # the reference copy for scaling the HBM byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan_S32760_H40_D128_traffic.json")
+KERNEL_SOURCES = ("attention.hip", "pack.hpp", "common.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_antidiagonal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on
+    the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
 
 
 def executed_pairs(res, cfg):
@@ -91,12 +121,45 @@ def cpu_baseline(wl, seconds_hint=20.0):
     }
 
 
+def profile_kernels(bsa, path, cfg, q, k, v, reps):
+    """One path call, then `reps` launches of the pack, the scores and the attention alone,
+    then one plain device copy of COPY_BYTES (reads and writes that many bytes)."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+
+    res = path(q, k, v)
+    torch.cuda.synchronize()
+    kv = api.kv_pack(k, v, res.layout)
+    for i in range(reps):
+        api.kv_pack(k, v, res.layout, kv.buffer)
+        torch.cuda.synchronize()
+        print(f"[profile] pack {i}", flush=True)
+    for i in range(reps):
+        api.antidiagonal_block_scores(q, k, res.layout, cfg.block, cfg.stride,
+                                      cfg.score_scale or 1.0 / math.sqrt(cfg.D), cfg.pool_gqa)
+        torch.cuda.synchronize()
+        print(f"[profile] scores {i}", flush=True)
+    for i in range(reps):
+        api.block_sparse_attention(q, kv, res.layout, res.mask, cfg.compensate, cfg.scale, A=res.A, c=res.c)
+        torch.cuda.synchronize()
+        print(f"[profile] attention {i}", flush=True)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=q.device).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[profile] copy {COPY_BYTES} bytes", flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
+                    help="launch each kernel K times on its own, then one plain copy (for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path runs on a single MI355X (asked for --gpus {args.gpus}). "
@@ -118,6 +181,9 @@ def main() -> int:
     k = torch.from_numpy(wl.k).to(torch.bfloat16).cuda()
     v = torch.from_numpy(wl.v).to(torch.bfloat16).cuda()
     torch.cuda.synchronize()
+
+    if args.profile_kernels:
+        return profile_kernels(bsa, path, cfg, q, k, v, args.profile_kernels)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     res = None
@@ -163,6 +229,7 @@ def main() -> int:
     attn_flops = 4 * D * pairs
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     kv_bytes = 2 * cfg.B * cfg.Hkv * S * D * 2
+    traffic = measured_traffic()
     qk_bytes = cfg.B * (cfg.Hq + cfg.Hkv) * S * D * 2
     score_flops = 2 * cfg.B * cfg.Hq * (math.ceil(S / 128) * 128) ** 2 * D / 16
 
@@ -193,16 +260,16 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel": "sparse_attn_kernel (compensated, correction epilogue)",
             "algorithmic_tflop_per_launch": attn_flops / 1e12,
             "avg_launch_ms": round(attn_ms, 4),
         },
         "stages_ms": {kk: round(vv, 4) for kk, vv in stages_ms.items()},
         "stage_rates": {
-            "centroids_GBps": round(kv_bytes / (stages_ms.get("centroids", float("nan")) * 1e-3) / 1e9, 1),
-            "centroids_hbm_frac": round(kv_bytes / (stages_ms.get("centroids", float("nan")) * 1e-3) / 1e9
-                                        / PEAK_HBM_GBS, 4),
+            # the pack reads K and V once and writes them once as tiles
+            "pack_GBps": round(2 * kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9, 1),
+            "pack_hbm_frac": round(2 * kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_GBps": round(qk_bytes / (stages_ms["scores"] * 1e-3) / 1e9, 1),
             "scores_hbm_frac": round(qk_bytes / (stages_ms["scores"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_TFLOPs": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12, 2),
