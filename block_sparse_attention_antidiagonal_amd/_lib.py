@@ -9,7 +9,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsa.so")
+# The in-tree build; BSA_LIB_PATH may name another build of the same library.
+LIB_PATH = os.environ.get("BSA_LIB_PATH") or os.path.join(_HERE, "libbsa.so")
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_size_p = ctypes.POINTER(ctypes.c_size_t)
@@ -62,6 +63,10 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: its HIP runtime must be the one libbsa.so binds to (loading the library
+    # first would bring in a second runtime whose launches fail).
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "

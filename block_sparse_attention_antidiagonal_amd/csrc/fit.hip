@@ -20,38 +20,81 @@ namespace bsa {
 namespace {
 
 constexpr int kMaxM = 64;
+constexpr int kN = 64;  // Jacobi size: the M x M Gram matrix padded with zero rows
+constexpr int kHalf = kN / 2;
 constexpr int kFitThreads = 256;
+constexpr int kMaxRank = 16;
 
 struct FitSmem {
-  float Y[kMaxM][128 + 1];       // Omega^1/2 X (float32 copy of the float64 values)
-  double G[kMaxM][kMaxM + 1];    // T T^T; later Y Y^T + lambda I and its Cholesky factor
+  float Y[kN][128 + 1];  // raw sparse rows, then Omega^1/2 X (float32 of the float64 values)
   union {
-    float T[kMaxM][128 + 1];     // Omega^1/2 Rc, until T T^T is formed
-    double E[kMaxM][kMaxM + 1];  // eigenvectors of T T^T (columns)
-    double WV[128][17];          // W V_r, once the eigenvectors are consumed
-  } u;
-  double Zr[kMaxM][17];          // U_r Lambda_r^1/2, then (Y Y^T + lambda I)^-1 of it
-  double Vr[16][128 + 1];        // V_r^T
+    float T[kN][128 + 1];          // raw dense rows, then Omega^1/2 Rc
+    double Vr[kMaxRank][128 + 1];  // V_r^T, once T is consumed
+  } t;
+  double G[kN][kN + 1];  // T T^T; later Y Y^T + lambda I and its Cholesky factor
+  union {
+    double E[kN][kN + 1];          // eigenvectors of T T^T (columns)
+    double WV[128][kMaxRank + 1];  // diag(1/sigma) W V_r, once the eigenvectors are consumed
+  } e;
+  double Zr[kN][kMaxRank + 1];  // U_r Lambda_r^1/2, then (Y Y^T + lambda I)^-1 of it
   double mu[128], sig[128], rbar[128];
-  double w[kMaxM], sw[kMaxM];
-  double eval[kMaxM];
-  int order[kMaxM];
-  double rot_c[kMaxM / 2], rot_s[kMaxM / 2];
-  int pair_p[kMaxM / 2], pair_q[kMaxM / 2];
-  double scratch[kFitThreads];
+  double w[kN], sw[kN];
+  double eval[kN];
+  double u[kMaxRank];  // (mu / sigma)^T W V_r
+  double rot_c[kHalf], rot_s[kHalf], rot_t[kHalf];
+  int pair_p[kHalf], pair_q[kHalf];
+  int order[kN];
+  double wave_part[kFitThreads / 64];
   int r_eff;
 };
 
-__device__ double block_sum(double v, double* scratch) {
-  scratch[threadIdx.x] = v;
+// Sum over the workgroup (every thread gets the total).
+__device__ double block_sum(double v, double* part) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();  // earlier readers of `part` are done
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int d = kFitThreads / 2; d > 0; d >>= 1) {
-    if (threadIdx.x < static_cast<unsigned>(d)) scratch[threadIdx.x] += scratch[threadIdx.x + d];
-    __syncthreads();
-  }
-  const double s = scratch[0];
-  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kFitThreads / 64; ++i) s += part[i];
   return s;
+}
+
+// Round-robin pairing of 64 indices: index 0 stays, the other 63 rotate by one each round,
+// so 63 rounds pair every index with every other once.
+__device__ __forceinline__ void round_pair(int k, int round, int& p, int& q) {
+  const int pa = k, pb = kN - 1 - k;
+  p = pa == 0 ? 0 : 1 + (pa - 1 + round) % (kN - 1);
+  q = 1 + (pb - 1 + round) % (kN - 1);
+  if (p > q) {
+    const int tmp = p;
+    p = q;
+    q = tmp;
+  }
+}
+
+// out[i][j] = sum_d X[i][d] X[j][d] over 64 x 64 (rows of X in LDS, float32), float64 sums;
+// each thread owns a 4 x 4 block.
+__device__ __forceinline__ void gram64(const float (*X)[128 + 1], int D, double (*out)[kN + 1], double diag_add) {
+  const int i0 = (threadIdx.x / 16) * 4, j0 = (threadIdx.x % 16) * 4;
+  double acc[4][4] = {};
+  for (int d = 0; d < D; ++d) {
+    double a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = static_cast<double>(X[i0 + r][d]);
+      b[r] = static_cast<double>(X[j0 + r][d]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] += a[r] * b[c];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[i0 + r][j0 + c] = acc[r][c] + (i0 + r == j0 + c ? diag_add : 0.0);
 }
 
 __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __restrict__ Os,
@@ -59,20 +102,24 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
                                                                  const float* __restrict__ weights, int D, int M,
                                                                  float lambda, int rank, float* __restrict__ Aout,
                                                                  float* __restrict__ cout) {
+  static_assert(kFitThreads == 256, "the 4 x 4 blocking assumes 256 threads");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FitSmem& sm = *reinterpret_cast<FitSmem*>(smem_raw);
   const int bh = blockIdx.x;
   const int t = threadIdx.x;
   const float* Osh = Os + static_cast<size_t>(bh) * M * D;
   const float* Odh = Od + static_cast<size_t>(bh) * M * D;
-  // Pad the problem to an even size n for the round-robin Jacobi ordering; padded rows are 0.
-  const int n = (M + 1) & ~1;
 
-  // Normalized weights.
+  // Raw rows into LDS (rows past M are zero), normalized weights.
+  for (int e = t; e < kN * D; e += kFitThreads) {
+    const int m = e / D, d = e % D;
+    sm.Y[m][d] = m < M ? Osh[e] : 0.0f;
+    sm.t.T[m][d] = m < M ? Odh[e] : 0.0f;
+  }
   double wsum_part = 0.0;
   for (int m = t; m < M; m += kFitThreads) wsum_part += static_cast<double>(weights[m]);
-  const double wsum = block_sum(wsum_part, sm.scratch);
-  for (int m = t; m < kMaxM; m += kFitThreads) {
+  const double wsum = block_sum(wsum_part, sm.wave_part);
+  for (int m = t; m < kN; m += kFitThreads) {
     const double wm = m < M ? static_cast<double>(weights[m]) / wsum : 0.0;
     sm.w[m] = wm;
     sm.sw[m] = sqrt(wm);
@@ -82,14 +129,14 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   for (int d = t; d < D; d += kFitThreads) {
     double mu = 0.0, rb = 0.0;
     for (int m = 0; m < M; ++m) {
-      const double x = static_cast<double>(Osh[m * D + d]);
+      const double x = static_cast<double>(sm.Y[m][d]);
       mu += sm.w[m] * x;
-      rb += sm.w[m] * (static_cast<double>(Odh[m * D + d]) - x);
+      rb += sm.w[m] * (static_cast<double>(sm.t.T[m][d]) - x);
     }
     double var = 0.0;
     for (int m = 0; m < M; ++m) {
-      const double x = static_cast<double>(Osh[m * D + d]);
-      var += sm.w[m] * (x - mu) * (x - mu);
+      const double x = static_cast<double>(sm.Y[m][d]) - mu;
+      var += sm.w[m] * x * x;
     }
     double sg = sqrt(var);
     if (sg < 1e-6) sg = 1.0;
@@ -98,189 +145,239 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     sm.rbar[d] = rb;
   }
   __syncthreads();
-  // Y = sqrt(w) (X0 - mu) / sigma,  T = sqrt(w) (R - rbar); rows past M are zero.
-  for (int e = t; e < kMaxM * D; e += kFitThreads) {
+  // Y = sqrt(w) (X0 - mu) / sigma,  T = sqrt(w) (R - rbar), in place; rows past M stay zero.
+  for (int e = t; e < M * D; e += kFitThreads) {
     const int m = e / D, d = e % D;
-    float y = 0.0f, tr = 0.0f;
-    if (m < M) {
-      const double x = static_cast<double>(Osh[m * D + d]);
-      const double rres = static_cast<double>(Odh[m * D + d]) - x;
-      y = static_cast<float>(sm.sw[m] * (x - sm.mu[d]) / sm.sig[d]);
-      tr = static_cast<float>(sm.sw[m] * (rres - sm.rbar[d]));
-    }
-    sm.Y[m][d] = y;
-    sm.u.T[m][d] = tr;
+    const double x = static_cast<double>(sm.Y[m][d]);
+    const double rres = static_cast<double>(sm.t.T[m][d]) - x;
+    sm.Y[m][d] = static_cast<float>(sm.sw[m] * (x - sm.mu[d]) / sm.sig[d]);
+    sm.t.T[m][d] = static_cast<float>(sm.sw[m] * (rres - sm.rbar[d]));
   }
   __syncthreads();
-  // G = T T^T (n x n).
-  for (int e = t; e < n * n; e += kFitThreads) {
-    const int i = e / n, j = e % n;
-    double g = 0.0;
-    for (int d = 0; d < D; ++d) g += static_cast<double>(sm.u.T[i][d]) * sm.u.T[j][d];
-    sm.G[i][j] = g;
-  }
-  __syncthreads();
-  for (int e = t; e < n * n; e += kFitThreads) sm.u.E[e / n][e % n] = (e / n == e % n) ? 1.0 : 0.0;
+  // G = T T^T (64 x 64) and E = I.
+  gram64(sm.t.T, D, sm.G, 0.0);
+  for (int e = t; e < kN * kN; e += kFitThreads) sm.e.E[e / kN][e % kN] = (e / kN == e % kN) ? 1.0 : 0.0;
   __syncthreads();
 
-  // Cyclic Jacobi on G (round-robin pairing of n indices, n/2 disjoint rotations a round).
+  // Cyclic Jacobi.  Each round rotates 32 disjoint index pairs at once: G <- J^T G J is applied
+  // 2 x 2 block by block (block (k, l) = rows of pair k, columns of pair l), E <- E J.
   double fro_part = 0.0;
-  for (int e = t; e < n * n; e += kFitThreads) fro_part += sm.G[e / n][e % n] * sm.G[e / n][e % n];
-  const double fro = sqrt(block_sum(fro_part, sm.scratch));
-  const int half = n / 2;
+  for (int e = t; e < kN * kN; e += kFitThreads) fro_part += sm.G[e / kN][e % kN] * sm.G[e / kN][e % kN];
+  const double fro = sqrt(block_sum(fro_part, sm.wave_part));
+  constexpr int kBlkPer = kHalf * kHalf / kFitThreads;  // 2 x 2 blocks per thread
+  constexpr int kEPer = kHalf * kN / kFitThreads;       // eigenvector pairs per thread
+  const int bl = t % kHalf, ei = t % kN;
   for (int sweep = 0; sweep < 30; ++sweep) {
     double off_part = 0.0;
-    for (int e = t; e < n * n; e += kFitThreads) {
-      const int i = e / n, j = e % n;
+    for (int e = t; e < kN * kN; e += kFitThreads) {
+      const int i = e / kN, j = e % kN;
       if (i != j) off_part += sm.G[i][j] * sm.G[i][j];
     }
-    const double off = sqrt(block_sum(off_part, sm.scratch));
+    const double off = sqrt(block_sum(off_part, sm.wave_part));
     if (!(off > 1e-15 * fro)) break;
-    for (int round = 0; round < n - 1; ++round) {
-      if (t < half) {
-        // Position 0 holds index 0; positions 1..n-1 rotate by one each round.
-        const int pos_a = t, pos_b = n - 1 - t;
-        int p = pos_a == 0 ? 0 : 1 + (pos_a - 1 + round) % (n - 1);
-        int q = pos_b == 0 ? 0 : 1 + (pos_b - 1 + round) % (n - 1);
-        if (p > q) {
-          const int tmp = p;
-          p = q;
-          q = tmp;
-        }
-        const double apq = sm.G[p][q];
-        double c = 1.0, s = 0.0;
+    for (int round = 0; round < kN - 1; ++round) {
+      if (t < kHalf) {
+        int p, q;
+        round_pair(t, round, p, q);
+        const double app = sm.G[p][p], aqq = sm.G[q][q], apq = sm.G[p][q];
+        double c = 1.0, s = 0.0, tt = 0.0;
         if (apq != 0.0) {
-          const double theta = (sm.G[q][q] - sm.G[p][p]) / (2.0 * apq);
-          const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-          c = 1.0 / sqrt(tt * tt + 1.0);
+          // tan of the rotation angle, the smaller root: 2 apq / (d + sign(d) sqrt(d^2 + 4 apq^2)).
+          const double d = aqq - app;
+          const double r = sqrt(d * d + 4.0 * apq * apq);
+          const double den = d >= 0.0 ? d + r : d - r;
+          tt = den != 0.0 ? 2.0 * apq / den : (apq > 0.0 ? 1.0 : -1.0);
+          c = 1.0 / sqrt(1.0 + tt * tt);
           s = tt * c;
         }
         sm.pair_p[t] = p;
         sm.pair_q[t] = q;
         sm.rot_c[t] = c;
         sm.rot_s[t] = s;
+        sm.rot_t[t] = tt;
       }
       __syncthreads();
-      // Columns of G and E: (G J)_ip = c G_ip - s G_iq, (G J)_iq = s G_ip + c G_iq.
-      for (int e = t; e < half * n; e += kFitThreads) {
-        const int k = e / n, i = e % n;
-        const int p = sm.pair_p[k], q = sm.pair_q[k];
-        const double c = sm.rot_c[k], s = sm.rot_s[k];
-        const double gp = sm.G[i][p], gq = sm.G[i][q];
-        sm.G[i][p] = c * gp - s * gq;
-        sm.G[i][q] = s * gp + c * gq;
-        const double ep = sm.u.E[i][p], eq = sm.u.E[i][q];
-        sm.u.E[i][p] = c * ep - s * eq;
-        sm.u.E[i][q] = s * ep + c * eq;
+      const int pl = sm.pair_p[bl], ql = sm.pair_q[bl];
+      const double cl = sm.rot_c[bl], sl = sm.rot_s[bl];
+#pragma unroll
+      for (int it = 0; it < kBlkPer; ++it) {
+        const int k = t / kHalf + it * (kFitThreads / kHalf);
+        const int pk = sm.pair_p[k], qk = sm.pair_q[k];
+        if (k == bl) {  // the rotated pair itself: closed form, off-diagonal exactly 0
+          const double apq = sm.G[pk][qk], tk = sm.rot_t[k];
+          sm.G[pk][pk] -= tk * apq;
+          sm.G[qk][qk] += tk * apq;
+          sm.G[pk][qk] = 0.0;
+          sm.G[qk][pk] = 0.0;
+        } else {
+          const double ck = sm.rot_c[k], sk = sm.rot_s[k];
+          const double b00 = sm.G[pk][pl], b01 = sm.G[pk][ql], b10 = sm.G[qk][pl], b11 = sm.G[qk][ql];
+          const double x00 = b00 * cl - b01 * sl, x01 = b00 * sl + b01 * cl;
+          const double x10 = b10 * cl - b11 * sl, x11 = b10 * sl + b11 * cl;
+          sm.G[pk][pl] = ck * x00 - sk * x10;
+          sm.G[pk][ql] = ck * x01 - sk * x11;
+          sm.G[qk][pl] = sk * x00 + ck * x10;
+          sm.G[qk][ql] = sk * x01 + ck * x11;
+        }
       }
-      __syncthreads();
-      // Rows: (J^T G)_pj = c G_pj - s G_qj, (J^T G)_qj = s G_pj + c G_qj.
-      for (int e = t; e < half * n; e += kFitThreads) {
-        const int k = e / n, j = e % n;
+#pragma unroll
+      for (int it = 0; it < kEPer; ++it) {
+        const int k = t / kN + it * (kFitThreads / kN);
         const int p = sm.pair_p[k], q = sm.pair_q[k];
         const double c = sm.rot_c[k], s = sm.rot_s[k];
-        const double gp = sm.G[p][j], gq = sm.G[q][j];
-        sm.G[p][j] = c * gp - s * gq;
-        sm.G[q][j] = s * gp + c * gq;
+        const double ep = sm.e.E[ei][p], eq = sm.e.E[ei][q];
+        sm.e.E[ei][p] = c * ep - s * eq;
+        sm.e.E[ei][q] = s * ep + c * eq;
       }
       __syncthreads();
     }
   }
-  // Eigenvalues sorted descending; kept directions have eigenvalue > 1e-12 of the largest.
-  if (t == 0) {
-    for (int i = 0; i < n; ++i) {
-      sm.eval[i] = sm.G[i][i];
-      sm.order[i] = i;
+  // Eigenvalues ranked descending (ties by index); kept directions have eigenvalue above
+  // 1e-12 of the largest.
+  if (t < kN) {
+    const double ev = sm.G[t][t];
+    int rk = 0;
+    for (int j = 0; j < kN; ++j) {
+      const double ej = sm.G[j][j];
+      rk += (ej > ev || (ej == ev && j < t)) ? 1 : 0;
     }
-    for (int i = 0; i < n; ++i)
-      for (int j = i + 1; j < n; ++j)
-        if (sm.eval[sm.order[j]] > sm.eval[sm.order[i]]) {
-          const int tmp = sm.order[i];
-          sm.order[i] = sm.order[j];
-          sm.order[j] = tmp;
-        }
+    sm.eval[t] = ev;
+    sm.order[rk] = t;
+  }
+  __syncthreads();
+  if (t == 0) {
     const double emax = sm.eval[sm.order[0]];
     int r_eff = 0;
     if (emax > 0.0)
-      for (int i = 0; i < n && r_eff < rank; ++i)
+      for (int i = 0; i < kN && r_eff < rank; ++i)
         if (sm.eval[sm.order[i]] > 1e-12 * emax) ++r_eff;
     sm.r_eff = r_eff;
   }
   __syncthreads();
   const int r_eff = sm.r_eff;
-  // Zr = U_r Lambda_r^1/2 (M x r);  V_r^T row k = T^T u_k / sqrt(lambda_k), with T
-  // recomputed from the inputs (its LDS copy was overwritten by the eigenvectors).
-  for (int e = t; e < M * r_eff; e += kFitThreads) {
-    const int m = e / r_eff, k = e % r_eff;
-    const int col = sm.order[k];
-    sm.Zr[m][k] = sm.u.E[m][col] * sqrt(sm.eval[col]);
+  // Zr = U_r Lambda_r^1/2 (rows past M are zero);  V_r^T row k = T^T u_k / sqrt(lambda_k),
+  // staged in registers while T is still read, then stored over T.
+  for (int e = t; e < kN * kMaxRank; e += kFitThreads) {
+    const int m = e / kMaxRank, k = e % kMaxRank;
+    double z = 0.0;
+    if (k < r_eff && m < M) {
+      const int col = sm.order[k];
+      z = sm.e.E[m][col] * sqrt(sm.eval[col]);
+    }
+    sm.Zr[m][k] = z;
   }
-  for (int e = t; e < r_eff * D; e += kFitThreads) {
+  constexpr int kVrPer = kMaxRank * 128 / kFitThreads;
+  double vr[kVrPer];
+#pragma unroll
+  for (int i = 0; i < kVrPer; ++i) {
+    const int e = t + i * kFitThreads;
     const int k = e / D, d = e % D;
-    const int col = sm.order[k];
     double v = 0.0;
-    for (int m = 0; m < M; ++m) {
-      const double x = static_cast<double>(Osh[m * D + d]);
-      const double tr = sm.sw[m] * ((static_cast<double>(Odh[m * D + d]) - x) - sm.rbar[d]);
-      v += tr * sm.u.E[m][col];
+    if (k < r_eff) {
+      const int col = sm.order[k];
+      for (int m = 0; m < M; ++m) v += static_cast<double>(sm.t.T[m][d]) * sm.e.E[m][col];
+      v /= sqrt(sm.eval[col]);
     }
-    sm.Vr[k][d] = v / sqrt(sm.eval[col]);
+    vr[i] = v;
+  }
+  // G <- Y Y^T + lambda I over all 64 rows: the zero rows past M give the block sqrt(lambda) I
+  // in the factor, which the zero right-hand sides there leave at zero.
+  gram64(sm.Y, D, sm.G, static_cast<double>(lambda));
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kVrPer; ++i) {
+    const int e = t + i * kFitThreads;
+    const int k = e / D, d = e % D;
+    if (k < kMaxRank) sm.t.Vr[k][d] = vr[i];
+  }
+  // Cholesky, right-looking, one barrier per step: step k subtracts the outer product of the
+  // unscaled column k divided by its pivot; the columns are scaled at the end.  Thread t owns
+  // row t / 4 and the columns congruent to t mod 4.
+  const int ci = t / 4, cj0 = t % 4;
+  for (int k = 0; k < kN - 1; ++k) {
+    if (ci > k) {
+      const double f = sm.G[ci][k] / sm.G[k][k];
+#pragma unroll
+      for (int jj = 0; jj < kN / 4; ++jj) {
+        const int j = cj0 + 4 * jj;
+        if (j > k && j <= ci) sm.G[ci][j] -= f * sm.G[j][k];
+      }
+    }
+    __syncthreads();
+  }
+  // L = column k / sqrt(pivot k) (lower part only; the diagonal becomes sqrt(pivot)).
+  double lrow[kN / 4];
+#pragma unroll
+  for (int jj = 0; jj < kN / 4; ++jj) {
+    const int j = cj0 + 4 * jj;
+    lrow[jj] = j <= ci ? sm.G[ci][j] / sqrt(sm.G[j][j]) : 0.0;
   }
   __syncthreads();
-  // G <- Y Y^T + lambda I (M x M), then its Cholesky factor (lower, right-looking).
-  for (int e = t; e < M * M; e += kFitThreads) {
-    const int i = e / M, j = e % M;
-    double g = 0.0;
-    for (int d = 0; d < D; ++d) g += static_cast<double>(sm.Y[i][d]) * sm.Y[j][d];
-    sm.G[i][j] = g + (i == j ? static_cast<double>(lambda) : 0.0);
+#pragma unroll
+  for (int jj = 0; jj < kN / 4; ++jj) {
+    const int j = cj0 + 4 * jj;
+    if (j <= ci) sm.G[ci][j] = lrow[jj];
   }
   __syncthreads();
-  for (int k = 0; k < M; ++k) {
-    if (t == 0) sm.G[k][k] = sqrt(sm.G[k][k]);
-    __syncthreads();
-    const double dkk = sm.G[k][k];
-    for (int i = k + 1 + t; i < M; i += kFitThreads) sm.G[i][k] /= dkk;
-    __syncthreads();
-    const int rem = M - k - 1;
-    for (int e = t; e < rem * rem; e += kFitThreads) {
-      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
-      if (j <= i) sm.G[i][j] -= sm.G[i][k] * sm.G[j][k];
+  // Solve L y = Zr, then L^T z = y, column by column (one barrier per step): thread t owns
+  // right-hand side t % 16 of rows t / 16 + 16 i.
+  const int rhs = t % kMaxRank, rq = t / kMaxRank;
+  for (int k = 0; k < kN - 1; ++k) {
+    const double yk = sm.Zr[k][rhs] / sm.G[k][k];
+#pragma unroll
+    for (int ii = 0; ii < kN / 16; ++ii) {
+      const int i = rq + 16 * ii;
+      if (i > k) sm.Zr[i][rhs] -= sm.G[i][k] * yk;
     }
     __syncthreads();
   }
-  // Solve (L L^T) z = Zr, one right-hand side per thread.
-  if (t < r_eff) {
-    for (int i = 0; i < M; ++i) {
-      double v = sm.Zr[i][t];
-      for (int j = 0; j < i; ++j) v -= sm.G[i][j] * sm.Zr[j][t];
-      sm.Zr[i][t] = v / sm.G[i][i];
-    }
-    for (int i = M - 1; i >= 0; --i) {
-      double v = sm.Zr[i][t];
-      for (int j = i + 1; j < M; ++j) v -= sm.G[j][i] * sm.Zr[j][t];
-      sm.Zr[i][t] = v / sm.G[i][i];
-    }
+#pragma unroll
+  for (int ii = 0; ii < kN / 16; ++ii) {
+    const int i = rq + 16 * ii;
+    sm.Zr[i][rhs] /= sm.G[i][i];
   }
   __syncthreads();
-  // W V_r = Y^T z (D x r), stored over the eigenvectors (no longer needed).
+  for (int k = kN - 1; k > 0; --k) {
+    const double zk = sm.Zr[k][rhs] / sm.G[k][k];
+#pragma unroll
+    for (int ii = 0; ii < kN / 16; ++ii) {
+      const int i = rq + 16 * ii;
+      if (i < k) sm.Zr[i][rhs] -= sm.G[k][i] * zk;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int ii = 0; ii < kN / 16; ++ii) {
+    const int i = rq + 16 * ii;
+    sm.Zr[i][rhs] /= sm.G[i][i];
+  }
+  __syncthreads();
+  // diag(1/sigma) W V_r = diag(1/sigma) Y^T z (D x r), stored over the eigenvectors.
   for (int e = t; e < D * r_eff; e += kFitThreads) {
     const int d = e / r_eff, k = e % r_eff;
     double v = 0.0;
     for (int m = 0; m < M; ++m) v += static_cast<double>(sm.Y[m][d]) * sm.Zr[m][k];
-    sm.u.WV[d][k] = v;
+    sm.e.WV[d][k] = v / sm.sig[d];
   }
   __syncthreads();
-  // A = diag(1/sigma) (W V_r) V_r^T;  c = rbar - mu A.  One thread per output column j.
+  // u = mu^T diag(1/sigma) W V_r, so that c = rbar - mu A = rbar - u V_r^T.
+  if (t < r_eff) {
+    double v = 0.0;
+    for (int d = 0; d < D; ++d) v += sm.mu[d] * sm.e.WV[d][t];
+    sm.u[t] = v;
+  }
+  __syncthreads();
+  // A = diag(1/sigma) (W V_r) V_r^T: one output element per thread pass, rows coalesced.
   float* Ah = Aout + static_cast<size_t>(bh) * D * D;
+  for (int e = t; e < D * D; e += kFitThreads) {
+    const int i = e / D, j = e % D;
+    double a = 0.0;
+    for (int k = 0; k < r_eff; ++k) a += sm.e.WV[i][k] * sm.t.Vr[k][j];
+    Ah[e] = static_cast<float>(a);
+  }
   for (int j = t; j < D; j += kFitThreads) {
     double cj = sm.rbar[j];
-    for (int i = 0; i < D; ++i) {
-      double a = 0.0;
-      for (int k = 0; k < r_eff; ++k) a += sm.u.WV[i][k] * sm.Vr[k][j];
-      a /= sm.sig[i];
-      Ah[static_cast<size_t>(i) * D + j] = static_cast<float>(a);
-      cj -= sm.mu[i] * a;
-    }
+    for (int k = 0; k < r_eff; ++k) cj -= sm.u[k] * sm.t.Vr[k][j];
     cout[static_cast<size_t>(bh) * D + j] = static_cast<float>(cj);
   }
 }
@@ -389,7 +486,7 @@ extern "C" bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_
   if (M > kMaxM) return BSA_E_UNSUPPORTED;
   if (!(lambda > 0.0f) || !(lambda < INFINITY)) return BSA_E_ARG;
   if (rank < 1 || rank > D) return BSA_E_ARG;
-  if (rank > 16) return BSA_E_UNSUPPORTED;
+  if (rank > kMaxRank) return BSA_E_UNSUPPORTED;
   const int smem = static_cast<int>(sizeof(FitSmem));
   hipFuncSetAttribute(reinterpret_cast<const void*>(probe_fit_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   hipLaunchKernelGGL(probe_fit_kernel, dim3(B * Hq), dim3(kFitThreads), smem, stream, O_sparse_probe, O_dense_probe,
