@@ -258,22 +258,9 @@ struct PaddedLds {
   }
 };
 
-// Unpadded rows with an XOR swizzle of 16-byte chunks (tiles copied from the packed buffer
-// straight into LDS).  Chunk c of row r sits at chunk position c ^ ((r / RP) & MASK), where
-// RP rows share one 256-byte bank line; the 16 lanes of a read then hit 16 distinct chunks.
-// V^T rows hold the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15, so the
-// eight keys one lane needs in a P V step are one contiguous 16 bytes.
-template <int ROWB>
-struct Swz {
-  static constexpr int CPR = ROWB / 16;
-  static constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;
-  static constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
-  static __device__ __forceinline__ int pos(int r, int c) { return c ^ ((r / RP) & MASK); }
-  static __device__ __forceinline__ const uint4* chunk(const void* base, int r, int c) {
-    return reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(base) + r * ROWB + pos(r, c) * 16);
-  }
-};
-
+// Unpadded rows with the XOR chunk swizzle (tiles copied from the packed buffer straight
+// into LDS).  V^T rows hold the keys of each 16-key group in the order 0-3, 8-11, 4-7,
+// 12-15, so the eight keys one lane needs in a P V step are one contiguous 16 bytes.
 template <typename T, int D>
 struct SwzLds {
   static constexpr int KROWB = D * static_cast<int>(sizeof(T));
@@ -599,9 +586,6 @@ struct TileDma {
 #endif
   }
 };
-
-// Wait for this wave's outstanding global memory operations, tile copies included.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Walks the tiles of one workgroup: the centroid tiles (compensation), then the tiles of
 // every kept key cluster in list order.  A cluster's tile count is clamped to the tiles the

@@ -146,6 +146,37 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, workgroups dispatched round-robin
 
+// ------------------------------------------------------------------ swizzled LDS rows
+// Unpadded LDS rows of ROWB bytes with an XOR swizzle of 16-byte chunks: chunk c of row r
+// sits at chunk position c ^ ((r / RP) & MASK), where RP rows share one 256-byte bank line;
+// the 16 lanes of a fragment read then hit 16 distinct chunks.  Tiles land in such rows by
+// direct global-to-LDS copies, each lane fetching the chunk that the swizzle puts in its slot.
+template <int ROWB>
+struct Swz {
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;
+  static constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+  static __device__ __forceinline__ int pos(int r, int c) { return c ^ ((r / RP) & MASK); }
+  static __device__ __forceinline__ const uint4* chunk(const void* base, int r, int c) {
+    return reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(base) + r * ROWB + pos(r, c) * 16);
+  }
+};
+
+// Fragment of 8 consecutive elements starting at element e0 of swizzled row `row`.
+template <typename S>
+__device__ __forceinline__ void swz_frag(Frag<bf16_t>& f, const void* base, int row, int e0) {
+  f.v = __builtin_bit_cast(bf16x8, *S::chunk(base, row, e0 / 8));
+}
+template <typename S>
+__device__ __forceinline__ void swz_frag(Frag<float>& f, const void* base, int row, int e0) {
+  const f32x4 lo = __builtin_bit_cast(f32x4, *S::chunk(base, row, e0 / 4));
+  const f32x4 hi = __builtin_bit_cast(f32x4, *S::chunk(base, row, e0 / 4 + 1));
+  f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Wait for this wave's outstanding global memory operations, tile copies included.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // ------------------------------------------------------------------ host helpers
 inline bsa_status launch_status() {
   hipError_t e = hipGetLastError();

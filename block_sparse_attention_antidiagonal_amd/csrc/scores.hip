@@ -10,99 +10,149 @@
 // The anti-diagonal sum of sub-block (i', j') is the dot product of two length stride*D
 // vectors: strided query row i' lists tokens i'*s+s-1, ..., i'*s (reverse order) and strided
 // key row j' lists tokens j'*s, ..., j'*s+s-1.  So the strided logits are one GEMM with
-// contraction length stride*D, computed here with bf16 MFMA in tiles of 128 x 128 strided
-// rows.  Its epilogue keeps, per strided query row, the tile max, the tile sum of
-// exponentials and the per-block sums relative to that max; a second pass merges the
-// tiles of a row (the full-row softmax), sums the rows of a query block and normalizes.
+// contraction length stride*D, computed here with MFMA in tiles of 256 x 256 strided rows
+// (8 waves of 128 keys x 64 queries), the operands streaming through LDS in stages of one
+// token column (tt) and 128 bytes of head dimension, copied straight from global memory
+// (gathered through the cluster order) into XOR-swizzled LDS rows, two stages in flight.
+// Its epilogue keeps, per strided query row, the tile max, the tile sum of exponentials and
+// the per-block sums relative to that max; a second pass merges the tiles of a row (the
+// full-row softmax), sums the rows of a query block and normalizes.
 // Workspace: part[bh][key block][strided row], mstat/lstat[bh][key tile][strided row].
 #include "common.hpp"
 
 namespace bsa {
 namespace {
 
-constexpr int kTile = 128;  // strided rows per tile side
-constexpr int kKC = 64;     // contraction elements per LDS stage
+constexpr int kTile = 256;      // strided rows per tile side
+constexpr int kSThreads = 512;  // 8 waves: 2 (keys) x 4 (queries)
+constexpr int kRowB = 128;      // bytes of one strided row per stage
+using SRow = Swz<kRowB>;
 
 template <typename T>
-struct SCfg {
+struct SStage {
+  static constexpr int KCE = kRowB / static_cast<int>(sizeof(T));  // elements per row per stage
+  static constexpr int KS = KCE / 16;                              // 16-wide MFMA steps per stage
+  static constexpr int OP_BYTES = kTile * kRowB;                   // one operand of a stage
+  static constexpr int BUF_BYTES = 2 * OP_BYTES;                   // keys + queries
+  static constexpr int NCH = OP_BYTES / 16 / kSThreads;            // 16-byte chunks per thread per operand
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
-  static constexpr int CPR = kKC / EPC;  // 16-byte chunks per stage row
-  static constexpr int ROW = kKC + EPC;  // padded LDS row (elements)
-  static constexpr int ELEMS = kTile * ROW;
+  static constexpr int LDS_BYTES = 2 * BUF_BYTES + 2 * kTile * 4;  // two stages + row reductions
 };
 
-// S^T tile: keys (A operand) x queries (B operand).  Wave w: keys 64*(w/2).., queries 64*(w%2)..
+// S^T tile: keys (A operand) x queries (B operand).  Wave w: keys 128*(w/4).., queries 64*(w%4)..
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                             const int32_t* __restrict__ perm, int Hq, int Hkv,
-                                                             int S, int stride, int Ns, int nb, int ntk, float c2,
-                                                             float* __restrict__ part, float* __restrict__ mstat,
-                                                             float* __restrict__ lstat) {
-  using C = SCfg<T>;
-  __shared__ __align__(16) T As[C::ELEMS];
-  __shared__ __align__(16) T Bs[C::ELEMS];
-  __shared__ float red[2][kTile];
+__global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                                   const int32_t* __restrict__ perm, int Hq, int Hkv,
+                                                                   int S, int stride, int Ns, int nb, int ntk, float c2,
+                                                                   float* __restrict__ part, float* __restrict__ mstat,
+                                                                   float* __restrict__ lstat) {
+  using C = SStage<T>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem + 2 * C::BUF_BYTES);  // [2][kTile]
   const int kt = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
-  const T* Qh = Q + static_cast<size_t>(bh) * S * D;
-  const T* Kh = K + (static_cast<size_t>(b) * Hkv + kvh) * S * D;
+  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(Q + static_cast<size_t>(bh) * S * D);
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (static_cast<size_t>(b) * Hkv + kvh) * S * D);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
-  const int kw = wave >> 1, qw = wave & 1;
-  f32x16 acc[2][2];
+  const int kw = wave >> 2, qw = wave & 3;
+
+  // This thread's copy slots: chunk j of each operand is LDS slot (8 j + wave) * 64 + lane,
+  // i.e. row slot / 8 and swizzled chunk position slot % 8 of that row.
+  int srow[C::NCH], scol[C::NCH];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < C::NCH; ++j) {
+    const int slot = (j * 8 + wave) * 64 + lane;
+    srow[j] = slot / SRow::CPR;
+    scol[j] = SRow::pos(srow[j], slot % SRow::CPR);  // the global chunk that lands in this slot
+  }
+  // Token of every slot row for one token column tt (-1: padding, contributes zeros).
+  auto tokens = [&](int tt, int* ktok, int* qtok) {
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int jk = kt * kTile + srow[j], iq = qt * kTile + srow[j];
+      const int pk = jk * stride + tt, pq = iq * stride + stride - 1 - tt;
+      ktok[j] = (jk < Ns && pk < S) ? (perm ? perm[pk] : pk) : -1;
+      qtok[j] = (iq < Ns && pq < S) ? (perm ? perm[pq] : pq) : -1;
+    }
+  };
+  auto issue = [&](int buf, int dc, const int* ktok, const int* qtok) {
+    unsigned char* As = smem + buf * C::BUF_BYTES;
+    unsigned char* Bs = As + C::OP_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int slot_base = (j * 8 + wave) * 64;
+      const size_t off = static_cast<size_t>(dc) * sizeof(T) + scol[j] * 16;
+      if (ktok[j] >= 0)
+        __builtin_amdgcn_global_load_lds(Kh + static_cast<size_t>(ktok[j]) * D * sizeof(T) + off,
+                                         As + slot_base * 16, 16, 0, 0);
+      else
+        *reinterpret_cast<uint4*>(As + (slot_base + lane) * 16) = make_uint4(0, 0, 0, 0);
+      if (qtok[j] >= 0)
+        __builtin_amdgcn_global_load_lds(Qh + static_cast<size_t>(qtok[j]) * D * sizeof(T) + off,
+                                         Bs + slot_base * 16, 16, 0, 0);
+      else
+        *reinterpret_cast<uint4*>(Bs + (slot_base + lane) * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  for (int tt = 0; tt < stride; ++tt) {
-    for (int dc = 0; dc < D; dc += kKC) {
-      // Stage rows: key strided row j' takes token j'*s + tt; query row i' takes i'*s + s-1-tt.
+  constexpr int kDC = D / C::KCE;  // stages per token column
+  const int nst = stride * kDC;
+  int ktok[C::NCH], qtok[C::NCH], nktok[C::NCH], nqtok[C::NCH];
+  tokens(0, ktok, qtok);
+  if (stride > 1) tokens(1, nktok, nqtok);
+  issue(0, 0, ktok, qtok);
+  wait_vmem();
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const int nx = st + 1;
+    if (nx < nst) {
+      const int tt = nx / kDC, dc = (nx % kDC) * C::KCE;
+      if (dc == 0) {  // a new token column: its tokens were fetched one column ahead
 #pragma unroll
-      for (int i = 0; i < kTile * C::CPR / 256; ++i) {
-        const int idx = t + i * 256;
-        const int row = idx / C::CPR, ch = idx % C::CPR;
-        const int jk = kt * kTile + row, iq = qt * kTile + row;
-        const int pk = jk * stride + tt, pq = iq * stride + stride - 1 - tt;
-        uint4 vk = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
-        if (jk < Ns && pk < S) {
-          const int tok = perm ? perm[pk] : pk;
-          vk = *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(tok) * D + dc + ch * C::EPC);
+        for (int j = 0; j < C::NCH; ++j) {
+          ktok[j] = nktok[j];
+          qtok[j] = nqtok[j];
         }
-        if (iq < Ns && pq < S) {
-          const int tok = perm ? perm[pq] : pq;
-          vq = *reinterpret_cast<const uint4*>(Qh + static_cast<size_t>(tok) * D + dc + ch * C::EPC);
-        }
-        *reinterpret_cast<uint4*>(As + row * C::ROW + ch * C::EPC) = vk;
-        *reinterpret_cast<uint4*>(Bs + row * C::ROW + ch * C::EPC) = vq;
+        if (tt + 1 < stride) tokens(tt + 1, nktok, nqtok);
       }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < kKC / 16; ++ks) {
-        Frag<T> fa[2], fb[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) load_frag(fa[m], As + (kw * 64 + m * 32 + r) * C::ROW + ks * 16 + 8 * h);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) load_frag(fb[n], Bs + (qw * 64 + n * 32 + r) * C::ROW + ks * 16 + 8 * h);
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
-      }
-      __syncthreads();
+      issue(buf ^ 1, dc, ktok, qtok);
     }
+    const unsigned char* As = smem + buf * C::BUF_BYTES;
+    const unsigned char* Bs = As + C::OP_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      Frag<T> fa[4], fb[2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) swz_frag<SRow>(fa[m], As, kw * 128 + m * 32 + r, ks * 16 + 8 * h);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) swz_frag<SRow>(fb[n], Bs, qw * 64 + n * 32 + r, ks * 16 + 8 * h);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
+    }
+    wait_vmem();
+    __syncthreads();
   }
 
-  // Epilogue.  acc[m][n][j]: key kt*128 + kw*64 + m*32 + 8*(j/4) + 4*h + j%4,
-  //                          query qt*128 + qw*64 + n*32 + r.
+  // Epilogue.  acc[m][n][j]: key kt*256 + kw*128 + m*32 + 8*(j/4) + 4*h + j%4,
+  //                          query qt*256 + qw*64 + n*32 + r.
   float mx[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     float v = -INFINITY;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = kt * kTile + kw * 64 + m * 32 + 8 * (j / 4) + 4 * h + (j % 4);
+        const int key = kt * kTile + kw * 128 + m * 32 + 8 * (j / 4) + 4 * h + (j % 4);
         const float y = key < Ns ? acc[m][n][j] * c2 : -INFINITY;
         acc[m][n][j] = y;
         v = fmaxf(v, y);
@@ -112,17 +162,20 @@ __global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict_
   }
   if (h == 0) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) red[kw][qw * 64 + n * 32 + r] = mx[n];
+    for (int n = 0; n < 2; ++n) red[kw * kTile + qw * 64 + n * 32 + r] = mx[n];
   }
   __syncthreads();
 #pragma unroll
-  for (int n = 0; n < 2; ++n) mx[n] = fmaxf(red[0][qw * 64 + n * 32 + r], red[1][qw * 64 + n * 32 + r]);
+  for (int n = 0; n < 2; ++n) {
+    const int ql = qw * 64 + n * 32 + r;
+    mx[n] = fmaxf(red[ql], red[kTile + ql]);
+  }
   __syncthreads();
   float ls[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float e = fast_exp2(acc[m][n][j] - mx[n]);
@@ -135,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict_
   for (int n = 0; n < 2; ++n) {
     const int query = qt * kTile + qw * 64 + n * 32 + r;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int kbase = kt * kTile + kw * 64 + m * 32;  // first key of this 32-key group
+    for (int m = 0; m < 4; ++m) {
+      const int kbase = kt * kTile + kw * 128 + m * 32;  // first key of this 32-key group
       if constexpr (R <= 4) {
         // Blocks lie inside one lane's 4-key runs.
 #pragma unroll
@@ -169,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict_
   }
   if (h == 0) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) red[kw][qw * 64 + n * 32 + r] = ls[n];
+    for (int n = 0; n < 2; ++n) red[kw * kTile + qw * 64 + n * 32 + r] = ls[n];
   }
   __syncthreads();
   if (kw == 0 && h == 0) {
@@ -180,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void score_gemm_kernel(const T* __restrict_
       if (query < Ns) {
         const size_t s_idx = (static_cast<size_t>(bh) * ntk + kt) * Ns + query;
         mstat[s_idx] = mx[n];
-        lstat[s_idx] = red[0][ql] + red[1][ql];
+        lstat[s_idx] = red[ql] + red[kTile + ql];
       }
     }
   }
@@ -273,7 +326,10 @@ void launch_scores(int B, int Hq, int Hkv, int S, const void* Q, const void* K, 
   float* part = static_cast<float*>(ws);
   float* mstat = part + static_cast<size_t>(B) * Hq * sd.nb * sd.Ns;
   float* lstat = mstat + static_cast<size_t>(B) * Hq * sd.ntk * sd.Ns;
-  hipLaunchKernelGGL((score_gemm_kernel<T, D, R>), dim3(sd.ntk, sd.ntk, B * Hq), dim3(256), 0, stream,
+  auto kern = score_gemm_kernel<T, D, R>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      SStage<T>::LDS_BYTES);
+  hipLaunchKernelGGL(kern, dim3(sd.ntk, sd.ntk, B * Hq), dim3(kSThreads), SStage<T>::LDS_BYTES, stream,
                      static_cast<const T*>(Q), static_cast<const T*>(K), perm, Hq, Hkv, S, stride, sd.Ns, sd.nb, sd.ntk,
                      score_scale * kLog2e, part, mstat, lstat);
   const int Hs = pool_gqa ? Hkv : Hq;

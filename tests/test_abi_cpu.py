@@ -142,7 +142,7 @@ def test_workspace_sizes(lib):
     from block_sparse_attention_antidiagonal_amd import _lib
 
     assert _lib.size_query("bsa_cluster_layout_workspace_size", 32760, 256) == 32 * 256 * 4
-    nb, ns, ntk = 256, 2048, 16
+    nb, ns, ntk = 256, 2048, 8  # key tiles of 256 strided rows
     assert _lib.size_query("bsa_antidiag_scores_workspace_size", 1, 40, 40, 32760, 128, 128, 16) == \
         40 * ns * (nb + 2 * ntk) * 4
     assert _lib.size_query("bsa_probe_attention_workspace_size", 1, 40, 32760, 128, 64) == 40 * 17 * 64 * 130 * 4

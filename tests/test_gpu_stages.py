@@ -202,6 +202,8 @@ def test_mask_lists(bsa):
         (777, 128, 64, 16, "bf16", 2, 2, False),     # R = 4
         (900, 64, 32, 16, "bf16", 1, 1, True),       # R = 2
         (3000, 128, 256, 16, "bf16", 1, 1, False),   # R = 16
+        (10000, 128, 128, 16, "bf16", 2, 1, True),   # three 256-row tiles of strided rows, ragged
+        (9000, 64, 64, 4, "f32", 1, 1, True),        # stride 4: nine tiles, float32
     ],
 )
 def test_antidiagonal_scores_and_mask(bsa, S, D, block, stride, dtype, Hq, Hkv, shuffle):
