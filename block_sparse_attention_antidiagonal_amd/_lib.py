@@ -31,9 +31,10 @@ SIGNATURES = {
     "bsa_kv_pack_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_kv_pack": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                     c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_sparse_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_int,
                              c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
-                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,

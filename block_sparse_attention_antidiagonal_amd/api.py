@@ -191,7 +191,7 @@ def mask_from_keep(keep: torch.Tensor) -> BlockMask:
 def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
                            compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
                            out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
-                           c: Optional[torch.Tensor] = None):
+                           c: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Block-sparse attention over packed K/V; compensated by the skipped clusters'
     centroids, or hard drop with compensate=False; with A, c every output row o becomes
     o + o A + c before rounding (bsa_sparse_attention)."""
@@ -206,11 +206,22 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
         raise ValueError("mask shape does not match batch / cluster counts")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = _lib.size_query("bsa_sparse_attention_workspace_size", B, Hq, mask.Hm, q_layout.C, S, Ck)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
     _lib.call("bsa_sparse_attention", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
               _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
               _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
-              int(bool(compensate)), _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _stream())
+              int(bool(compensate)), _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+              _stream())
     return (o, lse) if return_lse else o
+
+
+def attention_workspace(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask) -> torch.Tensor:
+    """Workspace for block_sparse_attention (the mask rows' tile lists), for reuse across calls."""
+    B, Hq, S, _ = q.shape
+    nbytes = _lib.size_query("bsa_sparse_attention_workspace_size", B, Hq, mask.Hm, q_layout.C, S, kv.layout.C)
+    return _workspace(nbytes, q.device)
 
 
 def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: ClusterLayout, mask: BlockMask,

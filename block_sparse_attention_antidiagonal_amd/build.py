@@ -3,7 +3,9 @@
     python block_sparse_attention_antidiagonal_amd/build.py
 
 Every HIP source is compiled with hipcc for gfx950 only; the host helpers are plain C++.
-Packed fp32 instruction selection is disabled for all device code.
+Packed fp32 instruction selection is disabled for all device code.  Device code is compiled
+assuming no NaN operands (inputs are finite; the kernels produce -inf but never NaN), which
+lets max/min skip NaN quieting.
 """
 
 from __future__ import annotations
@@ -31,6 +33,9 @@ HIP_FLAGS = [
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Device code assumes no NaN inputs (max/min skip NaN quieting); host validation keeps
+    # full IEEE semantics.
+    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

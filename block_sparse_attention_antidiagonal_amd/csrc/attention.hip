@@ -305,36 +305,50 @@ struct KeyBias {  // one bias per key from LDS (centroid columns: log2 n_c or -i
   __device__ float operator()(int key) const { return bias[key]; }
 };
 
-// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// qf: this wave's Q fragments; c2 = scale * log2(e); keys at or past `nvalid` do not exist.
-// pv16: for bfloat16 inputs the tile's V^T in LDS is float16 and P is rounded to float16
-// (else both are bfloat16).  Bias, nvalid and pv16 are uniform over the workgroup, so the
-// branches on them cost no divergence and the tile step is instantiated once per call site.
-template <typename T, int D, typename Lds, typename Bias>
-__device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
-                                          const Bias& bias, int nvalid, bool pv16) {
+// One 64-key tile for one wave, in three parts: S^T = K Q^T (tile_qk), the online softmax
+// (tile_softmax) and O^T += V^T P^T (tile_pv).  qf: this wave's Q fragments; c2 = scale *
+// log2(e); keys at or past `nvalid` do not exist.  pv16: for bfloat16 inputs the tile's V^T in
+// LDS is float16 and P is rounded to float16 (else both are bfloat16).  Bias, nvalid and pv16
+// are uniform over the workgroup, so the branches on them cost no divergence.
+template <typename T, int D, typename Lds>
+__device__ __forceinline__ void tile_qk(const T* Ks, const Frag<T>* qf, f32x16& s0, f32x16& s1) {
   using C = Cfg<T, D>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
-  f32x16 s0 = {}, s1 = {};
+  s0 = f32x16{};
+  s1 = f32x16{};
+  // The fragments of step kk+1 are read while step kk's products run.
+  Frag<T> a0[2], a1[2];
+  Lds::kfrag(a0[0], Ks, r, 0, h);
+  Lds::kfrag(a1[0], Ks, 32 + r, 0, h);
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk) {
-    Frag<T> a0, a1;
-    Lds::kfrag(a0, Ks, r, kk, h);
-    Lds::kfrag(a1, Ks, 32 + r, kk, h);
-    s0 = mma(a0, qf[kk], s0);
-    s1 = mma(a1, qf[kk], s1);
+    if (kk + 1 < C::KK) {
+      Lds::kfrag(a0[(kk + 1) & 1], Ks, r, kk + 1, h);
+      Lds::kfrag(a1[(kk + 1) & 1], Ks, 32 + r, kk + 1, h);
+    }
+    s0 = mma(a0[kk & 1], qf[kk], s0);
+    s1 = mma(a1[kk & 1], qf[kk], s1);
   }
-  // Logits in log2 units.  Key of s_mt[j]: mt*32 + 8*(j/4) + 4*h + j%4.  Without a bias the
-  // max is taken on the raw products (c2 > 0) and the scale folds into the exponent's FMA.
-  float x[32];
+}
+
+// Online softmax of one tile's logits (s0, s1 in, P out in x[32], log2 units).  Key of x[j]:
+// (j/16)*32 + 8*((j%16)/4) + 4*h + j%4.  Without a bias the max is taken on the raw products
+// (c2 > 0) and the scale folds into the exponent's FMA.  The running max may lag the true
+// max by up to kRescaleSlack, so P <= 2^kRescaleSlack; O and l are rescaled only when a row
+// exceeds that (a wave-uniform branch, rarely taken after the first tiles).
+template <typename T, int D, typename Bias>
+__device__ __forceinline__ void tile_softmax(const f32x16& s0, const f32x16& s1, float* x, RowState<D>& st,
+                                             float c2, const Bias& bias, int nvalid) {
+  using C = Cfg<T, D>;
+  const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     x[j] = s0[j];
     x[16 + j] = s1[j];
   }
   float xs = c2;  // scale still to apply to x
-  if (bias.active()) {
+  if (__builtin_expect(bias.active(), 0)) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -342,19 +356,20 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
         x[mt * 16 + j] = x[mt * 16 + j] * c2 + bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
     xs = 1.0f;
   }
-  if (nvalid < kNK) {  // ragged last tile of a cluster (uniform branch)
+  if (__builtin_expect(nvalid < kNK, 0)) {  // ragged last tile of a cluster
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (mt * 32 + 8 * (j / 4) + 4 * h + (j % 4) >= nvalid) x[mt * 16 + j] = -INFINITY;
   }
-  float mx = fmaxf(x[0], x[1]);
+  // Tree reductions keep the dependency chains short.
+  float t8[8];
 #pragma unroll
-  for (int j = 2; j < 32; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+  for (int i = 0; i < 8; ++i) t8[i] = fmaxf(fmaxf(x[4 * i], x[4 * i + 1]), fmaxf(x[4 * i + 2], x[4 * i + 3]));
+  float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])), fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
   mx = fmaxf(mx, swap_halves(mx)) * xs;
-  // Raise the running max only when a row exceeds it by the slack (wave-uniform branch).
-  if (__ballot(mx > st.m + kRescaleSlack) != 0) {
+  if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0, 0)) {
     const float m_new = fmaxf(st.m, mx);
     const float alpha = (st.m == -INFINITY) ? 0.0f : fast_exp2(st.m - m_new);
     st.m = m_new;
@@ -365,26 +380,34 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
       for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
   }
   const float m_use = st.m == -INFINITY ? 0.0f : st.m;
-  float lsum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    x[j] = fast_exp2(__builtin_fmaf(x[j], xs, -m_use));
-    lsum += x[j];
-  }
-  st.l += lsum;
-  // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
-  // ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
-  if (sizeof(T) == 2 && pv16) {
+  for (int j = 0; j < 32; ++j) x[j] = fast_exp2(__builtin_fmaf(x[j], xs, -m_use));
+  float s8[8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      Frag16 pb;
-      frag16_from_f32(pb, x + ks * 8);
+  for (int i = 0; i < 8; ++i) s8[i] = (x[4 * i] + x[4 * i + 1]) + (x[4 * i + 2] + x[4 * i + 3]);
+  st.l += ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+}
+
+// O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
+// ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
+template <typename T, int D, typename Lds>
+__device__ __forceinline__ void tile_pv(const T* Vt, const float* x, RowState<D>& st, bool pv16) {
+  using C = Cfg<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31;
+  const int h = lane >> 5;
+  if (sizeof(T) == 2 && __builtin_expect(pv16, 1)) {
+    // Fragment n = ks * DT + dt; fragment n+1 is read while product n runs.
+    constexpr int NF = 4 * C::DT;
+    Frag16 va[2];
+    Lds::vfrag16(va[0], Vt, r, 0, h);
+    Frag16 pb;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        Frag16 va;
-        Lds::vfrag16(va, Vt, dt * 32 + r, ks, h);
-        st.o[dt] = mma(va, pb, st.o[dt]);
-      }
+    for (int n = 0; n < NF; ++n) {
+      const int ks = n / C::DT, dt = n % C::DT;
+      if (n + 1 < NF) Lds::vfrag16(va[(n + 1) & 1], Vt, ((n + 1) % C::DT) * 32 + r, (n + 1) / C::DT, h);
+      if (dt == 0) frag16_from_f32(pb, x + ks * 8);
+      st.o[dt] = mma(va[n & 1], pb, st.o[dt]);
     }
   } else {
 #pragma unroll
@@ -399,6 +422,16 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
       }
     }
   }
+}
+
+template <typename T, int D, typename Lds, typename Bias>
+__device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
+                                          const Bias& bias, int nvalid, bool pv16) {
+  f32x16 s0, s1;
+  float x[32];
+  tile_qk<T, D, Lds>(Ks, qf, s0, s1);
+  tile_softmax<T, D>(s0, s1, x, st, c2, bias, nvalid);
+  tile_pv<T, D, Lds>(Vt, x, st, pv16);
 }
 
 template <typename T, int D>
@@ -416,25 +449,13 @@ __device__ __forceinline__ void init_state(RowState<D>& st) {
   st.l = 0.0f;
 }
 
-// Workgroup -> (kv unit, query cluster, head-in-group).  Workgroups are dispatched to the
-// 8 XCDs round-robin by linear id; consecutive K/V heads are kept on one XCD and the query
-// heads sharing a K/V head (and a mask) run back to back, so their key tiles hit that
-// XCD's L2.
-__device__ __forceinline__ void decode_block(int n_units, int Cq, int G, int& unit, int& a, int& g) {
-  const int i = blockIdx.x;
-  const int per_unit = Cq * G;
-  int s;
-  if (n_units % kXcds == 0) {
-    const int x = i % kXcds;
-    s = i / kXcds;
-    unit = x * (n_units / kXcds) + s / per_unit;
-  } else {
-    s = i;
-    unit = s / per_unit;
-  }
-  const int rem = s % per_unit;
-  a = rem / G;
-  g = rem % G;
+// Work unit -> (batch x K/V head, query cluster, head in group): unit = ((b Hkv + kvh) Cq + a) G + g,
+// so the query heads that share a K/V head (and a mask) are adjacent.
+__device__ __forceinline__ void decode_unit(int u, int Cq, int G, int& bk, int& a, int& g) {
+  g = u % G;
+  const int r = u / G;
+  a = r % Cq;
+  bk = r / Cq;
 }
 
 // ----------------------------------------------------------------- correction epilogue
@@ -450,9 +471,13 @@ __device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __
                                                 const float* __restrict__ ch, unsigned char* smem) {
   constexpr int ROWA = D + 4;
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16{};
   if constexpr (sizeof(T) == 2) {
     bf16_t* AtH = reinterpret_cast<bf16_t*>(smem);
     bf16_t* AtL = AtH + D * ROWA;
+    float* cs = reinterpret_cast<float*>(AtL + D * ROWA);
     // 4 x 4 blocks: four coalesced float4 row loads, transposed in registers, written as
     // 8-byte runs of A^T rows (high and low bfloat16 parts).
     constexpr int kBlk = (D / 4) * (D / 4);
@@ -477,61 +502,67 @@ __device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __
             make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
       }
     }
+    for (int d = threadIdx.x; d < D; d += kThreads) cs[d] = ch[d];
     __syncthreads();
-    Frag<bf16_t> oh[D / 16], ol[D / 16];
+    // O fragments are split into high and low bfloat16 parts as they are consumed.
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < D / 16; ++kk) {
+      Frag<bf16_t> oh, ol;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = st.o[kk / 2][(kk % 2) * 8 + e];
         const __bf16 hi = static_cast<__bf16>(x);
-        oh[kk].v[e] = hi;
-        ol[kk].v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+        oh.v[e] = hi;
+        ol.v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
       }
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+      for (int mt = 0; mt < D / 32; ++mt) {
         Frag<bf16_t> ahf, alf;
         load_frag_split(ahf, AtH + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
         load_frag_split(alf, AtL + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
-        acc = mma(ahf, oh[kk], acc);
-        acc = mma(ahf, ol[kk], acc);
-        acc = mma(alf, oh[kk], acc);
+        acc[mt] = mma(ahf, oh, acc[mt]);
+        acc[mt] = mma(ahf, ol, acc[mt]);
+        acc[mt] = mma(alf, oh, acc[mt]);
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[j] + ch[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
+      // Keep the scheduler from hoisting later steps' LDS reads (it would run out of
+      // registers and spill).
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[mt][j] + cs[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
   } else {
     float* At = reinterpret_cast<float*>(smem);
+    float* cs = At + D * ROWA;
 #pragma unroll 2
     for (int e = threadIdx.x; e < D * D; e += kThreads) At[(e % D) * ROWA + e / D] = Ah[e];
+    for (int d = threadIdx.x; d < D; d += kThreads) cs[d] = ch[d];
     __syncthreads();
-    Frag<float> of[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < D / 16; ++kk) {
+      Frag<float> of;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) of[kk].v[e] = st.o[kk / 2][(kk % 2) * 8 + e];
+      for (int e = 0; e < 8; ++e) of.v[e] = st.o[kk / 2][(kk % 2) * 8 + e];
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+      for (int mt = 0; mt < D / 32; ++mt) {
         Frag<float> af;
         load_frag_split(af, At + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
-        acc = mma(af, of[kk], acc);
+        acc[mt] = mma(af, of, acc[mt]);
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[j] + ch[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[mt][j] + cs[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
   }
   __syncthreads();
 }
 
 template <typename T, int D>
 constexpr int repair_lds_bytes() {
-  return (sizeof(T) == 2 ? 2 * D * (D + 4) * 2 : D * (D + 4) * 4);
+  return (sizeof(T) == 2 ? 2 * D * (D + 4) * 2 : D * (D + 4) * 4) + D * 4;  // A^T parts + c
 }
 
 template <typename T, int D, bool REPAIR>
@@ -554,102 +585,172 @@ struct TileDma {
   static constexpr int NK = S::K_BYTES / 16 / kThreads;  // K chunks per thread
   static constexpr int NV = S::V_BYTES / 16 / kThreads;  // V^T chunks per thread
   static_assert(S::K_BYTES % (16 * kThreads) == 0 && S::V_BYTES % (16 * kThreads) == 0, "tile split");
-  int koff[NK];
-  int voff[NV];
+  // Copy j of a thread fills LDS slot (4 j + wave) * 64 + lane.  Successive copies are 4 KB
+  // apart in both LDS and global memory: they move whole rows (16 rows of 256 B, 32 of 128 B
+  // ...), and the swizzle pattern repeats every 16 rows, so one per-lane offset serves all.
+  static constexpr int kStep = kThreads * 16;
+  // Whether the swizzle of a row repeats kStep bytes further on (else each copy computes its
+  // own offset).
+  template <typename W>
+  static constexpr bool repeats() {
+    return ((kThreads / W::CPR) / W::RP) % (W::MASK + 1) == 0;
+  }
+  template <typename W, int ROWB>
+  static __device__ __forceinline__ int offset(int j) {
+    const int slot = (j * 4 + (static_cast<int>(threadIdx.x) >> 6)) * 64 + (threadIdx.x & 63);
+    const int r = slot / W::CPR;
+    return r * ROWB + W::pos(r, slot % W::CPR) * 16;
+  }
+  int koff, voff;
   __device__ __forceinline__ void init() {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int slot = wave * 64 + lane;
+    const int rk = slot / S::SK::CPR, rv = slot / S::SV::CPR;
+    koff = rk * S::KROWB + S::SK::pos(rk, slot % S::SK::CPR) * 16;
+    voff = rv * S::VROWB + S::SV::pos(rv, slot % S::SV::CPR) * 16;
+  }
+  // Start copying a K tile (gk) into LDS at Ks, or a V^T tile (gv) into LDS at Vt.
+  __device__ __forceinline__ void issue_k(const unsigned char* gk, T* Ks) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's launch stub
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    unsigned char* lk = reinterpret_cast<unsigned char*>(Ks) + wave * 1024;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const int slot = (j * 4 + wave) * 64 + lane;
-      const int r = slot / S::SK::CPR, p = slot % S::SK::CPR;
-      koff[j] = r * S::KROWB + S::SK::pos(r, p) * 16;
+      const int off = repeats<typename S::SK>() ? j * kStep + koff : offset<typename S::SK, S::KROWB>(j);
+      __builtin_amdgcn_global_load_lds(gk + off, lk + j * kStep, 16, 0, 0);
     }
+#endif
+  }
+  __device__ __forceinline__ void issue_v(const unsigned char* gv, T* Vt) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    unsigned char* lv = reinterpret_cast<unsigned char*>(Vt) + wave * 1024;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int slot = (j * 4 + wave) * 64 + lane;
-      const int r = slot / S::SV::CPR, p = slot % S::SV::CPR;
-      voff[j] = r * S::VROWB + S::SV::pos(r, p) * 16;
+      const int off = repeats<typename S::SV>() ? j * kStep + voff : offset<typename S::SV, S::VROWB>(j);
+      __builtin_amdgcn_global_load_lds(gv + off, lv + j * kStep, 16, 0, 0);
     }
-  }
-  // Start copying the tile at gk (K) / gv (V^T) into LDS at Ks / Vt.
-  __device__ __forceinline__ void issue(const unsigned char* gk, const unsigned char* gv, T* Ks, T* Vt) const {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's launch stub
-    const int wave = threadIdx.x >> 6;
-    unsigned char* lk = reinterpret_cast<unsigned char*>(Ks);
-    unsigned char* lv = reinterpret_cast<unsigned char*>(Vt);
-#pragma unroll
-    for (int j = 0; j < NK; ++j)
-      __builtin_amdgcn_global_load_lds(gk + koff[j], lk + (j * 4 + wave) * 1024, 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-      __builtin_amdgcn_global_load_lds(gv + voff[j], lv + (j * 4 + wave) * 1024, 16, 0, 0);
 #endif
   }
 };
 
-// Walks the tiles of one workgroup: the centroid tiles (compensation), then the tiles of
-// every kept key cluster in list order.  A cluster's tile count is clamped to the tiles the
-// packed buffer gives it, so keys past it are never read.
-struct PackCursor {
-  int phase;   // 0: centroid tiles, 1: kept clusters
-  int it;      // centroid tile index, or position in the kept list
-  int j;       // tile within the cluster
-  int nt;      // tiles of the current cluster
-  int n;       // keys of the current cluster
-  int t0;      // first tile of the current cluster
-  int tile;    // packed tile index within the head
-  int nvalid;  // keys of the tile
-};
-__device__ __forceinline__ bool pack_next(PackCursor& c, bool comp, int ctiles, int first_ctile,
-                                          const int16_t* __restrict__ list, int cnt,
-                                          const int32_t* __restrict__ k_off, const int32_t* __restrict__ tile_off,
-                                          int Ck) {
-  if (c.phase == 0) {
-    if (comp && c.it + 1 < ctiles) {
-      ++c.it;
-      c.tile = first_ctile + c.it;
-      c.nvalid = kNK;
-      return true;
+// The tile sequence of one mask row, expanded ahead of the attention by tile_list_kernel:
+// the centroid tiles (compensation), then the tiles of every kept key cluster in list order,
+// one int32 entry per tile: bits 0-22 the packed tile index, bits 23-28 the tile's key count
+// minus one, bit 29 set for centroid tiles.  A cluster's tile count is clamped to the tiles
+// the packed buffer gives it, so keys past it are never read.
+constexpr int kEntryTileBits = 23;
+constexpr int kEntryCentroid = 1 << 29;
+__device__ __forceinline__ int entry_make(int tile, int nvalid, bool centroid) {
+  return tile | ((nvalid - 1) << kEntryTileBits) | (centroid ? kEntryCentroid : 0);
+}
+__device__ __forceinline__ int entry_tile(int e) { return e & ((1 << kEntryTileBits) - 1); }
+__device__ __forceinline__ int entry_nvalid(int e) { return ((e >> kEntryTileBits) & 63) + 1; }
+__device__ __forceinline__ bool entry_centroid(int e) { return (e & kEntryCentroid) != 0; }
+
+constexpr int kListThreads = 256;
+
+// One workgroup per mask row: writes the row's entries (at most maxe) and their count.
+__global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* __restrict__ kv_count,
+                                                                  const int16_t* __restrict__ kv_idx, int Ck,
+                                                                  const int32_t* __restrict__ k_off,
+                                                                  const int32_t* __restrict__ tile_off, int first_ctile,
+                                                                  int ctiles, int comp, int maxe,
+                                                                  int32_t* __restrict__ entries,
+                                                                  int32_t* __restrict__ counts) {
+  __shared__ int scan[kListThreads];
+  const size_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int cnt = kv_count[row];
+  const int16_t* list = kv_idx + row * Ck;
+  int32_t* out = entries + row * maxe;
+  int base = 0;
+  if (comp) {
+    for (int e = t; e < ctiles && e < maxe; e += kListThreads) out[e] = entry_make(first_ctile + e, kNK, true);
+    base = min(ctiles, maxe);
+  }
+  for (int p0 = 0; p0 < cnt; p0 += kListThreads) {
+    const int p = p0 + t;
+    int nt = 0, n = 0, t0 = 0;
+    if (p < cnt) {
+      const int cl = list[p];
+      if (cl >= 0 && cl < Ck) {
+        n = k_off[cl + 1] - k_off[cl];
+        t0 = tile_off[cl];
+        nt = min((n + kNK - 1) / kNK, min(tile_off[cl + 1], first_ctile) - t0);
+        if (n <= 0 || t0 < 0 || nt < 0) nt = 0;
+      }
     }
-    c.phase = 1;
-    c.it = -1;
-    c.j = 0;
-    c.nt = 0;
+    // Inclusive scan of the tile counts over the workgroup.
+    scan[t] = nt;
+    __syncthreads();
+    for (int d = 1; d < kListThreads; d <<= 1) {
+      const int add = t >= d ? scan[t - d] : 0;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    const int first = base + scan[t] - nt;
+    for (int j = 0; j < nt && first + j < maxe; ++j) out[first + j] = entry_make(t0 + j, min(kNK, n - j * kNK), false);
+    base += scan[kListThreads - 1];
+    __syncthreads();
   }
-  if (c.j + 1 < c.nt) {  // next tile of the current cluster
-    ++c.j;
-    c.tile = c.t0 + c.j;
-    c.nvalid = min(kNK, c.n - c.j * kNK);
-    return true;
+  if (t == 0) counts[row] = min(base, maxe);
+}
+
+// Work order for the attention: units sorted by descending tile count (coarse buckets), so
+// the longest rows start first and the tail of the launch is short.  One workgroup; it also
+// resets the counter the attention workgroups take units from.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 256;
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts, int B, int Hq,
+                                                               int Hkv, int Hm, int Cq, int maxe,
+                                                               int32_t* __restrict__ order,
+                                                               int32_t* __restrict__ counter) {
+  __shared__ int hist[kOrderBuckets];
+  const int t = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int units = B * Hq * Cq;
+  auto bucket_of = [&](int u) {
+    int bk, a, g;
+    decode_unit(u, Cq, G, bk, a, g);
+    const int b = bk / Hkv, kvh = bk % Hkv, hq = kvh * G + g;
+    const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+    const int w = counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a];
+    const int k = static_cast<int>((static_cast<long long>(w) * kOrderBuckets) / (maxe + 1));
+    return kOrderBuckets - 1 - min(k, kOrderBuckets - 1);
+  };
+  if (t < kOrderBuckets) hist[t] = 0;
+  __syncthreads();
+  for (int u = t; u < units; u += kOrderThreads) atomicAdd(&hist[bucket_of(u)], 1);
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < kOrderBuckets; ++i) {
+      const int c = hist[i];
+      hist[i] = run;
+      run += c;
+    }
+    *counter = 0;
   }
-  while (++c.it < cnt) {  // first tile of the next non-empty kept cluster
-    const int cl = list[c.it];
-    if (cl < 0 || cl >= Ck) continue;
-    const int n = k_off[cl + 1] - k_off[cl];
-    const int t0 = tile_off[cl];
-    const int nt = min((n + kNK - 1) / kNK, min(tile_off[cl + 1], first_ctile) - t0);
-    if (n <= 0 || t0 < 0 || nt <= 0) continue;
-    c.j = 0;
-    c.nt = nt;
-    c.n = n;
-    c.t0 = t0;
-    c.tile = t0;
-    c.nvalid = min(kNK, n);
-    return true;
-  }
-  return false;
+  __syncthreads();
+  for (int u = t; u < units; u += kOrderThreads) order[atomicAdd(&hist[bucket_of(u)], 1)] = u;
 }
 
 template <typename T, int D, bool REPAIR>
 struct AttnLds {
   using C = Cfg<T, D>;
-  static constexpr int BUF_BYTES = SwzLds<T, D>::K_BYTES + SwzLds<T, D>::V_BYTES;  // one K + V^T tile
-  static constexpr int TILES = 2 * BUF_BYTES;
+  static constexpr int KB = SwzLds<T, D>::K_BYTES;  // one K tile
+  static constexpr int VB = SwzLds<T, D>::V_BYTES;  // one V^T tile
+  static constexpr int K0 = 0;                      // K buffers [2]
+  static constexpr int V0 = 2 * KB;                 // V^T buffers [2]
+  static constexpr int TILES = 2 * KB + 2 * VB;
   static constexpr int REP = REPAIR ? repair_lds_bytes<T, D>() : 0;
   static constexpr int MAIN0 = TILES > C::Z_BYTES ? TILES : C::Z_BYTES;
   static constexpr int MAIN = MAIN0 > REP ? MAIN0 : REP;
   static constexpr int BIAS = MAIN;  // float[2 buffers][kNK]
-  static constexpr int TOTAL = BIAS + 2 * kNK * 4;
+  static constexpr int UNIT = BIAS + 2 * kNK * 4;  // the workgroup's current work unit
+  static constexpr int TOTAL = UNIT + 16;
 };
 
 // Workgroups resident per CU: bfloat16 kernels keep two (eight waves, two per SIMD, so
@@ -663,11 +764,10 @@ template <typename T, int D, bool COMP, bool REPAIR>
 __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_kernel(
     const T* __restrict__ Q, T* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
-    int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ kv_count,
-    const int16_t* __restrict__ kv_idx, int Hm, const int32_t* __restrict__ tile_off,
-    const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
-    int tiles_per_head, int first_ctile, int ctiles, const float* __restrict__ Acorr,
-    const float* __restrict__ ccorr) {
+    int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
+    int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
+    int tiles_per_head, int first_ctile, const float* __restrict__ Acorr, const float* __restrict__ ccorr,
+    const int32_t* __restrict__ order, int32_t* __restrict__ next_unit, int units) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, REPAIR>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
@@ -676,9 +776,20 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   float* bias0 = reinterpret_cast<float*>(smem + L::BIAS);
 
   const int G = Hq / Hkv;
-  int unit, a, g;
-  decode_block(B * Hkv, Cq, G, unit, a, g);
-  const int b = unit / Hkv, kvh = unit % Hkv;
+  int* unit_slot = reinterpret_cast<int*>(smem + L::UNIT);
+  TileDma<T, D> dma;
+  dma.init();
+  // Persistent workgroups: each takes the next unit of the (longest-first) work order until
+  // the order is exhausted; every wave leaves the loop at the same check.
+  for (;;) {
+  if (threadIdx.x == 0) *unit_slot = atomicAdd(next_unit, 1);
+  __syncthreads();
+  const int idx = *unit_slot;
+  __syncthreads();
+  if (idx >= units) break;
+  int bk, a, g;
+  decode_unit(order[idx], Cq, G, bk, a, g);
+  const int b = bk / Hkv, kvh = bk % Hkv;
   const int hq = kvh * G + g;
   const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
   const size_t mrow = (static_cast<size_t>(b) * Hm + hm) * Cq + a;
@@ -690,13 +801,11 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
   const uint8_t* keep_row = keep + mrow * Ck;
-  const int16_t* list = kv_idx + mrow * Ck;
-  const int cnt = kv_count[mrow];
+  const int32_t* ent = entries + mrow * maxe;
+  const int ecount = counts[mrow];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int q_lo = q_off[a], q_hi = q_off[a + 1];
-  TileDma<T, D> dma;
-  dma.init();
 
   // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise).
   auto write_bias = [&](float* dst, int ct) {
@@ -724,38 +833,51 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     RowState<D> st;
     init_state<D>(st);
 
-    // Tiles stream through two LDS buffers: while tile i is computed, tile i+1 is copied
-    // from global memory into the other buffer; one wait and one barrier per tile.
-    PackCursor cur{0, -1, 0, 0, 0, 0, 0, 0};
-    bool have = pack_next(cur, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
-    if (have) {
-      T* K0 = reinterpret_cast<T*>(smem);
-      dma.issue(Kph + cur.tile * kTileBytes, Vph + cur.tile * kTileBytes, K0,
-                reinterpret_cast<T*>(smem + SwzLds<T, D>::K_BYTES));
-      if (cur.phase == 0) write_bias(bias0, cur.it);
+    // Tiles (centroid tiles, then kept tiles) stream through two LDS buffers: while tile j is
+    // computed, tile j+1 is copied from global memory into the other buffer; one wait and one
+    // barrier per tile.  The row's tile entries are read 64 at a time, one per lane, and each
+    // tile takes its entry from a lane; its V^T format flag is fetched one tile ahead.
+    auto kbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::K0 + i * L::KB); };
+    auto vbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::V0 + i * L::VB); };
+    int chunk = lane < ecount ? ent[lane] : 0;
+    int chunk_next = 64 + lane < ecount ? ent[64 + lane] : 0;
+    int e0 = ecount > 0 ? __builtin_amdgcn_readlane(chunk, 0) : 0;
+    int pv0 = 0;
+    if (ecount > 0) {
+      const int tl = entry_tile(e0);
+      dma.issue_k(Kph + tl * kTileBytes, kbuf(0));
+      dma.issue_v(Vph + tl * kTileBytes, vbuf(0));
+      if (entry_centroid(e0)) write_bias(bias0, tl - first_ctile);
+      pv0 = __builtin_amdgcn_readfirstlane(static_cast<int>(flags_h[tl]));
     }
     wait_vmem();
     __syncthreads();
-    int buf = 0;
-    while (have) {
-      PackCursor nxt = cur;
-      const bool have_next = pack_next(nxt, COMP, ctiles, first_ctile, list, cnt, k_off, tile_off, Ck);
-      if (have_next) {
-        unsigned char* nb = smem + (buf ^ 1) * L::BUF_BYTES;
-        dma.issue(Kph + nxt.tile * kTileBytes, Vph + nxt.tile * kTileBytes, reinterpret_cast<T*>(nb),
-                  reinterpret_cast<T*>(nb + SwzLds<T, D>::K_BYTES));
-        if (nxt.phase == 0) write_bias(bias0 + (buf ^ 1) * kNK, nxt.it);
+    int bj = 0;
+    for (int p = 0; p < ecount; ++p) {
+      const int pn = p + 1;
+      const bool have1 = pn < ecount;
+      if ((pn & 63) == 0) {  // entries pn .. pn+63 move in; fetch the block after them
+        chunk = chunk_next;
+        const int q = pn + 64 + lane;
+        chunk_next = q < ecount ? ent[q] : 0;
       }
-      const unsigned char* cb = smem + buf * L::BUF_BYTES;
-      const bool pv16 = flags_h[cur.tile] != 0;
-      tile_step<T, D, SwzLds<T, D>>(reinterpret_cast<const T*>(cb),
-                                    reinterpret_cast<const T*>(cb + SwzLds<T, D>::K_BYTES), qf, st, c2,
-                                    KeyBias{cur.phase == 0 ? bias0 + buf * kNK : nullptr}, cur.nvalid, pv16);
+      int e1 = 0, pv1 = 0;
+      if (have1) {
+        e1 = __builtin_amdgcn_readlane(chunk, pn & 63);
+        const int tl = entry_tile(e1);
+        dma.issue_k(Kph + tl * kTileBytes, kbuf(bj ^ 1));
+        dma.issue_v(Vph + tl * kTileBytes, vbuf(bj ^ 1));
+        if (entry_centroid(e1)) write_bias(bias0 + (bj ^ 1) * kNK, tl - first_ctile);
+        pv1 = flags_h[tl];
+      }
+      tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2,
+                                    KeyBias{entry_centroid(e0) ? bias0 + bj * kNK : nullptr}, entry_nvalid(e0),
+                                    pv0 != 0);
       wait_vmem();
       __syncthreads();
-      cur = nxt;
-      have = have_next;
-      buf ^= 1;
+      e0 = e1;
+      pv0 = __builtin_amdgcn_readfirstlane(pv1);
+      bj ^= 1;
     }
 
     const float l_tot = st.l + swap_halves(st.l);
@@ -789,6 +911,7 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     }
     __syncthreads();
   }
+  }  // units
 }
 
 // ----------------------------------------------------------------- probe rows
@@ -971,35 +1094,84 @@ struct PackedKV {
   int tiles_per_head, first_ctile, ctiles;
 };
 
+// Tile entries per mask row: the centroid tiles plus at most every token tile of the head.
+inline int list_stride(int S, int Ck) {
+  const PackLayout L = pack_layout(1, 1, S, 64, Ck, 2);
+  return L.centroid_tiles + L.first_centroid_tile;
+}
+// Workspace of the attention: tile entries [rows][stride], counts [rows], the work order
+// [units] and the unit counter.
+struct AttnWs {
+  size_t entries, counts, order, counter, total;
+};
+inline AttnWs attn_ws(int B, int Hq, int Hm, int Cq, int S, int Ck) {
+  const size_t rows = static_cast<size_t>(B) * Hm * Cq;
+  const size_t units = static_cast<size_t>(B) * Hq * Cq;
+  AttnWs w;
+  w.entries = 0;
+  w.counts = pack_align(rows * list_stride(S, Ck) * sizeof(int32_t));
+  w.order = w.counts + pack_align(rows * sizeof(int32_t));
+  w.counter = w.order + pack_align(units * sizeof(int32_t));
+  w.total = w.counter + 256;
+  return w;
+}
+
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <typename T, int D, bool COMP, bool REPAIR>
-void launch_sparse_variant(dim3 grid, hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv,
-                           int S, float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off,
-                           int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                           const PackedKV& P, const float* A, const float* c) {
+void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
+                           float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
+                           const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
+                           const PackedKV& P, const float* A, const float* c, const int32_t* order, int32_t* counter,
+                           int units) {
   constexpr int LDS = AttnLds<T, D, REPAIR>::TOTAL;
   auto kern = sparse_attn_kernel<T, D, COMP, REPAIR>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<T*>(O), lse, B,
-                     Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, kv_count, kv_idx, Hm, P.tile_off, P.flags,
-                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, P.ctiles, A, c);
+  const int grid = min(units, device_cus() * attn_occupancy<T>());
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<T*>(O), lse,
+                     B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags,
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, A, c, order, counter, units);
 }
 
 template <typename T, int D>
 bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* q_perm,
                          const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const uint8_t* keep,
                          const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed, bool comp,
-                         const float* A, const float* c, void* O, float* lse, hipStream_t stream) {
-  const long long nblocks = static_cast<long long>(B) * Hq * Cq;
-  if (nblocks > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
-  const dim3 grid(static_cast<unsigned>(nblocks));
+                         const float* A, const float* c, void* O, float* lse, void* ws, hipStream_t stream) {
+  const long long nunits = static_cast<long long>(B) * Hq * Cq;
+  if (nunits > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
+  const int units = static_cast<int>(nunits);
   const float c2 = scale * kLog2e;
   const PackLayout L = pack_layout(B, Hkv, S, D, Ck, sizeof(T));
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off), base + L.flags, base + L.k, base + L.v,
                    L.tiles_per_head, L.first_centroid_tile, L.centroid_tiles};
-#define BSA_LAUNCH(COMP, REP)                                                                                  \
-  launch_sparse_variant<T, D, COMP, REP>(grid, stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, \
-                                         keep, kv_count, kv_idx, Hm, P, A, c)
+  const size_t rows = static_cast<size_t>(B) * Hm * Cq;
+  const int maxe = list_stride(S, Ck);
+  const AttnWs W = attn_ws(B, Hq, Hm, Cq, S, Ck);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  int32_t* entries = reinterpret_cast<int32_t*>(wsb + W.entries);
+  int32_t* counts = reinterpret_cast<int32_t*>(wsb + W.counts);
+  int32_t* order = reinterpret_cast<int32_t*>(wsb + W.order);
+  int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
+                     kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, maxe, order,
+                     counter);
+#define BSA_LAUNCH(COMP, REP)                                                                                    \
+  launch_sparse_variant<T, D, COMP, REP>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, \
+                                         entries, counts, maxe, Hm, P, A, c, order, counter, units)
   if (comp) {
     if (A != nullptr) BSA_LAUNCH(true, true); else BSA_LAUNCH(true, false);
   } else {
@@ -1057,12 +1229,22 @@ bsa_status launch_probe(int B, int Hq, int Hkv, int S, const void* Q, const void
 
 using namespace bsa;
 
+extern "C" bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, int S, int Ck,
+                                                          size_t* bytes) {
+  if (!bytes || B < 1 || Hq < 1 || Hm < 1 || Cq < 1 || S < 1 || Ck < 1) return BSA_E_ARG;
+  if (Ck > 32767) return BSA_E_UNSUPPORTED;
+  if (list_stride(S, Ck) >= (1 << kEntryTileBits)) return BSA_E_UNSUPPORTED;
+  *bytes = attn_ws(B, Hq, Hm, Cq, S, Ck).total;
+  return BSA_OK;
+}
+
 extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
                                            float scale, const int32_t* q_perm, const int32_t* q_offsets, int Cq,
                                            const int32_t* k_offsets, int Ck, const uint8_t* keep,
                                            const int32_t* kv_count, const int16_t* kv_idx, int Hm,
                                            const void* packed, size_t packed_bytes, int compensate, const float* A,
-                                           const float* c, void* O, float* lse, hipStream_t stream) {
+                                           const float* c, void* O, float* lse, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
   if (!valid_dtype(dtype)) return BSA_E_DTYPE;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
   if (!Q || !O || !q_perm || !q_offsets || !k_offsets || !keep || !kv_count || !kv_idx || !packed) return BSA_E_ARG;
@@ -1071,10 +1253,13 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
-  if (Ck > 32767) return BSA_E_UNSUPPORTED;
+  size_t need = 0;
+  const bsa_status st = bsa_sparse_attention_workspace_size(B, Hq, Hm, Cq, S, Ck, &need);
+  if (st != BSA_OK) return st;
   if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype)).total) return BSA_E_WORKSPACE;
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
 #define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
-                 compensate != 0, A, c, O, lse, stream
+                 compensate != 0, A, c, O, lse, ws, stream
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS

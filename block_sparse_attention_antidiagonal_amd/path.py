@@ -74,6 +74,7 @@ class SparseAttentionPath:
         self.cfg = cfg
         self.device = torch.device(device)
         self._pack_buffer = None  # reused across calls
+        self._attn_ws = None
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -122,8 +123,12 @@ class SparseAttentionPath:
             A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
             mark("fit")
             res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
-            if keep_sparse:
-                res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale)
-        res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, A=A, c=c)
+        if self._attn_ws is None:
+            self._attn_ws = api.attention_workspace(q, kv, layout, mask)
+        if cfg.probes and keep_sparse:
+            res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale,
+                                                        workspace=self._attn_ws)
+        res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, A=A, c=c,
+                                             workspace=self._attn_ws)
         mark("attention")
         return res

@@ -173,12 +173,16 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  *   packed, packed_bytes: the bsa_kv_pack buffer (BSA_E_WORKSPACE if smaller than its size)
  *   A float [B, Hq, D, D], c float [B, Hq, D] (correction) or both NULL
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
+ *   ws: workspace of bsa_sparse_attention_workspace_size bytes (each mask row's tile list and the
+ *       order in which workgroups take the (batch, head, query cluster) units, longest first)
+ * Needs Ck <= 32767.  BSA_E_WORKSPACE if the packed buffer or the workspace is too small.
  */
+bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, int S, int Ck, size_t* bytes_host);
 bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                 const int32_t* q_perm, const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
                                 int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
                                 const void* packed, size_t packed_bytes, int compensate, const float* A,
-                                const float* c, void* O, float* lse, hipStream_t stream);
+                                const float* c, void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)

@@ -98,22 +98,25 @@ def test_host_validation_rejects_before_launch(lib):
     # unknown dtype
     assert lib.bsa_centroids(1, 1, 8, 128, 7, dummy, dummy, dummy, dummy, 1, dummy, dummy, None) == 3
     # sparse attention: (B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
-    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, O, lse, stream)
+    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, O, lse, ws, ws_bytes, stream)
     f = ctypes.c_float(0.1)
     big = 1 << 40
     # unsupported head dim
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, None, None, dummy, None, None) == 4
+                                    dummy, big, 1, None, None, dummy, None, dummy, big, None) == 4
     # Hq not a multiple of Hkv
     assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, None, None, dummy, None, None) == 2
+                                    dummy, big, 1, None, None, dummy, None, dummy, big, None) == 2
     # only one of A / c; no packed buffer; packed buffer too small
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, dummy, None, dummy, None, None) == 1
+                                    dummy, big, 1, dummy, None, dummy, None, dummy, big, None) == 1
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    None, big, 1, None, None, dummy, None, None) == 1
+                                    None, big, 1, None, None, dummy, None, dummy, big, None) == 1
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, 1024, 1, None, None, dummy, None, None) == 5
+                                    dummy, 1024, 1, None, None, dummy, None, dummy, big, None) == 5
+    # attention workspace too small
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, None, None, dummy, None, dummy, 16, None) == 5
     # K/V packing: centroid outputs are required; buffer too small; unsupported head dim
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, None, None, dummy, big, None) == 1
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, 64, None) == 5
@@ -152,3 +155,8 @@ def test_workspace_sizes(lib):
     tile_bytes = 64 * 128 * 2
     expect = 1280 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
     assert _lib.size_query("bsa_kv_pack_workspace_size", 1, 40, 32760, 128, 1, 256) == expect
+    # attention tile lists: per mask row one int32 per centroid or token tile, plus a count
+    # and the work order (one int32 per batch x head x query cluster) with its counter
+    rows, stride = 40 * 256, 4 + 512 + 256
+    assert _lib.size_query("bsa_sparse_attention_workspace_size", 1, 40, 40, 256, 32760, 256) == \
+        -(-rows * stride * 4 // 256) * 256 + 2 * (-(-rows * 4 // 256) * 256) + 256
