@@ -19,6 +19,8 @@ from .api import (  # noqa: E402,F401
     centroid_compensated_attention,
     centroids,
     cluster_layout,
+    correct,
+    gather_rows,
     kv_pack,
     mask_from_keep,
     probe_apply,

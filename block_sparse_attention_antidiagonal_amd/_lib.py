@@ -33,8 +33,8 @@ SIGNATURES = {
                     c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_sparse_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_int,
-                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
-                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int, c_int,
+                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -42,6 +42,8 @@ SIGNATURES = {
     "bsa_probe_fit": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, c_void_p,
                       c_void_p],
     "bsa_probe_apply": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_correct": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+    "bsa_gather_rows": [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p],
     "bsa_select_probe_rows": [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p],
     "bsa_tile_labels": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
 }

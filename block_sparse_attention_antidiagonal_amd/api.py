@@ -190,12 +190,12 @@ def mask_from_keep(keep: torch.Tensor) -> BlockMask:
 
 def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
                            compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
-                           out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
-                           c: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                           out: Optional[torch.Tensor] = None, out_f32: bool = False,
+                           workspace: Optional[torch.Tensor] = None):
     """Block-sparse attention over packed K/V; compensated by the skipped clusters'
-    centroids, or hard drop with compensate=False; with A, c every output row o becomes
-    o + o A + c before rounding (bsa_sparse_attention)."""
-    _check_cuda(q, A, c)
+    centroids, or hard drop with compensate=False (bsa_sparse_attention).  With out_f32 the
+    rows are returned in float32 (for a later correction, see correct)."""
+    _check_cuda(q, out)
     B, Hq, S, D = q.shape
     if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
         raise ValueError("q does not match the packed K/V")
@@ -204,7 +204,10 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
     Ck = kv.layout.C
     if mask.keep.shape[0] != B or mask.keep.shape[2] != q_layout.C or mask.keep.shape[3] != Ck:
         raise ValueError("mask shape does not match batch / cluster counts")
-    o = torch.empty_like(q) if out is None else out
+    odt = torch.float32 if out_f32 else q.dtype
+    o = torch.empty(B, Hq, S, D, dtype=odt, device=q.device) if out is None else out
+    if o.dtype != odt or o.shape != q.shape:
+        raise ValueError("out has the wrong shape or dtype")
     lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device) if return_lse else None
     nbytes = _lib.size_query("bsa_sparse_attention_workspace_size", B, Hq, mask.Hm, q_layout.C, S, Ck)
     if workspace is None or workspace.numel() < nbytes:
@@ -212,9 +215,32 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
     _lib.call("bsa_sparse_attention", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
               _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
               _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
-              int(bool(compensate)), _ptr(A), _ptr(c), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+              int(bool(compensate)), _dtype_code(o), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
               _stream())
     return (o, lse) if return_lse else o
+
+
+def correct(o32: torch.Tensor, A: torch.Tensor, c: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Every row o of the float32 output becomes o + o A + c, rounded once to dtype (bsa_correct)."""
+    _check_cuda(o32, A, c, out)
+    if o32.dtype != torch.float32:
+        raise ValueError("o32 must be float32")
+    B, Hq, S, D = o32.shape
+    o = torch.empty(B, Hq, S, D, dtype=dtype, device=o32.device) if out is None else out
+    code = BSA_BF16 if o.dtype == torch.bfloat16 else BSA_F32
+    _lib.call("bsa_correct", B, Hq, S, D, code, _ptr(o32), _ptr(A), _ptr(c), _ptr(o), _stream())
+    return o
+
+
+def gather_rows(x: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """Rows idx of float32 x [B, H, S, D] -> [B, H, M, D] (bsa_gather_rows)."""
+    _check_cuda(x, idx)
+    B, H, S, D = x.shape
+    M = idx.numel()
+    out = torch.empty(B, H, M, D, dtype=torch.float32, device=x.device)
+    _lib.call("bsa_gather_rows", B * H, S, D, _ptr(x), _ptr(idx), M, _ptr(out), _stream())
+    return out
 
 
 def attention_workspace(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask) -> torch.Tensor:
@@ -228,9 +254,15 @@ def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: C
                                    compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
                                    out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
                                    c: Optional[torch.Tensor] = None):
-    """kv_pack followed by block_sparse_attention, for callers holding plain K/V."""
+    """kv_pack and block_sparse_attention for callers holding plain K/V; with A, c every output
+    row o becomes o + o A + c before it is rounded (attention in float32, then correct)."""
     kv = kv_pack(k, v, k_layout)
-    return block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out, A, c)
+    if A is None:
+        return block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out)
+    res = block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out_f32=True)
+    o32, lse = res if return_lse else (res, None)
+    o = correct(o32, A, c, q.dtype, out)
+    return (o, lse) if return_lse else o
 
 
 def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = None,

@@ -7,9 +7,9 @@
 // online softmax per query row: centroid columns and kept key tiles stream through the
 // same running max and sum, so no mask or log-sum-exp merge is ever materialised.
 // "Partition the Support, Reconstruct the Residual" (summary page), Probe-Fitted Residual
-// Reconstruction: probe rows attend to every key, and their block-sparse rows are computed
-// again in float32 for the fit (bsa_probe_attention); the fitted correction is applied to
-// every output row in the attention epilogue, before the output is rounded.
+// Reconstruction: probe rows attend to every key (bsa_probe_attention); when a correction
+// follows, the attention keeps its rows in float32 so that the fit reads the probes' sparse
+// rows from them and the correction (bsa_correct) rounds each row once.
 //
 // Work decomposition (gfx950): a workgroup of 4 waves owns 128 query rows of one query
 // cluster (the cluster's rows are gathered through the cluster layout); each wave owns 32
@@ -458,119 +458,11 @@ __device__ __forceinline__ void decode_unit(int u, int Cq, int G, int& bk, int& 
   bk = r / Cq;
 }
 
-// ----------------------------------------------------------------- correction epilogue
-
-// O^T <- O^T + (O A)^T + c for the wave's 32 normalized rows ("Partition the Support,
-// Reconstruct the Residual": the fitted correction applied to every row), before the output
-// is rounded.  (O A)^T = A^T O^T on MFMA: the A^T fragments come from LDS (At[j][i]); the O^T
-// fragments come straight from the accumulators, in the same permuted contraction order the
-// P V product uses.  For bfloat16 both operands are split into high and low bfloat16 parts
-// (hi*hi + hi*lo + lo*hi), keeping the product accurate to float32 rounding.
 template <typename T, int D>
-__device__ __forceinline__ void repair_epilogue(RowState<D>& st, const float* __restrict__ Ah,
-                                                const float* __restrict__ ch, unsigned char* smem) {
-  constexpr int ROWA = D + 4;
-  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16{};
-  if constexpr (sizeof(T) == 2) {
-    bf16_t* AtH = reinterpret_cast<bf16_t*>(smem);
-    bf16_t* AtL = AtH + D * ROWA;
-    float* cs = reinterpret_cast<float*>(AtL + D * ROWA);
-    // 4 x 4 blocks: four coalesced float4 row loads, transposed in registers, written as
-    // 8-byte runs of A^T rows (high and low bfloat16 parts).
-    constexpr int kBlk = (D / 4) * (D / 4);
-#pragma unroll 1
-    for (int blk = threadIdx.x; blk < kBlk; blk += kThreads) {
-      const int i0 = (blk / (D / 4)) * 4, j0 = (blk % (D / 4)) * 4;
-      f32x4 rowv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) rowv[k] = *reinterpret_cast<const f32x4*>(Ah + (i0 + k) * D + j0);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float hi[4], lo[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const __bf16 hb = static_cast<__bf16>(rowv[k][jj]);
-          hi[k] = static_cast<float>(hb);
-          lo[k] = rowv[k][jj] - hi[k];
-        }
-        *reinterpret_cast<uint2*>(AtH + (j0 + jj) * ROWA + i0) =
-            make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
-        *reinterpret_cast<uint2*>(AtL + (j0 + jj) * ROWA + i0) =
-            make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
-      }
-    }
-    for (int d = threadIdx.x; d < D; d += kThreads) cs[d] = ch[d];
-    __syncthreads();
-    // O fragments are split into high and low bfloat16 parts as they are consumed.
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      Frag<bf16_t> oh, ol;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = st.o[kk / 2][(kk % 2) * 8 + e];
-        const __bf16 hi = static_cast<__bf16>(x);
-        oh.v[e] = hi;
-        ol.v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
-      }
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        Frag<bf16_t> ahf, alf;
-        load_frag_split(ahf, AtH + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
-        load_frag_split(alf, AtL + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
-        acc[mt] = mma(ahf, oh, acc[mt]);
-        acc[mt] = mma(ahf, ol, acc[mt]);
-        acc[mt] = mma(alf, oh, acc[mt]);
-      }
-      // Keep the scheduler from hoisting later steps' LDS reads (it would run out of
-      // registers and spill).
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[mt][j] + cs[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
-  } else {
-    float* At = reinterpret_cast<float*>(smem);
-    float* cs = At + D * ROWA;
-#pragma unroll 2
-    for (int e = threadIdx.x; e < D * D; e += kThreads) At[(e % D) * ROWA + e / D] = Ah[e];
-    for (int d = threadIdx.x; d < D; d += kThreads) cs[d] = ch[d];
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      Frag<float> of;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) of.v[e] = st.o[kk / 2][(kk % 2) * 8 + e];
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        Frag<float> af;
-        load_frag_split(af, At + (mt * 32 + r) * ROWA + kk * 16 + 4 * h);
-        acc[mt] = mma(af, of, acc[mt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[mt][j] += acc[mt][j] + cs[mt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
-  }
-  __syncthreads();
-}
-
-template <typename T, int D>
-constexpr int repair_lds_bytes() {
-  return (sizeof(T) == 2 ? 2 * D * (D + 4) * 2 : D * (D + 4) * 4) + D * 4;  // A^T parts + c
-}
-
-template <typename T, int D, bool REPAIR>
 constexpr int attn_lds_bytes() {
   using C = Cfg<T, D>;
   const int base = C::KV_BYTES > C::Z_BYTES ? C::KV_BYTES : C::Z_BYTES;
-  const int rep = REPAIR ? repair_lds_bytes<T, D>() : 0;
-  return (base > rep ? base : rep) + kNK * 4 + kFlagBytes;
+  return base + kNK * 4 + kFlagBytes;
 }
 
 // ----------------------------------------------------------------- sparse attention
@@ -737,7 +629,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   for (int u = t; u < units; u += kOrderThreads) order[atomicAdd(&hist[bucket_of(u)], 1)] = u;
 }
 
-template <typename T, int D, bool REPAIR>
+template <typename T, int D, typename TO>
 struct AttnLds {
   using C = Cfg<T, D>;
   static constexpr int KB = SwzLds<T, D>::K_BYTES;  // one K tile
@@ -745,10 +637,11 @@ struct AttnLds {
   static constexpr int K0 = 0;                      // K buffers [2]
   static constexpr int V0 = 2 * KB;                 // V^T buffers [2]
   static constexpr int TILES = 2 * KB + 2 * VB;
-  static constexpr int REP = REPAIR ? repair_lds_bytes<T, D>() : 0;
-  static constexpr int MAIN0 = TILES > C::Z_BYTES ? TILES : C::Z_BYTES;
-  static constexpr int MAIN = MAIN0 > REP ? MAIN0 : REP;
-  static constexpr int BIAS = MAIN;  // float[2 buffers][kNK]
+  static constexpr int ZEPC = 16 / static_cast<int>(sizeof(TO));  // output elements per 16-byte chunk
+  static constexpr int ZROW = D + ZEPC;                             // output staging row (elements)
+  static constexpr int Z_BYTES = kRowsWG * ZROW * static_cast<int>(sizeof(TO));
+  static constexpr int MAIN = TILES > Z_BYTES ? TILES : Z_BYTES;
+  static constexpr int BIAS = MAIN;                // float[2 buffers][kNK]
   static constexpr int UNIT = BIAS + 2 * kNK * 4;  // the workgroup's current work unit
   static constexpr int TOTAL = UNIT + 16;
 };
@@ -760,19 +653,20 @@ constexpr int attn_occupancy() {
   return sizeof(T) == 2 ? 2 : 1;
 }
 
-template <typename T, int D, bool COMP, bool REPAIR>
+// TO: output element type (the input type, or float32 when a correction pass follows).
+template <typename T, int D, bool COMP, typename TO>
 __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_kernel(
-    const T* __restrict__ Q, T* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
+    const T* __restrict__ Q, TO* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
     int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
-    int tiles_per_head, int first_ctile, const float* __restrict__ Acorr, const float* __restrict__ ccorr,
-    const int32_t* __restrict__ order, int32_t* __restrict__ next_unit, int units) {
+    int tiles_per_head, int first_ctile, const int32_t* __restrict__ order, int32_t* __restrict__ next_unit,
+    int units) {
   using C = Cfg<T, D>;
-  using L = AttnLds<T, D, REPAIR>;
+  using L = AttnLds<T, D, TO>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
-  T* Z = reinterpret_cast<T*>(smem);
+  TO* Z = reinterpret_cast<TO*>(smem);
   float* bias0 = reinterpret_cast<float*>(smem + L::BIAS);
 
   const int G = Hq / Hkv;
@@ -796,7 +690,7 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   const size_t bhq = static_cast<size_t>(b) * Hq + hq;
   const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
   const T* Qh = Q + bhq * S * D;
-  T* Oh = O + bhq * S * D;
+  TO* Oh = O + bhq * S * D;
   const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
   const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
@@ -886,27 +780,27 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st.o[dt][j] *= inv;
-    if constexpr (REPAIR) repair_epilogue<T, D>(st, Acorr + bhq * D * D, ccorr + bhq * D, smem);
     // Stage the tile as rows in LDS, then store rows with 16-byte writes.
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int d = dt * 32 + 8 * (j / 4) + 4 * h + (j % 4);
-        Z[my * C::ZROW + d] = from_f32<T>(st.o[dt][j]);
+        Z[my * L::ZROW + d] = from_f32<TO>(st.o[dt][j]);
       }
     if (lse != nullptr && h == 0 && my < nrows) {
       const float v = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
       lse[bhq * S + qtok] = v;
     }
     __syncthreads();
+    constexpr int ZCPR = D / L::ZEPC;  // 16-byte chunks per output row
 #pragma unroll 2
-    for (int idx = threadIdx.x; idx < kRowsWG * C::CPR; idx += kThreads) {
-      const int row = idx / C::CPR, ch = idx % C::CPR;
+    for (int idx = threadIdx.x; idx < kRowsWG * ZCPR; idx += kThreads) {
+      const int row = idx / ZCPR, ch = idx % ZCPR;
       if (row < nrows) {
         const int tok = q_perm[rt + row];
-        *reinterpret_cast<uint4*>(Oh + static_cast<size_t>(tok) * D + ch * C::EPC) =
-            *reinterpret_cast<const uint4*>(Z + row * C::ZROW + ch * C::EPC);
+        *reinterpret_cast<uint4*>(Oh + static_cast<size_t>(tok) * D + ch * L::ZEPC) =
+            *reinterpret_cast<const uint4*>(Z + row * L::ZROW + ch * L::ZEPC);
       }
     }
     __syncthreads();
@@ -961,7 +855,7 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
     const float* __restrict__ Vbar, float* __restrict__ Opart, float* __restrict__ mpart,
     float* __restrict__ lpart) {
   using C = Cfg<T, D>;
-  constexpr int LDS = attn_lds_bytes<T, D, false>();
+  constexpr int LDS = attn_lds_bytes<T, D>();
   extern __shared__ __align__(16) unsigned char smem[];
   T* Ks = reinterpret_cast<T*>(smem);
   T* Vt = Ks + C::K_ELEMS;
@@ -1129,26 +1023,25 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <typename T, int D, bool COMP, bool REPAIR>
+template <typename T, int D, bool COMP, typename TO>
 void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
                            float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
-                           const PackedKV& P, const float* A, const float* c, const int32_t* order, int32_t* counter,
-                           int units) {
-  constexpr int LDS = AttnLds<T, D, REPAIR>::TOTAL;
-  auto kern = sparse_attn_kernel<T, D, COMP, REPAIR>;
+                           const PackedKV& P, const int32_t* order, int32_t* counter, int units) {
+  constexpr int LDS = AttnLds<T, D, TO>::TOTAL;
+  auto kern = sparse_attn_kernel<T, D, COMP, TO>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   const int grid = min(units, device_cus() * attn_occupancy<T>());
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<T*>(O), lse,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
                      B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags,
-                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, A, c, order, counter, units);
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, counter, units);
 }
 
 template <typename T, int D>
 bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* q_perm,
                          const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const uint8_t* keep,
                          const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed, bool comp,
-                         const float* A, const float* c, void* O, float* lse, void* ws, hipStream_t stream) {
+                         bool out_f32, void* O, float* lse, void* ws, hipStream_t stream) {
   const long long nunits = static_cast<long long>(B) * Hq * Cq;
   if (nunits > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
   const int units = static_cast<int>(nunits);
@@ -1169,13 +1062,13 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
                      kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
   hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, maxe, order,
                      counter);
-#define BSA_LAUNCH(COMP, REP)                                                                                    \
-  launch_sparse_variant<T, D, COMP, REP>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, \
-                                         entries, counts, maxe, Hm, P, A, c, order, counter, units)
+#define BSA_LAUNCH(COMP, TO)                                                                                   \
+  launch_sparse_variant<T, D, COMP, TO>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, \
+                                        entries, counts, maxe, Hm, P, order, counter, units)
   if (comp) {
-    if (A != nullptr) BSA_LAUNCH(true, true); else BSA_LAUNCH(true, false);
+    if (out_f32) BSA_LAUNCH(true, float); else BSA_LAUNCH(true, T);
   } else {
-    if (A != nullptr) BSA_LAUNCH(false, true); else BSA_LAUNCH(false, false);
+    if (out_f32) BSA_LAUNCH(false, float); else BSA_LAUNCH(false, T);
   }
 #undef BSA_LAUNCH
   return launch_status();
@@ -1186,7 +1079,7 @@ void launch_probe_pass(int B, int Hq, int Hkv, int S, const void* Q, const void*
                        const int32_t* probe_idx, int M, const int32_t* q_labels, const int32_t* k_labels,
                        const uint8_t* keep, int Hm, int Cq, int Ck, const int32_t* k_off, const float* Kbar,
                        const float* Vbar, float* out, float* ws, hipStream_t stream) {
-  constexpr int LDS = attn_lds_bytes<T, D, false>();
+  constexpr int LDS = attn_lds_bytes<T, D>();
   const int ntok = (S + kProbeChunk - 1) / kProbeChunk;
   const int nchunks = ntok + ((SPARSE && Kbar != nullptr) ? 1 : 0);
   const int qtiles = (M + kRowsWG - 1) / kRowsWG;
@@ -1242,13 +1135,12 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
                                            float scale, const int32_t* q_perm, const int32_t* q_offsets, int Cq,
                                            const int32_t* k_offsets, int Ck, const uint8_t* keep,
                                            const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                           const void* packed, size_t packed_bytes, int compensate, const float* A,
-                                           const float* c, void* O, float* lse, void* ws, size_t ws_bytes,
-                                           hipStream_t stream) {
-  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+                                           const void* packed, size_t packed_bytes, int compensate, int out_dtype,
+                                           void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return BSA_E_DTYPE;
+  if (out_dtype != dtype && out_dtype != BSA_F32) return BSA_E_DTYPE;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
   if (!Q || !O || !q_perm || !q_offsets || !k_offsets || !keep || !kv_count || !kv_idx || !packed) return BSA_E_ARG;
-  if ((A == nullptr) != (c == nullptr)) return BSA_E_ARG;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
@@ -1258,8 +1150,9 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   if (st != BSA_OK) return st;
   if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype)).total) return BSA_E_WORKSPACE;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  const bool out_f32 = out_dtype == BSA_F32 && dtype != BSA_F32;
 #define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
-                 compensate != 0, A, c, O, lse, ws, stream
+                 compensate != 0, out_f32, O, lse, ws, stream
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS

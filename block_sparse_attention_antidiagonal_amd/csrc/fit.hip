@@ -472,6 +472,139 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(float* __restrict__ O, c
   }
 }
 
+// O_out <- O + O A + c from float32 rows O (the uncorrected attention output), rounded once to
+// bfloat16.  A workgroup stages A^T once (high and low bfloat16 parts, transposed through 4 x 4
+// register blocks) and then walks kCorrRows rows in blocks of 128: (O A)^T = A^T O^T on MFMA with
+// O split into high and low parts as well (hi*hi + hi*lo + lo*hi, float32 accuracy); each lane
+// adds its O entries and c, rounds, and the rows leave through LDS as 16-byte chunks.
+constexpr int kCorrRows = 1024;
+template <int D>
+__global__ __launch_bounds__(256) void correct_bf16_kernel(const float* __restrict__ Oin, const float* __restrict__ A,
+                                                            const float* __restrict__ cvec, int S,
+                                                            bf16_t* __restrict__ Oout) {
+  constexpr int ROWA = D + 8;  // A^T staging row (elements; 16-byte aligned rows)
+  constexpr int ZROW = D + 8;  // output staging row (elements)
+  extern __shared__ __align__(16) unsigned char smem_corr[];
+  bf16_t* AtH = reinterpret_cast<bf16_t*>(smem_corr);  // A^T rows: At[j][i] = A[i][j]
+  bf16_t* AtL = AtH + D * ROWA;
+  bf16_t* Z = AtL + D * ROWA;  // [128][ZROW]
+  float* cs = reinterpret_cast<float*>(Z + 128 * ZROW);
+  const int bh = blockIdx.y;
+  const float* Ah = A + static_cast<size_t>(bh) * D * D;
+  const float* Oh = Oin + static_cast<size_t>(bh) * S * D;
+  bf16_t* Ph = Oout + static_cast<size_t>(bh) * S * D;
+  constexpr int kBlk = (D / 4) * (D / 4);
+  for (int blk = threadIdx.x; blk < kBlk; blk += 256) {
+    const int i0 = (blk / (D / 4)) * 4, j0 = (blk % (D / 4)) * 4;
+    f32x4 rowv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rowv[k] = *reinterpret_cast<const f32x4*>(Ah + (i0 + k) * D + j0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const __bf16 hb = static_cast<__bf16>(rowv[k][jj]);
+        hi[k] = static_cast<float>(hb);
+        lo[k] = rowv[k][jj] - hi[k];
+      }
+      *reinterpret_cast<uint2*>(AtH + (j0 + jj) * ROWA + i0) =
+          make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+      *reinterpret_cast<uint2*>(AtL + (j0 + jj) * ROWA + i0) =
+          make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+    }
+  }
+  for (int d = threadIdx.x; d < D; d += 256) cs[d] = cvec[static_cast<size_t>(bh) * D + d];
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int rows_end = min(S, static_cast<int>(blockIdx.x + 1) * kCorrRows);
+  for (int row0 = blockIdx.x * kCorrRows; row0 < rows_end; row0 += 128) {
+    // Output^T tile (D x 32 rows of this wave): A-operand = A^T rows, B-operand = O rows.
+    const int my = row0 + wave * 32 + r;
+    const float* orow = Oh + static_cast<size_t>(my < S ? my : S - 1) * D;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow + kk * 16 + 8 * h);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow + kk * 16 + 8 * h + 4);
+      Frag<bf16_t> oh, ol;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const __bf16 hi = static_cast<__bf16>(x);
+        oh.v[e] = hi;
+        ol.v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+      }
+#pragma unroll
+      for (int jt = 0; jt < D / 32; ++jt) {
+        Frag<bf16_t> ah, al;
+        load_frag(ah, AtH + (jt * 32 + r) * ROWA + kk * 16 + 8 * h);
+        load_frag(al, AtL + (jt * 32 + r) * ROWA + kk * 16 + 8 * h);
+        acc[jt] = mma(ah, oh, acc[jt]);
+        acc[jt] = mma(ah, ol, acc[jt]);
+        acc[jt] = mma(al, oh, acc[jt]);
+      }
+    }
+    // Entry j of acc[jt] is feature jt*32 + 8*(j/4) + 4h + j%4 of this lane's row.
+#pragma unroll
+    for (int jt = 0; jt < D / 32; ++jt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = jt * 32 + 8 * q + 4 * h;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(orow + f);
+        const uint32_t w0 = pack_bf16x2(o[0] + acc[jt][4 * q] + cs[f], o[1] + acc[jt][4 * q + 1] + cs[f + 1]);
+        const uint32_t w1 = pack_bf16x2(o[2] + acc[jt][4 * q + 2] + cs[f + 2], o[3] + acc[jt][4 * q + 3] + cs[f + 3]);
+        *reinterpret_cast<uint2*>(Z + (wave * 32 + r) * ZROW + f) = make_uint2(w0, w1);
+      }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 128 * (D / 8); e += 256) {
+      const int rr = e / (D / 8), g = e % (D / 8);
+      const int row = row0 + rr;
+      if (row < S)
+        *reinterpret_cast<uint4*>(Ph + static_cast<size_t>(row) * D + g * 8) =
+            *reinterpret_cast<const uint4*>(Z + rr * ZROW + g * 8);
+    }
+    __syncthreads();
+  }
+}
+
+// Float32 rows: plain float32 arithmetic (Oout may be Oin).
+__global__ __launch_bounds__(256) void correct_f32_kernel(const float* __restrict__ Oin, const float* __restrict__ A,
+                                                          const float* __restrict__ cvec, int S, int D,
+                                                          float* Oout) {
+  extern __shared__ float rows_c[];  // 8 rows x D
+  const int bh = blockIdx.y;
+  const int row0 = blockIdx.x * 8;
+  const float* Ih = Oin + static_cast<size_t>(bh) * S * D;
+  float* Oh = Oout + static_cast<size_t>(bh) * S * D;
+  const float* Ah = A + static_cast<size_t>(bh) * D * D;
+  for (int e = threadIdx.x; e < 8 * D; e += 256) {
+    const int rr = e / D, d = e % D;
+    rows_c[e] = row0 + rr < S ? Ih[static_cast<size_t>(row0 + rr) * D + d] : 0.0f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 8 * D; e += 256) {
+    const int rr = e / D, j = e % D;
+    if (row0 + rr >= S) continue;
+    float v = rows_c[e] + cvec[static_cast<size_t>(bh) * D + j];
+    for (int i = 0; i < D; ++i) v += rows_c[rr * D + i] * Ah[static_cast<size_t>(i) * D + j];
+    Oh[static_cast<size_t>(row0 + rr) * D + j] = v;
+  }
+}
+
+// out[bh][m][:] = X[bh][idx[m]][:] (float32 rows).
+__global__ __launch_bounds__(128) void gather_rows_kernel(const float* __restrict__ X, int S, int D,
+                                                          const int32_t* __restrict__ idx, int M,
+                                                          float* __restrict__ out) {
+  const int m = blockIdx.x, bh = blockIdx.y;
+  const int i = idx[m];
+  if (i < 0 || i >= S) return;
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    out[(static_cast<size_t>(bh) * M + m) * D + d] = X[(static_cast<size_t>(bh) * S + i) * D + d];
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -518,5 +651,41 @@ extern "C" bsa_status bsa_probe_apply(int B, int Hq, int S, int D, int dtype, vo
     hipLaunchKernelGGL(apply_f32_kernel, grid, dim3(256), 8 * D * sizeof(float), stream, static_cast<float*>(O), A, c,
                        S, D);
   }
+  return launch_status();
+}
+
+extern "C" bsa_status bsa_correct(int B, int Hq, int S, int D, int out_dtype, const float* O_in, const float* A,
+                                  const float* c, void* O_out, hipStream_t stream) {
+  if (!valid_dtype(out_dtype)) return BSA_E_DTYPE;
+  if (B < 1 || Hq < 1 || S < 1 || !O_in || !O_out || !A || !c) return BSA_E_ARG;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+  if (out_dtype == BSA_BF16) {
+    const dim3 grid((S + kCorrRows - 1) / kCorrRows, B * Hq);
+    const int smem = 2 * D * (D + 8) * 2 + 128 * (D + 8) * 2 + D * 4;
+    if (D == 128) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(correct_bf16_kernel<128>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      hipLaunchKernelGGL((correct_bf16_kernel<128>), grid, dim3(256), smem, stream, O_in, A, c, S,
+                         static_cast<bf16_t*>(O_out));
+    } else {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(correct_bf16_kernel<64>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      hipLaunchKernelGGL((correct_bf16_kernel<64>), grid, dim3(256), smem, stream, O_in, A, c, S,
+                         static_cast<bf16_t*>(O_out));
+    }
+  } else {
+    const dim3 grid((S + 7) / 8, B * Hq);
+    hipLaunchKernelGGL(correct_f32_kernel, grid, dim3(256), 8 * D * sizeof(float), stream, O_in, A, c, S, D,
+                       static_cast<float*>(O_out));
+  }
+  return launch_status();
+}
+
+extern "C" bsa_status bsa_gather_rows(int BH, int S, int D, const float* X, const int32_t* idx, int M, float* out,
+                                      hipStream_t stream) {
+  if (BH < 1 || S < 1 || D < 1 || M < 1 || !X || !idx || !out) return BSA_E_ARG;
+  if (BH > 65535) return BSA_E_UNSUPPORTED;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(M, BH), dim3(128), 0, stream, X, S, D, idx, M, out);
   return launch_status();
 }

@@ -59,7 +59,7 @@ class PathResult:
     scores: Optional[torch.Tensor] = None
     kbar: Optional[torch.Tensor] = None
     vbar: Optional[torch.Tensor] = None
-    out_sparse: Optional[torch.Tensor] = None  # before the correction (copy; only if requested)
+    out_sparse: Optional[torch.Tensor] = None  # float32 rows before the correction (only if requested)
     o_dense_probe: Optional[torch.Tensor] = None
     o_sparse_probe: Optional[torch.Tensor] = None
     A: Optional[torch.Tensor] = None
@@ -75,6 +75,7 @@ class SparseAttentionPath:
         self.device = torch.device(device)
         self._pack_buffer = None  # reused across calls
         self._attn_ws = None
+        self._o32 = None  # float32 attention rows before the correction
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -90,10 +91,11 @@ class SparseAttentionPath:
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False,
                  mark: Optional[Callable[[str], None]] = None) -> PathResult:
-        """Run the path.  With probes the fit runs before the attention, whose epilogue
-        applies the correction to every row; keep_sparse additionally returns the output
-        without correction (one more attention launch, for inspection).  ``mark(stage)`` is
-        called after each stage's launches (for stream-ordered timing events)."""
+        """Run the path.  With probes the attention keeps its rows in float32, the fit reads
+        the probe rows from them, and the correction pass writes every corrected row, rounded
+        once; keep_sparse also returns the float32 rows before the correction.
+        ``mark(stage)`` is called after each stage's launches (for stream-ordered timing
+        events)."""
         cfg = self.cfg
         mark = mark or (lambda name: None)
         mark("start")
@@ -104,6 +106,10 @@ class SparseAttentionPath:
         self._pack_buffer = kv.buffer
         kbar, vbar = (kv.kbar, kv.vbar) if cfg.compensate else (None, None)
         mark("pack")
+        od = None
+        if cfg.probes:  # exact dense probe rows: independent of the mask
+            od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
+            mark("probe_rows")
         scores = None
         if cfg.mask_mode == "scored":
             scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
@@ -115,20 +121,24 @@ class SparseAttentionPath:
             mask = api.mask_from_keep(self.given_keep)
             mark("mask_lists")
         res = PathResult(out=None, layout=layout, mask=mask, scores=scores, kbar=kbar, vbar=vbar)
-        A = c = None
-        if cfg.probes:
-            od, os_ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale, self.labels, self.labels, layout, mask,
-                                          kbar, vbar)
-            mark("probe_rows")
-            A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
-            mark("fit")
-            res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
         if self._attn_ws is None:
             self._attn_ws = api.attention_workspace(q, kv, layout, mask)
-        if cfg.probes and keep_sparse:
-            res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale,
-                                                        workspace=self._attn_ws)
-        res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, A=A, c=c,
-                                             workspace=self._attn_ws)
+        if not cfg.probes:
+            res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale,
+                                                 workspace=self._attn_ws)
+            mark("attention")
+            return res
+        if self._o32 is None or self._o32.shape != q.shape:
+            self._o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o32 = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, out=self._o32, out_f32=True,
+                                         workspace=self._attn_ws)
         mark("attention")
+        os_ = api.gather_rows(o32, self.probe_idx)
+        A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
+        mark("fit")
+        res.out = api.correct(o32, A, c, q.dtype)
+        mark("correct")
+        res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
+        if keep_sparse:
+            res.out_sparse = o32.clone()
         return res

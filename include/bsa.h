@@ -163,15 +163,14 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  * extra column per skipped non-empty key cluster c with logit q_i . kbar_c * scale + log n_c
  * and value vbar_c, all inside one softmax.  With compensate == 0 skipped blocks are dropped
  * (hard drop; the softmax renormalizes over kept keys).  A row with no column at all gets
- * O = 0 and lse = -inf.  With A and c given (from bsa_probe_fit), every output row o is
- * replaced by o + o A + c before it is rounded to dtype ([SPR]: the correction is applied to
- * all rows).  Keys, values and centroids are read from the buffer bsa_kv_pack wrote.
- *   Q [B, Hq, S, D], O [B, Hq, S, D] out, both dtype
+ * O = 0 and lse = -inf.  Keys, values and centroids are read from the buffer bsa_kv_pack
+ * wrote.  out_dtype is dtype, or BSA_F32 to keep the rows in float32 for a later
+ * correction (bsa_correct).
+ *   Q [B, Hq, S, D] dtype, O [B, Hq, S, D] out_dtype out
  *   q_perm/q_offsets (Cq clusters): query cluster layout; k_offsets [Ck+1]: the key layout
  *     the buffer was packed with
  *   keep/kv_count/kv_idx: block mask with Hm in {1, Hkv, Hq}
  *   packed, packed_bytes: the bsa_kv_pack buffer (BSA_E_WORKSPACE if smaller than its size)
- *   A float [B, Hq, D, D], c float [B, Hq, D] (correction) or both NULL
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
  *   ws: workspace of bsa_sparse_attention_workspace_size bytes (each mask row's tile list and the
  *       order in which workgroups take the (batch, head, query cluster) units, longest first)
@@ -181,8 +180,8 @@ bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, in
 bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                 const int32_t* q_perm, const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
                                 int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                const void* packed, size_t packed_bytes, int compensate, const float* A,
-                                const float* c, void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                                const void* packed, size_t packed_bytes, int compensate, int out_dtype, void* O,
+                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)
@@ -223,12 +222,23 @@ bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_probe, cons
                          const float* weights, int M, float lambda, int rank, float* A, float* c, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
- * Correction of an existing output ([SPR]: the correction is applied to all rows; probe rows
- * are corrected too, not overwritten):  O <- O + O A + c, in place, per (batch, head).
- * bsa_sparse_attention applies the same correction in its epilogue; this call serves
- * outputs computed elsewhere.
+ * Correction of every row ([SPR]: the correction is applied to all rows; probe rows are
+ * corrected too, not overwritten), per (batch, head).
+ * bsa_correct: O_out = O_in + O_in A + c from float32 rows O_in [B, Hq, S, D] (the attention
+ *   output kept in float32), rounded once to out_dtype; O_out [B, Hq, S, D] out_dtype.  For
+ *   bfloat16 output the product O_in A is taken with both operands split into high and low
+ *   bfloat16 parts (float32 accuracy).  With out_dtype BSA_F32, O_out may be O_in.
+ * bsa_probe_apply: O <- O + O A + c, in place, for outputs already rounded to dtype.
  */
+bsa_status bsa_correct(int B, int Hq, int S, int D, int out_dtype, const float* O_in, const float* A,
+                       const float* c, void* O_out, hipStream_t stream);
 bsa_status bsa_probe_apply(int B, int Hq, int S, int D, int dtype, void* O, const float* A, const float* c,
+                           hipStream_t stream);
+
+/* Rows of float32 outputs at given positions: out [BH, M, D] = X [BH, S, D] at rows idx [M]
+ * (the probe rows of the uncorrected attention output, for bsa_probe_fit).  Indices outside
+ * [0, S) leave their output row untouched. */
+bsa_status bsa_gather_rows(int BH, int S, int D, const float* X, const int32_t* idx, int M, float* out,
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------

@@ -98,25 +98,27 @@ def test_host_validation_rejects_before_launch(lib):
     # unknown dtype
     assert lib.bsa_centroids(1, 1, 8, 128, 7, dummy, dummy, dummy, dummy, 1, dummy, dummy, None) == 3
     # sparse attention: (B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
-    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, O, lse, ws, ws_bytes, stream)
+    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, out_dtype, O, lse, ws, ws_bytes, stream)
     f = ctypes.c_float(0.1)
     big = 1 << 40
     # unsupported head dim
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, None, None, dummy, None, dummy, big, None) == 4
+                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 4
     # Hq not a multiple of Hkv
     assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, None, None, dummy, None, dummy, big, None) == 2
-    # only one of A / c; no packed buffer; packed buffer too small
+                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 2
+    # output type must be the input type or float32; no packed buffer; packed buffer too small
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 0, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 3
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, dummy, None, dummy, None, dummy, big, None) == 1
+                                    dummy, big, 1, 9, dummy, None, dummy, big, None) == 3
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    None, big, 1, None, None, dummy, None, dummy, big, None) == 1
+                                    None, big, 1, 1, dummy, None, dummy, big, None) == 1
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, 1024, 1, None, None, dummy, None, dummy, big, None) == 5
+                                    dummy, 1024, 1, 1, dummy, None, dummy, big, None) == 5
     # attention workspace too small
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, None, None, dummy, None, dummy, 16, None) == 5
+                                    dummy, big, 1, 1, dummy, None, dummy, 16, None) == 5
     # K/V packing: centroid outputs are required; buffer too small; unsupported head dim
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, None, None, dummy, big, None) == 1
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, 64, None) == 5
@@ -127,8 +129,11 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.bsa_probe_attention(1, 1, 1, 8, 128, 1, dummy, dummy, dummy, ctypes.c_float(0.1), dummy, 4, dummy,
                                    dummy, dummy, 1, 1, 4096, dummy, None, None, dummy, dummy, dummy, 1 << 30,
                                    None) == 4
-    # null output
+    # null output; correction: unsupported head dim, null input
     assert lib.bsa_probe_apply(1, 1, 8, 128, 1, None, dummy, dummy, None) == 1
+    assert lib.bsa_correct(1, 1, 8, 96, 1, dummy, dummy, dummy, dummy, None) == 4
+    assert lib.bsa_correct(1, 1, 8, 128, 1, None, dummy, dummy, dummy, None) == 1
+    assert lib.bsa_gather_rows(1, 8, 128, dummy, None, 4, dummy, None) == 1
     # block not a multiple of stride
     assert lib.bsa_antidiag_scores_workspace_size(1, 1, 1, 1024, 128, 100, 16, ctypes.byref(size)) == 1
     # workspace too small

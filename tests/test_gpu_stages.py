@@ -382,10 +382,19 @@ def test_probe_apply(bsa, dtype, D):
         check_output(after[0, h], orep.apply_correction(before[0, h], A[0, h], c[0, h]), dtype, f"apply h{h}")
 
 
+def test_gather_rows_bit_exact(bsa):
+    say("gather rows")
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 3, 300, 64)).astype(np.float32)
+    idx = np.array([0, 299, 17, 150, 17], dtype=np.int32)
+    got = bsa.gather_rows(torch.from_numpy(x).cuda(), torch.from_numpy(idx).cuda()).cpu().numpy()
+    assert np.array_equal(got, x[:, :, idx])
+
+
 @pytest.mark.parametrize("dtype,D,compensate", [("bf16", 128, True), ("f32", 64, True), ("bf16", 64, False)])
 def test_attention_with_correction_epilogue(bsa, dtype, D, compensate):
-    """The correction applied inside the attention epilogue equals the oracle's
-    o + o A + c on the exact attention output (one rounding, at the end)."""
+    """Attention kept in float32, then the correction pass: equals the oracle's o + o A + c on
+    the exact attention output (one rounding, at the end)."""
     say(f"attention epilogue {dtype} D={D}")
     wl = make_custom(77, B=1, Hq=2, Hkv=1, S=1200, D=D, dtype=dtype)
     rng = np.random.default_rng(3)
