@@ -11,7 +11,8 @@
 // system is solved in its M x M dual form, which gives the same W:
 //   W = (Y^T Y + lambda I)^-1 Y^T T  =  Y^T (Y Y^T + lambda I)^-1 T,
 // with Y = Omega^1/2 X and T = Omega^1/2 Rc.  The principal directions of Rc^T Omega Rc = T^T T
-// come from the eigenvectors U of the M x M Gram matrix T T^T (cyclic Jacobi): V_r =
+// come from the eigenvectors U of the M x M Gram matrix T T^T (Householder tridiagonalization,
+// multisection on Sturm counts, inverse iteration, back-transformation): V_r =
 // T^T U_r Lambda_r^-1/2, and T V_r = U_r Lambda_r^1/2, so W V_r = Y^T (Y Y^T + lambda I)^-1 U_r
 // Lambda_r^1/2.  The folded map is A = diag(1/sigma) (W V_r) V_r^T, c = rbar - mu A.
 #include "common.hpp"
@@ -20,8 +21,7 @@ namespace bsa {
 namespace {
 
 constexpr int kMaxM = 64;
-constexpr int kN = 64;  // Jacobi size: the M x M Gram matrix padded with zero rows
-constexpr int kHalf = kN / 2;
+constexpr int kN = 64;  // eigenproblem size: the M x M Gram matrix padded with zero rows
 constexpr int kFitThreads = 256;
 constexpr int kMaxRank = 16;
 
@@ -41,8 +41,9 @@ struct FitSmem {
   double w[kN], sw[kN];
   double eval[kN];
   double u[kMaxRank];  // (mu / sigma)^T W V_r
-  double rot_c[kHalf], rot_s[kHalf], rot_t[kHalf];
-  int pair_p[kHalf], pair_q[kHalf];
+  double dg[kN], od[kN], e2[kN];  // tridiagonal form: diagonal, off-diagonal, off-diagonal squared
+  double pv[kN], wv[kN];          // Householder step vectors
+  double lam[kMaxRank];           // the largest eigenvalues, descending
   int order[kN];
   double wave_part[kFitThreads / 64];
   int r_eff;
@@ -59,19 +60,6 @@ __device__ double block_sum(double v, double* part) {
 #pragma unroll
   for (int i = 0; i < kFitThreads / 64; ++i) s += part[i];
   return s;
-}
-
-// Round-robin pairing of 64 indices: index 0 stays, the other 63 rotate by one each round,
-// so 63 rounds pair every index with every other once.
-__device__ __forceinline__ void round_pair(int k, int round, int& p, int& q) {
-  const int pa = k, pb = kN - 1 - k;
-  p = pa == 0 ? 0 : 1 + (pa - 1 + round) % (kN - 1);
-  q = 1 + (pb - 1 + round) % (kN - 1);
-  if (p > q) {
-    const int tmp = p;
-    p = q;
-    q = tmp;
-  }
 }
 
 // out[i][j] = sum_d X[i][d] X[j][d] over 64 x 64 (rows of X in LDS, float32), float64 sums;
@@ -154,104 +142,191 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     sm.t.T[m][d] = static_cast<float>(sm.sw[m] * (rres - sm.rbar[d]));
   }
   __syncthreads();
-  // G = T T^T (64 x 64) and E = I.
+  // G = T T^T (64 x 64).
   gram64(sm.t.T, D, sm.G, 0.0);
-  for (int e = t; e < kN * kN; e += kFitThreads) sm.e.E[e / kN][e % kN] = (e / kN == e % kN) ? 1.0 : 0.0;
   __syncthreads();
 
-  // Cyclic Jacobi.  Each round rotates 32 disjoint index pairs at once: G <- J^T G J is applied
-  // 2 x 2 block by block (block (k, l) = rows of pair k, columns of pair l), E <- E J.
-  double fro_part = 0.0;
-  for (int e = t; e < kN * kN; e += kFitThreads) fro_part += sm.G[e / kN][e % kN] * sm.G[e / kN][e % kN];
-  const double fro = sqrt(block_sum(fro_part, sm.wave_part));
-  constexpr int kBlkPer = kHalf * kHalf / kFitThreads;  // 2 x 2 blocks per thread
-  constexpr int kEPer = kHalf * kN / kFitThreads;       // eigenvector pairs per thread
-  const int bl = t % kHalf, ei = t % kN;
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    double off_part = 0.0;
-    for (int e = t; e < kN * kN; e += kFitThreads) {
-      const int i = e / kN, j = e % kN;
-      if (i != j) off_part += sm.G[i][j] * sm.G[i][j];
+  // Leading eigenpairs of G, in four steps: Householder reduction to tridiagonal form, the
+  // largest kMaxRank eigenvalues by multisection on Sturm counts, their eigenvectors by inverse
+  // iteration on the tridiagonal matrix (orthogonalized), and the back-transformation.
+  //
+  // (1) Step k reflects rows and columns k+1.. so that column k has zeros below the
+  // subdiagonal: H = I - 2 v v^T with |v| = 1; the trailing block becomes G - v w^T - w v^T with
+  // w = 2 G v - 2 (v^T G v) v.  v is kept in column k below the diagonal.
+  for (int k = 0; k < kN - 2; ++k) {
+    const int m = kN - 1 - k;
+    double part = 0.0;
+    if (t < m) {
+      const double x = sm.G[k + 1 + t][k];
+      part = x * x;
     }
-    const double off = sqrt(block_sum(off_part, sm.wave_part));
-    if (!(off > 1e-15 * fro)) break;
-    for (int round = 0; round < kN - 1; ++round) {
-      if (t < kHalf) {
-        int p, q;
-        round_pair(t, round, p, q);
-        const double app = sm.G[p][p], aqq = sm.G[q][q], apq = sm.G[p][q];
-        double c = 1.0, s = 0.0, tt = 0.0;
-        if (apq != 0.0) {
-          // tan of the rotation angle, the smaller root: 2 apq / (d + sign(d) sqrt(d^2 + 4 apq^2)).
-          const double d = aqq - app;
-          const double r = sqrt(d * d + 4.0 * apq * apq);
-          const double den = d >= 0.0 ? d + r : d - r;
-          tt = den != 0.0 ? 2.0 * apq / den : (apq > 0.0 ? 1.0 : -1.0);
-          c = 1.0 / sqrt(1.0 + tt * tt);
-          s = tt * c;
-        }
-        sm.pair_p[t] = p;
-        sm.pair_q[t] = q;
-        sm.rot_c[t] = c;
-        sm.rot_s[t] = s;
-        sm.rot_t[t] = tt;
-      }
-      __syncthreads();
-      const int pl = sm.pair_p[bl], ql = sm.pair_q[bl];
-      const double cl = sm.rot_c[bl], sl = sm.rot_s[bl];
-#pragma unroll
-      for (int it = 0; it < kBlkPer; ++it) {
-        const int k = t / kHalf + it * (kFitThreads / kHalf);
-        const int pk = sm.pair_p[k], qk = sm.pair_q[k];
-        if (k == bl) {  // the rotated pair itself: closed form, off-diagonal exactly 0
-          const double apq = sm.G[pk][qk], tk = sm.rot_t[k];
-          sm.G[pk][pk] -= tk * apq;
-          sm.G[qk][qk] += tk * apq;
-          sm.G[pk][qk] = 0.0;
-          sm.G[qk][pk] = 0.0;
-        } else {
-          const double ck = sm.rot_c[k], sk = sm.rot_s[k];
-          const double b00 = sm.G[pk][pl], b01 = sm.G[pk][ql], b10 = sm.G[qk][pl], b11 = sm.G[qk][ql];
-          const double x00 = b00 * cl - b01 * sl, x01 = b00 * sl + b01 * cl;
-          const double x10 = b10 * cl - b11 * sl, x11 = b10 * sl + b11 * cl;
-          sm.G[pk][pl] = ck * x00 - sk * x10;
-          sm.G[pk][ql] = ck * x01 - sk * x11;
-          sm.G[qk][pl] = sk * x00 + ck * x10;
-          sm.G[qk][ql] = sk * x01 + ck * x11;
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < kEPer; ++it) {
-        const int k = t / kN + it * (kFitThreads / kN);
-        const int p = sm.pair_p[k], q = sm.pair_q[k];
-        const double c = sm.rot_c[k], s = sm.rot_s[k];
-        const double ep = sm.e.E[ei][p], eq = sm.e.E[ei][q];
-        sm.e.E[ei][p] = c * ep - s * eq;
-        sm.e.E[ei][q] = s * ep + c * eq;
-      }
-      __syncthreads();
+    const double s2 = block_sum(part, sm.wave_part);
+    const double x0 = sm.G[k + 1][k];
+    double alpha = 0.0, vn2 = 0.0;
+    if (s2 > 0.0) {
+      alpha = x0 >= 0.0 ? -sqrt(s2) : sqrt(s2);
+      vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
     }
+    const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
+    if (t < m) sm.G[k + 1 + t][k] = (sm.G[k + 1 + t][k] - (t == 0 ? alpha : 0.0)) * vinv;
+    if (t == 0) {
+      sm.dg[k] = sm.G[k][k];
+      sm.od[k] = alpha;
+    }
+    __syncthreads();
+    if (!(vn2 > 0.0)) continue;  // the column is already zero: H = I
+    {  // p = G_sub v, four threads per row
+      const int i = t >> 2, q = t & 3;
+      double acc = 0.0;
+      if (i < m)
+        for (int j = q; j < m; j += 4) acc += sm.G[k + 1 + i][k + 1 + j] * sm.G[k + 1 + j][k];
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (i < m && q == 0) sm.pv[i] = acc;
+    }
+    __syncthreads();
+    const double vp = block_sum(t < m ? sm.G[k + 1 + t][k] * sm.pv[t] : 0.0, sm.wave_part);
+    if (t < m) sm.wv[t] = 2.0 * sm.pv[t] - 2.0 * vp * sm.G[k + 1 + t][k];
+    __syncthreads();
+    {  // G_sub -= v w^T + w v^T: thread t owns column t % 64 of rows t / 64, +4, ...
+      const int j = t & 63;
+      if (j < m) {
+        const double vj = sm.G[k + 1 + j][k], wj = sm.wv[j];
+        for (int i = t >> 6; i < m; i += 4)
+          sm.G[k + 1 + i][k + 1 + j] -= sm.G[k + 1 + i][k] * wj + sm.wv[i] * vj;
+      }
+    }
+    __syncthreads();
   }
-  // Eigenvalues ranked descending (ties by index); kept directions have eigenvalue above
-  // 1e-12 of the largest.
-  if (t < kN) {
-    const double ev = sm.G[t][t];
-    int rk = 0;
-    for (int j = 0; j < kN; ++j) {
-      const double ej = sm.G[j][j];
-      rk += (ej > ev || (ej == ev && j < t)) ? 1 : 0;
+  if (t == 0) {
+    sm.dg[kN - 2] = sm.G[kN - 2][kN - 2];
+    sm.od[kN - 2] = sm.G[kN - 1][kN - 2];
+    sm.dg[kN - 1] = sm.G[kN - 1][kN - 1];
+    sm.od[kN - 1] = 0.0;
+  }
+  __syncthreads();
+  if (t < kN) sm.e2[t] = sm.od[t] * sm.od[t];
+  __syncthreads();
+
+  // (2) Sturm count: eigenvalues below x = sign changes of the LDL^T pivots of T - x I.
+  double emax2 = 0.0, glo = INFINITY, ghi = -INFINITY;
+  for (int i = 0; i < kN; ++i) {
+    const double r0 = i > 0 ? fabs(sm.od[i - 1]) : 0.0;
+    const double r1 = i < kN - 1 ? fabs(sm.od[i]) : 0.0;
+    glo = fmin(glo, sm.dg[i] - r0 - r1);
+    ghi = fmax(ghi, sm.dg[i] + r0 + r1);
+    emax2 = fmax(emax2, sm.e2[i]);
+  }
+  const double span = fmax(ghi - glo, 1e-300);
+  const double pivmin = 1e-290 * fmax(1.0, emax2);
+  auto below = [&](double x) {
+    int neg = 0;
+    double q = 1.0;
+    for (int i = 0; i < kN; ++i) {
+      q = (sm.dg[i] - x) - (i > 0 ? sm.e2[i - 1] / q : 0.0);
+      if (fabs(q) < pivmin) q = -pivmin;
+      neg += q < 0.0 ? 1 : 0;
     }
-    sm.eval[t] = ev;
-    sm.order[rk] = t;
+    return neg;
+  };
+  {  // 16 eigenvalues at once: lanes of a 16-lane group probe 16 points of its interval
+    const int k = t >> 4, j = t & 15;
+    double a = glo - 1e-3 * span, b = ghi + 1e-3 * span;
+    for (int it = 0; it < 14; ++it) {
+      const double x = a + (b - a) * static_cast<double>(j + 1) / 17.0;
+      const bool ok = (kN - below(x)) <= k;  // at most k eigenvalues above x: lambda_k <= x
+      const unsigned long long mask = __ballot(ok);
+      const unsigned bits = static_cast<unsigned>(mask >> (16 * ((threadIdx.x & 63) >> 4))) & 0xffffu;
+      const int f = bits ? __builtin_ctz(bits) : 16;
+      const double na = f == 0 ? a : a + (b - a) * static_cast<double>(f) / 17.0;
+      const double nb = f == 16 ? b : a + (b - a) * static_cast<double>(f + 1) / 17.0;
+      a = na;
+      b = nb;
+    }
+    if (j == 0) sm.lam[k] = 0.5 * (a + b);
   }
   __syncthreads();
   if (t == 0) {
-    const double emax = sm.eval[sm.order[0]];
+    const double lmax = sm.lam[0];
     int r_eff = 0;
-    if (emax > 0.0)
-      for (int i = 0; i < kN && r_eff < rank; ++i)
-        if (sm.eval[sm.order[i]] > 1e-12 * emax) ++r_eff;
+    if (lmax > 0.0) r_eff = min(rank, kN - below(1e-12 * lmax));
     sm.r_eff = r_eff;
+  }
+  __syncthreads();
+  const int nvec = sm.r_eff;
+
+  // (3) Inverse iteration on T for each kept eigenvalue (one thread per vector): LU of
+  // T - lambda I without pivoting (tiny pivots replaced), three solves from a fixed start,
+  // normalized each time.  Column k of E holds the vector, columns 16+k and 32+k U and L.
+  if (t < nvec) {
+    const int k = t;
+    const double lk = sm.lam[k];
+    const double tiny = 1e-14 * fmax(fabs(glo), fabs(ghi)) + pivmin;
+    double u = sm.dg[0] - lk;
+    if (fabs(u) < tiny) u = tiny;
+    sm.e.E[0][16 + k] = u;
+    for (int i = 1; i < kN; ++i) {
+      const double l = sm.od[i - 1] / u;
+      u = (sm.dg[i] - lk) - l * sm.od[i - 1];
+      if (fabs(u) < tiny) u = tiny;
+      sm.e.E[i][16 + k] = u;
+      sm.e.E[i][32 + k] = l;
+    }
+    for (int i = 0; i < kN; ++i) sm.e.E[i][k] = 1.0 + static_cast<double>((i * 7 + k * 13) % 11) / 11.0;
+    for (int iter = 0; iter < 3; ++iter) {
+      for (int i = 1; i < kN; ++i) sm.e.E[i][k] -= sm.e.E[i][32 + k] * sm.e.E[i - 1][k];
+      sm.e.E[kN - 1][k] /= sm.e.E[kN - 1][16 + k];
+      for (int i = kN - 2; i >= 0; --i)
+        sm.e.E[i][k] = (sm.e.E[i][k] - sm.od[i] * sm.e.E[i + 1][k]) / sm.e.E[i][16 + k];
+      double nrm = 0.0;
+      for (int i = 0; i < kN; ++i) nrm += sm.e.E[i][k] * sm.e.E[i][k];
+      const double inv = 1.0 / sqrt(nrm);
+      for (int i = 0; i < kN; ++i) sm.e.E[i][k] *= inv;
+    }
+  }
+  __syncthreads();
+  // Modified Gram-Schmidt over the vectors in eigenvalue order (one wave, lane = element).
+  if (t < 64) {
+    for (int k = 0; k < nvec; ++k) {
+      for (int j = 0; j < k; ++j) {
+        double dot = sm.e.E[t][j] * sm.e.E[t][k];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        sm.e.E[t][k] -= dot * sm.e.E[t][j];
+      }
+      double nrm = sm.e.E[t][k] * sm.e.E[t][k];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) nrm += __shfl_xor(nrm, o);
+      sm.e.E[t][k] *= 1.0 / sqrt(nrm);
+    }
+  }
+  __syncthreads();
+  // (4) Eigenvectors of G = H_0 H_1 ... H_61 y: 16-lane groups, one vector each.
+  {
+    const int k = t >> 4, q = t & 15;
+    if (k < nvec) {
+      for (int s = kN - 3; s >= 0; --s) {
+        double dot = 0.0;
+#pragma unroll
+        for (int c = 0; c < kN / 16; ++c) {
+          const int i = q + 16 * c;
+          if (i > s) dot += sm.G[i][s] * sm.e.E[i][k];
+        }
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        dot += __shfl_xor(dot, 8);
+#pragma unroll
+        for (int c = 0; c < kN / 16; ++c) {
+          const int i = q + 16 * c;
+          if (i > s) sm.e.E[i][k] -= 2.0 * dot * sm.G[i][s];
+        }
+      }
+    }
+  }
+  if (t < kN) {
+    sm.eval[t] = t < kMaxRank ? sm.lam[t] : 0.0;
+    sm.order[t] = t;
   }
   __syncthreads();
   const int r_eff = sm.r_eff;
