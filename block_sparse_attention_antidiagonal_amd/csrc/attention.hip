@@ -590,43 +590,81 @@ __global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* 
   if (t == 0) counts[row] = min(base, maxe);
 }
 
-// Work order for the attention: units sorted by descending tile count (coarse buckets), so
-// the longest rows start first and the tail of the launch is short.  One workgroup; it also
-// resets the counter the attention workgroups take units from.
+// Work order for the attention.  Workgroups are dispatched to the 8 XCDs round-robin, and
+// each XCD has its own L2.  The units of one K/V group -- every query cluster of its query
+// heads, which read the same key tiles and (for GQA) share masks -- go to one XCD, query
+// cluster by query cluster, so that workgroups running together on an XCD sweep nearby
+// tiles and hit its L2.  Groups are spread over the XCDs longest-processing-time first by
+// their total tile count.  ctl[x] is XCD x's unit counter, ctl[8 + x] the start of its
+// segment of `order` (ctl[16] = end).  One workgroup.
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderBuckets = 256;
+constexpr int kMaxGroups = 2048;
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts, int B, int Hq,
-                                                               int Hkv, int Hm, int Cq, int maxe,
-                                                               int32_t* __restrict__ order,
-                                                               int32_t* __restrict__ counter) {
-  __shared__ int hist[kOrderBuckets];
+                                                               int Hkv, int Hm, int Cq, int32_t* __restrict__ order,
+                                                               int32_t* __restrict__ ctl) {
+  __shared__ int wsum[kMaxGroups];
+  __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
+  __shared__ int seg[kXcds + 1];
   const int t = threadIdx.x;
   const int G = Hq / Hkv;
-  const int units = B * Hq * Cq;
-  auto bucket_of = [&](int u) {
+  const int ng = B * Hkv;
+  const int per = Cq * G;  // units per group, contiguous in unit numbering
+  const int units = ng * per;
+  if (ng > kMaxGroups) {  // too many groups to balance here: plain order, split evenly
+    for (int u = t; u < units; u += kOrderThreads) order[u] = u;
+    if (t <= kXcds) {
+      ctl[8 + t] = static_cast<int>((static_cast<long long>(units) * t) / kXcds);
+      if (t < kXcds) ctl[t] = 0;
+    }
+    return;
+  }
+  for (int i = t; i < ng; i += kOrderThreads) wsum[i] = 0;
+  __syncthreads();
+  for (int u = t; u < units; u += kOrderThreads) {
     int bk, a, g;
     decode_unit(u, Cq, G, bk, a, g);
     const int b = bk / Hkv, kvh = bk % Hkv, hq = kvh * G + g;
     const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
-    const int w = counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a];
-    const int k = static_cast<int>((static_cast<long long>(w) * kOrderBuckets) / (maxe + 1));
-    return kOrderBuckets - 1 - min(k, kOrderBuckets - 1);
-  };
-  if (t < kOrderBuckets) hist[t] = 0;
-  __syncthreads();
-  for (int u = t; u < units; u += kOrderThreads) atomicAdd(&hist[bucket_of(u)], 1);
-  __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int i = 0; i < kOrderBuckets; ++i) {
-      const int c = hist[i];
-      hist[i] = run;
-      run += c;
-    }
-    *counter = 0;
+    atomicAdd(&wsum[bk], counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a] + 1);
   }
   __syncthreads();
-  for (int u = t; u < units; u += kOrderThreads) order[atomicAdd(&hist[bucket_of(u)], 1)] = u;
+  // Rank the groups by descending work (ties by index).
+  for (int i = t; i < ng; i += kOrderThreads) {
+    const int w = wsum[i];
+    int r = 0;
+    for (int j = 0; j < ng; ++j) r += (wsum[j] > w) | ((wsum[j] == w) & (j < i));
+    place[r] = i;
+  }
+  __syncthreads();
+  if (t == 0) {
+    // Longest processing time first: each group to the least loaded XCD.
+    long long load[kXcds];
+    int ngx[kXcds];
+    for (int x = 0; x < kXcds; ++x) load[x] = ngx[x] = 0;
+    for (int r = 0; r < ng; ++r) {
+      const int gi = place[r];
+      int xs = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[xs]) xs = x;
+      load[xs] += wsum[gi];
+      wsum[gi] = xs * kMaxGroups + ngx[xs]++;  // the group's XCD and its slot there
+    }
+    int run = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      seg[x] = run;
+      ctl[8 + x] = run;
+      ctl[x] = 0;
+      run += ngx[x] * per;
+    }
+    seg[kXcds] = run;
+    ctl[8 + kXcds] = run;
+  }
+  __syncthreads();
+  for (int u = t; u < units; u += kOrderThreads) {
+    const int bk = u / per;
+    const int x = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
+    order[seg[x] + slot * per + u % per] = u;
+  }
 }
 
 template <typename T, int D, typename TO>
@@ -660,8 +698,7 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
     int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
-    int tiles_per_head, int first_ctile, const int32_t* __restrict__ order, int32_t* __restrict__ next_unit,
-    int units) {
+    int tiles_per_head, int first_ctile, const int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, TO>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
@@ -673,14 +710,28 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   int* unit_slot = reinterpret_cast<int*>(smem + L::UNIT);
   TileDma<T, D> dma;
   dma.init();
-  // Persistent workgroups: each takes the next unit of the (longest-first) work order until
-  // the order is exhausted; every wave leaves the loop at the same check.
+  // Persistent workgroups: each takes units from its XCD's segment of the work order, then
+  // helps the other XCDs once its own is exhausted; -1 ends the loop for every wave at once.
+  const int x0 = static_cast<int>(blockIdx.x % kXcds);  // dispatch is round-robin over XCDs
+  int tries = 0;                                        // used by thread 0 only
   for (;;) {
-  if (threadIdx.x == 0) *unit_slot = atomicAdd(next_unit, 1);
+  if (threadIdx.x == 0) {
+    int got = -1;
+    while (tries < kXcds) {
+      const int q = (x0 + tries) % kXcds;
+      const int i = atomicAdd(&ctl[q], 1);
+      if (i < ctl[8 + q + 1] - ctl[8 + q]) {
+        got = ctl[8 + q] + i;
+        break;
+      }
+      ++tries;
+    }
+    *unit_slot = got;
+  }
   __syncthreads();
   const int idx = *unit_slot;
   __syncthreads();
-  if (idx >= units) break;
+  if (idx < 0) break;
   int bk, a, g;
   decode_unit(order[idx], Cq, G, bk, a, g);
   const int b = bk / Hkv, kvh = bk % Hkv;
@@ -1027,14 +1078,14 @@ template <typename T, int D, bool COMP, typename TO>
 void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
                            float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
-                           const PackedKV& P, const int32_t* order, int32_t* counter, int units) {
+                           const PackedKV& P, const int32_t* order, int32_t* ctl, int units) {
   constexpr int LDS = AttnLds<T, D, TO>::TOTAL;
   auto kern = sparse_attn_kernel<T, D, COMP, TO>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   const int grid = min(units, device_cus() * attn_occupancy<T>());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
                      B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags,
-                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, counter, units);
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, ctl);
 }
 
 template <typename T, int D>
@@ -1060,8 +1111,7 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
   hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
                      kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, maxe, order,
-                     counter);
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, order, counter);
 #define BSA_LAUNCH(COMP, TO)                                                                                   \
   launch_sparse_variant<T, D, COMP, TO>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, \
                                         entries, counts, maxe, Hm, P, order, counter, units)
