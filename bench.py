@@ -24,6 +24,8 @@ of the same workload (one head, a subset of query clusters).
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --profile-kernels K   # for rocprofv3: K launches of each kernel alone,
                                           # then one plain copy of a known size
+    python bench.py --summarize-profiles DIR  # write the profiles/ summaries from the csv
+                                              # files of the PROFILE_COMMANDS runs in DIR
 """
 
 from __future__ import annotations
@@ -51,6 +53,17 @@ WORKLOAD = ("wan_video_21x30x52_S32760_H40_D128_bf16: scored top-p masks + compe
 COPY_BYTES = 1 << 30  # the reference copy for scaling the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan_S32760_H40_D128_traffic.json")
 KERNEL_SOURCES = ("attention.hip", "pack.hpp", "common.hpp")
+ATTN_KERNEL = "sparse_attn_kernel"
+# The rocprofv3 runs behind the profiles/ summaries, from the repository root; each writes
+# <name>_*.csv into DIR (gpurun_out/prof).
+PROFILE_COMMANDS = {
+    "trace": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d $R/gpurun_out/prof -o trace -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "fetch": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+             "-d $R/gpurun_out/prof -o fetch -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    "write": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+             "-d $R/gpurun_out/prof -o write -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+}
 
 
 def kernel_source_hash() -> str:
@@ -72,6 +85,89 @@ def measured_traffic():
     if t.get("source_sha256") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("void ", "").replace("bsa::(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:  # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def _counter_per_dispatch(path: str):
+    """{kernel: [counter value per dispatch]} from a rocprofv3 counter_collection csv."""
+    import csv
+
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_profiles(d: str) -> int:
+    """Write the kernel-trace table, the HBM counter table and the attention kernel's traffic
+    record (profiles/) from the csv files of the PROFILE_COMMANDS runs in directory d."""
+    import csv
+
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    stem = "wan_S32760_H40_D128"
+    stats = os.path.join(d, "trace_kernel_stats.csv")
+    if os.path.exists(stats):
+        rows = list(csv.DictReader(open(stats)))
+        lines = [f"# Kernel trace: whole path, video workload (B=1, H=40, S=32760, D=128, bf16)", "",
+                 "Command (from the repository root, on one MI355X):", "", "```", PROFILE_COMMANDS["trace"], "```",
+                 "", "7 calls per path kernel = 2 warmup + 5 timed path calls.  Durations in microseconds.", "",
+                 "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+        for r in rows:
+            lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.2f} |")
+        with open(os.path.join(out_dir, f"path_kernels_{stem}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    fetch = os.path.join(d, "fetch_counter_collection.csv")
+    write = os.path.join(d, "write_counter_collection.csv")
+    if not (os.path.exists(fetch) and os.path.exists(write)):
+        return 0
+    fe, wr = _counter_per_dispatch(fetch), _counter_per_dispatch(write)
+    copy = "__amd_rocclr_copyBuffer"
+    # The plain copy moves COPY_BYTES each way, possibly over several dispatches.
+    fetch_scale = COPY_BYTES / (sum(fe[copy]) * 1024.0)
+    write_scale = COPY_BYTES / (sum(wr[copy]) * 1024.0)
+    lines = ["# HBM byte counters per dispatch, video workload (B=1, H=40, S=32760, D=128, bf16)", "",
+             "Commands (from the repository root, on one MI355X), one counter per run:", "", "```",
+             PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"], "```", "",
+             f"Each run ends with one plain device copy of {COPY_BYTES} bytes.  Its counters, summed over its "
+             f"dispatches, read {sum(fe[copy]):.0f} KiB (FETCH_SIZE) and {sum(wr[copy]):.0f} KiB (WRITE_SIZE), "
+             f"so the counters below are scaled by {fetch_scale:.3f} and {write_scale:.3f} to bytes.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB |",
+             "|---|---:|---:|---:|---:|---:|"]
+    traffic = None
+    for k in fe:
+        if k == copy or k not in wr:
+            continue
+        f_kib = sum(fe[k]) / len(fe[k])
+        w_kib = sum(wr[k]) / len(wr[k])
+        rd, wt = f_kib * 1024 * fetch_scale, w_kib * 1024 * write_scale
+        lines.append(f"| `{k}` | {len(fe[k])} | {f_kib:.0f} | {w_kib:.0f} | {rd / 1e9:.3f} | {wt / 1e9:.3f} |")
+        if k.startswith(ATTN_KERNEL):
+            traffic = {"kernel": k, "fetch_kib": f_kib, "write_kib": w_kib, "fetch_scale": fetch_scale,
+                       "write_scale": write_scale, "read_bytes": rd, "write_bytes": wt,
+                       "bytes_per_launch": rd + wt, "source_sha256": kernel_source_hash(),
+                       "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"]]}
+    with open(os.path.join(out_dir, f"hbm_counters_{stem}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if traffic is not None:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(traffic, f, indent=1)
+            f.write("\n")
+    return 0
 
 
 def executed_pairs(res, cfg):
@@ -163,7 +259,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
                     help="launch each kernel K times on its own, then one plain copy (for rocprofv3)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from the rocprofv3 csv files in DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path runs on a single MI355X (asked for --gpus {args.gpus}). "
               "Heads and K/V groups are independent, so a multi-GPU run would shard them without exchange.",
