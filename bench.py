@@ -186,7 +186,7 @@ def executed_pairs(res, cfg):
 
 def cpu_baseline(wl, seconds_hint=20.0):
     """The float64 oracle on a bounded sample: head 0, its scores and mask, the attention
-    rows of every 4th query cluster, the 64 probe rows and the fit."""
+    rows of every 2nd query cluster, the 64 probe rows and the fit."""
     from oracle import pipeline
 
     try:
@@ -195,7 +195,7 @@ def cpu_baseline(wl, seconds_hint=20.0):
         threads = max((d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()), default=1)
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = len(os.sched_getaffinity(0))
-    clusters = list(range(0, wl.C, 4))
+    clusters = list(range(0, wl.C, 2))
     rows = np.nonzero(np.isin(wl.labels, clusters))[0]
     t0 = time.perf_counter()
     keep = pipeline.head_mask(wl, 0, 0)
