@@ -20,6 +20,8 @@
 #include "common.hpp"
 #include "pack.hpp"
 
+#include <type_traits>
+
 namespace bsa {
 namespace {
 
@@ -332,28 +334,22 @@ __device__ __forceinline__ void tile_qk(const T* Ks, const Frag<T>* qf, f32x16& 
   }
 }
 
-// Online softmax of one tile's logits (s0, s1 in, P out in x[32], log2 units).  Key of x[j]:
-// (j/16)*32 + 8*((j%16)/4) + 4*h + j%4.  Without a bias the max is taken on the raw products
-// (c2 > 0) and the scale folds into the exponent's FMA.  The running max may lag the true
-// max by up to kRescaleSlack, so P <= 2^kRescaleSlack; O and l are rescaled only when a row
-// exceeds that (a wave-uniform branch, rarely taken after the first tiles).
+// Online softmax of one tile's logits, in place: s[0], s[1] hold S^T in, P out (log2 units).
+// Key of s[mt][j]: mt*32 + 8*(j/4) + 4*h + j%4.  Without a bias the max is taken on the raw
+// products (c2 > 0) and the scale folds into the exponent's FMA.  The running max may lag the
+// true max by up to kRescaleSlack, so P <= 2^kRescaleSlack; O and l are rescaled only when a
+// row exceeds that (a wave-uniform branch, rarely taken after the first tiles).
 template <typename T, int D, typename Bias>
-__device__ __forceinline__ void tile_softmax(const f32x16& s0, const f32x16& s1, float* x, RowState<D>& st,
-                                             float c2, const Bias& bias, int nvalid) {
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], RowState<D>& st, float c2, const Bias& bias,
+                                             int nvalid) {
   using C = Cfg<T, D>;
   const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    x[j] = s0[j];
-    x[16 + j] = s1[j];
-  }
-  float xs = c2;  // scale still to apply to x
+  float xs = c2;  // scale still to apply to s
   if (__builtin_expect(bias.active(), 0)) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        x[mt * 16 + j] = x[mt * 16 + j] * c2 + bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
+      for (int j = 0; j < 16; ++j) s[mt][j] = s[mt][j] * c2 + bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
     xs = 1.0f;
   }
   if (__builtin_expect(nvalid < kNK, 0)) {  // ragged last tile of a cluster
@@ -361,12 +357,16 @@ __device__ __forceinline__ void tile_softmax(const f32x16& s0, const f32x16& s1,
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (mt * 32 + 8 * (j / 4) + 4 * h + (j % 4) >= nvalid) x[mt * 16 + j] = -INFINITY;
+        if (mt * 32 + 8 * (j / 4) + 4 * h + (j % 4) >= nvalid) s[mt][j] = -INFINITY;
   }
   // Tree reductions keep the dependency chains short.
   float t8[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t8[i] = fmaxf(fmaxf(x[4 * i], x[4 * i + 1]), fmaxf(x[4 * i + 2], x[4 * i + 3]));
+  for (int i = 0; i < 8; ++i) {
+    const f32x16& v = s[i / 4];
+    const int o = 4 * (i % 4);
+    t8[i] = fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3]));
+  }
   float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])), fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
   mx = fmaxf(mx, swap_halves(mx)) * xs;
   if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0, 0)) {
@@ -381,17 +381,36 @@ __device__ __forceinline__ void tile_softmax(const f32x16& s0, const f32x16& s1,
   }
   const float m_use = st.m == -INFINITY ? 0.0f : st.m;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) x[j] = fast_exp2(__builtin_fmaf(x[j], xs, -m_use));
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[mt][j] = fast_exp2(__builtin_fmaf(s[mt][j], xs, -m_use));
   float s8[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s8[i] = (x[4 * i] + x[4 * i + 1]) + (x[4 * i + 2] + x[4 * i + 3]);
+  for (int i = 0; i < 8; ++i) {
+    const f32x16& v = s[i / 4];
+    const int o = 4 * (i % 4);
+    s8[i] = (v[o] + v[o + 1]) + (v[o + 2] + v[o + 3]);
+  }
   st.l += ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
 }
 
+// P fragment of contraction step ks (keys ks*16 .. ks*16+15): elements s[ks/2][(ks%2)*8 + i].
+__device__ __forceinline__ void p_frag16(Frag16& f, const f32x16 (&s)[2], int ks) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = static_cast<_Float16>(s[ks >> 1][(ks & 1) * 8 + i]);
+}
+template <typename T>
+__device__ __forceinline__ void p_frag(Frag<T>& f, const f32x16 (&s)[2], int ks) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = s[ks >> 1][(ks & 1) * 8 + i];
+  frag_from_f32(f, x);
+}
+
 // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
-// ks*16 + 8*(i/4) + 4*h + i%4, which is x[ks*8 + i]; the V^T fragment reads the same keys.
+// ks*16 + 8*(i/4) + 4*h + i%4; the V^T fragment reads the same keys.
 template <typename T, int D, typename Lds>
-__device__ __forceinline__ void tile_pv(const T* Vt, const float* x, RowState<D>& st, bool pv16) {
+__device__ __forceinline__ void tile_pv(const T* Vt, const f32x16 (&s)[2], RowState<D>& st, bool pv16) {
   using C = Cfg<T, D>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31;
@@ -406,14 +425,14 @@ __device__ __forceinline__ void tile_pv(const T* Vt, const float* x, RowState<D>
     for (int n = 0; n < NF; ++n) {
       const int ks = n / C::DT, dt = n % C::DT;
       if (n + 1 < NF) Lds::vfrag16(va[(n + 1) & 1], Vt, ((n + 1) % C::DT) * 32 + r, (n + 1) / C::DT, h);
-      if (dt == 0) frag16_from_f32(pb, x + ks * 8);
+      if (dt == 0) p_frag16(pb, s, ks);
       st.o[dt] = mma(va[n & 1], pb, st.o[dt]);
     }
   } else {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       Frag<T> pb;
-      frag_from_f32(pb, x + ks * 8);
+      p_frag(pb, s, ks);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         Frag<T> va;
@@ -427,11 +446,10 @@ __device__ __forceinline__ void tile_pv(const T* Vt, const float* x, RowState<D>
 template <typename T, int D, typename Lds, typename Bias>
 __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
                                           const Bias& bias, int nvalid, bool pv16) {
-  f32x16 s0, s1;
-  float x[32];
-  tile_qk<T, D, Lds>(Ks, qf, s0, s1);
-  tile_softmax<T, D>(s0, s1, x, st, c2, bias, nvalid);
-  tile_pv<T, D, Lds>(Vt, x, st, pv16);
+  f32x16 s[2];
+  tile_qk<T, D, Lds>(Ks, qf, s[0], s[1]);
+  tile_softmax<T, D>(s, st, c2, bias, nvalid);
+  tile_pv<T, D, Lds>(Vt, s, st, pv16);
 }
 
 template <typename T, int D>
@@ -697,8 +715,9 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     const T* __restrict__ Q, TO* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
-    int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const T* __restrict__ Kp, const void* __restrict__ Vtp,
-    int tiles_per_head, int first_ctile, const int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
+    int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const int32_t* __restrict__ hmix,
+    const T* __restrict__ Kp, const void* __restrict__ Vtp, int tiles_per_head, int first_ctile,
+    const int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, TO>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
@@ -784,6 +803,11 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     // tile takes its entry from a lane; its V^T format flag is fetched one tile ahead.
     auto kbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::K0 + i * L::KB); };
     auto vbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::V0 + i * L::VB); };
+    // ALL16: every V^T tile of this head is float16 (the usual case), so the tile loop needs
+    // neither the format flags nor the bfloat16 product; it is compiled separately from the
+    // general loop so that the rare format switch does not burden its registers.
+    auto tile_loop = [&](auto all16_tag) {
+    constexpr bool ALL16 = decltype(all16_tag)::value;
     int chunk = lane < ecount ? ent[lane] : 0;
     int chunk_next = 64 + lane < ecount ? ent[64 + lane] : 0;
     int e0 = ecount > 0 ? __builtin_amdgcn_readlane(chunk, 0) : 0;
@@ -793,7 +817,7 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
       dma.issue_k(Kph + tl * kTileBytes, kbuf(0));
       dma.issue_v(Vph + tl * kTileBytes, vbuf(0));
       if (entry_centroid(e0)) write_bias(bias0, tl - first_ctile);
-      pv0 = __builtin_amdgcn_readfirstlane(static_cast<int>(flags_h[tl]));
+      if (!ALL16) pv0 = __builtin_amdgcn_readfirstlane(static_cast<int>(flags_h[tl]));
     }
     wait_vmem();
     __syncthreads();
@@ -813,17 +837,22 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
         dma.issue_k(Kph + tl * kTileBytes, kbuf(bj ^ 1));
         dma.issue_v(Vph + tl * kTileBytes, vbuf(bj ^ 1));
         if (entry_centroid(e1)) write_bias(bias0 + (bj ^ 1) * kNK, tl - first_ctile);
-        pv1 = flags_h[tl];
+        if (!ALL16) pv1 = flags_h[tl];
       }
       tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2,
                                     KeyBias{entry_centroid(e0) ? bias0 + bj * kNK : nullptr}, entry_nvalid(e0),
-                                    pv0 != 0);
+                                    ALL16 || pv0 != 0);
       wait_vmem();
       __syncthreads();
       e0 = e1;
-      pv0 = __builtin_amdgcn_readfirstlane(pv1);
+      if (!ALL16) pv0 = __builtin_amdgcn_readfirstlane(pv1);
       bj ^= 1;
     }
+    };
+    if (sizeof(T) == 2 && hmix[bkv] == 0)
+      tile_loop(std::true_type{});
+    else
+      tile_loop(std::false_type{});
 
     const float l_tot = st.l + swap_halves(st.l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -1033,6 +1062,7 @@ constexpr int kProbeChunk = 2048;
 
 struct PackedKV {
   const int32_t* tile_off;
+  const int32_t* hmix;
   const uint8_t* flags;
   const void* k;
   const void* v;
@@ -1084,7 +1114,7 @@ void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* ls
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   const int grid = min(units, device_cus() * attn_occupancy<T>());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
-                     B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags,
+                     B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags, P.hmix,
                      static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, ctl);
 }
 
@@ -1099,7 +1129,8 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   const float c2 = scale * kLog2e;
   const PackLayout L = pack_layout(B, Hkv, S, D, Ck, sizeof(T));
   const unsigned char* base = static_cast<const unsigned char*>(packed);
-  const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off), base + L.flags, base + L.k, base + L.v,
+  const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off),
+                   reinterpret_cast<const int32_t*>(base + L.hmix), base + L.flags, base + L.k, base + L.v,
                    L.tiles_per_head, L.first_centroid_tile, L.centroid_tiles};
   const size_t rows = static_cast<size_t>(B) * Hm * Cq;
   const int maxe = list_stride(S, Ck);

@@ -26,10 +26,13 @@ namespace {
 
 constexpr int kPackThreads = 256;
 
-// tile_off[c] = first tile of cluster c (exclusive prefix of ceil(n_c / 64)); one workgroup.
+// tile_off[c] = first tile of cluster c (exclusive prefix of ceil(n_c / 64)); clears the
+// per-head format summary hmix[nh].  One workgroup.
 __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __restrict__ offsets, int C,
-                                                             int32_t* __restrict__ tile_off) {
+                                                             int32_t* __restrict__ tile_off, int32_t* __restrict__ hmix,
+                                                             int nh) {
   __shared__ int32_t part[1024];
+  for (int i = threadIdx.x; i < nh; i += blockDim.x) hmix[i] = 0;
   const int per = (C + blockDim.x - 1) / blockDim.x;
   const int c0 = threadIdx.x * per;
   int32_t run = 0;
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int S, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, int C, const int32_t* __restrict__ tile_off, int tiles_per_head,
     T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
-    float* __restrict__ Kbar, float* __restrict__ Vbar) {
+    int32_t* __restrict__ hmix, float* __restrict__ Kbar, float* __restrict__ Vbar) {
   constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;                            // chunks per row
   constexpr int kItems = kPackTile * CPR / kPackThreads;  // (key, chunk) items per thread
@@ -112,7 +115,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).
     if constexpr (sizeof(T) == 2) {
       const bool f16 = emax_s <= 142u && emax_s >= 119u;  // bfloat16 exponent 142: [2^15, 2^16); 119: 2^-8
-      if (t == 0) flags[tile] = f16 ? 1 : 0;
+      if (t == 0) {
+        flags[tile] = f16 ? 1 : 0;
+        if (!f16) atomicOr(&hmix[bh], 1);
+      }
       for (int idx = t; idx < D * (kPackTile / 8); idx += kPackThreads) {
         const int d = idx / (kPackTile / 8), k0 = (idx % (kPackTile / 8)) * 8;
         uint32_t w[4];
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
 template <typename T, int D>
 __global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
     const float* __restrict__ Kbar, const float* __restrict__ Vbar, int C, int tiles_per_head, int first_tile,
-    T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags) {
+    T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
+    int32_t* __restrict__ hmix) {
   __shared__ float vmax_s;
   const int j = blockIdx.x;
   const size_t bh = blockIdx.y;
@@ -177,7 +184,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
   __syncthreads();
   if constexpr (sizeof(T) == 2) {
     const bool f16 = vmax_s <= 65504.0f && vmax_s >= 0.00390625f;
-    if (t == 0) flags[tile] = f16 ? 1 : 0;
+    if (t == 0) {
+      flags[tile] = f16 ? 1 : 0;
+      if (!f16) atomicOr(&hmix[bh], 1);
+    }
     for (int idx = t; idx < D * kPackTile; idx += kPackThreads) {
       const int d = idx / kPackTile, pos = idx % kPackTile;
       const int cc = j * kPackTile + vt_key(pos);
@@ -202,15 +212,16 @@ bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, cons
   unsigned char* base = static_cast<unsigned char*>(packed);
   int32_t* tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
   uint8_t* flags = base + L.flags;
+  int32_t* hmix = reinterpret_cast<int32_t*>(base + L.hmix);
   T* Kp = reinterpret_cast<T*>(base + L.k);
   uint16_t* V16 = reinterpret_cast<uint16_t*>(base + L.v);
   float* V32 = reinterpret_cast<float*>(base + L.v);
-  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, tile_off);
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, tile_off, hmix, B * Hkv);
   hipLaunchKernelGGL((pack_cluster_kernel<T, D>), dim3(C, B * Hkv), dim3(kPackThreads), 0, stream,
                      static_cast<const T*>(K), static_cast<const T*>(V), S, perm, offsets, C, tile_off, L.tiles_per_head,
-                     Kp, V16, V32, flags, Kbar, Vbar);
+                     Kp, V16, V32, flags, hmix, Kbar, Vbar);
   hipLaunchKernelGGL((pack_centroid_kernel<T, D>), dim3(L.centroid_tiles, B * Hkv), dim3(kPackThreads), 0, stream,
-                     Kbar, Vbar, C, L.tiles_per_head, L.first_centroid_tile, Kp, V16, V32, flags);
+                     Kbar, Vbar, C, L.tiles_per_head, L.first_centroid_tile, Kp, V16, V32, flags, hmix);
   return launch_status();
 }
 

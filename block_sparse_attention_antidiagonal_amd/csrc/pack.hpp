@@ -10,6 +10,7 @@ constexpr int kPackTile = 64;  // keys per packed tile
 
 // Byte offsets of the packed buffer's sections, and its tile counts.
 //   tile_off  int32 [C + 1]            first tile of each key cluster (shared by all heads)
+//   hmix      int32 [B*Hkv]            nonzero when some V^T tile of the head is bfloat16
 //   flags     uint8 [B*Hkv][tiles]     V^T tile format: 1 = float16 / float32, 0 = bfloat16
 //   k         T     [B*Hkv][tiles][64][D]
 //   v         [B*Hkv][tiles][D][64]    16-bit for bfloat16 inputs, float32 for float32 inputs;
@@ -18,7 +19,7 @@ constexpr int kPackTile = 64;  // keys per packed tile
 // Per head, token tiles come first (sum over clusters of ceil(n_c / 64) <= ceil(S/64) + C of
 // them), then ceil(C / 64) centroid tiles starting at first_centroid_tile.
 struct PackLayout {
-  size_t tile_off, flags, k, v, total;
+  size_t tile_off, hmix, flags, k, v, total;
   int tiles_per_head, first_centroid_tile, centroid_tiles;
 };
 
@@ -34,6 +35,8 @@ inline PackLayout pack_layout(int B, int Hkv, int S, int D, int C, size_t elem) 
   size_t off = 0;
   L.tile_off = off;
   off = pack_align(off + (static_cast<size_t>(C) + 1) * 4);
+  L.hmix = off;
+  off = pack_align(off + static_cast<size_t>(B) * Hkv * 4);
   L.flags = off;
   off = pack_align(off + nt);
   L.k = off;

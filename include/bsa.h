@@ -102,7 +102,8 @@ bsa_status bsa_centroids(int B, int Hkv, int S, int D, int dtype, const void* K,
  *   V^T tile  [D][64 keys]  (keys of each 16-key group stored in the order 0-3, 8-11, 4-7,
  *             12-15) float32 inputs: float32.  bfloat16 inputs: float16 when every
  *             value of the tile is below 2^16 in magnitude and some is at least 2^-8, else
- *             bfloat16 (a per-tile flag records which)
+ *             bfloat16 (a per-tile flag records which, and a per-head word whether any
+ *             tile of the head is bfloat16)
  * plus the first tile of every cluster.  The buffer is opaque to callers: its size comes
  * from bsa_kv_pack_workspace_size, it is valid for the key layout (perm, offsets, C) it was
  * packed with, and bsa_sparse_attention must be given the same offsets.

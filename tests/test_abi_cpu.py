@@ -155,10 +155,11 @@ def test_workspace_sizes(lib):
         40 * ns * (nb + 2 * ntk) * 4
     assert _lib.size_query("bsa_probe_attention_workspace_size", 1, 40, 32760, 128, 64) == 40 * 17 * 64 * 130 * 4
     # packed K/V: per head ceil(S/64) + C token tiles and ceil(C/64) centroid tiles of 64 x D
-    # keys and 64 x D values; sections (cluster tile offsets, tile flags, K, V) 256-byte aligned
+    # keys and 64 x D values; sections (cluster tile offsets, per-head format summary, tile flags,
+    # K, V) 256-byte aligned
     tiles = 40 * (512 + 256 + 4)
     tile_bytes = 64 * 128 * 2
-    expect = 1280 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
+    expect = 1280 + 256 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
     assert _lib.size_query("bsa_kv_pack_workspace_size", 1, 40, 32760, 128, 1, 256) == expect
     # attention tile lists: per mask row one int32 per centroid or token tile, plus a count
     # and the work order (one int32 per batch x head x query cluster) with its counter

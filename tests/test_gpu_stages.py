@@ -74,7 +74,8 @@ def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem):
     ctiles = -(-C // 64)
     tph = tok + ctiles
     nt = B * Hkv * tph
-    off_flags = _align(4 * (C + 1))
+    off_hmix = _align(4 * (C + 1))
+    off_flags = off_hmix + _align(4 * B * Hkv)
     off_k = off_flags + _align(nt)
     off_v = off_k + _align(nt * 64 * D * elem)
     tile_off = buf[: 4 * (C + 1)].view(np.int32)
@@ -87,20 +88,35 @@ def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem):
     key_at = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)
     vt_nat = np.empty_like(vt)
     vt_nat[..., key_at] = vt
-    return tile_off, flags, kt, vt_nat, tok
+    hmix = buf[off_hmix: off_hmix + 4 * B * Hkv].view(np.int32)
+    return tile_off, flags, kt, vt_nat, tok, hmix
 
 
 def _as_f16_bits(x):
     return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("dtype,D,sizes", [("bf16", 128, None), ("f32", 64, None), ("bf16", 64, [0, 1, 63, 64, 65, 130, 7])])
-def test_kv_pack(bsa, dtype, D, sizes):
+def scale_v_clusters(wl, scales):
+    """Multiply V of whole clusters by powers of two (exact in bfloat16): {(b, kvh, c): 2^e}."""
+    for (b, h, c), f in scales.items():
+        wl.v[b, h][wl.labels == c] *= f
+    return wl
+
+
+MIXED = {(0, 0, 1): 2.0 ** 17, (0, 1, 2): 2.0 ** -14, (1, 0, 0): 2.0 ** 20}
+
+
+@pytest.mark.parametrize("dtype,D,sizes,mixed", [("bf16", 128, None, False), ("f32", 64, None, False),
+                                                 ("bf16", 64, [0, 1, 63, 64, 65, 130, 7], False),
+                                                 ("bf16", 128, None, True)])
+def test_kv_pack(bsa, dtype, D, sizes, mixed):
     """Packed tiles hold every cluster's keys in layout order, zero-padded to 64, V^T as float16
     exactly when the tile's values fit (else bfloat16), and the centroid tiles; bit-exact."""
-    say(f"kv pack {dtype} D={D} sizes={sizes}")
+    say(f"kv pack {dtype} D={D} sizes={sizes} mixed={mixed}")
     if sizes is None:
         wl = make_custom(13, B=2, Hq=2, Hkv=2, S=1500, D=D, dtype=dtype)
+        if mixed:
+            scale_v_clusters(wl, MIXED)
     else:
         wl = make_custom(14, B=1, Hq=1, Hkv=1, S=sum(sizes), D=D, dtype=dtype, cluster_sizes=sizes,
                          shuffle_labels=True)
@@ -109,7 +125,7 @@ def test_kv_pack(bsa, dtype, D, sizes):
     lay = bsa.cluster_layout(lab, C)
     kv = bsa.kv_pack(dev(wl.k, dtype), dev(wl.v, dtype), lay)
     elem = 2 if dtype == "bf16" else 4
-    tile_off, flags, kt, vt, tok = decode_packed(kv.buffer.cpu().numpy(), B, Hkv, S, D, C, elem)
+    tile_off, flags, kt, vt, tok, hmix = decode_packed(kv.buffer.cpu().numpy(), B, Hkv, S, D, C, elem)
     perm, off, cnt = olay.cluster_layout(wl.labels, C)
     ntiles = -(-cnt // 64)
     assert np.array_equal(tile_off, np.concatenate([[0], np.cumsum(ntiles)]))
@@ -156,6 +172,10 @@ def test_kv_pack(bsa, dtype, D, sizes):
                 else:
                     want_v = vv.T.astype(np.float32)
                 assert np.array_equal(vt[u, t, :, :n], want_v)
+            # per-head summary: nonzero exactly when some token or centroid V^T tile is bfloat16
+            used = [tile_off[c] + j for c in range(C) for j in range(ntiles[c])] + \
+                [tok + j for j in range(-(-C // 64))]
+            assert (hmix[u] != 0) == bool(np.any(flags[u, used] == 0)), (b, h)
 
 
 # ------------------------------------------------------------------ top-p
@@ -271,11 +291,15 @@ def oracle_attention(wl, keep_np, compensate, b, hq):
         ("all_kept", dict(S=1000, D=128, dtype="bf16", mask="all"), True),
         ("nothing_kept_compensated", dict(S=1000, D=128, dtype="bf16", mask="none"), True),
         ("student_t_values", dict(S=1300, D=128, dtype="bf16", v_kind="t3"), True),
+        # heads whose V holds tiles outside float16's range next to all-float16 heads
+        ("mixed_v_formats", dict(S=1500, D=128, dtype="bf16", Hq=2, Hkv=2, B=2), True),
     ],
 )
 def test_sparse_attention(bsa, name, kw, compensate):
     say(f"attention {name}")
     wl = make_custom(100 + len(name), **kw)
+    if name == "mixed_v_formats":
+        scale_v_clusters(wl, MIXED)
     out, lse = run_attention(bsa, wl, wl.mask, compensate, lse=True)
     got = host(out)
     got_lse = lse.cpu().numpy()
