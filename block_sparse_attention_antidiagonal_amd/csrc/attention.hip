@@ -613,26 +613,34 @@ __global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* 
 // heads, which read the same key tiles and (for GQA) share masks -- go to one XCD, query
 // cluster by query cluster, so that workgroups running together on an XCD sweep nearby
 // tiles and hit its L2.  Groups are spread over the XCDs longest-processing-time first by
-// their total tile count.  ctl[x] is XCD x's unit counter, ctl[8 + x] the start of its
-// segment of `order` (ctl[16] = end).  One workgroup.
+// their total tile count.  There are two queues: groups whose V^T tiles are all float16
+// (hmix[group] == 0 with fast_ok) for the float16 kernel, the others for the general one.
+// Queue q uses ctl[32 q + x] as XCD x's unit counter and ctl[32 q + 8 + x] as the start of
+// its segment of `order` (ctl[32 q + 16] = end).  One workgroup.
 constexpr int kOrderThreads = 1024;
 constexpr int kMaxGroups = 2048;
+constexpr int kQueueCtl = 32;  // ints of ctl per queue
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts, int B, int Hq,
-                                                               int Hkv, int Hm, int Cq, int32_t* __restrict__ order,
-                                                               int32_t* __restrict__ ctl) {
+                                                               int Hkv, int Hm, int Cq,
+                                                               const int32_t* __restrict__ hmix, int fast_ok,
+                                                               int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
   __shared__ int wsum[kMaxGroups];
   __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
-  __shared__ int seg[kXcds + 1];
+  __shared__ int seg[2][kXcds + 1];
+  __shared__ long long load[2][kXcds];
+  __shared__ int ngx[2][kXcds];
   const int t = threadIdx.x;
   const int G = Hq / Hkv;
   const int ng = B * Hkv;
   const int per = Cq * G;  // units per group, contiguous in unit numbering
   const int units = ng * per;
-  if (ng > kMaxGroups) {  // too many groups to balance here: plain order, split evenly
+  if (ng > kMaxGroups) {  // too many groups to balance here: plain order in the general queue
     for (int u = t; u < units; u += kOrderThreads) order[u] = u;
     if (t <= kXcds) {
-      ctl[8 + t] = static_cast<int>((static_cast<long long>(units) * t) / kXcds);
+      ctl[8 + t] = 0;  // empty float16 queue
       if (t < kXcds) ctl[t] = 0;
+      ctl[kQueueCtl + 8 + t] = static_cast<int>((static_cast<long long>(units) * t) / kXcds);
+      if (t < kXcds) ctl[kQueueCtl + t] = 0;
     }
     return;
   }
@@ -655,33 +663,35 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   }
   __syncthreads();
   if (t == 0) {
-    // Longest processing time first: each group to the least loaded XCD.
-    long long load[kXcds];
-    int ngx[kXcds];
-    for (int x = 0; x < kXcds; ++x) load[x] = ngx[x] = 0;
+    // Longest processing time first: each group to the least loaded XCD of its queue.
+    for (int q = 0; q < 2; ++q)
+      for (int x = 0; x < kXcds; ++x) load[q][x] = ngx[q][x] = 0;
     for (int r = 0; r < ng; ++r) {
       const int gi = place[r];
+      const int q = (fast_ok && hmix[gi] == 0) ? 0 : 1;
       int xs = 0;
       for (int x = 1; x < kXcds; ++x)
-        if (load[x] < load[xs]) xs = x;
-      load[xs] += wsum[gi];
-      wsum[gi] = xs * kMaxGroups + ngx[xs]++;  // the group's XCD and its slot there
+        if (load[q][x] < load[q][xs]) xs = x;
+      load[q][xs] += wsum[gi];
+      wsum[gi] = (q * kXcds + xs) * kMaxGroups + ngx[q][xs]++;  // queue, XCD and slot of the group
     }
     int run = 0;
-    for (int x = 0; x < kXcds; ++x) {
-      seg[x] = run;
-      ctl[8 + x] = run;
-      ctl[x] = 0;
-      run += ngx[x] * per;
+    for (int q = 0; q < 2; ++q) {
+      for (int x = 0; x < kXcds; ++x) {
+        seg[q][x] = run;
+        ctl[q * kQueueCtl + 8 + x] = run;
+        ctl[q * kQueueCtl + x] = 0;
+        run += ngx[q][x] * per;
+      }
+      seg[q][kXcds] = run;
+      ctl[q * kQueueCtl + 8 + kXcds] = run;
     }
-    seg[kXcds] = run;
-    ctl[8 + kXcds] = run;
   }
   __syncthreads();
   for (int u = t; u < units; u += kOrderThreads) {
     const int bk = u / per;
-    const int x = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
-    order[seg[x] + slot * per + u % per] = u;
+    const int qx = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
+    order[seg[qx / kXcds][qx % kXcds] + slot * per + u % per] = u;
   }
 }
 
@@ -704,14 +714,17 @@ struct AttnLds {
 
 // Workgroups resident per CU: bfloat16 kernels keep two (eight waves, two per SIMD, so
 // one wave's softmax overlaps the other's MFMAs); float32 tiles need the LDS of one.
-template <typename T>
+template <typename T, bool FAST = true>
 constexpr int attn_occupancy() {
-  return sizeof(T) == 2 ? 2 : 1;
+  return (sizeof(T) == 2 && FAST) ? 2 : 1;
 }
 
 // TO: output element type (the input type, or float32 when a correction pass follows).
-template <typename T, int D, bool COMP, typename TO>
-__global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_kernel(
+// FAST: the kernel for heads whose V^T tiles are all float16 (bfloat16 inputs only); the
+// general kernel handles the others with a per-tile format switch.  Each takes its units
+// from its own queue, and keeping the two apart gives each its own register allocation.
+template <typename T, int D, bool COMP, typename TO, bool FAST>
+__global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_attn_kernel(
     const T* __restrict__ Q, TO* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
@@ -733,14 +746,15 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
   // helps the other XCDs once its own is exhausted; -1 ends the loop for every wave at once.
   const int x0 = static_cast<int>(blockIdx.x % kXcds);  // dispatch is round-robin over XCDs
   int tries = 0;                                        // used by thread 0 only
+  int32_t* qctl = ctl + (FAST ? 0 : kQueueCtl);
   for (;;) {
   if (threadIdx.x == 0) {
     int got = -1;
     while (tries < kXcds) {
       const int q = (x0 + tries) % kXcds;
-      const int i = atomicAdd(&ctl[q], 1);
-      if (i < ctl[8 + q + 1] - ctl[8 + q]) {
-        got = ctl[8 + q] + i;
+      const int i = atomicAdd(&qctl[q], 1);
+      if (i < qctl[8 + q + 1] - qctl[8 + q]) {
+        got = qctl[8 + q] + i;
         break;
       }
       ++tries;
@@ -821,8 +835,10 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
     }
     wait_vmem();
     __syncthreads();
-    int bj = 0;
-    for (int p = 0; p < ecount; ++p) {
+    // One tile step on buffer BJ.  The float16 loop passes BJ as a compile-time constant (two
+    // steps per iteration), so LDS addresses fold into the instructions' offsets; the general
+    // loop keeps one step per iteration, which costs it fewer registers.
+    auto step = [&](int p, int BJ) {
       const int pn = p + 1;
       const bool have1 = pn < ecount;
       if ((pn & 63) == 0) {  // entries pn .. pn+63 move in; fetch the block after them
@@ -834,25 +850,29 @@ __global__ __launch_bounds__(kThreads, attn_occupancy<T>()) void sparse_attn_ker
       if (have1) {
         e1 = __builtin_amdgcn_readlane(chunk, pn & 63);
         const int tl = entry_tile(e1);
-        dma.issue_k(Kph + tl * kTileBytes, kbuf(bj ^ 1));
-        dma.issue_v(Vph + tl * kTileBytes, vbuf(bj ^ 1));
-        if (entry_centroid(e1)) write_bias(bias0 + (bj ^ 1) * kNK, tl - first_ctile);
+        dma.issue_k(Kph + tl * kTileBytes, kbuf(BJ ^ 1));
+        dma.issue_v(Vph + tl * kTileBytes, vbuf(BJ ^ 1));
+        if (entry_centroid(e1)) write_bias(bias0 + (BJ ^ 1) * kNK, tl - first_ctile);
         if (!ALL16) pv1 = flags_h[tl];
       }
-      tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2,
-                                    KeyBias{entry_centroid(e0) ? bias0 + bj * kNK : nullptr}, entry_nvalid(e0),
-                                    ALL16 || pv0 != 0);
+      tile_step<T, D, SwzLds<T, D>>(
+          kbuf(BJ), vbuf(BJ), qf, st, c2, KeyBias{entry_centroid(e0) ? bias0 + BJ * kNK : nullptr},
+          entry_nvalid(e0), ALL16 || pv0 != 0);
       wait_vmem();
       __syncthreads();
       e0 = e1;
       if (!ALL16) pv0 = __builtin_amdgcn_readfirstlane(pv1);
-      bj ^= 1;
+    };
+    if constexpr (ALL16) {
+      for (int p = 0; p < ecount; p += 2) {
+        step(p, 0);
+        if (p + 1 < ecount) step(p + 1, 1);
+      }
+    } else {
+      for (int p = 0; p < ecount; ++p) step(p, p & 1);
     }
     };
-    if (sizeof(T) == 2 && hmix[bkv] == 0)
-      tile_loop(std::true_type{});
-    else
-      tile_loop(std::false_type{});
+    tile_loop(std::integral_constant<bool, FAST && sizeof(T) == 2>{});
 
     const float l_tot = st.l + swap_halves(st.l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -1104,15 +1124,15 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <typename T, int D, bool COMP, typename TO>
+template <typename T, int D, bool COMP, typename TO, bool FAST>
 void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
                            float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
                            const PackedKV& P, const int32_t* order, int32_t* ctl, int units) {
   constexpr int LDS = AttnLds<T, D, TO>::TOTAL;
-  auto kern = sparse_attn_kernel<T, D, COMP, TO>;
+  auto kern = sparse_attn_kernel<T, D, COMP, TO, FAST>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  const int grid = min(units, device_cus() * attn_occupancy<T>());
+  const int grid = min(units, device_cus() * attn_occupancy<T, FAST>());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
                      B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags, P.hmix,
                      static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, ctl);
@@ -1142,10 +1162,18 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
   hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
                      kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, order, counter);
-#define BSA_LAUNCH(COMP, TO)                                                                                   \
-  launch_sparse_variant<T, D, COMP, TO>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, \
-                                        entries, counts, maxe, Hm, P, order, counter, units)
+  constexpr bool kHalf = sizeof(T) == 2;  // float16 products exist for bfloat16 inputs only
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, P.hmix,
+                     kHalf ? 1 : 0, order, counter);
+  // The general kernel first (usually without work), then the float16 one.
+#define BSA_LAUNCH(COMP, TO)                                                                                          \
+  do {                                                                                                                 \
+    launch_sparse_variant<T, D, COMP, TO, false>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck,  \
+                                                 keep, entries, counts, maxe, Hm, P, order, counter, units);          \
+    if (kHalf)                                                                                                         \
+      launch_sparse_variant<T, D, COMP, TO, kHalf>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off,   \
+                                                   Ck, keep, entries, counts, maxe, Hm, P, order, counter, units);    \
+  } while (0)
   if (comp) {
     if (out_f32) BSA_LAUNCH(true, float); else BSA_LAUNCH(true, T);
   } else {
