@@ -257,6 +257,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the K/V packing and probe rows on the caller's stream too")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
                     help="launch each kernel K times on its own, then one plain copy (for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -279,6 +281,7 @@ def main() -> int:
     wl = make_config(2)
     wl.probes, wl.lam, wl.rank = PROBES, LAMBDA, RANK
     cfg = bsa.PathConfig.from_workload(wl)
+    cfg.overlap = not args.no_overlap
     path = bsa.SparseAttentionPath(cfg)
     q = torch.from_numpy(wl.q).to(torch.bfloat16).cuda()
     k = torch.from_numpy(wl.k).to(torch.bfloat16).cuda()
@@ -304,10 +307,15 @@ def main() -> int:
     marks = []  # per step: list of (stage, event)
 
     def recorder(step_marks):
+        last = {}  # stream -> its latest event; a stage spans from there to its own mark
+
         def mark(name):
+            stream = torch.cuda.current_stream()
             ev = torch.cuda.Event(enable_timing=True)
-            ev.record()
-            step_marks.append((name, ev))
+            ev.record(stream)
+            if stream.cuda_stream in last:
+                step_marks.append((name, last[stream.cuda_stream], ev))
+            last[stream.cuda_stream] = ev
         return mark
 
     torch.cuda.synchronize()
@@ -322,7 +330,7 @@ def main() -> int:
 
     stages = {}
     for sm in marks:
-        for (_, e0), (name, e1) in zip(sm[:-1], sm[1:]):
+        for name, e0, e1 in sm:
             stages.setdefault(name, []).append(e0.elapsed_time(e1))
     stages_ms = {name: float(np.mean(v)) for name, v in stages.items()}
     attn_ms = stages_ms["attention"]

@@ -7,6 +7,10 @@ top-p mask, labels, compensated attention) and "Sparse-block compensation", sect
 residual correction).  Every stage is one or two kernel launches on the current stream;
 nothing is computed on the host except the probe selection, which depends only on the
 labels and is done once.
+
+Streams: the K/V packing and the dense probe rows depend only on the inputs and the layout,
+so they run on a second stream (default priority) while the scores and the top-p masks run
+on the caller's stream; the attention waits for both.
 """
 
 from __future__ import annotations
@@ -42,6 +46,7 @@ class PathConfig:
     probes: int = 0
     lam: float = 0.1
     rank: int = 16
+    overlap: bool = True  # pack and probe rows on a second stream, beside scores and top-p
 
     @classmethod
     def from_workload(cls, wl) -> "PathConfig":
@@ -76,6 +81,7 @@ class SparseAttentionPath:
         self._pack_buffer = None  # reused across calls
         self._attn_ws = None
         self._o32 = None  # float32 attention rows before the correction
+        self._side = None  # second stream for the mask-independent stages
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -94,22 +100,40 @@ class SparseAttentionPath:
         """Run the path.  With probes the attention keeps its rows in float32, the fit reads
         the probe rows from them, and the correction pass writes every corrected row, rounded
         once; keep_sparse also returns the float32 rows before the correction.
-        ``mark(stage)`` is called after each stage's launches (for stream-ordered timing
-        events)."""
+        ``mark(stage)`` is called after each stage's launches, with the stage's stream current
+        (for stream-ordered timing events; a stage spans from the previous mark on its
+        stream)."""
         cfg = self.cfg
         mark = mark or (lambda name: None)
+        main = torch.cuda.current_stream(q.device)
         mark("start")
         layout = api.cluster_layout(self.labels, cfg.C)
         mark("layout")
-        # One pass over K/V: cluster tiles for the attention kernel and the centroids.
-        kv = api.kv_pack(k, v, layout, self._pack_buffer)
+        side = main
+        if cfg.overlap:
+            if self._side is None:
+                self._side = torch.cuda.Stream(device=q.device)
+            side = self._side
+            side.wait_stream(main)
+        with torch.cuda.stream(side):
+            mark("side")
+            # One pass over K/V: cluster tiles for the attention kernel and the centroids.
+            kv = api.kv_pack(k, v, layout, self._pack_buffer)
+            mark("pack")
+            od = None
+            if cfg.probes:  # exact dense probe rows: independent of the mask
+                od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
+                mark("probe_rows")
+        if side is not main:
+            # Tensors made on the side stream and read on the caller's stream, and the
+            # reverse, stay allocated until both streams are past them.
+            for t in (kv.buffer, kv.kbar, kv.vbar, od):
+                if t is not None:
+                    t.record_stream(main)
+            for t in (layout.perm, layout.offsets, layout.counts, q, k, v):
+                t.record_stream(side)
         self._pack_buffer = kv.buffer
         kbar, vbar = (kv.kbar, kv.vbar) if cfg.compensate else (None, None)
-        mark("pack")
-        od = None
-        if cfg.probes:  # exact dense probe rows: independent of the mask
-            od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
-            mark("probe_rows")
         scores = None
         if cfg.mask_mode == "scored":
             scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
@@ -120,6 +144,9 @@ class SparseAttentionPath:
         else:
             mask = api.mask_from_keep(self.given_keep)
             mark("mask_lists")
+        if side is not main:
+            main.wait_stream(side)
+        mark("join")
         res = PathResult(out=None, layout=layout, mask=mask, scores=scores, kbar=kbar, vbar=vbar)
         if self._attn_ws is None:
             self._attn_ws = api.attention_workspace(q, kv, layout, mask)
