@@ -42,12 +42,42 @@ struct FitSmem {
   double eval[kN];
   double u[kMaxRank];  // (mu / sigma)^T W V_r
   double dg[kN], od[kN], e2[kN];  // tridiagonal form: diagonal, off-diagonal, off-diagonal squared
-  double pv[kN], wv[kN];          // Householder step vectors
+  double pw[kFitThreads / 64][kN];  // Householder step: partial sums of p = G v per wave
   double lam[kMaxRank];           // the largest eigenvalues, descending
   int order[kN];
   double wave_part[kFitThreads / 64];
   int r_eff;
 };
+
+// Cross-lane moves of a double with DPP (VALU, no LDS round trip): CTRL is the DPP control.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b & 0xffffffffu), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                              static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffu), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                              static_cast<unsigned>(lo));
+}
+// Sum over each 16-lane row: lane pairs, quads, half rows, rows (every lane gets its row's sum).
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  return v;
+}
+// Sum over the wave (every lane gets the total).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = row16_sum(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
 
 // Sum over the workgroup (every thread gets the total).
 __device__ double block_sum(double v, double* part) {
@@ -152,51 +182,49 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   //
   // (1) Step k reflects rows and columns k+1.. so that column k has zeros below the
   // subdiagonal: H = I - 2 v v^T with |v| = 1; the trailing block becomes G - v w^T - w v^T with
-  // w = 2 G v - 2 (v^T G v) v.  v is kept in column k below the diagonal.
-  for (int k = 0; k < kN - 2; ++k) {
-    const int m = kN - 1 - k;
-    double part = 0.0;
-    if (t < m) {
-      const double x = sm.G[k + 1 + t][k];
-      part = x * x;
-    }
-    const double s2 = block_sum(part, sm.wave_part);
-    const double x0 = sm.G[k + 1][k];
-    double alpha = 0.0, vn2 = 0.0;
-    if (s2 > 0.0) {
-      alpha = x0 >= 0.0 ? -sqrt(s2) : sqrt(s2);
-      vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
-    }
-    const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
-    if (t < m) sm.G[k + 1 + t][k] = (sm.G[k + 1 + t][k] - (t == 0 ? alpha : 0.0)) * vinv;
-    if (t == 0) {
-      sm.dg[k] = sm.G[k][k];
-      sm.od[k] = alpha;
-    }
-    __syncthreads();
-    if (!(vn2 > 0.0)) continue;  // the column is already zero: H = I
-    {  // p = G_sub v, four threads per row
-      const int i = t >> 2, q = t & 3;
-      double acc = 0.0;
-      if (i < m)
-        for (int j = q; j < m; j += 4) acc += sm.G[k + 1 + i][k + 1 + j] * sm.G[k + 1 + j][k];
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (i < m && q == 0) sm.pv[i] = acc;
-    }
-    __syncthreads();
-    const double vp = block_sum(t < m ? sm.G[k + 1 + t][k] * sm.pv[t] : 0.0, sm.wave_part);
-    if (t < m) sm.wv[t] = 2.0 * sm.pv[t] - 2.0 * vp * sm.G[k + 1 + t][k];
-    __syncthreads();
-    {  // G_sub -= v w^T + w v^T: thread t owns column t % 64 of rows t / 64, +4, ...
-      const int j = t & 63;
-      if (j < m) {
-        const double vj = sm.G[k + 1 + j][k], wj = sm.wv[j];
-        for (int i = t >> 6; i < m; i += 4)
-          sm.G[k + 1 + i][k + 1 + j] -= sm.G[k + 1 + i][k] * wj + sm.wv[i] * vj;
+  // w = 2 G v - 2 (v^T G v) v.  v is kept in column k below the diagonal.  G stays symmetric,
+  // so every wave reads the column as row k (lane = element) and forms v itself; wave q
+  // handles rows k+1+q, k+5+q, ... of p = G v (partial sums over its rows, added after the
+  // first barrier) and of the update.  Lanes index columns, so LDS rows are read whole.
+  {
+    const int wave = t >> 6, lane = t & 63;
+    for (int k = 0; k < kN - 2; ++k) {
+      const bool act = lane > k;  // trailing column
+      const double x = act ? sm.G[k][lane] : 0.0;
+      const double s2 = wave_sum_f64(x * x);
+      const double x0 = readlane_f64(x, k + 1);
+      double alpha = 0.0, vn2 = 0.0;
+      if (s2 > 0.0) {
+        alpha = x0 >= 0.0 ? -sqrt(s2) : sqrt(s2);
+        vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
       }
+      const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
+      const double v = act ? (x - (lane == k + 1 ? alpha : 0.0)) * vinv : 0.0;
+      double acc = 0.0;  // sum over this wave's rows c of G[c][lane] v_c
+      for (int c = k + 1 + wave; c < kN; c += kFitThreads / 64) acc += sm.G[c][lane] * readlane_f64(v, c);
+      sm.pw[wave][lane] = acc;
+      __syncthreads();  // partial products complete; every wave has read row k
+      if (wave == 0) {
+        if (act) sm.G[lane][k] = v;
+        if (lane == 0) {
+          sm.dg[k] = sm.G[k][k];
+          sm.od[k] = alpha;
+        }
+      }
+      if (vn2 > 0.0) {  // else the column is already zero: H = I
+        double pl = 0.0;
+        if (act) {
+#pragma unroll
+          for (int q = 0; q < kFitThreads / 64; ++q) pl += sm.pw[q][lane];
+        }
+        const double vp = wave_sum_f64(v * pl);
+        const double w = 2.0 * pl - 2.0 * vp * v;
+        if (act)
+          for (int c = k + 1 + wave; c < kN; c += kFitThreads / 64)
+            sm.G[c][lane] -= readlane_f64(v, c) * w + readlane_f64(w, c) * v;
+      }
+      __syncthreads();  // the trailing block is updated
     }
-    __syncthreads();
   }
   if (t == 0) {
     sm.dg[kN - 2] = sm.G[kN - 2][kN - 2];
@@ -219,11 +247,12 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   }
   const double span = fmax(ghi - glo, 1e-300);
   const double pivmin = 1e-290 * fmax(1.0, emax2);
+  // Only the signs of the pivots matter, so the hardware reciprocal stands in for division.
   auto below = [&](double x) {
     int neg = 0;
     double q = 1.0;
     for (int i = 0; i < kN; ++i) {
-      q = (sm.dg[i] - x) - (i > 0 ? sm.e2[i - 1] / q : 0.0);
+      q = (sm.dg[i] - x) - (i > 0 ? sm.e2[i - 1] * __builtin_amdgcn_rcp(q) : 0.0);
       if (fabs(q) < pivmin) q = -pivmin;
       neg += q < 0.0 ? 1 : 0;
     }
@@ -232,7 +261,7 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   {  // 16 eigenvalues at once: lanes of a 16-lane group probe 16 points of its interval
     const int k = t >> 4, j = t & 15;
     double a = glo - 1e-3 * span, b = ghi + 1e-3 * span;
-    for (int it = 0; it < 14; ++it) {
+    for (int it = 0; it < 13; ++it) {  // 17^13 > 1e15: the interval shrinks to rounding level
       const double x = a + (b - a) * static_cast<double>(j + 1) / 17.0;
       const bool ok = (kN - below(x)) <= k;  // at most k eigenvalues above x: lambda_k <= x
       const unsigned long long mask = __ballot(ok);
@@ -257,31 +286,66 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
 
   // (3) Inverse iteration on T for each kept eigenvalue (one thread per vector): LU of
   // T - lambda I without pivoting (tiny pivots replaced), three solves from a fixed start,
-  // normalized each time.  Column k of E holds the vector, columns 16+k and 32+k U and L.
+  // normalized each time.  The vector lives in registers (the loops are unrolled); column
+  // 16+k of E holds the reciprocal pivots and column 32+k the multipliers; the result goes
+  // to column k.
   if (t < nvec) {
     const int k = t;
     const double lk = sm.lam[k];
     const double tiny = 1e-14 * fmax(fabs(glo), fabs(ghi)) + pivmin;
     double u = sm.dg[0] - lk;
     if (fabs(u) < tiny) u = tiny;
-    sm.e.E[0][16 + k] = u;
+    sm.e.E[0][16 + k] = 1.0 / u;
     for (int i = 1; i < kN; ++i) {
       const double l = sm.od[i - 1] / u;
       u = (sm.dg[i] - lk) - l * sm.od[i - 1];
       if (fabs(u) < tiny) u = tiny;
-      sm.e.E[i][16 + k] = u;
+      sm.e.E[i][16 + k] = 1.0 / u;
       sm.e.E[i][32 + k] = l;
     }
-    for (int i = 0; i < kN; ++i) sm.e.E[i][k] = 1.0 + static_cast<double>((i * 7 + k * 13) % 11) / 11.0;
+    double* x = &sm.e.E[0][k];  // x[i * (kN + 1)] = element i
+    constexpr int RS = kN + 1;
+    for (int i = 0; i < kN; ++i) x[i * RS] = 1.0 + static_cast<double>((i * 7 + k * 13) % 11) / 11.0;
+    // The recurrences run through registers; elements and factors move in blocks of 8 so
+    // their LDS accesses overlap.
     for (int iter = 0; iter < 3; ++iter) {
-      for (int i = 1; i < kN; ++i) sm.e.E[i][k] -= sm.e.E[i][32 + k] * sm.e.E[i - 1][k];
-      sm.e.E[kN - 1][k] /= sm.e.E[kN - 1][16 + k];
-      for (int i = kN - 2; i >= 0; --i)
-        sm.e.E[i][k] = (sm.e.E[i][k] - sm.od[i] * sm.e.E[i + 1][k]) / sm.e.E[i][16 + k];
-      double nrm = 0.0;
-      for (int i = 0; i < kN; ++i) nrm += sm.e.E[i][k] * sm.e.E[i][k];
+      double prev = x[0];
+      for (int i0 = 0; i0 < kN; i0 += 8) {
+        double xb[8], lb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xb[j] = x[(i0 + j) * RS];
+          lb[j] = sm.e.E[i0 + j][32 + k];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (i0 + j > 0) xb[j] -= lb[j] * prev;
+          prev = xb[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[(i0 + j) * RS] = xb[j];
+      }
+      double next = 0.0, nrm = 0.0;
+      for (int i0 = kN - 8; i0 >= 0; i0 -= 8) {
+        double xb[8], ub[8], ob[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xb[j] = x[(i0 + j) * RS];
+          ub[j] = sm.e.E[i0 + j][16 + k];
+          ob[j] = sm.od[i0 + j];
+        }
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+          const double v = (i0 + j == kN - 1) ? xb[j] * ub[j] : (xb[j] - ob[j] * next) * ub[j];
+          xb[j] = v;
+          next = v;
+          nrm += v * v;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[(i0 + j) * RS] = xb[j];
+      }
       const double inv = 1.0 / sqrt(nrm);
-      for (int i = 0; i < kN; ++i) sm.e.E[i][k] *= inv;
+      for (int i = 0; i < kN; ++i) x[i * RS] *= inv;
     }
   }
   __syncthreads();
@@ -289,14 +353,10 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   if (t < 64) {
     for (int k = 0; k < nvec; ++k) {
       for (int j = 0; j < k; ++j) {
-        double dot = sm.e.E[t][j] * sm.e.E[t][k];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        const double dot = wave_sum_f64(sm.e.E[t][j] * sm.e.E[t][k]);
         sm.e.E[t][k] -= dot * sm.e.E[t][j];
       }
-      double nrm = sm.e.E[t][k] * sm.e.E[t][k];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) nrm += __shfl_xor(nrm, o);
+      const double nrm = wave_sum_f64(sm.e.E[t][k] * sm.e.E[t][k]);
       sm.e.E[t][k] *= 1.0 / sqrt(nrm);
     }
   }
@@ -312,10 +372,7 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
           const int i = q + 16 * c;
           if (i > s) dot += sm.G[i][s] * sm.e.E[i][k];
         }
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
-        dot += __shfl_xor(dot, 4);
-        dot += __shfl_xor(dot, 8);
+        dot = row16_sum(dot);
 #pragma unroll
         for (int c = 0; c < kN / 16; ++c) {
           const int i = q + 16 * c;
@@ -365,73 +422,50 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     const int k = e / D, d = e % D;
     if (k < kMaxRank) sm.t.Vr[k][d] = vr[i];
   }
-  // Cholesky, right-looking, one barrier per step: step k subtracts the outer product of the
-  // unscaled column k divided by its pivot; the columns are scaled at the end.  Thread t owns
-  // row t / 4 and the columns congruent to t mod 4.
-  const int ci = t / 4, cj0 = t % 4;
-  for (int k = 0; k < kN - 1; ++k) {
-    if (ci > k) {
-      const double f = sm.G[ci][k] / sm.G[k][k];
-#pragma unroll
-      for (int jj = 0; jj < kN / 4; ++jj) {
-        const int j = cj0 + 4 * jj;
-        if (j > k && j <= ci) sm.G[ci][j] -= f * sm.G[j][k];
+  // G2 = L D L^T (L unit lower triangular, D the pivots) by right-looking elimination on the
+  // whole symmetric matrix: step k subtracts G[i][k] G[k][j] / G[k][k] from both triangles of
+  // the trailing block, so row k stays equal to column k and every access reads an LDS row
+  // whole (lane = column).  Wave q updates rows k+1+q, k+5+q, ...; one barrier per step.
+  // Afterwards G[k][k] = d_k and G[k][i] = G[i][k] = L[i][k] d_k for i > k.
+  {
+    const int wave = t >> 6, lane = t & 63;
+    for (int k = 0; k < kN - 1; ++k) {
+      if (lane > k) {
+        const double rk = sm.G[k][lane] / sm.G[k][k];
+        for (int i = k + 1 + wave; i < kN; i += kFitThreads / 64) sm.G[i][lane] -= sm.G[i][k] * rk;
       }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  // L = column k / sqrt(pivot k) (lower part only; the diagonal becomes sqrt(pivot)).
-  double lrow[kN / 4];
+    // z = G2^-1 Zr: wave q solves right-hand sides 4q .. 4q+3 with lane = row, in registers,
+    // without barriers: L a = Zr (a_k broadcast from lane k), b = D^-1 a, then L^T z = b.
+    constexpr int kRhsPerWave = kMaxRank / (kFitThreads / 64);
+    const double rdl = 1.0 / sm.G[lane][lane];
+    double z[kRhsPerWave];
 #pragma unroll
-  for (int jj = 0; jj < kN / 4; ++jj) {
-    const int j = cj0 + 4 * jj;
-    lrow[jj] = j <= ci ? sm.G[ci][j] / sqrt(sm.G[j][j]) : 0.0;
-  }
-  __syncthreads();
+    for (int r = 0; r < kRhsPerWave; ++r) z[r] = sm.Zr[lane][kRhsPerWave * wave + r];
+    for (int k = 0; k < kN - 1; ++k) {
+      const double g = lane > k ? sm.G[k][lane] * readlane_f64(rdl, k) : 0.0;  // L[lane][k]
 #pragma unroll
-  for (int jj = 0; jj < kN / 4; ++jj) {
-    const int j = cj0 + 4 * jj;
-    if (j <= ci) sm.G[ci][j] = lrow[jj];
-  }
-  __syncthreads();
-  // Solve L y = Zr, then L^T z = y, column by column (one barrier per step): thread t owns
-  // right-hand side t % 16 of rows t / 16 + 16 i.
-  const int rhs = t % kMaxRank, rq = t / kMaxRank;
-  for (int k = 0; k < kN - 1; ++k) {
-    const double yk = sm.Zr[k][rhs] / sm.G[k][k];
-#pragma unroll
-    for (int ii = 0; ii < kN / 16; ++ii) {
-      const int i = rq + 16 * ii;
-      if (i > k) sm.Zr[i][rhs] -= sm.G[i][k] * yk;
+      for (int r = 0; r < kRhsPerWave; ++r) z[r] -= g * readlane_f64(z[r], k);
     }
-    __syncthreads();
-  }
 #pragma unroll
-  for (int ii = 0; ii < kN / 16; ++ii) {
-    const int i = rq + 16 * ii;
-    sm.Zr[i][rhs] /= sm.G[i][i];
-  }
-  __syncthreads();
-  for (int k = kN - 1; k > 0; --k) {
-    const double zk = sm.Zr[k][rhs] / sm.G[k][k];
+    for (int r = 0; r < kRhsPerWave; ++r) z[r] *= rdl;
+    for (int k = kN - 1; k > 0; --k) {
+      const double g = lane < k ? sm.G[k][lane] * rdl : 0.0;  // L[k][lane]
 #pragma unroll
-    for (int ii = 0; ii < kN / 16; ++ii) {
-      const int i = rq + 16 * ii;
-      if (i < k) sm.Zr[i][rhs] -= sm.G[k][i] * zk;
+      for (int r = 0; r < kRhsPerWave; ++r) z[r] -= g * readlane_f64(z[r], k);
     }
-    __syncthreads();
-  }
+    __syncthreads();  // every wave is done reading Zr
 #pragma unroll
-  for (int ii = 0; ii < kN / 16; ++ii) {
-    const int i = rq + 16 * ii;
-    sm.Zr[i][rhs] /= sm.G[i][i];
+    for (int r = 0; r < kRhsPerWave; ++r) sm.Zr[lane][kRhsPerWave * wave + r] = z[r];
   }
   __syncthreads();
   // diag(1/sigma) W V_r = diag(1/sigma) Y^T z (D x r), stored over the eigenvectors.
-  for (int e = t; e < D * r_eff; e += kFitThreads) {
-    const int d = e / r_eff, k = e % r_eff;
+  for (int e = t; e < D * kMaxRank; e += kFitThreads) {  // columns past r_eff are zero
+    const int d = e / kMaxRank, k = e % kMaxRank;
     double v = 0.0;
-    for (int m = 0; m < M; ++m) v += static_cast<double>(sm.Y[m][d]) * sm.Zr[m][k];
+    if (k < r_eff)
+      for (int m = 0; m < M; ++m) v += static_cast<double>(sm.Y[m][d]) * sm.Zr[m][k];
     sm.e.WV[d][k] = v / sm.sig[d];
   }
   __syncthreads();
@@ -442,13 +476,21 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     sm.u[t] = v;
   }
   __syncthreads();
-  // A = diag(1/sigma) (W V_r) V_r^T: one output element per thread pass, rows coalesced.
+  // A = diag(1/sigma) (W V_r) V_r^T: each thread keeps its column of V_r^T in registers (its
+  // column index is the same for all its outputs), rows coalesced.
   float* Ah = Aout + static_cast<size_t>(bh) * D * D;
-  for (int e = t; e < D * D; e += kFitThreads) {
-    const int i = e / D, j = e % D;
-    double a = 0.0;
-    for (int k = 0; k < r_eff; ++k) a += sm.e.WV[i][k] * sm.t.Vr[k][j];
-    Ah[e] = static_cast<float>(a);
+  {
+    static_assert(kFitThreads % 128 == 0, "one column per thread for D up to 128");
+    const int j = t % D;
+    double vcol[kMaxRank];
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) vcol[k] = k < r_eff ? sm.t.Vr[k][j] : 0.0;
+    for (int i = t / D; i < D; i += kFitThreads / D) {
+      double a = 0.0;
+#pragma unroll
+      for (int k = 0; k < kMaxRank; ++k) a += sm.e.WV[i][k] * vcol[k];
+      Ah[i * D + j] = static_cast<float>(a);
+    }
   }
   for (int j = t; j < D; j += kFitThreads) {
     double cj = sm.rbar[j];
