@@ -591,21 +591,24 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(float* __restrict__ O, c
 
 // O_out <- O + O A + c from float32 rows O (the uncorrected attention output), rounded once to
 // bfloat16.  A workgroup stages A^T once (high and low bfloat16 parts, transposed through 4 x 4
-// register blocks) and then walks kCorrRows rows in blocks of 128: (O A)^T = A^T O^T on MFMA with
-// O split into high and low parts as well (hi*hi + hi*lo + lo*hi, float32 accuracy); each lane
-// adds its O entries and c, rounds, and the rows leave through LDS as 16-byte chunks.
+// register blocks); then each wave takes blocks of 32 rows on its own: (O A)^T = A^T O^T on MFMA
+// with O split into high and low parts as well (hi*hi + hi*lo + lo*hi, float32 accuracy).  The
+// contraction runs over each 16-feature group in the order 0-3, 8-11, 4-7, 12-15 (A^T rows are
+// stored that way), so the O entries a lane loads for the products are exactly those of the
+// output features it holds afterwards: the row is read once, into registers.  Partner lanes
+// (same row, other half) swap halves of their results so that each stores 16-byte chunks.
 constexpr int kCorrRows = 1024;
+__device__ __forceinline__ int corr_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
 template <int D>
-__global__ __launch_bounds__(256) void correct_bf16_kernel(const float* __restrict__ Oin, const float* __restrict__ A,
-                                                            const float* __restrict__ cvec, int S,
-                                                            bf16_t* __restrict__ Oout) {
+__global__ __launch_bounds__(256, 1) void correct_bf16_kernel(const float* __restrict__ Oin,
+                                                               const float* __restrict__ A,
+                                                               const float* __restrict__ cvec, int S,
+                                                               bf16_t* __restrict__ Oout) {
   constexpr int ROWA = D + 8;  // A^T staging row (elements; 16-byte aligned rows)
-  constexpr int ZROW = D + 8;  // output staging row (elements)
   extern __shared__ __align__(16) unsigned char smem_corr[];
-  bf16_t* AtH = reinterpret_cast<bf16_t*>(smem_corr);  // A^T rows: At[j][i] = A[i][j]
+  bf16_t* AtH = reinterpret_cast<bf16_t*>(smem_corr);  // A^T rows: At[j][corr_pos(i)] = A[i][j]
   bf16_t* AtL = AtH + D * ROWA;
-  bf16_t* Z = AtL + D * ROWA;  // [128][ZROW]
-  float* cs = reinterpret_cast<float*>(Z + 128 * ZROW);
+  float* cs = reinterpret_cast<float*>(AtL + D * ROWA);
   const int bh = blockIdx.y;
   const float* Ah = A + static_cast<size_t>(bh) * D * D;
   const float* Oh = Oin + static_cast<size_t>(bh) * S * D;
@@ -625,9 +628,9 @@ __global__ __launch_bounds__(256) void correct_bf16_kernel(const float* __restri
         hi[k] = static_cast<float>(hb);
         lo[k] = rowv[k][jj] - hi[k];
       }
-      *reinterpret_cast<uint2*>(AtH + (j0 + jj) * ROWA + i0) =
+      *reinterpret_cast<uint2*>(AtH + (j0 + jj) * ROWA + corr_pos(i0)) =
           make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
-      *reinterpret_cast<uint2*>(AtL + (j0 + jj) * ROWA + i0) =
+      *reinterpret_cast<uint2*>(AtL + (j0 + jj) * ROWA + corr_pos(i0)) =
           make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
     }
   }
@@ -635,21 +638,22 @@ __global__ __launch_bounds__(256) void correct_bf16_kernel(const float* __restri
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int rows_end = min(S, static_cast<int>(blockIdx.x + 1) * kCorrRows);
-  for (int row0 = blockIdx.x * kCorrRows; row0 < rows_end; row0 += 128) {
-    // Output^T tile (D x 32 rows of this wave): A-operand = A^T rows, B-operand = O rows.
-    const int my = row0 + wave * 32 + r;
+  for (int row0 = blockIdx.x * kCorrRows + wave * 32; row0 < rows_end; row0 += 4 * 32) {
+    const int my = row0 + r;
     const float* orow = Oh + static_cast<size_t>(my < S ? my : S - 1) * D;
+    // o[4 jt + q] = features 32 jt + 8 q + 4 h + (0..3) of this lane's row.
+    f32x4 o[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) o[i] = *reinterpret_cast<const f32x4*>(orow + 8 * i + 4 * h);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow + kk * 16 + 8 * h);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow + kk * 16 + 8 * h + 4);
       Frag<bf16_t> oh, ol;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const float x = o[2 * kk + e / 4][e % 4];
         const __bf16 hi = static_cast<__bf16>(x);
         oh.v[e] = hi;
         ol.v[e] = static_cast<__bf16>(x - static_cast<float>(hi));
@@ -664,26 +668,26 @@ __global__ __launch_bounds__(256) void correct_bf16_kernel(const float* __restri
         acc[jt] = mma(al, oh, acc[jt]);
       }
     }
-    // Entry j of acc[jt] is feature jt*32 + 8*(j/4) + 4h + j%4 of this lane's row.
+    // Entry 4q+e of acc[jt] is feature 32 jt + 8 q + 4 h + e, as is o[4 jt + q][e].  Chunk
+    // pair (2c, 2c+1) of 8 features: the lower half (h = 0) stores chunk 2c, the upper half
+    // chunk 2c+1; each gives its partner the 4 values the partner lacks.
+    bf16_t* prow = Ph + static_cast<size_t>(my < S ? my : 0) * D;
 #pragma unroll
-    for (int jt = 0; jt < D / 32; ++jt)
+    for (int c = 0; c < D / 16; ++c) {
+      uint32_t w[2][2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int u = 0; u < 2; ++u) {
+        const int jt = c / 2, q = 2 * (c % 2) + u;
         const int f = jt * 32 + 8 * q + 4 * h;
-        const f32x4 o = *reinterpret_cast<const f32x4*>(orow + f);
-        const uint32_t w0 = pack_bf16x2(o[0] + acc[jt][4 * q] + cs[f], o[1] + acc[jt][4 * q + 1] + cs[f + 1]);
-        const uint32_t w1 = pack_bf16x2(o[2] + acc[jt][4 * q + 2] + cs[f + 2], o[3] + acc[jt][4 * q + 3] + cs[f + 3]);
-        *reinterpret_cast<uint2*>(Z + (wave * 32 + r) * ZROW + f) = make_uint2(w0, w1);
+        const f32x4 ov = o[4 * jt + q];
+        w[u][0] = pack_bf16x2(ov[0] + acc[jt][4 * q] + cs[f], ov[1] + acc[jt][4 * q + 1] + cs[f + 1]);
+        w[u][1] = pack_bf16x2(ov[2] + acc[jt][4 * q + 2] + cs[f + 2], ov[3] + acc[jt][4 * q + 3] + cs[f + 3]);
       }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 128 * (D / 8); e += 256) {
-      const int rr = e / (D / 8), g = e % (D / 8);
-      const int row = row0 + rr;
-      if (row < S)
-        *reinterpret_cast<uint4*>(Ph + static_cast<size_t>(row) * D + g * 8) =
-            *reinterpret_cast<const uint4*>(Z + rr * ZROW + g * 8);
+      const uint32_t got0 = __float_as_uint(swap_halves(__uint_as_float(h ? w[0][0] : w[1][0])));
+      const uint32_t got1 = __float_as_uint(swap_halves(__uint_as_float(h ? w[0][1] : w[1][1])));
+      const uint4 v = h ? make_uint4(got0, got1, w[1][0], w[1][1]) : make_uint4(w[0][0], w[0][1], got0, got1);
+      if (my < S) *reinterpret_cast<uint4*>(prow + 16 * c + 8 * h) = v;
     }
-    __syncthreads();
   }
 }
 
@@ -779,7 +783,7 @@ extern "C" bsa_status bsa_correct(int B, int Hq, int S, int D, int out_dtype, co
   if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
   if (out_dtype == BSA_BF16) {
     const dim3 grid((S + kCorrRows - 1) / kCorrRows, B * Hq);
-    const int smem = 2 * D * (D + 8) * 2 + 128 * (D + 8) * 2 + D * 4;
+    const int smem = 2 * D * (D + 8) * 2 + D * 4;
     if (D == 128) {
       hipFuncSetAttribute(reinterpret_cast<const void*>(correct_bf16_kernel<128>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
