@@ -49,7 +49,27 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
   using C = SStage<T>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem + 2 * C::BUF_BYTES);  // [2][kTile]
-  const int kt = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  // Workgroups are dispatched to the 8 XCDs round-robin in linear order, and each XCD has its
+  // own L2: the tiles of one (batch, head) are mapped to one XCD, query strip by query strip,
+  // so that the workgroups running together there read the same strided rows at about the
+  // same contraction step.  Heads beyond a multiple of 8 keep the plain order.
+  int kt, qt, bh;
+  {
+    const int ntt = ntk * ntk;
+    const int L = static_cast<int>(blockIdx.x + ntk * (blockIdx.y + ntk * blockIdx.z));
+    const int nbh = static_cast<int>(gridDim.z), full = (nbh / kXcds) * kXcds;
+    int tile;
+    if (L < full * ntt) {
+      const int x = L % kXcds, slot = L / kXcds;
+      bh = (slot / ntt) * kXcds + x;
+      tile = slot % ntt;
+    } else {
+      bh = L / ntt;
+      tile = L % ntt;
+    }
+    qt = tile / ntk;
+    kt = tile % ntk;
+  }
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
   const unsigned char* Qh = reinterpret_cast<const unsigned char*>(Q + static_cast<size_t>(bh) * S * D);
   const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (static_cast<size_t>(b) * Hkv + kvh) * S * D);
