@@ -156,7 +156,7 @@ def summarize_profiles(d: str) -> int:
         w_kib = sum(wr[k]) / len(wr[k])
         rd, wt = f_kib * 1024 * fetch_scale, w_kib * 1024 * write_scale
         lines.append(f"| `{k}` | {len(fe[k])} | {f_kib:.0f} | {w_kib:.0f} | {rd / 1e9:.3f} | {wt / 1e9:.3f} |")
-        if k.startswith(ATTN_KERNEL):
+        if k.startswith(ATTN_KERNEL) and (traffic is None or rd + wt > traffic["bytes_per_launch"]):
             traffic = {"kernel": k, "fetch_kib": f_kib, "write_kib": w_kib, "fetch_scale": fetch_scale,
                        "write_scale": write_scale, "read_bytes": rd, "write_bytes": wt,
                        "bytes_per_launch": rd + wt, "source_sha256": kernel_source_hash(),

@@ -623,7 +623,8 @@ constexpr int kQueueCtl = 32;  // ints of ctl per queue
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts, int B, int Hq,
                                                                int Hkv, int Hm, int Cq,
                                                                const int32_t* __restrict__ hmix, int fast_ok,
-                                                               int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
+                                                               int sort_ok, int32_t* __restrict__ order,
+                                                               int32_t* __restrict__ ctl) {
   __shared__ int wsum[kMaxGroups];
   __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
   __shared__ int seg[2][kXcds + 1];
@@ -688,10 +689,33 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
   }
   __syncthreads();
+  // Within a group, units by descending tile count (ties by query cluster): workgroups that
+  // run side by side then sweep the key tiles at similar rates and meet in the L2 more often,
+  // and the longest units start first.  The counts sit in dynamic LDS (sort_ok: it fits).
+  extern __shared__ int ucnt[];
+  if (sort_ok) {
+    for (int u = t; u < units; u += kOrderThreads) {
+      int bk, a, g;
+      decode_unit(u, Cq, G, bk, a, g);
+      const int b = bk / Hkv, kvh = bk % Hkv, hq = kvh * G + g;
+      const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+      ucnt[u] = counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a];
+    }
+    __syncthreads();
+  }
   for (int u = t; u < units; u += kOrderThreads) {
-    const int bk = u / per;
+    const int bk = u / per, j = u % per;
+    int rank = j;
+    if (sort_ok) {
+      const int c = ucnt[u];
+      rank = 0;
+      for (int j2 = 0; j2 < per; ++j2) {
+        const int c2 = ucnt[bk * per + j2];
+        rank += (c2 > c) | ((c2 == c) & (j2 < j));
+      }
+    }
     const int qx = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
-    order[seg[qx / kXcds][qx % kXcds] + slot * per + u % per] = u;
+    order[seg[qx / kXcds][qx % kXcds] + slot * per + rank] = u;
   }
 }
 
@@ -752,10 +776,14 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     int got = -1;
     while (tries < kXcds) {
       const int q = (x0 + tries) % kXcds;
-      const int i = atomicAdd(&qctl[q], 1);
-      if (i < qctl[8 + q + 1] - qctl[8 + q]) {
-        got = qctl[8 + q] + i;
-        break;
+      const int n = qctl[8 + q + 1] - qctl[8 + q];
+      // A plain read first: a queue already drained (or empty) costs no atomic.
+      if (__hip_atomic_load(&qctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+        const int i = atomicAdd(&qctl[q], 1);
+        if (i < n) {
+          got = qctl[8 + q] + i;
+          break;
+        }
       }
       ++tries;
     }
@@ -1163,8 +1191,12 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
                      kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
   constexpr bool kHalf = sizeof(T) == 2;  // float16 products exist for bfloat16 inputs only
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, counts, B, Hq, Hkv, Hm, Cq, P.hmix,
-                     kHalf ? 1 : 0, order, counter);
+  constexpr int kSortLds = 128 * 1024;  // dynamic LDS for the per-unit tile counts of the sort
+  const bool sort_ok = static_cast<size_t>(units) * 4 <= kSortLds;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(order_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      kSortLds);
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), sort_ok ? units * 4 : 0, stream, counts, B, Hq,
+                     Hkv, Hm, Cq, P.hmix, kHalf ? 1 : 0, sort_ok ? 1 : 0, order, counter);
   // The general kernel first (usually without work), then the float16 one.
 #define BSA_LAUNCH(COMP, TO)                                                                                          \
   do {                                                                                                                 \
