@@ -176,6 +176,17 @@ __device__ __forceinline__ void swz_frag(Frag<float>& f, const void* base, int r
 
 // Wait for this wave's outstanding global memory operations, tile copies included.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt vmcnt(N): at most N vector memory operations of this wave still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Workgroup barrier for copy pipelines: waits for this wave's LDS operations and then for
+// every wave, but not for outstanding global loads, including copies into LDS, which are
+// awaited explicitly with wait_vmem_n (the compiler's own barrier lowering would wait for all
+// of them).  The memory clobber keeps memory accesses on their side of it.
+__device__ __forceinline__ void pipe_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------------ host helpers
 inline bsa_status launch_status() {

@@ -12,8 +12,9 @@
 // key row j' lists tokens j'*s, ..., j'*s+s-1.  So the strided logits are one GEMM with
 // contraction length stride*D, computed here with MFMA in tiles of 256 x 256 strided rows
 // (8 waves of 128 keys x 64 queries), the operands streaming through LDS in stages of one
-// token column (tt) and 128 bytes of head dimension, copied straight from global memory
-// (gathered through the cluster order) into XOR-swizzled LDS rows, two stages in flight.
+// token column (tt) and 64 bytes of head dimension, copied straight from global memory
+// (gathered through the cluster order) into XOR-swizzled LDS rows through a ring of four
+// stage buffers, three stages in flight.
 // Its epilogue keeps, per strided query row, the tile max, the tile sum of exponentials and
 // the per-block sums relative to that max; a second pass merges the tiles of a row (the
 // full-row softmax), sums the rows of a query block and normalizes.
@@ -25,8 +26,12 @@ namespace {
 
 constexpr int kTile = 256;      // strided rows per tile side
 constexpr int kSThreads = 512;  // 8 waves: 2 (keys) x 4 (queries)
-constexpr int kRowB = 128;      // bytes of one strided row per stage
+constexpr int kRowB = 64;       // bytes of one strided row per stage
+constexpr int kNBuf = 4;        // stage buffers in LDS (kNBuf - 1 stages copied ahead)
 using SRow = Swz<kRowB>;
+static_assert(kNBuf == 4, "the stage waits assume at most two later stages in flight");
+// Source of the zero padding copies: one token row of the widest input (128 float32).
+__device__ const uint4 kZeroRow[32] = {};
 
 template <typename T>
 struct SStage {
@@ -36,7 +41,7 @@ struct SStage {
   static constexpr int BUF_BYTES = 2 * OP_BYTES;                   // keys + queries
   static constexpr int NCH = OP_BYTES / 16 / kSThreads;            // 16-byte chunks per thread per operand
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
-  static constexpr int LDS_BYTES = 2 * BUF_BYTES + 2 * kTile * 4;  // two stages + row reductions
+  static constexpr int LDS_BYTES = kNBuf * BUF_BYTES + 2 * kTile * 4 + 3 * 2 * kTile * 4;  // stages, reductions, tokens
 };
 
 // S^T tile: keys (A operand) x queries (B operand).  Wave w: keys 128*(w/4).., queries 64*(w%4)..
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
                                                                    float* __restrict__ lstat) {
   using C = SStage<T>;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem + 2 * C::BUF_BYTES);  // [2][kTile]
+  float* red = reinterpret_cast<float*>(smem + kNBuf * C::BUF_BYTES);  // [2][kTile]
   // Workgroups are dispatched to the 8 XCDs round-robin in linear order, and each XCD has its
   // own L2: the tiles of one (batch, head) are mapped to one XCD, query strip by query strip,
   // so that the workgroups running together there read the same strided rows at about the
@@ -85,33 +90,63 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
     srow[j] = slot / SRow::CPR;
     scol[j] = SRow::pos(srow[j], slot % SRow::CPR);  // the global chunk that lands in this slot
   }
-  // Token of every slot row for one token column tt (-1: padding, contributes zeros).
-  auto tokens = [&](int tt, int* ktok, int* qtok) {
+  // Tokens of the tile's strided rows, one token column at a time, in an LDS ring of three
+  // columns: tok[c % 3][operand][row] = perm of the row's token in column c.  Each thread
+  // copies one entry (4 bytes) straight from perm, two columns ahead of use, so the token
+  // lookups never wait on a register load.  Rows past the sequence copy perm[0] and are
+  // recognized as padding when used.  Without perm the token is the position itself.
+  int* tok = reinterpret_cast<int*>(smem + kNBuf * C::BUF_BYTES + 2 * kTile * 4);  // [3][2][kTile]
+  auto copy_tokens = [&](int tt) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (perm != nullptr) {
+      const int op = t / kTile, i = t % kTile;  // operand 0 = keys, 1 = queries
+      const int row = (op == 0 ? kt : qt) * kTile + i;
+      const int pos = op == 0 ? row * stride + tt : row * stride + stride - 1 - tt;
+      const int* src = (row < Ns && pos < S) ? perm + pos : perm;
+      __builtin_amdgcn_global_load_lds(src, tok + ((tt % 3) * 2 + op) * kTile + (t & ~63) % kTile, 4, 0, 0);
+    }
+#endif
+  };
+  constexpr int kDC = D * static_cast<int>(sizeof(T)) / kRowB;  // stages per token column
+  // Copy sources of this thread's chunks for one token column: row address plus chunk offset,
+  // or the zero row for padding.  Computed once per column; each stage adds a constant.
+  const unsigned char* ksrc[C::NCH];
+  const unsigned char* qsrc[C::NCH];
+  auto column_sources = [&](int tt) {
+    const int* ktab = tok + ((tt % 3) * 2) * kTile;
+    const int* qtab = ktab + kTile;
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j) {
       const int jk = kt * kTile + srow[j], iq = qt * kTile + srow[j];
       const int pk = jk * stride + tt, pq = iq * stride + stride - 1 - tt;
-      ktok[j] = (jk < Ns && pk < S) ? (perm ? perm[pk] : pk) : -1;
-      qtok[j] = (iq < Ns && pq < S) ? (perm ? perm[pq] : pq) : -1;
+      const bool kval = jk < Ns && pk < S, qval = iq < Ns && pq < S;
+      const int ktk = perm ? ktab[srow[j]] : pk, qtk = perm ? qtab[srow[j]] : pq;
+      const size_t off = scol[j] * 16;
+      // Padding copies zeros from kZeroRow, so that every thread issues the same number of
+      // copies per stage (the stage waits count them).
+      ksrc[j] = (kval ? Kh + static_cast<size_t>(ktk) * D * sizeof(T) : reinterpret_cast<const unsigned char*>(kZeroRow)) + off;
+      qsrc[j] = (qval ? Qh + static_cast<size_t>(qtk) * D * sizeof(T) : reinterpret_cast<const unsigned char*>(kZeroRow)) + off;
     }
   };
-  auto issue = [&](int buf, int dc, const int* ktok, const int* qtok) {
-    unsigned char* As = smem + buf * C::BUF_BYTES;
+  // Stage x (token column x / kDC, bytes (x % kDC) * kRowB of each token row) goes to buffer
+  // x % kNBuf.  Entering token column tt, the tokens of column tt + 2 are copied (into the
+  // ring slot column tt - 1 used).
+  auto issue = [&](int x) {
+    const int xb = x % kNBuf, xd = x % kDC;
+    if (xd == 0) {
+      const int tt = x / kDC;
+      if (tt + 2 < stride) copy_tokens(tt + 2);
+      column_sources(tt);
+    }
+    unsigned char* As = smem + xb * C::BUF_BYTES;
     unsigned char* Bs = As + C::OP_BYTES;
 #pragma unroll
     for (int j = 0; j < C::NCH; ++j) {
       const int slot_base = (j * 8 + wave) * 64;
-      const size_t off = static_cast<size_t>(dc) * sizeof(T) + scol[j] * 16;
-      if (ktok[j] >= 0)
-        __builtin_amdgcn_global_load_lds(Kh + static_cast<size_t>(ktok[j]) * D * sizeof(T) + off,
-                                         As + slot_base * 16, 16, 0, 0);
-      else
-        *reinterpret_cast<uint4*>(As + (slot_base + lane) * 16) = make_uint4(0, 0, 0, 0);
-      if (qtok[j] >= 0)
-        __builtin_amdgcn_global_load_lds(Qh + static_cast<size_t>(qtok[j]) * D * sizeof(T) + off,
-                                         Bs + slot_base * 16, 16, 0, 0);
-      else
-        *reinterpret_cast<uint4*>(Bs + (slot_base + lane) * 16) = make_uint4(0, 0, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_global_load_lds(ksrc[j] + xd * kRowB, As + slot_base * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qsrc[j] + xd * kRowB, Bs + slot_base * 16, 16, 0, 0);
+#endif
     }
   };
 
@@ -121,46 +156,50 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  constexpr int kDC = D / C::KCE;  // stages per token column
-  const int nst = stride * kDC;
-  int ktok[C::NCH], qtok[C::NCH], nktok[C::NCH], nqtok[C::NCH];
-  tokens(0, ktok, qtok);
-  if (stride > 1) tokens(1, nktok, nqtok);
-  issue(0, 0, ktok, qtok);
+  constexpr int kG = kDC > kNBuf ? kDC : kNBuf;  // stages per unrolled group
+  const int nst = stride * kDC;  // a multiple of kG (stride >= 4)
+  copy_tokens(0);
+  if (stride > 1) copy_tokens(1);
   wait_vmem();
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    const int nx = st + 1;
-    if (nx < nst) {
-      const int tt = nx / kDC, dc = (nx % kDC) * C::KCE;
-      if (dc == 0) {  // a new token column: its tokens were fetched one column ahead
 #pragma unroll
-        for (int j = 0; j < C::NCH; ++j) {
-          ktok[j] = nktok[j];
-          qtok[j] = nqtok[j];
-        }
-        if (tt + 1 < stride) tokens(tt + 1, nktok, nqtok);
+  for (int x = 0; x < kNBuf - 1; ++x) issue(x);
+  constexpr int kPerStage = 2 * C::NCH;  // tile copies per thread per stage
+  for (int base = 0; base < nst; base += kG) {
+    // Unrolled so that every buffer index and head-dimension offset is a constant.
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      const int st = base + u;
+      // Stage st is in LDS for every wave (the copies issued after it are the later stages'
+      // and possibly token copies, which only lengthen the wait), and every wave is done with
+      // stage st - 1, whose buffer the next copy refills.
+      const int later = min(kNBuf - 2, nst - 1 - st);
+      if (later >= 2)
+        wait_vmem_n<2 * kPerStage>();
+      else if (later == 1)
+        wait_vmem_n<kPerStage>();
+      else
+        wait_vmem_n<0>();
+      pipe_barrier();
+      if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
+      const unsigned char* As = smem + (u % kNBuf) * C::BUF_BYTES;
+      const unsigned char* Bs = As + C::OP_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        Frag<T> fa[4], fb[2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) swz_frag<SRow>(fa[m], As, kw * 128 + m * 32 + r, ks * 16 + 8 * h);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) swz_frag<SRow>(fb[n], Bs, qw * 64 + n * 32 + r, ks * 16 + 8 * h);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
       }
-      issue(buf ^ 1, dc, ktok, qtok);
     }
-    const unsigned char* As = smem + buf * C::BUF_BYTES;
-    const unsigned char* Bs = As + C::OP_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      Frag<T> fa[4], fb[2];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) swz_frag<SRow>(fa[m], As, kw * 128 + m * 32 + r, ks * 16 + 8 * h);
-#pragma unroll
-      for (int n = 0; n < 2; ++n) swz_frag<SRow>(fb[n], Bs, qw * 64 + n * 32 + r, ks * 16 + 8 * h);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
-    }
-    wait_vmem();
-    __syncthreads();
   }
+  wait_vmem();
+  __syncthreads();
 
   // Epilogue.  acc[m][n][j]: key kt*256 + kw*128 + m*32 + 8*(j/4) + 4*h + j%4,
   //                          query qt*256 + qw*64 + n*32 + r.
