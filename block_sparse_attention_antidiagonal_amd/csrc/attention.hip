@@ -617,13 +617,68 @@ __global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* 
 // (hmix[group] == 0 with fast_ok) for the float16 kernel, the others for the general one.
 // Queue q uses ctl[32 q + x] as XCD x's unit counter and ctl[32 q + 8 + x] as the start of
 // its segment of `order` (ctl[32 q + 16] = end).  One workgroup.
+// Per K/V group (one workgroup each): the group's work, the sum over its units of their tile
+// counts + 1, and with sort_ok the rank of each unit within its group by descending tile count
+// (ties by unit index), else its index.  Unit u of group bk is u = bk * per + j with
+// j = a * G + g (decode_unit).  Dynamic LDS: the group's counts (per ints, sort_ok only).
+constexpr int kGroupThreads = 256;
+constexpr int kMaxSortUnits = 12288;  // units per group ranked in LDS (48 KB)
+__global__ __launch_bounds__(kGroupThreads) void group_rank_kernel(const int32_t* __restrict__ counts, int Hq,
+                                                                   int Hkv, int Hm, int Cq, int sort_ok,
+                                                                   int32_t* __restrict__ rank,
+                                                                   int32_t* __restrict__ gsum) {
+  extern __shared__ int ucnt[];
+  __shared__ int red[kGroupThreads / 64];
+  const int bk = blockIdx.x;
+  const int G = Hq / Hkv;
+  const int per = Cq * G;
+  const int b = bk / Hkv, kvh = bk % Hkv;
+  int local = 0;
+  for (int j = threadIdx.x; j < per; j += kGroupThreads) {
+    const int a = j / G, g = j % G, hq = kvh * G + g;
+    const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+    const int c = counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a];
+    local += c + 1;
+    if (sort_ok) ucnt[j] = c;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupThreads / 64; ++w) tot += red[w];
+    gsum[bk] = tot;
+  }
+  int32_t* rk = rank + static_cast<size_t>(bk) * per;
+  for (int j = threadIdx.x; j < per; j += kGroupThreads) {
+    int r = j;
+    if (sort_ok) {
+      const int c = ucnt[j];
+      r = 0;
+      for (int j2 = 0; j2 < per; ++j2) {
+        const int c2 = ucnt[j2];  // the same address for every lane: a broadcast read
+        r += (c2 > c) | ((c2 == c) & (j2 < j));
+      }
+    }
+    rk[j] = r;
+  }
+}
+
+// Work order of the attention units, from the group totals and ranks above.  K/V groups go
+// to the 8 XCDs longest processing time first (the float16 and the general queue apart);
+// inside an XCD's segment the groups follow in assignment order and a group's units by rank:
+// workgroups that run side by side then sweep the key tiles of one head at similar rates and
+// meet in the L2 more often, and the longest units start first.  ctl: queue q's counters at
+// ctl[32 q + x], its segment starts at ctl[32 q + 8 + x] (x <= 8).
 constexpr int kOrderThreads = 1024;
 constexpr int kMaxGroups = 2048;
 constexpr int kQueueCtl = 32;  // ints of ctl per queue
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts, int B, int Hq,
-                                                               int Hkv, int Hm, int Cq,
-                                                               const int32_t* __restrict__ hmix, int fast_ok,
-                                                               int sort_ok, int32_t* __restrict__ order,
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ gsum,
+                                                               const int32_t* __restrict__ rank, int B, int Hq,
+                                                               int Hkv, int Cq, const int32_t* __restrict__ hmix,
+                                                               int fast_ok, int32_t* __restrict__ order,
                                                                int32_t* __restrict__ ctl) {
   __shared__ int wsum[kMaxGroups];
   __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
@@ -645,15 +700,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
     return;
   }
-  for (int i = t; i < ng; i += kOrderThreads) wsum[i] = 0;
-  __syncthreads();
-  for (int u = t; u < units; u += kOrderThreads) {
-    int bk, a, g;
-    decode_unit(u, Cq, G, bk, a, g);
-    const int b = bk / Hkv, kvh = bk % Hkv, hq = kvh * G + g;
-    const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
-    atomicAdd(&wsum[bk], counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a] + 1);
-  }
+  for (int i = t; i < ng; i += kOrderThreads) wsum[i] = gsum[i];
   __syncthreads();
   // Rank the groups by descending work (ties by index).
   for (int i = t; i < ng; i += kOrderThreads) {
@@ -689,33 +736,10 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
   }
   __syncthreads();
-  // Within a group, units by descending tile count (ties by query cluster): workgroups that
-  // run side by side then sweep the key tiles at similar rates and meet in the L2 more often,
-  // and the longest units start first.  The counts sit in dynamic LDS (sort_ok: it fits).
-  extern __shared__ int ucnt[];
-  if (sort_ok) {
-    for (int u = t; u < units; u += kOrderThreads) {
-      int bk, a, g;
-      decode_unit(u, Cq, G, bk, a, g);
-      const int b = bk / Hkv, kvh = bk % Hkv, hq = kvh * G + g;
-      const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
-      ucnt[u] = counts[(static_cast<size_t>(b) * Hm + hm) * Cq + a];
-    }
-    __syncthreads();
-  }
   for (int u = t; u < units; u += kOrderThreads) {
-    const int bk = u / per, j = u % per;
-    int rank = j;
-    if (sort_ok) {
-      const int c = ucnt[u];
-      rank = 0;
-      for (int j2 = 0; j2 < per; ++j2) {
-        const int c2 = ucnt[bk * per + j2];
-        rank += (c2 > c) | ((c2 == c) & (j2 < j));
-      }
-    }
+    const int bk = u / per;
     const int qx = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
-    order[seg[qx / kXcds][qx % kXcds] + slot * per + rank] = u;
+    order[seg[qx / kXcds][qx % kXcds] + slot * per + rank[u]] = u;
   }
 }
 
@@ -1125,7 +1149,7 @@ inline int list_stride(int S, int Ck) {
 // Workspace of the attention: tile entries [rows][stride], counts [rows], the work order
 // [units] and the unit counter.
 struct AttnWs {
-  size_t entries, counts, order, counter, total;
+  size_t entries, counts, order, rank, gsum, counter, total;
 };
 inline AttnWs attn_ws(int B, int Hq, int Hm, int Cq, int S, int Ck) {
   const size_t rows = static_cast<size_t>(B) * Hm * Cq;
@@ -1134,7 +1158,9 @@ inline AttnWs attn_ws(int B, int Hq, int Hm, int Cq, int S, int Ck) {
   w.entries = 0;
   w.counts = pack_align(rows * list_stride(S, Ck) * sizeof(int32_t));
   w.order = w.counts + pack_align(rows * sizeof(int32_t));
-  w.counter = w.order + pack_align(units * sizeof(int32_t));
+  w.rank = w.order + pack_align(units * sizeof(int32_t));
+  w.gsum = w.rank + pack_align(units * sizeof(int32_t));  // one int per K/V group (<= B * Hq)
+  w.counter = w.gsum + pack_align(static_cast<size_t>(B) * Hq * sizeof(int32_t));
   w.total = w.counter + 256;
   return w;
 }
@@ -1187,16 +1213,18 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   int32_t* entries = reinterpret_cast<int32_t*>(wsb + W.entries);
   int32_t* counts = reinterpret_cast<int32_t*>(wsb + W.counts);
   int32_t* order = reinterpret_cast<int32_t*>(wsb + W.order);
+  int32_t* rank = reinterpret_cast<int32_t*>(wsb + W.rank);
+  int32_t* gsum = reinterpret_cast<int32_t*>(wsb + W.gsum);
   int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
   hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
                      kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
   constexpr bool kHalf = sizeof(T) == 2;  // float16 products exist for bfloat16 inputs only
-  constexpr int kSortLds = 128 * 1024;  // dynamic LDS for the per-unit tile counts of the sort
-  const bool sort_ok = static_cast<size_t>(units) * 4 <= kSortLds;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(order_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      kSortLds);
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), sort_ok ? units * 4 : 0, stream, counts, B, Hq,
-                     Hkv, Hm, Cq, P.hmix, kHalf ? 1 : 0, sort_ok ? 1 : 0, order, counter);
+  const int per = Cq * (Hq / Hkv);
+  const bool sort_ok = per <= kMaxSortUnits;
+  hipLaunchKernelGGL(group_rank_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(kGroupThreads),
+                     sort_ok ? per * 4 : 0, stream, counts, Hq, Hkv, Hm, Cq, sort_ok ? 1 : 0, rank, gsum);
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, gsum, rank, B, Hq, Hkv, Cq, P.hmix,
+                     kHalf ? 1 : 0, order, counter);
   // The general kernel first (usually without work), then the float16 one.
 #define BSA_LAUNCH(COMP, TO)                                                                                          \
   do {                                                                                                                 \

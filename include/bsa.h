@@ -173,8 +173,9 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  *   keep/kv_count/kv_idx: block mask with Hm in {1, Hkv, Hq}
  *   packed, packed_bytes: the bsa_kv_pack buffer (BSA_E_WORKSPACE if smaller than its size)
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
- *   ws: workspace of bsa_sparse_attention_workspace_size bytes (each mask row's tile list and the
- *       order in which workgroups take the (batch, head, query cluster) units, longest first)
+ *   ws: workspace of bsa_sparse_attention_workspace_size bytes (each mask row's tile list, each
+ *       K/V group's total work and the rank of each (batch, head, query cluster) unit in its
+ *       group, and the order in which workgroups take the units, longest first)
  * Needs Ck <= 32767.  BSA_E_WORKSPACE if the packed buffer or the workspace is too small.
  */
 bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, int S, int Ck, size_t* bytes_host);

@@ -161,8 +161,11 @@ def test_workspace_sizes(lib):
     tile_bytes = 64 * 128 * 2
     expect = 1280 + 256 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
     assert _lib.size_query("bsa_kv_pack_workspace_size", 1, 40, 32760, 128, 1, 256) == expect
-    # attention tile lists: per mask row one int32 per centroid or token tile, plus a count
-    # and the work order (one int32 per batch x head x query cluster) with its counter
+    # attention tile lists: per mask row one int32 per centroid or token tile, plus a count;
+    # the work order and each unit's rank in its group (one int32 per batch x head x query
+    # cluster each), one total per K/V group (sized for B x Hq groups) and the queue counters
     rows, stride = 40 * 256, 4 + 512 + 256
+    units = 40 * 256
     assert _lib.size_query("bsa_sparse_attention_workspace_size", 1, 40, 40, 256, 32760, 256) == \
-        -(-rows * stride * 4 // 256) * 256 + 2 * (-(-rows * 4 // 256) * 256) + 256
+        -(-rows * stride * 4 // 256) * 256 + (-(-rows * 4 // 256) * 256) + 2 * (-(-units * 4 // 256) * 256) + \
+        (-(-40 * 4 // 256) * 256) + 256
