@@ -13,8 +13,9 @@ Pages (cited by title and section):
          "SVG-EAR -- centroid compensation", "SparsePR -- probe-fitted residual repair",
          "No LSE needed", "Recipe: STA with both repairs", "Deviations from the papers".
   [HMR]  "Dynamic block masks and head-wise mask reuse" (mlx-arsenal research note):
-         sections "XAttention -- anti-diagonal block scoring", "Recipe", "Deviations from
-         the papers", "Out of scope, and why" (padding).
+         sections "XAttention -- anti-diagonal block scoring", "HEART -- head-wise temporal
+         mask reuse", "What mlx-arsenal ships", "Recipe", "Deviations from the papers",
+         "Out of scope, and why" (padding).
   [SPR]  "Partition the Support, Reconstruct the Residual" (paper summary page): the
          paragraphs on Probe-Fitted Residual Reconstruction, group-major permutation and
          grouped-query sharing, and the hard-drop residual statement.
@@ -31,9 +32,13 @@ Stages (module: function):
   repair.ridge_fit               weighted standardized ridge, top-r projection [SPR], [SBC]
   repair.apply_correction        O + dO on every row                           [SPR], [SBC]
   pipeline.run_head              the whole path for one (batch, head)
+  reuse.pooled_summary           token means of Q and K per mask head          [HMR] HEART
+  reuse.l1_drift                 L1 drift from the anchor (optionally relative) [HMR] HEART, Deviations
+  reuse.layer_gate, refresh_decision  per-head refresh with the 40%/80% override [HMR] HEART
+  reuse.HeadMaskCache            two-phase cache of masks and anchors          [HMR] ships, Recipe
 
 Every function above is pinned by a test under tests/ (test_oracle_*.py) against closed
 forms, brute force, library routines or hand-worked fixtures in tests/golden/.
 """
 
-from . import attention, centroids, layout, pipeline, repair, scoring, topp  # noqa: F401
+from . import attention, centroids, layout, pipeline, repair, reuse, scoring, topp  # noqa: F401
