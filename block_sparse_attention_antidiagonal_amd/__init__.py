@@ -1,7 +1,8 @@
 """Block-sparse video-DiT attention for AMD Instinct MI355X (gfx950).
 
 Antidiagonal block scoring, per-row top-p block masks, block-sparse flash attention with
-centroid compensation, and probe-fitted residual repair, as hand-written HIP kernels
+centroid compensation, probe-fitted residual repair, and head-wise reuse of block masks
+across calls (pooled Q/K drift with a layer gate), as hand-written HIP kernels
 behind a C ABI (include/bsa.h, libbsa.so).  This package is the thin Python binding:
 importing it loads libbsa.so and fails if the library has not been built.
 """
@@ -13,6 +14,7 @@ _lib.load()
 from .api import (  # noqa: E402,F401
     BlockMask,
     ClusterLayout,
+    HeadMaskCache,
     PackedKV,
     antidiagonal_block_scores,
     block_sparse_attention,
@@ -23,9 +25,12 @@ from .api import (  # noqa: E402,F401
     gather_rows,
     kv_pack,
     mask_from_keep,
+    mask_reuse_decide,
+    mask_reuse_update,
     probe_apply,
     probe_attention,
     probe_fit,
+    pooled_qk,
     select_probe_rows,
     tile_labels,
     top_p_block_mask,

@@ -26,6 +26,15 @@ SIGNATURES = {
     "bsa_antidiag_scores_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_antidiag_scores": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int,
                             c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_antidiag_scores_heads": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                  c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_pooled_qk_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_pooled_qk": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                      c_void_p, c_size_t, c_void_p],
+    "bsa_mask_reuse_decide": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int,
+                              c_int, c_void_p, c_void_p, c_void_p],
+    "bsa_mask_reuse_update": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_top_p_mask": [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_mask_lists": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
     "bsa_kv_pack_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],

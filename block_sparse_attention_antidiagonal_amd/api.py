@@ -125,8 +125,12 @@ def kv_pack(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout,
 
 def antidiagonal_block_scores(q: torch.Tensor, k: torch.Tensor, layout: Optional[ClusterLayout] = None,
                               block_size: int = 128, stride: int = 16, score_scale: Optional[float] = None,
-                              pool_gqa: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Normalized antidiagonal block scores [B, Hs, nb, nb] (bsa_antidiag_scores)."""
+                              pool_gqa: bool = False, workspace: Optional[torch.Tensor] = None,
+                              heads: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Normalized antidiagonal block scores [B, Hs, nb, nb] (bsa_antidiag_scores).  With
+    ``heads`` (uint8 [B, Hs]) only the flagged heads are scored (bsa_antidiag_scores_heads);
+    the other rows of ``out`` are left as they were."""
     _check_cuda(q, k)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
@@ -136,13 +140,27 @@ def antidiagonal_block_scores(q: torch.Tensor, k: torch.Tensor, layout: Optional
         score_scale = 1.0 / math.sqrt(D)
     nb = -(-S // block_size)
     Hs = Hkv if pool_gqa else Hq
-    scores = torch.empty(B, Hs, nb, nb, dtype=torch.float32, device=q.device)
+    if out is not None:
+        _check_cuda(out)
+        if out.shape != (B, Hs, nb, nb) or out.dtype != torch.float32:
+            raise ValueError("out must be float32 [B, Hs, nb, nb]")
+        scores = out
+    else:
+        scores = torch.empty(B, Hs, nb, nb, dtype=torch.float32, device=q.device)
     nbytes = _lib.size_query("bsa_antidiag_scores_workspace_size", B, Hq, Hkv, S, D, block_size, stride)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, q.device)
-    _lib.call("bsa_antidiag_scores", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k),
-              _ptr(layout.perm) if layout is not None else None, block_size, stride, float(score_scale),
-              int(pool_gqa), _ptr(scores), _ptr(workspace), workspace.numel(), _stream())
+    perm = _ptr(layout.perm) if layout is not None else None
+    if heads is None:
+        _lib.call("bsa_antidiag_scores", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), perm, block_size, stride,
+                  float(score_scale), int(pool_gqa), _ptr(scores), _ptr(workspace), workspace.numel(), _stream())
+    else:
+        _check_cuda(heads)
+        if heads.dtype != torch.uint8 or heads.shape != (B, Hs):
+            raise ValueError("heads must be uint8 [B, Hs]")
+        _lib.call("bsa_antidiag_scores_heads", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), perm, block_size,
+                  stride, float(score_scale), int(pool_gqa), _ptr(heads), _ptr(scores), _ptr(workspace),
+                  workspace.numel(), _stream())
     return scores
 
 
@@ -312,6 +330,105 @@ def probe_apply(o: torch.Tensor, A: torch.Tensor, c: torch.Tensor) -> torch.Tens
     B, Hq, S, D = o.shape
     _lib.call("bsa_probe_apply", B, Hq, S, D, _dtype_code(o), _ptr(o), _ptr(A), _ptr(c), _stream())
     return o
+
+
+# ----------------------------------------------------------------- head-wise mask reuse
+
+def pooled_qk(q: torch.Tensor, k: torch.Tensor, Hm: Optional[int] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token means of Q and K per mask head, float32 [B, Hm, D] each (bsa_pooled_qk).
+    Hm defaults to the number of query heads."""
+    _check_cuda(q, k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k shapes/dtypes do not match")
+    Hm = Hq if Hm is None else int(Hm)
+    qbar = torch.empty(B, Hm, D, dtype=torch.float32, device=q.device)
+    kbar = torch.empty_like(qbar)
+    nbytes = _lib.size_query("bsa_pooled_qk_workspace_size", B, Hq, Hkv, S, D)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
+    _lib.call("bsa_pooled_qk", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), Hm, _ptr(qbar), _ptr(kbar),
+              _ptr(workspace), workspace.numel(), _stream())
+    return qbar, kbar
+
+
+def mask_reuse_decide(qbar: torch.Tensor, kbar: torch.Tensor, anchor_q: Optional[torch.Tensor],
+                      anchor_k: Optional[torch.Tensor], delta: float, relative: bool = False,
+                      gate: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Drift from the anchors and the refresh flags (uint8 [B, Hm]) with the optional layer
+    gate (bsa_mask_reuse_decide).  anchor_q None: the first call, every head refreshes."""
+    _check_cuda(qbar, kbar, anchor_q, anchor_k)
+    B, Hm, D = qbar.shape
+    have = anchor_q is not None
+    if have and (anchor_k is None or anchor_q.shape != qbar.shape or anchor_k.shape != qbar.shape):
+        raise ValueError("anchors must match the summaries")
+    drift = torch.empty(B, Hm, dtype=torch.float32, device=qbar.device)
+    refresh = torch.empty(B, Hm, dtype=torch.uint8, device=qbar.device)
+    _lib.call("bsa_mask_reuse_decide", B, Hm, D, _ptr(qbar), _ptr(kbar), _ptr(anchor_q), _ptr(anchor_k), int(have),
+              float(delta), int(relative), int(gate), _ptr(drift), _ptr(refresh), _stream())
+    return drift, refresh
+
+
+def mask_reuse_update(refresh: torch.Tensor, qbar: torch.Tensor, kbar: torch.Tensor, new_mask: Optional[BlockMask],
+                      mask: Optional[BlockMask], anchor_q: torch.Tensor, anchor_k: torch.Tensor) -> None:
+    """Refreshed heads take the new mask rows and move their anchors (bsa_mask_reuse_update)."""
+    _check_cuda(refresh, qbar, kbar, anchor_q, anchor_k)
+    B, Hm, D = qbar.shape
+    if new_mask is not None:
+        _, _, Cq, Ck = new_mask.keep.shape
+        if mask is None or mask.keep.shape != new_mask.keep.shape:
+            raise ValueError("the cached mask must match the new mask")
+        args = (_ptr(new_mask.keep), _ptr(new_mask.kv_count), _ptr(new_mask.kv_idx), _ptr(mask.keep),
+                _ptr(mask.kv_count), _ptr(mask.kv_idx))
+    else:
+        Cq = Ck = 1
+        args = (None, None, None, None, None, None)
+    _lib.call("bsa_mask_reuse_update", B, Hm, Cq, Ck, D, _ptr(refresh), _ptr(qbar), _ptr(kbar), *args, _ptr(anchor_q),
+              _ptr(anchor_k), _stream())
+
+
+class HeadMaskCache:
+    """Per-head block masks and their anchors on the device, used in two phases per step
+    ("Dynamic block masks and head-wise mask reuse", sections "HEART -- head-wise temporal
+    mask reuse", "What mlx-arsenal ships" and "Recipe"):
+
+        refresh = cache.should_refresh(q, k)          # uint8 [B, Hm] on the device
+        scores = antidiagonal_block_scores(q, k, heads=refresh, out=...)   # refreshed heads only
+        mask = cache.update(top_p_block_mask(scores, tau), refresh)
+
+    One cache per layer (and per guidance branch); reset it when the token grid changes."""
+
+    def __init__(self, delta: float, relative: bool = False, gate: bool = True, Hm: Optional[int] = None):
+        self.delta, self.relative, self.gate, self.Hm = float(delta), bool(relative), bool(gate), Hm
+        self.anchor_q: Optional[torch.Tensor] = None
+        self.anchor_k: Optional[torch.Tensor] = None
+        self.mask: Optional[BlockMask] = None
+        self.drift: Optional[torch.Tensor] = None
+        self._cur: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+
+    def reset(self) -> None:
+        self.anchor_q = self.anchor_k = self.mask = self.drift = self._cur = None
+
+    def should_refresh(self, q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+        qbar, kbar = pooled_qk(q, k, self.Hm)
+        self._cur = (qbar, kbar)
+        self.drift, refresh = mask_reuse_decide(qbar, kbar, self.anchor_q, self.anchor_k, self.delta, self.relative,
+                                                self.gate)
+        return refresh
+
+    def update(self, new_mask: BlockMask, refresh: torch.Tensor) -> BlockMask:
+        if self._cur is None:
+            raise RuntimeError("update() needs a preceding should_refresh()")
+        qbar, kbar = self._cur
+        if self.mask is None:  # first step: every head refreshed
+            self.mask = BlockMask(new_mask.keep.clone(), new_mask.kv_count.clone(), new_mask.kv_idx.clone())
+            self.anchor_q, self.anchor_k = qbar.clone(), kbar.clone()
+        else:
+            mask_reuse_update(refresh, qbar, kbar, new_mask, self.mask, self.anchor_q, self.anchor_k)
+        self._cur = None
+        return self.mask
 
 
 def select_probe_rows(labels: np.ndarray, C: int, M: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
                                                                    const int32_t* __restrict__ perm, int Hq, int Hkv,
                                                                    int S, int stride, int Ns, int nb, int ntk, float c2,
                                                                    float* __restrict__ part, float* __restrict__ mstat,
-                                                                   float* __restrict__ lstat) {
+                                                                   float* __restrict__ lstat,
+                                                                   const uint8_t* __restrict__ heads, int Hs) {
   using C = SStage<T>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem + kNBuf * C::BUF_BYTES);  // [2][kTile]
@@ -76,6 +77,9 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
     kt = tile % ntk;
   }
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
+  // Score heads whose mask is kept from an earlier call are not scored (the whole workgroup
+  // leaves before any barrier).
+  if (heads != nullptr && heads[static_cast<size_t>(b) * Hs + (Hs == Hq ? hq : kvh)] == 0) return;
   const unsigned char* Qh = reinterpret_cast<const unsigned char*>(Q + static_cast<size_t>(bh) * S * D);
   const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (static_cast<size_t>(b) * Hkv + kvh) * S * D);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
@@ -305,10 +309,12 @@ template <int R>
 __global__ __launch_bounds__(256) void score_finalize_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ mstat,
                                                               const float* __restrict__ lstat, int Hq, int Hs,
-                                                              int Ns, int nb, int ntk, float* __restrict__ scores) {
+                                                              int Ns, int nb, int ntk, float* __restrict__ scores,
+                                                              const uint8_t* __restrict__ heads) {
   __shared__ float Mrow[R], Lrow[R];
   __shared__ float red[256];
   const int a = blockIdx.x, bhs = blockIdx.y;
+  if (heads != nullptr && heads[bhs] == 0) return;  // row kept from an earlier call
   const int b = bhs / Hs, hs = bhs % Hs;
   const int G = Hq / Hs;
   constexpr int kPerT = 4;  // blocks per thread (nb <= 1024)
@@ -381,7 +387,9 @@ inline ScoreDims score_dims(int S, int block, int stride) {
 
 template <typename T, int D, int R>
 void launch_scores(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const int32_t* perm, int stride,
-                   float score_scale, int pool_gqa, float* scores, void* ws, hipStream_t stream, const ScoreDims& sd) {
+                   float score_scale, int pool_gqa, float* scores, void* ws, hipStream_t stream, const ScoreDims& sd,
+                   const uint8_t* heads) {
+  const int Hs = pool_gqa ? Hkv : Hq;
   float* part = static_cast<float*>(ws);
   float* mstat = part + static_cast<size_t>(B) * Hq * sd.nb * sd.Ns;
   float* lstat = mstat + static_cast<size_t>(B) * Hq * sd.ntk * sd.Ns;
@@ -390,24 +398,48 @@ void launch_scores(int B, int Hq, int Hkv, int S, const void* Q, const void* K, 
                       SStage<T>::LDS_BYTES);
   hipLaunchKernelGGL(kern, dim3(sd.ntk, sd.ntk, B * Hq), dim3(kSThreads), SStage<T>::LDS_BYTES, stream,
                      static_cast<const T*>(Q), static_cast<const T*>(K), perm, Hq, Hkv, S, stride, sd.Ns, sd.nb, sd.ntk,
-                     score_scale * kLog2e, part, mstat, lstat);
-  const int Hs = pool_gqa ? Hkv : Hq;
+                     score_scale * kLog2e, part, mstat, lstat, heads, Hs);
   hipLaunchKernelGGL((score_finalize_kernel<R>), dim3(sd.nb, B * Hs), dim3(256), 0, stream, part, mstat, lstat, Hq, Hs,
-                     sd.Ns, sd.nb, sd.ntk, scores);
+                     sd.Ns, sd.nb, sd.ntk, scores, heads);
 }
 
 template <typename T, int D>
 bsa_status dispatch_r(int R, int B, int Hq, int Hkv, int S, const void* Q, const void* K, const int32_t* perm,
                       int stride, float score_scale, int pool_gqa, float* scores, void* ws, hipStream_t stream,
-                      const ScoreDims& sd) {
+                      const ScoreDims& sd, const uint8_t* heads) {
+#define BSA_R(RR) launch_scores<T, D, RR>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd, heads)
   switch (R) {
-    case 2: launch_scores<T, D, 2>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
-    case 4: launch_scores<T, D, 4>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
-    case 8: launch_scores<T, D, 8>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
-    case 16: launch_scores<T, D, 16>(B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd); break;
+    case 2: BSA_R(2); break;
+    case 4: BSA_R(4); break;
+    case 8: BSA_R(8); break;
+    case 16: BSA_R(16); break;
     default: return BSA_E_UNSUPPORTED;
   }
+#undef BSA_R
   return launch_status();
+}
+
+bsa_status scores_entry(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                        const int32_t* perm, int block, int stride, float score_scale, int pool_gqa, float* scores,
+                        void* ws, size_t ws_bytes, hipStream_t stream, const uint8_t* heads) {
+  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
+  size_t need = 0;
+  bsa_status st = bsa_antidiag_scores_workspace_size(B, Hq, Hkv, S, D, block, stride, &need);
+  if (st != BSA_OK) return st;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (!Q || !K || !scores) return BSA_E_ARG;
+  if (!(score_scale > 0.0f) || !(score_scale < INFINITY)) return BSA_E_ARG;
+  if (pool_gqa != 0 && pool_gqa != 1) return BSA_E_ARG;
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+  const ScoreDims sd = score_dims(S, block, stride);
+  const int R = block / stride;
+  if (dtype == BSA_BF16) {
+    if (D == 128) return dispatch_r<bf16_t, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd, heads);
+    return dispatch_r<bf16_t, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd, heads);
+  }
+  if (D == 128) return dispatch_r<float, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd, heads);
+  return dispatch_r<float, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd, heads);
 }
 
 }  // namespace
@@ -432,22 +464,15 @@ extern "C" bsa_status bsa_antidiag_scores_workspace_size(int B, int Hq, int Hkv,
 extern "C" bsa_status bsa_antidiag_scores(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
                                           const int32_t* perm, int block, int stride, float score_scale, int pool_gqa,
                                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(dtype)) return BSA_E_DTYPE;
-  size_t need = 0;
-  bsa_status st = bsa_antidiag_scores_workspace_size(B, Hq, Hkv, S, D, block, stride, &need);
-  if (st != BSA_OK) return st;
-  if (Hq % Hkv != 0) return BSA_E_SHAPE;
-  if (!Q || !K || !scores) return BSA_E_ARG;
-  if (!(score_scale > 0.0f) || !(score_scale < INFINITY)) return BSA_E_ARG;
-  if (pool_gqa != 0 && pool_gqa != 1) return BSA_E_ARG;
-  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
-  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
-  const ScoreDims sd = score_dims(S, block, stride);
-  const int R = block / stride;
-  if (dtype == BSA_BF16) {
-    if (D == 128) return dispatch_r<bf16_t, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
-    return dispatch_r<bf16_t, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
-  }
-  if (D == 128) return dispatch_r<float, 128>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
-  return dispatch_r<float, 64>(R, B, Hq, Hkv, S, Q, K, perm, stride, score_scale, pool_gqa, scores, ws, stream, sd);
+  return scores_entry(B, Hq, Hkv, S, D, dtype, Q, K, perm, block, stride, score_scale, pool_gqa, scores, ws, ws_bytes,
+                      stream, nullptr);
+}
+
+extern "C" bsa_status bsa_antidiag_scores_heads(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
+                                                const void* K, const int32_t* perm, int block, int stride,
+                                                float score_scale, int pool_gqa, const uint8_t* heads, float* scores,
+                                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!heads) return BSA_E_ARG;
+  return scores_entry(B, Hq, Hkv, S, D, dtype, Q, K, perm, block, stride, score_scale, pool_gqa, scores, ws, ws_bytes,
+                      stream, heads);
 }

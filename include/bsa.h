@@ -138,6 +138,14 @@ bsa_status bsa_antidiag_scores_workspace_size(int B, int Hq, int Hkv, int S, int
 bsa_status bsa_antidiag_scores(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
                                const int32_t* perm, int block, int stride, float score_scale, int pool_gqa,
                                float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* The same scores for selected score heads only ([HMR] "HEART -- head-wise temporal mask reuse":
+ * a head that keeps its mask skips the predictor).  heads: uint8 [B, Hs], nonzero = score this
+ * head; rows of the other heads are left untouched in `scores` (and in the workspace).
+ * BSA_E_ARG when heads is NULL; otherwise as bsa_antidiag_scores. */
+bsa_status bsa_antidiag_scores_heads(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                                     const int32_t* perm, int block, int stride, float score_scale, int pool_gqa,
+                                     const uint8_t* heads, float* scores, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Per-row top-p block mask.  [HMR] "XAttention -- anti-diagonal block scoring": each row
@@ -242,6 +250,54 @@ bsa_status bsa_probe_apply(int B, int Hq, int S, int D, int dtype, void* O, cons
  * [0, S) leave their output row untouched. */
 bsa_status bsa_gather_rows(int BH, int S, int D, const float* X, const int32_t* idx, int M, float* out,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Head-wise temporal mask reuse.  [HMR] "HEART -- head-wise temporal mask reuse" (Temporal
+ * Mask Reuse), "What mlx-arsenal ships" (pooled summary, L1 drift, two-phase cache with an
+ * optional layer gate), "Recipe" (the first call refreshes every head), "Deviations from the
+ * papers" (relative drift).  A step is: bsa_pooled_qk, bsa_mask_reuse_decide, then the
+ * predictor for the refreshed heads (bsa_antidiag_scores_heads + bsa_top_p_mask into fresh
+ * mask buffers), then bsa_mask_reuse_update; attention then reads the cached mask.  The cache
+ * (anchors and mask) is caller-owned device memory; calls only touch the rows of heads
+ * whose refresh flag is set.
+ *
+ * bsa_pooled_qk: the summary of each mask head, the token mean of the queries and keys its
+ * mask serves: Hm == Hq: query head m and its K/V head; Hm == Hkv: the group's query heads
+ * and its K/V head; Hm == 1: all heads.  Float32 sums in a fixed order.
+ *   Q [B, Hq, S, D], K [B, Hkv, S, D] dtype;  qbar, kbar float [B, Hm, D] out
+ *   workspace: bsa_pooled_qk_workspace_size bytes (per-chunk partial sums)
+ * Needs D in {64, 128}, Hq % Hkv == 0, Hm in {Hq, Hkv, 1}.
+ */
+bsa_status bsa_pooled_qk_workspace_size(int B, int Hq, int Hkv, int S, int D, size_t* bytes_host);
+bsa_status bsa_pooled_qk(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K, int Hm,
+                         float* qbar, float* kbar, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* bsa_mask_reuse_decide: drift[b, m] = ||qbar - anchor_q||_1 + ||kbar - anchor_k||_1 over D
+ * (relative = 1: divided by ||anchor_q||_1 + ||anchor_k||_1; a zero anchor norm gives 0 if
+ * nothing moved, +inf otherwise), in float32.  A head asks for a refresh when drift > delta.
+ * gate = 1 applies the layer override per batch entry over its Hm heads: fewer than 40%
+ * asking -> no head refreshes, more than 80% -> every head; otherwise each head's own request.
+ * have_anchor = 0 (the first call; anchors may be NULL): every head refreshes, drift = 0.
+ *   qbar, kbar, anchor_q, anchor_k float [B, Hm, D]
+ *   drift float [B, Hm] out (or NULL);  refresh uint8 [B, Hm] out (1 = rebuild the mask)
+ * BSA_E_ARG for flags outside {0, 1}, a NaN delta or missing pointers.
+ */
+bsa_status bsa_mask_reuse_decide(int B, int Hm, int D, const float* qbar, const float* kbar, const float* anchor_q,
+                                 const float* anchor_k, int have_anchor, float delta, int relative, int gate,
+                                 float* drift, uint8_t* refresh, hipStream_t stream);
+
+/* bsa_mask_reuse_update: for every (b, m) with refresh[b, m] != 0, copy that head's rows of
+ * the new mask into the cached mask and move its anchor to the current summary; other heads
+ * are untouched.  With new_keep == NULL only the anchors move (new_count and new_idx must be
+ * NULL too; the cached mask pointers may then be NULL).
+ *   refresh uint8 [B, Hm];  qbar, kbar float [B, Hm, D];  anchor_q, anchor_k float [B, Hm, D] in/out
+ *   new_keep uint8 [B, Hm, Cq, Ck], new_count int32 [B, Hm, Cq], new_idx int16 [B, Hm, Cq, Ck]
+ *   keep, kv_count, kv_idx: the cached mask, same layouts, in/out
+ */
+bsa_status bsa_mask_reuse_update(int B, int Hm, int Cq, int Ck, int D, const uint8_t* refresh, const float* qbar,
+                                 const float* kbar, const uint8_t* new_keep, const int32_t* new_count,
+                                 const int16_t* new_idx, uint8_t* keep, int32_t* kv_count, int16_t* kv_idx,
+                                 float* anchor_q, float* anchor_k, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Host helpers (host pointers only).
