@@ -217,6 +217,66 @@ def cpu_baseline(wl, seconds_hint=20.0):
     }
 
 
+def measure_reuse(bsa, cfg, q, k, res, reps=10):
+    """Head-wise mask reuse on the same inputs, timed with events on the current stream:
+    the pooled Q/K pass (reads Q and K once), the drift/gate decision, and one cache step
+    (summary + decision + predictor for the refreshed heads + top-p + cache update) when
+    every head rebuilds its mask (a new cache) and when no head does (the same Q and K again,
+    drift 0)."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    score_scale = cfg.score_scale or 1.0 / math.sqrt(cfg.D)
+    Hs = cfg.Hkv if cfg.pool_gqa else cfg.Hq
+    nb = -(-cfg.S // cfg.block)
+    scores = torch.empty(cfg.B, Hs, nb, nb, dtype=torch.float32, device=q.device)
+    ws = torch.empty(bsa._lib.size_query("bsa_antidiag_scores_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D,
+                                         cfg.block, cfg.stride), dtype=torch.uint8, device=q.device)
+    tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(q.device)
+    qbar, kbar = api.pooled_qk(q, k, Hs)
+    pooled_ms = timed(lambda: api.pooled_qk(q, k, Hs))
+    anchors = (qbar.clone(), kbar.clone())
+    decide_ms = timed(lambda: api.mask_reuse_decide(qbar, kbar, *anchors, 1.0))
+
+    def step(cache):
+        refresh = cache.should_refresh(q, k)
+        api.antidiagonal_block_scores(q, k, res.layout, cfg.block, cfg.stride, score_scale, cfg.pool_gqa,
+                                      workspace=ws, heads=refresh, out=scores)
+        return cache.update(api.top_p_block_mask(scores, tau), refresh)
+
+    def rebuild():
+        step(api.HeadMaskCache(delta=1.0))
+
+    warm = api.HeadMaskCache(delta=1.0)
+    step(warm)
+    rebuild_ms = timed(rebuild)
+    reuse_ms = timed(lambda: step(warm))  # same Q and K: drift 0, every head keeps its mask
+    torch.cuda.synchronize()
+    qk_bytes = cfg.B * (cfg.Hq + cfg.Hkv) * cfg.S * cfg.D * q.element_size()
+    gbs = qk_bytes / (pooled_ms * 1e-3) / 1e9
+    return {
+        "pooled_qk_ms": round(pooled_ms, 4),
+        "pooled_qk_GBps": round(gbs, 1),
+        "pooled_qk_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "decide_ms": round(decide_ms, 4),
+        "step_all_rebuild_ms": round(rebuild_ms, 4),
+        "step_all_reuse_ms": round(reuse_ms, 4),
+    }
+
+
 def profile_kernels(bsa, path, cfg, q, k, v, reps):
     """One path call, then `reps` launches of the pack, the scores and the attention alone,
     then one plain device copy of COPY_BYTES (reads and writes that many bytes)."""
@@ -242,6 +302,10 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
                                    workspace=ws)
         torch.cuda.synchronize()
         print(f"[profile] attention {i}", flush=True)
+    for i in range(reps):
+        api.pooled_qk(q, k)
+        torch.cuda.synchronize()
+        print(f"[profile] pooled_qk {i}", flush=True)
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=q.device).fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -391,6 +455,8 @@ def main() -> int:
             "scores_mfma_frac": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
     }
+    print("[bench] mask reuse", file=sys.stderr, flush=True)
+    line["mask_reuse"] = measure_reuse(bsa, cfg, q, k, res)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl)
