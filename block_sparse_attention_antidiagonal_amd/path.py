@@ -82,6 +82,7 @@ class SparseAttentionPath:
         self._attn_ws = None
         self._o32 = None  # float32 attention rows before the correction
         self._side = None  # second stream for the mask-independent stages
+        self._scores = None  # score rows kept across calls when a mask cache is used
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -96,13 +97,16 @@ class SparseAttentionPath:
             self.probe_w = torch.as_tensor(w).to(self.device)
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False,
-                 mark: Optional[Callable[[str], None]] = None) -> PathResult:
+                 mark: Optional[Callable[[str], None]] = None,
+                 cache: Optional[api.HeadMaskCache] = None) -> PathResult:
         """Run the path.  With probes the attention keeps its rows in float32, the fit reads
         the probe rows from them, and the correction pass writes every corrected row, rounded
         once; keep_sparse also returns the float32 rows before the correction.
         ``mark(stage)`` is called after each stage's launches, with the stage's stream current
         (for stream-ordered timing events; a stage spans from the previous mark on its
-        stream)."""
+        stream).  ``cache`` (scored masks only): head-wise mask reuse across calls -- only the
+        heads whose Q/K summaries drifted are scored, and the attention uses the cached mask
+        ("Dynamic block masks and head-wise mask reuse", "Recipe"); one cache per layer."""
         cfg = self.cfg
         mark = mark or (lambda name: None)
         main = torch.cuda.current_stream(q.device)
@@ -135,7 +139,24 @@ class SparseAttentionPath:
         self._pack_buffer = kv.buffer
         kbar, vbar = (kv.kbar, kv.vbar) if cfg.compensate else (None, None)
         scores = None
-        if cfg.mask_mode == "scored":
+        if cfg.mask_mode == "scored" and cache is not None:
+            Hs = cfg.Hkv if cfg.pool_gqa else cfg.Hq
+            if cache.Hm is None:
+                cache.Hm = Hs
+            if cache.Hm != Hs:
+                raise ValueError(f"the cache keeps {cache.Hm} mask heads, the scores have {Hs}")
+            refresh = cache.should_refresh(q, k)
+            mark("reuse_decide")
+            nb = -(-cfg.S // cfg.block)
+            if self._scores is None or self._scores.shape != (cfg.B, Hs, nb, nb):
+                self._scores = torch.empty(cfg.B, Hs, nb, nb, dtype=torch.float32, device=q.device)
+            scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
+                                                   cfg.score_scale or 1.0 / math.sqrt(cfg.D), cfg.pool_gqa,
+                                                   heads=refresh, out=self._scores)
+            mark("scores")
+            mask = cache.update(api.top_p_block_mask(scores, self.tau), refresh)
+            mark("top_p")
+        elif cfg.mask_mode == "scored":
             scores = api.antidiagonal_block_scores(q, k, layout, cfg.block, cfg.stride,
                                                    cfg.score_scale or 1.0 / math.sqrt(cfg.D), cfg.pool_gqa)
             mark("scores")

@@ -201,3 +201,33 @@ def test_cache_steps_match_oracle(bsa):
         for h in range(5):
             if built[h] == 0:
                 assert np.array_equal(mask.keep.cpu().numpy()[0, h], first[0, h])
+
+
+def test_path_with_cache(bsa):
+    """The whole path with a mask cache: the first call equals the path without a cache; a
+    second call on the same inputs reuses every mask and returns the same output; a call where
+    one head's queries moved far rebuilds that head's mask only (other heads' rows equal
+    the first call's)."""
+    from synthetic.workloads import make_custom as mk
+    wl = mk(610, B=1, Hq=5, Hkv=5, S=1024, D=128, dtype="bf16", block=128, mask="scored", probes=0)
+    cfg = bsa.PathConfig.from_workload(wl)
+    cfg.overlap = False
+    path = bsa.SparseAttentionPath(cfg)
+    q, k, v = dev(wl.q, "bf16"), dev(wl.k, "bf16"), dev(wl.v, "bf16")
+    say("path with cache")
+    plain = path(q, k, v).out.float().cpu().numpy()
+    cache = bsa.HeadMaskCache(delta=50.0, gate=False)
+    first = path(q, k, v, cache=cache).out.float().cpu().numpy()
+    assert np.array_equal(first, plain)
+    keep0 = cache.mask.keep.cpu().numpy().copy()
+    again = path(q, k, v, cache=cache).out.float().cpu().numpy()
+    assert np.array_equal(again, first)
+    assert float(cache.drift.max().item()) == 0.0
+    q2 = wl.q.copy()
+    q2[:, 3] = -q2[:, 3] + 3.0  # head 3 only: its mean moves by far more than delta
+    out2 = path(dev(q2, "bf16"), k, v, cache=cache).out.float().cpu().numpy()
+    d = cache.drift.cpu().numpy()[0]
+    assert d[3] > 50.0 and np.all(np.delete(d, 3) == 0.0)
+    keep2 = cache.mask.keep.cpu().numpy()
+    assert np.array_equal(np.delete(keep2, 3, axis=1), np.delete(keep0, 3, axis=1))
+    assert np.array_equal(np.delete(out2, 3, axis=1), np.delete(first, 3, axis=1))
