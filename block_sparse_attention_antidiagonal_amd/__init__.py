@@ -29,6 +29,7 @@ from .api import (  # noqa: E402,F401
     mask_reuse_update,
     probe_apply,
     probe_attention,
+    probe_attention_packed,
     probe_fit,
     pooled_qk,
     select_probe_rows,

@@ -48,6 +48,9 @@ SIGNATURES = {
     "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_probe_attention_packed_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_probe_attention_packed": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_int,
+                                   c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_fit": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, c_void_p,
                       c_void_p],
     "bsa_probe_apply": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],

@@ -312,6 +312,28 @@ def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = N
     return od, os_
 
 
+def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tensor, scale: Optional[float] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact dense probe rows, float32 [B, Hq, M, D], from the packed K/V tiles of kv_pack
+    (bfloat16 inputs; bsa_probe_attention_packed)."""
+    _check_cuda(q, probe_idx)
+    B, Hq, S, D = q.shape
+    if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
+        raise ValueError("packed K/V do not match q")
+    M = probe_idx.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    od = torch.empty(B, Hq, M, D, dtype=torch.float32, device=q.device)
+    C = kv.layout.C
+    nbytes = _lib.size_query("bsa_probe_attention_packed_workspace_size", B, Hq, kv.Hkv, S, D, M, C)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
+    _lib.call("bsa_probe_attention_packed", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
+              _ptr(probe_idx), M, _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), C, _ptr(od),
+              _ptr(workspace), workspace.numel(), _stream())
+    return od
+
+
 def probe_fit(o_sparse_probe: torch.Tensor, o_dense_probe: torch.Tensor, weights: torch.Tensor,
               lam: float = 0.1, rank: int = 16) -> Tuple[torch.Tensor, torch.Tensor]:
     """Folded correction map A [B, Hq, D, D], c [B, Hq, D] from float32 probe rows (bsa_probe_fit)."""

@@ -1110,6 +1110,90 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
   }
 }
 
+// Exact dense probe rows from the packed K/V tiles (bfloat16 inputs): the same rows as the dense
+// pass of probe_partial_kernel, with the keys taken in packed (cluster-major) order, which the
+// softmax does not depend on.  Workgroup (chunk, row tile, head): tiles [chunk * tpc, ...) of
+// the head's token tiles stream through two LDS buffers by global-to-LDS copies, as in the
+// attention kernel; a tile's key count comes from the cluster it belongs to (the last tile
+// of a cluster is ragged) and its V^T format from the pack's flags.  Partial rows, running
+// max and sum go to probe_merge_kernel.  Chunks past the head's last tile write empty partials.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
+    const bf16_t* __restrict__ Q, int Hq, int Hkv, int S, float c2, const int32_t* __restrict__ probe_idx, int M,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C,
+    const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
+    int tiles_per_head, int tpc, int nchunks, float* __restrict__ Opart, float* __restrict__ mpart,
+    float* __restrict__ lpart) {
+  using T = bf16_t;
+  using L = AttnLds<T, D, float>;
+  constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* nv = reinterpret_cast<int*>(smem + L::BIAS);  // key count of each tile of the chunk (tpc <= 2 kNK)
+  const int ci = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
+  const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
+  const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
+  const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
+  const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
+  const int ntiles = tile_off[C];
+  const int t0 = ci * tpc, t1 = min(ntiles, t0 + tpc);
+  // Tile t belongs to cluster c with tile_off[c] <= t < tile_off[c + 1].
+  if (static_cast<int>(threadIdx.x) < t1 - t0) {
+    const int t = t0 + static_cast<int>(threadIdx.x);
+    int lo = 0, hi = C;  // invariant: tile_off[lo] <= t < tile_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_off[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int n = k_off[lo + 1] - k_off[lo];
+    nv[threadIdx.x] = min(kNK, n - kNK * (t - tile_off[lo]));
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int my = qt * kRowsWG + wave * 32 + r;
+  const int qtok = probe_idx[my < M ? my : 0];
+  Frag<T> qf[D / 16];
+  load_q_frags<T, D>(qf, Q + static_cast<size_t>(bh) * S * D + static_cast<size_t>(qtok) * D);
+  __builtin_amdgcn_s_waitcnt(0);
+  RowState<D> st;
+  init_state<D>(st);
+  TileDma<T, D> dma;
+  dma.init();
+  auto kbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::K0 + i * L::KB); };
+  auto vbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::V0 + i * L::VB); };
+  if (t0 < t1) {
+    dma.issue_k(Kph + t0 * kTileBytes, kbuf(0));
+    dma.issue_v(Vph + t0 * kTileBytes, vbuf(0));
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int bj = (t - t0) & 1;
+    if (t + 1 < t1) {
+      dma.issue_k(Kph + (t + 1) * kTileBytes, kbuf(bj ^ 1));
+      dma.issue_v(Vph + (t + 1) * kTileBytes, vbuf(bj ^ 1));
+    }
+    tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2, NoBias{}, nv[t - t0], flags_h[t] != 0);
+    wait_vmem();
+    __syncthreads();
+  }
+  const float l_tot = st.l + swap_halves(st.l);
+  if (my < M) {
+    const size_t prow = (static_cast<size_t>(bh) * nchunks + ci) * M + my;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + 8 * g4 + 4 * h;
+        *reinterpret_cast<f32x4*>(Opart + prow * D + d) =
+            f32x4{st.o[dt][4 * g4], st.o[dt][4 * g4 + 1], st.o[dt][4 * g4 + 2], st.o[dt][4 * g4 + 3]};
+      }
+    if (h == 0) {
+      mpart[prow] = st.m;
+      lpart[prow] = l_tot;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ Opart,
                                                         const float* __restrict__ mpart,
@@ -1271,6 +1355,37 @@ size_t probe_ws_floats(int B, int Hq, int S, int D, int M) {
   return static_cast<size_t>(B) * Hq * nchunks * M * (D + 2);
 }
 
+// Dense probe rows from the packed tiles: chunks of tpc tiles, sized so that about 32 chunks
+// cover the largest possible token-tile count of a head.
+inline int packed_probe_tpc(int first_ctile) { return max(4, min(2 * kNK, (first_ctile + 31) / 32)); }
+inline int packed_probe_chunks(int first_ctile) {
+  const int tpc = packed_probe_tpc(first_ctile);
+  return (first_ctile + tpc - 1) / tpc;
+}
+
+template <int D>
+bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* probe_idx,
+                               int M, const void* packed, const int32_t* k_off, int C, float* Od, void* ws,
+                               hipStream_t stream) {
+  const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
+  const unsigned char* base = static_cast<const unsigned char*>(packed);
+  const int tpc = packed_probe_tpc(PL.first_centroid_tile);
+  const int nchunks = packed_probe_chunks(PL.first_centroid_tile);
+  const int qtiles = (M + kRowsWG - 1) / kRowsWG;
+  float* Opart = static_cast<float*>(ws);
+  float* mpart = Opart + static_cast<size_t>(B) * Hq * nchunks * M * D;
+  float* lpart = mpart + static_cast<size_t>(B) * Hq * nchunks * M;
+  constexpr int LDS = AttnLds<bf16_t, D, float>::TOTAL;
+  auto kern = probe_dense_packed_kernel<D>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  hipLaunchKernelGGL(kern, dim3(nchunks, qtiles, B * Hq), dim3(kThreads), LDS, stream, static_cast<const bf16_t*>(Q),
+                     Hq, Hkv, S, scale * kLog2e, probe_idx, M, reinterpret_cast<const int32_t*>(base + PL.tile_off),
+                     k_off, C, base + PL.flags, reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v,
+                     PL.tiles_per_head, tpc, nchunks, Opart, mpart, lpart);
+  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks, Od);
+  return launch_status();
+}
+
 template <typename T, int D>
 bsa_status launch_probe(int B, int Hq, int Hkv, int S, const void* Q, const void* K, const void* V, float scale,
                         const int32_t* probe_idx, int M, const int32_t* q_labels, const int32_t* k_labels,
@@ -1333,6 +1448,37 @@ extern "C" bsa_status bsa_probe_attention_workspace_size(int B, int Hq, int S, i
   if (M > 1024) return BSA_E_UNSUPPORTED;
   *bytes = probe_ws_floats(B, Hq, S, D, M) * sizeof(float);
   return BSA_OK;
+}
+
+extern "C" bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, int Hkv, int S, int D, int M, int C,
+                                                                 size_t* bytes) {
+  if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || S < 1 || M < 1 || C < 1) return BSA_E_ARG;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
+  *bytes = static_cast<size_t>(B) * Hq * packed_probe_chunks(PL.first_centroid_tile) * M * (D + 2) * sizeof(float);
+  return BSA_OK;
+}
+
+extern "C" bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
+                                                 float scale, const int32_t* probe_idx, int M, const void* packed,
+                                                 size_t packed_bytes, const int32_t* k_offsets, int C,
+                                                 float* O_dense_probe, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  if (dtype != BSA_BF16) return valid_dtype(dtype) ? BSA_E_UNSUPPORTED : BSA_E_DTYPE;
+  size_t need = 0;
+  const bsa_status st = bsa_probe_attention_packed_workspace_size(B, Hq, Hkv, S, D, M, C, &need);
+  if (st != BSA_OK) return st;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (!Q || !probe_idx || !packed || !k_offsets || !O_dense_probe) return BSA_E_ARG;
+  if (M > 1024) return BSA_E_UNSUPPORTED;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
+  if (packed_bytes < pack_layout(B, Hkv, S, D, C, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+  return D == 128 ? launch_probe_packed<128>(B, Hq, Hkv, S, Q, scale, probe_idx, M, packed, k_offsets, C, O_dense_probe,
+                                             ws, stream)
+                  : launch_probe_packed<64>(B, Hq, Hkv, S, Q, scale, probe_idx, M, packed, k_offsets, C, O_dense_probe,
+                                            ws, stream);
 }
 
 extern "C" bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,

@@ -22,7 +22,7 @@ from typing import Callable, Optional
 import numpy as np
 import torch
 
-from . import api
+from . import _lib, api
 
 
 @dataclass
@@ -83,6 +83,7 @@ class SparseAttentionPath:
         self._o32 = None  # float32 attention rows before the correction
         self._side = None  # second stream for the mask-independent stages
         self._scores = None  # score rows kept across calls when a mask cache is used
+        self._probe_ws = None  # dense probe partials (bfloat16 inputs)
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
         if cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
@@ -126,7 +127,14 @@ class SparseAttentionPath:
             mark("pack")
             od = None
             if cfg.probes:  # exact dense probe rows: independent of the mask
-                od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
+                if q.dtype == torch.bfloat16:  # from the packed tiles just written
+                    if self._probe_ws is None:
+                        n = _lib.size_query("bsa_probe_attention_packed_workspace_size", cfg.B, cfg.Hq, cfg.Hkv,
+                                            cfg.S, cfg.D, cfg.probes, cfg.C)
+                        self._probe_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+                    od = api.probe_attention_packed(q, kv, self.probe_idx, cfg.scale, workspace=self._probe_ws)
+                else:
+                    od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
                 mark("probe_rows")
         if side is not main:
             # Tensors made on the side stream and read on the caller's stream, and the

@@ -214,6 +214,22 @@ bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, 
                                const int32_t* k_offsets, const float* Kbar, const float* Vbar, float* O_dense_probe,
                                float* O_sparse_probe, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The dense probe rows of bsa_probe_attention from the packed K/V buffer of bsa_kv_pack
+ * (bfloat16 inputs): the same rows, with the keys visited in the packed cluster-major order
+ * (the softmax over all keys does not depend on it), streamed by tile copies as in the
+ * attention.  packed, packed_bytes: the bsa_kv_pack buffer made from the same K, V and key
+ * layout; k_offsets int32 [C+1] and C: that layout's cluster offsets and count.
+ *   O_dense_probe float [B, Hq, M, D] out
+ * Needs dtype BSA_BF16 (BSA_E_UNSUPPORTED for float32: use bsa_probe_attention), 1 <= M <= 1024,
+ * and workspace of bsa_probe_attention_packed_workspace_size bytes.
+ */
+bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, int Hkv, int S, int D, int M, int C,
+                                                     size_t* bytes_host);
+bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
+                                      const int32_t* probe_idx, int M, const void* packed, size_t packed_bytes,
+                                      const int32_t* k_offsets, int C, float* O_dense_probe, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Ridge fit.  [SPR] Probe-Fitted Residual Reconstruction and [SBC] "Deviations from the
  * papers".  Per (batch, head), from the sparse rows X0 = O_sparse_probe and the exact rows

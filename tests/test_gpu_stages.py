@@ -367,6 +367,32 @@ def test_probe_attention(bsa, dtype, D, M, compensate, Hkv):
         check_output(os_[0, h], ref_s, dtype, f"sparse probe rows h{h}")
 
 
+@pytest.mark.parametrize("D,M,Hkv,sizes,mixed", [(128, 64, 1, None, False), (64, 33, 2, None, False),
+                                                   (128, 130, 2, None, True),
+                                                   (128, 64, 1, [0, 1, 63, 64, 65, 130, 7, 1000, 3000], False)])
+def test_probe_attention_packed(bsa, D, M, Hkv, sizes, mixed):
+    """Dense probe rows from the packed tiles against the oracle's dense rows: ragged and empty
+    clusters (the last tile of a cluster is partial), two row tiles (M = 130), and heads whose
+    V^T tiles are partly bfloat16 (values outside the float16 range)."""
+    say(f"probe rows from packed tiles D={D} M={M} Hkv={Hkv} sizes={sizes} mixed={mixed}")
+    if sizes is None:
+        wl = make_custom(41 + M, B=1, Hq=2, Hkv=Hkv, S=5000, D=D, dtype="bf16")
+        if mixed:
+            scale_v_clusters(wl, {key: f for key, f in MIXED.items() if key[0] < wl.B and key[1] < wl.Hkv})
+    else:
+        wl = make_custom(42, B=1, Hq=2, Hkv=Hkv, S=sum(sizes), D=D, dtype="bf16", cluster_sizes=sizes,
+                         shuffle_labels=True)
+    idx = np.random.default_rng(1).choice(wl.S, size=M, replace=False).astype(np.int32)
+    lay = bsa.cluster_layout(torch.from_numpy(wl.labels).cuda(), wl.C)
+    q, k, v = dev(wl.q, "bf16"), dev(wl.k, "bf16"), dev(wl.v, "bf16")
+    kv = bsa.kv_pack(k, v, lay)
+    od = host(bsa.probe_attention_packed(q, kv, torch.from_numpy(idx).cuda(), wl.scale))
+    for h in range(2):
+        kvh = h // (2 // Hkv)
+        ref = oatt.dense_attention_rows(wl.q[0, h][idx], wl.k[0, kvh], wl.v[0, kvh], wl.scale)
+        check_output(od[0, h], ref, "bf16", f"dense probe rows (packed) h{h}")
+
+
 def fit_inputs(M, D, H=3, seed=0):
     rng = np.random.default_rng(seed)
     xs = rng.standard_normal((1, H, M, D)) * rng.uniform(0.3, 2.0, size=D)
