@@ -9,7 +9,7 @@
 // a two-phase cache as separate steps.  Section "Deviations from the papers": the relative
 // drift divides by the anchor's L1 norm.
 //
-// The summary pass is bound by HBM: it reads Q and K once.  Workgroups own a chunk of 512 rows
+// The summary pass is bound by HBM: it reads Q and K once.  Workgroups own a chunk of 2048 rows
 // of one head; 16-byte loads, a row's chunks on consecutive lanes, float32 sums; the chunk
 // partials are summed by a second kernel in a fixed order, so results do not depend on timing.
 #include "common.hpp"
@@ -18,7 +18,7 @@ namespace bsa {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kPoolRows = 512;  // rows of one head per workgroup
+constexpr int kPoolRows = 2048;  // rows of one head per workgroup
 
 // Partial sums over one chunk of rows of one head (heads 0..Hq-1 of Q, then Hkv heads of K):
 // part[(head * nchunk + chunk) * D + d].

@@ -1,9 +1,9 @@
 """GPU parity of head-wise temporal mask reuse against the oracle (oracle/reuse.py).
 
-Pooled summaries: the kernel sums in float32 (per thread up to 32 rows, then 16 or 32 row
-slots, then the chunks of 512 rows, then the heads of a mask head), so its worst-case
-absolute error is below (32 + 32 + nchunk + G) * 2^-24 * mean|x| per component; the tests
-allow 2e-5 * mean|x| at S = 1000 and 1e-4 * mean|x| at S = 32760.  Drifts are float32 sums
+Pooled summaries: the kernel sums in float32 (per thread up to 128 rows, then 16 or 32 row
+slots, then the chunks of 2048 rows, then the heads of a mask head), so its worst-case
+absolute error is below (128 + 32 + nchunk + G) * 2^-24 * mean|x| per component (< 1e-5
+mean|x|); the tests allow 2e-5 * mean|x| at S <= 4096 and 1e-4 * mean|x| at S = 32760.  Drifts are float32 sums
 of 2D terms: relative error below 2D * 2^-24 plus the summaries' error.  Refresh decisions
 are integers decided by floating point: the thresholds are placed midway between
 consecutive oracle drifts, far from every drift, so both sides decide the same way; then
