@@ -36,9 +36,10 @@ Stages (module: function):
   reuse.l1_drift                 L1 drift from the anchor (optionally relative) [HMR] HEART, Deviations
   reuse.layer_gate, refresh_decision  per-head refresh with the 40%/80% override [HMR] HEART
   reuse.HeadMaskCache            two-phase cache of masks and anchors          [HMR] ships, Recipe
+  static_masks.sliding_tile_block_mask  static sliding-tile (STA) block mask   [SBC] Recipe: STA
 
 Every function above is pinned by a test under tests/ (test_oracle_*.py) against closed
 forms, brute force, library routines or hand-worked fixtures in tests/golden/.
 """
 
-from . import attention, centroids, layout, pipeline, repair, reuse, scoring, topp  # noqa: F401
+from . import attention, centroids, layout, pipeline, repair, reuse, scoring, static_masks, topp  # noqa: F401
