@@ -277,6 +277,53 @@ def measure_reuse(bsa, cfg, q, k, res, reps=10):
     }
 
 
+STA_TILE = (2, 8, 8)  # 128-token tiles of the 21 x 30 x 52 latent grid (edge tiles partial)
+STA_WINDOW = (7, 3, 3)  # tiles: 63 of the 11 x 4 x 7 = 308 tiles per row
+
+
+def measure_sliding_tile(bsa, cfg, wl, q, k, v, reps=5):
+    """The compensated attention on a static sliding-tile mask over the same Q, K, V: tile
+    labels as the clusters and the tile-level mask from the host helper, timed with events on
+    the current stream (the kernel's second workload: a static mask instead of a scored one)."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+
+    T, H, W = wl.grid
+    labels = api.tile_labels(T, H, W, STA_TILE)
+    C = int(labels.max()) + 1
+    nt, nh, nw = (-(-T // STA_TILE[0]), -(-H // STA_TILE[1]), -(-W // STA_TILE[2]))
+    keep_tile = api.sliding_tile_block_mask(nt, nh, nw, (1, 1, 1), STA_WINDOW)
+    layout = api.cluster_layout(torch.from_numpy(labels).to(q.device), C)
+    kv = api.kv_pack(k, v, layout)
+    keep = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(keep_tile, (cfg.B, cfg.Hkv, C, C)))).to(q.device)
+    mask = api.mask_from_keep(keep)
+    ws = api.attention_workspace(q, kv, layout, mask)
+    out = torch.empty_like(q)
+
+    def run():
+        api.block_sparse_attention(q, kv, layout, mask, True, cfg.scale, out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = np.bincount(labels, minlength=C).astype(np.float64)
+    pairs = float((keep_tile.astype(np.float64) @ n) @ n) * cfg.B * cfg.Hq
+    tflops = 4 * cfg.D * pairs / (ms * 1e-3) / 1e12
+    return {
+        "tile": list(STA_TILE), "window_tiles": list(STA_WINDOW), "clusters": C,
+        "density": round(pairs / (cfg.B * cfg.Hq * float(cfg.S) ** 2), 4),
+        "attention_ms": round(ms, 4), "executed_pair_TFLOPs": round(tflops, 2),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def profile_kernels(bsa, path, cfg, q, k, v, reps):
     """One path call, then `reps` launches of the pack, the scores and the attention alone,
     then one plain device copy of COPY_BYTES (reads and writes that many bytes)."""
@@ -457,6 +504,8 @@ def main() -> int:
     }
     print("[bench] mask reuse", file=sys.stderr, flush=True)
     line["mask_reuse"] = measure_reuse(bsa, cfg, q, k, res)
+    print("[bench] sliding-tile mask", file=sys.stderr, flush=True)
+    line["sliding_tile_attention"] = measure_sliding_tile(bsa, cfg, wl, q, k, v)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl)

@@ -33,6 +33,7 @@ from .api import (  # noqa: E402,F401
     probe_fit,
     pooled_qk,
     select_probe_rows,
+    sliding_tile_block_mask,
     tile_labels,
     top_p_block_mask,
 )

@@ -58,6 +58,7 @@ SIGNATURES = {
     "bsa_gather_rows": [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p],
     "bsa_select_probe_rows": [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p],
     "bsa_tile_labels": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
+    "bsa_sliding_tile_mask": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
 }
 _RESTYPES = {"bsa_status_string": ctypes.c_char_p}
 

@@ -463,6 +463,17 @@ def select_probe_rows(labels: np.ndarray, C: int, M: int) -> Tuple[np.ndarray, n
     return idx, w
 
 
+def sliding_tile_block_mask(nT: int, nH: int, nW: int, tile=(1, 1, 1), window=(1, 1, 1)) -> np.ndarray:
+    """Host helper: static sliding-tile keep bits uint8 [N, N] over the cells of a raster
+    nT x nH x nW grid (bsa_sliding_tile_mask); with tile = (1, 1, 1) the cluster-level mask
+    for tile_labels clusters.  Use mask_from_keep to hand it to the attention."""
+    N = nT * nH * nW
+    out = np.empty((N, N), dtype=np.uint8)
+    _lib.call("bsa_sliding_tile_mask", nT, nH, nW, int(tile[0]), int(tile[1]), int(tile[2]), int(window[0]),
+              int(window[1]), int(window[2]), out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
 def tile_labels(T: int, H: int, W: int, tile, chunk: int = 0) -> np.ndarray:
     """Host helper: sliding-tile labels of a raster T x H x W grid (bsa_tile_labels)."""
     out = np.empty(T * H * W, dtype=np.int32)

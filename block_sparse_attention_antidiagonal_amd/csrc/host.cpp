@@ -103,3 +103,38 @@ extern "C" bsa_status bsa_tile_labels(int T, int H, int W, int tt, int th, int t
   for (long long i = 0; i < S; ++i) labels[i] = static_cast<int32_t>(start[tile[i]]++ / chunk);
   return BSA_OK;
 }
+
+// Sliding-tile block mask over the cells of an nT x nH x nW raster grid grouped into tiles of
+// (tt, th, tw) cells: cell i keeps cell j when j's tile lies in the window of i's tile; along
+// each axis the window of `w` tiles around coordinate a starts at min(max(a - w/2, 0),
+// max(n - w, 0)) for n tiles on that axis.
+extern "C" bsa_status bsa_sliding_tile_mask(int nT, int nH, int nW, int tt, int th, int tw, int wt, int wh, int ww,
+                                            uint8_t* keep) {
+  if (!keep || nT < 1 || nH < 1 || nW < 1 || tt < 1 || th < 1 || tw < 1 || wt < 1 || wh < 1 || ww < 1)
+    return BSA_E_ARG;
+  const long long N = static_cast<long long>(nT) * nH * nW;
+  if (N > 65535) return BSA_E_UNSUPPORTED;
+  const int n[3] = {(nT + tt - 1) / tt, (nH + th - 1) / th, (nW + tw - 1) / tw};
+  const int w[3] = {wt, wh, ww};
+  std::vector<int> coord[3];
+  for (int a = 0; a < 3; ++a) coord[a].resize(static_cast<size_t>(N));
+  for (int t = 0; t < nT; ++t)
+    for (int y = 0; y < nH; ++y)
+      for (int x = 0; x < nW; ++x) {
+        const size_t i = (static_cast<size_t>(t) * nH + y) * nW + x;
+        coord[0][i] = t / tt;
+        coord[1][i] = y / th;
+        coord[2][i] = x / tw;
+      }
+  for (long long i = 0; i < N; ++i) {
+    int lo[3];
+    for (int a = 0; a < 3; ++a) lo[a] = std::min(std::max(coord[a][i] - w[a] / 2, 0), std::max(n[a] - w[a], 0));
+    uint8_t* row = keep + static_cast<size_t>(i) * N;
+    for (long long j = 0; j < N; ++j) {
+      bool in = true;
+      for (int a = 0; a < 3; ++a) in = in && coord[a][j] >= lo[a] && coord[a][j] < lo[a] + w[a];
+      row[j] = in ? 1 : 0;
+    }
+  }
+  return BSA_OK;
+}

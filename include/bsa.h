@@ -336,6 +336,19 @@ bsa_status bsa_select_probe_rows(const int32_t* labels_host, int S, int C, int M
  * label = rank / chunk.   labels_host int32 [T*H*W] out. */
 bsa_status bsa_tile_labels(int T, int H, int W, int tt, int th, int tw, int chunk, int32_t* labels_host);
 
+/* Static sliding-tile block mask ([SBC] "Recipe: STA with both repairs": built at tile
+ * resolution and used with the tile labels; expanded through them it is the token-level
+ * mask).  Cells of an nT x nH x nW raster grid form tiles of (tt, th, tw) cells (edge tiles
+ * partial); cell i keeps cell j when j's tile lies in the window of (wt, wh, ww) tiles around
+ * i's tile.  Along an axis of n tiles the window of w tiles around coordinate a starts at
+ * min(max(a - w/2, 0), max(n - w, 0)): it slides inward at the edges, so every row keeps
+ * the same number of tiles.  With (tt, th, tw) = (1, 1, 1) the cells are tiles and the
+ * result is the cluster-level mask for bsa_tile_labels clusters.
+ *   keep_host uint8 [N, N] out, N = nT * nH * nW (at most 65535)
+ */
+bsa_status bsa_sliding_tile_mask(int nT, int nH, int nW, int tt, int th, int tw, int wt, int wh, int ww,
+                                 uint8_t* keep_host);
+
 #ifdef __cplusplus
 }
 #endif

@@ -169,3 +169,13 @@ def test_workspace_sizes(lib):
     assert _lib.size_query("bsa_sparse_attention_workspace_size", 1, 40, 40, 256, 32760, 256) == \
         -(-rows * stride * 4 // 256) * 256 + (-(-rows * 4 // 256) * 256) + 2 * (-(-units * 4 // 256) * 256) + \
         (-(-40 * 4 // 256) * 256) + 256
+
+
+@pytest.mark.parametrize("grid,tile,window", [((1, 3, 4), (1, 1, 1), (1, 3, 3)), ((4, 8, 12), (2, 4, 4), (1, 2, 3)),
+                                              ((5, 9, 10), (2, 4, 4), (3, 1, 3)), ((11, 4, 7), (1, 1, 1), (7, 3, 3))])
+def test_sliding_tile_mask_host_helper(lib, grid, tile, window):
+    """The host helper (C++) against the oracle, bit for bit."""
+    from block_sparse_attention_antidiagonal_amd import api
+    from oracle import static_masks as osm
+    got = api.sliding_tile_block_mask(*grid, tile, window)
+    assert np.array_equal(got, osm.sliding_tile_block_mask(*grid, tile, window))

@@ -315,6 +315,32 @@ def test_sparse_attention(bsa, name, kw, compensate):
             assert np.max(np.abs(got_lse[b, hq][fin] - ref_lse[fin])) < lse_tol
 
 
+@pytest.mark.parametrize("grid,tile,window,compensate", [((4, 16, 24), (2, 8, 8), (1, 2, 3), True),
+                                                         ((5, 18, 20), (2, 8, 8), (3, 1, 3), True),
+                                                         ((5, 18, 20), (2, 8, 8), (1, 3, 1), False)])
+def test_attention_sliding_tile_mask(bsa, grid, tile, window, compensate):
+    """Static sliding-tile masks ([SBC] "Recipe: STA with both repairs"): tile labels as the
+    clusters (edge tiles partial on the second grid), the tile-level mask from the host
+    helper, compensated and hard-drop attention against the oracle with the oracle's mask."""
+    from oracle import layout as olay
+    from oracle import static_masks as osm
+    T, H, W = grid
+    say(f"attention sliding tile grid={grid} tile={tile} window={window} compensate={compensate}")
+    wl = make_custom(90 + sum(grid), B=1, Hq=2, Hkv=2, S=T * H * W, D=128, dtype="bf16", mask="all")
+    wl.labels = olay.tile_labels(T, H, W, tile)
+    wl.C = int(wl.labels.max()) + 1
+    nt, nh, nw = -(-T // tile[0]), -(-H // tile[1]), -(-W // tile[2])
+    keep_tile = bsa.sliding_tile_block_mask(nt, nh, nw, (1, 1, 1), window)
+    assert np.array_equal(keep_tile, osm.sliding_tile_block_mask(nt, nh, nw, (1, 1, 1), window))
+    keep = np.broadcast_to(keep_tile, (1, wl.Hkv) + keep_tile.shape).copy()
+    out = host(run_attention(bsa, wl, keep, compensate))
+    oracle_keep = np.broadcast_to(osm.sliding_tile_block_mask(nt, nh, nw, (1, 1, 1), window),
+                                  (1, wl.Hkv, wl.C, wl.C))
+    for hq in range(wl.Hq):
+        ref, _ = oracle_attention(wl, oracle_keep, compensate, 0, hq)
+        check_output(out[0, hq], ref, "bf16", f"sliding tile h{hq}")
+
+
 def test_hard_drop_empty_rows_are_zero(bsa):
     say("attention empty rows")
     wl = make_custom(7, S=600, D=128, dtype="bf16", mask="random", p_keep=0.2)
