@@ -21,6 +21,8 @@
 // V-bar like V).
 #include "pack.hpp"
 
+#include <type_traits>
+
 namespace bsa {
 namespace {
 
@@ -59,20 +61,38 @@ __device__ __forceinline__ uint32_t bf16_exp(uint16_t b) { return (b >> 7) & 0xf
 // swapped (order 0-3, 8-11, 4-7, 12-15), an involution.
 __device__ __forceinline__ int vt_key(int pos) { return (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1); }
 
-// One workgroup per (key cluster, batch x K/V head).
+// One workgroup per (key cluster, batch x K/V head).  V is staged in LDS in its own 16-bit
+// encoding for bfloat16 inputs (float32 otherwise); the buffer for the centroid reduction
+// reuses that memory once the last tile is written, so a workgroup needs about 17 KB of LDS
+// (bfloat16, D = 128) and many are resident per CU.
+template <typename T, int D>
+struct PackSmem {
+  using VS = std::conditional_t<sizeof(T) == 2, uint16_t, float>;
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  static constexpr int CPR = D / EPC;
+  static constexpr int kKeyGroups = kPackThreads / CPR;
+  static constexpr int VROW = D + 16 / static_cast<int>(sizeof(VS));  // padded row (elements)
+  static constexpr int V_BYTES = kPackTile * VROW * static_cast<int>(sizeof(VS));
+  static constexpr int RED_BYTES = 2 * kKeyGroups * D * 4;
+  static constexpr int BYTES = V_BYTES > RED_BYTES ? V_BYTES : RED_BYTES;
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int S, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, int C, const int32_t* __restrict__ tile_off, int tiles_per_head,
     T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
     int32_t* __restrict__ hmix, float* __restrict__ Kbar, float* __restrict__ Vbar) {
-  constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;                            // chunks per row
+  using M = PackSmem<T, D>;
+  using VS = typename M::VS;
+  constexpr int EPC = M::EPC;                             // elements per 16-byte chunk
+  constexpr int CPR = M::CPR;                             // chunks per row
   constexpr int kItems = kPackTile * CPR / kPackThreads;  // (key, chunk) items per thread
-  constexpr int kKeyGroups = kPackThreads / CPR;          // keys covered in one pass
-  __shared__ float vt[kPackTile][D + 1];                  // the tile's V as float32
-  __shared__ float red[2][kKeyGroups][D];
+  constexpr int kKeyGroups = M::kKeyGroups;               // keys covered in one pass
+  __shared__ __align__(16) unsigned char smem[M::BYTES];
   __shared__ uint32_t emax_s;
+  VS* vt = reinterpret_cast<VS*>(smem);                      // [kPackTile][VROW]: the tile's V
+  float* red = reinterpret_cast<float*>(smem);               // [2][kKeyGroups][D], after the tiles
   const int c = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int lo = offsets[c], n = offsets[c + 1] - lo;
@@ -86,28 +106,36 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
   for (int j = 0; j < ntiles; ++j) {
     const size_t tile = bh * tiles_per_head + tile_off[c] + j;
     if (t == 0) emax_s = 0;
-    __syncthreads();
+    uint4 kv[kItems], vv[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int r = j * kPackTile + kg + i * kKeyGroups;
+      kv[i] = vv[i] = make_uint4(0, 0, 0, 0);
+      if (r < n) {
+        const size_t row = static_cast<size_t>(perm[lo + r]) * D + ch * EPC;
+        kv[i] = *reinterpret_cast<const uint4*>(Kh + row);
+        vv[i] = *reinterpret_cast<const uint4*>(Vh + row);
+      }
+    }
+    __syncthreads();  // emax_s cleared; the previous tile's V^T reads are done
     uint32_t emax = 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int key = kg + i * kKeyGroups;
-      const int r = j * kPackTile + key;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (r < n) {
-        const size_t row = static_cast<size_t>(perm[lo + r]) * D + ch * EPC;
-        kv = *reinterpret_cast<const uint4*>(Kh + row);
-        vv = *reinterpret_cast<const uint4*>(Vh + row);
-      }
-      *reinterpret_cast<uint4*>(Kp + (tile * kPackTile + key) * D + ch * EPC) = kv;
-      const T* ke = reinterpret_cast<const T*>(&kv);
-      const T* ve = reinterpret_cast<const T*>(&vv);
+      *reinterpret_cast<uint4*>(Kp + (tile * kPackTile + key) * D + ch * EPC) = kv[i];
+      const T* ke = reinterpret_cast<const T*>(&kv[i]);
+      const T* ve = reinterpret_cast<const T*>(&vv[i]);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const float kf = to_f32(ke[e]), vf = to_f32(ve[e]);
-        ks[e] += kf;
-        vs[e] += vf;
-        vt[key][ch * EPC + e] = vf;
-        if constexpr (sizeof(T) == 2) emax = max(emax, bf16_exp(ve[e].bits));
+        ks[e] += to_f32(ke[e]);
+        vs[e] += to_f32(ve[e]);
+      }
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vv[i];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) emax = max(emax, bf16_exp(ve[e].bits));
+      } else {
+        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vv[i];
       }
     }
     if constexpr (sizeof(T) == 2) atomicMax(&emax_s, emax);
@@ -124,8 +152,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float a = vt[vt_key(k0 + 2 * p)][d], b = vt[vt_key(k0 + 2 * p + 1)][d];
-          w[p] = f16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+          const uint32_t a = vt[vt_key(k0 + 2 * p) * M::VROW + d], b = vt[vt_key(k0 + 2 * p + 1) * M::VROW + d];
+          w[p] = f16 ? pack_f16x2(__uint_as_float(a << 16), __uint_as_float(b << 16)) : (a | (b << 16));
         }
         *reinterpret_cast<uint4*>(Vtp16 + (tile * D + d) * kPackTile + k0) = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -134,23 +162,24 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
       for (int idx = t; idx < D * (kPackTile / 4); idx += kPackThreads) {
         const int d = idx / (kPackTile / 4), k0 = (idx % (kPackTile / 4)) * 4;
         *reinterpret_cast<f32x4*>(Vtp32 + (tile * D + d) * kPackTile + k0) =
-            f32x4{vt[vt_key(k0)][d], vt[vt_key(k0 + 1)][d], vt[vt_key(k0 + 2)][d], vt[vt_key(k0 + 3)][d]};
+            f32x4{vt[vt_key(k0) * M::VROW + d], vt[vt_key(k0 + 1) * M::VROW + d], vt[vt_key(k0 + 2) * M::VROW + d],
+                  vt[vt_key(k0 + 3) * M::VROW + d]};
       }
     }
-    __syncthreads();
   }
+  __syncthreads();  // the last tile's V^T reads are done before red reuses the memory
   // Centroid means: reduce the per-thread column sums over the key groups.
 #pragma unroll
   for (int e = 0; e < EPC; ++e) {
-    red[0][kg][ch * EPC + e] = ks[e];
-    red[1][kg][ch * EPC + e] = vs[e];
+    red[kg * D + ch * EPC + e] = ks[e];
+    red[(kKeyGroups + kg) * D + ch * EPC + e] = vs[e];
   }
   __syncthreads();
   const float inv = n > 0 ? 1.0f / static_cast<float>(n) : 0.0f;
   for (int e = t; e < 2 * D; e += kPackThreads) {
     const int which = e / D, d = e % D;
     float s = 0.0f;
-    for (int g = 0; g < kKeyGroups; ++g) s += red[which][g][d];
+    for (int g = 0; g < kKeyGroups; ++g) s += red[(which * kKeyGroups + g) * D + d];
     (which == 0 ? Kbar : Vbar)[(bh * C + c) * D + d] = s * inv;
   }
 }
