@@ -19,6 +19,7 @@ Pages (cited by title and section):
   [SPR]  "Partition the Support, Reconstruct the Residual" (paper summary page): the
          paragraphs on Probe-Fitted Residual Reconstruction, group-major permutation and
          grouped-query sharing, and the hard-drop residual statement.
+  [BSA]  "Block-sparse attention" (topic page of paper cards): the SVG-EAR card.
 
 Stages (module: function):
   layout.cluster_layout          stable cluster-major order of tokens          [SPR] permutation
@@ -37,9 +38,12 @@ Stages (module: function):
   reuse.layer_gate, refresh_decision  per-head refresh with the 40%/80% override [HMR] HEART
   reuse.HeadMaskCache            two-phase cache of masks and anchors          [HMR] ships, Recipe
   static_masks.sliding_tile_block_mask  static sliding-tile (STA) block mask   [SBC] Recipe: STA
+  routing.query_centroids        query-cluster means as the routing probes     [BSA] SVG-EAR, [SBC]
+  routing.block_compensation_error  first-order output error per block         [BSA] SVG-EAR, [SBC]
+  routing.error_aware_route      error-to-cost order under a token budget      [BSA] SVG-EAR
 
 Every function above is pinned by a test under tests/ (test_oracle_*.py) against closed
 forms, brute force, library routines or hand-worked fixtures in tests/golden/.
 """
 
-from . import attention, centroids, layout, pipeline, repair, reuse, scoring, static_masks, topp  # noqa: F401
+from . import attention, centroids, layout, pipeline, repair, reuse, routing, scoring, static_masks, topp  # noqa: F401
