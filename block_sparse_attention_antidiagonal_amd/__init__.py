@@ -1,8 +1,9 @@
 """Block-sparse video-DiT attention for AMD Instinct MI355X (gfx950).
 
 Antidiagonal block scoring, per-row top-p block masks, block-sparse flash attention with
-centroid compensation, probe-fitted residual repair, and head-wise reuse of block masks
-across calls (pooled Q/K drift with a layer gate), as hand-written HIP kernels
+centroid compensation, probe-fitted residual repair, head-wise reuse of block masks across
+calls (pooled Q/K drift with a layer gate) and error-aware block routing (query-centroid
+probes, per-block compensation error, error-to-cost routes), as hand-written HIP kernels
 behind a C ABI (include/bsa.h, libbsa.so).  This package is the thin Python binding:
 importing it loads libbsa.so and fails if the library has not been built.
 """
@@ -17,11 +18,13 @@ from .api import (  # noqa: E402,F401
     HeadMaskCache,
     PackedKV,
     antidiagonal_block_scores,
+    block_error,
     block_sparse_attention,
     centroid_compensated_attention,
     centroids,
     cluster_layout,
     correct,
+    error_route,
     gather_rows,
     kv_pack,
     mask_from_keep,
@@ -32,6 +35,7 @@ from .api import (  # noqa: E402,F401
     probe_attention_packed,
     probe_fit,
     pooled_qk,
+    query_centroids,
     select_probe_rows,
     sliding_tile_block_mask,
     tile_labels,

@@ -53,6 +53,11 @@ SIGNATURES = {
                                    c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_fit": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, c_void_p,
                       c_void_p],
+    "bsa_query_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p],
+    "bsa_block_error_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_block_error": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_float, c_void_p, c_size_t,
+                        c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_error_route": [c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_probe_apply": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_correct": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_gather_rows": [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p],

@@ -334,6 +334,51 @@ def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tenso
     return od
 
 
+def query_centroids(q: torch.Tensor, layout: ClusterLayout) -> torch.Tensor:
+    """Mean query row of every query cluster [B, Hq, Cq, D], rounded to q's dtype: the
+    probes of the error-aware router (bsa_query_centroids)."""
+    _check_cuda(q)
+    B, Hq, S, D = q.shape
+    out = torch.empty(B, Hq, layout.C, D, dtype=q.dtype, device=q.device)
+    _lib.call("bsa_query_centroids", B, Hq, S, D, _dtype_code(q), _ptr(q), _ptr(layout.perm), _ptr(layout.offsets),
+              layout.C, _ptr(out), _stream())
+    return out
+
+
+def block_error(qbar: torch.Tensor, kv: PackedKV, scale: Optional[float] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compensation error of every block, float32 [B, Hq, Cq, Ck], for the probes qbar
+    [B, Hq, Cq, D] against the packed keys and values (bfloat16; bsa_block_error)."""
+    _check_cuda(qbar)
+    B, Hq, Cq, D = qbar.shape
+    if (kv.B, kv.D, kv.dtype) != (B, D, qbar.dtype) or Hq % kv.Hkv != 0:
+        raise ValueError("packed K/V do not match qbar")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Ck = kv.layout.C
+    err = torch.empty(B, Hq, Cq, Ck, dtype=torch.float32, device=qbar.device)
+    nbytes = _lib.size_query("bsa_block_error_workspace_size", B, Hq, kv.Hkv, kv.S, D, Cq, Ck)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, qbar.device)
+    _lib.call("bsa_block_error", B, Hq, kv.Hkv, kv.S, D, _dtype_code(qbar), _ptr(qbar), Cq, float(scale),
+              _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), Ck, _ptr(kv.kbar), _ptr(kv.vbar), _ptr(err),
+              _ptr(workspace), workspace.numel(), _stream())
+    return err
+
+
+def error_route(err: torch.Tensor, k_layout: ClusterLayout, budget: int) -> BlockMask:
+    """Error-aware routes from block errors [B, H, Cq, Ck]: per row the clusters by err / n_c
+    until `budget` key tokens are kept (bsa_error_route)."""
+    _check_cuda(err)
+    B, H, Cq, Ck = err.shape
+    keep = torch.empty(B, H, Cq, Ck, dtype=torch.uint8, device=err.device)
+    cnt = torch.empty(B, H, Cq, dtype=torch.int32, device=err.device)
+    idx = torch.empty(B, H, Cq, Ck, dtype=torch.int16, device=err.device)
+    _lib.call("bsa_error_route", _ptr(err), B * H * Cq, Ck, _ptr(k_layout.offsets), int(budget), _ptr(keep), _ptr(cnt),
+              _ptr(idx), _stream())
+    return BlockMask(keep, cnt, idx)
+
+
 def probe_fit(o_sparse_probe: torch.Tensor, o_dense_probe: torch.Tensor, weights: torch.Tensor,
               lam: float = 0.1, rank: int = 16) -> Tuple[torch.Tensor, torch.Tensor]:
     """Folded correction map A [B, Hq, D, D], c [B, Hq, D] from float32 probe rows (bsa_probe_fit)."""

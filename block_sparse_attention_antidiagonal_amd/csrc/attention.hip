@@ -1119,7 +1119,7 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
 // max and sum go to probe_merge_kernel.  Chunks past the head's last tile write empty partials.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
-    const bf16_t* __restrict__ Q, int Hq, int Hkv, int S, float c2, const int32_t* __restrict__ probe_idx, int M,
+    const bf16_t* __restrict__ Q, int Hq, int Hkv, int Sq, float c2, const int32_t* __restrict__ probe_idx, int M,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C,
     const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
     int tiles_per_head, int tpc, int nchunks, float* __restrict__ Opart, float* __restrict__ mpart,
@@ -1150,9 +1150,9 @@ __global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int my = qt * kRowsWG + wave * 32 + r;
-  const int qtok = probe_idx[my < M ? my : 0];
+  const int qtok = probe_idx != nullptr ? probe_idx[my < M ? my : 0] : (my < M ? my : 0);
   Frag<T> qf[D / 16];
-  load_q_frags<T, D>(qf, Q + static_cast<size_t>(bh) * S * D + static_cast<size_t>(qtok) * D);
+  load_q_frags<T, D>(qf, Q + static_cast<size_t>(bh) * Sq * D + static_cast<size_t>(qtok) * D);
   __builtin_amdgcn_s_waitcnt(0);
   RowState<D> st;
   init_state<D>(st);
@@ -1198,7 +1198,7 @@ template <int D>
 __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ Opart,
                                                         const float* __restrict__ mpart,
                                                         const float* __restrict__ lpart, int M, int nchunks,
-                                                        float* __restrict__ Od) {
+                                                        float* __restrict__ Od, float* __restrict__ lse2) {
   const int m = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
   float mx = -INFINITY;
   for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, mpart[(static_cast<size_t>(bh) * nchunks + c) * M + m]);
@@ -1212,6 +1212,175 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
     o += Opart[prow * D + d] * w;
   }
   Od[(static_cast<size_t>(bh) * M + m) * D + d] = l > 0.0f ? o / l : 0.0f;
+  // Log-sum-exp of the scaled logits in log2 units (running max plus log2 of the sum).
+  if (lse2 != nullptr && d == 0) lse2[static_cast<size_t>(bh) * M + m] = l > 0.0f ? mx + __log2f(l) : -INFINITY;
+}
+
+// ----------------------------------------------------------------- block compensation error
+
+// Compensation error of every block for the error-aware router ("Block-sparse attention"
+// topic page, SVG-EAR card: a light probe estimates each block's compensation error; the
+// probe of query cluster a is its mean row q_bar_a).  With the probe's dense output O_a and
+// log-sum-exp lse_a (log2 units, from the dense probe pass), weights p_j = 2^(s_j c2 - lse_a)
+// and, for key cluster c, N_c = sum_{j in c} p_j v_j, Z_c = sum_{j in c} p_j and
+// z_hat = 2^(q_bar_a . k_bar_c c2 + log2 n_c - lse_a), the error is the norm of the
+// first-order change of O_a when the block is compensated: ||z_hat v_bar_c - N_c - O_a
+// (z_hat - Z_c)||_2.  Workgroup (chunk of kErrClusters key clusters, 128 probe rows, batch x
+// query head): the chunk's tiles, contiguous in the packed buffer, stream through two LDS
+// buffers; N_c and Z_c accumulate over a cluster's tiles and the error is formed after its
+// last tile.  N_c and O_a Z_c nearly cancel where a centroid is accurate, so the P V product
+// takes P as a high and a low float16 (or bfloat16) part.
+constexpr int kErrClusters = 8;
+
+template <int D>
+__device__ __forceinline__ void tile_pv_split(const bf16_t* Vt, const f32x16 (&s)[2], RowState<D>& st, bool pv16) {
+  using Lds = SwzLds<bf16_t, D>;
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (pv16) {
+      Frag16 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = s[ks >> 1][(ks & 1) * 8 + i];
+        const _Float16 xh = static_cast<_Float16>(x);
+        hi.v[i] = xh;
+        lo.v[i] = static_cast<_Float16>(x - static_cast<float>(xh));
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        Frag16 va;
+        Lds::vfrag16(va, Vt, dt * 32 + r, ks, h);
+        st.o[dt] = mma(va, hi, st.o[dt]);
+        st.o[dt] = mma(va, lo, st.o[dt]);
+      }
+    } else {
+      Frag<bf16_t> hi, lo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = s[ks >> 1][(ks & 1) * 8 + i];
+        const __bf16 xh = static_cast<__bf16>(x);
+        hi.v[i] = xh;
+        lo.v[i] = static_cast<__bf16>(x - static_cast<float>(xh));
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        Frag<bf16_t> va;
+        Lds::vfrag(va, Vt, dt * 32 + r, ks, h);
+        st.o[dt] = mma(va, hi, st.o[dt]);
+        st.o[dt] = mma(va, lo, st.o[dt]);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void block_error_kernel(
+    const bf16_t* __restrict__ Qb, int Hq, int Hkv, int Cq, float c2, const float* __restrict__ O1,
+    const float* __restrict__ lse2, const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int Ck,
+    const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
+    int tiles_per_head, const float* __restrict__ Kbar, const float* __restrict__ Vbar, float* __restrict__ err) {
+  using T = bf16_t;
+  using L = AttnLds<T, D, float>;
+  constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* kb_s = reinterpret_cast<float*>(smem + L::TILES);   // [kErrClusters][D] centroid keys
+  float* vb_s = kb_s + kErrClusters * D;                     // [kErrClusters][D] centroid values
+  int* toff_s = reinterpret_cast<int*>(vb_s + kErrClusters * D);  // first tile of each cluster (+ end)
+  int* n_s = toff_s + kErrClusters + 1;                      // cluster sizes
+  const int chunk = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
+  const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
+  const int c0 = chunk * kErrClusters, nc = min(kErrClusters, Ck - c0);
+  const int t = threadIdx.x;
+  for (int i = t; i < nc * D; i += kThreads) {
+    kb_s[i] = Kbar[(bkv * Ck + c0) * D + i];
+    vb_s[i] = Vbar[(bkv * Ck + c0) * D + i];
+  }
+  if (t <= nc) toff_s[t] = tile_off[c0 + t];
+  if (t < nc) n_s[t] = k_off[c0 + t + 1] - k_off[c0 + t];
+  const int wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int my = qt * kRowsWG + wave * 32 + r;
+  const size_t prow = static_cast<size_t>(bh) * Cq + (my < Cq ? my : Cq - 1);
+  Frag<T> qf[D / 16];
+  load_q_frags<T, D>(qf, Qb + prow * D);
+  const float lse_r = lse2[prow];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bool store = h == 0 && my < Cq;
+  float* err_row = err + (static_cast<size_t>(bh) * Cq + my) * Ck + c0;
+  for (int ci = 0; ci < nc; ++ci)
+    if (store && n_s[ci] <= 0) err_row[ci] = 0.0f;  // an empty cluster: no tiles, no error
+  const int T0 = toff_s[0], T1 = toff_s[nc];
+  const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
+  const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
+  const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
+  RowState<D> st;
+  init_state<D>(st);
+  float zl = 0.0f;  // this lane's part of Z_c
+  TileDma<T, D> dma;
+  dma.init();
+  auto kbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::K0 + i * L::KB); };
+  auto vbuf = [&](int i) { return reinterpret_cast<T*>(smem + L::V0 + i * L::VB); };
+  if (T0 < T1) {
+    dma.issue_k(Kph + T0 * kTileBytes, kbuf(0));
+    dma.issue_v(Vph + T0 * kTileBytes, vbuf(0));
+  }
+  wait_vmem();
+  __syncthreads();
+  int ci = 0;
+  for (int tt = T0; tt < T1; ++tt) {
+    const int bj = (tt - T0) & 1;
+    if (tt + 1 < T1) {
+      dma.issue_k(Kph + (tt + 1) * kTileBytes, kbuf(bj ^ 1));
+      dma.issue_v(Vph + (tt + 1) * kTileBytes, vbuf(bj ^ 1));
+    }
+    while (tt >= toff_s[ci + 1]) ++ci;  // the same for every lane; skips empty clusters
+    const int nv = min(kNK, n_s[ci] - kNK * (tt - toff_s[ci]));
+    f32x16 s[2];
+    tile_qk<T, D, SwzLds<T, D>>(kbuf(bj), qf, s[0], s[1]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = mt * 32 + 8 * (j / 4) + 4 * h + (j % 4);
+        const float p = key < nv ? fast_exp2(__builtin_fmaf(s[mt][j], c2, -lse_r)) : 0.0f;
+        s[mt][j] = p;
+        zl += p;
+      }
+    tile_pv_split<D>(vbuf(bj), s, st, flags_h[tt] != 0);
+    if (tt == toff_s[ci + 1] - 1) {  // the cluster's last tile: its error
+      const float zc = zl + swap_halves(zl);
+      float dot = 0.0f;  // q_bar . k_bar_c over this lane's half of D, then both halves
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot += static_cast<float>(qf[kk].v[i]) * kb_s[ci * D + kk * 16 + 8 * h + i];
+      dot += swap_halves(dot);
+      const float zh = fast_exp2(__builtin_fmaf(dot, c2, __log2f(static_cast<float>(n_s[ci])) - lse_r));
+      const float dz = zh - zc;
+      const float* orow = O1 + prow * D;
+      float e2 = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = dt * 32 + 8 * g4 + 4 * h;
+          const f32x4 o = *reinterpret_cast<const f32x4*>(orow + d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float delta = zh * vb_s[ci * D + d + i] - st.o[dt][4 * g4 + i] - o[i] * dz;
+            e2 += delta * delta;
+          }
+        }
+      e2 += swap_halves(e2);
+      if (store) err_row[ci] = sqrtf(e2);
+      init_state<D>(st);
+      zl = 0.0f;
+    }
+    wait_vmem();
+    __syncthreads();
+  }
 }
 
 constexpr int kProbeChunk = 2048;
@@ -1347,7 +1516,7 @@ void launch_probe_pass(int B, int Hq, int Hkv, int S, const void* Q, const void*
                      probe_idx, M, kProbeChunk, ntok, nchunks, q_labels, k_labels, keep, Hm, Cq, Ck, k_off, Kbar,
                      Vbar, Opart, mpart, lpart);
   hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks,
-                     out);
+                     out, nullptr);
 }
 
 size_t probe_ws_floats(int B, int Hq, int S, int D, int M) {
@@ -1363,10 +1532,12 @@ inline int packed_probe_chunks(int first_ctile) {
   return (first_ctile + tpc - 1) / tpc;
 }
 
+// Q holds Sq rows per head; probe_idx == nullptr takes rows 0 .. M-1; lse2 (log2 units) is
+// optional.
 template <int D>
-bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* probe_idx,
-                               int M, const void* packed, const int32_t* k_off, int C, float* Od, void* ws,
-                               hipStream_t stream) {
+bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void* Q, float scale,
+                               const int32_t* probe_idx, int M, const void* packed, const int32_t* k_off, int C,
+                               float* Od, float* lse2, void* ws, hipStream_t stream) {
   const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const int tpc = packed_probe_tpc(PL.first_centroid_tile);
@@ -1379,10 +1550,11 @@ bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, const void* Q, flo
   auto kern = probe_dense_packed_kernel<D>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   hipLaunchKernelGGL(kern, dim3(nchunks, qtiles, B * Hq), dim3(kThreads), LDS, stream, static_cast<const bf16_t*>(Q),
-                     Hq, Hkv, S, scale * kLog2e, probe_idx, M, reinterpret_cast<const int32_t*>(base + PL.tile_off),
+                     Hq, Hkv, Sq, scale * kLog2e, probe_idx, M, reinterpret_cast<const int32_t*>(base + PL.tile_off),
                      k_off, C, base + PL.flags, reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v,
                      PL.tiles_per_head, tpc, nchunks, Opart, mpart, lpart);
-  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks, Od);
+  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks, Od,
+                     lse2);
   return launch_status();
 }
 
@@ -1398,6 +1570,50 @@ bsa_status launch_probe(int B, int Hq, int Hkv, int S, const void* Q, const void
   if (Os != nullptr)
     launch_probe_pass<T, D, true>(B, Hq, Hkv, S, Q, K, V, c2, probe_idx, M, q_labels, k_labels, keep, Hm, Cq, Ck,
                                   k_off, Kbar, Vbar, Os, w, stream);
+  return launch_status();
+}
+
+
+// ----------------------------------------------------------------- error-aware routing: block errors
+
+// Workspace of bsa_block_error: the dense probe pass's partials, its rows O_a [B, Hq, Cq, D]
+// and log-sum-exp [B, Hq, Cq] (float32).
+struct ErrWs {
+  size_t part, o1, lse, total;
+};
+inline ErrWs err_ws(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck) {
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t));
+  ErrWs w;
+  w.part = 0;
+  w.o1 = pack_align(static_cast<size_t>(B) * Hq * packed_probe_chunks(PL.first_centroid_tile) * Cq * (D + 2) *
+                    sizeof(float));
+  w.lse = w.o1 + pack_align(static_cast<size_t>(B) * Hq * Cq * D * sizeof(float));
+  w.total = w.lse + pack_align(static_cast<size_t>(B) * Hq * Cq * sizeof(float));
+  return w;
+}
+
+template <int D>
+bsa_status launch_block_error(int B, int Hq, int Hkv, int S, const void* qbar, int Cq, float scale, const void* packed,
+                              const int32_t* k_off, int Ck, const float* Kbar, const float* Vbar, float* err, void* ws,
+                              hipStream_t stream) {
+  const ErrWs W = err_ws(B, Hq, Hkv, S, D, Cq, Ck);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  float* O1 = reinterpret_cast<float*>(wsb + W.o1);
+  float* lse2 = reinterpret_cast<float*>(wsb + W.lse);
+  // Pass 1: the probes' dense rows and log-sum-exp (rows 0 .. Cq-1 of qbar).
+  const bsa_status st = launch_probe_packed<D>(B, Hq, Hkv, S, Cq, qbar, scale, nullptr, Cq, packed, k_off, Ck, O1,
+                                               lse2, wsb + W.part, stream);
+  if (st != BSA_OK) return st;
+  // Pass 2: the per-block errors.
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t));
+  const unsigned char* base = static_cast<const unsigned char*>(packed);
+  constexpr int LDS = AttnLds<bf16_t, D, float>::TILES + 2 * kErrClusters * D * 4 + (2 * kErrClusters + 1) * 4;
+  auto kern = block_error_kernel<D>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  hipLaunchKernelGGL(kern, dim3((Ck + kErrClusters - 1) / kErrClusters, (Cq + kRowsWG - 1) / kRowsWG, B * Hq),
+                     dim3(kThreads), LDS, stream, static_cast<const bf16_t*>(qbar), Hq, Hkv, Cq, scale * kLog2e, O1,
+                     lse2, reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, Ck, base + PL.flags,
+                     reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v, PL.tiles_per_head, Kbar, Vbar, err);
   return launch_status();
 }
 
@@ -1475,10 +1691,10 @@ extern "C" bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, 
   if (packed_bytes < pack_layout(B, Hkv, S, D, C, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
-  return D == 128 ? launch_probe_packed<128>(B, Hq, Hkv, S, Q, scale, probe_idx, M, packed, k_offsets, C, O_dense_probe,
-                                             ws, stream)
-                  : launch_probe_packed<64>(B, Hq, Hkv, S, Q, scale, probe_idx, M, packed, k_offsets, C, O_dense_probe,
-                                            ws, stream);
+  return D == 128 ? launch_probe_packed<128>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
+                                             O_dense_probe, nullptr, ws, stream)
+                  : launch_probe_packed<64>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
+                                            O_dense_probe, nullptr, ws, stream);
 }
 
 extern "C" bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
@@ -1507,4 +1723,33 @@ extern "C" bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, 
   if (dtype == BSA_BF16) return D == 128 ? launch_probe<bf16_t, 128>(BSA_ARGS) : launch_probe<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_probe<float, 128>(BSA_ARGS) : launch_probe<float, 64>(BSA_ARGS);
 #undef BSA_ARGS
+}
+
+extern "C" bsa_status bsa_block_error_workspace_size(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck,
+                                                      size_t* bytes) {
+  if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
+  if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
+  if (Cq > 4096 || Ck > 32767) return BSA_E_UNSUPPORTED;
+  *bytes = bsa::err_ws(B, Hq, Hkv, S, D, Cq, Ck).total;
+  return BSA_OK;
+}
+
+extern "C" bsa_status bsa_block_error(int B, int Hq, int Hkv, int S, int D, int dtype, const void* qbar, int Cq,
+                                      float scale, const void* packed, size_t packed_bytes, const int32_t* k_offsets,
+                                      int Ck, const float* Kbar, const float* Vbar, float* err, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  if (dtype != BSA_BF16) return valid_dtype(dtype) ? BSA_E_UNSUPPORTED : BSA_E_DTYPE;
+  size_t need = 0;
+  const bsa_status st = bsa_block_error_workspace_size(B, Hq, Hkv, S, D, Cq, Ck, &need);
+  if (st != BSA_OK) return st;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (!qbar || !packed || !k_offsets || !Kbar || !Vbar || !err) return BSA_E_ARG;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
+  if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
+  if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
+  return D == 128 ? launch_block_error<128>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, Kbar, Vbar, err, ws,
+                                            stream)
+                  : launch_block_error<64>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, Kbar, Vbar, err, ws,
+                                           stream);
 }

@@ -149,6 +149,115 @@ __global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restri
   if (threadIdx.x == 0) kv_count[row] = offset;
 }
 
+// Error-aware routes ("Block-sparse attention" topic page, SVG-EAR card: the blocks with the
+// highest error-to-cost ratio are computed exactly, the rest compensated).  One workgroup per
+// mask row: the row's non-empty key clusters in order of err / n_c (float32, correctly
+// rounded; descending, ties by lower index) -- the cost of block (a, c) is n_a n_c, and n_a
+// is the same along the row -- and the shortest prefix whose key count reaches `budget`
+// tokens, at least one cluster.  Empty clusters are never kept.
+__global__ __launch_bounds__(256) void error_route_kernel(const float* __restrict__ err, int Ck,
+                                                          const int32_t* __restrict__ k_off, int budget,
+                                                          uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
+                                                          int16_t* __restrict__ kv_idx) {
+  __shared__ uint64_t key[kMaxCk];
+  __shared__ int csum[kMaxCk];
+  __shared__ int tmpi[256];
+  __shared__ uint8_t kb[kMaxCk];
+  const size_t row = blockIdx.x;
+  const float* erow = err + row * Ck;
+  int n2 = 1;
+  while (n2 < Ck) n2 <<= 1;
+  for (int i = threadIdx.x; i < n2; i += 256) {
+    uint64_t k = 0;  // empty clusters (and padding) sort last
+    if (i < Ck) {
+      const int n = k_off[i + 1] - k_off[i];
+      if (n > 0)
+        k = (static_cast<uint64_t>(sortable(__fdiv_rn(erow[i], static_cast<float>(n)))) << 32) |
+            static_cast<uint32_t>(0xffffffffu - i);
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 256) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t a = key[i], b = key[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            key[i] = b;
+            key[p] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Inclusive prefix sum of the key counts in sorted order (4 entries per thread).
+  int loc[4];
+  int run = 0;
+  const int b0 = threadIdx.x * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = b0 + e;
+    int n = 0;
+    if (i < Ck && key[i] != 0) {
+      const int c = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key[i]));
+      n = k_off[c + 1] - k_off[c];
+    }
+    run += n;
+    loc[e] = run;
+  }
+  int total;
+  const int before = block_excl_scan(run, tmpi, &total);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (b0 + e < kMaxCk) csum[b0 + e] = before + loc[e];
+  __syncthreads();
+  // Last kept rank: the first non-empty rank whose cumulative count reaches the budget, else
+  // the last non-empty rank.
+  int first = 0x7fffffff, last_ne = -1;
+  for (int i = threadIdx.x; i < Ck; i += 256) {
+    if (key[i] == 0) continue;
+    last_ne = max(last_ne, i);
+    if (csum[i] >= budget) first = min(first, i);
+  }
+  tmpi[threadIdx.x] = first;
+  __syncthreads();
+  for (int d = 128; d > 0; d >>= 1) {
+    if (threadIdx.x < static_cast<unsigned>(d)) tmpi[threadIdx.x] = min(tmpi[threadIdx.x], tmpi[threadIdx.x + d]);
+    __syncthreads();
+  }
+  const int first_all = tmpi[0];
+  __syncthreads();
+  tmpi[threadIdx.x] = last_ne;
+  __syncthreads();
+  for (int d = 128; d > 0; d >>= 1) {
+    if (threadIdx.x < static_cast<unsigned>(d)) tmpi[threadIdx.x] = max(tmpi[threadIdx.x], tmpi[threadIdx.x + d]);
+    __syncthreads();
+  }
+  const int last = min(first_all, tmpi[0]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < Ck; i += 256) kb[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i <= last; i += 256) kb[0xffffffffu - static_cast<uint32_t>(key[i])] = 1;
+  __syncthreads();
+  uint8_t* krow = keep + row * Ck;
+  for (int i = threadIdx.x; i < Ck; i += 256) krow[i] = kb[i];
+  int16_t* lrow = kv_idx + row * Ck;
+  int offset = 0;
+  for (int c0 = 0; c0 < Ck; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int bit = c < Ck ? kb[c] : 0;
+    int tot;
+    const int pos = block_excl_scan(bit, tmpi, &tot);
+    if (bit) lrow[offset + pos] = static_cast<int16_t>(c);
+    offset += tot;
+  }
+  if (threadIdx.x == 0) kv_count[row] = offset;
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -173,5 +282,14 @@ extern "C" bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int3
   if (!keep || !kv_count || !kv_idx || rows < 1 || Ck < 1) return BSA_E_ARG;
   if (Ck > 32767) return BSA_E_UNSUPPORTED;
   hipLaunchKernelGGL(mask_lists_kernel, dim3(rows), dim3(256), 0, stream, keep, Ck, kv_count, kv_idx);
+  return launch_status();
+}
+
+extern "C" bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int budget,
+                                      uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream) {
+  if (!err || !k_offsets || !keep || !kv_count || !kv_idx || rows < 1 || Ck < 1) return BSA_E_ARG;
+  if (Ck > kMaxCk) return BSA_E_UNSUPPORTED;
+  hipLaunchKernelGGL(error_route_kernel, dim3(rows), dim3(256), 0, stream, err, Ck, k_offsets, budget, keep, kv_count,
+                     kv_idx);
   return launch_status();
 }

@@ -10,6 +10,7 @@
  *   [SBC] "Sparse-block compensation" (mlx-arsenal research note)
  *   [HMR] "Dynamic block masks and head-wise mask reuse" (mlx-arsenal research note)
  *   [SPR] "Partition the Support, Reconstruct the Residual" (paper summary page)
+ *   [BSA] "Block-sparse attention" (topic page of paper cards), the SVG-EAR card
  *
  * Conventions shared by every call
  * --------------------------------
@@ -314,6 +315,52 @@ bsa_status bsa_mask_reuse_update(int B, int Hm, int Cq, int Ck, int D, const uin
                                  const float* kbar, const uint8_t* new_keep, const int32_t* new_count,
                                  const int16_t* new_idx, uint8_t* keep, int32_t* kv_count, int16_t* kv_idx,
                                  float* anchor_q, float* anchor_k, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Error-aware routing.  [BSA] SVG-EAR card: centroid compensation fails on a few blocks;
+ * a light probe estimates every block's compensation error and the blocks with the highest
+ * error-to-cost ratio are computed exactly, the rest compensated ([SBC] "SVG-EAR --
+ * centroid compensation" and "Out of scope, and why": a routing policy on top of the
+ * compensated attention).  Three calls, in order: the probes, the block errors, the routes;
+ * the routes are a block mask (Hm = Hq) for bsa_sparse_attention.
+ *
+ * bsa_query_centroids: the probe of query cluster a is its mean query row, rounded to dtype
+ * (as the centroid keys are); an empty cluster gets a zero row.  Float32 sums.
+ *   Q [B, Hq, S, D] dtype; q_perm/q_offsets: the query cluster layout (Cq clusters);
+ *   qbar [B, Hq, Cq, D] dtype out
+ */
+bsa_status bsa_query_centroids(int B, int Hq, int S, int D, int dtype, const void* Q, const int32_t* q_perm,
+                               const int32_t* q_offsets, int Cq, void* qbar, hipStream_t stream);
+
+/* bsa_block_error: for probe q = qbar[b, h, a] with softmax weights p_j over all keys, dense
+ * output O_a, and for key cluster c (n_c keys, means k_bar_c, v_bar_c from bsa_kv_pack):
+ * N_c = sum_{j in c} p_j v_j, Z_c = sum_{j in c} p_j, z_hat = exp(q . k_bar_c * scale +
+ * log n_c - lse_a), err[b, h, a, c] = || z_hat v_bar_c - N_c - O_a (z_hat - Z_c) ||_2, the
+ * first-order change of the probe's output when block (a, c) alone is compensated; 0 for
+ * an empty cluster.  Two passes over the packed tiles: the probes' dense rows and
+ * log-sum-exp, then the per-cluster sums (P V with P split into two float16 parts).
+ *   qbar [B, Hq, Cq, D] bfloat16; packed/packed_bytes, k_offsets [Ck+1], Kbar/Vbar float
+ *   [B, Hkv, Ck, D]: the bsa_kv_pack buffer and centroids; err float [B, Hq, Cq, Ck] out
+ *   ws: workspace of bsa_block_error_workspace_size bytes (the first pass's partial rows,
+ *       its rows and log-sum-exp)
+ * bfloat16 only (BSA_E_UNSUPPORTED for float32).  Needs Cq <= 4096, Ck <= 32767.
+ */
+bsa_status bsa_block_error_workspace_size(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck, size_t* bytes_host);
+bsa_status bsa_block_error(int B, int Hq, int Hkv, int S, int D, int dtype, const void* qbar, int Cq, float scale,
+                           const void* packed, size_t packed_bytes, const int32_t* k_offsets, int Ck,
+                           const float* Kbar, const float* Vbar, float* err, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* bsa_error_route: per mask row, the non-empty key clusters in order of err / n_c (float32,
+ * correctly rounded; descending, ties by lower index -- the cost of block (a, c) is
+ * n_a n_c and n_a is fixed along a row) and the shortest prefix whose key count reaches
+ * `budget` tokens; at least one cluster; empty clusters are never kept.
+ *   err float [rows, Ck]; k_offsets [Ck+1]; keep uint8 [rows, Ck], kv_count int32 [rows],
+ *   kv_idx int16 [rows, Ck] out (the bsa_top_p_mask conventions)
+ * Needs Ck <= 1024.
+ */
+bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int budget, uint8_t* keep,
+                           int32_t* kv_count, int16_t* kv_idx, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Host helpers (host pointers only).

@@ -92,17 +92,19 @@ def block_compensation_error(qbar, k, v, k_labels, Ck: int, scale: float) -> np.
     return err
 
 
-def error_aware_route(err, k_counts, budget: float) -> np.ndarray:
+def error_aware_route(err, k_counts, budget: float, ratio_dtype=np.float64) -> np.ndarray:
     """Keep bits uint8 [B, H, Cq, Ck]: per row, the shortest prefix of the non-empty clusters
     in order of err / n_c (descending, ties by index) whose key count reaches `budget`, and
-    at least one cluster (see the header)."""
-    err = np.asarray(err, dtype=np.float64)
+    at least one cluster (see the header).  ratio_dtype=np.float32 forms the ratios as
+    correctly rounded float32 quotients of float32 errors, the precision in which the kernel
+    takes the same decision."""
+    err = np.asarray(err, dtype=ratio_dtype)
     n = np.asarray(k_counts, dtype=np.int64)
     keep = np.zeros(err.shape, dtype=np.uint8)
     nz = np.nonzero(n > 0)[0]
     for idx in np.ndindex(*err.shape[:-1]):
         row = err[idx]
-        ratio = row[nz] / n[nz]
+        ratio = row[nz] / n[nz].astype(ratio_dtype)
         order = nz[np.lexsort((nz, -ratio))]  # descending ratio, lower index first on ties
         total = 0
         for c in order:

@@ -144,6 +144,20 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.bsa_probe_fit(1, 1, 128, dummy, dummy, dummy, 64, ctypes.c_float(0.1), 17, dummy, dummy, None) == 4
     # tau count must be 1 or one per head
     assert lib.bsa_top_p_mask(dummy, 4, 8, 8, dummy, 3, 4, dummy, dummy, dummy, None) == 2
+    # error-aware routing: block errors need bfloat16 and at most 4096 probes; routes at most
+    # 1024 key clusters; null pointers
+    f = ctypes.c_float(0.125)
+    assert lib.bsa_block_error(1, 2, 2, 1024, 128, 0, dummy, 16, f, dummy, 1 << 30, dummy, 16, dummy, dummy, dummy,
+                               dummy, 1 << 30, None) == 4
+    assert lib.bsa_block_error(1, 2, 2, 1024, 128, 1, dummy, 4097, f, dummy, 1 << 30, dummy, 16, dummy, dummy, dummy,
+                               dummy, 1 << 30, None) == 4
+    assert lib.bsa_block_error(1, 3, 2, 1024, 128, 1, dummy, 16, f, dummy, 1 << 30, dummy, 16, dummy, dummy, dummy,
+                               dummy, 1 << 30, None) == 2
+    assert lib.bsa_block_error(1, 2, 2, 1024, 128, 1, dummy, 16, f, dummy, 16, dummy, 16, dummy, dummy, dummy,
+                               dummy, 1 << 30, None) == 5
+    assert lib.bsa_error_route(dummy, 4, 1025, dummy, 10, dummy, dummy, dummy, None) == 4
+    assert lib.bsa_error_route(None, 4, 16, dummy, 10, dummy, dummy, dummy, None) == 1
+    assert lib.bsa_query_centroids(1, 1, 100, 96, 1, dummy, dummy, dummy, 4, dummy, None) == 4
 
 
 def test_workspace_sizes(lib):
@@ -169,6 +183,16 @@ def test_workspace_sizes(lib):
     assert _lib.size_query("bsa_sparse_attention_workspace_size", 1, 40, 40, 256, 32760, 256) == \
         -(-rows * stride * 4 // 256) * 256 + (-(-rows * 4 // 256) * 256) + 2 * (-(-units * 4 // 256) * 256) + \
         (-(-40 * 4 // 256) * 256) + 256
+
+
+def test_block_error_workspace_size(lib):
+    """The first pass's partial rows (32 chunks of 24 token tiles for S = 32760, 256 clusters),
+    its rows and its log-sum-exp, each section 256-byte aligned."""
+    from block_sparse_attention_antidiagonal_amd import _lib
+
+    a = lambda n: -(-n // 256) * 256
+    assert _lib.size_query("bsa_block_error_workspace_size", 1, 40, 40, 32760, 128, 256, 256) == \
+        a(40 * 32 * 256 * 130 * 4) + a(40 * 256 * 128 * 4) + a(40 * 256 * 4)
 
 
 @pytest.mark.parametrize("grid,tile,window", [((1, 3, 4), (1, 1, 1), (1, 3, 3)), ((4, 8, 12), (2, 4, 4), (1, 2, 3)),

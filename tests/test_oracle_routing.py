@@ -125,3 +125,14 @@ def test_route_rows_independent():
     keep = ort.error_aware_route(err, n, 8)
     assert keep[0, 0].tolist() == [[0, 1, 1], [1, 1, 0]]
     assert keep[0, 1].tolist() == [[1, 1, 0], [1, 1, 0]]
+
+
+def test_route_float32_ratios_take_the_kernel_decision():
+    """1 / 3 and the float32 nearest to 1/3 tie in float32 (the lower index wins) but not in
+    float64 (the larger quotient wins)."""
+    n = np.array([3, 1])
+    third = float(np.float32(1.0) / np.float32(3.0))
+    err = np.array([[[[1.0, third]]]])
+    assert np.float32(1.0) / np.float32(3.0) == np.float32(third) and 1.0 / 3.0 != third
+    assert ort.error_aware_route(err, n, 1, ratio_dtype=np.float32)[0, 0, 0].tolist() == [1, 0]
+    assert ort.error_aware_route(err, n, 1)[0, 0, 0].tolist() == [0, 1]
