@@ -326,6 +326,63 @@ def measure_sliding_tile(bsa, cfg, wl, q, k, v, reps=5):
     }
 
 
+def measure_routing(bsa, cfg, q, k, v, res, density, reps=5):
+    """Error-aware routing on the same Q, K, V and clusters as the path: the query-centroid
+    probes, the per-block errors (a dense pass of the Cq probes per head, then the per-cluster
+    sums) and the routes under a key budget equal to the scored masks' density, then the
+    compensated attention on the routed masks.  Each stage is timed alone with events on the
+    current stream."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+
+    layout = res.layout
+    kv = api.kv_pack(k, v, layout)
+    budget = int(round(density * cfg.S))
+    ws = torch.empty(_lib_size("bsa_block_error_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D, layout.C,
+                               layout.C), dtype=torch.uint8, device=q.device)
+    qbar = api.query_centroids(q, layout)
+    err = api.block_error(qbar, kv, cfg.scale, workspace=ws)
+    mask = api.error_route(err, layout, budget)
+    aws = api.attention_workspace(q, kv, layout, mask)
+    out = torch.empty_like(q)
+    stages = {
+        "probes": lambda: api.query_centroids(q, layout),
+        "block_error": lambda: api.block_error(qbar, kv, cfg.scale, workspace=ws),
+        "route": lambda: api.error_route(err, layout, budget),
+        "attention": lambda: api.block_sparse_attention(q, kv, layout, mask, True, cfg.scale, out=out, workspace=aws),
+    }
+    stream = torch.cuda.current_stream()
+    ms = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    n = layout.counts.double()
+    pairs = float(((mask.keep.double() @ n) * n).sum()) * (cfg.Hq // mask.keep.shape[1])
+    # Two passes of the Cq probes over every key: 4 D flops per (probe, key) pair each.
+    err_flops = 2 * 4 * cfg.D * layout.C * cfg.S * cfg.B * cfg.Hq
+    att_tflops = 4 * cfg.D * pairs / (ms["attention"] * 1e-3) / 1e12
+    return {
+        "budget_tokens": budget, "density": round(pairs / (cfg.B * cfg.Hq * float(cfg.S) ** 2), 4),
+        "probes_ms": round(ms["probes"], 4), "block_error_ms": round(ms["block_error"], 4),
+        "route_ms": round(ms["route"], 4),
+        "block_error_TFLOPs": round(err_flops / (ms["block_error"] * 1e-3) / 1e12, 2),
+        "block_error_mfma_frac": round(err_flops / (ms["block_error"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attention_ms": round(ms["attention"], 4), "attention_executed_pair_TFLOPs": round(att_tflops, 2),
+    }
+
+
+def _lib_size(name, *args):
+    from block_sparse_attention_antidiagonal_amd import _lib
+    return _lib.size_query(name, *args)
+
+
 def profile_kernels(bsa, path, cfg, q, k, v, reps):
     """One path call, then `reps` launches of the pack, the scores and the attention alone,
     then one plain device copy of COPY_BYTES (reads and writes that many bytes)."""
@@ -508,6 +565,8 @@ def main() -> int:
     line["mask_reuse"] = measure_reuse(bsa, cfg, q, k, res)
     print("[bench] sliding-tile mask", file=sys.stderr, flush=True)
     line["sliding_tile_attention"] = measure_sliding_tile(bsa, cfg, wl, q, k, v)
+    print("[bench] error-aware routing", file=sys.stderr, flush=True)
+    line["error_aware_routing"] = measure_routing(bsa, cfg, q, k, v, res, line["config"]["density"])
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl)
