@@ -124,8 +124,9 @@ def summarize_profiles(d: str) -> int:
         lines = [f"# Kernel trace: whole path, video workload (B=1, H=40, S=32760, D=128, bf16)", "",
                  "Command (from the repository root, on one MI355X):", "", "```", PROFILE_COMMANDS["trace"], "```",
                  "", "7 calls per path kernel = 2 warmup + 5 timed path calls.  The other dispatches come from "
-                 "the same run's mask-reuse and sliding-tile measurements (the `bfloat16`-output "
-                 "attention kernel is the sliding-tile workload).  Durations in microseconds.", "",
+                 "the same run's mask-reuse, sliding-tile and error-aware-routing measurements (the "
+                 "`bfloat16`-output attention kernel runs the sliding-tile and the routed masks).  "
+                 "Durations in microseconds.", "",
                  "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
         for r in rows:
             lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
