@@ -682,6 +682,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
                                                                int32_t* __restrict__ ctl) {
   __shared__ int wsum[kMaxGroups];
   __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
+  __shared__ int8_t gq[kMaxGroups];  // the queue of each group (read by the serial loop below)
   __shared__ int seg[2][kXcds + 1];
   __shared__ long long load[2][kXcds];
   __shared__ int ngx[2][kXcds];
@@ -700,7 +701,10 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
     return;
   }
-  for (int i = t; i < ng; i += kOrderThreads) wsum[i] = gsum[i];
+  for (int i = t; i < ng; i += kOrderThreads) {
+    wsum[i] = gsum[i];
+    gq[i] = (fast_ok && hmix[i] == 0) ? 0 : 1;
+  }
   __syncthreads();
   // Rank the groups by descending work (ties by index).
   for (int i = t; i < ng; i += kOrderThreads) {
@@ -716,7 +720,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
       for (int x = 0; x < kXcds; ++x) load[q][x] = ngx[q][x] = 0;
     for (int r = 0; r < ng; ++r) {
       const int gi = place[r];
-      const int q = (fast_ok && hmix[gi] == 0) ? 0 : 1;
+      const int q = gq[gi];
       int xs = 0;
       for (int x = 1; x < kXcds; ++x)
         if (load[q][x] < load[q][xs]) xs = x;

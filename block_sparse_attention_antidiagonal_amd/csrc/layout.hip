@@ -68,19 +68,58 @@ __global__ __launch_bounds__(1024) void layout_scan(int C, int nchunks, int32_t*
 }
 
 // Stable scatter: the rank of token p among earlier tokens of its chunk with the same label.
+// The chunk is cut into 64-token segments, one wave each: inside a segment, one ballot per
+// distinct label gives every lane its rank among earlier lanes and the label's count, which
+// the segment lists in LDS; a token's rank adds the counts of its label in earlier segments.
+// The work grows with the number of distinct labels per segment (a few for tile labels).
+constexpr int kSeg = 64;
+constexpr int kSegs = kChunk / kSeg;
 __global__ __launch_bounds__(256) void layout_scatter(const int32_t* __restrict__ labels, int S, int C,
                                                        const int32_t* __restrict__ base, int32_t* __restrict__ perm) {
-  __shared__ int32_t lab[kChunk];
+  __shared__ int32_t seg_lab[kSegs][kSeg];  // distinct labels of each segment
+  __shared__ int32_t seg_cnt[kSegs][kSeg];  // and their counts
+  __shared__ int32_t seg_n[kSegs];
+  constexpr int kWaves = 256 / 64;
   const int start = blockIdx.x * kChunk;
   const int n = min(kChunk, S - start);
-  for (int i = threadIdx.x; i < kChunk; i += blockDim.x) lab[i] = i < n ? labels[start + i] : -1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int lab_r[kSegs / kWaves], rank_r[kSegs / kWaves];
+#pragma unroll
+  for (int k = 0; k < kSegs / kWaves; ++k) {
+    const int seg = wave + k * kWaves;
+    const int i = seg * kSeg + lane;
+    int li = i < n ? labels[start + i] : -1;
+    if (li < 0 || li >= C) li = -1;
+    int rank = 0, nd = 0;
+    unsigned long long left = __ballot(li >= 0);
+    while (left) {
+      const int leader = __ffsll(static_cast<long long>(left)) - 1;
+      const int l = __builtin_amdgcn_readlane(li, leader);
+      const unsigned long long m = __ballot(li == l);
+      if (li == l) rank = __popcll(m & below);
+      if (lane == 0) {
+        seg_lab[seg][nd] = l;
+        seg_cnt[seg][nd] = __popcll(m);
+      }
+      ++nd;
+      left &= ~m;
+    }
+    if (lane == 0) seg_n[seg] = nd;
+    lab_r[k] = li;
+    rank_r[k] = rank;
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int li = lab[i];
-    if (li < 0 || li >= C) continue;
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += (lab[j] == li);
-    perm[base[static_cast<size_t>(blockIdx.x) * C + li] + rank] = start + i;
+#pragma unroll
+  for (int k = 0; k < kSegs / kWaves; ++k) {
+    const int seg = wave + k * kWaves;
+    const int li = lab_r[k];
+    int pre = 0;
+    for (int s2 = 0; s2 < seg; ++s2) {
+      const int nd = seg_n[s2];
+      for (int d = 0; d < nd; ++d) pre += seg_lab[s2][d] == li ? seg_cnt[s2][d] : 0;
+    }
+    if (li >= 0) perm[base[static_cast<size_t>(blockIdx.x) * C + li] + pre + rank_r[k]] = start + seg * kSeg + lane;
   }
 }
 
