@@ -35,7 +35,7 @@ class PathConfig:
     labels: np.ndarray  # int32 [S] (host)
     C: int
     scale: float
-    mask_mode: str  # "given" or "scored"
+    mask_mode: str  # "given", "scored" or "routed" (error-aware routes under route_density)
     keep: Optional[np.ndarray] = None  # given mode: uint8 [B or 1, Hm, C, C]
     block: int = 128
     stride: int = 16
@@ -47,6 +47,7 @@ class PathConfig:
     lam: float = 0.1
     rank: int = 16
     overlap: bool = True  # pack and probe rows on a second stream, beside scores and top-p
+    route_density: float = 0.2  # routed mode: keys each row computes exactly, as a fraction of S
 
     @classmethod
     def from_workload(cls, wl) -> "PathConfig":
@@ -85,12 +86,18 @@ class SparseAttentionPath:
         self._scores = None  # score rows kept across calls when a mask cache is used
         self._probe_ws = None  # dense probe partials (bfloat16 inputs)
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
-        if cfg.mask_mode == "given":
+        if cfg.mask_mode not in ("given", "scored", "routed"):
+            raise ValueError(f"unknown mask mode {cfg.mask_mode!r}")
+        self._err_ws = None  # routed mode: block-error workspace
+        if cfg.mask_mode == "routed":
+            if cfg.D not in (64, 128) or not 0.0 <= cfg.route_density <= 1.0:
+                raise ValueError("routed mode needs D in {64, 128} and 0 <= route_density <= 1")
+        elif cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
             if keep.shape[0] == 1 and cfg.B > 1:
                 keep = np.broadcast_to(keep, (cfg.B,) + keep.shape[1:])
             self.given_keep = torch.as_tensor(np.ascontiguousarray(keep)).to(self.device)
-        else:
+        elif cfg.mask_mode == "scored":
             self.tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(self.device)
         if cfg.probes:
             idx, w = api.select_probe_rows(cfg.labels, cfg.C, cfg.probes)
@@ -170,6 +177,20 @@ class SparseAttentionPath:
             mark("scores")
             mask = api.top_p_block_mask(scores, self.tau)
             mark("top_p")
+        elif cfg.mask_mode == "routed":
+            # Error-aware routes need the packed tiles and centroids: wait for the pack.
+            if side is not main:
+                main.wait_stream(side)
+            qbar = api.query_centroids(q, layout)
+            mark("route_probes")
+            if self._err_ws is None:
+                n = _lib.size_query("bsa_block_error_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D, cfg.C,
+                                    cfg.C)
+                self._err_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+            err = api.block_error(qbar, kv, cfg.scale, workspace=self._err_ws)
+            mark("block_error")
+            mask = api.error_route(err, layout, int(round(cfg.route_density * cfg.S)))
+            mark("route")
         else:
             mask = api.mask_from_keep(self.given_keep)
             mark("mask_lists")

@@ -184,3 +184,39 @@ def test_block_error_video_sampled(bsa):
             assert np.all(np.abs(got - want) <= 2 * bound), float(np.max(np.abs(got - want) - 2 * bound))
             kr = keep[0, h, a]
             assert n[kr].sum() >= budget and not np.any(kr & (n == 0))
+
+
+def test_path_routed(bsa):
+    """The whole path with error-aware routes in place of scores and top-p (compensated, no
+    probes): its mask equals the stage-by-stage routes, and the rows of every query cluster
+    whose route equals the oracle's match the oracle's compensated attention on that route."""
+    from oracle import attention as oatt
+    from gpu_common import check_output
+
+    S, density = 1800, 0.3
+    say("routed path")
+    wl = make_custom(41, B=1, Hq=2, Hkv=1, S=S, D=128, dtype="bf16", cluster_sizes=_sizes(41, S, 20, 160))
+    cfg = bsa.PathConfig.from_workload(wl)
+    cfg.mask_mode, cfg.route_density = "routed", density
+    path = bsa.SparseAttentionPath(cfg)
+    q, k, v = dev(wl.q, "bf16"), dev(wl.k, "bf16"), dev(wl.v, "bf16")
+    res = path(q, k, v)
+    torch.cuda.synchronize()
+    budget = int(round(density * S))
+    lay = bsa.cluster_layout(torch.from_numpy(wl.labels).cuda(), wl.C)
+    err = bsa.block_error(bsa.query_centroids(q, lay), bsa.kv_pack(k, v, lay), wl.scale)
+    keep = res.mask.keep.cpu().numpy()
+    assert np.array_equal(keep, bsa.error_route(err, lay, budget).keep.cpu().numpy())
+    n = np.bincount(wl.labels, minlength=wl.C)
+    oq = ort.query_centroids(wl.q, wl.labels, wl.C, bf16=True)
+    okeep = ort.error_aware_route(ort.block_compensation_error(oq, wl.k, wl.v, wl.labels, wl.C, wl.scale), n, budget)
+    out = host(res.out)
+    checked = 0
+    for h in range(2):
+        same = np.all(keep[0, h] == okeep[0, h], axis=1)
+        rows = np.nonzero(same[wl.labels])[0]
+        ref, _ = oatt.compensated_attention(wl.q[0, h], wl.k[0, 0], wl.v[0, 0], wl.labels, wl.labels, okeep[0, h],
+                                            wl.scale, True, rows=rows)
+        check_output(out[0, h][rows], ref, "bf16", f"routed path h{h}")
+        checked += rows.size
+    assert checked >= 0.8 * 2 * S
