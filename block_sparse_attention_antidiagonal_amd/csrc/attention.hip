@@ -684,8 +684,6 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   __shared__ int place[kMaxGroups];  // first the group of each rank, then the slot of each group
   __shared__ int8_t gq[kMaxGroups];  // the queue of each group (read by the serial loop below)
   __shared__ int seg[2][kXcds + 1];
-  __shared__ long long load[2][kXcds];
-  __shared__ int ngx[2][kXcds];
   const int t = threadIdx.x;
   const int G = Hq / Hkv;
   const int ng = B * Hkv;
@@ -715,35 +713,75 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   }
   __syncthreads();
   if (t == 0) {
-    // Longest processing time first: each group to the least loaded XCD of its queue.
-    for (int q = 0; q < 2; ++q)
-      for (int x = 0; x < kXcds; ++x) load[q][x] = ngx[q][x] = 0;
+    // Longest processing time first: each group to the least loaded XCD of its queue.  The
+    // per-XCD loads and group counts of both queues stay in registers (the loops over XCDs
+    // are unrolled), so the serial loop waits on no memory but the group's own entries.
+    long long ld[2][kXcds];
+    int cnt[2][kXcds];
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x) ld[0][x] = ld[1][x] = cnt[0][x] = cnt[1][x] = 0;
     for (int r = 0; r < ng; ++r) {
       const int gi = place[r];
-      const int q = gq[gi];
+      const bool q1 = gq[gi] != 0;
+      const long long w = wsum[gi];
       int xs = 0;
-      for (int x = 1; x < kXcds; ++x)
-        if (load[q][x] < load[q][xs]) xs = x;
-      load[q][xs] += wsum[gi];
-      wsum[gi] = (q * kXcds + xs) * kMaxGroups + ngx[q][xs]++;  // queue, XCD and slot of the group
+      long long best = q1 ? ld[1][0] : ld[0][0];
+#pragma unroll
+      for (int x = 1; x < kXcds; ++x) {
+        const long long lx = q1 ? ld[1][x] : ld[0][x];
+        if (lx < best) {
+          best = lx;
+          xs = x;
+        }
+      }
+      int slot = 0;
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) {
+        if (x == xs) {
+          if (q1) {
+            ld[1][x] += w;
+            slot = cnt[1][x]++;
+          } else {
+            ld[0][x] += w;
+            slot = cnt[0][x]++;
+          }
+        }
+      }
+      wsum[gi] = ((q1 ? kXcds : 0) + xs) * kMaxGroups + slot;  // queue, XCD and slot of the group
     }
     int run = 0;
+#pragma unroll
     for (int q = 0; q < 2; ++q) {
+#pragma unroll
       for (int x = 0; x < kXcds; ++x) {
         seg[q][x] = run;
         ctl[q * kQueueCtl + 8 + x] = run;
         ctl[q * kQueueCtl + x] = 0;
-        run += ngx[q][x] * per;
+        run += cnt[q][x] * per;
       }
       seg[q][kXcds] = run;
       ctl[q * kQueueCtl + 8 + kXcds] = run;
     }
   }
   __syncthreads();
-  for (int u = t; u < units; u += kOrderThreads) {
-    const int bk = u / per;
-    const int qx = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
-    order[seg[qx / kXcds][qx % kXcds] + slot * per + rank[u]] = u;
+  // Each thread's ranks are loaded together before any store depends on them.
+  constexpr int kOrderBatch = 16;
+  for (int u0 = t; u0 < units; u0 += kOrderThreads * kOrderBatch) {
+    int rk[kOrderBatch];
+#pragma unroll
+    for (int i = 0; i < kOrderBatch; ++i) {
+      const int u = u0 + i * kOrderThreads;
+      rk[i] = u < units ? rank[u] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kOrderBatch; ++i) {
+      const int u = u0 + i * kOrderThreads;
+      if (u < units) {
+        const int bk = u / per;
+        const int qx = wsum[bk] / kMaxGroups, slot = wsum[bk] % kMaxGroups;
+        order[seg[qx / kXcds][qx % kXcds] + slot * per + rk[i]] = u;
+      }
+    }
   }
 }
 
@@ -1312,7 +1350,7 @@ __global__ __launch_bounds__(kThreads, 2) void block_error_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const bool store = h == 0 && my < Cq;
-  float* err_row = err + (static_cast<size_t>(bh) * Cq + my) * Ck + c0;
+  float* err_row = err + (static_cast<size_t>(bh) * Cq + (my < Cq ? my : 0)) * Ck + c0;  // used only with store
   for (int ci = 0; ci < nc; ++ci)
     if (store && n_s[ci] <= 0) err_row[ci] = 0.0f;  // an empty cluster: no tiles, no error
   const int T0 = toff_s[0], T1 = toff_s[nc];
