@@ -186,13 +186,15 @@ def test_workspace_sizes(lib):
 
 
 def test_block_error_workspace_size(lib):
-    """The first pass's partial rows (32 chunks of 24 token tiles for S = 32760, 256 clusters),
+    """The first pass's partial rows (24 chunks of 32 token tiles for S = 32760, 256 clusters),
     its rows and its log-sum-exp, each section 256-byte aligned."""
     from block_sparse_attention_antidiagonal_amd import _lib
 
     a = lambda n: -(-n // 256) * 256
     assert _lib.size_query("bsa_block_error_workspace_size", 1, 40, 40, 32760, 128, 256, 256) == \
-        a(40 * 32 * 256 * 130 * 4) + a(40 * 256 * 128 * 4) + a(40 * 256 * 4)
+        a(40 * 24 * 256 * 130 * 4) + a(40 * 256 * 128 * 4) + a(40 * 256 * 4)
+    assert _lib.size_query("bsa_probe_attention_packed_workspace_size", 1, 40, 40, 32760, 128, 64, 256) == \
+        40 * 24 * 64 * 130 * 4
 
 
 @pytest.mark.parametrize("grid,tile,window", [((1, 3, 4), (1, 1, 1), (1, 3, 3)), ((4, 8, 12), (2, 4, 4), (1, 2, 3)),
