@@ -130,6 +130,134 @@ __global__ __launch_bounds__(256) void top_p_kernel(const float* __restrict__ sc
   if (threadIdx.x == 0) kv_count[row] = offset;
 }
 
+// Rows of at most 256 clusters: one wave per row, four keys per lane (lane l holds sorted
+// positions 4l .. 4l+3), so the bitonic sort runs in registers -- partners one to three
+// positions away within the lane, farther ones in another lane by a shuffle -- and the
+// prefix sum, the cut and the kept list use wave scans, without barriers.  The keys, the
+// order and the cut rule are those of top_p_kernel.
+constexpr int kWaveCk = 256;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const int lo = __shfl_xor(static_cast<int>(x & 0xffffffffu), m);
+  const int hi = __shfl_xor(static_cast<int>(x >> 32), m);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+__global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict__ scores, int rows, int Cq, int Ck,
+                                                          const float* __restrict__ tau, int n_tau, int Hs,
+                                                          uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
+                                                          int16_t* __restrict__ kv_idx) {
+  __shared__ uint8_t kb_s[4][kWaveCk];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
+  const int g = static_cast<int>(row / Cq);
+  const float tau_r = n_tau == 1 ? tau[0] : tau[g % Hs];
+  const float* srow = scores + row * Ck;
+  uint64_t key[4];
+  float sv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane * 4 + j;
+    sv[j] = i < Ck ? srow[i] : 0.0f;
+    key[j] = i < Ck ? (static_cast<uint64_t>(sortable(sv[j])) << 32) | static_cast<uint32_t>(0xffffffffu - i) : 0ull;
+  }
+  // Bitonic sort of 256 keys, descending (position i = 4 lane + j).
+#pragma unroll
+  for (int k = 2; k <= kWaveCk; k <<= 1) {
+#pragma unroll
+    for (int d = k >> 1; d > 0; d >>= 1) {
+      if (d >= 4) {
+        const int dl = d >> 2;
+        const bool lower = (lane & dl) == 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint64_t other = shfl_xor_u64(key[j], dl);
+          const bool desc = ((lane * 4 + j) & k) == 0;
+          const bool keep_max = desc == lower;
+          key[j] = keep_max ? (key[j] > other ? key[j] : other) : (key[j] < other ? key[j] : other);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if ((j & d) != 0) continue;
+          const int p = j | d;
+          const bool desc = ((lane * 4 + j) & k) == 0;
+          const uint64_t a = key[j], b = key[p];
+          if (desc ? (a < b) : (a > b)) {
+            key[j] = b;
+            key[p] = a;
+          }
+        }
+      }
+    }
+  }
+  // Inclusive prefix sum of the sorted scores: 4 per lane, then over the lanes.
+  float loc[4];
+  float run = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane * 4 + j;
+    float x = 0.0f;
+    if (i < Ck) x = srow[0xffffffffu - static_cast<uint32_t>(key[j])];
+    run += x;
+    loc[j] = run;
+  }
+  const float incl = wave_incl_scan(run);
+  const float before = incl - run;
+  const float total = __shfl(incl, 63);
+  const float target = tau_r * total;
+  // The first rank whose cumulative mass reaches the target (Ck - 1 if none does).
+  int mine = kWaveCk;
+#pragma unroll
+  for (int j = 3; j >= 0; --j)
+    if (lane * 4 + j < Ck && before + loc[j] >= target) mine = lane * 4 + j;
+  const unsigned long long hit = __ballot(mine < kWaveCk);
+  int last = Ck - 1;
+  if (hit) last = __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1);
+  uint8_t* kb = kb_s[wave];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kb[lane * 4 + j] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane * 4 + j <= last) kb[0xffffffffu - static_cast<uint32_t>(key[j])] = 1;
+  __builtin_amdgcn_wave_barrier();
+  uint8_t* krow = keep + row * Ck;
+  int bits[4], nb = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane * 4 + j;
+    bits[j] = c < Ck ? kb[c] : 0;
+    if (c < Ck) krow[c] = static_cast<uint8_t>(bits[j]);
+    nb += bits[j];
+  }
+  // Ascending kept list.
+  const int ni = wave_incl_scan_i(nb);
+  int pos = ni - nb;
+  int16_t* lrow = kv_idx + row * Ck;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (bits[j]) lrow[pos++] = static_cast<int16_t>(lane * 4 + j);
+  if (lane == 63) kv_count[row] = ni;
+}
+
 __global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restrict__ keep, int Ck,
                                                           int32_t* __restrict__ kv_count,
                                                           int16_t* __restrict__ kv_idx) {
@@ -272,6 +400,11 @@ extern "C" bsa_status bsa_top_p_mask(const float* scores, int G, int Cq, int Ck,
   if (Ck > kMaxCk) return BSA_E_UNSUPPORTED;
   const long long rows = static_cast<long long>(G) * Cq;
   if (rows > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
+  if (Ck <= kWaveCk) {
+    hipLaunchKernelGGL(top_p_wave_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, scores,
+                       static_cast<int>(rows), Cq, Ck, tau, n_tau, Hs, keep, kv_count, kv_idx);
+    return launch_status();
+  }
   hipLaunchKernelGGL(top_p_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, scores, Cq, Ck, tau, n_tau,
                      Hs, keep, kv_count, kv_idx);
   return launch_status();

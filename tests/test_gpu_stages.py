@@ -181,11 +181,14 @@ def test_kv_pack(bsa, dtype, D, sizes, mixed):
 # ------------------------------------------------------------------ top-p
 
 
-@pytest.mark.parametrize("Ck,seed", [(1, 0), (16, 1), (32, 2), (256, 3), (1000, 4)])
-def test_top_p(bsa, Ck, seed):
-    say(f"top-p Ck={Ck}")
+# Rows of at most 256 clusters take the one-wave-per-row kernel (four rows per workgroup; 41
+# query blocks leave a part-filled last workgroup), wider rows the workgroup-per-row kernel.
+@pytest.mark.parametrize("Ck,seed,Cq", [(1, 0, 40), (16, 1, 40), (32, 2, 40), (200, 5, 41), (256, 3, 40),
+                                        (257, 6, 41), (1000, 4, 40)])
+def test_top_p(bsa, Ck, seed, Cq):
+    say(f"top-p Ck={Ck} Cq={Cq}")
     rng = np.random.default_rng(seed)
-    B, Hs, Cq = 2, 3, 40
+    B, Hs = 2, 3
     scores = rng.dirichlet(np.full(Ck, 0.3), size=(B, Hs, Cq)).astype(np.float32)
     scores[0, 0, 0] = 1.0 / Ck  # an all-equal row: ties by lower index
     taus = np.array([0.85, 0.9, 0.95], dtype=np.float32)
