@@ -159,26 +159,10 @@ __device__ __forceinline__ int wave_incl_scan_i(int x) {
   }
   return x;
 }
-__global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict__ scores, int rows, int Cq, int Ck,
-                                                          const float* __restrict__ tau, int n_tau, int Hs,
-                                                          uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
-                                                          int16_t* __restrict__ kv_idx) {
-  __shared__ uint8_t kb_s[4][kWaveCk];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;
-  if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
-  const int g = static_cast<int>(row / Cq);
-  const float tau_r = n_tau == 1 ? tau[0] : tau[g % Hs];
-  const float* srow = scores + row * Ck;
-  uint64_t key[4];
-  float sv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = lane * 4 + j;
-    sv[j] = i < Ck ? srow[i] : 0.0f;
-    key[j] = i < Ck ? (static_cast<uint64_t>(sortable(sv[j])) << 32) | static_cast<uint32_t>(0xffffffffu - i) : 0ull;
-  }
-  // Bitonic sort of 256 keys, descending (position i = 4 lane + j).
+
+// Bitonic sort of 256 keys held four per lane (position i = 4 lane + j), descending.
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&key)[4]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 2; k <= kWaveCk; k <<= 1) {
 #pragma unroll
@@ -208,6 +192,28 @@ __global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict__ scores, int rows, int Cq, int Ck,
+                                                          const float* __restrict__ tau, int n_tau, int Hs,
+                                                          uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
+                                                          int16_t* __restrict__ kv_idx) {
+  __shared__ uint8_t kb_s[4][kWaveCk];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
+  const int g = static_cast<int>(row / Cq);
+  const float tau_r = n_tau == 1 ? tau[0] : tau[g % Hs];
+  const float* srow = scores + row * Ck;
+  uint64_t key[4];
+  float sv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane * 4 + j;
+    sv[j] = i < Ck ? srow[i] : 0.0f;
+    key[j] = i < Ck ? (static_cast<uint64_t>(sortable(sv[j])) << 32) | static_cast<uint32_t>(0xffffffffu - i) : 0ull;
+  }
+  wave_sort_desc(key);
   // Inclusive prefix sum of the sorted scores: 4 per lane, then over the lanes.
   float loc[4];
   float run = 0.0f;
@@ -249,6 +255,85 @@ __global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict
     nb += bits[j];
   }
   // Ascending kept list.
+  const int ni = wave_incl_scan_i(nb);
+  int pos = ni - nb;
+  int16_t* lrow = kv_idx + row * Ck;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (bits[j]) lrow[pos++] = static_cast<int16_t>(lane * 4 + j);
+  if (lane == 63) kv_count[row] = ni;
+}
+
+// Error-aware routes for rows of at most 256 clusters: one wave per row, as top_p_wave_kernel
+// (keys: err / n_c as in error_route_kernel; the prefix sum counts keys).
+__global__ __launch_bounds__(256) void error_route_wave_kernel(const float* __restrict__ err, int rows, int Ck,
+                                                               const int32_t* __restrict__ k_off, int budget,
+                                                               uint8_t* __restrict__ keep,
+                                                               int32_t* __restrict__ kv_count,
+                                                               int16_t* __restrict__ kv_idx) {
+  __shared__ uint8_t kb_s[4][kWaveCk];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
+  const float* erow = err + row * Ck;
+  uint64_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane * 4 + j;
+    key[j] = 0;  // empty clusters (and padding) sort last
+    if (i < Ck) {
+      const int n = k_off[i + 1] - k_off[i];
+      if (n > 0)
+        key[j] = (static_cast<uint64_t>(sortable(__fdiv_rn(erow[i], static_cast<float>(n)))) << 32) |
+                 static_cast<uint32_t>(0xffffffffu - i);
+    }
+  }
+  wave_sort_desc(key);
+  int loc[4];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int n = 0;
+    if (key[j] != 0) {
+      const int c = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key[j]));
+      n = k_off[c + 1] - k_off[c];
+    }
+    run += n;
+    loc[j] = run;
+  }
+  const int before = wave_incl_scan_i(run) - run;
+  // Last kept rank: the first non-empty rank whose cumulative count reaches the budget, else
+  // the last non-empty rank.
+  int mine = kWaveCk, last_ne = -1;
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    if (key[j] == 0) continue;
+    last_ne = max(last_ne, lane * 4 + j);
+    if (before + loc[j] >= budget) mine = lane * 4 + j;
+  }
+  const unsigned long long hit = __ballot(mine < kWaveCk);
+  int last = -1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last_ne = max(last_ne, __shfl_xor(last_ne, o));
+  last = last_ne;
+  if (hit) last = min(last, __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1));
+  uint8_t* kb = kb_s[wave];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kb[lane * 4 + j] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane * 4 + j <= last) kb[0xffffffffu - static_cast<uint32_t>(key[j])] = 1;
+  __builtin_amdgcn_wave_barrier();
+  uint8_t* krow = keep + row * Ck;
+  int bits[4], nb = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane * 4 + j;
+    bits[j] = c < Ck ? kb[c] : 0;
+    if (c < Ck) krow[c] = static_cast<uint8_t>(bits[j]);
+    nb += bits[j];
+  }
   const int ni = wave_incl_scan_i(nb);
   int pos = ni - nb;
   int16_t* lrow = kv_idx + row * Ck;
@@ -422,6 +507,11 @@ extern "C" bsa_status bsa_error_route(const float* err, int rows, int Ck, const 
                                       uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream) {
   if (!err || !k_offsets || !keep || !kv_count || !kv_idx || rows < 1 || Ck < 1) return BSA_E_ARG;
   if (Ck > kMaxCk) return BSA_E_UNSUPPORTED;
+  if (Ck <= kWaveCk) {
+    hipLaunchKernelGGL(error_route_wave_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, err, rows, Ck, k_offsets,
+                       budget, keep, kv_count, kv_idx);
+    return launch_status();
+  }
   hipLaunchKernelGGL(error_route_kernel, dim3(rows), dim3(256), 0, stream, err, Ck, k_offsets, budget, keep, kv_count,
                      kv_idx);
   return launch_status();
