@@ -544,7 +544,7 @@ struct TileDma {
   }
 };
 
-// The tile sequence of one mask row, expanded ahead of the attention by tile_list_kernel:
+// The tile sequence of one mask row, expanded ahead of the attention by tile_list_wave_kernel:
 // the centroid tiles (compensation), then the tiles of every kept key cluster in list order,
 // one int32 entry per tile: bits 0-22 the packed tile index, bits 23-28 the tile's key count
 // minus one, bit 29 set for centroid tiles.  A cluster's tile count is clamped to the tiles
@@ -558,29 +558,29 @@ __device__ __forceinline__ int entry_tile(int e) { return e & ((1 << kEntryTileB
 __device__ __forceinline__ int entry_nvalid(int e) { return ((e >> kEntryTileBits) & 63) + 1; }
 __device__ __forceinline__ bool entry_centroid(int e) { return (e & kEntryCentroid) != 0; }
 
-constexpr int kListThreads = 256;
-
-// One workgroup per mask row: writes the row's entries (at most maxe) and their count.
-__global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* __restrict__ kv_count,
-                                                                  const int16_t* __restrict__ kv_idx, int Ck,
-                                                                  const int32_t* __restrict__ k_off,
-                                                                  const int32_t* __restrict__ tile_off, int first_ctile,
-                                                                  int ctiles, int comp, int maxe,
-                                                                  int32_t* __restrict__ entries,
-                                                                  int32_t* __restrict__ counts) {
-  __shared__ int scan[kListThreads];
-  const size_t row = blockIdx.x;
-  const int t = threadIdx.x;
+// One wave per mask row (four rows per workgroup): writes the row's entries (at most maxe)
+// and their count.  The row's clusters go 64 at a time, one per lane, and a wave scan of their
+// tile counts places their entries.
+__global__ __launch_bounds__(256) void tile_list_wave_kernel(const int32_t* __restrict__ kv_count,
+                                                             const int16_t* __restrict__ kv_idx, int rows, int Ck,
+                                                             const int32_t* __restrict__ k_off,
+                                                             const int32_t* __restrict__ tile_off, int first_ctile,
+                                                             int ctiles, int comp, int maxe,
+                                                             int32_t* __restrict__ entries,
+                                                             int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
   const int cnt = kv_count[row];
   const int16_t* list = kv_idx + row * Ck;
   int32_t* out = entries + row * maxe;
   int base = 0;
   if (comp) {
-    for (int e = t; e < ctiles && e < maxe; e += kListThreads) out[e] = entry_make(first_ctile + e, kNK, true);
+    for (int e = lane; e < ctiles && e < maxe; e += 64) out[e] = entry_make(first_ctile + e, kNK, true);
     base = min(ctiles, maxe);
   }
-  for (int p0 = 0; p0 < cnt; p0 += kListThreads) {
-    const int p = p0 + t;
+  for (int p0 = 0; p0 < cnt; p0 += 64) {
+    const int p = p0 + lane;
     int nt = 0, n = 0, t0 = 0;
     if (p < cnt) {
       const int cl = list[p];
@@ -591,21 +591,17 @@ __global__ __launch_bounds__(kListThreads) void tile_list_kernel(const int32_t* 
         if (n <= 0 || t0 < 0 || nt < 0) nt = 0;
       }
     }
-    // Inclusive scan of the tile counts over the workgroup.
-    scan[t] = nt;
-    __syncthreads();
-    for (int d = 1; d < kListThreads; d <<= 1) {
-      const int add = t >= d ? scan[t - d] : 0;
-      __syncthreads();
-      scan[t] += add;
-      __syncthreads();
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
     }
-    const int first = base + scan[t] - nt;
+    const int first = base + incl - nt;
     for (int j = 0; j < nt && first + j < maxe; ++j) out[first + j] = entry_make(t0 + j, min(kNK, n - j * kNK), false);
-    base += scan[kListThreads - 1];
-    __syncthreads();
+    base += __shfl(incl, 63);
   }
-  if (t == 0) counts[row] = min(base, maxe);
+  if (lane == 0) counts[row] = min(base, maxe);
 }
 
 // Work order for the attention.  Workgroups are dispatched to the 8 XCDs round-robin, and
@@ -1511,8 +1507,9 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   int32_t* rank = reinterpret_cast<int32_t*>(wsb + W.rank);
   int32_t* gsum = reinterpret_cast<int32_t*>(wsb + W.gsum);
   int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
-  hipLaunchKernelGGL(tile_list_kernel, dim3(static_cast<unsigned>(rows)), dim3(kListThreads), 0, stream, kv_count,
-                     kv_idx, Ck, k_off, P.tile_off, P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
+  hipLaunchKernelGGL(tile_list_wave_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream,
+                     kv_count, kv_idx, static_cast<int>(rows), Ck, k_off, P.tile_off, P.first_ctile, P.ctiles,
+                     comp ? 1 : 0, maxe, entries, counts);
   constexpr bool kHalf = sizeof(T) == 2;  // float16 products exist for bfloat16 inputs only
   const int per = Cq * (Hq / Hkv);
   const bool sort_ok = per <= kMaxSortUnits;
