@@ -302,28 +302,34 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
   }
 }
 
-// One workgroup per (batch, score head, query block): merge the key tiles of each strided
-// row (full-row softmax), sum the block's rows, normalize, and average over the query heads
-// of a group when pooling.
+// One workgroup per (batch, score head, kFinQB query blocks): merge the key tiles of each
+// strided row (full-row softmax), sum each block's rows, normalize, and average over the query
+// heads of a group when pooling.  A thread owns key blocks c and reads, for each, the kFinQB R
+// consecutive strided rows of the workgroup (128 contiguous bytes for R = 8), so the rows
+// 8 KB apart in the partial sums are read in whole cache lines.  Per query block the
+// arithmetic and its order are those of one block per workgroup.
+constexpr int kFinQB = 4;
 template <int R>
 __global__ __launch_bounds__(256) void score_finalize_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ mstat,
                                                               const float* __restrict__ lstat, int Hq, int Hs,
                                                               int Ns, int nb, int ntk, float* __restrict__ scores,
                                                               const uint8_t* __restrict__ heads) {
-  __shared__ float Mrow[R], Lrow[R];
-  __shared__ float red[256];
-  const int a = blockIdx.x, bhs = blockIdx.y;
-  if (heads != nullptr && heads[bhs] == 0) return;  // row kept from an earlier call
+  constexpr int QR = kFinQB * R;  // strided rows of the workgroup
+  __shared__ float Mrow[QR], Lrow[QR];
+  __shared__ float red[kFinQB][256];
+  const int a0 = blockIdx.x * kFinQB, bhs = blockIdx.y;
+  if (heads != nullptr && heads[bhs] == 0) return;  // rows kept from an earlier call
+  const int nq = min(kFinQB, nb - a0);              // query blocks of this workgroup
   const int b = bhs / Hs, hs = bhs % Hs;
   const int G = Hq / Hs;
-  constexpr int kPerT = 4;  // blocks per thread (nb <= 1024)
-  float acc[kPerT] = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kPerT = 4;  // key blocks per thread (nb <= 1024)
+  float acc[kFinQB][kPerT] = {};
   for (int gi = 0; gi < G; ++gi) {
     const int hq = hs * G + gi;
     const size_t bh = static_cast<size_t>(b) * Hq + hq;
-    if (threadIdx.x < R) {
-      const int row = a * R + threadIdx.x;
+    if (threadIdx.x < QR && static_cast<int>(threadIdx.x) < nq * R) {
+      const int row = a0 * R + threadIdx.x;
       float M = -INFINITY;
       for (int k = 0; k < ntk; ++k) M = fmaxf(M, mstat[(bh * ntk + k) * Ns + row]);
       float L = 0.0f;
@@ -335,41 +341,60 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(const float* __rest
       Lrow[threadIdx.x] = L;
     }
     __syncthreads();
-    float mass[kPerT];
+    float mass[kFinQB][kPerT];
 #pragma unroll
     for (int e = 0; e < kPerT; ++e) {
       const int c = threadIdx.x + e * 256;
-      mass[e] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kFinQB; ++q) mass[q][e] = 0.0f;
       if (c < nb) {
         const int k = c * R / kTile;
+        const float* prow = part + (bh * nb + c) * Ns + a0 * R;
+        const float* mrow = mstat + (bh * ntk + k) * Ns + a0 * R;
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int row = a * R + i;
-          const float w = fast_exp2(mstat[(bh * ntk + k) * Ns + row] - Mrow[i]) / Lrow[i];
-          mass[e] += part[(bh * nb + c) * Ns + row] * w;
+        for (int q = 0; q < kFinQB; ++q) {
+          if (q < nq) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+              const float w = fast_exp2(mrow[q * R + i] - Mrow[q * R + i]) / Lrow[q * R + i];
+              mass[q][e] += prow[q * R + i] * w;
+            }
+          }
         }
       }
     }
-    float tot = 0.0f;
 #pragma unroll
-    for (int e = 0; e < kPerT; ++e) tot += mass[e];
-    red[threadIdx.x] = tot;
+    for (int q = 0; q < kFinQB; ++q) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kPerT; ++e) tot += mass[q][e];
+      red[q][threadIdx.x] = tot;
+    }
     __syncthreads();
     for (int d = 128; d > 0; d >>= 1) {
-      if (threadIdx.x < static_cast<unsigned>(d)) red[threadIdx.x] += red[threadIdx.x + d];
+      if (threadIdx.x < static_cast<unsigned>(d))
+#pragma unroll
+        for (int q = 0; q < kFinQB; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + d];
       __syncthreads();
     }
-    const float inv = 1.0f / red[0];
 #pragma unroll
-    for (int e = 0; e < kPerT; ++e) acc[e] += mass[e] * inv;
+    for (int q = 0; q < kFinQB; ++q) {
+      const float inv = 1.0f / red[q][0];
+#pragma unroll
+      for (int e = 0; e < kPerT; ++e) acc[q][e] += mass[q][e] * inv;
+    }
     __syncthreads();
   }
   const float invG = 1.0f / static_cast<float>(G);
-  float* out = scores + (static_cast<size_t>(bhs) * nb + a) * nb;
 #pragma unroll
-  for (int e = 0; e < kPerT; ++e) {
-    const int c = threadIdx.x + e * 256;
-    if (c < nb) out[c] = G == 1 ? acc[e] : acc[e] * invG;
+  for (int q = 0; q < kFinQB; ++q) {
+    if (q >= nq) break;
+    float* out = scores + (static_cast<size_t>(bhs) * nb + a0 + q) * nb;
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) {
+      const int c = threadIdx.x + e * 256;
+      if (c < nb) out[c] = G == 1 ? acc[q][e] : acc[q][e] * invG;
+    }
   }
 }
 
@@ -399,8 +424,8 @@ void launch_scores(int B, int Hq, int Hkv, int S, const void* Q, const void* K, 
   hipLaunchKernelGGL(kern, dim3(sd.ntk, sd.ntk, B * Hq), dim3(kSThreads), SStage<T>::LDS_BYTES, stream,
                      static_cast<const T*>(Q), static_cast<const T*>(K), perm, Hq, Hkv, S, stride, sd.Ns, sd.nb, sd.ntk,
                      score_scale * kLog2e, part, mstat, lstat, heads, Hs);
-  hipLaunchKernelGGL((score_finalize_kernel<R>), dim3(sd.nb, B * Hs), dim3(256), 0, stream, part, mstat, lstat, Hq, Hs,
-                     sd.Ns, sd.nb, sd.ntk, scores, heads);
+  hipLaunchKernelGGL((score_finalize_kernel<R>), dim3((sd.nb + kFinQB - 1) / kFinQB, B * Hs), dim3(256), 0, stream,
+                     part, mstat, lstat, Hq, Hs, sd.Ns, sd.nb, sd.ntk, scores, heads);
 }
 
 template <typename T, int D>
