@@ -55,7 +55,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan_S32760_H40
 KERNEL_SOURCES = ("attention.hip", "pack.hpp", "common.hpp")
 ATTN_KERNEL = "sparse_attn_kernel"
 # The rocprofv3 runs behind the profiles/ summaries, from the repository root; each writes
-# <name>_*.csv into DIR (gpurun_out/prof).
+# <name>_*.csv into the directory given after -d, which --summarize-profiles then reads.
 PROFILE_COMMANDS = {
     "trace": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $R/gpurun_out/prof -o trace -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
