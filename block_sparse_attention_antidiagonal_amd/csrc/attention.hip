@@ -1239,8 +1239,11 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
                                                         float* __restrict__ Od, float* __restrict__ lse2) {
   const int m = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
   float mx = -INFINITY;
+  // Unrolled so that the loads of several chunks are in flight together.
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, mpart[(static_cast<size_t>(bh) * nchunks + c) * M + m]);
   float l = 0.0f, o = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
     const size_t prow = (static_cast<size_t>(bh) * nchunks + c) * M + m;
     const float mc = mpart[prow];
