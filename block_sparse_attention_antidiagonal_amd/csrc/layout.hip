@@ -39,6 +39,7 @@ __global__ __launch_bounds__(1024) void layout_scan(int C, int nchunks, int32_t*
   int32_t run = 0;
   for (int c = c0; c < c0 + per && c < C; ++c) {
     int32_t n = 0;
+#pragma unroll 8
     for (int k = 0; k < nchunks; ++k) n += hist[static_cast<size_t>(k) * C + c];
     counts[c] = n;
     run += n;
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(1024) void layout_scan(int C, int nchunks, int32_t*
   for (int c = c0; c < c0 + per && c < C; ++c) {
     offsets[c] = off;
     int32_t within = off;
+#pragma unroll 8
     for (int k = 0; k < nchunks; ++k) {
       const size_t idx = static_cast<size_t>(k) * C + c;
       const int32_t n = hist[idx];

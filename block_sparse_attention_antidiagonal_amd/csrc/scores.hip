@@ -331,8 +331,10 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(const float* __rest
     if (threadIdx.x < QR && static_cast<int>(threadIdx.x) < nq * R) {
       const int row = a0 * R + threadIdx.x;
       float M = -INFINITY;
+#pragma unroll 8
       for (int k = 0; k < ntk; ++k) M = fmaxf(M, mstat[(bh * ntk + k) * Ns + row]);
       float L = 0.0f;
+#pragma unroll 8
       for (int k = 0; k < ntk; ++k) {
         const size_t s = (bh * ntk + k) * Ns + row;
         L += lstat[s] * fast_exp2(mstat[s] - M);
