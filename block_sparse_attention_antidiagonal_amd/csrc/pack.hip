@@ -90,7 +90,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
   constexpr int kItems = kPackTile * CPR / kPackThreads;  // (key, chunk) items per thread
   constexpr int kKeyGroups = M::kKeyGroups;               // keys covered in one pass
   __shared__ __align__(16) unsigned char smem[M::BYTES];
-  __shared__ uint32_t emax_s;
+  // Largest bfloat16 exponent of the tile's values, one slot per tile parity: slot j & 1 is
+  // cleared at the top of tile j, when every wave has passed tile j-1's first barrier and so
+  // has finished reading the slot's value of tile j-2.  (With one slot, a wave still reading
+  // tile j's value after the second barrier could see thread 0's reset for tile j+1.)
+  __shared__ uint32_t emax_s[2];
   VS* vt = reinterpret_cast<VS*>(smem);                      // [kPackTile][VROW]: the tile's V
   float* red = reinterpret_cast<float*>(smem);               // [2][kKeyGroups][D], after the tiles
   const int c = blockIdx.x;
@@ -105,7 +109,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
   const int ntiles = (n + kPackTile - 1) / kPackTile;
   for (int j = 0; j < ntiles; ++j) {
     const size_t tile = bh * tiles_per_head + tile_off[c] + j;
-    if (t == 0) emax_s = 0;
+    uint32_t* emax_slot = &emax_s[j & 1];
+    if (t == 0) *emax_slot = 0;
     uint4 kv[kItems], vv[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         vv[i] = *reinterpret_cast<const uint4*>(Vh + row);
       }
     }
-    __syncthreads();  // emax_s cleared; the previous tile's V^T reads are done
+    __syncthreads();  // the slot cleared; the previous tile's V^T reads are done
     uint32_t emax = 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
@@ -138,11 +143,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vv[i];
       }
     }
-    if constexpr (sizeof(T) == 2) atomicMax(&emax_s, emax);
+    if constexpr (sizeof(T) == 2) atomicMax(emax_slot, emax);
     __syncthreads();
     // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).
     if constexpr (sizeof(T) == 2) {
-      const bool f16 = emax_s <= 142u && emax_s >= 119u;  // bfloat16 exponent 142: [2^15, 2^16); 119: 2^-8
+      const uint32_t tile_emax = *emax_slot;
+      const bool f16 = tile_emax <= 142u && tile_emax >= 119u;  // bfloat16 exponent 142: [2^15, 2^16); 119: 2^-8
       if (t == 0) {
         flags[tile] = f16 ? 1 : 0;
         if (!f16) atomicOr(&hmix[bh], 1);
