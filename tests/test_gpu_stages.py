@@ -106,20 +106,36 @@ def scale_v_clusters(wl, scales):
 MIXED = {(0, 0, 1): 2.0 ** 17, (0, 1, 2): 2.0 ** -14, (1, 0, 0): 2.0 ** 20}
 
 
+def scale_v_alternate_tiles(wl, factor):
+    """Multiply V of every second 64-key tile of each cluster (tiles 1, 3, ... in layout order)
+    by a power of two, so that consecutive tiles of one cluster take different V^T formats."""
+    perm, off, _ = olay.cluster_layout(wl.labels, wl.C)
+    for c in range(wl.C):
+        rows = perm[off[c]: off[c + 1]]
+        for j in range(1, -(-rows.size // 64), 2):
+            wl.v[:, :, rows[j * 64: (j + 1) * 64]] *= factor
+    return wl
+
+
 @pytest.mark.parametrize("dtype,D,sizes,mixed", [("bf16", 128, None, False), ("f32", 64, None, False),
                                                  ("bf16", 64, [0, 1, 63, 64, 65, 130, 7], False),
-                                                 ("bf16", 128, None, True)])
+                                                 ("bf16", 128, None, True),
+                                                 ("bf16", 128, [200, 150, 70, 64, 300, 129, 1], "tiles")])
 def test_kv_pack(bsa, dtype, D, sizes, mixed):
     """Packed tiles hold every cluster's keys in layout order, zero-padded to 64, V^T as float16
-    exactly when the tile's values fit (else bfloat16), and the centroid tiles; bit-exact."""
+    exactly when the tile's values fit (else bfloat16), and the centroid tiles; bit-exact.
+    The "tiles" case alternates the format from tile to tile inside clusters of several tiles,
+    so that each tile's format decision must not leak into its neighbour's."""
     say(f"kv pack {dtype} D={D} sizes={sizes} mixed={mixed}")
     if sizes is None:
         wl = make_custom(13, B=2, Hq=2, Hkv=2, S=1500, D=D, dtype=dtype)
         if mixed:
             scale_v_clusters(wl, MIXED)
     else:
-        wl = make_custom(14, B=1, Hq=1, Hkv=1, S=sum(sizes), D=D, dtype=dtype, cluster_sizes=sizes,
-                         shuffle_labels=True)
+        wl = make_custom(14, B=1 if mixed != "tiles" else 2, Hq=1, Hkv=1, S=sum(sizes), D=D, dtype=dtype,
+                         cluster_sizes=sizes, shuffle_labels=True)
+        if mixed == "tiles":
+            scale_v_alternate_tiles(wl, 2.0 ** 17)
     B, Hkv, S, C = wl.B, wl.Hkv, wl.S, wl.C
     lab = torch.from_numpy(wl.labels).cuda()
     lay = bsa.cluster_layout(lab, C)
@@ -134,8 +150,11 @@ def test_kv_pack(bsa, dtype, D, sizes, mixed):
         for h in range(Hkv):
             u = b * Hkv + h
             kb, vb, _ = ocen.centroids(wl.k[b, h], wl.v[b, h], wl.labels, C)
-            assert np.allclose(kbar[b, h], kb, rtol=1e-5, atol=1e-6)
-            assert np.allclose(vbar[b, h], vb, rtol=1e-5, atol=1e-6)
+            # float32 sums: the rounding is relative to the terms' magnitude, not the mean's
+            # (a cluster mixing tiles scaled by 2^17 with plain ones cancels to small means)
+            ka, va, _ = ocen.centroids(np.abs(wl.k[b, h]), np.abs(wl.v[b, h]), wl.labels, C)
+            assert np.all(np.abs(kbar[b, h] - kb) <= 1e-5 * ka + 1e-6)
+            assert np.all(np.abs(vbar[b, h] - vb) <= 1e-5 * va + 1e-6)
             kbits = bf16_bits(wl.k[b, h]) if elem == 2 else wl.k[b, h].astype(np.float32)
             for c in range(C):
                 rows = perm[off[c]: off[c + 1]]
@@ -196,8 +215,11 @@ def test_top_p(bsa, Ck, seed, Cq):
     keep, cnt, idx = mask.keep.cpu().numpy(), mask.kv_count.cpu().numpy(), mask.kv_idx.cpu().numpy()
     for b in range(B):
         for h in range(Hs):
+            # Both sides sort the same float32 scores, so only the prefix sums round apart.  The
+            # 1000-cluster Dirichlet rows put many tiny scores at the cut: up to 15% of their
+            # rows decide a block within 1e-5 of tau.
             compare_masks(keep[b, h], cnt[b, h], idx[b, h], scores[b, h].astype(np.float64), float(taus[h]),
-                          f"top-p b{b} h{h}")
+                          f"top-p b{b} h{h}", eps_tie=0.0, max_fragile=0.15 if Ck > 256 else 0.10)
     assert cnt.min() >= 1
 
 
