@@ -14,8 +14,9 @@ Pages:
 The pages give no formula for the probe, the error or the budget.  Readings (the plainest
 ones the rest of the pages support):
   * Probe.  One probe per query cluster a: its centroid q_bar_a, the mean of the cluster's
-    query rows (the query-side counterpart of k_bar_c), rounded to the input type like the
-    centroid keys the attention uses.  Empty query clusters get a zero probe and no route.
+    query rows (the query-side counterpart of k_bar_c), here in float64.  Empty query clusters
+    get a zero probe and no route.  (A kernel may hand its probes to the error pass in the
+    input type; parity then compares within that rounding.)
   * Error.  For the probe, with logits s_j = q_bar_a . k_j * scale over all keys, softmax
     weights p_j = exp(s_j - lse) and dense output O_a = sum_j p_j v_j: compensating block
     (a, c) alone replaces the cluster's exact terms (N_c = sum_{j in c} p_j v_j,
@@ -37,17 +38,9 @@ from __future__ import annotations
 import numpy as np
 
 
-def round_bf16(x) -> np.ndarray:
-    """Round float64 values to bfloat16 (nearest, ties to even), returned as float64."""
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
-
-
-def query_centroids(q, q_labels, Cq: int, bf16: bool = False) -> np.ndarray:
-    """Probe rows q_bar [B, Hq, Cq, D]: the mean of each query cluster's rows (zero for an
-    empty cluster), rounded to bfloat16 when the inputs are bfloat16."""
+def query_centroids(q, q_labels, Cq: int) -> np.ndarray:
+    """Probe rows q_bar [B, Hq, Cq, D] in float64: the mean of each query cluster's rows
+    (zero for an empty cluster)."""
     q = np.asarray(q, dtype=np.float64)
     lab = np.asarray(q_labels)
     B, H, S, D = q.shape
@@ -56,7 +49,7 @@ def query_centroids(q, q_labels, Cq: int, bf16: bool = False) -> np.ndarray:
         rows = np.nonzero(lab == a)[0]
         if rows.size:
             out[:, :, a, :] = q[:, :, rows, :].mean(axis=2)
-    return round_bf16(out) if bf16 else out
+    return out
 
 
 def block_compensation_error(qbar, k, v, k_labels, Ck: int, scale: float) -> np.ndarray:
@@ -92,19 +85,17 @@ def block_compensation_error(qbar, k, v, k_labels, Ck: int, scale: float) -> np.
     return err
 
 
-def error_aware_route(err, k_counts, budget: float, ratio_dtype=np.float64) -> np.ndarray:
+def error_aware_route(err, k_counts, budget: float) -> np.ndarray:
     """Keep bits uint8 [B, H, Cq, Ck]: per row, the shortest prefix of the non-empty clusters
     in order of err / n_c (descending, ties by index) whose key count reaches `budget`, and
-    at least one cluster (see the header).  ratio_dtype=np.float32 forms the ratios as
-    correctly rounded float32 quotients of float32 errors, the precision in which the kernel
-    takes the same decision."""
-    err = np.asarray(err, dtype=ratio_dtype)
+    at least one cluster (see the header).  Ratios are formed in float64."""
+    err = np.asarray(err, dtype=np.float64)
     n = np.asarray(k_counts, dtype=np.int64)
     keep = np.zeros(err.shape, dtype=np.uint8)
     nz = np.nonzero(n > 0)[0]
     for idx in np.ndindex(*err.shape[:-1]):
         row = err[idx]
-        ratio = row[nz] / n[nz].astype(ratio_dtype)
+        ratio = row[nz] / n[nz].astype(np.float64)
         order = nz[np.lexsort((nz, -ratio))]  # descending ratio, lower index first on ties
         total = 0
         for c in order:

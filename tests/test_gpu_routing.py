@@ -9,7 +9,7 @@ import torch
 from oracle import routing as ort
 from synthetic import make_custom
 
-from gpu_common import dev, host, say
+from gpu_common import dev, host, round_bf16, route_fragile_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -51,11 +51,12 @@ def test_query_centroids(bsa, dtype, D, S, Hq):
     wl = make_custom(21, B=2, Hq=Hq, Hkv=Hq, S=S, D=D, dtype=dtype, cluster_sizes=_sizes(5, S, 1, 160))
     lay = bsa.cluster_layout(torch.from_numpy(wl.labels).cuda(), wl.C)
     got = host(bsa.query_centroids(dev(wl.q, dtype), lay))
-    want = ort.query_centroids(wl.q, wl.labels, wl.C, bf16=dtype == "bf16")
+    want = ort.query_centroids(wl.q, wl.labels, wl.C)  # float64 means
     assert np.all(got[:, :, 3] == 0.0)  # the empty cluster
     if dtype == "bf16":
-        # Float32 sums in another order may round the mean to the neighbouring bfloat16 value.
-        ulps = _bf16_ulps(got, want)
+        # The kernel returns its float32 mean rounded to bfloat16: within one bfloat16 step of
+        # the float64 mean's rounding (float32 sums in another order may round either way).
+        ulps = _bf16_ulps(got, round_bf16(want))
         assert ulps.max() <= 1 and np.mean(ulps) < 0.01, (ulps.max(), np.mean(ulps))
     else:
         assert np.allclose(got, want, rtol=1e-5, atol=1e-6)
@@ -74,7 +75,9 @@ def test_block_error(bsa, seed, B, Hq, Hkv, S, D, sizes):
     wl = make_custom(seed, B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype="bf16", cluster_sizes=_sizes(seed, S, *sizes))
     lay = bsa.cluster_layout(torch.from_numpy(wl.labels).cuda(), wl.C)
     kv = bsa.kv_pack(dev(wl.k, "bf16"), dev(wl.v, "bf16"), lay)
-    qbar = ort.query_centroids(wl.q, wl.labels, wl.C, bf16=True)  # probes: the oracle's (exact in bfloat16)
+    # The probes are an input of the error pass: the float64 means rounded to bfloat16, the
+    # element type the kernel takes, hand both sides identical probe rows.
+    qbar = round_bf16(ort.query_centroids(wl.q, wl.labels, wl.C))
     err = host(bsa.block_error(dev(qbar, "bf16"), kv, wl.scale))
     want = ort.block_compensation_error(qbar, wl.k, wl.v, wl.labels, wl.C, wl.scale)
     assert np.all(err[..., 3] == 0.0)  # the empty cluster
@@ -93,7 +96,11 @@ def test_block_error(bsa, seed, B, Hq, Hkv, S, D, sizes):
                                             (7, 5, 10 ** 9)])
 def test_error_route_bit_exact(bsa, Ck, rows, budget):
     """Seeded errors with many exact ties and quotient near-ties, cluster sizes with empty
-    clusters: the kernel against the oracle taking its decisions in float32."""
+    clusters.  The kernel orders by float32 quotients, the oracle by float64 ones; rounding
+    can only tie near-equal quotients (then the lower index goes first), so every row whose
+    cut is not inside a near-tied run of float64 ratios must match bit for bit, and the others
+    must still be valid routes (budget reached, nothing ranked clearly below a dropped
+    cluster kept)."""
     say(f"route Ck={Ck} rows={rows} budget={budget}")
     rng = np.random.default_rng(Ck + rows)
     n = rng.integers(0, 90, Ck)
@@ -104,14 +111,27 @@ def test_error_route_bit_exact(bsa, Ck, rows, budget):
     class _L:  # the route reads only the key offsets
         offsets = torch.from_numpy(off).cuda()
     m = bsa.error_route(torch.from_numpy(err).cuda(), _L, budget)
-    want = ort.error_aware_route(err, n, budget, ratio_dtype=np.float32)
+    want = ort.error_aware_route(err, n, budget)
+    fragile = route_fragile_rows(err, n, budget)[0, 0]
     keep = m.keep.cpu().numpy()
-    assert np.array_equal(keep, want)
     cnt = m.kv_count.cpu().numpy()
     idx = m.kv_idx.cpu().numpy()
+    ratio = err[0, 0].astype(np.float64) / np.maximum(n, 1)
     for r in range(rows):
-        lst = np.nonzero(want[0, 0, r])[0]
-        assert cnt[0, 0, r] == lst.size and np.array_equal(idx[0, 0, r, :lst.size], lst)
+        got = keep[0, 0, r]
+        lst = np.nonzero(got)[0]
+        assert cnt[0, 0, r] == lst.size and np.array_equal(idx[0, 0, r, :lst.size], lst), r
+        if not fragile[r]:
+            assert np.array_equal(got, want[0, 0, r]), r
+            continue
+        kr = got.astype(bool)
+        assert lst.size >= 1 and not np.any(kr & (n == 0))
+        assert n[kr].sum() >= budget or np.all(kr == (n > 0))
+        dropped = ~kr & (n > 0)
+        if dropped.any():
+            assert ratio[r][kr].min() >= ratio[r][dropped].max() * (1 - 1e-6), r
+    print(f"[err] route rows with a float32 near-tie at the cut: {int(fragile.sum())} of {rows}", flush=True)
+    assert fragile.sum() <= max(2, rows // 10)
 
 
 @pytest.mark.parametrize("seed,B,Hq,Hkv,S,D,sizes", CASES[:2])
@@ -130,7 +150,7 @@ def test_routes_end_to_end(bsa, seed, B, Hq, Hkv, S, D, sizes):
     m = bsa.error_route(err, lay, budget)
     keep = m.keep.cpu().numpy().astype(bool)
     n = np.bincount(wl.labels, minlength=wl.C)
-    oq = ort.query_centroids(wl.q, wl.labels, wl.C, bf16=True)
+    oq = ort.query_centroids(wl.q, wl.labels, wl.C)  # float64 probes (the kernel's are bfloat16)
     oerr = ort.block_compensation_error(oq, wl.k, wl.v, wl.labels, wl.C, wl.scale)
     want = ort.error_aware_route(oerr, n, budget).astype(bool)
     same = 0
@@ -171,16 +191,16 @@ def test_block_error_video_sampled(bsa):
     n = np.bincount(wl.labels, minlength=wl.C)
     vmax = np.abs(wl.v).max()
     for h in (0, 17, 39):
-        oq = ort.query_centroids(wl.q[:, h:h + 1], wl.labels, wl.C, bf16=True)
+        oq = ort.query_centroids(wl.q[:, h:h + 1], wl.labels, wl.C)  # float64 probes
         gq = host(qbar[:, h:h + 1])
-        assert _bf16_ulps(gq, oq).max() <= 1
+        assert _bf16_ulps(gq, round_bf16(oq)).max() <= 1
         for a in (0, 101, wl.C - 1):
             say(f"routing video h{h} a{a}")
             want = ort.block_compensation_error(oq[:, :, a:a + 1], wl.k[:, h:h + 1], wl.v[:, h:h + 1], wl.labels, wl.C,
                                                 wl.scale)[0, 0, 0]
             got = err[0, h, a]
             bound = 1e-2 * want + 2e-3 * want.max() + 1e-5 * vmax
-            # the GPU's probe may sit one bfloat16 step away from the oracle's in a few features
+            # the GPU's probe is the float64 mean rounded to bfloat16 (within one step)
             assert np.all(np.abs(got - want) <= 2 * bound), float(np.max(np.abs(got - want) - 2 * bound))
             kr = keep[0, h, a]
             assert n[kr].sum() >= budget and not np.any(kr & (n == 0))
@@ -208,7 +228,7 @@ def test_path_routed(bsa):
     keep = res.mask.keep.cpu().numpy()
     assert np.array_equal(keep, bsa.error_route(err, lay, budget).keep.cpu().numpy())
     n = np.bincount(wl.labels, minlength=wl.C)
-    oq = ort.query_centroids(wl.q, wl.labels, wl.C, bf16=True)
+    oq = ort.query_centroids(wl.q, wl.labels, wl.C)
     okeep = ort.error_aware_route(ort.block_compensation_error(oq, wl.k, wl.v, wl.labels, wl.C, wl.scale), n, budget)
     out = host(res.out)
     checked = 0

@@ -207,6 +207,23 @@ def test_topp_golden():
     assert otp.top_p_row(np.array(g["row_block0_small"]), g["tau_block0_small"]).tolist() == g["keep_block0_small"]
 
 
+def test_fragile_blocks_golden():
+    """Hand-worked rows for the mask-parity exclusion: near-mass blocks on both sides of tau,
+    near-ties straddling the cut (two and three blocks), a near-tie inside the kept set and
+    ties just outside the window, which must not be excluded."""
+    g = golden("fragile_blocks_tiny.json")
+    for case in g["cases"]:
+        row = np.array(case["row"])
+        assert otp.top_p_row(row, case["tau"]).tolist() == case["keep"], case["name"]
+        got = otp.fragile_blocks(row, case["tau"]).astype(int).tolist()
+        assert got == case["fragile"], (case["name"], got)
+    # Permuting the blocks permutes the exclusion (the definition does not depend on position).
+    for case in g["cases"]:
+        row = np.array(case["row"])
+        p = np.arange(row.size)[::-1]
+        assert np.array_equal(otp.fragile_blocks(row[p], case["tau"]), np.array(case["fragile"], bool)[p]), case["name"]
+
+
 def brute_topp(row, tau):
     """All subsets: minimum cardinality with mass >= tau * total; among those the largest
     mass; remaining ties by lexicographically smallest sorted index tuple."""

@@ -1,12 +1,13 @@
 """Pins for the oracle's error-aware routing (CPU only).
 
 The pages print no worked example for the router, so the oracle is pinned by what the
-definitions fix: bfloat16 rounding against torch's conversion; query centroids of ramps in
+definitions fix: query centroids of ramps in
 closed form; zero compensation error where a centroid is exact (identical keys and values,
 one-key clusters); the exact identity between the first-order error and the brute-force
 output change of compensating one block, (O' - O)(1 + z_hat - Z_c) = delta, with O' from a
 softmax over the modified key set written out as a loop; invariance under reordering keys
-inside a cluster; and hand-worked routes.
+inside a cluster; and hand-worked routes.  The near-tie exclusion that the GPU route
+parity uses (a test helper, not part of the oracle) is pinned on hand-worked rows here too.
 """
 
 import numpy as np
@@ -14,16 +15,6 @@ import pytest
 import torch
 
 from oracle import routing as ort
-
-
-def test_round_bf16_matches_torch():
-    rng = np.random.default_rng(3)
-    x = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000),
-                        [1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]])
-    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
-    assert np.array_equal(ort.round_bf16(x), want)
-    assert ort.round_bf16([1.0 + 2 ** -8])[0] == 1.0              # tie to even (down)
-    assert ort.round_bf16([1.0 + 3 * 2 ** -8])[0] == 1.0 + 2 ** -6  # tie to even (up)
 
 
 def test_query_centroids_ramp_and_empty_cluster():
@@ -127,12 +118,37 @@ def test_route_rows_independent():
     assert keep[0, 1].tolist() == [[1, 1, 0], [1, 1, 0]]
 
 
-def test_route_float32_ratios_take_the_kernel_decision():
-    """1 / 3 and the float32 nearest to 1/3 tie in float32 (the lower index wins) but not in
-    float64 (the larger quotient wins)."""
+def test_route_float64_ratios():
+    """1 / 3 and the float32 nearest to 1/3 are distinct float64 quotients: the larger one
+    wins in float64 (a float32 evaluation would tie them and take the lower index)."""
     n = np.array([3, 1])
     third = float(np.float32(1.0) / np.float32(3.0))
     err = np.array([[[[1.0, third]]]])
-    assert np.float32(1.0) / np.float32(3.0) == np.float32(third) and 1.0 / 3.0 != third
-    assert ort.error_aware_route(err, n, 1, ratio_dtype=np.float32)[0, 0, 0].tolist() == [1, 0]
+    assert third > 1.0 / 3.0
     assert ort.error_aware_route(err, n, 1)[0, 0, 0].tolist() == [0, 1]
+
+
+def test_route_fragile_rows_helper():
+    """The GPU route comparison skips rows whose cut falls inside a run of float64 ratios that
+    are near-tied but not all equal (a float32 quotient can tie them and order them by index):
+    hand-worked rows."""
+    from gpu_common import round_bf16, route_fragile_rows
+
+    n = np.array([3, 1, 2, 4])
+    third = float(np.float32(1.0) / np.float32(3.0))
+    # ratios 1/3, third, 0.25, 0.5: cut after one cluster (budget 1) lands on ratio 0.5 (alone) -> fine
+    err = np.array([[[[1.0, third, 0.5, 2.0]]]])
+    assert not route_fragile_rows(err, n, 1)[0, 0, 0]
+    # budget 5: 0.5 (4 keys), then third (1 key): the cut at third, near-tied with 1/3 -> fragile
+    assert route_fragile_rows(err, n, 5)[0, 0, 0]
+    # exact ties only (0.5 and 0.5) at the cut: both sides order them by index -> not fragile
+    err2 = np.array([[[[1.5, 0.5, 1.0, 2.0]]]])
+    assert not route_fragile_rows(err2, n, 5)[0, 0, 0]
+    # bfloat16 rounding helper: torch's conversion, ties to even
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000),
+                        [1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_bf16(x), want)
+    assert round_bf16([1.0 + 2 ** -8])[0] == 1.0
+    assert round_bf16([1.0 + 3 * 2 ** -8])[0] == 1.0 + 2 ** -6
