@@ -68,6 +68,7 @@ SIGNATURES = {
 _RESTYPES = {"bsa_status_string": ctypes.c_char_p}
 
 BSA_F32, BSA_BF16 = 0, 1
+MAX_FIT_PROBES = 64  # bsa_probe_fit: 2 <= M <= this
 
 
 class BsaError(RuntimeError):

@@ -98,7 +98,17 @@ class SparseAttentionPath:
                 keep = np.broadcast_to(keep, (cfg.B,) + keep.shape[1:])
             self.given_keep = torch.as_tensor(np.ascontiguousarray(keep)).to(self.device)
         elif cfg.mask_mode == "scored":
+            # Score block i covers cluster-major tokens [i*block, (i+1)*block) and its mask row is
+            # used as query cluster i's row: every cluster must be exactly one block.
+            counts = np.bincount(np.asarray(cfg.labels, dtype=np.int64), minlength=cfg.C)
+            nb = -(-cfg.S // cfg.block)
+            if (cfg.C != nb or counts.size != cfg.C or np.any(counts[:-1] != cfg.block)
+                    or not 1 <= counts[-1] <= cfg.block):
+                raise ValueError("scored masks need clusters of exactly `block` tokens (the last one may be "
+                                 "shorter): cluster i must be score block i")
             self.tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(self.device)
+        if cfg.probes and not 2 <= cfg.probes <= _lib.MAX_FIT_PROBES:
+            raise ValueError(f"probes must lie in [2, {_lib.MAX_FIT_PROBES}] (the ridge fit's range)")
         if cfg.probes:
             idx, w = api.select_probe_rows(cfg.labels, cfg.C, cfg.probes)
             self.probe_idx = torch.as_tensor(idx).to(self.device)

@@ -10,3 +10,25 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Worst output error of each named workload (and overall), printed even under -q."""
+    try:
+        import gpu_common
+    except Exception:  # the CPU-only session never imports it
+        return
+    errs = getattr(gpu_common, "ERRORS", [])
+    if not errs:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "parity margins (worst error / bound)")
+    groups = {}
+    for what, metric, err, bound in errs:
+        key = " ".join(what.split()[:2]) if what.startswith("config") else "stage tests"
+        cur = groups.get((key, metric))
+        if cur is None or err / bound > cur[1] / cur[2]:
+            groups[(key, metric)] = (what, err, bound)
+    for (key, metric), (what, err, bound) in sorted(groups.items()):
+        tr.write_line(f"{key:12s} {metric:8s} worst {err:.3e} (bound {bound:.0e}, {err / bound:5.1%} of it) at {what}")
+    tr.write_line(f"{len(errs)} output comparisons")

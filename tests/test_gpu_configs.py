@@ -2,9 +2,10 @@
 
 Configs 0 and 1 are checked on every row of every head.  The video-shaped configs 2-4
 run at full size in the same launch configuration the benchmark times; the oracle then
-checks the masks of sampled heads (bit-exact outside fragile blocks) and the outputs of
-sampled rows (the ragged last cluster and the probe rows always included), using the GPU's
-own mask so that mask rounding cannot leak into output parity.
+checks the masks of every mask head (configs 2 and 4; bit-exact outside fragile blocks) and
+the outputs of sampled rows of sampled heads (the ragged last cluster and the probe rows
+always included), using the GPU's own mask so that mask rounding cannot leak into output
+parity.
 """
 
 import numpy as np
@@ -84,8 +85,11 @@ def test_video_config_sampled(bsa, cfg, heads):
     say(f"config {cfg} gpu path")
     path, res = run_gpu(bsa, wl)
     keep = res.mask.keep.cpu().numpy()
-    mask_pairs = sorted({(b, opipe.mask_head_of(wl, h)) for b, h in heads})
-    say(f"config {cfg} masks {mask_pairs}")
+    if cfg in (2, 4):  # every mask head (40, and 2 x 8 pooled group masks)
+        mask_pairs = [(b, hm) for b in range(wl.B) for hm in range(res.mask.Hm)]
+    else:  # the same inputs and masks as config 2
+        mask_pairs = sorted({(b, opipe.mask_head_of(wl, h)) for b, h in heads})
+    say(f"config {cfg} masks of {len(mask_pairs)} mask heads")
     check_masks(wl, res, mask_pairs)
     density = float(keep.mean())
     say(f"config {cfg} mask density {density:.4f}")
@@ -97,16 +101,16 @@ def test_video_config_sampled(bsa, cfg, heads):
         say(f"config {cfg} b{b} h{hq} rows {rows.size}")
         hm = opipe.mask_head_of(wl, hq)
         r = opipe.run_head(wl, b, hq, rows=rows, keep=keep[b, hm])
-        e1 = check_output(out_sparse[b, hq][rows], r["out_sparse"], wl.dtype, f"sparse b{b} h{hq}")
-        e2 = check_output(out[b, hq][rows], r["out"], wl.dtype, f"final b{b} h{hq}")
+        e1 = check_output(out_sparse[b, hq][rows], r["out_sparse"], wl.dtype, f"config {cfg} sparse b{b} h{hq}")
+        e2 = check_output(out[b, hq][rows], r["out"], wl.dtype, f"config {cfg} final b{b} h{hq}")
         say(f"config {cfg} b{b} h{hq} error sparse {e1:.3e} final {e2:.3e}")
         if wl.probes:
             # Probe invariant on the GPU's own numbers: repaired probe rows differ from the
             # exact rows by the fit residual of the oracle's fit on the same inputs.
             od = host(res.o_dense_probe)[b, hq]
-            check_output(od, r["o_dense_p"], wl.dtype, f"dense probe rows b{b} h{hq}")
+            check_output(od, r["o_dense_p"], wl.dtype, f"config {cfg} dense probe rows b{b} h{hq}")
             xs = host(res.o_sparse_probe)[b, hq]
-            check_output(xs, r["o_sparse_p"], wl.dtype, f"sparse probe rows b{b} h{hq}")
+            check_output(xs, r["o_sparse_p"], wl.dtype, f"config {cfg} sparse probe rows b{b} h{hq}")
             fit = orep.ridge_fit(xs, od, path.probe_w.cpu().numpy(), wl.lam, wl.rank)
             resid = fit["X"] @ fit["W"] @ fit["P"] - fit["Rc"]
             got = out[b, hq][probe_idx] - od
