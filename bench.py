@@ -1,27 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the whole block-sparse attention path on one MI355X.
 
-Workload: the Wan-shaped video case -- B=1, 40 heads, S=32760 tokens (a 21x30x52 latent
-grid), D=128, bfloat16, 256 tile-major clusters of 128 tokens (the last holds 120) --
-run through every stage of the path in one call: cluster layout, K/V packing with the
-centroids, antidiagonal
-block scores (block 128, stride 16), per-head top-p masks (tau per head from
-{0.85, 0.90, 0.95}), 64 probe rows (dense and block-sparse), the ridge fit (lambda 0.1,
-rank 16), and the compensated block-sparse attention whose epilogue applies the fitted
-correction.  Inputs are seeded synthetic fields (synthetic.make_config(2)) resident in
-HBM before timing starts.
+Headline workload: the Wan-shaped video case -- B=1, 40 heads, S=32760 tokens (a 21x30x52
+latent grid), D=128, bfloat16, 256 tile-major clusters of 128 tokens (the last holds 120)
+-- run through every stage of the path in one call: cluster layout, K/V packing with the
+centroids, antidiagonal block scores (block 128, stride 16), per-head top-p masks (tau per
+head from {0.85, 0.90, 0.95}) and the compensated block-sparse attention.  Inputs are seeded
+synthetic fields (synthetic.make_config(2)) resident in HBM before timing starts.
+
+Beside it, the two repair workloads are timed the same way (``repair_workloads``): the same
+inputs run as hard-drop attention with 64-probe ridge repair, and the grouped-query case
+(B=2, 40 query heads on 8 K/V heads, pooled masks, compensation and repair).
 
 Printed: one JSON line.  ``value`` is the executed-pair throughput of the whole call
-(4*D flops per executed token pair: kept-block pairs plus the probe rows' dense pairs,
-over the measured time per call); ``ms_per_step`` is the time per call.  ``roofline``
-covers the dominant kernel (the sparse attention): its algorithmic flops (4*D per kept
-token pair) over its average launch time, measured with events on the stream it runs on,
-against the bf16 dense MFMA peak; ``traffic`` is the kernel's HBM bytes per launch from the
-rocprofv3 counter summary in profiles/ when that summary was taken on the current kernel
-sources (else null).  ``cpu_baseline`` is the float64 CPU oracle timed on a bounded sample
-of the same workload (one head, a subset of query clusters).
+(4*D flops per kept token pair over the measured time per call); ``ms_per_step`` is the
+time per call.  ``roofline`` covers the dominant kernel (the sparse attention): its
+algorithmic flops (4*D per kept token pair) over its average launch time, measured with
+events on the stream it runs on, against the bf16 dense MFMA peak; ``traffic`` is the
+kernel's HBM bytes per launch from the rocprofv3 counter summary in profiles/ when that
+summary was taken on the current kernel sources (else null).  ``cpu_baseline`` is the
+float64 CPU oracle timed on a bounded sample of the same workload (one head, a subset of
+query clusters).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--path-only]
     python bench.py --profile-kernels K   # for rocprofv3: K launches of each kernel alone,
                                           # then one plain copy of a known size
     python bench.py --summarize-profiles DIR  # write the profiles/ summaries from the csv
@@ -31,6 +32,7 @@ of the same workload (one head, a subset of query clusters).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -47,18 +49,19 @@ if ROOT not in sys.path:
 METRIC = "ms/call + executed-pair TFLOP/s (% MFMA peak), S=32760 H=40 D=128 bf16"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-PROBES, LAMBDA, RANK = 64, 0.1, 16
-WORKLOAD = ("wan_video_21x30x52_S32760_H40_D128_bf16: scored top-p masks + compensated block-sparse "
-            "attention + 64-probe ridge repair")
+WORKLOAD = ("wan_video_21x30x52_S32760_H40_D128_bf16: antidiagonal scores + per-head top-p masks + "
+            "compensated block-sparse attention")
 COPY_BYTES = 1 << 30  # the reference copy for scaling the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan_S32760_H40_D128_traffic.json")
 KERNEL_SOURCES = ("attention.hip", "pack.hpp", "common.hpp")
 ATTN_KERNEL = "sparse_attn_kernel"
+TRACE_STEPS, TRACE_WARMUP = 5, 2  # the path calls of the "trace" command below
 # The rocprofv3 runs behind the profiles/ summaries, from the repository root; each writes
 # <name>_*.csv into the directory given after -d, which --summarize-profiles then reads.
 PROFILE_COMMANDS = {
     "trace": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d $R/gpurun_out/prof -o trace -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "-d $R/gpurun_out/prof -o trace -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+             "--path-only",
     "fetch": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
              "-d $R/gpurun_out/prof -o fetch -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
     "write": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
@@ -118,20 +121,37 @@ def summarize_profiles(d: str) -> int:
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     stem = "wan_S32760_H40_D128"
-    stats = os.path.join(d, "trace_kernel_stats.csv")
-    if os.path.exists(stats):
-        rows = list(csv.DictReader(open(stats)))
+    trace = os.path.join(d, "trace_kernel_trace.csv")
+    if os.path.exists(trace):
+        calls, warm = TRACE_STEPS + TRACE_WARMUP, TRACE_WARMUP
+        per = {}  # kernel -> durations in dispatch order (us)
+        with open(trace) as f:
+            for r in csv.DictReader(f):
+                per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+                    (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
         lines = [f"# Kernel trace: whole path, video workload (B=1, H=40, S=32760, D=128, bf16)", "",
-                 "Command (from the repository root, on one MI355X):", "", "```", PROFILE_COMMANDS["trace"], "```",
-                 "", "7 calls per path kernel = 2 warmup + 5 timed path calls.  The other dispatches come from "
-                 "the same run's mask-reuse, sliding-tile and error-aware-routing measurements (the "
-                 "`bfloat16`-output attention kernel runs the sliding-tile and the routed masks).  "
-                 "Durations in microseconds.", "",
-                 "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
-        for r in rows:
-            lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                         f"{float(r['Percentage']):.2f} |")
+                 "Command (from the repository root, on one MI355X):", "", "```", PROFILE_COMMANDS["trace"], "```", "",
+                 f"The run makes {calls} path calls: {warm} warm-up calls, then the {TRACE_STEPS} timed calls.  Each "
+                 f"kernel launched a whole number of times per call is summarized over the launches of the timed "
+                 f"calls only (its first {warm}/{calls} of launches dropped); durations in microseconds.", "",
+                 "| kernel | launches per call | timed launches | avg us | min us | max us |",
+                 "|---|---:|---:|---:|---:|---:|"]
+        per_call_total = {}
+        for k, ds in sorted(per.items(), key=lambda kv: -sum(x for _, x in kv[1])):
+            ds.sort()
+            if len(ds) % calls:
+                lines.append(f"| `{k}` | ? | {len(ds)} (all) | {np.mean([x for _, x in ds]):.1f} | "
+                             f"{min(x for _, x in ds):.1f} | {max(x for _, x in ds):.1f} |")
+                continue
+            m = len(ds) // calls
+            timed = [x for _, x in ds[warm * m:]]
+            per_call_total[k] = sum(timed) / TRACE_STEPS
+            lines.append(f"| `{k}` | {m} | {len(timed)} | {np.mean(timed):.1f} | {min(timed):.1f} | {max(timed):.1f} |")
+        attn = sum(v for k, v in per_call_total.items() if k.startswith(ATTN_KERNEL))
+        stage = sum(v for k, v in per_call_total.items() if k.startswith(ATTN_KERNEL) or k.split("<")[0] in
+                    ("tile_list_wave_kernel", "tile_list_kernel", "group_rank_kernel", "order_kernel"))
+        lines += ["", f"Attention kernels (`{ATTN_KERNEL}`, all variants) per timed call: {attn:.1f} us; with the "
+                  f"tile-list and work-order kernels of the attention stage: {stage:.1f} us."]
         with open(os.path.join(out_dir, f"path_kernels_{stem}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     fetch = os.path.join(d, "fetch_counter_collection.csv")
@@ -188,8 +208,9 @@ def executed_pairs(res, cfg):
 
 
 def cpu_baseline(wl, seconds_hint=20.0):
-    """The float64 oracle on a bounded sample: head 0, its scores and mask, the attention
-    rows of every 2nd query cluster, the 64 probe rows and the fit."""
+    """The float64 oracle on a bounded sample: head 0, its scores and mask, and the attention
+    rows of every 2nd query cluster (plus the probe rows and the fit when the workload has
+    them)."""
     from oracle import pipeline
 
     try:
@@ -214,8 +235,8 @@ def cpu_baseline(wl, seconds_hint=20.0):
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"head 0 of {wl.Hq}: scores + top-p mask, compensated attention for {rows.size} rows "
-                   f"({len(clusters)} of {wl.C} query clusters), {wl.probes} dense probe rows, ridge fit; "
-                   f"{elapsed:.1f} s"),
+                   f"({len(clusters)} of {wl.C} query clusters)"
+                   + (f", {wl.probes} dense probe rows, ridge fit" if wl.probes else "") + f"; {elapsed:.1f} s"),
         "seconds": elapsed,
     }
 
@@ -394,7 +415,7 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
     torch.cuda.synchronize()
     kv = api.kv_pack(k, v, res.layout)
     ws = api.attention_workspace(q, kv, res.layout, res.mask)
-    o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
     for i in range(reps):
         api.kv_pack(k, v, res.layout, kv.buffer)
         torch.cuda.synchronize()
@@ -405,8 +426,7 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
         torch.cuda.synchronize()
         print(f"[profile] scores {i}", flush=True)
     for i in range(reps):
-        api.block_sparse_attention(q, kv, res.layout, res.mask, cfg.compensate, cfg.scale, out=o32, out_f32=True,
-                                   workspace=ws)
+        api.block_sparse_attention(q, kv, res.layout, res.mask, cfg.compensate, cfg.scale, out=out, workspace=ws)
         torch.cuda.synchronize()
         print(f"[profile] attention {i}", flush=True)
     for i in range(reps):
@@ -422,12 +442,124 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
     return 0
 
 
+def time_path(path, q, k, v, steps, warmup):
+    """Warm up, then time `steps` whole path calls between two device synchronizations; per
+    stage, the mean of the events each stage records on its own stream."""
+    import torch
+
+    res = None
+    for _ in range(warmup):
+        res = path(q, k, v)
+    torch.cuda.synchronize()
+    if res is None:
+        res = path(q, k, v)
+        torch.cuda.synchronize()
+    marks = []  # per step: list of (stage, start event, end event)
+
+    def recorder(step_marks):
+        last = {}  # stream -> its latest event; a stage spans from there to its own mark
+
+        def mark(name):
+            stream = torch.cuda.current_stream()
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            if stream.cuda_stream in last:
+                step_marks.append((name, last[stream.cuda_stream], ev))
+            last[stream.cuda_stream] = ev
+        return mark
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sm = []
+        path(q, k, v, mark=recorder(sm))
+        marks.append(sm)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    stages = {}
+    for sm in marks:
+        for name, e0, e1 in sm:
+            stages.setdefault(name, []).append(e0.elapsed_time(e1))
+    return ms_per_step, {name: float(np.mean(x)) for name, x in stages.items()}, res
+
+
+def centroid_columns(res, cfg):
+    """Centroid columns per call: for every query row, one per skipped non-empty key cluster
+    (counted over all query heads)."""
+    import torch
+
+    keep = res.mask.keep.to(torch.float64)  # [B, Hm, Cq, Ck]
+    n = res.layout.counts.to(torch.float64)
+    nonempty = (n > 0).to(torch.float64)
+    skipped = ((1.0 - keep) * nonempty).sum(dim=-1)  # [B, Hm, Cq]
+    return float((skipped * n).sum().item()) * (cfg.Hq // keep.shape[1])
+
+
+def path_figures(res, cfg, ms_per_step, stages_ms, probes):
+    """Throughput and density figures of one timed path workload."""
+    pairs = executed_pairs(res, cfg)
+    cols = centroid_columns(res, cfg) if cfg.compensate else 0.0
+    full = cfg.B * cfg.Hq * float(cfg.S) ** 2
+    probe_pairs = float(cfg.B * cfg.Hq * probes * cfg.S)
+    attn_ms = stages_ms["attention"]
+    D = cfg.D
+    return {
+        "ms_per_call": round(ms_per_step, 4),
+        "density": round(pairs / full, 4),  # kept token pairs / S^2, averaged over heads
+        "density_with_probes": round((pairs + probe_pairs) / full, 4),  # + M*S per head
+        "executed_pairs": pairs + probe_pairs,
+        "executed_pair_TFLOPs": round(4 * D * (pairs + probe_pairs) / (ms_per_step * 1e-3) / 1e12, 2),
+        "attention_ms": round(attn_ms, 4),
+        "attention_TFLOPs": round(4 * D * pairs / (attn_ms * 1e-3) / 1e12, 2),
+        "attention_mfma_frac": round(4 * D * pairs / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        # the same kernel counting the centroid columns too (4*D flops each)
+        "attention_TFLOPs_with_centroids": round(4 * D * (pairs + cols) / (attn_ms * 1e-3) / 1e12, 2),
+        "centroid_columns": cols,
+        "stages_ms": {kk: round(vv, 4) for kk, vv in stages_ms.items()},
+    }
+
+
+def measure_repair_workloads(bsa, steps, warmup, wl2, q, k, v):
+    """The hard-drop + probe-repair workload on the headline inputs, then the grouped-query
+    workload (compensation + repair), each timed like the headline."""
+    import torch
+    from synthetic import make_config
+
+    out = {}
+    # The hard-drop repair workload is the headline's inputs with another path (the fields of
+    # make_config(3) are those of make_config(2)).
+    cfg3 = bsa.PathConfig.from_workload(dataclasses.replace(wl2, compensate=False, probes=64, lam=0.1, rank=16))
+    path3 = bsa.SparseAttentionPath(cfg3)
+    ms, st, res = time_path(path3, q, k, v, steps, warmup)
+    out["video_harddrop_probe_repair"] = dict(
+        workload="same inputs, hard-drop block-sparse attention + 64 probe rows + ridge fit (lambda 0.1, rank 16) "
+                 "+ correction of every row", **path_figures(res, cfg3, ms, st, cfg3.probes))
+    del path3, res
+    print("[bench] grouped-query workload", file=sys.stderr, flush=True)
+    wl4 = make_config(4)
+    q4 = torch.from_numpy(wl4.q).to(torch.bfloat16).cuda()
+    k4 = torch.from_numpy(wl4.k).to(torch.bfloat16).cuda()
+    v4 = torch.from_numpy(wl4.v).to(torch.bfloat16).cuda()
+    cfg4 = bsa.PathConfig.from_workload(wl4)
+    path4 = bsa.SparseAttentionPath(cfg4)
+    ms, st, res = time_path(path4, q4, k4, v4, steps, warmup)
+    out["video_gqa_compensated_probe_repair"] = dict(
+        workload="B=2, 40 query heads on 8 K/V heads, S=32760, D=128, bf16, Student-t values; masks pooled per K/V "
+                 "group; compensated attention + 64 probe rows + ridge fit + correction",
+        **path_figures(res, cfg4, ms, st, cfg4.probes))
+    del path4, res, q4, k4, v4
+    torch.cuda.synchronize()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path-only", action="store_true",
+                    help="time the headline path only (no repair workloads or side measurements)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the K/V packing and probe rows on the caller's stream too")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
@@ -450,7 +582,6 @@ def main() -> int:
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     wl = make_config(2)
-    wl.probes, wl.lam, wl.rank = PROBES, LAMBDA, RANK
     cfg = bsa.PathConfig.from_workload(wl)
     cfg.overlap = not args.no_overlap
     path = bsa.SparseAttentionPath(cfg)
@@ -462,56 +593,17 @@ def main() -> int:
     if args.profile_kernels:
         return profile_kernels(bsa, path, cfg, q, k, v, args.profile_kernels)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    res = None
-    for _ in range(args.warmup):
-        res = path(q, k, v)
-    torch.cuda.synchronize()
-    if res is None:
-        res = path(q, k, v)
-        torch.cuda.synchronize()
-    pairs = executed_pairs(res, cfg)
-    density = pairs / (cfg.B * cfg.Hq * float(cfg.S) ** 2)
-    probe_pairs = float(cfg.B * cfg.Hq * PROBES * cfg.S)
-
     print("[bench] timing", file=sys.stderr, flush=True)
-    marks = []  # per step: list of (stage, event)
-
-    def recorder(step_marks):
-        last = {}  # stream -> its latest event; a stage spans from there to its own mark
-
-        def mark(name):
-            stream = torch.cuda.current_stream()
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record(stream)
-            if stream.cuda_stream in last:
-                step_marks.append((name, last[stream.cuda_stream], ev))
-            last[stream.cuda_stream] = ev
-        return mark
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sm = []
-        path(q, k, v, mark=recorder(sm))
-        marks.append(sm)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    stages = {}
-    for sm in marks:
-        for name, e0, e1 in sm:
-            stages.setdefault(name, []).append(e0.elapsed_time(e1))
-    stages_ms = {name: float(np.mean(v)) for name, v in stages.items()}
+    ms_per_step, stages_ms, res = time_path(path, q, k, v, args.steps, args.warmup)
+    fig = path_figures(res, cfg, ms_per_step, stages_ms, 0)
+    pairs = executed_pairs(res, cfg)
     attn_ms = stages_ms["attention"]
 
     D, S, H = cfg.D, cfg.S, cfg.Hq
-    value = 4 * D * (pairs + probe_pairs) / (ms_per_step * 1e-3) / 1e12
+    value = 4 * D * pairs / (ms_per_step * 1e-3) / 1e12
     attn_flops = 4 * D * pairs
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     kv_bytes = 2 * cfg.B * cfg.Hkv * S * D * 2
-    B_H_S_D = cfg.B * cfg.Hq * S * D
     traffic = measured_traffic()
     qk_bytes = cfg.B * (cfg.Hq + cfg.Hkv) * S * D * 2
     score_flops = 2 * cfg.B * cfg.Hq * (math.ceil(S / 128) * 128) ** 2 * D / 16
@@ -532,11 +624,10 @@ def main() -> int:
         "config": {
             "workload": WORKLOAD,
             "B": cfg.B, "H": H, "S": S, "D": D, "block": 128, "stride": 16,
-            "tau": "per head from {0.85, 0.90, 0.95}", "density": round(density, 4),
-            "probes": PROBES, "lambda": LAMBDA, "rank": RANK, "compensation": True,
+            "tau": "per head from {0.85, 0.90, 0.95}", "density": fig["density"], "compensation": True,
         },
         "ms_per_call": round(ms_per_step, 4),
-        "executed_pairs": pairs + probe_pairs,
+        "executed_pairs": pairs,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -544,30 +635,34 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "sparse_attn_kernel (compensated, float32 rows)",
+            "kernel": ATTN_KERNEL + " (compensated)",
             "algorithmic_tflop_per_launch": attn_flops / 1e12,
             "avg_launch_ms": round(attn_ms, 4),
         },
-        "stages_ms": {kk: round(vv, 4) for kk, vv in stages_ms.items()},
+        "attention_TFLOPs_with_centroids": fig["attention_TFLOPs_with_centroids"],
+        "stages_ms": fig["stages_ms"],
         "stage_rates": {
             # the pack reads K and V once and writes them once as tiles
             "pack_GBps": round(2 * kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9, 1),
             "pack_hbm_frac": round(2 * kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            # the correction reads the float32 rows and writes the bfloat16 output once
-            "correct_GBps": round(3 * B_H_S_D * 2 / (stages_ms["correct"] * 1e-3) / 1e9, 1),
-            "correct_hbm_frac": round(3 * B_H_S_D * 2 / (stages_ms["correct"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            # the centroid sums alone must read K and V once (their algorithmic bytes)
+            "centroids_GBps": round(kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9, 1),
+            "centroids_hbm_frac": round(kv_bytes / (stages_ms["pack"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_GBps": round(qk_bytes / (stages_ms["scores"] * 1e-3) / 1e9, 1),
             "scores_hbm_frac": round(qk_bytes / (stages_ms["scores"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_TFLOPs": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12, 2),
             "scores_mfma_frac": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
     }
-    print("[bench] mask reuse", file=sys.stderr, flush=True)
-    line["mask_reuse"] = measure_reuse(bsa, cfg, q, k, res)
-    print("[bench] sliding-tile mask", file=sys.stderr, flush=True)
-    line["sliding_tile_attention"] = measure_sliding_tile(bsa, cfg, wl, q, k, v)
-    print("[bench] error-aware routing", file=sys.stderr, flush=True)
-    line["error_aware_routing"] = measure_routing(bsa, cfg, q, k, v, res, line["config"]["density"])
+    if not args.path_only:
+        print("[bench] repair workloads", file=sys.stderr, flush=True)
+        line["repair_workloads"] = measure_repair_workloads(bsa, args.steps, args.warmup, wl, q, k, v)
+        print("[bench] mask reuse", file=sys.stderr, flush=True)
+        line["mask_reuse"] = measure_reuse(bsa, cfg, q, k, res)
+        print("[bench] sliding-tile mask", file=sys.stderr, flush=True)
+        line["sliding_tile_attention"] = measure_sliding_tile(bsa, cfg, wl, q, k, v)
+        print("[bench] error-aware routing", file=sys.stderr, flush=True)
+        line["error_aware_routing"] = measure_routing(bsa, cfg, q, k, v, res, line["config"]["density"])
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl)
