@@ -27,6 +27,7 @@ from .api import (  # noqa: E402,F401
     error_route,
     gather_rows,
     kv_pack,
+    kv_pack_centroids,
     mask_from_keep,
     mask_reuse_decide,
     mask_reuse_update,

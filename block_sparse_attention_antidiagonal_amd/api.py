@@ -123,6 +123,29 @@ def kv_pack(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout,
     return PackedKV(buffer, kbar, vbar, layout, B, Hkv, S, D, k.dtype)
 
 
+def kv_pack_centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout, kbar: torch.Tensor,
+                      vbar: torch.Tensor, counts: torch.Tensor, buffer: Optional[torch.Tensor] = None) -> PackedKV:
+    """Pack K/V into cluster tiles with the caller's centroids kbar, vbar (float32 [B, Hkv, C, D])
+    and counts (int32 [C], the n_c of each centroid column) (bsa_kv_pack_centroids)."""
+    _check_cuda(k, v, kbar, vbar, counts)
+    B, Hkv, S, D = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must match")
+    if kbar.shape != (B, Hkv, layout.C, D) or vbar.shape != kbar.shape or kbar.dtype != torch.float32 \
+            or vbar.dtype != torch.float32:
+        raise ValueError("kbar and vbar must be float32 [B, Hkv, C, D]")
+    if counts.shape != (layout.C,) or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [C]")
+    code = _dtype_code(k)
+    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C)
+    if buffer is None or buffer.numel() < nbytes:
+        buffer = _workspace(nbytes, k.device)
+    _lib.call("bsa_kv_pack_centroids", B, Hkv, S, D, code, _ptr(k), _ptr(v), _ptr(layout.perm),
+              _ptr(layout.offsets), layout.C, _ptr(kbar), _ptr(vbar), _ptr(counts), _ptr(buffer), buffer.numel(),
+              _stream())
+    return PackedKV(buffer, kbar, vbar, layout, B, Hkv, S, D, k.dtype)
+
+
 def antidiagonal_block_scores(q: torch.Tensor, k: torch.Tensor, layout: Optional[ClusterLayout] = None,
                               block_size: int = 128, stride: int = 16, score_scale: Optional[float] = None,
                               pool_gqa: bool = False, workspace: Optional[torch.Tensor] = None,
@@ -209,11 +232,21 @@ def mask_from_keep(keep: torch.Tensor) -> BlockMask:
 def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
                            compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
                            out: Optional[torch.Tensor] = None, out_f32: bool = False,
-                           workspace: Optional[torch.Tensor] = None):
+                           workspace: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                           c: Optional[torch.Tensor] = None):
     """Block-sparse attention over packed K/V; compensated by the skipped clusters'
     centroids, or hard drop with compensate=False (bsa_sparse_attention).  With out_f32 the
-    rows are returned in float32 (for a later correction, see correct)."""
-    _check_cuda(q, out)
+    rows are returned in float32 (for a later correction, see correct).  With A, c (from
+    probe_fit) every row o is written as o + o A + c, rounded once (the repair epilogue)."""
+    _check_cuda(q, out, A, c)
+    if (A is None) != (c is None):
+        raise ValueError("A and c go together")
+    if A is not None:
+        if out_f32:
+            raise ValueError("the repair epilogue writes the input type")
+        if A.shape != (q.shape[0], q.shape[1], q.shape[3], q.shape[3]) or c.shape != (q.shape[0], q.shape[1], q.shape[3]) \
+                or A.dtype != torch.float32 or c.dtype != torch.float32:
+            raise ValueError("A must be float32 [B, Hq, D, D] and c float32 [B, Hq, D]")
     B, Hq, S, D = q.shape
     if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
         raise ValueError("q does not match the packed K/V")
@@ -233,8 +266,8 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
     _lib.call("bsa_sparse_attention", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
               _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
               _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
-              int(bool(compensate)), _dtype_code(o), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
-              _stream())
+              int(bool(compensate)), _ptr(A), _ptr(c), _dtype_code(o), _ptr(o), _ptr(lse), _ptr(workspace),
+              workspace.numel(), _stream())
     return (o, lse) if return_lse else o
 
 
@@ -271,16 +304,17 @@ def attention_workspace(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, 
 def centroid_compensated_attention(q, k, v, q_layout: ClusterLayout, k_layout: ClusterLayout, mask: BlockMask,
                                    compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
                                    out: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
-                                   c: Optional[torch.Tensor] = None):
-    """kv_pack and block_sparse_attention for callers holding plain K/V; with A, c every output
-    row o becomes o + o A + c before it is rounded (attention in float32, then correct)."""
-    kv = kv_pack(k, v, k_layout)
-    if A is None:
-        return block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out)
-    res = block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out_f32=True)
-    o32, lse = res if return_lse else (res, None)
-    o = correct(o32, A, c, q.dtype, out)
-    return (o, lse) if return_lse else o
+                                   c: Optional[torch.Tensor] = None, kbar: Optional[torch.Tensor] = None,
+                                   vbar: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None):
+    """The pages' compensated attention for callers holding plain K/V ("Sparse-block
+    compensation", API table): packs K/V (with the caller's centroids kbar, vbar and counts
+    when given, else the clusters' means and sizes) and runs block_sparse_attention; with A, c
+    every output row o becomes o + o A + c before it is rounded (the repair epilogue)."""
+    if kbar is not None or vbar is not None or counts is not None:
+        kv = kv_pack_centroids(k, v, k_layout, kbar, vbar, counts)
+    else:
+        kv = kv_pack(k, v, k_layout)
+    return block_sparse_attention(q, kv, q_layout, mask, compensate, scale, return_lse, out, A=A, c=c)
 
 
 def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = None,
@@ -313,10 +347,13 @@ def probe_attention(q, k, v, probe_idx: torch.Tensor, scale: Optional[float] = N
 
 
 def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tensor, scale: Optional[float] = None,
-                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Exact dense probe rows, float32 [B, Hq, M, D], from the packed K/V tiles of kv_pack
-    (bfloat16 inputs; bsa_probe_attention_packed)."""
-    _check_cuda(q, probe_idx)
+                           workspace: Optional[torch.Tensor] = None, q_labels: Optional[torch.Tensor] = None,
+                           mask: Optional[BlockMask] = None, compensate: bool = True):
+    """Probe rows, float32 [B, Hq, M, D], from the packed K/V tiles of kv_pack (bfloat16 inputs;
+    bsa_probe_attention_packed): the exact dense rows, and with q_labels and a mask also the
+    same rows under the block-sparse rule (compensated or hard drop), from the same pass.
+    Returns the dense rows, or (dense, sparse) when a mask is given."""
+    _check_cuda(q, probe_idx, q_labels)
     B, Hq, S, D = q.shape
     if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
         raise ValueError("packed K/V do not match q")
@@ -324,14 +361,21 @@ def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tenso
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     od = torch.empty(B, Hq, M, D, dtype=torch.float32, device=q.device)
+    os_ = torch.empty_like(od) if mask is not None else None
     C = kv.layout.C
     nbytes = _lib.size_query("bsa_probe_attention_packed_workspace_size", B, Hq, kv.Hkv, S, D, M, C)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, q.device)
+    if mask is not None:
+        if q_labels is None or mask.keep.shape[0] != B or mask.keep.shape[3] != C:
+            raise ValueError("sparse probe rows need the query labels and a [B, Hm, Cq, Ck] mask")
+        sargs = (_ptr(q_labels), _ptr(mask.keep), mask.Hm, int(mask.keep.shape[2]), int(bool(compensate)))
+    else:
+        sargs = (None, None, 1, 1, 0)
     _lib.call("bsa_probe_attention_packed", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
-              _ptr(probe_idx), M, _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), C, _ptr(od),
-              _ptr(workspace), workspace.numel(), _stream())
-    return od
+              _ptr(probe_idx), M, _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), C, *sargs, _ptr(od),
+              _ptr(os_), _ptr(workspace), workspace.numel(), _stream())
+    return od if mask is None else (od, os_)
 
 
 def query_centroids(q: torch.Tensor, layout: ClusterLayout) -> torch.Tensor:

@@ -781,7 +781,122 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   }
 }
 
-template <typename T, int D, typename TO>
+// The correction o + o A + c applied in the attention's epilogue ("Partition the Support,
+// Reconstruct the Residual", Probe-Fitted Residual Reconstruction: the fitted map corrects
+// every row).  A is staged in LDS transposed, with each 16-feature group of a row in the
+// order 0-3, 8-11, 4-7, 12-15 -- the order in which the output accumulators hold a row's
+// features, so they feed the product as they are -- as bfloat16 high and low parts for
+// bfloat16 inputs (o A by three products, hi*hi + hi*lo + lo*hi: float32 accuracy) or float32
+// for float32 inputs; then c.  The image is built once per head by corr_image_kernel and
+// copied into LDS per row block.
+template <typename T, int D>
+struct CorrImage {
+  static constexpr bool kSplit = sizeof(T) == 2;
+  static constexpr int ROW = kSplit ? D + 8 : D + 4;  // elements per A^T row (16-byte aligned)
+  static constexpr int A_BYTES = (kSplit ? 2 : 1) * D * ROW * static_cast<int>(sizeof(T));
+  static constexpr int BYTES = A_BYTES + D * 4;  // + c
+  // Whole 1 KB blocks: one wave instruction copies 1 KB from global memory into LDS.
+  static constexpr int STRIDE = (BYTES + 1023) / 1024 * 1024;
+};
+__host__ __device__ constexpr int corr_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
+// Largest image of any instantiation (the workspace reserves it per (batch, query head)).
+constexpr size_t kCorrImageStride = CorrImage<bf16_t, 128>::STRIDE > CorrImage<float, 128>::STRIDE
+                                        ? CorrImage<bf16_t, 128>::STRIDE
+                                        : CorrImage<float, 128>::STRIDE;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void corr_image_kernel(const float* __restrict__ A, const float* __restrict__ cvec,
+                                                         unsigned char* __restrict__ img) {
+  using I = CorrImage<T, D>;
+  const size_t bh = blockIdx.x;
+  const float* Ah = A + bh * D * D;
+  unsigned char* out = img + bh * kCorrImageStride;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;  // A[i][j] -> row j (output feature), position corr_pos(i)
+    const float x = Ah[e];
+    if constexpr (I::kSplit) {
+      bf16_t* hi = reinterpret_cast<bf16_t*>(out);
+      bf16_t* lo = hi + D * I::ROW;
+      const __bf16 hb = static_cast<__bf16>(x);
+      hi[j * I::ROW + corr_pos(i)].bits = __builtin_bit_cast(uint16_t, hb);
+      lo[j * I::ROW + corr_pos(i)].bits = f32_to_bf16(x - static_cast<float>(hb));
+    } else {
+      reinterpret_cast<float*>(out)[j * I::ROW + corr_pos(i)] = x;
+    }
+  }
+  for (int d = threadIdx.x; d < D; d += 256)
+    reinterpret_cast<float*>(out + I::A_BYTES)[d] = cvec[bh * D + d];
+}
+
+// o (the accumulator layout of a wave's 32 rows) += o A + c, with the image in LDS at `img`.
+// The product accumulates straight into o: the operand fragments of o are taken first.
+template <typename T, int D>
+__device__ __forceinline__ void apply_correction(f32x16 (&o)[D / 32], const unsigned char* img) {
+  using I = CorrImage<T, D>;
+  constexpr int DT = D / 32, KK = D / 16;
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  // Contraction positions 16 kk + 8 h + e hold features 16 kk + 4 h + (e % 4) + 8 (e / 4):
+  // entries 8 (kk % 2) + e of accumulator kk / 2.
+  if constexpr (I::kSplit) {
+    const bf16_t* AtH = reinterpret_cast<const bf16_t*>(img);
+    const bf16_t* AtL = AtH + D * I::ROW;
+    Frag<bf16_t> oh[KK], ol[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = o[kk / 2][8 * (kk % 2) + e];
+        const __bf16 hb = static_cast<__bf16>(x);
+        oh[kk].v[e] = hb;
+        ol[kk].v[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+      }
+#pragma unroll
+    for (int jt = 0; jt < DT; ++jt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        Frag<bf16_t> ah, al;
+        load_frag(ah, AtH + (jt * 32 + r) * I::ROW + kk * 16 + 8 * h);
+        load_frag(al, AtL + (jt * 32 + r) * I::ROW + kk * 16 + 8 * h);
+        o[jt] = mma(ah, oh[kk], o[jt]);
+        o[jt] = mma(ah, ol[kk], o[jt]);
+        o[jt] = mma(al, oh[kk], o[jt]);
+      }
+  } else {
+    const float* At = reinterpret_cast<const float*>(img);
+    Frag<float> of[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) of[kk].v[e] = o[kk / 2][8 * (kk % 2) + e];
+#pragma unroll
+    for (int jt = 0; jt < DT; ++jt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        Frag<float> af;
+        load_frag(af, At + (jt * 32 + r) * I::ROW + kk * 16 + 8 * h);
+        o[jt] = mma(af, of[kk], o[jt]);
+      }
+  }
+  const float* cs = reinterpret_cast<const float*>(img + I::A_BYTES);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[dt][j] += cs[dt * 32 + 8 * (j / 4) + 4 * h + (j % 4)];
+}
+
+// Copy this head's correction image into LDS (1 KB per wave instruction, straight into LDS).
+template <typename T, int D>
+__device__ __forceinline__ void load_correction_image(const unsigned char* src, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NB = CorrImage<T, D>::STRIDE / 1024;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  for (int blk = wave; blk < NB; blk += kThreads / 64)
+    __builtin_amdgcn_global_load_lds(src + blk * 1024 + lane * 16, lds + blk * 1024, 16, 0, 0);
+#endif
+}
+
+template <typename T, int D, typename TO, bool CORR = false>
 struct AttnLds {
   using C = Cfg<T, D>;
   static constexpr int KB = SwzLds<T, D>::K_BYTES;  // one K tile
@@ -792,7 +907,8 @@ struct AttnLds {
   static constexpr int ZEPC = 16 / static_cast<int>(sizeof(TO));  // output elements per 16-byte chunk
   static constexpr int ZROW = D + ZEPC;                             // output staging row (elements)
   static constexpr int Z_BYTES = kRowsWG * ZROW * static_cast<int>(sizeof(TO));
-  static constexpr int MAIN = TILES > Z_BYTES ? TILES : Z_BYTES;
+  static constexpr int MAIN0 = TILES > Z_BYTES ? TILES : Z_BYTES;
+  static constexpr int MAIN = (CORR && CorrImage<T, D>::STRIDE > MAIN0) ? CorrImage<T, D>::STRIDE : MAIN0;
   static constexpr int BIAS = MAIN;                // float[2 buffers][kNK]
   static constexpr int UNIT = BIAS + 2 * kNK * 4;  // the workgroup's current work unit
   static constexpr int TOTAL = UNIT + 16;
@@ -809,16 +925,17 @@ constexpr int attn_occupancy() {
 // FAST: the kernel for heads whose V^T tiles are all float16 (bfloat16 inputs only); the
 // general kernel handles the others with a per-tile format switch.  Each takes its units
 // from its own queue, and keeping the two apart gives each its own register allocation.
-template <typename T, int D, bool COMP, typename TO, bool FAST>
+template <typename T, int D, bool COMP, typename TO, bool FAST, bool CORR>
 __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_attn_kernel(
     const T* __restrict__ Q, TO* __restrict__ O, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c2,
     const int32_t* __restrict__ q_perm, const int32_t* __restrict__ q_off, int Cq, const int32_t* __restrict__ k_off,
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
     int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const int32_t* __restrict__ hmix,
     const T* __restrict__ Kp, const void* __restrict__ Vtp, int tiles_per_head, int first_ctile,
-    const int32_t* __restrict__ order, int32_t* __restrict__ ctl) {
+    const float* __restrict__ clog2n, const int32_t* __restrict__ order, int32_t* __restrict__ ctl,
+    const unsigned char* __restrict__ corr_img) {
   using C = Cfg<T, D>;
-  using L = AttnLds<T, D, TO>;
+  using L = AttnLds<T, D, TO, CORR>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
   TO* Z = reinterpret_cast<TO*>(smem);
@@ -875,15 +992,13 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   const int q_lo = q_off[a], q_hi = q_off[a + 1];
 
-  // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise).
+  // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise;
+  // log2 n_c comes from the pack, -inf for a count of 0).
   auto write_bias = [&](float* dst, int ct) {
     if (threadIdx.x < kNK) {
       const int cc = ct * kNK + static_cast<int>(threadIdx.x);
       float bv = -INFINITY;
-      if (cc < Ck) {
-        const int n = k_off[cc + 1] - k_off[cc];
-        if (n > 0 && keep_row[cc] == 0) bv = __log2f(static_cast<float>(n));
-      }
+      if (cc < Ck && keep_row[cc] == 0) bv = clog2n[cc];
       dst[threadIdx.x] = bv;
     }
   };
@@ -970,6 +1085,15 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st.o[dt][j] *= inv;
+    if constexpr (CORR) {
+      // The tile buffers are free (the loop ended on a barrier): copy this head's image of A
+      // and c into them, then every row gets o + o A + c before its single rounding.
+      load_correction_image<T, D>(corr_img + bhq * kCorrImageStride, smem);
+      wait_vmem();
+      __syncthreads();
+      apply_correction<T, D>(st.o, smem);
+      __syncthreads();  // every wave is done with the image before the rows are staged over it
+    }
     // Stage the tile as rows in LDS, then store rows with 16-byte writes.
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -1148,35 +1272,76 @@ __global__ __launch_bounds__(kThreads, 2) void probe_partial_kernel(
   }
 }
 
-// Exact dense probe rows from the packed K/V tiles (bfloat16 inputs): the same rows as the dense
-// pass of probe_partial_kernel, with the keys taken in packed (cluster-major) order, which the
-// softmax does not depend on.  Workgroup (chunk, row tile, head): tiles [chunk * tpc, ...) of
-// the head's token tiles stream through two LDS buffers by global-to-LDS copies, as in the
-// attention kernel; a tile's key count comes from the cluster it belongs to (the last tile
-// of a cluster is ragged) and its V^T format from the pack's flags.  Partial rows, running
-// max and sum go to probe_merge_kernel.  Chunks past the head's last tile write empty partials.
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
+// One lane-uniform logit bias for a whole tile (log2 units): 0 where the lane's row takes the
+// tile, -inf where it does not.
+struct LaneBias {
+  float b;
+  __device__ bool active() const { return true; }
+  __device__ float operator()(int) const { return b; }
+};
+// Centroid columns of a tile for a lane's row: log2 n_c where the row's query cluster skipped
+// key cluster c (keep bits in LDS), -inf where it kept c or for a row without centroids.
+struct RowCentroids {
+  const uint32_t* bits;  // the row's keep bits (nullptr: no centroid columns)
+  const float* log2n;    // tile column -> log2 n_c (-inf for a count of 0 or a column past Ck)
+  int c0;
+  __device__ bool active() const { return true; }
+  __device__ float operator()(int key) const {
+    if (bits == nullptr) return -INFINITY;
+    const int c = c0 + key;
+    const float b = log2n[key];
+    if (b == -INFINITY) return -INFINITY;
+    return ((bits[c >> 5] >> (c & 31)) & 1u) ? -INFINITY : b;
+  }
+};
+
+// Probe rows from the packed K/V tiles of bsa_kv_pack (bfloat16).  Dense rows attend to
+// every key: the softmax over all keys does not depend on their order, so a workgroup streams
+// a run of `tpc` consecutive token tiles of one head through two LDS buffers with
+// global-to-LDS copies, exactly as the attention does, for up to 128 rows; a tile's key count
+// comes from its cluster (the last tile of a cluster is ragged) and its V^T format from the
+// pack's flags.  SPARSE: rows [M, 2M) repeat the M probes under the block-sparse rule of the
+// attention -- a token tile counts for a row only when the row's query cluster keeps the
+// tile's key cluster (keep bits in LDS) -- and one more chunk, index nchunks, holds the
+// centroid tiles, whose columns count for the sparse rows of the clusters that skipped them
+// (with compensation; the chunk is empty without).  Partial rows, running max and sum go to
+// probe_merge_kernel.  Chunks past the head's last tile write empty partials.
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
     const bf16_t* __restrict__ Q, int Hq, int Hkv, int Sq, float c2, const int32_t* __restrict__ probe_idx, int M,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C,
     const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
-    int tiles_per_head, int tpc, int nchunks, float* __restrict__ Opart, float* __restrict__ mpart,
-    float* __restrict__ lpart) {
+    int tiles_per_head, int tpc, int nchunks, const int32_t* __restrict__ q_labels, const uint8_t* __restrict__ keep,
+    int Hm, int Cq, const float* __restrict__ clog2n, int first_ctile, int ctiles, int comp, int words,
+    float* __restrict__ Opart, float* __restrict__ mpart, float* __restrict__ lpart) {
   using T = bf16_t;
   using L = AttnLds<T, D, float>;
   constexpr size_t kTileBytes = static_cast<size_t>(kNK) * D * sizeof(T);
   extern __shared__ __align__(16) unsigned char smem[];
-  int* nv = reinterpret_cast<int*>(smem + L::BIAS);  // key count of each tile of the chunk (tpc <= 2 kNK)
+  int* nv = reinterpret_cast<int*>(smem + L::BIAS);   // key count of each tile of the chunk (tpc <= 2 kNK)
+  int* clus = nv + 2 * kNK;                            // key cluster of each tile of the chunk
+  float* cbias = reinterpret_cast<float*>(clus + 2 * kNK);  // log2 n_c of a centroid tile's columns
+  uint32_t* bits = reinterpret_cast<uint32_t*>(cbias + kNK);  // [128 rows][words]: sparse rows' keep bits
   const int ci = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
   const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
   const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
   const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
-  const int ntiles = tile_off[C];
-  const int t0 = ci * tpc, t1 = min(ntiles, t0 + tpc);
+  const bool cen = SPARSE && ci == nchunks;  // the centroid chunk
+  const int nrows = SPARSE ? 2 * M : M;
+  const int nch = SPARSE ? nchunks + 1 : nchunks;
+  int t0, t1;
+  if (cen) {
+    t0 = first_ctile;
+    t1 = comp ? first_ctile + ctiles : first_ctile;
+  } else {
+    const int ntiles = tile_off[C];
+    t0 = ci * tpc;
+    t1 = min(ntiles, t0 + tpc);
+  }
   // Tile t belongs to cluster c with tile_off[c] <= t < tile_off[c + 1].
-  if (static_cast<int>(threadIdx.x) < t1 - t0) {
+  if (!cen && static_cast<int>(threadIdx.x) < t1 - t0) {
     const int t = t0 + static_cast<int>(threadIdx.x);
     int lo = 0, hi = C;  // invariant: tile_off[lo] <= t < tile_off[hi]
     while (hi - lo > 1) {
@@ -1185,10 +1350,40 @@ __global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
     }
     const int n = k_off[lo + 1] - k_off[lo];
     nv[threadIdx.x] = min(kNK, n - kNK * (t - tile_off[lo]));
+    clus[threadIdx.x] = lo;
+  }
+  if (cen && static_cast<int>(threadIdx.x) < t1 - t0) {
+    const int jt = static_cast<int>(threadIdx.x);
+    nv[jt] = min(kNK, C - kNK * jt);
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  const int my = qt * kRowsWG + wave * 32 + r;
-  const int qtok = probe_idx != nullptr ? probe_idx[my < M ? my : 0] : (my < M ? my : 0);
+  const int R = qt * kRowsWG + wave * 32 + r;  // this lane's row
+  const bool sparse_row = SPARSE && R >= M && R < nrows;
+  const int pj = SPARSE && R >= M ? R - M : R;  // its probe
+  const int qtok = probe_idx != nullptr ? probe_idx[pj < M ? pj : 0] : (pj < M ? pj : 0);
+  if constexpr (SPARSE) {
+    // Keep bits of the sparse rows' query clusters (a dense row, or a row past the probes,
+    // keeps every cluster: its bits are never read).
+    const int hm = Hm == 1 ? 0 : (Hm == Hq ? hq : kvh);
+    for (int e = threadIdx.x; e < kRowsWG * words; e += kThreads) {
+      const int row = e / words, w = e % words;
+      const int Rr = qt * kRowsWG + row;
+      uint32_t v = 0;
+      if (Rr >= M && Rr < nrows) {
+        const int tok = probe_idx != nullptr ? probe_idx[Rr - M] : Rr - M;
+        const int a = q_labels[tok];
+        if (a >= 0 && a < Cq) {
+          const uint8_t* kr = keep + ((static_cast<size_t>(b) * Hm + hm) * Cq + a) * C;
+          for (int i = 0; i < 32; ++i) {
+            const int c = w * 32 + i;
+            if (c < C && kr[c] != 0) v |= 1u << i;
+          }
+        }
+      }
+      bits[row * words + w] = v;
+    }
+  }
+  const uint32_t* mybits = bits + (wave * 32 + r) * words;
   Frag<T> qf[D / 16];
   load_q_frags<T, D>(qf, Q + static_cast<size_t>(bh) * Sq * D + static_cast<size_t>(qtok) * D);
   __builtin_amdgcn_s_waitcnt(0);
@@ -1206,17 +1401,34 @@ __global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
   __syncthreads();
   for (int t = t0; t < t1; ++t) {
     const int bj = (t - t0) & 1;
+    if (cen && threadIdx.x < kNK) {  // this centroid tile's log2 n_c (read before the barrier below)
+      const int c = (t - first_ctile) * kNK + static_cast<int>(threadIdx.x);
+      cbias[threadIdx.x] = c < C ? clog2n[c] : -INFINITY;
+    }
+    if (cen) __syncthreads();
     if (t + 1 < t1) {
       dma.issue_k(Kph + (t + 1) * kTileBytes, kbuf(bj ^ 1));
       dma.issue_v(Vph + (t + 1) * kTileBytes, vbuf(bj ^ 1));
     }
-    tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2, NoBias{}, nv[t - t0], flags_h[t] != 0);
+    const bool pv16 = flags_h[t] != 0;
+    if (cen) {
+      tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2,
+                                    RowCentroids{sparse_row ? mybits : nullptr, cbias, (t - first_ctile) * kNK},
+                                    nv[t - t0], pv16);
+    } else if (SPARSE) {
+      const int c = clus[t - t0];
+      const bool take = !sparse_row || ((mybits[c >> 5] >> (c & 31)) & 1u);
+      tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2, LaneBias{take ? 0.0f : -INFINITY}, nv[t - t0],
+                                    pv16);
+    } else {
+      tile_step<T, D, SwzLds<T, D>>(kbuf(bj), vbuf(bj), qf, st, c2, NoBias{}, nv[t - t0], pv16);
+    }
     wait_vmem();
     __syncthreads();
   }
   const float l_tot = st.l + swap_halves(st.l);
-  if (my < M) {
-    const size_t prow = (static_cast<size_t>(bh) * nchunks + ci) * M + my;
+  if (R < nrows) {
+    const size_t prow = (static_cast<size_t>(bh) * nch + ci) * nrows + R;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1232,11 +1444,14 @@ __global__ __launch_bounds__(kThreads, 2) void probe_dense_packed_kernel(
   }
 }
 
+// Rows m < split go to Od[bh][m], rows m >= split to Os[bh][m - split] (both with `split`
+// rows per head).
 template <int D>
 __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ Opart,
                                                         const float* __restrict__ mpart,
                                                         const float* __restrict__ lpart, int M, int nchunks,
-                                                        float* __restrict__ Od, float* __restrict__ lse2) {
+                                                        float* __restrict__ Od, float* __restrict__ lse2, int split,
+                                                        float* __restrict__ Os) {
   const int m = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
   float mx = -INFINITY;
   // Unrolled so that the loads of several chunks are in flight together.
@@ -1252,9 +1467,14 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
     l += lpart[prow] * w;
     o += Opart[prow * D + d] * w;
   }
-  Od[(static_cast<size_t>(bh) * M + m) * D + d] = l > 0.0f ? o / l : 0.0f;
+  const float val = l > 0.0f ? o / l : 0.0f;
+  if (m < split)
+    Od[(static_cast<size_t>(bh) * split + m) * D + d] = val;
+  else
+    Os[(static_cast<size_t>(bh) * split + (m - split)) * D + d] = val;
   // Log-sum-exp of the scaled logits in log2 units (running max plus log2 of the sum).
-  if (lse2 != nullptr && d == 0) lse2[static_cast<size_t>(bh) * M + m] = l > 0.0f ? mx + __log2f(l) : -INFINITY;
+  if (lse2 != nullptr && d == 0 && m < split)
+    lse2[static_cast<size_t>(bh) * split + m] = l > 0.0f ? mx + __log2f(l) : -INFINITY;
 }
 
 // ----------------------------------------------------------------- block compensation error
@@ -1432,6 +1652,7 @@ struct PackedKV {
   const uint8_t* flags;
   const void* k;
   const void* v;
+  const float* clog2n;
   int tiles_per_head, first_ctile, ctiles;
 };
 
@@ -1443,7 +1664,7 @@ inline int list_stride(int S, int Ck) {
 // Workspace of the attention: tile entries [rows][stride], counts [rows], the work order
 // [units] and the unit counter.
 struct AttnWs {
-  size_t entries, counts, order, rank, gsum, counter, total;
+  size_t entries, counts, order, rank, gsum, counter, aimg, total;
 };
 inline AttnWs attn_ws(int B, int Hq, int Hm, int Cq, int S, int Ck) {
   const size_t rows = static_cast<size_t>(B) * Hm * Cq;
@@ -1455,7 +1676,8 @@ inline AttnWs attn_ws(int B, int Hq, int Hm, int Cq, int S, int Ck) {
   w.rank = w.order + pack_align(units * sizeof(int32_t));
   w.gsum = w.rank + pack_align(units * sizeof(int32_t));  // one int per K/V group (<= B * Hq)
   w.counter = w.gsum + pack_align(static_cast<size_t>(B) * Hq * sizeof(int32_t));
-  w.total = w.counter + 256;
+  w.aimg = w.counter + 256;  // correction images, one per (batch, query head)
+  w.total = w.aimg + static_cast<size_t>(B) * Hq * kCorrImageStride;
   return w;
 }
 
@@ -1472,25 +1694,28 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <typename T, int D, bool COMP, typename TO, bool FAST>
+template <typename T, int D, bool COMP, typename TO, bool FAST, bool CORR>
 void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
                            float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
-                           const PackedKV& P, const int32_t* order, int32_t* ctl, int units) {
-  constexpr int LDS = AttnLds<T, D, TO>::TOTAL;
-  auto kern = sparse_attn_kernel<T, D, COMP, TO, FAST>;
+                           const PackedKV& P, const int32_t* order, int32_t* ctl, int units,
+                           const unsigned char* corr_img) {
+  constexpr int LDS = AttnLds<T, D, TO, CORR>::TOTAL;
+  auto kern = sparse_attn_kernel<T, D, COMP, TO, FAST, CORR>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   const int grid = min(units, device_cus() * attn_occupancy<T, FAST>());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
                      B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags, P.hmix,
-                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, order, ctl);
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, P.clog2n, order, ctl,
+                     corr_img);
 }
 
 template <typename T, int D>
 bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* q_perm,
                          const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const uint8_t* keep,
                          const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed, bool comp,
-                         bool out_f32, void* O, float* lse, void* ws, hipStream_t stream) {
+                         bool out_f32, const float* A, const float* cvec, void* O, float* lse, void* ws,
+                         hipStream_t stream) {
   const long long nunits = static_cast<long long>(B) * Hq * Cq;
   if (nunits > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
   const int units = static_cast<int>(nunits);
@@ -1499,7 +1724,8 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off),
                    reinterpret_cast<const int32_t*>(base + L.hmix), base + L.flags, base + L.k, base + L.v,
-                   L.tiles_per_head, L.first_centroid_tile, L.centroid_tiles};
+                   reinterpret_cast<const float*>(base + L.clog2n), L.tiles_per_head, L.first_centroid_tile,
+                   L.centroid_tiles};
   const size_t rows = static_cast<size_t>(B) * Hm * Cq;
   const int maxe = list_stride(S, Ck);
   const AttnWs W = attn_ws(B, Hq, Hm, Cq, S, Ck);
@@ -1510,6 +1736,11 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   int32_t* rank = reinterpret_cast<int32_t*>(wsb + W.rank);
   int32_t* gsum = reinterpret_cast<int32_t*>(wsb + W.gsum);
   int32_t* counter = reinterpret_cast<int32_t*>(wsb + W.counter);
+  unsigned char* aimg = wsb + W.aimg;
+  const bool corr = A != nullptr;
+  if (corr)
+    hipLaunchKernelGGL((corr_image_kernel<T, D>), dim3(static_cast<unsigned>(B * Hq)), dim3(256), 0, stream, A, cvec,
+                       aimg);
   hipLaunchKernelGGL(tile_list_wave_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream,
                      kv_count, kv_idx, static_cast<int>(rows), Ck, k_off, P.tile_off, P.first_ctile, P.ctiles,
                      comp ? 1 : 0, maxe, entries, counts);
@@ -1521,18 +1752,20 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, gsum, rank, B, Hq, Hkv, Cq, P.hmix,
                      kHalf ? 1 : 0, order, counter);
   // The general kernel first (usually without work), then the float16 one.
-#define BSA_LAUNCH(COMP, TO)                                                                                          \
+#define BSA_LAUNCH(COMP, TO, CORR)                                                                                    \
   do {                                                                                                                 \
-    launch_sparse_variant<T, D, COMP, TO, false>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck,  \
-                                                 keep, entries, counts, maxe, Hm, P, order, counter, units);          \
+    launch_sparse_variant<T, D, COMP, TO, false, CORR>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq,       \
+                                                       k_off, Ck, keep, entries, counts, maxe, Hm, P, order, counter, \
+                                                       units, aimg);                                                  \
     if (kHalf)                                                                                                         \
-      launch_sparse_variant<T, D, COMP, TO, kHalf>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off,   \
-                                                   Ck, keep, entries, counts, maxe, Hm, P, order, counter, units);    \
+      launch_sparse_variant<T, D, COMP, TO, kHalf, CORR>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq,     \
+                                                         k_off, Ck, keep, entries, counts, maxe, Hm, P, order,        \
+                                                         counter, units, aimg);                                       \
   } while (0)
   if (comp) {
-    if (out_f32) BSA_LAUNCH(true, float); else BSA_LAUNCH(true, T);
+    if (corr) BSA_LAUNCH(true, T, true); else if (out_f32) BSA_LAUNCH(true, float, false); else BSA_LAUNCH(true, T, false);
   } else {
-    if (out_f32) BSA_LAUNCH(false, float); else BSA_LAUNCH(false, T);
+    if (corr) BSA_LAUNCH(false, T, true); else if (out_f32) BSA_LAUNCH(false, float, false); else BSA_LAUNCH(false, T, false);
   }
 #undef BSA_LAUNCH
   return launch_status();
@@ -1558,7 +1791,7 @@ void launch_probe_pass(int B, int Hq, int Hkv, int S, const void* Q, const void*
                      probe_idx, M, kProbeChunk, ntok, nchunks, q_labels, k_labels, keep, Hm, Cq, Ck, k_off, Kbar,
                      Vbar, Opart, mpart, lpart);
   hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks,
-                     out, nullptr);
+                     out, nullptr, M, nullptr);
 }
 
 size_t probe_ws_floats(int B, int Hq, int S, int D, int M) {
@@ -1576,29 +1809,52 @@ inline int packed_probe_chunks(int first_ctile) {
   return (first_ctile + tpc - 1) / tpc;
 }
 
+// Partial rows of the packed probe pass: per (batch x query head) up to nchunks + 1 chunks of
+// 2 M rows (dense and sparse), D + 2 floats each.
+inline size_t packed_probe_ws_bytes(int B, int Hq, int D, int M, int first_ctile) {
+  return static_cast<size_t>(B) * Hq * (packed_probe_chunks(first_ctile) + 1) * 2 * M * (D + 2) * sizeof(float);
+}
+
 // Q holds Sq rows per head; probe_idx == nullptr takes rows 0 .. M-1; lse2 (log2 units) is
-// optional.
+// optional.  Os != nullptr: also the sparse rows (q_labels, keep with Hm mask heads of Cq rows,
+// compensate), from the same pass.
 template <int D>
 bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void* Q, float scale,
                                const int32_t* probe_idx, int M, const void* packed, const int32_t* k_off, int C,
-                               float* Od, float* lse2, void* ws, hipStream_t stream) {
+                               float* Od, float* lse2, void* ws, hipStream_t stream,
+                               const int32_t* q_labels = nullptr, const uint8_t* keep = nullptr, int Hm = 1,
+                               int Cq = 1, bool comp = false, float* Os = nullptr) {
   const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const int tpc = packed_probe_tpc(PL.first_centroid_tile);
   const int nchunks = packed_probe_chunks(PL.first_centroid_tile);
-  const int qtiles = (M + kRowsWG - 1) / kRowsWG;
+  const bool sparse = Os != nullptr;
+  const int nrows = sparse ? 2 * M : M;
+  const int nch = sparse ? nchunks + 1 : nchunks;
+  const int qtiles = (nrows + kRowsWG - 1) / kRowsWG;
+  const int words = sparse ? (C + 31) / 32 : 0;
   float* Opart = static_cast<float*>(ws);
-  float* mpart = Opart + static_cast<size_t>(B) * Hq * nchunks * M * D;
-  float* lpart = mpart + static_cast<size_t>(B) * Hq * nchunks * M;
-  constexpr int LDS = AttnLds<bf16_t, D, float>::TOTAL;
-  auto kern = probe_dense_packed_kernel<D>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  hipLaunchKernelGGL(kern, dim3(nchunks, qtiles, B * Hq), dim3(kThreads), LDS, stream, static_cast<const bf16_t*>(Q),
-                     Hq, Hkv, Sq, scale * kLog2e, probe_idx, M, reinterpret_cast<const int32_t*>(base + PL.tile_off),
-                     k_off, C, base + PL.flags, reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v,
-                     PL.tiles_per_head, tpc, nchunks, Opart, mpart, lpart);
-  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(M, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, M, nchunks, Od,
-                     lse2);
+  float* mpart = Opart + static_cast<size_t>(B) * Hq * nch * nrows * D;
+  float* lpart = mpart + static_cast<size_t>(B) * Hq * nch * nrows;
+  const int LDS = AttnLds<bf16_t, D, float>::BIAS + (4 * kNK + kNK) * 4 + kRowsWG * words * 4;
+#define BSA_PROBE_ARGS                                                                                                \
+  static_cast<const bf16_t*>(Q), Hq, Hkv, Sq, scale * kLog2e, probe_idx, M,                                         \
+      reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, C, base + PL.flags,                              \
+      reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v, PL.tiles_per_head, tpc, nchunks, q_labels, keep, Hm, \
+      Cq, reinterpret_cast<const float*>(base + PL.clog2n), PL.first_centroid_tile, PL.centroid_tiles, comp ? 1 : 0, \
+      words, Opart, mpart, lpart
+  if (sparse) {
+    auto kern = probe_packed_kernel<D, true>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    hipLaunchKernelGGL(kern, dim3(nch, qtiles, B * Hq), dim3(kThreads), LDS, stream, BSA_PROBE_ARGS);
+  } else {
+    auto kern = probe_packed_kernel<D, false>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    hipLaunchKernelGGL(kern, dim3(nch, qtiles, B * Hq), dim3(kThreads), LDS, stream, BSA_PROBE_ARGS);
+  }
+#undef BSA_PROBE_ARGS
+  hipLaunchKernelGGL((probe_merge_kernel<D>), dim3(nrows, B * Hq), dim3(D), 0, stream, Opart, mpart, lpart, nrows,
+                     nch, Od, lse2, M, Os);
   return launch_status();
 }
 
@@ -1679,10 +1935,14 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
                                            float scale, const int32_t* q_perm, const int32_t* q_offsets, int Cq,
                                            const int32_t* k_offsets, int Ck, const uint8_t* keep,
                                            const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                           const void* packed, size_t packed_bytes, int compensate, int out_dtype,
-                                           void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                           const void* packed, size_t packed_bytes, int compensate,
+                                           const float* A, const float* c, int out_dtype, void* O, float* lse,
+                                           void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return BSA_E_DTYPE;
   if (out_dtype != dtype && out_dtype != BSA_F32) return BSA_E_DTYPE;
+  if ((A == nullptr) != (c == nullptr)) return BSA_E_ARG;
+  if (A != nullptr && out_dtype != dtype) return BSA_E_UNSUPPORTED;  // the epilogue writes the input type
+  if (A != nullptr && static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Cq < 1 || Ck < 1) return BSA_E_ARG;
   if (!Q || !O || !q_perm || !q_offsets || !k_offsets || !keep || !kv_count || !kv_idx || !packed) return BSA_E_ARG;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
@@ -1696,7 +1956,7 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   const bool out_f32 = out_dtype == BSA_F32 && dtype != BSA_F32;
 #define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
-                 compensate != 0, out_f32, O, lse, ws, stream
+                 compensate != 0, out_f32, A, c, O, lse, ws, stream
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS
@@ -1715,30 +1975,38 @@ extern "C" bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, i
   if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || S < 1 || M < 1 || C < 1) return BSA_E_ARG;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
-  *bytes = static_cast<size_t>(B) * Hq * packed_probe_chunks(PL.first_centroid_tile) * M * (D + 2) * sizeof(float);
+  *bytes = packed_probe_ws_bytes(B, Hq, D, M, PL.first_centroid_tile);
   return BSA_OK;
 }
 
 extern "C" bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
                                                  float scale, const int32_t* probe_idx, int M, const void* packed,
                                                  size_t packed_bytes, const int32_t* k_offsets, int C,
-                                                 float* O_dense_probe, void* ws, size_t ws_bytes,
-                                                 hipStream_t stream) {
+                                                 const int32_t* q_labels, const uint8_t* keep, int Hm, int Cq,
+                                                 int compensate, float* O_dense_probe, float* O_sparse_probe,
+                                                 void* ws, size_t ws_bytes, hipStream_t stream) {
   if (dtype != BSA_BF16) return valid_dtype(dtype) ? BSA_E_UNSUPPORTED : BSA_E_DTYPE;
   size_t need = 0;
   const bsa_status st = bsa_probe_attention_packed_workspace_size(B, Hq, Hkv, S, D, M, C, &need);
   if (st != BSA_OK) return st;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (!Q || !probe_idx || !packed || !k_offsets || !O_dense_probe) return BSA_E_ARG;
+  if (O_sparse_probe != nullptr) {
+    if (!q_labels || !keep || Cq < 1) return BSA_E_ARG;
+    if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
+    if (C > 1024) return BSA_E_UNSUPPORTED;  // keep bits of 128 rows in LDS
+  }
   if (M > 1024) return BSA_E_UNSUPPORTED;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
   if (packed_bytes < pack_layout(B, Hkv, S, D, C, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
   return D == 128 ? launch_probe_packed<128>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
-                                             O_dense_probe, nullptr, ws, stream)
+                                             O_dense_probe, nullptr, ws, stream, q_labels, keep, Hm, Cq,
+                                             compensate != 0, O_sparse_probe)
                   : launch_probe_packed<64>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
-                                            O_dense_probe, nullptr, ws, stream);
+                                            O_dense_probe, nullptr, ws, stream, q_labels, keep, Hm, Cq,
+                                            compensate != 0, O_sparse_probe);
 }
 
 extern "C" bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,

@@ -18,7 +18,9 @@
 //                            the tile's largest; else bfloat16.  float32 inputs: float32)
 // and the per-tile format flag.  The same pass sums each cluster's keys and values for the
 // centroids, which are packed afterwards as extra tiles (K-bar rounded to the input type,
-// V-bar like V).
+// V-bar like V), with log2 n_c for each centroid column.  A caller holding its own centroids
+// and counts (the page API takes them as inputs) packs the token tiles alone and has its
+// centroids and counts packed instead.
 #include "pack.hpp"
 
 #include <type_traits>
@@ -29,12 +31,18 @@ namespace {
 constexpr int kPackThreads = 256;
 
 // tile_off[c] = first tile of cluster c (exclusive prefix of ceil(n_c / 64)); clears the
-// per-head format summary hmix[nh].  One workgroup.
+// per-head format summary hmix[nh]; clog2n[c] = log2 of the centroid count (the caller's
+// counts when given, else the cluster size), -inf for 0.  One workgroup.
 __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __restrict__ offsets, int C,
+                                                             const int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ tile_off, int32_t* __restrict__ hmix,
-                                                             int nh) {
+                                                             int nh, float* __restrict__ clog2n) {
   __shared__ int32_t part[1024];
   for (int i = threadIdx.x; i < nh; i += blockDim.x) hmix[i] = 0;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    const int n = counts != nullptr ? counts[c] : offsets[c + 1] - offsets[c];
+    clog2n[c] = n > 0 ? __log2f(static_cast<float>(n)) : -INFINITY;
+  }
   const int per = (C + blockDim.x - 1) / blockDim.x;
   const int c0 = threadIdx.x * per;
   int32_t run = 0;
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     const int32_t* __restrict__ offsets, int C, const int32_t* __restrict__ tile_off, int tiles_per_head,
     T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
     int32_t* __restrict__ hmix, float* __restrict__ Kbar, float* __restrict__ Vbar) {
+  // Kbar == nullptr: the caller gives the centroids; only the token tiles are written.
   using M = PackSmem<T, D>;
   using VS = typename M::VS;
   constexpr int EPC = M::EPC;                             // elements per 16-byte chunk
@@ -173,6 +182,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
       }
     }
   }
+  if (Kbar == nullptr) return;  // (uniform over the workgroup)
   __syncthreads();  // the last tile's V^T reads are done before red reuses the memory
   // Centroid means: reduce the per-thread column sums over the key groups.
 #pragma unroll
@@ -240,9 +250,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
   }
 }
 
+// given == true: Kbar, Vbar and counts are the caller's (read only).
 template <typename T, int D>
 bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, const int32_t* perm,
-                       const int32_t* offsets, int C, float* Kbar, float* Vbar, void* packed, hipStream_t stream) {
+                       const int32_t* offsets, int C, const float* Kbar, const float* Vbar, const int32_t* counts,
+                       bool given, void* packed, hipStream_t stream) {
   const PackLayout L = pack_layout(B, Hkv, S, D, C, sizeof(T));
   unsigned char* base = static_cast<unsigned char*>(packed);
   int32_t* tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
@@ -251,10 +263,13 @@ bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, cons
   T* Kp = reinterpret_cast<T*>(base + L.k);
   uint16_t* V16 = reinterpret_cast<uint16_t*>(base + L.v);
   float* V32 = reinterpret_cast<float*>(base + L.v);
-  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, tile_off, hmix, B * Hkv);
+  float* clog2n = reinterpret_cast<float*>(base + L.clog2n);
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, given ? counts : nullptr,
+                     tile_off, hmix, B * Hkv, clog2n);
   hipLaunchKernelGGL((pack_cluster_kernel<T, D>), dim3(C, B * Hkv), dim3(kPackThreads), 0, stream,
                      static_cast<const T*>(K), static_cast<const T*>(V), S, perm, offsets, C, tile_off, L.tiles_per_head,
-                     Kp, V16, V32, flags, hmix, Kbar, Vbar);
+                     Kp, V16, V32, flags, hmix, given ? nullptr : const_cast<float*>(Kbar),
+                     given ? nullptr : const_cast<float*>(Vbar));
   hipLaunchKernelGGL((pack_centroid_kernel<T, D>), dim3(L.centroid_tiles, B * Hkv), dim3(kPackThreads), 0, stream,
                      Kbar, Vbar, C, L.tiles_per_head, L.first_centroid_tile, Kp, V16, V32, flags, hmix);
   return launch_status();
@@ -283,9 +298,26 @@ extern "C" bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const
   if (!K || !V || !perm || !offsets || !Kbar || !Vbar) return BSA_E_ARG;
   if (!packed || packed_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hkv > 65535) return BSA_E_UNSUPPORTED;
+#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, nullptr, false, packed, stream
   if (dtype == BSA_BF16)
-    return D == 128 ? launch_pack<bf16_t, 128>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream)
-                    : launch_pack<bf16_t, 64>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream);
-  return D == 128 ? launch_pack<float, 128>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream)
-                  : launch_pack<float, 64>(B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, packed, stream);
+    return D == 128 ? launch_pack<bf16_t, 128>(BSA_PACK_ARGS) : launch_pack<bf16_t, 64>(BSA_PACK_ARGS);
+  return D == 128 ? launch_pack<float, 128>(BSA_PACK_ARGS) : launch_pack<float, 64>(BSA_PACK_ARGS);
+#undef BSA_PACK_ARGS
+}
+
+extern "C" bsa_status bsa_kv_pack_centroids(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
+                                            const int32_t* perm, const int32_t* offsets, int C, const float* Kbar,
+                                            const float* Vbar, const int32_t* counts, void* packed,
+                                            size_t packed_bytes, hipStream_t stream) {
+  size_t need = 0;
+  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, &need);
+  if (st != BSA_OK) return st;
+  if (!K || !V || !perm || !offsets || !Kbar || !Vbar || !counts) return BSA_E_ARG;
+  if (!packed || packed_bytes < need) return BSA_E_WORKSPACE;
+  if (static_cast<long long>(B) * Hkv > 65535) return BSA_E_UNSUPPORTED;
+#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, counts, true, packed, stream
+  if (dtype == BSA_BF16)
+    return D == 128 ? launch_pack<bf16_t, 128>(BSA_PACK_ARGS) : launch_pack<bf16_t, 64>(BSA_PACK_ARGS);
+  return D == 128 ? launch_pack<float, 128>(BSA_PACK_ARGS) : launch_pack<float, 64>(BSA_PACK_ARGS);
+#undef BSA_PACK_ARGS
 }

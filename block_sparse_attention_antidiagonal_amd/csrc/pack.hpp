@@ -16,10 +16,12 @@ constexpr int kPackTile = 64;  // keys per packed tile
 //   v         [B*Hkv][tiles][D][64]    16-bit for bfloat16 inputs, float32 for float32 inputs;
 //                                      within each group of 16 keys the positions hold keys
 //                                      0-3, 8-11, 4-7, 12-15
+//   clog2n    float [C]                log2 of the count n_c that weighs centroid column c
+//                                      (-inf for n_c = 0: the column vanishes)
 // Per head, token tiles come first (sum over clusters of ceil(n_c / 64) <= ceil(S/64) + C of
 // them), then ceil(C / 64) centroid tiles starting at first_centroid_tile.
 struct PackLayout {
-  size_t tile_off, hmix, flags, k, v, total;
+  size_t tile_off, hmix, flags, k, v, clog2n, total;
   int tiles_per_head, first_centroid_tile, centroid_tiles;
 };
 
@@ -43,6 +45,8 @@ inline PackLayout pack_layout(int B, int Hkv, int S, int D, int C, size_t elem) 
   off = pack_align(off + nt * kPackTile * D * elem);
   L.v = off;
   off = pack_align(off + nt * kPackTile * D * elem);
+  L.clog2n = off;
+  off = pack_align(off + static_cast<size_t>(C) * 4);
   L.total = off;
   return L;
 }

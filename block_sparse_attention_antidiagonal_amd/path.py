@@ -1,16 +1,19 @@
-"""The whole path as one call: layout -> centroids -> scores -> top-p -> sparse attention
--> probe rows -> fit -> correction.
+"""The whole path as one call: layout -> centroids -> scores -> top-p -> (probe rows ->
+fit) -> sparse attention with the correction in its epilogue.
 
 Order of stages: "Dynamic block masks and head-wise mask reuse", section "Recipe" (scores,
 top-p mask, labels, compensated attention) and "Sparse-block compensation", section
 "Recipe: STA with both repairs" (compensated attention, probe selection, dense probe rows,
-residual correction).  Every stage is one or two kernel launches on the current stream;
-nothing is computed on the host except the probe selection, which depends only on the
-labels and is done once.
+residual correction).  The probes' block-sparse rows are computed by the probe pass itself
+(the same rule as the attention, "Partition the Support, Reconstruct the Residual": a few
+exact probe rows against their sparse counterparts), so the fit is known before the
+attention runs and every row is corrected before its single rounding.  Every stage is one
+or a few kernel launches on the current stream; nothing is computed on the host except the
+probe selection, which depends only on the labels and is done once.
 
-Streams: the K/V packing and the dense probe rows depend only on the inputs and the layout,
-so they run on a second stream (default priority) while the scores and the top-p masks run
-on the caller's stream; the attention waits for both.
+Streams: the K/V packing depends only on the inputs and the layout, so it runs on a second
+stream (default priority) while the scores and the top-p masks run on the caller's stream;
+the probe rows and the attention wait for both.
 """
 
 from __future__ import annotations
@@ -46,7 +49,7 @@ class PathConfig:
     probes: int = 0
     lam: float = 0.1
     rank: int = 16
-    overlap: bool = True  # pack and probe rows on a second stream, beside scores and top-p
+    overlap: bool = True  # the pack on a second stream, beside scores and top-p
     route_density: float = 0.2  # routed mode: keys each row computes exactly, as a fraction of S
 
     @classmethod
@@ -65,7 +68,7 @@ class PathResult:
     scores: Optional[torch.Tensor] = None
     kbar: Optional[torch.Tensor] = None
     vbar: Optional[torch.Tensor] = None
-    out_sparse: Optional[torch.Tensor] = None  # float32 rows before the correction (only if requested)
+    out_sparse: Optional[torch.Tensor] = None  # rows before the correction (only if requested)
     o_dense_probe: Optional[torch.Tensor] = None
     o_sparse_probe: Optional[torch.Tensor] = None
     A: Optional[torch.Tensor] = None
@@ -81,7 +84,6 @@ class SparseAttentionPath:
         self.device = torch.device(device)
         self._pack_buffer = None  # reused across calls
         self._attn_ws = None
-        self._o32 = None  # float32 attention rows before the correction
         self._side = None  # second stream for the mask-independent stages
         self._scores = None  # score rows kept across calls when a mask cache is used
         self._probe_ws = None  # dense probe partials (bfloat16 inputs)
@@ -117,9 +119,9 @@ class SparseAttentionPath:
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_sparse: bool = False,
                  mark: Optional[Callable[[str], None]] = None,
                  cache: Optional[api.HeadMaskCache] = None) -> PathResult:
-        """Run the path.  With probes the attention keeps its rows in float32, the fit reads
-        the probe rows from them, and the correction pass writes every corrected row, rounded
-        once; keep_sparse also returns the float32 rows before the correction.
+        """Run the path.  With probes, the probe rows (dense and block-sparse) and the fit come
+        before the attention, whose epilogue writes every corrected row, rounded once;
+        keep_sparse also returns the rows without the correction (one more attention call).
         ``mark(stage)`` is called after each stage's launches, with the stage's stream current
         (for stream-ordered timing events; a stage spans from the previous mark on its
         stream).  ``cache`` (scored masks only): head-wise mask reuse across calls -- only the
@@ -142,21 +144,10 @@ class SparseAttentionPath:
             # One pass over K/V: cluster tiles for the attention kernel and the centroids.
             kv = api.kv_pack(k, v, layout, self._pack_buffer)
             mark("pack")
-            od = None
-            if cfg.probes:  # exact dense probe rows: independent of the mask
-                if q.dtype == torch.bfloat16:  # from the packed tiles just written
-                    if self._probe_ws is None:
-                        n = _lib.size_query("bsa_probe_attention_packed_workspace_size", cfg.B, cfg.Hq, cfg.Hkv,
-                                            cfg.S, cfg.D, cfg.probes, cfg.C)
-                        self._probe_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
-                    od = api.probe_attention_packed(q, kv, self.probe_idx, cfg.scale, workspace=self._probe_ws)
-                else:
-                    od, _ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale)
-                mark("probe_rows")
         if side is not main:
             # Tensors made on the side stream and read on the caller's stream, and the
             # reverse, stay allocated until both streams are past them.
-            for t in (kv.buffer, kv.kbar, kv.vbar, od):
+            for t in (kv.buffer, kv.kbar, kv.vbar):
                 if t is not None:
                     t.record_stream(main)
             for t in (layout.perm, layout.offsets, layout.counts, q, k, v):
@@ -215,17 +206,27 @@ class SparseAttentionPath:
                                                  workspace=self._attn_ws)
             mark("attention")
             return res
-        if self._o32 is None or self._o32.shape != q.shape:
-            self._o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        o32 = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, out=self._o32, out_f32=True,
-                                         workspace=self._attn_ws)
-        mark("attention")
-        os_ = api.gather_rows(o32, self.probe_idx)
+        # Fit before attending: the probes' dense and block-sparse rows (one pass over the packed
+        # tiles, float32), the ridge fit, then the attention applies o + o A + c to every row
+        # in its epilogue and rounds each row once.
+        if q.dtype == torch.bfloat16:
+            if self._probe_ws is None:
+                n = _lib.size_query("bsa_probe_attention_packed_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S,
+                                    cfg.D, cfg.probes, cfg.C)
+                self._probe_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+            od, os_ = api.probe_attention_packed(q, kv, self.probe_idx, cfg.scale, workspace=self._probe_ws,
+                                                 q_labels=self.labels, mask=mask, compensate=cfg.compensate)
+        else:
+            od, os_ = api.probe_attention(q, k, v, self.probe_idx, cfg.scale, q_labels=self.labels,
+                                          k_labels=self.labels, k_layout=layout, mask=mask, kbar=kbar, vbar=vbar)
+        mark("probe_rows")
         A, c = api.probe_fit(os_, od, self.probe_w, cfg.lam, cfg.rank)
         mark("fit")
-        res.out = api.correct(o32, A, c, q.dtype)
-        mark("correct")
+        res.out = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale, workspace=self._attn_ws,
+                                             A=A, c=c)
+        mark("attention")
         res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
-        if keep_sparse:
-            res.out_sparse = o32.clone()
+        if keep_sparse:  # the uncorrected rows too (an extra attention call, for inspection)
+            res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale,
+                                                        workspace=self._attn_ws)
         return res

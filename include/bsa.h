@@ -118,6 +118,17 @@ bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, i
 bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, int C, float* Kbar, float* Vbar, void* packed, size_t packed_bytes,
                        hipStream_t stream);
+/* The same packing with caller-given centroids and counts ([SBC] API table: the compensated
+ * attention takes the keys, values and clusters from the caller; "SVG-EAR -- centroid
+ * compensation": column c carries log n_c and v_bar_c).  Only the token tiles are packed from
+ * K and V; the centroid tiles come from Kbar/Vbar (read only), and centroid column c is
+ * weighted by log(counts[c]) (a count of 0 removes the column).
+ *   Kbar, Vbar float [B, Hkv, C, D]; counts int32 [C] (>= 0, shared by all heads)
+ * Other arguments, requirements and errors as bsa_kv_pack. */
+bsa_status bsa_kv_pack_centroids(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
+                                 const int32_t* perm, const int32_t* offsets, int C, const float* Kbar,
+                                 const float* Vbar, const int32_t* counts, void* packed, size_t packed_bytes,
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Antidiagonal block scores.  [HMR] "XAttention -- anti-diagonal block scoring": over the
@@ -173,9 +184,15 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  * extra column per skipped non-empty key cluster c with logit q_i . kbar_c * scale + log n_c
  * and value vbar_c, all inside one softmax.  With compensate == 0 skipped blocks are dropped
  * (hard drop; the softmax renormalizes over kept keys).  A row with no column at all gets
- * O = 0 and lse = -inf.  Keys, values and centroids are read from the buffer bsa_kv_pack
- * wrote.  out_dtype is dtype, or BSA_F32 to keep the rows in float32 for a later
- * correction (bsa_correct).
+ * O = 0 and lse = -inf.  Keys, values, centroids and the centroid counts are read from the
+ * buffer bsa_kv_pack (or bsa_kv_pack_centroids) wrote.  out_dtype is dtype, or BSA_F32 to keep
+ * the rows in float32 for a later correction (bsa_correct).
+ * Repair epilogue ([SPR] Probe-Fitted Residual Reconstruction: the fitted correction applies
+ * to every row): with A and c given, every row o becomes o + o A + c before it is rounded
+ * once to out_dtype (o A with float32 accuracy: bfloat16 high and low parts of both operands
+ * for bfloat16 inputs).  A float [B, Hq, D, D] (row-major, correction_j = sum_i o_i A[i][j]),
+ * c float [B, Hq, D], both from bsa_probe_fit; NULL, NULL for no epilogue (one of them NULL:
+ * BSA_E_ARG).  With A given out_dtype must equal dtype (else BSA_E_UNSUPPORTED).
  *   Q [B, Hq, S, D] dtype, O [B, Hq, S, D] out_dtype out
  *   q_perm/q_offsets (Cq clusters): query cluster layout; k_offsets [Ck+1]: the key layout
  *     the buffer was packed with
@@ -184,15 +201,17 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
  *   ws: workspace of bsa_sparse_attention_workspace_size bytes (each mask row's tile list, each
  *       K/V group's total work and the rank of each (batch, head, query cluster) unit in its
- *       group, and the order in which workgroups take the units, longest first)
+ *       group, the order in which workgroups take the units, longest first, and the staged
+ *       correction of each (batch, query head))
  * Needs Ck <= 32767.  BSA_E_WORKSPACE if the packed buffer or the workspace is too small.
  */
 bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, int S, int Ck, size_t* bytes_host);
 bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                 const int32_t* q_perm, const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
                                 int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                const void* packed, size_t packed_bytes, int compensate, int out_dtype, void* O,
-                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                                const void* packed, size_t packed_bytes, int compensate, const float* A,
+                                const float* c, int out_dtype, void* O, float* lse, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)
@@ -215,21 +234,28 @@ bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, 
                                const int32_t* k_offsets, const float* Kbar, const float* Vbar, float* O_dense_probe,
                                float* O_sparse_probe, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The dense probe rows of bsa_probe_attention from the packed K/V buffer of bsa_kv_pack
- * (bfloat16 inputs): the same rows, with the keys visited in the packed cluster-major order
- * (the softmax over all keys does not depend on it), streamed by tile copies as in the
- * attention.  packed, packed_bytes: the bsa_kv_pack buffer made from the same K, V and key
- * layout; k_offsets int32 [C+1] and C: that layout's cluster offsets and count.
- *   O_dense_probe float [B, Hq, M, D] out
+/* The probe rows of bsa_probe_attention from the packed K/V buffer of bsa_kv_pack (bfloat16
+ * inputs), in one pass over the packed tiles: the dense rows with the keys visited in the
+ * packed cluster-major order (the softmax over all keys does not depend on it), and, when
+ * O_sparse_probe is given, the same probes under the block-sparse rule of
+ * bsa_sparse_attention (the kept key clusters of each probe's query cluster, plus, with
+ * compensate != 0, the centroid columns of its skipped clusters, weighted by the pack's
+ * counts), both in float32 -- the inputs of bsa_probe_fit, available before the attention runs.
+ * packed, packed_bytes: the bsa_kv_pack buffer made from the same K, V and key layout;
+ * k_offsets int32 [C+1] and C: that layout's cluster offsets and count (C = Ck).
+ *   q_labels int32 [S]: query cluster labels; keep uint8 [B, Hm, Cq, C]: the block mask
+ *     (Hm in {1, Hkv, Hq}); both ignored when O_sparse_probe is NULL
+ *   O_dense_probe, O_sparse_probe float [B, Hq, M, D] out (O_sparse_probe may be NULL)
  * Needs dtype BSA_BF16 (BSA_E_UNSUPPORTED for float32: use bsa_probe_attention), 1 <= M <= 1024,
- * and workspace of bsa_probe_attention_packed_workspace_size bytes.
+ * C <= 1024 for sparse rows, and workspace of bsa_probe_attention_packed_workspace_size bytes.
  */
 bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, int Hkv, int S, int D, int M, int C,
                                                      size_t* bytes_host);
 bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                       const int32_t* probe_idx, int M, const void* packed, size_t packed_bytes,
-                                      const int32_t* k_offsets, int C, float* O_dense_probe, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream);
+                                      const int32_t* k_offsets, int C, const int32_t* q_labels, const uint8_t* keep,
+                                      int Hm, int Cq, int compensate, float* O_dense_probe, float* O_sparse_probe,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Ridge fit.  [SPR] Probe-Fitted Residual Reconstruction and [SBC] "Deviations from the

@@ -22,12 +22,14 @@ from .centroids import centroids
 
 
 def compensated_attention(q, k, v, q_labels, k_labels, keep, scale: float, compensate: bool,
-                          rows=None, chunk: int = 512):
+                          rows=None, chunk: int = 512, kbar=None, vbar=None, counts=None):
     """Output rows of block-sparse attention for one head.
 
     q: [Sq, D]; k, v: [Sk, D]; q_labels [Sq] in [0, Cq); k_labels [Sk] in [0, Ck);
     keep: [Cq, Ck] (nonzero = kept block).  ``compensate`` adds the centroid columns;
     otherwise skipped blocks are dropped.  ``rows`` selects query rows (default: all).
+    ``kbar``, ``vbar`` [Ck, D] and ``counts`` [Ck]: centroid columns given by the caller (the
+    page's API takes them as inputs); by default the clusters' means and sizes.
     Returns (out [len(rows), D], lse [len(rows)]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -35,7 +37,12 @@ def compensated_attention(q, k, v, q_labels, k_labels, keep, scale: float, compe
     v = np.asarray(v, dtype=np.float64)
     keep = np.asarray(keep) != 0
     Ck = keep.shape[1]
-    kbar, vbar, n = centroids(k, v, k_labels, Ck)
+    if kbar is None:
+        kbar, vbar, n = centroids(k, v, k_labels, Ck)
+    else:
+        kbar = np.asarray(kbar, dtype=np.float64)
+        vbar = np.asarray(vbar, dtype=np.float64)
+        n = np.asarray(counts, dtype=np.int64)
     with np.errstate(divide="ignore"):
         log_n = np.log(n.astype(np.float64))  # log 0 = -inf: an empty cluster adds nothing
     k_ext = np.concatenate([k, kbar], axis=0)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.bsa_abi_version() == 2
+    assert lib.bsa_abi_version() == 3
     assert lib.bsa_status_string(0) == b"ok"
     assert b"workspace" in lib.bsa_status_string(5)
 
@@ -98,27 +98,37 @@ def test_host_validation_rejects_before_launch(lib):
     # unknown dtype
     assert lib.bsa_centroids(1, 1, 8, 128, 7, dummy, dummy, dummy, dummy, 1, dummy, dummy, None) == 3
     # sparse attention: (B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
-    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, out_dtype, O, lse, ws, ws_bytes, stream)
+    # kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, out_dtype, O, lse, ws, ws_bytes, stream)
     f = ctypes.c_float(0.1)
     big = 1 << 40
     # unsupported head dim
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 96, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 4
+                                    dummy, big, 1, None, None, 1, dummy, None, dummy, big, None) == 4
     # Hq not a multiple of Hkv
     assert lib.bsa_sparse_attention(1, 3, 2, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 2
+                                    dummy, big, 1, None, None, 1, dummy, None, dummy, big, None) == 2
     # output type must be the input type or float32; no packed buffer; packed buffer too small
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 0, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, 1, dummy, None, dummy, big, None) == 3
+                                    dummy, big, 1, None, None, 1, dummy, None, dummy, big, None) == 3
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, 9, dummy, None, dummy, big, None) == 3
+                                    dummy, big, 1, None, None, 9, dummy, None, dummy, big, None) == 3
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    None, big, 1, 1, dummy, None, dummy, big, None) == 1
+                                    None, big, 1, None, None, 1, dummy, None, dummy, big, None) == 1
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, 1024, 1, 1, dummy, None, dummy, big, None) == 5
+                                    dummy, 1024, 1, None, None, 1, dummy, None, dummy, big, None) == 5
     # attention workspace too small
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
-                                    dummy, big, 1, 1, dummy, None, dummy, 16, None) == 5
+                                    dummy, big, 1, None, None, 1, dummy, None, dummy, 16, None) == 5
+    # repair epilogue: A without c; float32 rows with the epilogue
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, dummy, None, 1, dummy, None, dummy, big, None) == 1
+    assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
+                                    dummy, big, 1, dummy, dummy, 0, dummy, None, dummy, big, None) == 4
+    # caller centroids: counts are required; buffer too small
+    assert lib.bsa_kv_pack_centroids(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, None, dummy, big,
+                                     None) == 1
+    assert lib.bsa_kv_pack_centroids(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, dummy, 64,
+                                     None) == 5
     # K/V packing: centroid outputs are required; buffer too small; unsupported head dim
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, None, None, dummy, big, None) == 1
     assert lib.bsa_kv_pack(1, 1, 8, 128, 1, dummy, dummy, dummy, dummy, 1, dummy, dummy, dummy, 64, None) == 5
@@ -170,19 +180,23 @@ def test_workspace_sizes(lib):
     assert _lib.size_query("bsa_probe_attention_workspace_size", 1, 40, 32760, 128, 64) == 40 * 17 * 64 * 130 * 4
     # packed K/V: per head ceil(S/64) + C token tiles and ceil(C/64) centroid tiles of 64 x D
     # keys and 64 x D values; sections (cluster tile offsets, per-head format summary, tile flags,
-    # K, V) 256-byte aligned
+    # K, V, log2 of each centroid count) 256-byte aligned
     tiles = 40 * (512 + 256 + 4)
     tile_bytes = 64 * 128 * 2
-    expect = 1280 + 256 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes
+    expect = 1280 + 256 + (-(-tiles // 256) * 256) + 2 * tiles * tile_bytes + 256 * 4
     assert _lib.size_query("bsa_kv_pack_workspace_size", 1, 40, 32760, 128, 1, 256) == expect
     # attention tile lists: per mask row one int32 per centroid or token tile, plus a count;
     # the work order and each unit's rank in its group (one int32 per batch x head x query
-    # cluster each), one total per K/V group (sized for B x Hq groups) and the queue counters
+    # cluster each), one total per K/V group (sized for B x Hq groups), the queue counters, and
+    # the staged correction of each (batch, query head): A^T as bfloat16 high and low parts in
+    # rows of D + 8, then c (the largest of the bfloat16 and float32 forms at D = 128), in
+    # whole kilobytes
     rows, stride = 40 * 256, 4 + 512 + 256
     units = 40 * 256
+    image = -(-(2 * 128 * 136 * 2 + 128 * 4) // 1024) * 1024
     assert _lib.size_query("bsa_sparse_attention_workspace_size", 1, 40, 40, 256, 32760, 256) == \
         -(-rows * stride * 4 // 256) * 256 + (-(-rows * 4 // 256) * 256) + 2 * (-(-units * 4 // 256) * 256) + \
-        (-(-40 * 4 // 256) * 256) + 256
+        (-(-40 * 4 // 256) * 256) + 256 + 40 * image
 
 
 def test_block_error_workspace_size(lib):
@@ -193,8 +207,9 @@ def test_block_error_workspace_size(lib):
     a = lambda n: -(-n // 256) * 256
     assert _lib.size_query("bsa_block_error_workspace_size", 1, 40, 40, 32760, 128, 256, 256) == \
         a(40 * 24 * 256 * 130 * 4) + a(40 * 256 * 128 * 4) + a(40 * 256 * 4)
+    # packed probe rows: 24 token chunks plus the centroid chunk, dense and sparse rows
     assert _lib.size_query("bsa_probe_attention_packed_workspace_size", 1, 40, 40, 32760, 128, 64, 256) == \
-        40 * 24 * 64 * 130 * 4
+        40 * 25 * 128 * 130 * 4
 
 
 @pytest.mark.parametrize("grid,tile,window", [((1, 3, 4), (1, 1, 1), (1, 3, 3)), ((4, 8, 12), (2, 4, 4), (1, 2, 3)),

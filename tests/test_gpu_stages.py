@@ -422,9 +422,10 @@ def test_probe_attention(bsa, dtype, D, M, compensate, Hkv):
                                                    (128, 130, 2, None, True),
                                                    (128, 64, 1, [0, 1, 63, 64, 65, 130, 7, 1000, 3000], False)])
 def test_probe_attention_packed(bsa, D, M, Hkv, sizes, mixed):
-    """Dense probe rows from the packed tiles against the oracle's dense rows: ragged and empty
-    clusters (the last tile of a cluster is partial), two row tiles (M = 130), and heads whose
-    V^T tiles are partly bfloat16 (values outside the float16 range)."""
+    """Probe rows from the packed tiles against the oracle: the dense rows, and the same probes
+    under the block-sparse rule (compensated and hard drop) from the same pass; ragged and empty
+    clusters (the last tile of a cluster is partial), several row tiles (M = 130: 260 rows),
+    and heads whose V^T tiles are partly bfloat16 (values outside the float16 range)."""
     say(f"probe rows from packed tiles D={D} M={M} Hkv={Hkv} sizes={sizes} mixed={mixed}")
     if sizes is None:
         wl = make_custom(41 + M, B=1, Hq=2, Hkv=Hkv, S=5000, D=D, dtype="bf16")
@@ -437,11 +438,24 @@ def test_probe_attention_packed(bsa, D, M, Hkv, sizes, mixed):
     lay = bsa.cluster_layout(torch.from_numpy(wl.labels).cuda(), wl.C)
     q, k, v = dev(wl.q, "bf16"), dev(wl.k, "bf16"), dev(wl.v, "bf16")
     kv = bsa.kv_pack(k, v, lay)
-    od = host(bsa.probe_attention_packed(q, kv, torch.from_numpy(idx).cuda(), wl.scale))
+    pidx = torch.from_numpy(idx).cuda()
+    od = host(bsa.probe_attention_packed(q, kv, pidx, wl.scale))
     for h in range(2):
         kvh = h // (2 // Hkv)
         ref = oatt.dense_attention_rows(wl.q[0, h][idx], wl.k[0, kvh], wl.v[0, kvh], wl.scale)
         check_output(od[0, h], ref, "bf16", f"dense probe rows (packed) h{h}")
+    mask = bsa.mask_from_keep(torch.from_numpy(wl.mask).cuda())  # one mask per K/V head
+    lab = torch.from_numpy(wl.labels).cuda()
+    for comp in (True, False):
+        od2, os_ = bsa.probe_attention_packed(q, kv, pidx, wl.scale, q_labels=lab, mask=mask, compensate=comp)
+        od2, os_ = host(od2), host(os_)
+        for h in range(2):
+            kvh = h // (2 // Hkv)
+            ref = oatt.dense_attention_rows(wl.q[0, h][idx], wl.k[0, kvh], wl.v[0, kvh], wl.scale)
+            check_output(od2[0, h], ref, "bf16", f"dense probe rows beside sparse ones h{h}")
+            ref_s, _ = oatt.compensated_attention(wl.q[0, h], wl.k[0, kvh], wl.v[0, kvh], wl.labels, wl.labels,
+                                                  wl.mask[0, kvh], wl.scale, comp, rows=idx)
+            check_output(os_[0, h], ref_s, "bf16", f"sparse probe rows (packed, comp={comp}) h{h}")
 
 
 def fit_inputs(M, D, H=3, seed=0):
@@ -494,8 +508,8 @@ def test_gather_rows_bit_exact(bsa):
 
 @pytest.mark.parametrize("dtype,D,compensate", [("bf16", 128, True), ("f32", 64, True), ("bf16", 64, False)])
 def test_attention_with_correction_epilogue(bsa, dtype, D, compensate):
-    """Attention kept in float32, then the correction pass: equals the oracle's o + o A + c on
-    the exact attention output (one rounding, at the end)."""
+    """The attention's repair epilogue: every row o leaves as o + o A + c, which equals the
+    oracle's correction of its exact attention output (one rounding, at the end)."""
     say(f"attention epilogue {dtype} D={D}")
     wl = make_custom(77, B=1, Hq=2, Hkv=1, S=1200, D=D, dtype=dtype)
     rng = np.random.default_rng(3)
@@ -510,3 +524,36 @@ def test_attention_with_correction_epilogue(bsa, dtype, D, compensate):
     for h in range(2):
         ref, _ = oracle_attention(wl, wl.mask, compensate, 0, h)
         check_output(out[0, h], orep.apply_correction(ref, A[0, h], c[0, h]), dtype, f"epilogue h{h}")
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 2, 1), ("bf16", 64, 2, 2), ("f32", 128, 1, 1)])
+def test_attention_caller_centroids(bsa, dtype, D, Hq, Hkv):
+    """Centroid columns given by the caller (kv_pack_centroids): arbitrary centroids and counts,
+    a count of 0 included (its column vanishes), against the oracle's extended-key softmax with
+    the same columns; with the repair epilogue on top for bfloat16."""
+    say(f"caller centroids {dtype} D={D} Hq={Hq} Hkv={Hkv}")
+    wl = make_custom(91, B=1, Hq=Hq, Hkv=Hkv, S=1400, D=D, dtype=dtype)
+    rng = np.random.default_rng(5)
+    kb = (rng.standard_normal((1, Hkv, wl.C, D)) * 0.8).astype(np.float32)
+    vb = rng.standard_normal((1, Hkv, wl.C, D)).astype(np.float32)
+    n = rng.integers(0, 300, wl.C).astype(np.int32)
+    n[1] = 0
+    lab = torch.from_numpy(wl.labels).cuda()
+    lay = bsa.cluster_layout(lab, wl.C)
+    q, k, v = dev(wl.q, dtype), dev(wl.k, dtype), dev(wl.v, dtype)
+    mask = bsa.mask_from_keep(torch.from_numpy(wl.mask).cuda())
+    corr = dtype == "bf16"
+    A = (rng.standard_normal((1, Hq, D, D)) * 0.3).astype(np.float32) if corr else None
+    c = (rng.standard_normal((1, Hq, D)) * 0.1).astype(np.float32) if corr else None
+    out = host(bsa.centroid_compensated_attention(
+        q, k, v, lay, lay, mask, True, wl.scale, kbar=torch.from_numpy(kb).cuda(), vbar=torch.from_numpy(vb).cuda(),
+        counts=torch.from_numpy(n).cuda(), A=torch.from_numpy(A).cuda() if corr else None,
+        c=torch.from_numpy(c).cuda() if corr else None))
+    for h in range(Hq):
+        kvh = h // (Hq // Hkv)
+        ref, _ = oatt.compensated_attention(wl.q[0, h], wl.k[0, kvh], wl.v[0, kvh], wl.labels, wl.labels,
+                                            wl.mask[0, kvh], wl.scale, True, kbar=kb[0, kvh], vbar=vb[0, kvh],
+                                            counts=n)
+        if corr:
+            ref = orep.apply_correction(ref, A[0, h], c[0, h])
+        check_output(out[0, h], ref, dtype, f"caller centroids h{h}")

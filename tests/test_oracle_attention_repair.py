@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from oracle import attention as oa
+from oracle import centroids as oc
 from oracle import pipeline as op
 from oracle import repair as orp
 
@@ -64,10 +65,11 @@ def test_compensation_golden():
         assert abs(d[0, 0] - g[dense_key]) < 1e-14
 
 
-def collapsed_form(q, k, v, ql, kl, keep, scale, compensate):
+def collapsed_form(q, k, v, ql, kl, keep, scale, compensate, given=None):
     """[SBC] SVG-EAR form, written per cluster with Python loops: kept clusters contribute
     every key; each skipped non-empty cluster contributes n_c * exp(q . kbar_c * scale)
-    with value vbar_c."""
+    with value vbar_c.  ``given`` = (kbar, vbar, counts): the caller's centroid columns (a
+    count of 0 contributes nothing)."""
     Sq, D = q.shape
     Ck = keep.shape[1]
     out = np.zeros((Sq, D))
@@ -80,6 +82,9 @@ def collapsed_form(q, k, v, ql, kl, keep, scale, compensate):
             if keep[ql[i], c]:
                 for j in idx:
                     terms.append((float(q[i] @ k[j]) * scale, 1.0, v[j]))
+            elif compensate and given is not None:
+                if given[2][c] > 0:
+                    terms.append((float(q[i] @ given[0][c]) * scale, float(given[2][c]), given[1][c]))
             elif compensate:
                 kb = sum(k[j] for j in idx) / len(idx)
                 vb = sum(v[j] for j in idx) / len(idx)
@@ -99,6 +104,25 @@ def test_extended_key_form_equals_collapsed_form(seed, compensate):
     q, k, v, ql, kl, keep = random_case(seed)
     o, _ = oa.compensated_attention(q, k, v, ql, kl, keep, 0.4, compensate)
     assert np.allclose(o, collapsed_form(q, k, v, ql, kl, keep, 0.4, compensate), atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_caller_centroids(seed):
+    """Centroid columns given by the caller: the extended-key form equals the per-cluster loop
+    with those centroids and counts (a count of 0 removes the column), and giving the clusters'
+    own means and sizes reproduces the default."""
+    q, k, v, ql, kl, keep = random_case(seed)
+    Ck, D = keep.shape[1], k.shape[1]
+    rng = np.random.default_rng(100 + seed)
+    kb, vb = rng.standard_normal((Ck, D)), rng.standard_normal((Ck, D))
+    n = rng.integers(0, 9, Ck)
+    n[0] = 0
+    o, _ = oa.compensated_attention(q, k, v, ql, kl, keep, 0.4, True, kbar=kb, vbar=vb, counts=n)
+    want = collapsed_form(q, k, v, ql, kl, keep, 0.4, True, given=(kb, vb, n))
+    assert np.allclose(o, want, atol=1e-13)
+    kb0, vb0, n0 = oc.centroids(k, v, kl, Ck)
+    o0, _ = oa.compensated_attention(q, k, v, ql, kl, keep, 0.4, True, kbar=kb0, vbar=vb0, counts=n0)
+    assert np.array_equal(o0, oa.compensated_attention(q, k, v, ql, kl, keep, 0.4, True)[0])
 
 
 def test_all_kept_is_dense_sdpa():
