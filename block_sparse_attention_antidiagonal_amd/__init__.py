@@ -20,6 +20,7 @@ from .api import (  # noqa: E402,F401
     antidiagonal_block_scores,
     block_error,
     block_sparse_attention,
+    block_sparse_attention_noalloc,
     centroid_compensated_attention,
     centroids,
     cluster_layout,

@@ -44,6 +44,10 @@ SIGNATURES = {
     "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_int,
                              c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
                              c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_sparse_attention_static_scratch_bytes": [],
+    "bsa_sparse_attention_noalloc": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p,
+                                     c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
+                                     c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p],
     "bsa_kv_pack_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
@@ -68,7 +72,7 @@ SIGNATURES = {
     "bsa_tile_labels": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
     "bsa_sliding_tile_mask": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p],
 }
-_RESTYPES = {"bsa_status_string": ctypes.c_char_p}
+_RESTYPES = {"bsa_status_string": ctypes.c_char_p, "bsa_sparse_attention_static_scratch_bytes": ctypes.c_size_t}
 
 BSA_F32, BSA_BF16 = 0, 1
 MAX_FIT_PROBES = 64  # bsa_probe_fit: 2 <= M <= this

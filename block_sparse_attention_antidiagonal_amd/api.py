@@ -271,6 +271,31 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
     return (o, lse) if return_lse else o
 
 
+def block_sparse_attention_noalloc(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
+                                   out: torch.Tensor, compensate: bool = True, scale: Optional[float] = None,
+                                   A: Optional[torch.Tensor] = None, c: Optional[torch.Tensor] = None,
+                                   lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """block_sparse_attention without a workspace (bsa_sparse_attention_noalloc): the library's
+    static device scratch serves the call and nothing is allocated, so `out` (and `lse` if
+    wanted) must be given.  Calls that overlap on one GPU race (they share the scratch)."""
+    _check_cuda(q, out, A, c, lse)
+    B, Hq, S, D = q.shape
+    if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
+        raise ValueError("q does not match the packed K/V")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Ck = kv.layout.C
+    if mask.keep.shape[0] != B or mask.keep.shape[2] != q_layout.C or mask.keep.shape[3] != Ck:
+        raise ValueError("mask shape does not match batch / cluster counts")
+    if out.shape != q.shape or out.dtype not in (q.dtype, torch.float32):
+        raise ValueError("out has the wrong shape or dtype")
+    _lib.call("bsa_sparse_attention_noalloc", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
+              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
+              _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
+              int(bool(compensate)), _ptr(A), _ptr(c), _dtype_code(out), _ptr(out), _ptr(lse), _stream())
+    return out
+
+
 def correct(o32: torch.Tensor, A: torch.Tensor, c: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Every row o of the float32 output becomes o + o A + c, rounded once to dtype (bsa_correct)."""

@@ -20,6 +20,7 @@
 #include "common.hpp"
 #include "pack.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace bsa {
@@ -1960,6 +1961,59 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS
+}
+
+// ----------------------------------------------------------------- allocation-free variant
+
+// The attention's scratch memory (tile lists, work order, unit ranks, queue counters, staged
+// corrections) for callers that cannot allocate: a file-scope device array, one copy per GPU
+// for the life of the process.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t{48} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, or nullptr if it cannot be had.
+void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t bsa_sparse_attention_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" bsa_status bsa_sparse_attention_noalloc(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
+                                                   float scale, const int32_t* q_perm, const int32_t* q_offsets,
+                                                   int Cq, const int32_t* k_offsets, int Ck, const uint8_t* keep,
+                                                   const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                                                   const void* packed, size_t packed_bytes, int compensate,
+                                                   const float* A, const float* c, int out_dtype, void* O,
+                                                   float* lse, hipStream_t stream) {
+  size_t need = 0;
+  if (B < 1 || Hq < 1 || Hm < 1 || Cq < 1 || S < 1 || Ck < 1) return BSA_E_ARG;
+  const bsa_status st = bsa_sparse_attention_workspace_size(B, Hq, Hm, Cq, S, Ck, &need);
+  if (st != BSA_OK) return st;
+  if (need > kStaticScratchBytes) return BSA_E_WORKSPACE;  // larger than the static scratch
+  void* ws = static_scratch();
+  if (ws == nullptr) return BSA_E_HIP;
+  // Every scratch section is written by the call's own kernels before it is read (the lists,
+  // ranks, totals, order and queue counters by the list and order kernels, the corrections by
+  // corr_image_kernel), so nothing needs clearing between calls.
+  return bsa_sparse_attention(B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
+                              kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, out_dtype, O, lse, ws,
+                              kStaticScratchBytes, stream);
 }
 
 extern "C" bsa_status bsa_probe_attention_workspace_size(int B, int Hq, int S, int D, int M, size_t* bytes) {

@@ -213,6 +213,24 @@ bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype,
                                 const float* c, int out_dtype, void* O, float* lse, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): bsa_sparse_attention without a workspace
+ * argument.  Its scratch memory is a static device array of
+ * bsa_sparse_attention_static_scratch_bytes() bytes (48 MiB) that every GPU the library runs on
+ * holds until the process ends; the call allocates nothing.  Arguments, results and errors are
+ * those of bsa_sparse_attention, plus BSA_E_WORKSPACE when the problem needs more scratch than
+ * the static array holds (bsa_sparse_attention_workspace_size tells) and BSA_E_HIP when the
+ * array's device address cannot be obtained.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from several threads without
+ * ordering) race and give undefined results; calls ordered on one stream are safe. */
+size_t bsa_sparse_attention_static_scratch_bytes(void);
+bsa_status bsa_sparse_attention_noalloc(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
+                                        const int32_t* q_perm, const int32_t* q_offsets, int Cq,
+                                        const int32_t* k_offsets, int Ck, const uint8_t* keep,
+                                        const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed,
+                                        size_t packed_bytes, int compensate, const float* A, const float* c,
+                                        int out_dtype, void* O, float* lse, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * Probe rows.  [SPR] Probe-Fitted Residual Reconstruction: M query rows per (batch, head)
  * get exact dense attention over all S keys, O_dense[p] = softmax(q_p K^T scale) V ([SBC]

@@ -119,6 +119,11 @@ def test_host_validation_rejects_before_launch(lib):
     # attention workspace too small
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
                                     dummy, big, 1, None, None, 1, dummy, None, dummy, 16, None) == 5
+    # the allocation-free call: a problem needing more than the static scratch (the video shape
+    # with 200 heads needs about 165 MiB of tile lists)
+    assert lib.bsa_sparse_attention_noalloc(1, 200, 200, 32760, 128, 1, dummy, f, dummy, dummy, 256, dummy, 256,
+                                            dummy, dummy, dummy, 200, dummy, big, 1, None, None, 1, dummy, None,
+                                            None) == 5
     # repair epilogue: A without c; float32 rows with the epilogue
     assert lib.bsa_sparse_attention(1, 1, 1, 8, 128, 1, dummy, f, dummy, dummy, 1, dummy, 1, dummy, dummy, dummy, 1,
                                     dummy, big, 1, dummy, None, 1, dummy, None, dummy, big, None) == 1
