@@ -448,7 +448,11 @@ template <typename T, int D, typename Lds, typename Bias>
 __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T>* qf, RowState<D>& st, float c2,
                                           const Bias& bias, int nvalid, bool pv16) {
   f32x16 s[2];
+  // The Q K^T products issue at raised wave priority, so that of the two waves sharing a SIMD
+  // the one entering its products goes first and the other's softmax fills in beside them.
+  __builtin_amdgcn_s_setprio(1);
   tile_qk<T, D, Lds>(Ks, qf, s[0], s[1]);
+  __builtin_amdgcn_s_setprio(0);
   tile_softmax<T, D>(s, st, c2, bias, nvalid);
   tile_pv<T, D, Lds>(Vt, s, st, pv16);
 }
@@ -543,7 +547,31 @@ struct TileDma {
     }
 #endif
   }
+  // The same copies by buffer loads: the head's tiles are a buffer resource, the tile's byte
+  // offset a scalar, the per-lane offsets the constants above, so a tile costs no address
+  // arithmetic (16-bit tiles, whose swizzle repeats every kStep bytes).
+  static constexpr bool kBuffer = repeats<typename S::SK>() && repeats<typename S::SV>();
+  __device__ __forceinline__ void issue_kv_buf(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int toff, T* Ks,
+                                               T* Vt) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    lds_u8* lk = (lds_u8*)(reinterpret_cast<unsigned char*>(Ks) + wave * 1024);
+    lds_u8* lv = (lds_u8*)(reinterpret_cast<unsigned char*>(Vt) + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, lk + j * kStep, 16, koff + j * kStep, toff, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, lv + j * kStep, 16, voff + j * kStep, toff, 0, 0);
+#endif
+  }
 };
+// Buffer resource over `bytes` bytes at p (raw buffer, 32-bit elements; offsets past the end
+// read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
 
 // The tile sequence of one mask row, expanded ahead of the attention by tile_list_wave_kernel:
 // the centroid tiles (compensation), then the tiles of every kept key cluster in list order,
@@ -1026,6 +1054,10 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     // ALL16: every V^T tile of this head is float16 (the usual case), so the tile loop needs
     // neither the format flags nor the bfloat16 product; it is compiled separately from the
     // general loop so that the rare format switch does not burden its registers.
+    // The head's packed K and V^T tiles as buffer resources (one head: at most 772 tiles of
+    // 16 KB, well inside 32-bit offsets).
+    const __amdgpu_buffer_rsrc_t krsrc = raw_buffer(Kph, static_cast<int>(tiles_per_head * kTileBytes));
+    const __amdgpu_buffer_rsrc_t vrsrc = raw_buffer(Vph, static_cast<int>(tiles_per_head * kTileBytes));
     auto tile_loop = [&](auto all16_tag) {
     constexpr bool ALL16 = decltype(all16_tag)::value;
     int chunk = lane < ecount ? ent[lane] : 0;
@@ -1056,8 +1088,12 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
       if (have1) {
         e1 = __builtin_amdgcn_readlane(chunk, pn & 63);
         const int tl = entry_tile(e1);
-        dma.issue_k(Kph + tl * kTileBytes, kbuf(BJ ^ 1));
-        dma.issue_v(Vph + tl * kTileBytes, vbuf(BJ ^ 1));
+        if constexpr (TileDma<T, D>::kBuffer) {
+          dma.issue_kv_buf(krsrc, vrsrc, tl * static_cast<int>(kTileBytes), kbuf(BJ ^ 1), vbuf(BJ ^ 1));
+        } else {
+          dma.issue_k(Kph + tl * kTileBytes, kbuf(BJ ^ 1));
+          dma.issue_v(Vph + tl * kTileBytes, vbuf(BJ ^ 1));
+        }
         if (entry_centroid(e1)) write_bias(bias0 + (BJ ^ 1) * kNK, tl - first_ctile);
         if (!ALL16) pv1 = flags_h[tl];
       }
@@ -1953,7 +1989,10 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   size_t need = 0;
   const bsa_status st = bsa_sparse_attention_workspace_size(B, Hq, Hm, Cq, S, Ck, &need);
   if (st != BSA_OK) return st;
-  if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype)).total) return BSA_E_WORKSPACE;
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype));
+  if (packed_bytes < PL.total) return BSA_E_WORKSPACE;
+  // One head's tiles are addressed with 32-bit byte offsets.
+  if (static_cast<size_t>(PL.tiles_per_head) * 64 * D * dtype_size(dtype) > 0x7fffffffu) return BSA_E_UNSUPPORTED;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   const bool out_f32 = out_dtype == BSA_F32 && dtype != BSA_F32;
 #define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
