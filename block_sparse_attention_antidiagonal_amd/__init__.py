@@ -28,6 +28,7 @@ from .api import (  # noqa: E402,F401
     error_route,
     gather_rows,
     kv_pack,
+    kmeans,
     kv_pack_centroids,
     mask_from_keep,
     mask_reuse_decide,
@@ -38,6 +39,7 @@ from .api import (  # noqa: E402,F401
     probe_fit,
     pooled_qk,
     query_centroids,
+    response_partition,
     select_probe_rows,
     sliding_tile_block_mask,
     tile_labels,

@@ -48,6 +48,12 @@ SIGNATURES = {
     "bsa_sparse_attention_noalloc": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p,
                                      c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
                                      c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p],
+    "bsa_response_partition_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_response_partition": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float, c_int, c_int,
+                               c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                               c_void_p],
+    "bsa_kmeans_workspace_size": [c_int, c_int, c_int, c_size_p],
+    "bsa_kmeans": [c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_kv_pack_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],

@@ -567,6 +567,49 @@ class HeadMaskCache:
         return self.mask
 
 
+# ----------------------------------------------------------------- response-coupled partitioning
+
+def response_partition(q: torch.Tensor, k: torch.Tensor, Cq: int, Ck: int, scale: Optional[float] = None,
+                       rK: int = 48, rQ: int = 64, iters: int = 4, return_centres: bool = False,
+                       workspace: Optional[torch.Tensor] = None):
+    """Key and query groups of every (batch, K/V head) from the call's own responses
+    (bsa_response_partition): returns (k_labels, q_labels), int32 [B, Hkv, S] each, and with
+    return_centres also the final k-means centres [B, Hkv, Ck, 64] and [B, Hkv, Cq, 64]."""
+    _check_cuda(q, k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k shapes/dtypes do not match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kl = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
+    ql = torch.empty_like(kl)
+    kc = torch.empty(B, Hkv, Ck, 64, dtype=torch.float32, device=q.device) if return_centres else None
+    qc = torch.empty(B, Hkv, Cq, 64, dtype=torch.float32, device=q.device) if return_centres else None
+    nbytes = _lib.size_query("bsa_response_partition_workspace_size", B, Hkv, S, D, Cq, Ck)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, q.device)
+    _lib.call("bsa_response_partition", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(k), float(scale), int(rK),
+              int(rQ), int(Cq), int(Ck), int(iters), _ptr(kl), _ptr(ql), _ptr(kc), _ptr(qc), _ptr(workspace),
+              workspace.numel(), _stream())
+    return (kl, ql, kc, qc) if return_centres else (kl, ql)
+
+
+def kmeans(x: torch.Tensor, C: int, iters: int = 4, nf: Optional[int] = None):
+    """Batched k-means of float32 points x [P, N, 64] (features past nf zero) into C centres
+    (bsa_kmeans): returns (labels int32 [P, N], centres float32 [P, C, 64])."""
+    _check_cuda(x)
+    P, N, F = x.shape
+    if F != 64 or x.dtype != torch.float32:
+        raise ValueError("x must be float32 [P, N, 64]")
+    labels = torch.empty(P, N, dtype=torch.int32, device=x.device)
+    centres = torch.empty(P, C, 64, dtype=torch.float32, device=x.device)
+    ws = _workspace(_lib.size_query("bsa_kmeans_workspace_size", P, N, C), x.device)
+    _lib.call("bsa_kmeans", P, N, int(nf or 64), _ptr(x), int(C), int(iters), _ptr(labels), _ptr(centres), _ptr(ws),
+              ws.numel(), _stream())
+    return labels, centres
+
+
 def select_probe_rows(labels: np.ndarray, C: int, M: int) -> Tuple[np.ndarray, np.ndarray]:
     """Host helper: probe rows and normalized weights (bsa_select_probe_rows)."""
     lab = np.ascontiguousarray(labels, dtype=np.int32)

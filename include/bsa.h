@@ -407,6 +407,42 @@ bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_
                            int32_t* kv_count, int16_t* kv_idx, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Response-coupled partitioning.  [SPR] Response-Coupled Partitioning: queries sampled from
+ * the call; keys grouped by their pre-softmax response profiles to those queries (feature
+ * rank rK = 48); the key groups' centroids give the query coordinates (rank rQ = 64); one
+ * asymmetric pass (keys, then queries); [SPR] grouped-query sharing: one key partition and one
+ * query partition per (batch, K/V head), shared by the group's query heads; [SPR] timing: an
+ * online k-means inside the call.  Readings of what the page leaves open:
+ *   - the rK sampled queries are the tokens floor((j + 1/2) S / rK), j < rK, of query head
+ *     kvh * G + (j mod G) (G = Hq / Hkv); a key's profile is (k . q_s) * scale over them;
+ *   - a query token's coordinates are (qm . kbar_c) * scale for the key groups c =
+ *     floor((j + 1/2) Ck / rQ'), j < rQ' = min(rQ, Ck), with qm the mean of its G query rows
+ *     and kbar_c the mean of group c's keys, scaled to unit length (zero stays zero);
+ *   - k-means: starting centres at the points floor((c + 1/2) N / C); `iters` Lloyd
+ *     iterations (nearest centre by squared distance, equal distances to the lower index; a
+ *     centre without points keeps its place); then a last assignment, so every label is a
+ *     nearest centre of the final centres.  Distances are taken in float32 as |c|^2 - 2 x.c.
+ *   Q [B, Hq, S, D], K [B, Hkv, S, D] dtype; 1 <= rK, rQ <= 64; 1 <= Cq, Ck <= min(8192, S)
+ *   k_labels, q_labels int32 [B, Hkv, S] out: the key group of every key and the query group
+ *     of every query token of each (batch, K/V head)
+ *   k_centres float [B, Hkv, Ck, 64], q_centres float [B, Hkv, Cq, 64] out or NULL: the final
+ *     centres (features past the rank are zero)
+ *   ws: bsa_response_partition_workspace_size bytes (features, centroids, the k-means sort)
+ *
+ * bsa_kmeans: the k-means above on its own, for P independent problems of N points with nf <= 64
+ * features, stored 64 floats per point (zero past nf).  X float [P, N, 64]; labels int32 [P, N]
+ * out; centres float [P, C, 64] out; C <= min(8192, N); ws of bsa_kmeans_workspace_size bytes.
+ */
+bsa_status bsa_response_partition_workspace_size(int B, int Hkv, int S, int D, int Cq, int Ck, size_t* bytes_host);
+bsa_status bsa_response_partition(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const void* K,
+                                  float scale, int rK, int rQ, int Cq, int Ck, int iters, int32_t* k_labels,
+                                  int32_t* q_labels, float* k_centres, float* q_centres, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+bsa_status bsa_kmeans_workspace_size(int P, int N, int C, size_t* bytes_host);
+bsa_status bsa_kmeans(int P, int N, int nf, const float* X, int C, int iters, int32_t* labels, float* centres,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Host helpers (host pointers only).
  *
  * Probe rows.  [SBC] API table and "Deviations from the papers": probes are shared by all
