@@ -34,8 +34,9 @@ HIP_FLAGS = [
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # Device code assumes no NaN inputs (max/min skip NaN quieting); host validation keeps
-    # full IEEE semantics.
-    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
+    # full IEEE semantics.  (The hardware IEEE mode stays on: turning it off keeps the device
+    # library's work-item and work-group queries from being inlined.)
+    "-Xarch_device", "-fno-honor-nans",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -133,15 +133,77 @@ __global__ __launch_bounds__(256) void layout_scatter(const int32_t* __restrict_
   }
 }
 
+// The same stable scatter for labels that change from token to token (k-means labels: dozens
+// of distinct labels in every 64 tokens).  Wave w owns sub-chunk w (256 tokens, 4 segments
+// of 64) and walks its segments in order: one ballot per distinct label of a segment gives
+// every lane its rank among the earlier lanes with its label, to which it adds the wave's
+// running count of that label (LDS), which the label's first lane then advances.  After all
+// waves are done, a token adds the counts of its label in the earlier sub-chunks.  Dynamic
+// LDS: 4 C ints.
+constexpr int kSub = 256;
+__global__ __launch_bounds__(256) void layout_scatter_many(const int32_t* __restrict__ labels, int S, int C,
+                                                            int nchunks, const int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ perm) {
+  extern __shared__ int32_t sub_counts[];  // [4][C]: running, then total, counts per sub-chunk
+  labels += static_cast<size_t>(blockIdx.y) * S;
+  base += static_cast<size_t>(blockIdx.y) * nchunks * C;
+  perm += static_cast<size_t>(blockIdx.y) * S;
+  const int start = blockIdx.x * kChunk;
+  const int n = min(kChunk, S - start);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int e = threadIdx.x; e < (kChunk / kSub) * C; e += kSub) sub_counts[e] = 0;
+  __syncthreads();
+  int32_t* run = sub_counts + wave * C;
+  int lab_r[kSub / 64], rank_r[kSub / 64];
+#pragma unroll
+  for (int k = 0; k < kSub / 64; ++k) {
+    const int i = wave * kSub + k * 64 + lane;
+    int li = i < n ? labels[start + i] : -1;
+    if (li < 0 || li >= C) li = -1;
+    int rank = 0;
+    unsigned long long left = __ballot(li >= 0);
+    while (left) {
+      const int leader = __ffsll(static_cast<long long>(left)) - 1;
+      const int l = __builtin_amdgcn_readlane(li, leader);
+      const unsigned long long m = __ballot(li == l);
+      const int before = run[l];  // uniform: every lane reads the same count
+      if (li == l) rank = before + __popcll(m & below);
+      if (lane == leader) run[l] = before + __popcll(m);
+      left &= ~m;
+    }
+    lab_r[k] = li;
+    rank_r[k] = rank;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kSub / 64; ++k) {
+    const int li = lab_r[k];
+    if (li < 0) continue;
+    int r = rank_r[k];
+    for (int w2 = 0; w2 < wave; ++w2) r += sub_counts[w2 * C + li];
+    perm[base[static_cast<size_t>(blockIdx.x) * C + li] + r] = start + wave * kSub + k * 64 + lane;
+  }
+}
+
 inline int layout_chunks(int S) { return (S + kChunk - 1) / kChunk; }
 
-// P layouts of S labels into C clusters; hist holds P * layout_chunks(S) * C ints.
+// P layouts of S labels into C clusters; hist holds P * layout_chunks(S) * C ints.  many_labels
+// picks the scatter for labels that vary from token to token.
 inline void launch_layouts(const int32_t* labels, int S, int C, int P, int32_t* hist, int32_t* perm,
-                           int32_t* offsets, int32_t* counts, hipStream_t stream) {
+                           int32_t* offsets, int32_t* counts, hipStream_t stream, bool many_labels = false) {
   const int nchunks = layout_chunks(S);
   hipLaunchKernelGGL(layout_hist, dim3(nchunks, P), dim3(256), 0, stream, labels, S, C, nchunks, hist);
   hipLaunchKernelGGL(layout_scan, dim3(P), dim3(1024), 0, stream, C, nchunks, hist, offsets, counts);
-  hipLaunchKernelGGL(layout_scatter, dim3(nchunks, P), dim3(256), 0, stream, labels, S, C, nchunks, hist, perm);
+  if (many_labels) {
+    const size_t lds = static_cast<size_t>((kChunk / kSub) * C) * sizeof(int32_t);
+    hipFuncSetAttribute(reinterpret_cast<const void*>(layout_scatter_many),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    hipLaunchKernelGGL(layout_scatter_many, dim3(nchunks, P), dim3(kSub), lds, stream, labels, S, C, nchunks, hist,
+                       perm);
+  } else {
+    hipLaunchKernelGGL(layout_scatter, dim3(nchunks, P), dim3(256), 0, stream, labels, S, C, nchunks, hist, perm);
+  }
 }
 
 }  // namespace
