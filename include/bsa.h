@@ -421,7 +421,8 @@ bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_
  *   - k-means: starting centres at the points floor((c + 1/2) N / C); `iters` Lloyd
  *     iterations (nearest centre by squared distance, equal distances to the lower index; a
  *     centre without points keeps its place); then a last assignment, so every label is a
- *     nearest centre of the final centres.  Distances are taken in float32 as |c|^2 - 2 x.c.
+ *     nearest centre of the final centres.  Distances are taken as |c|^2 - 2 x.c, with x.c from
+ *     split-bfloat16 products (hi.hi + hi.lo + lo.hi, float32 sums: within about 3e-5 |x| |c|).
  *   Q [B, Hq, S, D], K [B, Hkv, S, D] dtype; 1 <= rK, rQ <= 64; 1 <= Cq, Ck <= min(8192, S)
  *   k_labels, q_labels int32 [B, Hkv, S] out: the key group of every key and the query group
  *     of every query token of each (batch, K/V head)

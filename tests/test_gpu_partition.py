@@ -1,9 +1,10 @@
 """GPU parity of response-coupled partitioning (bsa_kmeans, bsa_response_partition) against the
 oracle ("Partition the Support, Reconstruct the Residual", Response-Coupled Partitioning).
 
-The kernels take the nearest centre from float32 values of |c|^2 - 2 x.c, the oracle from
-float64 squared differences, so a point whose two nearest centres are closer than the float32
-rounding of those values may go either way.  Every comparison therefore checks what is
+The kernels take the nearest centre from |c|^2 - 2 x.c with x.c as split-bfloat16 products
+(x = hi + lo in bfloat16, hi.hi + hi.lo + lo.hi summed in float32: within about 3e-5 |x| |c|),
+the oracle from float64 squared differences, so a point whose two nearest centres are closer
+than that rounding may go either way.  Every comparison therefore checks what is
 unique exactly and the rest for validity: labels equal the oracle's wherever the oracle's
 best centre wins by more than the rounding bound; every label is a nearest centre (within the
 bound) of the centres it is returned with; centres are the means of the points they were
@@ -39,8 +40,8 @@ def _pad(X: np.ndarray) -> np.ndarray:
 
 
 def _bound(X: np.ndarray, centres: np.ndarray) -> np.ndarray:
-    """Per-point bound on the float32 rounding of |c|^2 - 2 x.c, [N]: a few ulps of the
-    magnitudes the sum runs over."""
+    """Per-point bound on the rounding of |c|^2 - 2 x.c, [N]: 2e-5 (|x| + |c|)^2 >= 8e-5 |x| |c|,
+    above the split-bfloat16 products' 2 * (3 * 2^-18 + 64 * 2^-24) |x| |c| ~ 3e-5 |x| |c|."""
     xn = (X * X).sum(axis=1)
     cn = (centres * centres).sum(axis=1).max()
     return 2e-5 * (xn + cn + 2.0 * np.sqrt(xn * cn)) + 1e-30
