@@ -41,6 +41,7 @@ from .api import (  # noqa: E402,F401
     query_centroids,
     response_partition,
     select_probe_rows,
+    select_probe_rows_layouts,
     sliding_tile_block_mask,
     tile_labels,
     top_p_block_mask,

@@ -19,8 +19,9 @@ c_size_p = ctypes.POINTER(ctypes.c_size_t)
 SIGNATURES = {
     "bsa_status_string": [c_int],
     "bsa_abi_version": [],
-    "bsa_cluster_layout_workspace_size": [c_int, c_int, c_size_p],
-    "bsa_cluster_layout": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_cluster_layout_workspace_size": [c_int, c_int, c_int, c_size_p],
+    "bsa_cluster_layout": [c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_select_probe_rows_layouts": [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                       c_void_p, c_void_p],
     "bsa_antidiag_scores_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
@@ -37,17 +38,17 @@ SIGNATURES = {
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_top_p_mask": [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_mask_lists": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
-    "bsa_kv_pack_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
-    "bsa_kv_pack": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+    "bsa_kv_pack_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
+    "bsa_kv_pack": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p,
                     c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_sparse_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_sparse_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p, c_int,
-                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
+                             c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_int,
                              c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_sparse_attention_static_scratch_bytes": [],
     "bsa_sparse_attention_noalloc": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_void_p,
-                                     c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
-                                     c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p],
+                                     c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                     c_size_t, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p],
     "bsa_response_partition_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_response_partition": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float, c_int, c_int,
                                c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
@@ -55,22 +56,23 @@ SIGNATURES = {
     "bsa_kmeans_workspace_size": [c_int, c_int, c_int, c_size_p],
     "bsa_kmeans": [c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_kv_pack_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
-                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+                              c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_probe_attention": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
                             c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "bsa_probe_attention_packed_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_probe_attention_packed": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_float, c_void_p, c_int,
-                                   c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                   c_void_p, c_size_t, c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
-    "bsa_probe_fit": [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, c_void_p,
-                      c_void_p],
-    "bsa_query_centroids": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p],
+    "bsa_probe_fit": [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, c_void_p,
+                      c_void_p, c_void_p],
+    "bsa_query_centroids": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                            c_void_p, c_void_p],
     "bsa_block_error_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_size_p],
     "bsa_block_error": [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_float, c_void_p, c_size_t,
-                        c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
-    "bsa_error_route": [c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
+                        c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "bsa_error_route": [c_void_p, c_int, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_probe_apply": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_correct": [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "bsa_gather_rows": [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p],

@@ -53,27 +53,49 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 class ClusterLayout:
     """Cluster-major order of tokens: cluster c owns perm[offsets[c]:offsets[c+1]]."""
 
-    perm: torch.Tensor  # int32 [S]
-    offsets: torch.Tensor  # int32 [C+1]
-    counts: torch.Tensor  # int32 [C]
+    perm: torch.Tensor  # int32 [S], or [P, S] for P layouts
+    offsets: torch.Tensor  # int32 [C+1] or [P, C+1]
+    counts: torch.Tensor  # int32 [C] or [P, C]
     C: int
+
+    @property
+    def n_layouts(self) -> int:
+        """1 for one layout shared by every head, else the number of layouts (B * Hkv: one per
+        (batch, K/V head), layout b * Hkv + kvh)."""
+        return 1 if self.perm.dim() == 1 else int(self.perm.shape[0])
 
 
 def cluster_layout(labels: torch.Tensor, C: int) -> ClusterLayout:
-    """Stable counting sort of int32 labels [S] in [0, C) (bsa_cluster_layout)."""
+    """Stable counting sort of int32 labels in [0, C) (bsa_cluster_layout): labels [S] give one
+    layout; labels [..., S] (e.g. [B, Hkv, S] from response_partition) give one per leading
+    index, flattened to [P, S]."""
     _check_cuda(labels)
-    if labels.dtype != torch.int32 or labels.dim() != 1:
-        raise ValueError("labels must be int32 [S]")
-    S = labels.numel()
+    if labels.dtype != torch.int32 or labels.dim() < 1:
+        raise ValueError("labels must be int32 [S] or [..., S]")
+    S = labels.shape[-1]
+    P = labels.numel() // S
     dev = labels.device
-    perm = torch.empty(S, dtype=torch.int32, device=dev)
-    offsets = torch.empty(C + 1, dtype=torch.int32, device=dev)
-    counts = torch.empty(C, dtype=torch.int32, device=dev)
-    nbytes = _lib.size_query("bsa_cluster_layout_workspace_size", S, C)
+    lead = () if labels.dim() == 1 else (P,)
+    perm = torch.empty(*lead, S, dtype=torch.int32, device=dev)
+    offsets = torch.empty(*lead, C + 1, dtype=torch.int32, device=dev)
+    counts = torch.empty(*lead, C, dtype=torch.int32, device=dev)
+    nbytes = _lib.size_query("bsa_cluster_layout_workspace_size", P, S, C)
     ws = _workspace(nbytes, dev)
-    _lib.call("bsa_cluster_layout", _ptr(labels), S, C, _ptr(perm), _ptr(offsets), _ptr(counts), _ptr(ws),
-              ws.numel(), _stream())
+    _lib.call("bsa_cluster_layout", P, _ptr(labels.contiguous()), S, C, _ptr(perm), _ptr(offsets), _ptr(counts),
+              _ptr(ws), ws.numel(), _stream())
     return ClusterLayout(perm, offsets, counts, C)
+
+
+def select_probe_rows_layouts(layout: ClusterLayout, M: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Probe rows and weights of every layout on the device (bsa_select_probe_rows_layouts):
+    int32 [P, M] and float32 [P, M]."""
+    perm = layout.perm if layout.perm.dim() == 2 else layout.perm[None]
+    P, S = perm.shape
+    idx = torch.empty(P, M, dtype=torch.int32, device=perm.device)
+    w = torch.empty(P, M, dtype=torch.float32, device=perm.device)
+    _lib.call("bsa_select_probe_rows_layouts", P, S, layout.C, int(M), _ptr(perm), _ptr(layout.offsets), _ptr(idx),
+              _ptr(w), _stream())
+    return idx, w
 
 
 def centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -113,20 +135,22 @@ def kv_pack(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout,
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must match")
     code = _dtype_code(k)
-    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C)
+    nl = layout.n_layouts
+    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C, nl)
     if buffer is None or buffer.numel() < nbytes:
         buffer = _workspace(nbytes, k.device)
     kbar = torch.empty(B, Hkv, layout.C, D, dtype=torch.float32, device=k.device)
     vbar = torch.empty_like(kbar)
     _lib.call("bsa_kv_pack", B, Hkv, S, D, code, _ptr(k), _ptr(v), _ptr(layout.perm), _ptr(layout.offsets),
-              layout.C, _ptr(kbar), _ptr(vbar), _ptr(buffer), buffer.numel(), _stream())
+              layout.C, nl, _ptr(kbar), _ptr(vbar), _ptr(buffer), buffer.numel(), _stream())
     return PackedKV(buffer, kbar, vbar, layout, B, Hkv, S, D, k.dtype)
 
 
 def kv_pack_centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout, kbar: torch.Tensor,
                       vbar: torch.Tensor, counts: torch.Tensor, buffer: Optional[torch.Tensor] = None) -> PackedKV:
     """Pack K/V into cluster tiles with the caller's centroids kbar, vbar (float32 [B, Hkv, C, D])
-    and counts (int32 [C], the n_c of each centroid column) (bsa_kv_pack_centroids)."""
+    and counts (int32 [C], or [P, C] with P layouts: the n_c of each centroid column)
+    (bsa_kv_pack_centroids)."""
     _check_cuda(k, v, kbar, vbar, counts)
     B, Hkv, S, D = k.shape
     if v.shape != k.shape or v.dtype != k.dtype:
@@ -134,15 +158,16 @@ def kv_pack_centroids(k: torch.Tensor, v: torch.Tensor, layout: ClusterLayout, k
     if kbar.shape != (B, Hkv, layout.C, D) or vbar.shape != kbar.shape or kbar.dtype != torch.float32 \
             or vbar.dtype != torch.float32:
         raise ValueError("kbar and vbar must be float32 [B, Hkv, C, D]")
-    if counts.shape != (layout.C,) or counts.dtype != torch.int32:
-        raise ValueError("counts must be int32 [C]")
+    nl = layout.n_layouts
+    if counts.shape != layout.counts.shape or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [C] (or [P, C] for P layouts)")
     code = _dtype_code(k)
-    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C)
+    nbytes = _lib.size_query("bsa_kv_pack_workspace_size", B, Hkv, S, D, code, layout.C, nl)
     if buffer is None or buffer.numel() < nbytes:
         buffer = _workspace(nbytes, k.device)
     _lib.call("bsa_kv_pack_centroids", B, Hkv, S, D, code, _ptr(k), _ptr(v), _ptr(layout.perm),
-              _ptr(layout.offsets), layout.C, _ptr(kbar), _ptr(vbar), _ptr(counts), _ptr(buffer), buffer.numel(),
-              _stream())
+              _ptr(layout.offsets), layout.C, nl, _ptr(kbar), _ptr(vbar), _ptr(counts), _ptr(buffer),
+              buffer.numel(), _stream())
     return PackedKV(buffer, kbar, vbar, layout, B, Hkv, S, D, k.dtype)
 
 
@@ -229,6 +254,15 @@ def mask_from_keep(keep: torch.Tensor) -> BlockMask:
     return BlockMask(keep, cnt, idx)
 
 
+def _layout_count(q_layout: ClusterLayout, kv: PackedKV) -> int:
+    """The layout count of a call: the query and key layouts must have the same (1, or one per
+    (batch, K/V head))."""
+    nl = kv.layout.n_layouts
+    if q_layout.n_layouts != nl or nl not in (1, kv.B * kv.Hkv):
+        raise ValueError("query and key layouts must both be shared, or both one per (batch, K/V head)")
+    return nl
+
+
 def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayout, mask: BlockMask,
                            compensate: bool = True, scale: Optional[float] = None, return_lse: bool = False,
                            out: Optional[torch.Tensor] = None, out_f32: bool = False,
@@ -260,11 +294,12 @@ def block_sparse_attention(q: torch.Tensor, kv: PackedKV, q_layout: ClusterLayou
     if o.dtype != odt or o.shape != q.shape:
         raise ValueError("out has the wrong shape or dtype")
     lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device) if return_lse else None
+    nl = _layout_count(q_layout, kv)
     nbytes = _lib.size_query("bsa_sparse_attention_workspace_size", B, Hq, mask.Hm, q_layout.C, S, Ck)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, q.device)
     _lib.call("bsa_sparse_attention", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
-              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
+              _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck, nl,
               _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
               int(bool(compensate)), _ptr(A), _ptr(c), _dtype_code(o), _ptr(o), _ptr(lse), _ptr(workspace),
               workspace.numel(), _stream())
@@ -291,7 +326,7 @@ def block_sparse_attention_noalloc(q: torch.Tensor, kv: PackedKV, q_layout: Clus
         raise ValueError("out has the wrong shape or dtype")
     _lib.call("bsa_sparse_attention_noalloc", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
               _ptr(q_layout.perm), _ptr(q_layout.offsets), q_layout.C, _ptr(kv.layout.offsets), Ck,
-              _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
+              _layout_count(q_layout, kv), _ptr(mask.keep), _ptr(mask.kv_count), _ptr(mask.kv_idx), mask.Hm, _ptr(kv.buffer), kv.buffer.numel(),
               int(bool(compensate)), _ptr(A), _ptr(c), _dtype_code(out), _ptr(out), _ptr(lse), _stream())
     return out
 
@@ -382,7 +417,10 @@ def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tenso
     B, Hq, S, D = q.shape
     if (kv.B, kv.S, kv.D, kv.dtype) != (B, S, D, q.dtype) or Hq % kv.Hkv != 0:
         raise ValueError("packed K/V do not match q")
-    M = probe_idx.numel()
+    nl = kv.layout.n_layouts
+    M = probe_idx.shape[-1]
+    if probe_idx.numel() != (nl if nl > 1 else 1) * M:
+        raise ValueError("probe_idx must be [M], or [P, M] with the P layouts of kv")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     od = torch.empty(B, Hq, M, D, dtype=torch.float32, device=q.device)
@@ -398,19 +436,23 @@ def probe_attention_packed(q: torch.Tensor, kv: PackedKV, probe_idx: torch.Tenso
     else:
         sargs = (None, None, 1, 1, 0)
     _lib.call("bsa_probe_attention_packed", B, Hq, kv.Hkv, S, D, _dtype_code(q), _ptr(q), float(scale),
-              _ptr(probe_idx), M, _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), C, *sargs, _ptr(od),
-              _ptr(os_), _ptr(workspace), workspace.numel(), _stream())
+              _ptr(probe_idx), M, _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), C, nl, *sargs,
+              _ptr(od), _ptr(os_), _ptr(workspace), workspace.numel(), _stream())
     return od if mask is None else (od, os_)
 
 
-def query_centroids(q: torch.Tensor, layout: ClusterLayout) -> torch.Tensor:
+def query_centroids(q: torch.Tensor, layout: ClusterLayout, Hkv: Optional[int] = None) -> torch.Tensor:
     """Mean query row of every query cluster [B, Hq, Cq, D], rounded to q's dtype: the
-    probes of the error-aware router (bsa_query_centroids)."""
+    probes of the error-aware router (bsa_query_centroids).  With one layout per (batch,
+    K/V head) the query heads of K/V head kvh use layout b * Hkv + kvh."""
     _check_cuda(q)
     B, Hq, S, D = q.shape
+    nl = layout.n_layouts
+    if Hkv is None:
+        Hkv = Hq if nl == 1 else nl // B
     out = torch.empty(B, Hq, layout.C, D, dtype=q.dtype, device=q.device)
-    _lib.call("bsa_query_centroids", B, Hq, S, D, _dtype_code(q), _ptr(q), _ptr(layout.perm), _ptr(layout.offsets),
-              layout.C, _ptr(out), _stream())
+    _lib.call("bsa_query_centroids", B, Hq, Hkv, S, D, _dtype_code(q), _ptr(q), _ptr(layout.perm),
+              _ptr(layout.offsets), layout.C, nl, _ptr(out), _stream())
     return out
 
 
@@ -430,8 +472,8 @@ def block_error(qbar: torch.Tensor, kv: PackedKV, scale: Optional[float] = None,
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, qbar.device)
     _lib.call("bsa_block_error", B, Hq, kv.Hkv, kv.S, D, _dtype_code(qbar), _ptr(qbar), Cq, float(scale),
-              _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), Ck, _ptr(kv.kbar), _ptr(kv.vbar), _ptr(err),
-              _ptr(workspace), workspace.numel(), _stream())
+              _ptr(kv.buffer), kv.buffer.numel(), _ptr(kv.layout.offsets), Ck, kv.layout.n_layouts, _ptr(kv.kbar),
+              _ptr(kv.vbar), _ptr(err), _ptr(workspace), workspace.numel(), _stream())
     return err
 
 
@@ -443,20 +485,25 @@ def error_route(err: torch.Tensor, k_layout: ClusterLayout, budget: int) -> Bloc
     keep = torch.empty(B, H, Cq, Ck, dtype=torch.uint8, device=err.device)
     cnt = torch.empty(B, H, Cq, dtype=torch.int32, device=err.device)
     idx = torch.empty(B, H, Cq, Ck, dtype=torch.int16, device=err.device)
-    _lib.call("bsa_error_route", _ptr(err), B * H * Cq, Ck, _ptr(k_layout.offsets), int(budget), _ptr(keep), _ptr(cnt),
-              _ptr(idx), _stream())
+    nl = k_layout.n_layouts
+    rows_per_layout = 0 if nl == 1 else (B * H * Cq) // nl  # rows of [B, H, Cq] by (batch, K/V head)
+    _lib.call("bsa_error_route", _ptr(err), B * H * Cq, Ck, _ptr(k_layout.offsets), rows_per_layout, int(budget),
+              _ptr(keep), _ptr(cnt), _ptr(idx), _stream())
     return BlockMask(keep, cnt, idx)
 
 
 def probe_fit(o_sparse_probe: torch.Tensor, o_dense_probe: torch.Tensor, weights: torch.Tensor,
               lam: float = 0.1, rank: int = 16) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Folded correction map A [B, Hq, D, D], c [B, Hq, D] from float32 probe rows (bsa_probe_fit)."""
+    """Folded correction map A [B, Hq, D, D], c [B, Hq, D] from float32 probe rows (bsa_probe_fit).
+    weights: [M] for every head, or [B * Hkv, M] for probes chosen per (batch, K/V head)."""
     _check_cuda(o_sparse_probe, o_dense_probe, weights)
     B, Hq, M, D = o_sparse_probe.shape
+    nl = 1 if weights.dim() == 1 else int(weights.shape[0])
+    Hkv = Hq if nl == 1 else nl // B
     A = torch.empty(B, Hq, D, D, dtype=torch.float32, device=o_sparse_probe.device)
     c = torch.empty(B, Hq, D, dtype=torch.float32, device=o_sparse_probe.device)
-    _lib.call("bsa_probe_fit", B, Hq, D, _ptr(o_sparse_probe), _ptr(o_dense_probe), _ptr(weights), M, float(lam),
-              int(rank), _ptr(A), _ptr(c), _stream())
+    _lib.call("bsa_probe_fit", B, Hq, Hkv, D, _ptr(o_sparse_probe), _ptr(o_dense_probe), _ptr(weights), M, nl,
+              float(lam), int(rank), _ptr(A), _ptr(c), _stream())
     return A, c
 
 

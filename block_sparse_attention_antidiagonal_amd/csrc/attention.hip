@@ -589,17 +589,25 @@ __device__ __forceinline__ bool entry_centroid(int e) { return (e & kEntryCentro
 
 // One wave per mask row (four rows per workgroup): writes the row's entries (at most maxe)
 // and their count.  The row's clusters go 64 at a time, one per lane, and a wave scan of their
-// tile counts places their entries.
+// tile counts places their entries.  Mask row (b Hm + hm) Cq + a reads the key layout of its
+// (batch, K/V head) when there is one per head (nl > 1, Hm in {Hkv, Hq}).
 __global__ __launch_bounds__(256) void tile_list_wave_kernel(const int32_t* __restrict__ kv_count,
                                                              const int16_t* __restrict__ kv_idx, int rows, int Ck,
                                                              const int32_t* __restrict__ k_off,
-                                                             const int32_t* __restrict__ tile_off, int first_ctile,
-                                                             int ctiles, int comp, int maxe,
-                                                             int32_t* __restrict__ entries,
+                                                             const int32_t* __restrict__ tile_off, int nl, int Hq,
+                                                             int Hkv, int Hm, int Cq, int first_ctile, int ctiles,
+                                                             int comp, int maxe, int32_t* __restrict__ entries,
                                                              int32_t* __restrict__ counts) {
   const int lane = threadIdx.x & 63;
   const size_t row = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
+  if (nl > 1) {
+    const size_t bh = row / Cq;
+    const int b = static_cast<int>(bh / Hm), hm = static_cast<int>(bh % Hm);
+    const size_t lay = static_cast<size_t>(b) * Hkv + (Hm == Hq ? hm / (Hq / Hkv) : hm);
+    k_off += lay * (Ck + 1);
+    tile_off += lay * (Ck + 1);
+  }
   const int cnt = kv_count[row];
   const int16_t* list = kv_idx + row * Ck;
   int32_t* out = entries + row * maxe;
@@ -961,7 +969,7 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     int Ck, const uint8_t* __restrict__ keep, const int32_t* __restrict__ entries, const int32_t* __restrict__ counts,
     int maxe, int Hm, const uint8_t* __restrict__ tile_flags, const int32_t* __restrict__ hmix,
     const T* __restrict__ Kp, const void* __restrict__ Vtp, int tiles_per_head, int first_ctile,
-    const float* __restrict__ clog2n, const int32_t* __restrict__ order, int32_t* __restrict__ ctl,
+    const float* __restrict__ clog2n, int nl, const int32_t* __restrict__ order, int32_t* __restrict__ ctl,
     const unsigned char* __restrict__ corr_img) {
   using C = Cfg<T, D>;
   using L = AttnLds<T, D, TO, CORR>;
@@ -1015,11 +1023,16 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
   const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
   const uint8_t* keep_row = keep + mrow * Ck;
+  // The query and key layouts of this (batch, K/V head): one shared layout (nl = 1) or its own.
+  const size_t lay = layout_of(nl, bkv);
+  const int32_t* qperm_h = q_perm + lay * S;
+  const int32_t* qoff_h = q_off + lay * (Cq + 1);
+  const float* clog2n_h = clog2n + lay * Ck;
   const int32_t* ent = entries + mrow * maxe;
   const int ecount = counts[mrow];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-  const int q_lo = q_off[a], q_hi = q_off[a + 1];
+  const int q_lo = qoff_h[a], q_hi = qoff_h[a + 1];
 
   // Centroid bias of a tile (log2 n_c where this row's cluster skipped c, -inf otherwise;
   // log2 n_c comes from the pack, -inf for a count of 0).
@@ -1027,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     if (threadIdx.x < kNK) {
       const int cc = ct * kNK + static_cast<int>(threadIdx.x);
       float bv = -INFINITY;
-      if (cc < Ck && keep_row[cc] == 0) bv = clog2n[cc];
+      if (cc < Ck && keep_row[cc] == 0) bv = clog2n_h[cc];
       dst[threadIdx.x] = bv;
     }
   };
@@ -1036,7 +1049,7 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     const int nrows = min(kRowsWG, q_hi - rt);
     // This lane's query row; rows past the cluster reuse row 0 and are not stored.
     const int my = wave * 32 + r;
-    const int qtok = q_perm[rt + (my < nrows ? my : 0)];
+    const int qtok = qperm_h[rt + (my < nrows ? my : 0)];
     Frag<T> qf[C::KK];
     load_q_frags<T, D>(qf, Qh + static_cast<size_t>(qtok) * D);
     // Wait for Q here: otherwise the loop's wait counters, merged over the loop entry, make
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
     for (int idx = threadIdx.x; idx < kRowsWG * ZCPR; idx += kThreads) {
       const int row = idx / ZCPR, ch = idx % ZCPR;
       if (row < nrows) {
-        const int tok = q_perm[rt + row];
+        const int tok = qperm_h[rt + row];
         *reinterpret_cast<uint4*>(Oh + static_cast<size_t>(tok) * D + ch * L::ZEPC) =
             *reinterpret_cast<const uint4*>(Z + row * L::ZROW + ch * L::ZEPC);
       }
@@ -1346,7 +1359,7 @@ struct RowCentroids {
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
     const bf16_t* __restrict__ Q, int Hq, int Hkv, int Sq, float c2, const int32_t* __restrict__ probe_idx, int M,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C, int nl,
     const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
     int tiles_per_head, int tpc, int nchunks, const int32_t* __restrict__ q_labels, const uint8_t* __restrict__ keep,
     int Hm, int Cq, const float* __restrict__ clog2n, int first_ctile, int ctiles, int comp, int words,
@@ -1365,6 +1378,13 @@ __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
   const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
   const unsigned char* Vph = static_cast<const unsigned char*>(Vtp) + bkv * tiles_per_head * kTileBytes;
   const uint8_t* flags_h = tile_flags + bkv * tiles_per_head;
+  // This head's layouts (nl > 1: one per (batch, K/V head), with its own probe rows).
+  const size_t lay = layout_of(nl, bkv);
+  tile_off += lay * (C + 1);
+  k_off += lay * (C + 1);
+  clog2n += lay * C;
+  if (q_labels != nullptr) q_labels += lay * Sq;
+  if (probe_idx != nullptr) probe_idx += lay * M;
   const bool cen = SPARSE && ci == nchunks;  // the centroid chunk
   const int nrows = SPARSE ? 2 * M : M;
   const int nch = SPARSE ? nchunks + 1 : nchunks;
@@ -1576,7 +1596,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void block_error_kernel(
     const bf16_t* __restrict__ Qb, int Hq, int Hkv, int Cq, float c2, const float* __restrict__ O1,
     const float* __restrict__ lse2, const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int Ck,
-    const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
+    int nl, const uint8_t* __restrict__ tile_flags, const bf16_t* __restrict__ Kp, const void* __restrict__ Vtp,
     int tiles_per_head, const float* __restrict__ Kbar, const float* __restrict__ Vbar, float* __restrict__ err) {
   using T = bf16_t;
   using L = AttnLds<T, D, float>;
@@ -1589,6 +1609,8 @@ __global__ __launch_bounds__(kThreads, 2) void block_error_kernel(
   const int chunk = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
   const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
+  tile_off += layout_of(nl, bkv) * (Ck + 1);  // this head's key layout
+  k_off += layout_of(nl, bkv) * (Ck + 1);
   const int c0 = chunk * kErrClusters, nc = min(kErrClusters, Ck - c0);
   const int t = threadIdx.x;
   for (int i = t; i < nc * D; i += kThreads) {
@@ -1735,7 +1757,7 @@ template <typename T, int D, bool COMP, typename TO, bool FAST, bool CORR>
 void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* lse, int B, int Hq, int Hkv, int S,
                            float c2, const int32_t* q_perm, const int32_t* q_off, int Cq, const int32_t* k_off, int Ck,
                            const uint8_t* keep, const int32_t* entries, const int32_t* counts, int maxe, int Hm,
-                           const PackedKV& P, const int32_t* order, int32_t* ctl, int units,
+                           const PackedKV& P, int nl, const int32_t* order, int32_t* ctl, int units,
                            const unsigned char* corr_img) {
   constexpr int LDS = AttnLds<T, D, TO, CORR>::TOTAL;
   auto kern = sparse_attn_kernel<T, D, COMP, TO, FAST, CORR>;
@@ -1743,13 +1765,13 @@ void launch_sparse_variant(hipStream_t stream, const void* Q, void* O, float* ls
   const int grid = min(units, device_cus() * attn_occupancy<T, FAST>());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), LDS, stream, static_cast<const T*>(Q), static_cast<TO*>(O), lse,
                      B, Hq, Hkv, S, c2, q_perm, q_off, Cq, k_off, Ck, keep, entries, counts, maxe, Hm, P.flags, P.hmix,
-                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, P.clog2n, order, ctl,
+                     static_cast<const T*>(P.k), P.v, P.tiles_per_head, P.first_ctile, P.clog2n, nl, order, ctl,
                      corr_img);
 }
 
 template <typename T, int D>
 bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float scale, const int32_t* q_perm,
-                         const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const uint8_t* keep,
+                         const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, int nl, const uint8_t* keep,
                          const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed, bool comp,
                          bool out_f32, const float* A, const float* cvec, void* O, float* lse, void* ws,
                          hipStream_t stream) {
@@ -1757,7 +1779,7 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
   if (nunits > 0x7fffffffLL) return BSA_E_UNSUPPORTED;
   const int units = static_cast<int>(nunits);
   const float c2 = scale * kLog2e;
-  const PackLayout L = pack_layout(B, Hkv, S, D, Ck, sizeof(T));
+  const PackLayout L = pack_layout(B, Hkv, S, D, Ck, sizeof(T), nl);
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const PackedKV P{reinterpret_cast<const int32_t*>(base + L.tile_off),
                    reinterpret_cast<const int32_t*>(base + L.hmix), base + L.flags, base + L.k, base + L.v,
@@ -1779,8 +1801,8 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
     hipLaunchKernelGGL((corr_image_kernel<T, D>), dim3(static_cast<unsigned>(B * Hq)), dim3(256), 0, stream, A, cvec,
                        aimg);
   hipLaunchKernelGGL(tile_list_wave_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream,
-                     kv_count, kv_idx, static_cast<int>(rows), Ck, k_off, P.tile_off, P.first_ctile, P.ctiles,
-                     comp ? 1 : 0, maxe, entries, counts);
+                     kv_count, kv_idx, static_cast<int>(rows), Ck, k_off, P.tile_off, nl, Hq, Hkv, Hm, Cq,
+                     P.first_ctile, P.ctiles, comp ? 1 : 0, maxe, entries, counts);
   constexpr bool kHalf = sizeof(T) == 2;  // float16 products exist for bfloat16 inputs only
   const int per = Cq * (Hq / Hkv);
   const bool sort_ok = per <= kMaxSortUnits;
@@ -1792,11 +1814,11 @@ bsa_status launch_sparse(int B, int Hq, int Hkv, int S, const void* Q, float sca
 #define BSA_LAUNCH(COMP, TO, CORR)                                                                                    \
   do {                                                                                                                 \
     launch_sparse_variant<T, D, COMP, TO, false, CORR>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq,       \
-                                                       k_off, Ck, keep, entries, counts, maxe, Hm, P, order, counter, \
-                                                       units, aimg);                                                  \
+                                                       k_off, Ck, keep, entries, counts, maxe, Hm, P, nl, order,      \
+                                                       counter, units, aimg);                                         \
     if (kHalf)                                                                                                         \
       launch_sparse_variant<T, D, COMP, TO, kHalf, CORR>(stream, Q, O, lse, B, Hq, Hkv, S, c2, q_perm, q_off, Cq,     \
-                                                         k_off, Ck, keep, entries, counts, maxe, Hm, P, order,        \
+                                                         k_off, Ck, keep, entries, counts, maxe, Hm, P, nl, order,    \
                                                          counter, units, aimg);                                       \
   } while (0)
   if (comp) {
@@ -1858,10 +1880,10 @@ inline size_t packed_probe_ws_bytes(int B, int Hq, int D, int M, int first_ctile
 template <int D>
 bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void* Q, float scale,
                                const int32_t* probe_idx, int M, const void* packed, const int32_t* k_off, int C,
-                               float* Od, float* lse2, void* ws, hipStream_t stream,
+                               float* Od, float* lse2, void* ws, hipStream_t stream, int nl,
                                const int32_t* q_labels = nullptr, const uint8_t* keep = nullptr, int Hm = 1,
                                int Cq = 1, bool comp = false, float* Os = nullptr) {
-  const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t));
+  const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t), nl);
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   const int tpc = packed_probe_tpc(PL.first_centroid_tile);
   const int nchunks = packed_probe_chunks(PL.first_centroid_tile);
@@ -1876,7 +1898,7 @@ bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void
   const int LDS = AttnLds<bf16_t, D, float>::BIAS + (4 * kNK + kNK) * 4 + kRowsWG * words * 4;
 #define BSA_PROBE_ARGS                                                                                                \
   static_cast<const bf16_t*>(Q), Hq, Hkv, Sq, scale * kLog2e, probe_idx, M,                                         \
-      reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, C, base + PL.flags,                              \
+      reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, C, nl, base + PL.flags,                          \
       reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v, PL.tiles_per_head, tpc, nchunks, q_labels, keep, Hm, \
       Cq, reinterpret_cast<const float*>(base + PL.clog2n), PL.first_centroid_tile, PL.centroid_tiles, comp ? 1 : 0, \
       words, Opart, mpart, lpart
@@ -1919,7 +1941,7 @@ struct ErrWs {
   size_t part, o1, lse, total;
 };
 inline ErrWs err_ws(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck) {
-  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t));
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t));  // (tile counts do not depend on layouts)
   ErrWs w;
   w.part = 0;
   w.o1 = pack_align(static_cast<size_t>(B) * Hq * packed_probe_chunks(PL.first_centroid_tile) * Cq * (D + 2) *
@@ -1931,25 +1953,25 @@ inline ErrWs err_ws(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck) {
 
 template <int D>
 bsa_status launch_block_error(int B, int Hq, int Hkv, int S, const void* qbar, int Cq, float scale, const void* packed,
-                              const int32_t* k_off, int Ck, const float* Kbar, const float* Vbar, float* err, void* ws,
-                              hipStream_t stream) {
+                              const int32_t* k_off, int Ck, int nl, const float* Kbar, const float* Vbar, float* err,
+                              void* ws, hipStream_t stream) {
   const ErrWs W = err_ws(B, Hq, Hkv, S, D, Cq, Ck);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   float* O1 = reinterpret_cast<float*>(wsb + W.o1);
   float* lse2 = reinterpret_cast<float*>(wsb + W.lse);
   // Pass 1: the probes' dense rows and log-sum-exp (rows 0 .. Cq-1 of qbar).
   const bsa_status st = launch_probe_packed<D>(B, Hq, Hkv, S, Cq, qbar, scale, nullptr, Cq, packed, k_off, Ck, O1,
-                                               lse2, wsb + W.part, stream);
+                                               lse2, wsb + W.part, stream, nl);
   if (st != BSA_OK) return st;
   // Pass 2: the per-block errors.
-  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t));
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t), nl);
   const unsigned char* base = static_cast<const unsigned char*>(packed);
   constexpr int LDS = AttnLds<bf16_t, D, float>::TILES + 2 * kErrClusters * D * 4 + (2 * kErrClusters + 1) * 4;
   auto kern = block_error_kernel<D>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   hipLaunchKernelGGL(kern, dim3((Ck + kErrClusters - 1) / kErrClusters, (Cq + kRowsWG - 1) / kRowsWG, B * Hq),
                      dim3(kThreads), LDS, stream, static_cast<const bf16_t*>(qbar), Hq, Hkv, Cq, scale * kLog2e, O1,
-                     lse2, reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, Ck, base + PL.flags,
+                     lse2, reinterpret_cast<const int32_t*>(base + PL.tile_off), k_off, Ck, nl, base + PL.flags,
                      reinterpret_cast<const bf16_t*>(base + PL.k), base + PL.v, PL.tiles_per_head, Kbar, Vbar, err);
   return launch_status();
 }
@@ -1970,7 +1992,7 @@ extern "C" bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm,
 
 extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
                                            float scale, const int32_t* q_perm, const int32_t* q_offsets, int Cq,
-                                           const int32_t* k_offsets, int Ck, const uint8_t* keep,
+                                           const int32_t* k_offsets, int Ck, int n_layouts, const uint8_t* keep,
                                            const int32_t* kv_count, const int16_t* kv_idx, int Hm,
                                            const void* packed, size_t packed_bytes, int compensate,
                                            const float* A, const float* c, int out_dtype, void* O, float* lse,
@@ -1985,18 +2007,21 @@ extern "C" bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D,
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
+  // Layouts per (batch, K/V head): every mask row then belongs to one of them.
+  if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
+  if (n_layouts > 1 && Hm == 1 && Hkv > 1) return BSA_E_SHAPE;  // Hm must be Hkv or Hq
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   size_t need = 0;
   const bsa_status st = bsa_sparse_attention_workspace_size(B, Hq, Hm, Cq, S, Ck, &need);
   if (st != BSA_OK) return st;
-  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype));
+  const PackLayout PL = pack_layout(B, Hkv, S, D, Ck, dtype_size(dtype), n_layouts);
   if (packed_bytes < PL.total) return BSA_E_WORKSPACE;
   // One head's tiles are addressed with 32-bit byte offsets.
   if (static_cast<size_t>(PL.tiles_per_head) * 64 * D * dtype_size(dtype) > 0x7fffffffu) return BSA_E_UNSUPPORTED;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   const bool out_f32 = out_dtype == BSA_F32 && dtype != BSA_F32;
-#define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep, kv_count, kv_idx, Hm, packed, \
-                 compensate != 0, out_f32, A, c, O, lse, ws, stream
+#define BSA_ARGS B, Hq, Hkv, S, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, n_layouts, keep, kv_count, kv_idx, Hm, \
+                 packed, compensate != 0, out_f32, A, c, O, lse, ws, stream
   if (dtype == BSA_BF16) return D == 128 ? launch_sparse<bf16_t, 128>(BSA_ARGS) : launch_sparse<bf16_t, 64>(BSA_ARGS);
   return D == 128 ? launch_sparse<float, 128>(BSA_ARGS) : launch_sparse<float, 64>(BSA_ARGS);
 #undef BSA_ARGS
@@ -2035,8 +2060,9 @@ extern "C" size_t bsa_sparse_attention_static_scratch_bytes(void) { return kStat
 
 extern "C" bsa_status bsa_sparse_attention_noalloc(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
                                                    float scale, const int32_t* q_perm, const int32_t* q_offsets,
-                                                   int Cq, const int32_t* k_offsets, int Ck, const uint8_t* keep,
-                                                   const int32_t* kv_count, const int16_t* kv_idx, int Hm,
+                                                   int Cq, const int32_t* k_offsets, int Ck, int n_layouts,
+                                                   const uint8_t* keep, const int32_t* kv_count,
+                                                   const int16_t* kv_idx, int Hm,
                                                    const void* packed, size_t packed_bytes, int compensate,
                                                    const float* A, const float* c, int out_dtype, void* O,
                                                    float* lse, hipStream_t stream) {
@@ -2050,9 +2076,9 @@ extern "C" bsa_status bsa_sparse_attention_noalloc(int B, int Hq, int Hkv, int S
   // Every scratch section is written by the call's own kernels before it is read (the lists,
   // ranks, totals, order and queue counters by the list and order kernels, the corrections by
   // corr_image_kernel), so nothing needs clearing between calls.
-  return bsa_sparse_attention(B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, keep,
-                              kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, out_dtype, O, lse, ws,
-                              kStaticScratchBytes, stream);
+  return bsa_sparse_attention(B, Hq, Hkv, S, D, dtype, Q, scale, q_perm, q_offsets, Cq, k_offsets, Ck, n_layouts,
+                              keep, kv_count, kv_idx, Hm, packed, packed_bytes, compensate, A, c, out_dtype, O, lse,
+                              ws, kStaticScratchBytes, stream);
 }
 
 extern "C" bsa_status bsa_probe_attention_workspace_size(int B, int Hq, int S, int D, int M, size_t* bytes) {
@@ -2075,30 +2101,33 @@ extern "C" bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, i
 extern "C" bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q,
                                                  float scale, const int32_t* probe_idx, int M, const void* packed,
                                                  size_t packed_bytes, const int32_t* k_offsets, int C,
-                                                 const int32_t* q_labels, const uint8_t* keep, int Hm, int Cq,
-                                                 int compensate, float* O_dense_probe, float* O_sparse_probe,
-                                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+                                                 int n_layouts, const int32_t* q_labels, const uint8_t* keep, int Hm,
+                                                 int Cq, int compensate, float* O_dense_probe,
+                                                 float* O_sparse_probe, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
   if (dtype != BSA_BF16) return valid_dtype(dtype) ? BSA_E_UNSUPPORTED : BSA_E_DTYPE;
   size_t need = 0;
   const bsa_status st = bsa_probe_attention_packed_workspace_size(B, Hq, Hkv, S, D, M, C, &need);
   if (st != BSA_OK) return st;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (!Q || !probe_idx || !packed || !k_offsets || !O_dense_probe) return BSA_E_ARG;
+  if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
   if (O_sparse_probe != nullptr) {
     if (!q_labels || !keep || Cq < 1) return BSA_E_ARG;
     if (Hm != 1 && Hm != Hkv && Hm != Hq) return BSA_E_SHAPE;
+    if (n_layouts > 1 && Hm == 1 && Hkv > 1) return BSA_E_SHAPE;  // Hm must be Hkv or Hq
     if (C > 1024) return BSA_E_UNSUPPORTED;  // keep bits of 128 rows in LDS
   }
   if (M > 1024) return BSA_E_UNSUPPORTED;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
-  if (packed_bytes < pack_layout(B, Hkv, S, D, C, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
+  if (packed_bytes < pack_layout(B, Hkv, S, D, C, sizeof(bf16_t), n_layouts).total) return BSA_E_WORKSPACE;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
   return D == 128 ? launch_probe_packed<128>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
-                                             O_dense_probe, nullptr, ws, stream, q_labels, keep, Hm, Cq,
+                                             O_dense_probe, nullptr, ws, stream, n_layouts, q_labels, keep, Hm, Cq,
                                              compensate != 0, O_sparse_probe)
                   : launch_probe_packed<64>(B, Hq, Hkv, S, S, Q, scale, probe_idx, M, packed, k_offsets, C,
-                                            O_dense_probe, nullptr, ws, stream, q_labels, keep, Hm, Cq,
+                                            O_dense_probe, nullptr, ws, stream, n_layouts, q_labels, keep, Hm, Cq,
                                             compensate != 0, O_sparse_probe);
 }
 
@@ -2141,20 +2170,21 @@ extern "C" bsa_status bsa_block_error_workspace_size(int B, int Hq, int Hkv, int
 
 extern "C" bsa_status bsa_block_error(int B, int Hq, int Hkv, int S, int D, int dtype, const void* qbar, int Cq,
                                       float scale, const void* packed, size_t packed_bytes, const int32_t* k_offsets,
-                                      int Ck, const float* Kbar, const float* Vbar, float* err, void* ws,
-                                      size_t ws_bytes, hipStream_t stream) {
+                                      int Ck, int n_layouts, const float* Kbar, const float* Vbar, float* err,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   if (dtype != BSA_BF16) return valid_dtype(dtype) ? BSA_E_UNSUPPORTED : BSA_E_DTYPE;
   size_t need = 0;
   const bsa_status st = bsa_block_error_workspace_size(B, Hq, Hkv, S, D, Cq, Ck, &need);
   if (st != BSA_OK) return st;
   if (Hq % Hkv != 0) return BSA_E_SHAPE;
   if (!qbar || !packed || !k_offsets || !Kbar || !Vbar || !err) return BSA_E_ARG;
+  if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return BSA_E_ARG;
-  if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t)).total) return BSA_E_WORKSPACE;
+  if (packed_bytes < pack_layout(B, Hkv, S, D, Ck, sizeof(bf16_t), n_layouts).total) return BSA_E_WORKSPACE;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hq > 65535) return BSA_E_UNSUPPORTED;
-  return D == 128 ? launch_block_error<128>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, Kbar, Vbar, err, ws,
-                                            stream)
-                  : launch_block_error<64>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, Kbar, Vbar, err, ws,
-                                           stream);
+  return D == 128 ? launch_block_error<128>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, n_layouts, Kbar,
+                                            Vbar, err, ws, stream)
+                  : launch_block_error<64>(B, Hq, Hkv, S, qbar, Cq, scale, packed, k_offsets, Ck, n_layouts, Kbar,
+                                           Vbar, err, ws, stream);
 }

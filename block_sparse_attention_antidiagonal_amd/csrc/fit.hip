@@ -118,8 +118,8 @@ __device__ __forceinline__ void gram64(const float (*X)[128 + 1], int D, double 
 __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __restrict__ Os,
                                                                  const float* __restrict__ Od,
                                                                  const float* __restrict__ weights, int D, int M,
-                                                                 float lambda, int rank, float* __restrict__ Aout,
-                                                                 float* __restrict__ cout) {
+                                                                 int Hq, int Hkv, int nl, float lambda, int rank,
+                                                                 float* __restrict__ Aout, float* __restrict__ cout) {
   static_assert(kFitThreads == 256, "the 4 x 4 blocking assumes 256 threads");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FitSmem& sm = *reinterpret_cast<FitSmem*>(smem_raw);
@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   const int t = threadIdx.x;
   const float* Osh = Os + static_cast<size_t>(bh) * M * D;
   const float* Odh = Od + static_cast<size_t>(bh) * M * D;
+  if (nl > 1) weights += ((bh / Hq) * static_cast<size_t>(Hkv) + (bh % Hq) / (Hq / Hkv)) * M;  // the head's layout
 
   // Raw rows into LDS (rows past M are zero), normalized weights.
   for (int e = t; e < kN * D; e += kFitThreads) {
@@ -731,10 +732,12 @@ __global__ __launch_bounds__(128) void gather_rows_kernel(const float* __restric
 
 using namespace bsa;
 
-extern "C" bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_probe, const float* O_dense_probe,
-                                    const float* weights, int M, float lambda, int rank, float* A, float* c,
-                                    hipStream_t stream) {
-  if (B < 1 || Hq < 1 || !O_sparse_probe || !O_dense_probe || !weights || !A || !c) return BSA_E_ARG;
+extern "C" bsa_status bsa_probe_fit(int B, int Hq, int Hkv, int D, const float* O_sparse_probe,
+                                    const float* O_dense_probe, const float* weights, int M, int n_layouts,
+                                    float lambda, int rank, float* A, float* c, hipStream_t stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || !O_sparse_probe || !O_dense_probe || !weights || !A || !c) return BSA_E_ARG;
+  if (Hq % Hkv != 0) return BSA_E_SHAPE;
+  if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   if (M < 2) return BSA_E_ARG;
   if (M > kMaxM) return BSA_E_UNSUPPORTED;
@@ -744,7 +747,7 @@ extern "C" bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_
   const int smem = static_cast<int>(sizeof(FitSmem));
   hipFuncSetAttribute(reinterpret_cast<const void*>(probe_fit_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   hipLaunchKernelGGL(probe_fit_kernel, dim3(B * Hq), dim3(kFitThreads), smem, stream, O_sparse_probe, O_dense_probe,
-                     weights, D, M, lambda, rank, A, c);
+                     weights, D, M, Hq, Hkv, n_layouts, lambda, rank, A, c);
   return launch_status();
 }
 

@@ -66,27 +66,118 @@ __global__ __launch_bounds__(256) void centroid_kernel(const T* __restrict__ K, 
   }
 }
 
+// Member of cluster position k in the middle-out order of a cluster of n members: m = n / 2
+// first, then m-1, m+1, m-2, m+2, ... while both sides last, then the longer side outwards.
+__device__ __forceinline__ int middle_out_member(int n, int k) {
+  const int m = n / 2, below = m, above = n - 1 - m;
+  if (k == 0) return m;
+  const int both = below < above ? below : above;
+  const int j = k - 1;
+  if (j < 2 * both) return (j % 2 == 0) ? m - (j / 2 + 1) : m + (j / 2 + 1);
+  const int d = both + 1 + (j - 2 * both);
+  return below > above ? m - d : m + d;
+}
+
+// Probe rows of every layout from its cluster layout (the rule of bsa_select_probe_rows, the
+// members in the layout's stable order): one thread per layout walks the rounds.  Rounds after
+// a partial first one visit every non-empty cluster; cluster a takes part in round r while it
+// has more than r members.
+__global__ __launch_bounds__(64) void select_probes_kernel(int P, int S, int C, int M, const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ probe_idx,
+                                                           float* __restrict__ weights) {
+  const int p = blockIdx.x * 64 + threadIdx.x;
+  if (p >= P) return;
+  const int32_t* off = offsets + static_cast<size_t>(p) * (C + 1);
+  const int32_t* pp = perm + static_cast<size_t>(p) * S;
+  int32_t* idx = probe_idx + static_cast<size_t>(p) * M;
+  float* w = weights + static_cast<size_t>(p) * M;
+  int nne = 0, maxn = 0;
+  for (int a = 0; a < C; ++a) {
+    const int n = off[a + 1] - off[a];
+    nne += n > 0 ? 1 : 0;
+    maxn = max(maxn, n);
+  }
+  int taken = 0;
+  if (M < nne) {  // one partial round over evenly spaced non-empty clusters, one probe each
+    int a = 0, seen = 0;  // the seen-th non-empty cluster is a
+    while (off[a + 1] <= off[a]) ++a;
+    for (int j = 0; j < M; ++j) {
+      const int k = static_cast<int>(floor((j + 0.5) * static_cast<double>(nne) / M));
+      while (seen < k) {
+        ++a;
+        while (off[a + 1] <= off[a]) ++a;
+        ++seen;
+      }
+      const int n = off[a + 1] - off[a];
+      idx[j] = pp[off[a] + middle_out_member(n, 0)];
+      w[j] = static_cast<float>(n);  // |G_a| / 1
+    }
+  }
+  if (M >= nne) {
+    // Full rounds: round r takes member r (middle-out) of every non-empty cluster with more
+    // than r members, in cluster order, until M probes are taken; the last probe is taken in
+    // round R from cluster a_last.
+    int R = 0, a_last = 0;
+    for (int r = 0; r < maxn && taken < M; ++r)
+      for (int a = 0; a < C && taken < M; ++a) {
+        const int n = off[a + 1] - off[a];
+        if (n > r) {
+          idx[taken++] = pp[off[a] + middle_out_member(n, r)];
+          R = r;
+          a_last = a;
+        }
+      }
+    // Weights |G_a| / m_a, m_a = the rounds cluster a took part in: every round before R it had
+    // members for, and round R if it came up before the last probe.
+    int t = 0;
+    for (int r = 0; r < maxn && t < M; ++r)
+      for (int a = 0; a < C && t < M; ++a) {
+        const int n = off[a + 1] - off[a];
+        if (n > r) {
+          const int m_a = min(n, R) + ((n > R && a <= a_last) ? 1 : 0);
+          w[t++] = static_cast<float>(static_cast<double>(n) / m_a);
+        }
+      }
+    for (; taken < M; ++taken) {  // fewer members than probes (labels outside [0, C)): padding
+      idx[taken] = 0;
+      w[taken] = 0.0f;
+    }
+  }
+  double total = 0.0;
+  for (int j = 0; j < M; ++j) total += static_cast<double>(w[j]);
+  for (int j = 0; j < M; ++j) w[j] = total > 0.0 ? static_cast<float>(static_cast<double>(w[j]) / total) : 0.0f;
+}
+
 }  // namespace
 }  // namespace bsa
 
 using namespace bsa;
 
-extern "C" bsa_status bsa_cluster_layout_workspace_size(int S, int C, size_t* bytes) {
-  if (!bytes || S < 1 || C < 1) return BSA_E_ARG;
-  if (C > kMaxC) return BSA_E_UNSUPPORTED;
-  const size_t nchunks = (static_cast<size_t>(S) + kChunk - 1) / kChunk;
-  *bytes = nchunks * static_cast<size_t>(C) * sizeof(int32_t);
+extern "C" bsa_status bsa_cluster_layout_workspace_size(int P, int S, int C, size_t* bytes) {
+  if (!bytes || P < 1 || S < 1 || C < 1) return BSA_E_ARG;
+  if (C > kMaxC || P > 65535) return BSA_E_UNSUPPORTED;
+  *bytes = static_cast<size_t>(P) * layout_chunks(S) * static_cast<size_t>(C) * sizeof(int32_t);
   return BSA_OK;
 }
 
-extern "C" bsa_status bsa_cluster_layout(const int32_t* labels, int S, int C, int32_t* perm, int32_t* offsets,
+extern "C" bsa_status bsa_cluster_layout(int P, const int32_t* labels, int S, int C, int32_t* perm, int32_t* offsets,
                                          int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream) {
   size_t need = 0;
-  bsa_status st = bsa_cluster_layout_workspace_size(S, C, &need);
+  bsa_status st = bsa_cluster_layout_workspace_size(P, S, C, &need);
   if (st != BSA_OK) return st;
   if (!labels || !perm || !offsets || !counts) return BSA_E_ARG;
   if (!ws || ws_bytes < need) return BSA_E_WORKSPACE;
-  launch_layouts(labels, S, C, 1, static_cast<int32_t*>(ws), perm, offsets, counts, stream);
+  launch_layouts(labels, S, C, P, static_cast<int32_t*>(ws), perm, offsets, counts, stream);
+  return launch_status();
+}
+
+extern "C" bsa_status bsa_select_probe_rows_layouts(int P, int S, int C, int M, const int32_t* perm,
+                                                    const int32_t* offsets, int32_t* probe_idx, float* weights,
+                                                    hipStream_t stream) {
+  if (!perm || !offsets || !probe_idx || !weights || P < 1 || S < 1 || C < 1 || M < 1 || M > S) return BSA_E_ARG;
+  hipLaunchKernelGGL(select_probes_kernel, dim3((P + 63) / 64), dim3(64), 0, stream, P, S, C, M, perm, offsets,
+                     probe_idx, weights);
   return launch_status();
 }
 

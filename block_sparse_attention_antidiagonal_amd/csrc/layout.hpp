@@ -74,76 +74,17 @@ __global__ __launch_bounds__(1024) void layout_scan(int C, int nchunks, int32_t*
   if (threadIdx.x == blockDim.x - 1) offsets[C] = part[blockDim.x - 1];
 }
 
-// Stable scatter: the rank of token p among earlier tokens of its chunk with the same label.
-// The chunk is cut into 64-token segments, one wave each: inside a segment, one ballot per
-// distinct label gives every lane its rank among earlier lanes and the label's count, which
-// the segment lists in LDS; a token's rank adds the counts of its label in earlier segments.
-// The work grows with the number of distinct labels per segment (a few for tile labels).
-constexpr int kSeg = 64;
-constexpr int kSegs = kChunk / kSeg;
-__global__ __launch_bounds__(256) void layout_scatter(const int32_t* __restrict__ labels, int S, int C, int nchunks,
-                                                       const int32_t* __restrict__ base, int32_t* __restrict__ perm) {
-  labels += static_cast<size_t>(blockIdx.y) * S;  // layout blockIdx.y of a batch
-  base += static_cast<size_t>(blockIdx.y) * nchunks * C;
-  perm += static_cast<size_t>(blockIdx.y) * S;
-  __shared__ int32_t seg_lab[kSegs][kSeg];  // distinct labels of each segment
-  __shared__ int32_t seg_cnt[kSegs][kSeg];  // and their counts
-  __shared__ int32_t seg_n[kSegs];
-  constexpr int kWaves = 256 / 64;
-  const int start = blockIdx.x * kChunk;
-  const int n = min(kChunk, S - start);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int lab_r[kSegs / kWaves], rank_r[kSegs / kWaves];
-#pragma unroll
-  for (int k = 0; k < kSegs / kWaves; ++k) {
-    const int seg = wave + k * kWaves;
-    const int i = seg * kSeg + lane;
-    int li = i < n ? labels[start + i] : -1;
-    if (li < 0 || li >= C) li = -1;
-    int rank = 0, nd = 0;
-    unsigned long long left = __ballot(li >= 0);
-    while (left) {
-      const int leader = __ffsll(static_cast<long long>(left)) - 1;
-      const int l = __builtin_amdgcn_readlane(li, leader);
-      const unsigned long long m = __ballot(li == l);
-      if (li == l) rank = __popcll(m & below);
-      if (lane == 0) {
-        seg_lab[seg][nd] = l;
-        seg_cnt[seg][nd] = __popcll(m);
-      }
-      ++nd;
-      left &= ~m;
-    }
-    if (lane == 0) seg_n[seg] = nd;
-    lab_r[k] = li;
-    rank_r[k] = rank;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kSegs / kWaves; ++k) {
-    const int seg = wave + k * kWaves;
-    const int li = lab_r[k];
-    int pre = 0;
-    for (int s2 = 0; s2 < seg; ++s2) {
-      const int nd = seg_n[s2];
-      for (int d = 0; d < nd; ++d) pre += seg_lab[s2][d] == li ? seg_cnt[s2][d] : 0;
-    }
-    if (li >= 0) perm[base[static_cast<size_t>(blockIdx.x) * C + li] + pre + rank_r[k]] = start + seg * kSeg + lane;
-  }
-}
-
-// The same stable scatter for labels that change from token to token (k-means labels: dozens
-// of distinct labels in every 64 tokens).  Wave w owns sub-chunk w (256 tokens, 4 segments
+// Stable scatter: a token's place is its chunk's base for its label plus the number of earlier
+// tokens of the chunk with the same label.  Wave w owns sub-chunk w (256 tokens, 4 segments
 // of 64) and walks its segments in order: one ballot per distinct label of a segment gives
 // every lane its rank among the earlier lanes with its label, to which it adds the wave's
 // running count of that label (LDS), which the label's first lane then advances.  After all
 // waves are done, a token adds the counts of its label in the earlier sub-chunks.  Dynamic
 // LDS: 4 C ints.
 constexpr int kSub = 256;
-__global__ __launch_bounds__(256) void layout_scatter_many(const int32_t* __restrict__ labels, int S, int C,
-                                                            int nchunks, const int32_t* __restrict__ base,
-                                                            int32_t* __restrict__ perm) {
+__global__ __launch_bounds__(256) void layout_scatter(const int32_t* __restrict__ labels, int S, int C,
+                                                       int nchunks, const int32_t* __restrict__ base,
+                                                       int32_t* __restrict__ perm) {
   extern __shared__ int32_t sub_counts[];  // [4][C]: running, then total, counts per sub-chunk
   labels += static_cast<size_t>(blockIdx.y) * S;
   base += static_cast<size_t>(blockIdx.y) * nchunks * C;
@@ -188,22 +129,16 @@ __global__ __launch_bounds__(256) void layout_scatter_many(const int32_t* __rest
 
 inline int layout_chunks(int S) { return (S + kChunk - 1) / kChunk; }
 
-// P layouts of S labels into C clusters; hist holds P * layout_chunks(S) * C ints.  many_labels
-// picks the scatter for labels that vary from token to token.
+// P layouts of S labels into C clusters; hist holds P * layout_chunks(S) * C ints.
 inline void launch_layouts(const int32_t* labels, int S, int C, int P, int32_t* hist, int32_t* perm,
-                           int32_t* offsets, int32_t* counts, hipStream_t stream, bool many_labels = false) {
+                           int32_t* offsets, int32_t* counts, hipStream_t stream) {
   const int nchunks = layout_chunks(S);
   hipLaunchKernelGGL(layout_hist, dim3(nchunks, P), dim3(256), 0, stream, labels, S, C, nchunks, hist);
   hipLaunchKernelGGL(layout_scan, dim3(P), dim3(1024), 0, stream, C, nchunks, hist, offsets, counts);
-  if (many_labels) {
-    const size_t lds = static_cast<size_t>((kChunk / kSub) * C) * sizeof(int32_t);
-    hipFuncSetAttribute(reinterpret_cast<const void*>(layout_scatter_many),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    hipLaunchKernelGGL(layout_scatter_many, dim3(nchunks, P), dim3(kSub), lds, stream, labels, S, C, nchunks, hist,
-                       perm);
-  } else {
-    hipLaunchKernelGGL(layout_scatter, dim3(nchunks, P), dim3(256), 0, stream, labels, S, C, nchunks, hist, perm);
-  }
+  const size_t lds = static_cast<size_t>((kChunk / kSub) * C) * sizeof(int32_t);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(layout_scatter), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      static_cast<int>(lds));
+  hipLaunchKernelGGL(layout_scatter, dim3(nchunks, P), dim3(kSub), lds, stream, labels, S, C, nchunks, hist, perm);
 }
 
 }  // namespace

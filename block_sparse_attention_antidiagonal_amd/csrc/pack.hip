@@ -32,13 +32,19 @@ constexpr int kPackThreads = 256;
 
 // tile_off[c] = first tile of cluster c (exclusive prefix of ceil(n_c / 64)); clears the
 // per-head format summary hmix[nh]; clog2n[c] = log2 of the centroid count (the caller's
-// counts when given, else the cluster size), -inf for 0.  One workgroup.
+// counts when given, else the cluster size), -inf for 0.  One workgroup per key layout.
 __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __restrict__ offsets, int C,
                                                              const int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ tile_off, int32_t* __restrict__ hmix,
                                                              int nh, float* __restrict__ clog2n) {
   __shared__ int32_t part[1024];
-  for (int i = threadIdx.x; i < nh; i += blockDim.x) hmix[i] = 0;
+  const size_t lay = blockIdx.x;
+  offsets += lay * (C + 1);
+  tile_off += lay * (C + 1);
+  clog2n += lay * C;
+  if (counts != nullptr) counts += lay * C;
+  if (lay == 0)
+    for (int i = threadIdx.x; i < nh; i += blockDim.x) hmix[i] = 0;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     const int n = counts != nullptr ? counts[c] : offsets[c + 1] - offsets[c];
     clog2n[c] = n > 0 ? __log2f(static_cast<float>(n)) : -INFINITY;
@@ -88,7 +94,7 @@ struct PackSmem {
 template <typename T, int D>
 __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int S, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, int C, const int32_t* __restrict__ tile_off, int tiles_per_head,
+    const int32_t* __restrict__ offsets, int C, int nl, const int32_t* __restrict__ tile_off, int tiles_per_head,
     T* __restrict__ Kp, uint16_t* __restrict__ Vtp16, float* __restrict__ Vtp32, uint8_t* __restrict__ flags,
     int32_t* __restrict__ hmix, float* __restrict__ Kbar, float* __restrict__ Vbar) {
   // Kbar == nullptr: the caller gives the centroids; only the token tiles are written.
@@ -108,6 +114,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
   float* red = reinterpret_cast<float*>(smem);               // [2][kKeyGroups][D], after the tiles
   const int c = blockIdx.x;
   const size_t bh = blockIdx.y;
+  const size_t lay = layout_of(nl, bh);  // this head's key layout
+  perm += lay * S;
+  offsets += lay * (C + 1);
+  tile_off += lay * (C + 1);
   const int lo = offsets[c], n = offsets[c + 1] - lo;
   const int t = threadIdx.x, ch = t % CPR, kg = t / CPR;
   const T* Kh = K + bh * static_cast<size_t>(S) * D;
@@ -250,12 +260,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_centroid_kernel(
   }
 }
 
-// given == true: Kbar, Vbar and counts are the caller's (read only).
+// given == true: Kbar, Vbar and counts are the caller's (read only).  nl key layouts (1 or
+// B * Hkv): perm [nl][S], offsets [nl][C + 1], counts [nl][C].
 template <typename T, int D>
 bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, const int32_t* perm,
-                       const int32_t* offsets, int C, const float* Kbar, const float* Vbar, const int32_t* counts,
-                       bool given, void* packed, hipStream_t stream) {
-  const PackLayout L = pack_layout(B, Hkv, S, D, C, sizeof(T));
+                       const int32_t* offsets, int C, int nl, const float* Kbar, const float* Vbar,
+                       const int32_t* counts, bool given, void* packed, hipStream_t stream) {
+  const PackLayout L = pack_layout(B, Hkv, S, D, C, sizeof(T), nl);
   unsigned char* base = static_cast<unsigned char*>(packed);
   int32_t* tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
   uint8_t* flags = base + L.flags;
@@ -264,10 +275,11 @@ bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, cons
   uint16_t* V16 = reinterpret_cast<uint16_t*>(base + L.v);
   float* V32 = reinterpret_cast<float*>(base + L.v);
   float* clog2n = reinterpret_cast<float*>(base + L.clog2n);
-  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, C, given ? counts : nullptr,
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(nl), dim3(1024), 0, stream, offsets, C, given ? counts : nullptr,
                      tile_off, hmix, B * Hkv, clog2n);
   hipLaunchKernelGGL((pack_cluster_kernel<T, D>), dim3(C, B * Hkv), dim3(kPackThreads), 0, stream,
-                     static_cast<const T*>(K), static_cast<const T*>(V), S, perm, offsets, C, tile_off, L.tiles_per_head,
+                     static_cast<const T*>(K), static_cast<const T*>(V), S, perm, offsets, C, nl, tile_off,
+                     L.tiles_per_head,
                      Kp, V16, V32, flags, hmix, given ? nullptr : const_cast<float*>(Kbar),
                      given ? nullptr : const_cast<float*>(Vbar));
   hipLaunchKernelGGL((pack_centroid_kernel<T, D>), dim3(L.centroid_tiles, B * Hkv), dim3(kPackThreads), 0, stream,
@@ -280,25 +292,27 @@ bsa_status launch_pack(int B, int Hkv, int S, const void* K, const void* V, cons
 
 using namespace bsa;
 
-extern "C" bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, size_t* bytes) {
+extern "C" bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, int n_layouts,
+                                                 size_t* bytes) {
   if (!bytes || B < 1 || Hkv < 1 || S < 1 || C < 1) return BSA_E_ARG;
+  if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
   if (!valid_dtype(dtype)) return BSA_E_DTYPE;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   if (C > 32767) return BSA_E_UNSUPPORTED;
-  *bytes = pack_layout(B, Hkv, S, D, C, dtype_size(dtype)).total;
+  *bytes = pack_layout(B, Hkv, S, D, C, dtype_size(dtype), n_layouts).total;
   return BSA_OK;
 }
 
 extern "C" bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
-                                  const int32_t* perm, const int32_t* offsets, int C, float* Kbar, float* Vbar,
-                                  void* packed, size_t packed_bytes, hipStream_t stream) {
+                                  const int32_t* perm, const int32_t* offsets, int C, int n_layouts, float* Kbar,
+                                  float* Vbar, void* packed, size_t packed_bytes, hipStream_t stream) {
   size_t need = 0;
-  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, &need);
+  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, n_layouts, &need);
   if (st != BSA_OK) return st;
   if (!K || !V || !perm || !offsets || !Kbar || !Vbar) return BSA_E_ARG;
   if (!packed || packed_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hkv > 65535) return BSA_E_UNSUPPORTED;
-#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, nullptr, false, packed, stream
+#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, n_layouts, Kbar, Vbar, nullptr, false, packed, stream
   if (dtype == BSA_BF16)
     return D == 128 ? launch_pack<bf16_t, 128>(BSA_PACK_ARGS) : launch_pack<bf16_t, 64>(BSA_PACK_ARGS);
   return D == 128 ? launch_pack<float, 128>(BSA_PACK_ARGS) : launch_pack<float, 64>(BSA_PACK_ARGS);
@@ -306,16 +320,16 @@ extern "C" bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const
 }
 
 extern "C" bsa_status bsa_kv_pack_centroids(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
-                                            const int32_t* perm, const int32_t* offsets, int C, const float* Kbar,
-                                            const float* Vbar, const int32_t* counts, void* packed,
-                                            size_t packed_bytes, hipStream_t stream) {
+                                            const int32_t* perm, const int32_t* offsets, int C, int n_layouts,
+                                            const float* Kbar, const float* Vbar, const int32_t* counts,
+                                            void* packed, size_t packed_bytes, hipStream_t stream) {
   size_t need = 0;
-  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, &need);
+  bsa_status st = bsa_kv_pack_workspace_size(B, Hkv, S, D, dtype, C, n_layouts, &need);
   if (st != BSA_OK) return st;
   if (!K || !V || !perm || !offsets || !Kbar || !Vbar || !counts) return BSA_E_ARG;
   if (!packed || packed_bytes < need) return BSA_E_WORKSPACE;
   if (static_cast<long long>(B) * Hkv > 65535) return BSA_E_UNSUPPORTED;
-#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, Kbar, Vbar, counts, true, packed, stream
+#define BSA_PACK_ARGS B, Hkv, S, K, V, perm, offsets, C, n_layouts, Kbar, Vbar, counts, true, packed, stream
   if (dtype == BSA_BF16)
     return D == 128 ? launch_pack<bf16_t, 128>(BSA_PACK_ARGS) : launch_pack<bf16_t, 64>(BSA_PACK_ARGS);
   return D == 128 ? launch_pack<float, 128>(BSA_PACK_ARGS) : launch_pack<float, 64>(BSA_PACK_ARGS);

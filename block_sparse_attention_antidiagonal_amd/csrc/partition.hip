@@ -461,7 +461,7 @@ void launch_kmeans(const float* X, int N, int nf, int C, int P, int iters, int32
   hipLaunchKernelGGL(init_centres_kernel, dim3(C, P), dim3(kF), 0, stream, X, N, C, cen);
   for (int it = 0; it < iters; ++it) {
     assign();
-    launch_layouts(labels, N, C, P, w.hist, w.perm, w.offsets, w.counts, stream, true);
+    launch_layouts(labels, N, C, P, w.hist, w.perm, w.offsets, w.counts, stream);
     hipLaunchKernelGGL((segment_mean_kernel<float, kF, true>), dim3(C, P), dim3(256), 0, stream, X, N, w.perm,
                        w.offsets, C, cen);
   }
@@ -551,7 +551,7 @@ extern "C" bsa_status bsa_response_partition(int B, int Hq, int Hkv, int S, int 
     hipLaunchKernelGGL((sample_queries_kernel<T, DD>), dim3(P), dim3(DD), 0, stream, Qt, Hq, Hkv, S, rK, qs);        \
     PROFILE;                                                                                                         \
     launch_kmeans(X, S, rK, Ck, P, iters, k_labels, kcen, kw, stream);                                               \
-    launch_layouts(k_labels, S, Ck, P, kw.hist, kw.perm, kw.offsets, kw.counts, stream, true);                      \
+    launch_layouts(k_labels, S, Ck, P, kw.hist, kw.perm, kw.offsets, kw.counts, stream);                      \
     hipLaunchKernelGGL((segment_mean_kernel<T, DD, false>), dim3(Ck, P), dim3(256), 0, stream, Kt, S, kw.perm,       \
                        kw.offsets, Ck, kbar);                                                                        \
     COORDS;                                                                                                          \

@@ -267,14 +267,15 @@ __global__ __launch_bounds__(256) void top_p_wave_kernel(const float* __restrict
 // Error-aware routes for rows of at most 256 clusters: one wave per row, as top_p_wave_kernel
 // (keys: err / n_c as in error_route_kernel; the prefix sum counts keys).
 __global__ __launch_bounds__(256) void error_route_wave_kernel(const float* __restrict__ err, int rows, int Ck,
-                                                               const int32_t* __restrict__ k_off, int budget,
-                                                               uint8_t* __restrict__ keep,
+                                                               const int32_t* __restrict__ k_off, int rows_per_layout,
+                                                               int budget, uint8_t* __restrict__ keep,
                                                                int32_t* __restrict__ kv_count,
                                                                int16_t* __restrict__ kv_idx) {
   __shared__ uint8_t kb_s[4][kWaveCk];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;
   if (row >= static_cast<size_t>(rows)) return;  // whole waves only; no barrier below
+  if (rows_per_layout > 0) k_off += (row / rows_per_layout) * (Ck + 1);  // the row's key layout
   const float* erow = err + row * Ck;
   uint64_t key[4];
 #pragma unroll
@@ -369,14 +370,16 @@ __global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restri
 // is the same along the row -- and the shortest prefix whose key count reaches `budget`
 // tokens, at least one cluster.  Empty clusters are never kept.
 __global__ __launch_bounds__(256) void error_route_kernel(const float* __restrict__ err, int Ck,
-                                                          const int32_t* __restrict__ k_off, int budget,
-                                                          uint8_t* __restrict__ keep, int32_t* __restrict__ kv_count,
+                                                          const int32_t* __restrict__ k_off, int rows_per_layout,
+                                                          int budget, uint8_t* __restrict__ keep,
+                                                          int32_t* __restrict__ kv_count,
                                                           int16_t* __restrict__ kv_idx) {
   __shared__ uint64_t key[kMaxCk];
   __shared__ int csum[kMaxCk];
   __shared__ int tmpi[256];
   __shared__ uint8_t kb[kMaxCk];
   const size_t row = blockIdx.x;
+  if (rows_per_layout > 0) k_off += (row / rows_per_layout) * (Ck + 1);  // the row's key layout
   const float* erow = err + row * Ck;
   int n2 = 1;
   while (n2 < Ck) n2 <<= 1;
@@ -503,16 +506,18 @@ extern "C" bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int3
   return launch_status();
 }
 
-extern "C" bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int budget,
-                                      uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream) {
+extern "C" bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int rows_per_layout,
+                                      int budget, uint8_t* keep, int32_t* kv_count, int16_t* kv_idx,
+                                      hipStream_t stream) {
   if (!err || !k_offsets || !keep || !kv_count || !kv_idx || rows < 1 || Ck < 1) return BSA_E_ARG;
+  if (rows_per_layout < 0 || (rows_per_layout > 0 && rows % rows_per_layout != 0)) return BSA_E_ARG;
   if (Ck > kMaxCk) return BSA_E_UNSUPPORTED;
   if (Ck <= kWaveCk) {
     hipLaunchKernelGGL(error_route_wave_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, err, rows, Ck, k_offsets,
-                       budget, keep, kv_count, kv_idx);
+                       rows_per_layout, budget, keep, kv_count, kv_idx);
     return launch_status();
   }
-  hipLaunchKernelGGL(error_route_kernel, dim3(rows), dim3(256), 0, stream, err, Ck, k_offsets, budget, keep, kv_count,
-                     kv_idx);
+  hipLaunchKernelGGL(error_route_kernel, dim3(rows), dim3(256), 0, stream, err, Ck, k_offsets, rows_per_layout, budget,
+                     keep, kv_count, kv_idx);
   return launch_status();
 }

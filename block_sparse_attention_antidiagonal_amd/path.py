@@ -35,10 +35,12 @@ class PathConfig:
     Hkv: int
     S: int
     D: int
-    labels: np.ndarray  # int32 [S] (host)
+    labels: np.ndarray  # int32 [S] (host); unused by "partitioned" (its labels come from the call)
     C: int
     scale: float
-    mask_mode: str  # "given", "scored" or "routed" (error-aware routes under route_density)
+    # "given", "scored", "routed" (error-aware routes under route_density) or "partitioned"
+    # (response-coupled partitions per (batch, K/V head), then error-aware routes)
+    mask_mode: str
     keep: Optional[np.ndarray] = None  # given mode: uint8 [B or 1, Hm, C, C]
     block: int = 128
     stride: int = 16
@@ -50,7 +52,8 @@ class PathConfig:
     lam: float = 0.1
     rank: int = 16
     overlap: bool = True  # the pack on a second stream, beside scores and top-p
-    route_density: float = 0.2  # routed mode: keys each row computes exactly, as a fraction of S
+    route_density: float = 0.2  # routed modes: executed-pair density (probe rows included), a fraction of S
+    partition_iters: int = 4  # partitioned mode: Lloyd iterations of each grouping
 
     @classmethod
     def from_workload(cls, wl) -> "PathConfig":
@@ -88,12 +91,13 @@ class SparseAttentionPath:
         self._scores = None  # score rows kept across calls when a mask cache is used
         self._probe_ws = None  # dense probe partials (bfloat16 inputs)
         self.labels = torch.as_tensor(np.ascontiguousarray(cfg.labels, dtype=np.int32)).to(self.device)
-        if cfg.mask_mode not in ("given", "scored", "routed"):
+        if cfg.mask_mode not in ("given", "scored", "routed", "partitioned"):
             raise ValueError(f"unknown mask mode {cfg.mask_mode!r}")
-        self._err_ws = None  # routed mode: block-error workspace
-        if cfg.mask_mode == "routed":
+        self._err_ws = None  # routed modes: block-error workspace
+        self._part_ws = None  # partitioned mode: partition workspace
+        if cfg.mask_mode in ("routed", "partitioned"):
             if cfg.D not in (64, 128) or not 0.0 <= cfg.route_density <= 1.0:
-                raise ValueError("routed mode needs D in {64, 128} and 0 <= route_density <= 1")
+                raise ValueError("routed modes need D in {64, 128} and 0 <= route_density <= 1")
         elif cfg.mask_mode == "given":
             keep = np.asarray(cfg.keep, dtype=np.uint8)
             if keep.shape[0] == 1 and cfg.B > 1:
@@ -111,7 +115,7 @@ class SparseAttentionPath:
             self.tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(self.device)
         if cfg.probes and not 2 <= cfg.probes <= _lib.MAX_FIT_PROBES:
             raise ValueError(f"probes must lie in [2, {_lib.MAX_FIT_PROBES}] (the ridge fit's range)")
-        if cfg.probes:
+        if cfg.probes and cfg.mask_mode != "partitioned":
             idx, w = api.select_probe_rows(cfg.labels, cfg.C, cfg.probes)
             self.probe_idx = torch.as_tensor(idx).to(self.device)
             self.probe_w = torch.as_tensor(w).to(self.device)
@@ -129,6 +133,8 @@ class SparseAttentionPath:
         ("Dynamic block masks and head-wise mask reuse", "Recipe"); one cache per layer."""
         cfg = self.cfg
         mark = mark or (lambda name: None)
+        if cfg.mask_mode == "partitioned":
+            return self._partitioned(q, k, v, keep_sparse, mark)
         main = torch.cuda.current_stream(q.device)
         mark("start")
         layout = api.cluster_layout(self.labels, cfg.C)
@@ -228,5 +234,68 @@ class SparseAttentionPath:
         res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
         if keep_sparse:  # the uncorrected rows too (an extra attention call, for inspection)
             res.out_sparse = api.block_sparse_attention(q, kv, layout, mask, cfg.compensate, cfg.scale,
+                                                        workspace=self._attn_ws)
+        return res
+
+    def _partitioned(self, q, k, v, keep_sparse, mark) -> PathResult:
+        """SparsePR's call ("Partition the Support, Reconstruct the Residual": partitioning,
+        routing, permutation, the sparse kernel, probes, the fit and write-back all inside the
+        call): response-coupled key and query groups per (batch, K/V head), their layouts, the
+        packed K/V, error-aware routes (the probe rows' cost reserved from the density target
+        first), then -- with probes -- the probes of every layout, their dense and sparse rows
+        and the fit, and the compensated attention with the correction in its epilogue."""
+        cfg = self.cfg
+        mark("start")
+        if q.dtype != torch.bfloat16:
+            raise ValueError("the partitioned path routes with block errors, which take bfloat16 inputs")
+        if self._part_ws is None:
+            n = _lib.size_query("bsa_response_partition_workspace_size", cfg.B, cfg.Hkv, cfg.S, cfg.D, cfg.C, cfg.C)
+            self._part_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        k_labels, q_labels = api.response_partition(q, k, cfg.C, cfg.C, cfg.scale, iters=cfg.partition_iters,
+                                                    workspace=self._part_ws)
+        mark("partition")
+        klay = api.cluster_layout(k_labels, cfg.C)
+        qlay = api.cluster_layout(q_labels, cfg.C)
+        mark("layout")
+        kv = api.kv_pack(k, v, klay, self._pack_buffer)
+        self._pack_buffer = kv.buffer
+        mark("pack")
+        qbar = api.query_centroids(q, qlay)
+        mark("route_probes")
+        if self._err_ws is None:
+            n = _lib.size_query("bsa_block_error_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D, cfg.C, cfg.C)
+            self._err_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        err = api.block_error(qbar, kv, cfg.scale, workspace=self._err_ws)
+        mark("block_error")
+        # Executed-pair density = routing density + M / S: the probe rows' share comes first.
+        budget = max(0, int(round(cfg.route_density * cfg.S)) - cfg.probes)
+        mask = api.error_route(err, klay, budget)
+        mark("route")
+        res = PathResult(out=None, layout=klay, mask=mask, kbar=kv.kbar if cfg.compensate else None,
+                         vbar=kv.vbar if cfg.compensate else None)
+        res.extras.update(q_layout=qlay, k_labels=k_labels, q_labels=q_labels, budget=budget)
+        if self._attn_ws is None:
+            self._attn_ws = api.attention_workspace(q, kv, qlay, mask)
+        A = c = None
+        if cfg.probes:
+            pidx, pw = api.select_probe_rows_layouts(qlay, cfg.probes)
+            mark("probe_select")
+            if self._probe_ws is None:
+                n = _lib.size_query("bsa_probe_attention_packed_workspace_size", cfg.B, cfg.Hq, cfg.Hkv, cfg.S,
+                                    cfg.D, cfg.probes, cfg.C)
+                self._probe_ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+            od, os_ = api.probe_attention_packed(q, kv, pidx, cfg.scale, workspace=self._probe_ws,
+                                                 q_labels=q_labels.reshape(-1, cfg.S), mask=mask,
+                                                 compensate=cfg.compensate)
+            mark("probe_rows")
+            A, c = api.probe_fit(os_, od, pw, cfg.lam, cfg.rank)
+            mark("fit")
+            res.o_dense_probe, res.o_sparse_probe, res.A, res.c = od, os_, A, c
+            res.extras.update(probe_idx=pidx, probe_w=pw)
+        res.out = api.block_sparse_attention(q, kv, qlay, mask, cfg.compensate, cfg.scale, workspace=self._attn_ws,
+                                             A=A, c=c)
+        mark("attention")
+        if keep_sparse and A is not None:
+            res.out_sparse = api.block_sparse_attention(q, kv, qlay, mask, cfg.compensate, cfg.scale,
                                                         workspace=self._attn_ws)
         return res

@@ -72,15 +72,23 @@ int bsa_abi_version(void);
 
 /* ------------------------------------------------------------------------------------
  * Cluster layout.  [SPR] group-major permutation: tokens are ordered cluster by cluster,
- * keeping their given order inside a cluster (a stable counting sort of the labels).
- *   labels  int32 [S] in [0, C)            (tokens with other labels are left out)
- *   perm    int32 [S]   out: token positions in cluster-major order
- *   offsets int32 [C+1] out: exclusive prefix sum of counts
- *   counts  int32 [C]   out: tokens per cluster
- * Needs S >= 1, 1 <= C <= 8192 and workspace of bsa_cluster_layout_workspace_size bytes.
+ * keeping their given order inside a cluster (a stable counting sort of the labels).  P
+ * independent layouts at once (P = 1 for one labelling of the sequence; P = B * Hkv for the
+ * per-(batch, K/V head) partitions of bsa_response_partition, [SPR] grouped-query sharing).
+ *   labels  int32 [P, S] in [0, C)         (tokens with other labels are left out)
+ *   perm    int32 [P, S]   out: token positions in cluster-major order
+ *   offsets int32 [P, C+1] out: exclusive prefix sum of counts
+ *   counts  int32 [P, C]   out: tokens per cluster
+ * Needs S >= 1, 1 <= C <= 8192, P <= 65535 and workspace of bsa_cluster_layout_workspace_size
+ * bytes.
+ *
+ * Layout counts.  The calls below that read cluster layouts take n_layouts: 1 when every
+ * (batch, head) shares one query layout and one key layout (arrays as above with P = 1), or
+ * B * Hkv when each (batch, K/V head) has its own (layout b * Hkv + kvh, shared by that K/V
+ * head's query heads; arrays [B * Hkv, ...]).  Any other value is BSA_E_ARG.
  */
-bsa_status bsa_cluster_layout_workspace_size(int S, int C, size_t* bytes_host);
-bsa_status bsa_cluster_layout(const int32_t* labels, int S, int C, int32_t* perm, int32_t* offsets,
+bsa_status bsa_cluster_layout_workspace_size(int P, int S, int C, size_t* bytes_host);
+bsa_status bsa_cluster_layout(int P, const int32_t* labels, int S, int C, int32_t* perm, int32_t* offsets,
                               int32_t* counts, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
@@ -106,27 +114,30 @@ bsa_status bsa_centroids(int B, int Hkv, int S, int D, int dtype, const void* K,
  *             bfloat16 (a per-tile flag records which, and a per-head word whether any
  *             tile of the head is bfloat16)
  * plus the first tile of every cluster.  The buffer is opaque to callers: its size comes
- * from bsa_kv_pack_workspace_size, it is valid for the key layout (perm, offsets, C) it was
- * packed with, and bsa_sparse_attention must be given the same offsets.
- *   K, V [B, Hkv, S, D] dtype;  perm int32 [S], offsets int32 [C+1]: key cluster layout
+ * from bsa_kv_pack_workspace_size, it is valid for the key layouts (perm, offsets, C,
+ * n_layouts) it was packed with, and the calls that read it must be given the same offsets
+ * and n_layouts.
+ *   K, V [B, Hkv, S, D] dtype;  perm int32 [n_layouts, S], offsets int32 [n_layouts, C+1]:
+ *   key cluster layouts (n_layouts 1 or B * Hkv, see "Layout counts")
  *   Kbar, Vbar float [B, Hkv, C, D] out (cluster means; an empty cluster gives zeros)
  *   packed: device buffer of at least bsa_kv_pack_workspace_size bytes, packed_bytes its size
  * Needs D in {64, 128}, 1 <= C <= 32767, B * Hkv <= 65535.  BSA_E_WORKSPACE if the buffer
  * is missing or too small.
  */
-bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, size_t* bytes_host);
+bsa_status bsa_kv_pack_workspace_size(int B, int Hkv, int S, int D, int dtype, int C, int n_layouts,
+                                      size_t* bytes_host);
 bsa_status bsa_kv_pack(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V, const int32_t* perm,
-                       const int32_t* offsets, int C, float* Kbar, float* Vbar, void* packed, size_t packed_bytes,
-                       hipStream_t stream);
+                       const int32_t* offsets, int C, int n_layouts, float* Kbar, float* Vbar, void* packed,
+                       size_t packed_bytes, hipStream_t stream);
 /* The same packing with caller-given centroids and counts ([SBC] API table: the compensated
  * attention takes the keys, values and clusters from the caller; "SVG-EAR -- centroid
  * compensation": column c carries log n_c and v_bar_c).  Only the token tiles are packed from
  * K and V; the centroid tiles come from Kbar/Vbar (read only), and centroid column c is
  * weighted by log(counts[c]) (a count of 0 removes the column).
- *   Kbar, Vbar float [B, Hkv, C, D]; counts int32 [C] (>= 0, shared by all heads)
+ *   Kbar, Vbar float [B, Hkv, C, D]; counts int32 [n_layouts, C] (>= 0, one row per layout)
  * Other arguments, requirements and errors as bsa_kv_pack. */
 bsa_status bsa_kv_pack_centroids(int B, int Hkv, int S, int D, int dtype, const void* K, const void* V,
-                                 const int32_t* perm, const int32_t* offsets, int C, const float* Kbar,
+                                 const int32_t* perm, const int32_t* offsets, int C, int n_layouts, const float* Kbar,
                                  const float* Vbar, const int32_t* counts, void* packed, size_t packed_bytes,
                                  hipStream_t stream);
 
@@ -194,8 +205,9 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
  * c float [B, Hq, D], both from bsa_probe_fit; NULL, NULL for no epilogue (one of them NULL:
  * BSA_E_ARG).  With A given out_dtype must equal dtype (else BSA_E_UNSUPPORTED).
  *   Q [B, Hq, S, D] dtype, O [B, Hq, S, D] out_dtype out
- *   q_perm/q_offsets (Cq clusters): query cluster layout; k_offsets [Ck+1]: the key layout
- *     the buffer was packed with
+ *   q_perm/q_offsets (Cq clusters): query cluster layouts; k_offsets [n_layouts, Ck+1]: the key
+ *     layouts the buffer was packed with; n_layouts 1 or B * Hkv ("Layout counts"; with
+ *     B * Hkv > 1 layouts Hm must be Hkv or Hq, else BSA_E_SHAPE)
  *   keep/kv_count/kv_idx: block mask with Hm in {1, Hkv, Hq}
  *   packed, packed_bytes: the bsa_kv_pack buffer (BSA_E_WORKSPACE if smaller than its size)
  *   lse float [B, Hq, S] out (natural log of the softmax denominator) or NULL
@@ -208,10 +220,10 @@ bsa_status bsa_mask_lists(const uint8_t* keep, int rows, int Ck, int32_t* kv_cou
 bsa_status bsa_sparse_attention_workspace_size(int B, int Hq, int Hm, int Cq, int S, int Ck, size_t* bytes_host);
 bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                 const int32_t* q_perm, const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
-                                int Ck, const uint8_t* keep, const int32_t* kv_count, const int16_t* kv_idx, int Hm,
-                                const void* packed, size_t packed_bytes, int compensate, const float* A,
-                                const float* c, int out_dtype, void* O, float* lse, void* ws, size_t ws_bytes,
-                                hipStream_t stream);
+                                int Ck, int n_layouts, const uint8_t* keep, const int32_t* kv_count,
+                                const int16_t* kv_idx, int Hm, const void* packed, size_t packed_bytes, int compensate,
+                                const float* A, const float* c, int out_dtype, void* O, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): bsa_sparse_attention without a workspace
@@ -226,7 +238,7 @@ bsa_status bsa_sparse_attention(int B, int Hq, int Hkv, int S, int D, int dtype,
 size_t bsa_sparse_attention_static_scratch_bytes(void);
 bsa_status bsa_sparse_attention_noalloc(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                         const int32_t* q_perm, const int32_t* q_offsets, int Cq,
-                                        const int32_t* k_offsets, int Ck, const uint8_t* keep,
+                                        const int32_t* k_offsets, int Ck, int n_layouts, const uint8_t* keep,
                                         const int32_t* kv_count, const int16_t* kv_idx, int Hm, const void* packed,
                                         size_t packed_bytes, int compensate, const float* A, const float* c,
                                         int out_dtype, void* O, float* lse, hipStream_t stream);
@@ -259,10 +271,12 @@ bsa_status bsa_probe_attention(int B, int Hq, int Hkv, int S, int D, int dtype, 
  * bsa_sparse_attention (the kept key clusters of each probe's query cluster, plus, with
  * compensate != 0, the centroid columns of its skipped clusters, weighted by the pack's
  * counts), both in float32 -- the inputs of bsa_probe_fit, available before the attention runs.
- * packed, packed_bytes: the bsa_kv_pack buffer made from the same K, V and key layout;
- * k_offsets int32 [C+1] and C: that layout's cluster offsets and count (C = Ck).
- *   q_labels int32 [S]: query cluster labels; keep uint8 [B, Hm, Cq, C]: the block mask
- *     (Hm in {1, Hkv, Hq}); both ignored when O_sparse_probe is NULL
+ * packed, packed_bytes: the bsa_kv_pack buffer made from the same K, V and key layouts;
+ * k_offsets int32 [n_layouts, C+1], C and n_layouts: those layouts' cluster offsets, cluster
+ * count (C = Ck) and number ("Layout counts").  With n_layouts = B * Hkv each layout has its
+ * own probes: probe_idx int32 [n_layouts, M] (else [M], shared by every head).
+ *   q_labels int32 [n_layouts, S]: query cluster labels; keep uint8 [B, Hm, Cq, C]: the block
+ *     mask (Hm in {1, Hkv, Hq}); both ignored when O_sparse_probe is NULL
  *   O_dense_probe, O_sparse_probe float [B, Hq, M, D] out (O_sparse_probe may be NULL)
  * Needs dtype BSA_BF16 (BSA_E_UNSUPPORTED for float32: use bsa_probe_attention), 1 <= M <= 1024,
  * C <= 1024 for sparse rows, and workspace of bsa_probe_attention_packed_workspace_size bytes.
@@ -271,9 +285,10 @@ bsa_status bsa_probe_attention_packed_workspace_size(int B, int Hq, int Hkv, int
                                                      size_t* bytes_host);
 bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, float scale,
                                       const int32_t* probe_idx, int M, const void* packed, size_t packed_bytes,
-                                      const int32_t* k_offsets, int C, const int32_t* q_labels, const uint8_t* keep,
-                                      int Hm, int Cq, int compensate, float* O_dense_probe, float* O_sparse_probe,
-                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                      const int32_t* k_offsets, int C, int n_layouts, const int32_t* q_labels,
+                                      const uint8_t* keep, int Hm, int Cq, int compensate, float* O_dense_probe,
+                                      float* O_sparse_probe, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Ridge fit.  [SPR] Probe-Fitted Residual Reconstruction and [SBC] "Deviations from the
@@ -285,12 +300,15 @@ bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int 
  *   P = V_r V_r^T with V_r the top min(rank, #eigenvalues > 1e-12 * max) eigenvectors of
  *   Rc^T diag(w) Rc;  A = diag(1/sigma) W P;  c = rbar - mu A.
  * The correction of any row o is then o A + c.  Computed in float64 on the device.
- *   O_sparse_probe, O_dense_probe float [B, Hq, M, D]; weights float [M] > 0
+ *   O_sparse_probe, O_dense_probe float [B, Hq, M, D]; weights float [n_layouts, M] > 0 (n_layouts
+ *   1: one set for every head; B * Hkv: head (b, h) takes row b * Hkv + h / (Hq / Hkv), the
+ *   weights of its layout's probes)
  *   A float [B, Hq, D, D] out (row-major: correction_j = sum_i o_i A[i][j] + c_j); c float [B, Hq, D] out
  * Needs 2 <= M <= 64, lambda > 0 and 1 <= rank <= 16 (rank <= D).
  */
-bsa_status bsa_probe_fit(int B, int Hq, int D, const float* O_sparse_probe, const float* O_dense_probe,
-                         const float* weights, int M, float lambda, int rank, float* A, float* c, hipStream_t stream);
+bsa_status bsa_probe_fit(int B, int Hq, int Hkv, int D, const float* O_sparse_probe, const float* O_dense_probe,
+                         const float* weights, int M, int n_layouts, float lambda, int rank, float* A, float* c,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Correction of every row ([SPR]: the correction is applied to all rows; probe rows are
@@ -370,11 +388,11 @@ bsa_status bsa_mask_reuse_update(int B, int Hm, int Cq, int Ck, int D, const uin
  *
  * bsa_query_centroids: the probe of query cluster a is its mean query row, rounded to dtype
  * (as the centroid keys are); an empty cluster gets a zero row.  Float32 sums.
- *   Q [B, Hq, S, D] dtype; q_perm/q_offsets: the query cluster layout (Cq clusters);
- *   qbar [B, Hq, Cq, D] dtype out
+ *   Q [B, Hq, S, D] dtype; q_perm/q_offsets: the query cluster layouts (Cq clusters,
+ *   n_layouts 1 or B * Hkv: "Layout counts"); qbar [B, Hq, Cq, D] dtype out
  */
-bsa_status bsa_query_centroids(int B, int Hq, int S, int D, int dtype, const void* Q, const int32_t* q_perm,
-                               const int32_t* q_offsets, int Cq, void* qbar, hipStream_t stream);
+bsa_status bsa_query_centroids(int B, int Hq, int Hkv, int S, int D, int dtype, const void* Q, const int32_t* q_perm,
+                               const int32_t* q_offsets, int Cq, int n_layouts, void* qbar, hipStream_t stream);
 
 /* bsa_block_error: for probe q = qbar[b, h, a] with softmax weights p_j over all keys, dense
  * output O_a, and for key cluster c (n_c keys, means k_bar_c, v_bar_c from bsa_kv_pack):
@@ -383,15 +401,16 @@ bsa_status bsa_query_centroids(int B, int Hq, int S, int D, int dtype, const voi
  * first-order change of the probe's output when block (a, c) alone is compensated; 0 for
  * an empty cluster.  Two passes over the packed tiles: the probes' dense rows and
  * log-sum-exp, then the per-cluster sums (P V with P split into two float16 parts).
- *   qbar [B, Hq, Cq, D] bfloat16; packed/packed_bytes, k_offsets [Ck+1], Kbar/Vbar float
- *   [B, Hkv, Ck, D]: the bsa_kv_pack buffer and centroids; err float [B, Hq, Cq, Ck] out
+ *   qbar [B, Hq, Cq, D] bfloat16; packed/packed_bytes, k_offsets [n_layouts, Ck+1], n_layouts,
+ *   Kbar/Vbar float [B, Hkv, Ck, D]: the bsa_kv_pack buffer, its layouts and centroids;
+ *   err float [B, Hq, Cq, Ck] out
  *   ws: workspace of bsa_block_error_workspace_size bytes (the first pass's partial rows,
  *       its rows and log-sum-exp)
  * bfloat16 only (BSA_E_UNSUPPORTED for float32).  Needs Cq <= 4096, Ck <= 32767.
  */
 bsa_status bsa_block_error_workspace_size(int B, int Hq, int Hkv, int S, int D, int Cq, int Ck, size_t* bytes_host);
 bsa_status bsa_block_error(int B, int Hq, int Hkv, int S, int D, int dtype, const void* qbar, int Cq, float scale,
-                           const void* packed, size_t packed_bytes, const int32_t* k_offsets, int Ck,
+                           const void* packed, size_t packed_bytes, const int32_t* k_offsets, int Ck, int n_layouts,
                            const float* Kbar, const float* Vbar, float* err, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
@@ -399,12 +418,15 @@ bsa_status bsa_block_error(int B, int Hq, int Hkv, int S, int D, int dtype, cons
  * correctly rounded; descending, ties by lower index -- the cost of block (a, c) is
  * n_a n_c and n_a is fixed along a row) and the shortest prefix whose key count reaches
  * `budget` tokens; at least one cluster; empty clusters are never kept.
- *   err float [rows, Ck]; k_offsets [Ck+1]; keep uint8 [rows, Ck], kv_count int32 [rows],
- *   kv_idx int16 [rows, Ck] out (the bsa_top_p_mask conventions)
- * Needs Ck <= 1024.
+ *   err float [rows, Ck]; keep uint8 [rows, Ck], kv_count int32 [rows], kv_idx int16 [rows, Ck]
+ *   out (the bsa_top_p_mask conventions)
+ *   k_offsets: the key layout [Ck+1] of every row (rows_per_layout = 0), or key layouts
+ *   [rows / rows_per_layout, Ck+1], row r reading layout r / rows_per_layout (rows of
+ *   [B, Hq, Cq] and per-(batch, K/V head) layouts: rows_per_layout = (Hq / Hkv) * Cq)
+ * Needs Ck <= 1024; rows a multiple of rows_per_layout.
  */
-bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int budget, uint8_t* keep,
-                           int32_t* kv_count, int16_t* kv_idx, hipStream_t stream);
+bsa_status bsa_error_route(const float* err, int rows, int Ck, const int32_t* k_offsets, int rows_per_layout,
+                           int budget, uint8_t* keep, int32_t* kv_count, int16_t* kv_idx, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Response-coupled partitioning.  [SPR] Response-Coupled Partitioning: queries sampled from
@@ -442,6 +464,16 @@ bsa_status bsa_response_partition(int B, int Hq, int Hkv, int S, int D, int dtyp
 bsa_status bsa_kmeans_workspace_size(int P, int N, int C, size_t* bytes_host);
 bsa_status bsa_kmeans(int P, int N, int nf, const float* X, int C, int iters, int32_t* labels, float* centres,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Probe rows on the device, from P cluster layouts (the per-(batch, K/V head) partitions of
+ * bsa_response_partition after bsa_cluster_layout): the rule of bsa_select_probe_rows below,
+ * applied to each layout with its members in layout order (ascending positions).
+ *   perm int32 [P, S], offsets int32 [P, C+1]; probe_idx int32 [P, M] out, weights float [P, M]
+ *   out (normalized per layout).  Needs 1 <= M <= S and every layout's perm a permutation of
+ *   its S tokens (labels in [0, C)).
+ */
+bsa_status bsa_select_probe_rows_layouts(int P, int S, int C, int M, const int32_t* perm, const int32_t* offsets,
+                                         int32_t* probe_idx, float* weights, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Host helpers (host pointers only).

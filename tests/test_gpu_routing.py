@@ -108,8 +108,9 @@ def test_error_route_bit_exact(bsa, Ck, rows, budget):
     off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
     err = (rng.integers(0, 40, (1, 1, rows, Ck)) / 8.0).astype(np.float32)
     err[..., ::5] *= np.float32(3.0)  # quotients that tie only after rounding
-    class _L:  # the route reads only the key offsets
+    class _L:  # the route reads only the key offsets (one layout for every row)
         offsets = torch.from_numpy(off).cuda()
+        n_layouts = 1
     m = bsa.error_route(torch.from_numpy(err).cuda(), _L, budget)
     want = ort.error_aware_route(err, n, budget)
     fragile = route_fragile_rows(err, n, budget)[0, 0]

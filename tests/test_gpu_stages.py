@@ -68,17 +68,22 @@ def _align(x):
     return (x + 255) // 256 * 256
 
 
-def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem):
-    """Sections of the packed buffer as documented for bsa_kv_pack (test-side decoding)."""
+def decode_packed(buf: np.ndarray, B, Hkv, S, D, C, elem, nl=1):
+    """Sections of the packed buffer as documented for bsa_kv_pack (test-side decoding):
+    per-head format summary, tile flags, K and V tiles, then per layout the cluster tile
+    offsets (returned [nl, C+1], or [C+1] for one layout) and the centroid log2 counts."""
     tok = -(-S // 64) + C
     ctiles = -(-C // 64)
     tph = tok + ctiles
     nt = B * Hkv * tph
-    off_hmix = _align(4 * (C + 1))
+    off_hmix = 0
     off_flags = off_hmix + _align(4 * B * Hkv)
     off_k = off_flags + _align(nt)
     off_v = off_k + _align(nt * 64 * D * elem)
-    tile_off = buf[: 4 * (C + 1)].view(np.int32)
+    off_toff = off_v + _align(nt * 64 * D * elem)
+    tile_off = buf[off_toff: off_toff + 4 * nl * (C + 1)].view(np.int32).reshape(nl, C + 1)
+    if nl == 1:
+        tile_off = tile_off[0]
     flags = buf[off_flags: off_flags + nt].reshape(B * Hkv, tph)
     kdt = np.uint16 if elem == 2 else np.float32
     kt = buf[off_k: off_k + nt * 64 * D * elem].view(kdt).reshape(B * Hkv, tph, 64, D)
