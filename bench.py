@@ -66,7 +66,19 @@ PROFILE_COMMANDS = {
              "-d $R/gpurun_out/prof -o fetch -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
     "write": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
              "-d $R/gpurun_out/prof -o write -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    # MFMA, VALU and LDS activity, then the L2 hit rate, of the same launches
+    "sq": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA "
+          "SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVES GRBM_GUI_ACTIVE "
+          "--output-format csv -d $R/gpurun_out/prof -o sq -- python3 $R/bench.py --profile-kernels 3 "
+          "--no-cpu-baseline",
+    "l2": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
+          "-d $R/gpurun_out/prof -o l2 -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    # the partitioned (SparsePR) call alone
+    "trace_partitioned": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
+                         "csv -d $R/gpurun_out/prof -o trace_partitioned -- python3 $R/bench.py --steps 5 "
+                         "--warmup 2 --partitioned-only",
 }
+SIMDS, NOMINAL_GHZ, XCDS = 1024, 2.4, 8  # MI355X: 256 CUs x 4 SIMDs, peak engine clock, XCDs
 
 
 def kernel_source_hash() -> str:
@@ -113,6 +125,103 @@ def _counter_per_dispatch(path: str):
     return per
 
 
+def _summarize_trace(trace: str, command: str, out_path: str, title: str) -> None:
+    """Kernel-trace table of a run of TRACE_STEPS + TRACE_WARMUP calls (warm-up launches dropped)."""
+    import csv
+
+    if not os.path.exists(trace):
+        return
+    calls, warm = TRACE_STEPS + TRACE_WARMUP, TRACE_WARMUP
+    per = {}
+    with open(trace) as f:
+        for r in csv.DictReader(f):
+            per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    lines = [f"# Kernel trace: {title}", "", "Command (from the repository root, on one MI355X):", "", "```",
+             PROFILE_COMMANDS[command], "```", "",
+             f"The run makes {calls} calls: {warm} warm-up calls, then the {TRACE_STEPS} timed calls.  Kernels "
+             f"launched a whole number of times per call are summarized over the timed calls' launches; durations "
+             f"in microseconds.", "",
+             "| kernel | launches per call | timed launches | avg us | min us | max us | us per call |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    total = 0.0
+    for k, ds in sorted(per.items(), key=lambda kv: -sum(x for _, x in kv[1])):
+        ds.sort()
+        if len(ds) % calls:
+            lines.append(f"| `{k}` | ? | {len(ds)} (all) | {np.mean([x for _, x in ds]):.1f} | "
+                         f"{min(x for _, x in ds):.1f} | {max(x for _, x in ds):.1f} | |")
+            continue
+        m = len(ds) // calls
+        timed = [x for _, x in ds[warm * m:]]
+        total += sum(timed) / TRACE_STEPS
+        lines.append(f"| `{k}` | {m} | {len(timed)} | {np.mean(timed):.1f} | {min(timed):.1f} | {max(timed):.1f} | "
+                     f"{sum(timed) / TRACE_STEPS:.1f} |")
+    lines += ["", f"Kernel time per timed call: {total:.1f} us."]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counters_by_dispatch(path: str):
+    """{kernel: [{counter: value, "dur_ns": ...} per dispatch]} from a counter_collection csv."""
+    import csv
+
+    disp = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], _short_kernel(r["Kernel_Name"]))
+            e = disp.setdefault(key, {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = {}
+    for (_, k), e in sorted(disp.items(), key=lambda kv: int(kv[0][0])):
+        per.setdefault(k, []).append(e)
+    return per
+
+
+def _summarize_counters(d: str, out_path: str) -> None:
+    """MFMA busy, instruction mix, LDS bank conflicts and L2 hit rate per kernel, from the "sq"
+    and "l2" runs (dispatches shorter than 20 us, such as the path's empty general-queue
+    attention launch, are left out)."""
+    sq_csv, l2_csv = os.path.join(d, "sq_counter_collection.csv"), os.path.join(d, "l2_counter_collection.csv")
+    if not (os.path.exists(sq_csv) and os.path.exists(l2_csv)):
+        return
+    sq, l2 = _counters_by_dispatch(sq_csv), _counters_by_dispatch(l2_csv)
+    lines = ["# SQ and L2 counters per kernel, video workload (B=1, H=40, S=32760, D=128, bf16)", "",
+             "Commands (from the repository root, on one MI355X), one counter set per run:", "", "```",
+             PROFILE_COMMANDS["sq"], PROFILE_COMMANDS["l2"], "```", "",
+             "Per kernel, the mean over its dispatches of at least 20 us.  MFMA busy is "
+             "SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles of the dispatch, counted two ways: at the nominal "
+             f"{NOMINAL_GHZ} GHz (duration x {NOMINAL_GHZ} GHz x {SIMDS} SIMDs; comparable with the fraction of "
+             f"the {PEAK_BF16_TFLOPS:.0f} TFLOP/s peak) and at the clock the counters saw (GRBM_GUI_ACTIVE, "
+             f"summed over the {XCDS} XCDs, divided by {XCDS}: the busy share of the cycles that elapsed).  "
+             "LDS conflicts are SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE; L2 hits are TCC_HIT over "
+             "TCC_HIT + TCC_MISS.", "",
+             "| kernel | dispatches | us | clock GHz | MFMA busy @2.4 GHz | MFMA busy @seen clock | MFMA insts | "
+             "VALU insts | LDS insts | LDS conflict | L2 hit |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    rows = []
+    for k, ds in sq.items():
+        ds = [e for e in ds if e["dur_ns"] >= 20000]
+        if not ds or k.startswith("__amd"):
+            continue
+        mean = lambda key: float(np.mean([e.get(key, 0.0) for e in ds]))
+        dur = mean("dur_ns")
+        busy, grbm = mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE")
+        clk = grbm / XCDS / dur if dur > 0 else 0.0
+        lds_act = mean("SQ_LDS_IDX_ACTIVE")
+        conf = mean("SQ_LDS_BANK_CONFLICT") / lds_act if lds_act > 0 else 0.0
+        l2d = [e for e in l2.get(k, []) if e["dur_ns"] >= 20000]
+        hit = float(np.mean([e.get("TCC_HIT_sum", 0.0) for e in l2d])) if l2d else 0.0
+        miss = float(np.mean([e.get("TCC_MISS_sum", 0.0) for e in l2d])) if l2d else 0.0
+        rows.append((dur, f"| `{k}` | {len(ds)} | {dur / 1e3:.1f} | {clk:.2f} | "
+                          f"{100 * busy / (dur * NOMINAL_GHZ * SIMDS):.1f}% | "
+                          f"{100 * busy / (grbm / XCDS * SIMDS) if grbm > 0 else 0.0:.1f}% | {mean('SQ_INSTS_MFMA'):.3g} | "
+                          f"{mean('SQ_INSTS_VALU'):.3g} | {mean('SQ_INSTS_LDS'):.3g} | {100 * conf:.1f}% | "
+                          f"{100 * hit / (hit + miss) if hit + miss > 0 else 0.0:.1f}% |"))
+    lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_profiles(d: str) -> int:
     """Write the kernel-trace table, the HBM counter table and the attention kernel's traffic
     record (profiles/) from the csv files of the PROFILE_COMMANDS runs in directory d."""
@@ -121,6 +230,10 @@ def summarize_profiles(d: str) -> int:
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     stem = "wan_S32760_H40_D128"
+    _summarize_trace(os.path.join(d, "trace_partitioned_kernel_trace.csv"), "trace_partitioned",
+                     os.path.join(out_dir, f"partitioned_kernels_{stem}.md"),
+                     "partitioned (SparsePR) call, video workload (B=1, H=40, S=32760, D=128, bf16)")
+    _summarize_counters(d, os.path.join(out_dir, f"sq_l2_counters_{stem}.md"))
     trace = os.path.join(d, "trace_kernel_trace.csv")
     if os.path.exists(trace):
         calls, warm = TRACE_STEPS + TRACE_WARMUP, TRACE_WARMUP
@@ -193,15 +306,32 @@ def summarize_profiles(d: str) -> int:
     return 0
 
 
+def _cluster_sizes(res, cfg):
+    """Query and key cluster sizes of every mask row's layout, each [B, Hm, C] float64: one
+    layout shared by every head, or (partitioned path) one per (batch, K/V head)."""
+    import torch
+
+    keep = res.mask.keep
+    B, Hm = keep.shape[:2]
+    nk = res.layout.counts.to(torch.float64)
+    qlay = res.extras.get("q_layout")
+    nq = (qlay.counts if qlay is not None else res.layout.counts).to(torch.float64)
+    if nk.dim() == 1:
+        return nq.expand(B, Hm, -1), nk.expand(B, Hm, -1)
+    kvh = torch.arange(Hm, device=keep.device) // ((cfg.Hq // cfg.Hkv) if Hm == cfg.Hq else 1)
+    idx = torch.arange(B, device=keep.device)[:, None] * cfg.Hkv + kvh[None, :]
+    return nq[idx], nk[idx]
+
+
 def executed_pairs(res, cfg):
     """Kept token pairs per call (sum over heads and query clusters of n_a times the kept key
     tokens) -- a measurement of the mask, computed with torch on the GPU."""
     import torch
 
     keep = res.mask.keep.to(torch.float64)  # [B, Hm, Cq, Ck]
-    n = res.layout.counts.to(torch.float64)  # [C]
-    kept_keys = keep @ n  # [B, Hm, Cq]
-    per_mask_head = (kept_keys * n).sum(dim=-1)  # [B, Hm]
+    nq, nk = _cluster_sizes(res, cfg)  # [B, Hm, C]
+    kept_keys = (keep * nk[:, :, None, :]).sum(dim=-1)  # [B, Hm, Cq]
+    per_mask_head = (kept_keys * nq).sum(dim=-1)  # [B, Hm]
     Hm = keep.shape[1]
     heads_per_mask = cfg.Hq // Hm
     return float(per_mask_head.sum().item()) * heads_per_mask
@@ -433,6 +563,10 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
         api.pooled_qk(q, k)
         torch.cuda.synchronize()
         print(f"[profile] pooled_qk {i}", flush=True)
+    for i in range(reps):
+        api.response_partition(q, k, cfg.C, cfg.C, cfg.scale)
+        torch.cuda.synchronize()
+        print(f"[profile] response partition {i}", flush=True)
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=q.device).fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -489,10 +623,10 @@ def centroid_columns(res, cfg):
     import torch
 
     keep = res.mask.keep.to(torch.float64)  # [B, Hm, Cq, Ck]
-    n = res.layout.counts.to(torch.float64)
-    nonempty = (n > 0).to(torch.float64)
+    nq, nk = _cluster_sizes(res, cfg)
+    nonempty = (nk > 0).to(torch.float64)[:, :, None, :]
     skipped = ((1.0 - keep) * nonempty).sum(dim=-1)  # [B, Hm, Cq]
-    return float((skipped * n).sum().item()) * (cfg.Hq // keep.shape[1])
+    return float((skipped * nq).sum().item()) * (cfg.Hq // keep.shape[1])
 
 
 def path_figures(res, cfg, ms_per_step, stages_ms, probes):
@@ -552,6 +686,23 @@ def measure_repair_workloads(bsa, steps, warmup, wl2, q, k, v):
     return out
 
 
+def measure_partitioned(bsa, steps, warmup, wl2, q, k, v):
+    """SparsePR's call on the headline inputs: response-coupled partitions per (batch, K/V
+    head) into 256 key and 256 query groups, error-aware routes at 22% executed-pair density
+    with the 64 probe rows' share reserved first, hard drop renormalized over the kept groups,
+    the probe rows, the fit and the corrected attention -- every stage inside the timed call."""
+    cfgp = bsa.PathConfig.from_workload(dataclasses.replace(wl2, compensate=False, probes=64, lam=0.1, rank=16))
+    cfgp.mask_mode, cfgp.route_density = "partitioned", 0.22
+    pathp = bsa.SparseAttentionPath(cfgp)
+    ms, st, res = time_path(pathp, q, k, v, steps, warmup)
+    fig = path_figures(res, cfgp, ms, st, cfgp.probes)
+    fig["partition_ms"] = round(st["partition"], 4)
+    return dict(workload="same inputs; response-coupled partitions (rK 48, rQ 64, 4 Lloyd iterations per grouping) "
+                         "into 256 key and 256 query groups per (batch, K/V head); error-aware routes at 22% "
+                         "executed-pair density including 64 probe rows; hard drop; ridge fit (lambda 0.1, rank 16); "
+                         "correction in the attention epilogue", **fig)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,6 +711,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path-only", action="store_true",
                     help="time the headline path only (no repair workloads or side measurements)")
+    ap.add_argument("--partitioned-only", action="store_true",
+                    help="time the partitioned (SparsePR) call alone and print its figures")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the K/V packing and probe rows on the caller's stream too")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
@@ -592,6 +745,9 @@ def main() -> int:
 
     if args.profile_kernels:
         return profile_kernels(bsa, path, cfg, q, k, v, args.profile_kernels)
+    if args.partitioned_only:
+        print(json.dumps(measure_partitioned(bsa, args.steps, args.warmup, wl, q, k, v)), flush=True)
+        return 0
 
     print("[bench] timing", file=sys.stderr, flush=True)
     ms_per_step, stages_ms, res = time_path(path, q, k, v, args.steps, args.warmup)
@@ -663,6 +819,8 @@ def main() -> int:
         line["sliding_tile_attention"] = measure_sliding_tile(bsa, cfg, wl, q, k, v)
         print("[bench] error-aware routing", file=sys.stderr, flush=True)
         line["error_aware_routing"] = measure_routing(bsa, cfg, q, k, v, res, line["config"]["density"])
+        print("[bench] partitioned call", file=sys.stderr, flush=True)
+        line["partitioned_sparsepr"] = measure_partitioned(bsa, args.steps, args.warmup, wl, q, k, v)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl)

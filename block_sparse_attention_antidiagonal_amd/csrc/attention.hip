@@ -1047,8 +1047,11 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
 
   for (int rt = q_lo; rt < q_hi; rt += kRowsWG) {
     const int nrows = min(kRowsWG, q_hi - rt);
-    // This lane's query row; rows past the cluster reuse row 0 and are not stored.
+    // This lane's query row; rows past the cluster reuse row 0 and are not stored.  A wave
+    // with no row of the cluster (a cluster's last block of fewer than 128 rows) only copies
+    // its share of the tiles and meets the barriers: its SIMD is left to the other workgroup.
     const int my = wave * 32 + r;
+    const bool wave_rows = wave * 32 < nrows;  // uniform over the wave
     const int qtok = qperm_h[rt + (my < nrows ? my : 0)];
     Frag<T> qf[C::KK];
     load_q_frags<T, D>(qf, Qh + static_cast<size_t>(qtok) * D);
@@ -1110,9 +1113,10 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
         if (entry_centroid(e1)) write_bias(bias0 + (BJ ^ 1) * kNK, tl - first_ctile);
         if (!ALL16) pv1 = flags_h[tl];
       }
-      tile_step<T, D, SwzLds<T, D>>(
-          kbuf(BJ), vbuf(BJ), qf, st, c2, KeyBias{entry_centroid(e0) ? bias0 + BJ * kNK : nullptr},
-          entry_nvalid(e0), ALL16 || pv0 != 0);
+      if (wave_rows)
+        tile_step<T, D, SwzLds<T, D>>(
+            kbuf(BJ), vbuf(BJ), qf, st, c2, KeyBias{entry_centroid(e0) ? bias0 + BJ * kNK : nullptr},
+            entry_nvalid(e0), ALL16 || pv0 != 0);
       wait_vmem();
       __syncthreads();
       e0 = e1;
@@ -1141,7 +1145,7 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
       load_correction_image<T, D>(corr_img + bhq * kCorrImageStride, smem);
       wait_vmem();
       __syncthreads();
-      apply_correction<T, D>(st.o, smem);
+      if (wave_rows) apply_correction<T, D>(st.o, smem);
       __syncthreads();  // every wave is done with the image before the rows are staged over it
     }
     // Stage the tile as rows in LDS, then store rows with 16-byte writes.

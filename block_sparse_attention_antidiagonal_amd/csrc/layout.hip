@@ -79,74 +79,84 @@ __device__ __forceinline__ int middle_out_member(int n, int k) {
 }
 
 // Probe rows of every layout from its cluster layout (the rule of bsa_select_probe_rows, the
-// members in the layout's stable order): one thread per layout walks the rounds.  Rounds after
-// a partial first one visit every non-empty cluster; cluster a takes part in round r while it
-// has more than r members.
-__global__ __launch_bounds__(64) void select_probes_kernel(int P, int S, int C, int M, const int32_t* __restrict__ perm,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ probe_idx,
-                                                           float* __restrict__ weights) {
-  const int p = blockIdx.x * 64 + threadIdx.x;
-  if (p >= P) return;
-  const int32_t* off = offsets + static_cast<size_t>(p) * (C + 1);
-  const int32_t* pp = perm + static_cast<size_t>(p) * S;
-  int32_t* idx = probe_idx + static_cast<size_t>(p) * M;
-  float* w = weights + static_cast<size_t>(p) * M;
-  int nne = 0, maxn = 0;
-  for (int a = 0; a < C; ++a) {
+// members in the layout's stable order), one workgroup per layout.  Cluster sizes and the list
+// of non-empty clusters (a block scan) go to LDS; a partial round (fewer probes than non-empty
+// clusters: one probe from each of M evenly spaced ones) is taken by M threads at once; full
+// rounds (round r takes member r, middle-out, of every cluster with more than r members, in
+// cluster order) are walked by one thread over the LDS copy.  Dynamic LDS: 2 C + 256 ints.
+constexpr int kSelThreads = 256;
+__global__ __launch_bounds__(kSelThreads) void select_probes_kernel(int S, int C, int M,
+                                                                    const int32_t* __restrict__ perm,
+                                                                    const int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ probe_idx,
+                                                                    float* __restrict__ weights) {
+  extern __shared__ int32_t sel_lds[];
+  int32_t* n_s = sel_lds;           // [C] cluster sizes
+  int32_t* ne_s = sel_lds + C;      // [C] the non-empty clusters in order
+  int32_t* part = sel_lds + 2 * C;  // [kSelThreads] scan of per-thread non-empty counts
+  const size_t p = blockIdx.x;
+  const int t = threadIdx.x;
+  const int32_t* off = offsets + p * (C + 1);
+  const int32_t* pp = perm + p * S;
+  int32_t* idx = probe_idx + p * M;
+  float* w = weights + p * M;
+  const int per = (C + kSelThreads - 1) / kSelThreads, c0 = t * per, c1 = min(C, c0 + per);
+  int mine = 0;
+  for (int a = c0; a < c1; ++a) {
     const int n = off[a + 1] - off[a];
-    nne += n > 0 ? 1 : 0;
-    maxn = max(maxn, n);
+    n_s[a] = n;
+    mine += n > 0 ? 1 : 0;
   }
-  int taken = 0;
-  if (M < nne) {  // one partial round over evenly spaced non-empty clusters, one probe each
-    int a = 0, seen = 0;  // the seen-th non-empty cluster is a
-    while (off[a + 1] <= off[a]) ++a;
-    for (int j = 0; j < M; ++j) {
-      const int k = static_cast<int>(floor((j + 0.5) * static_cast<double>(nne) / M));
-      while (seen < k) {
-        ++a;
-        while (off[a + 1] <= off[a]) ++a;
-        ++seen;
-      }
-      const int n = off[a + 1] - off[a];
-      idx[j] = pp[off[a] + middle_out_member(n, 0)];
-      w[j] = static_cast<float>(n);  // |G_a| / 1
+  part[t] = mine;
+  __syncthreads();
+  for (int d = 1; d < kSelThreads; d <<= 1) {  // inclusive scan of the counts
+    const int add = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int rank = part[t] - mine;
+  for (int a = c0; a < c1; ++a)
+    if (n_s[a] > 0) ne_s[rank++] = a;
+  const int nne = part[kSelThreads - 1];
+  __syncthreads();
+  if (M < nne) {
+    for (int j = t; j < M; j += kSelThreads) {
+      const int a = ne_s[static_cast<int>(floor((j + 0.5) * static_cast<double>(nne) / M))];
+      idx[j] = pp[off[a] + middle_out_member(n_s[a], 0)];
+      w[j] = static_cast<float>(n_s[a]);  // |G_a| / 1
     }
-  }
-  if (M >= nne) {
-    // Full rounds: round r takes member r (middle-out) of every non-empty cluster with more
-    // than r members, in cluster order, until M probes are taken; the last probe is taken in
-    // round R from cluster a_last.
-    int R = 0, a_last = 0;
-    for (int r = 0; r < maxn && taken < M; ++r)
-      for (int a = 0; a < C && taken < M; ++a) {
-        const int n = off[a + 1] - off[a];
-        if (n > r) {
-          idx[taken++] = pp[off[a] + middle_out_member(n, r)];
+  } else if (t == 0) {
+    int largest = 0;
+    for (int a = 0; a < C; ++a) largest = max(largest, n_s[a]);
+    int taken = 0, R = 0, a_last = 0;  // the last probe comes from cluster a_last in round R
+    for (int r = 0; r < largest && taken < M; ++r)
+      for (int a = 0; a < C && taken < M; ++a)
+        if (n_s[a] > r) {
+          idx[taken++] = pp[off[a] + middle_out_member(n_s[a], r)];
           R = r;
           a_last = a;
         }
-      }
     // Weights |G_a| / m_a, m_a = the rounds cluster a took part in: every round before R it had
     // members for, and round R if it came up before the last probe.
-    int t = 0;
-    for (int r = 0; r < maxn && t < M; ++r)
-      for (int a = 0; a < C && t < M; ++a) {
-        const int n = off[a + 1] - off[a];
-        if (n > r) {
-          const int m_a = min(n, R) + ((n > R && a <= a_last) ? 1 : 0);
-          w[t++] = static_cast<float>(static_cast<double>(n) / m_a);
+    int k = 0;
+    for (int r = 0; r < largest && k < M; ++r)
+      for (int a = 0; a < C && k < M; ++a)
+        if (n_s[a] > r) {
+          const int m_a = min(n_s[a], R) + ((n_s[a] > R && a <= a_last) ? 1 : 0);
+          w[k++] = static_cast<float>(static_cast<double>(n_s[a]) / m_a);
         }
-      }
     for (; taken < M; ++taken) {  // fewer members than probes (labels outside [0, C)): padding
       idx[taken] = 0;
       w[taken] = 0.0f;
     }
   }
-  double total = 0.0;
-  for (int j = 0; j < M; ++j) total += static_cast<double>(w[j]);
-  for (int j = 0; j < M; ++j) w[j] = total > 0.0 ? static_cast<float>(static_cast<double>(w[j]) / total) : 0.0f;
+  __syncthreads();  // the weights are written (global memory, visible to the workgroup)
+  if (t == 0) {  // normalized to sum to 1
+    double total = 0.0;
+    for (int j = 0; j < M; ++j) total += static_cast<double>(w[j]);
+    for (int j = 0; j < M; ++j) w[j] = total > 0.0 ? static_cast<float>(static_cast<double>(w[j]) / total) : 0.0f;
+  }
 }
 
 }  // namespace
@@ -176,8 +186,12 @@ extern "C" bsa_status bsa_select_probe_rows_layouts(int P, int S, int C, int M, 
                                                     const int32_t* offsets, int32_t* probe_idx, float* weights,
                                                     hipStream_t stream) {
   if (!perm || !offsets || !probe_idx || !weights || P < 1 || S < 1 || C < 1 || M < 1 || M > S) return BSA_E_ARG;
-  hipLaunchKernelGGL(select_probes_kernel, dim3((P + 63) / 64), dim3(64), 0, stream, P, S, C, M, perm, offsets,
-                     probe_idx, weights);
+  if (C > kMaxC || P > 65535) return BSA_E_UNSUPPORTED;
+  const size_t lds = (2 * static_cast<size_t>(C) + kSelThreads) * sizeof(int32_t);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(select_probes_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      static_cast<int>(lds));
+  hipLaunchKernelGGL(select_probes_kernel, dim3(P), dim3(kSelThreads), lds, stream, S, C, M, perm, offsets, probe_idx,
+                     weights);
   return launch_status();
 }
 
