@@ -603,10 +603,15 @@ def time_path(path, q, k, v, steps, warmup):
         return mark
 
     torch.cuda.synchronize()
+    calls = []  # per step: events on the caller's stream before and after the call
     t0 = time.perf_counter()
     for _ in range(steps):
         sm = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         path(q, k, v, mark=recorder(sm))
+        e1.record()
+        calls.append((e0, e1))
         marks.append(sm)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
@@ -614,7 +619,8 @@ def time_path(path, q, k, v, steps, warmup):
     for sm in marks:
         for name, e0, e1 in sm:
             stages.setdefault(name, []).append(e0.elapsed_time(e1))
-    return ms_per_step, {name: float(np.mean(x)) for name, x in stages.items()}, res
+    stages["call_median"] = float(np.median([e0.elapsed_time(e1) for e0, e1 in calls]))
+    return ms_per_step, {name: float(np.mean(x)) if name != "call_median" else x for name, x in stages.items()}, res
 
 
 def centroid_columns(res, cfg):
@@ -639,6 +645,7 @@ def path_figures(res, cfg, ms_per_step, stages_ms, probes):
     D = cfg.D
     return {
         "ms_per_call": round(ms_per_step, 4),
+        "ms_per_call_median": round(stages_ms.get("call_median", ms_per_step), 4),  # events around each call
         "density": round(pairs / full, 4),  # kept token pairs / S^2, averaged over heads
         "density_with_probes": round((pairs + probe_pairs) / full, 4),  # + M*S per head
         "executed_pairs": pairs + probe_pairs,
@@ -783,6 +790,8 @@ def main() -> int:
             "tau": "per head from {0.85, 0.90, 0.95}", "density": fig["density"], "compensation": True,
         },
         "ms_per_call": round(ms_per_step, 4),
+        "ms_per_call_median": fig["ms_per_call_median"],
+        "density_with_probes": fig["density_with_probes"],
         "executed_pairs": pairs,
         "roofline": {
             "bound": "mfma",

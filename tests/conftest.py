@@ -18,10 +18,17 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         import gpu_common
     except Exception:  # the CPU-only session never imports it
         return
+    tr = terminalreporter
+    frag = getattr(gpu_common, "FRAGILE", [])
+    if frag:
+        what, n, rows, bound = max(frag, key=lambda f: f[1] / max(f[2], 1))
+        total = sum(f[1] for f in frag), sum(f[2] for f in frag)
+        tr.write_sep("-", "mask parity: rows holding a fragile block")
+        tr.write_line(f"{len(frag)} mask heads, {total[0]} of {total[1]} rows ({total[0] / max(total[1], 1):.2%}); "
+                      f"worst head {n} of {rows} ({n / max(rows, 1):.1%}, bound {bound:.0%}) at {what}")
     errs = getattr(gpu_common, "ERRORS", [])
     if not errs:
         return
-    tr = terminalreporter
     tr.write_sep("-", "parity margins (worst error / bound)")
     groups = {}
     for what, metric, err, bound in errs:

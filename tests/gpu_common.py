@@ -37,6 +37,9 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
 
 
+# Every mask comparison of the session: (what, rows with a fragile block, rows, bound).
+FRAGILE: list = []
+
 # Every output comparison of the session: (what, metric, error, bound).  The terminal summary
 # (tests/conftest.py) prints the worst margins, so they are on record even under -q.
 ERRORS: list = []
@@ -136,5 +139,6 @@ def compare_masks(gpu_keep: np.ndarray, gpu_cnt: np.ndarray, gpu_idx: np.ndarray
             assert kept.sum() - kept.min() < target + 1e-5, f"{what}: row {a} keeps more blocks than needed"
     frac = n_frag_rows / max(rows, 1)
     print(f"[mask] {what}: {n_frag_rows} of {rows} rows hold a fragile block", flush=True)
+    FRAGILE.append((what, n_frag_rows, rows, max_fragile))
     assert frac <= max_fragile, f"{what}: {n_frag_rows} of {rows} rows fragile"
     return dict(fragile_rows=n_frag_rows)
