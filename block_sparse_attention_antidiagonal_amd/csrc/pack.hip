@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     }
     if constexpr (sizeof(T) == 2) atomicMax(emax_slot, emax);
     __syncthreads();
-    // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).
+    // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).  A wave
+    // takes 32 (16) consecutive d and 2 (4) neighbouring chunks of keys: its LDS reads then
+    // fall in distinct banks (key rows are D + 8 (D + 4) elements apart), and each V^T row
+    // gets 32 (64) contiguous bytes per store.
     if constexpr (sizeof(T) == 2) {
       const uint32_t tile_emax = *emax_slot;
       const bool f16 = tile_emax <= 142u && tile_emax >= 119u;  // bfloat16 exponent 142: [2^15, 2^16); 119: 2^-8
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         if (!f16) atomicOr(&hmix[bh], 1);
       }
       for (int idx = t; idx < D * (kPackTile / 8); idx += kPackThreads) {
-        const int d = idx / (kPackTile / 8), k0 = (idx % (kPackTile / 8)) * 8;
+        const int d = (idx / 2) % D, k0 = (2 * (idx / (2 * D)) + idx % 2) * 8;
         uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
     } else {
       if (t == 0) flags[tile] = 1;
       for (int idx = t; idx < D * (kPackTile / 4); idx += kPackThreads) {
-        const int d = idx / (kPackTile / 4), k0 = (idx % (kPackTile / 4)) * 4;
+        const int d = (idx / 4) % D, k0 = (4 * (idx / (4 * D)) + idx % 4) * 4;
         *reinterpret_cast<f32x4*>(Vtp32 + (tile * D + d) * kPackTile + k0) =
             f32x4{vt[vt_key(k0) * M::VROW + d], vt[vt_key(k0 + 1) * M::VROW + d], vt[vt_key(k0 + 2) * M::VROW + d],
                   vt[vt_key(k0 + 3) * M::VROW + d]};
