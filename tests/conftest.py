@@ -21,11 +21,16 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     tr = terminalreporter
     frag = getattr(gpu_common, "FRAGILE", [])
     if frag:
-        what, n, rows, bound = max(frag, key=lambda f: f[1] / max(f[2], 1))
-        total = sum(f[1] for f in frag), sum(f[2] for f in frag)
         tr.write_sep("-", "mask parity: rows holding a fragile block")
-        tr.write_line(f"{len(frag)} mask heads, {total[0]} of {total[1]} rows ({total[0] / max(total[1], 1):.2%}); "
-                      f"worst head {n} of {rows} ({n / max(rows, 1):.1%}, bound {bound:.0%}) at {what}")
+        for group in ("config", "stage"):
+            fs = [f for f in frag if f[0].startswith("config") == (group == "config")]
+            if not fs:
+                continue
+            what, n, rows, bound = max(fs, key=lambda f: f[1] / max(f[2], 1))
+            total = sum(f[1] for f in fs), sum(f[2] for f in fs)
+            tr.write_line(f"{group + ' masks':13s} {len(fs)} mask heads, {total[0]} of {total[1]} rows "
+                          f"({total[0] / max(total[1], 1):.2%}); worst head {n} of {rows} ({n / max(rows, 1):.1%}, "
+                          f"bound {bound:.0%}) at {what}")
     errs = getattr(gpu_common, "ERRORS", [])
     if not errs:
         return

@@ -49,8 +49,11 @@ def check_masks(wl, res, pairs):
             assert np.array_equal(keep[b, hm], want)
             continue
         ref = opipe.mask_scores(wl, b, hm)
+        # At most 6% of a head's rows may hold a fragile block: the oracle's scores alone decide
+        # which blocks are fragile, and the largest share on these workloads is 15 of 256 rows
+        # (video workload, head 1; 2.3% on average over its 40 heads).
         frag += compare_masks(keep[b, hm], cnt[b, hm], idx[b, hm], ref, float(wl.tau[hm]),
-                              f"mask b{b} head{hm}")["fragile_rows"]
+                              f"config {wl.name} mask b{b} head{hm}", max_fragile=0.06)["fragile_rows"]
     return frag
 
 
