@@ -14,7 +14,8 @@
 // (8 waves of 128 keys x 64 queries), the operands streaming through LDS in stages of one
 // token column (tt) and 64 bytes of head dimension, copied straight from global memory
 // (gathered through the cluster order) into XOR-swizzled LDS rows through a ring of four
-// stage buffers, three stages in flight.
+// stage buffers, copies three stages ahead of the products, and each wave reads the first
+// fragments of the next stage before the barrier that ends the current one.
 // Its epilogue keeps, per strided query row, the tile max, the tile sum of exponentials and
 // the per-block sums relative to that max; a second pass merges the tiles of a row (the
 // full-row softmax), sums the rows of a query block and normalizes.
@@ -166,40 +167,52 @@ __global__ __launch_bounds__(kSThreads, 1) void score_gemm_kernel(const T* __res
   if (stride > 1) copy_tokens(1);
   wait_vmem();
   __syncthreads();
-#pragma unroll
-  for (int x = 0; x < kNBuf - 1; ++x) issue(x);
   constexpr int kPerStage = 2 * C::NCH;  // tile copies per thread per stage
+  // Software pipeline across the barriers: at the barrier that ends stage st every stage up to
+  // st + 2 is in LDS for every wave, so a wave reads the first fragments of stage st + 1 before
+  // that barrier and starts its products right after it.  Copies run three stages ahead of
+  // the products (stage st + 4 is issued into the buffer stage st has just freed).
+  issue(0);
+  issue(1);
+  issue(2);
+  issue(3);
+  wait_vmem_n<2 * kPerStage>();  // stages 0 and 1 (the copies of 2 and 3 may be in flight)
+  pipe_barrier();
+  Frag<T> fa[4], fb[2];
+  auto load_frags = [&](const unsigned char* As, int ks) {
+    const unsigned char* Bs = As + C::OP_BYTES;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) swz_frag<SRow>(fa[m], As, kw * 128 + m * 32 + r, ks * 16 + 8 * h);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) swz_frag<SRow>(fb[n], Bs, qw * 64 + n * 32 + r, ks * 16 + 8 * h);
+  };
+  auto products = [&]() {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
+  };
+  load_frags(smem, 0);
   for (int base = 0; base < nst; base += kG) {
-    // Unrolled so that every buffer index and head-dimension offset is a constant.
 #pragma unroll
     for (int u = 0; u < kG; ++u) {
       const int st = base + u;
-      // Stage st is in LDS for every wave (the copies issued after it are the later stages'
-      // and possibly token copies, which only lengthen the wait), and every wave is done with
-      // stage st - 1, whose buffer the next copy refills.
-      const int later = min(kNBuf - 2, nst - 1 - st);
-      if (later >= 2)
-        wait_vmem_n<2 * kPerStage>();
-      else if (later == 1)
+      const unsigned char* As = smem + (u % kNBuf) * C::BUF_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        products();
+        if (ks + 1 < C::KS) load_frags(As, ks + 1);
+      }
+      if (st + 1 < nst) load_frags(smem + ((u + 1) % kNBuf) * C::BUF_BYTES, 0);
+      // The barrier ending stage st: stages up to st + 2 landed (st + 3 may be in flight);
+      // every wave is done with stage st's buffer, which stage st + 4 then refills.
+      const int later = min(1, nst - 3 - st);
+      if (later >= 1)
         wait_vmem_n<kPerStage>();
       else
         wait_vmem_n<0>();
       pipe_barrier();
-      if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
-      const unsigned char* As = smem + (u % kNBuf) * C::BUF_BYTES;
-      const unsigned char* Bs = As + C::OP_BYTES;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        Frag<T> fa[4], fb[2];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) swz_frag<SRow>(fa[m], As, kw * 128 + m * 32 + r, ks * 16 + 8 * h);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) swz_frag<SRow>(fb[n], Bs, qw * 64 + n * 32 + r, ks * 16 + 8 * h);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) acc[m][n] = mma(fa[m], fb[n], acc[m][n]);
-      }
+      if (st + 4 < nst) issue(st + 4);
     }
   }
   wait_vmem();
