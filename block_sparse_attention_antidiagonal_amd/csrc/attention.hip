@@ -31,6 +31,9 @@ constexpr int kRowsWG = 128;   // query rows per workgroup
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag (p <= 256)
 constexpr int kFlagBytes = 32;         // per-wave tile flags at the end of LDS (4 waves x 2 ints)
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 template <typename T, int D>
 struct Cfg {
@@ -54,7 +57,7 @@ struct Cfg {
 template <int D>
 struct RowState {
   f32x16 o[D / 32];
-  float m;  // running max, log2 units (may lag the true max by < kRescaleSlack)
+  float m;  // running max, log2 units (may lag the true max: < kRescaleSlack, < 14 in tile_step16)
   float l;  // this lane's partial sum (its 16 keys of every 32-key tile)
 };
 
@@ -313,25 +316,36 @@ struct KeyBias {  // one bias per key from LDS (centroid columns: log2 n_c or -i
 // log2(e); keys at or past `nvalid` do not exist.  pv16: for bfloat16 inputs the tile's V^T in
 // LDS is float16 and P is rounded to float16 (else both are bfloat16).  Bias, nvalid and pv16
 // are uniform over the workgroup, so the branches on them cost no divergence.
-template <typename T, int D, typename Lds>
+template <typename T, int D, typename Lds, int AHEAD = 1>
 __device__ __forceinline__ void tile_qk(const T* Ks, const Frag<T>* qf, f32x16& s0, f32x16& s1) {
   using C = Cfg<T, D>;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
   s0 = f32x16{};
   s1 = f32x16{};
-  // The fragments of step kk+1 are read while step kk's products run.
-  Frag<T> a0[2], a1[2];
-  Lds::kfrag(a0[0], Ks, r, 0, h);
-  Lds::kfrag(a1[0], Ks, 32 + r, 0, h);
+  // Fragments are read AHEAD steps before the products that use them.  The sparse attention's
+  // float16 loop reads two ahead (one ahead leaves each product waiting for its own LDS read),
+  // with group barriers that keep the compiler's schedule in that order; the other kernels,
+  // with less room in their registers, read one ahead.
+  Frag<T> a0[AHEAD + 1], a1[AHEAD + 1];
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    Lds::kfrag(a0[i], Ks, r, i, h);
+    Lds::kfrag(a1[i], Ks, 32 + r, i, h);
+  }
+  if constexpr (AHEAD > 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * AHEAD, 0);
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk) {
-    if (kk + 1 < C::KK) {
-      Lds::kfrag(a0[(kk + 1) & 1], Ks, r, kk + 1, h);
-      Lds::kfrag(a1[(kk + 1) & 1], Ks, 32 + r, kk + 1, h);
+    if (kk + AHEAD < C::KK) {
+      Lds::kfrag(a0[(kk + AHEAD) % (AHEAD + 1)], Ks, r, kk + AHEAD, h);
+      Lds::kfrag(a1[(kk + AHEAD) % (AHEAD + 1)], Ks, 32 + r, kk + AHEAD, h);
     }
-    s0 = mma(a0[kk & 1], qf[kk], s0);
-    s1 = mma(a1[kk & 1], qf[kk], s1);
+    s0 = mma(a0[kk % (AHEAD + 1)], qf[kk], s0);
+    s1 = mma(a1[kk % (AHEAD + 1)], qf[kk], s1);
+    if constexpr (AHEAD > 1) {
+      if (kk + AHEAD < C::KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
   }
 }
 
@@ -408,6 +422,33 @@ __device__ __forceinline__ void p_frag(Frag<T>& f, const f32x16 (&s)[2], int ks)
   frag_from_f32(f, x);
 }
 
+// O^T += V^T P^T over four 16-key steps with a float16 V^T tile; pfrag(ks, f) supplies the P
+// fragment of step ks.  Fragment n = ks * DT + dt of V^T is read PF products ahead (the
+// sparse attention's float16 loop: three, in the order the group barriers fix).
+template <typename T, int D, typename Lds, int PF = 1, typename PFrag>
+__device__ __forceinline__ void pv16_steps(const T* Vt, RowState<D>& st, PFrag&& pfrag) {
+  using C = Cfg<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, h = lane >> 5;
+  constexpr int NF = 4 * C::DT;
+  Frag16 va[PF + 1];
+#pragma unroll
+  for (int n = 0; n < PF; ++n) Lds::vfrag16(va[n], Vt, (n % C::DT) * 32 + r, n / C::DT, h);
+  if constexpr (PF > 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+  Frag16 pb;
+#pragma unroll
+  for (int n = 0; n < NF; ++n) {
+    const int ks = n / C::DT, dt = n % C::DT;
+    if (n + PF < NF) Lds::vfrag16(va[(n + PF) % (PF + 1)], Vt, ((n + PF) % C::DT) * 32 + r, (n + PF) / C::DT, h);
+    if (dt == 0) pfrag(ks, pb);
+    st.o[dt] = mma(va[n % (PF + 1)], pb, st.o[dt]);
+    if constexpr (PF > 1) {
+      if (n + PF < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+  }
+}
+
 // O^T += V^T P^T over four 16-key steps.  B fragment element i of step ks holds the key
 // ks*16 + 8*(i/4) + 4*h + i%4; the V^T fragment reads the same keys.
 template <typename T, int D, typename Lds>
@@ -417,18 +458,7 @@ __device__ __forceinline__ void tile_pv(const T* Vt, const f32x16 (&s)[2], RowSt
   const int r = lane & 31;
   const int h = lane >> 5;
   if (sizeof(T) == 2 && __builtin_expect(pv16, 1)) {
-    // Fragment n = ks * DT + dt; fragment n+1 is read while product n runs.
-    constexpr int NF = 4 * C::DT;
-    Frag16 va[2];
-    Lds::vfrag16(va[0], Vt, r, 0, h);
-    Frag16 pb;
-#pragma unroll
-    for (int n = 0; n < NF; ++n) {
-      const int ks = n / C::DT, dt = n % C::DT;
-      if (n + 1 < NF) Lds::vfrag16(va[(n + 1) & 1], Vt, ((n + 1) % C::DT) * 32 + r, (n + 1) / C::DT, h);
-      if (dt == 0) p_frag16(pb, s, ks);
-      st.o[dt] = mma(va[n & 1], pb, st.o[dt]);
-    }
+    pv16_steps<T, D, Lds>(Vt, st, [&](int ks, Frag16& f) { p_frag16(f, s, ks); });
   } else {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -455,6 +485,89 @@ __device__ __forceinline__ void tile_step(const T* Ks, const T* Vt, const Frag<T
   __builtin_amdgcn_s_setprio(0);
   tile_softmax<T, D>(s, st, c2, bias, nvalid);
   tile_pv<T, D, Lds>(Vt, s, st, pv16);
+}
+
+// Tile step of the float16 loop (bfloat16 inputs, every V^T tile float16).  The logits are
+// exponentiated against the running max as it stands, straight into the float16 P fragments,
+// and the row sums are taken from those fragments with float32 dot products, so the
+// normalisation adds exactly the weights that the P V product multiplies.  The tile's own max
+// is computed only when the running max is unset (first tile) or when some lane's sum of its 32
+// weights reaches 2^14 -- a logit at least 9 log2 units above the running max, with float16
+// range at stake; then the running max moves up to the tile's (O and l rescaled) and the
+// weights are formed again from the logits, which the first pass left intact.  Weights thus
+// stay below 2^14, and without the max the common tile saves its reduction.
+template <int D, typename Bias>
+__device__ __forceinline__ void tile_step16(const bf16_t* Ks, const bf16_t* Vt, const Frag<bf16_t>* qf,
+                                           RowState<D>& st, float c2, const Bias& bias, int nvalid) {
+  using C = Cfg<bf16_t, D>;
+  using Lds = SwzLds<bf16_t, D>;
+  const int h = (threadIdx.x & 63) >> 5;
+  f32x16 s[2];
+  __builtin_amdgcn_s_setprio(1);
+  tile_qk<bf16_t, D, Lds, 2>(Ks, qf, s[0], s[1]);
+  __builtin_amdgcn_s_setprio(0);
+  float xs = c2;  // scale still to apply to s
+  if (__builtin_expect(bias.active(), 0)) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[mt][j] = s[mt][j] * c2 + bias(mt * 32 + 8 * (j / 4) + 4 * h + (j % 4));
+    xs = 1.0f;
+  }
+  if (__builtin_expect(nvalid < kNK, 0)) {  // ragged last tile of a cluster
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (mt * 32 + 8 * (j / 4) + 4 * h + (j % 4) >= nvalid) s[mt][j] = -INFINITY;
+  }
+  Frag16 pf[4];  // P of the four 16-key steps
+  const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  auto weights = [&]() {
+    const float m_use = st.m == -INFINITY ? 0.0f : st.m;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[ks >> 1][(ks & 1) * 8 + i], xs, -m_use));
+        const float e1 = fast_exp2(__builtin_fmaf(s[ks >> 1][(ks & 1) * 8 + i + 1], xs, -m_use));
+        pf[ks].v[i] = static_cast<_Float16>(e0);
+        pf[ks].v[i + 1] = static_cast<_Float16>(e1);
+        const f16x2 pr = {pf[ks].v[i], pf[ks].v[i + 1]};
+        acc[ks] = __builtin_amdgcn_fdot2(pr, ones, acc[ks], false);
+      }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  float lsum = 0.0f;
+  bool need_max = __ballot(st.m == -INFINITY) != 0;
+  if (!need_max) {
+    lsum = weights();
+    need_max = __ballot(!(lsum < 16384.0f)) != 0;  // also catches an infinite weight
+  }
+  if (__builtin_expect(need_max, 0)) {
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x16& v = s[i / 4];
+      const int o = 4 * (i % 4);
+      t8[i] = fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3]));
+    }
+    float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])), fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    mx = fmaxf(mx, swap_halves(mx)) * xs;
+    if (mx > st.m) {
+      const float alpha = (st.m == -INFINITY) ? 0.0f : fast_exp2(st.m - mx);
+      st.m = mx;
+      st.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[dt][j] *= alpha;
+    }
+    lsum = weights();
+  }
+  st.l += lsum;
+  pv16_steps<bf16_t, D, Lds, 3>(Vt, st, [&](int ks, Frag16& f) { f = pf[ks]; });
 }
 
 template <typename T, int D>
@@ -1113,10 +1226,14 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
         if (entry_centroid(e1)) write_bias(bias0 + (BJ ^ 1) * kNK, tl - first_ctile);
         if (!ALL16) pv1 = flags_h[tl];
       }
-      if (wave_rows)
-        tile_step<T, D, SwzLds<T, D>>(
-            kbuf(BJ), vbuf(BJ), qf, st, c2, KeyBias{entry_centroid(e0) ? bias0 + BJ * kNK : nullptr},
-            entry_nvalid(e0), ALL16 || pv0 != 0);
+      if (wave_rows) {
+        const KeyBias kb{entry_centroid(e0) ? bias0 + BJ * kNK : nullptr};
+        if constexpr (ALL16)
+          tile_step16<D>(reinterpret_cast<const bf16_t*>(kbuf(BJ)), reinterpret_cast<const bf16_t*>(vbuf(BJ)),
+                         reinterpret_cast<const Frag<bf16_t>*>(qf), st, c2, kb, entry_nvalid(e0));
+        else
+          tile_step<T, D, SwzLds<T, D>>(kbuf(BJ), vbuf(BJ), qf, st, c2, kb, entry_nvalid(e0), pv0 != 0);
+      }
       wait_vmem();
       __syncthreads();
       e0 = e1;
