@@ -83,7 +83,8 @@ SIGNATURES = {
 _RESTYPES = {"bsa_status_string": ctypes.c_char_p, "bsa_sparse_attention_static_scratch_bytes": ctypes.c_size_t}
 
 BSA_F32, BSA_BF16 = 0, 1
-MAX_FIT_PROBES = 64  # bsa_probe_fit: 2 <= M <= this
+MAX_FIT_PROBES = 65536  # bsa_probe_fit: 2 <= M <= this
+MAX_PROBE_ROWS = 1024  # bsa_probe_attention(_packed): M <= this
 
 
 class BsaError(RuntimeError):

@@ -7,8 +7,9 @@
 // directions and applied to every row.  "Sparse-block compensation", section "Deviations
 // from the papers": probe weights are normalized to sum to 1.
 //
-// One workgroup per (batch, head) computes the fit in float64.  With M <= D probes the ridge
-// system is solved in its M x M dual form, which gives the same W:
+// One workgroup per (batch, head) computes the fit in float64.  With M <= 64 probes the ridge
+// system is solved in its M x M dual form, which gives the same W (more probes: the D x D
+// primal form further below):
 //   W = (Y^T Y + lambda I)^-1 Y^T T  =  Y^T (Y Y^T + lambda I)^-1 T,
 // with Y = Omega^1/2 X and T = Omega^1/2 Rc.  The principal directions of Rc^T Omega Rc = T^T T
 // come from the eigenvectors U of the M x M Gram matrix T T^T (Householder tridiagonalization,
@@ -500,6 +501,506 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   }
 }
 
+// ---------------------------------------------------------------- the fit for M > 64 probes
+//
+// The same fit in its D x D primal form, for more probes than the dual form's 64 (any M up
+// to kMaxPrimalM): with Y = Omega^1/2 X and T = Omega^1/2 Rc (rows y_m, t_m),
+//   C = T^T T = Rc^T Omega Rc  ->  V_r, its top eigenvectors (the principal residual directions);
+//   W V_r = (Y^T Y + lambda I)^-1 Y^T T V_r = (Y^T Y + lambda I)^-1 sum_m y_m (t_m^T V_r);
+//   A = diag(1/sigma) (W V_r) V_r^T,  c = rbar - mu A.
+// The probe rows stream from global memory in chunks of kChunkRows through LDS (three passes:
+// the weighted statistics, C, then Y^T Y and the right-hand sides), so M is not bounded by LDS;
+// the two N x N float64 matrices (N = D) take turns in one LDS array, each accumulated in
+// registers (a block of (N/16)^2 entries per thread) and stored when complete.  The eigenpairs
+// follow the dual kernel's four steps (Householder tridiagonalization, multisection on Sturm
+// counts, inverse iteration, back-transformation), with lanes holding N/64 columns each; the
+// Householder vector of step k is kept in row k right of the diagonal, the inverse iteration's
+// pivots and multipliers (for N = 128) in the lower-left block of the matrix, which the
+// reduction no longer reads.
+constexpr int kMaxPrimalM = 65536;
+constexpr int kChunkRows = 16;
+
+template <int N>
+struct PrimalSmem {
+  static constexpr int VS = kMaxRank + 1;  // row stride of the vector array
+  double G[N][N];  // C, then its reduction; later Y^T Y + lambda I and its factor; finally diag(1/sigma) W V_r
+  double V[N][VS];  // eigenvectors (column k = vector k); during the reduction, p = G v partial sums
+  double pv[N == 128 ? 1 : N][N == 128 ? 1 : 2 * kMaxRank];  // N = 64: pivots and multipliers
+  double mu[N], sig[N], rbar[N];
+  double dg[N], od[N], e2[N];
+  double lam[kMaxRank], u[kMaxRank];
+  double wave_part[kFitThreads / 64];
+  double wsum;
+  int r_eff;
+};
+
+// Reciprocal pivot (j = 0) and multiplier (j = 1) of element i of inverse-iteration vector k.
+template <int N>
+__device__ __forceinline__ double& inv_slot(PrimalSmem<N>& sm, int k, int i, int j) {
+  if constexpr (N == 128)
+    return sm.G[64 + (i >> 1)][32 * j + 16 * (i & 1) + k];  // row >= 64 > column: below the diagonal
+  else
+    return sm.pv[i][j * kMaxRank + k];
+}
+
+// Element i of a vector held N/64 per lane (lane i % 64, slot i / 64).
+template <int EL>
+__device__ __forceinline__ double lane_elem(const double (&x)[EL], int i) {
+  if constexpr (EL == 1) {
+    return readlane_f64(x[0], i);
+  } else {
+    return i < 64 ? readlane_f64(x[0], i) : readlane_f64(x[1], i - 64);
+  }
+}
+
+// out = sum over the rows m of f(m)^T g(m) (N x N, float64) with rows produced chunk by chunk:
+// fill(m0, rows) writes the rows m0 .. m0+rows-1 of f to stage_f and of g to stage_g
+// ([kChunkRows][N] each, float64, in LDS); each thread accumulates its block in registers.
+// diag_add is added on the diagonal.  Ends with every thread's block in acc (not stored).
+template <int N, typename Fill>
+__device__ __forceinline__ void gram_stream(int M, double* stage_f, double* stage_g, Fill&& fill,
+                                            double (&acc)[N / 16][N / 16]) {
+  constexpr int B = N / 16;
+  const int i0 = (threadIdx.x / 16) * B, j0 = (threadIdx.x % 16) * B;
+#pragma unroll
+  for (int r = 0; r < B; ++r)
+#pragma unroll
+    for (int c = 0; c < B; ++c) acc[r][c] = 0.0;
+  for (int m0 = 0; m0 < M; m0 += kChunkRows) {
+    const int rows = min(kChunkRows, M - m0);
+    fill(m0, rows);
+    __syncthreads();
+    for (int m = 0; m < rows; ++m) {
+      double a[B], b[B];
+#pragma unroll
+      for (int r = 0; r < B; ++r) {
+        a[r] = stage_f[m * N + i0 + r];
+        b[r] = stage_g[m * N + j0 + r];
+      }
+#pragma unroll
+      for (int r = 0; r < B; ++r)
+#pragma unroll
+        for (int c = 0; c < B; ++c) acc[r][c] += a[r] * b[c];
+    }
+    __syncthreads();  // the stage is read before the next chunk overwrites it
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(kFitThreads) void probe_fit_primal_kernel(const float* __restrict__ Os,
+                                                                        const float* __restrict__ Od,
+                                                                        const float* __restrict__ weights, int M,
+                                                                        int Hq, int Hkv, int nl, float lambda,
+                                                                        int rank, float* __restrict__ Aout,
+                                                                        float* __restrict__ cout) {
+  constexpr int D = N;
+  constexpr int EL = N / 64;  // columns per lane
+  constexpr int B = N / 16;   // Gram block per thread
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  PrimalSmem<N>& sm = *reinterpret_cast<PrimalSmem<N>*>(smem_raw);
+  const int bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const float* Osh = Os + static_cast<size_t>(bh) * M * D;
+  const float* Odh = Od + static_cast<size_t>(bh) * M * D;
+  if (nl > 1) weights += ((bh / Hq) * static_cast<size_t>(Hkv) + (bh % Hq) / (Hq / Hkv)) * M;  // the head's layout
+
+  double wp = 0.0;
+  for (int m = t; m < M; m += kFitThreads) wp += static_cast<double>(weights[m]);
+  const double wsum = block_sum(wp, sm.wave_part);
+  // Weighted mean and deviation of X0 = O[probe], weighted mean residual (one feature per thread).
+  for (int d = t; d < D; d += kFitThreads) {
+    double mu = 0.0, rb = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double wm = static_cast<double>(weights[m]) / wsum;
+      const double x = static_cast<double>(Osh[static_cast<size_t>(m) * D + d]);
+      mu += wm * x;
+      rb += wm * (static_cast<double>(Odh[static_cast<size_t>(m) * D + d]) - x);
+    }
+    double var = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double wm = static_cast<double>(weights[m]) / wsum;
+      const double x = static_cast<double>(Osh[static_cast<size_t>(m) * D + d]) - mu;
+      var += wm * x * x;
+    }
+    double sg = sqrt(var);
+    if (sg < 1e-6) sg = 1.0;
+    sm.mu[d] = mu;
+    sm.sig[d] = sg;
+    sm.rbar[d] = rb;
+  }
+  __syncthreads();
+  double* stage = &sm.G[0][0];  // the matrix is accumulated in registers while rows pass here
+  // t_m = sqrt(w_m) (R_m - rbar) and y_m = sqrt(w_m) (X0_m - mu) / sigma, float64.
+  auto row_t = [&](double* dst, int m0, int rows) {
+    for (int e = t; e < rows * D; e += kFitThreads) {
+      const int m = e / D, d = e % D;
+      const size_t g = static_cast<size_t>(m0 + m) * D + d;
+      const double sw = sqrt(static_cast<double>(weights[m0 + m]) / wsum);
+      dst[e] = sw * ((static_cast<double>(Odh[g]) - static_cast<double>(Osh[g])) - sm.rbar[d]);
+    }
+  };
+  auto row_y = [&](double* dst, int m0, int rows) {
+    for (int e = t; e < rows * D; e += kFitThreads) {
+      const int m = e / D, d = e % D;
+      const size_t g = static_cast<size_t>(m0 + m) * D + d;
+      const double sw = sqrt(static_cast<double>(weights[m0 + m]) / wsum);
+      dst[e] = sw * (static_cast<double>(Osh[g]) - sm.mu[d]) / sm.sig[d];
+    }
+  };
+  const int i0 = (t / 16) * B, j0 = (t % 16) * B;
+  {
+    double acc[B][B];
+    auto fill = [&](int m0, int rows) { row_t(stage, m0, rows); };
+    gram_stream<N>(M, stage, stage, fill, acc);
+#pragma unroll
+    for (int r = 0; r < B; ++r)
+#pragma unroll
+      for (int c = 0; c < B; ++c) sm.G[i0 + r][j0 + c] = acc[r][c];
+  }
+  __syncthreads();
+
+  // (1) Householder reduction of G to tridiagonal form (see the dual kernel); lane holds
+  // columns lane + 64 e.  The vector of step k is stored in row k right of the diagonal.
+  double (*pw)[N] = reinterpret_cast<double (*)[N]>(&sm.V[0][0]);  // [4][N] partial sums of G v
+  for (int k = 0; k < N - 2; ++k) {
+    double x[EL], v[EL];
+    double s2p = 0.0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int j = lane + 64 * e;
+      x[e] = j > k ? sm.G[k][j] : 0.0;
+      s2p += x[e] * x[e];
+    }
+    const double s2 = wave_sum_f64(s2p);
+    const double x0 = lane_elem<EL>(x, k + 1);
+    double alpha = 0.0, vn2 = 0.0;
+    if (s2 > 0.0) {
+      alpha = x0 >= 0.0 ? -sqrt(s2) : sqrt(s2);
+      vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
+    }
+    const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int j = lane + 64 * e;
+      v[e] = j > k ? (x[e] - (j == k + 1 ? alpha : 0.0)) * vinv : 0.0;
+    }
+    double acc[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = 0.0;
+    for (int c = k + 1 + wave; c < N; c += kFitThreads / 64) {
+      const double vc = lane_elem<EL>(v, c);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[e] += sm.G[c][lane + 64 * e] * vc;
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) pw[wave][lane + 64 * e] = acc[e];
+    __syncthreads();  // partial products complete; every wave has read row k
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < EL; ++e)
+        if (lane + 64 * e > k) sm.G[k][lane + 64 * e] = v[e];
+      if (lane == 0) {
+        sm.dg[k] = sm.G[k][k];
+        sm.od[k] = alpha;
+      }
+    }
+    if (vn2 > 0.0) {
+      double pl[EL], w[EL];
+      double vpp = 0.0;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int j = lane + 64 * e;
+        pl[e] = 0.0;
+        if (j > k) {
+#pragma unroll
+          for (int q = 0; q < kFitThreads / 64; ++q) pl[e] += pw[q][j];
+        }
+        vpp += v[e] * pl[e];
+      }
+      const double vp = wave_sum_f64(vpp);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) w[e] = 2.0 * pl[e] - 2.0 * vp * v[e];
+      for (int c = k + 1 + wave; c < N; c += kFitThreads / 64) {
+        const double vc = lane_elem<EL>(v, c), wc = lane_elem<EL>(w, c);
+#pragma unroll
+        for (int e = 0; e < EL; ++e)
+          if (lane + 64 * e > k) sm.G[c][lane + 64 * e] -= vc * w[e] + wc * v[e];
+      }
+    }
+    __syncthreads();  // the trailing block is updated
+  }
+  if (t == 0) {
+    sm.dg[N - 2] = sm.G[N - 2][N - 2];
+    sm.od[N - 2] = sm.G[N - 1][N - 2];
+    sm.dg[N - 1] = sm.G[N - 1][N - 1];
+    sm.od[N - 1] = 0.0;
+  }
+  __syncthreads();
+  if (t < N) sm.e2[t] = sm.od[t] * sm.od[t];
+  __syncthreads();
+
+  // (2) The largest kMaxRank eigenvalues by multisection on Sturm counts.
+  double emax2 = 0.0, glo = INFINITY, ghi = -INFINITY;
+  for (int i = 0; i < N; ++i) {
+    const double r0 = i > 0 ? fabs(sm.od[i - 1]) : 0.0;
+    const double r1 = i < N - 1 ? fabs(sm.od[i]) : 0.0;
+    glo = fmin(glo, sm.dg[i] - r0 - r1);
+    ghi = fmax(ghi, sm.dg[i] + r0 + r1);
+    emax2 = fmax(emax2, sm.e2[i]);
+  }
+  const double span = fmax(ghi - glo, 1e-300);
+  const double pivmin = 1e-290 * fmax(1.0, emax2);
+  auto below = [&](double xv) {
+    int neg = 0;
+    double q = 1.0;
+    for (int i = 0; i < N; ++i) {
+      q = (sm.dg[i] - xv) - (i > 0 ? sm.e2[i - 1] * __builtin_amdgcn_rcp(q) : 0.0);
+      if (fabs(q) < pivmin) q = -pivmin;
+      neg += q < 0.0 ? 1 : 0;
+    }
+    return neg;
+  };
+  {
+    const int k = t >> 4, j = t & 15;
+    double a = glo - 1e-3 * span, b = ghi + 1e-3 * span;
+    for (int it = 0; it < 13; ++it) {
+      const double xv = a + (b - a) * static_cast<double>(j + 1) / 17.0;
+      const bool ok = (N - below(xv)) <= k;
+      const unsigned long long mask = __ballot(ok);
+      const unsigned bits = static_cast<unsigned>(mask >> (16 * ((threadIdx.x & 63) >> 4))) & 0xffffu;
+      const int f = bits ? __builtin_ctz(bits) : 16;
+      const double na = f == 0 ? a : a + (b - a) * static_cast<double>(f) / 17.0;
+      const double nb = f == 16 ? b : a + (b - a) * static_cast<double>(f + 1) / 17.0;
+      a = na;
+      b = nb;
+    }
+    if (j == 0) sm.lam[k] = 0.5 * (a + b);
+  }
+  __syncthreads();
+  if (t == 0) {
+    const double lmax = sm.lam[0];
+    int r_eff = 0;
+    if (lmax > 0.0) r_eff = min(rank, N - below(1e-12 * lmax));
+    sm.r_eff = r_eff;
+  }
+  __syncthreads();
+  const int r_eff = sm.r_eff;
+
+  // (3) Inverse iteration (one thread per vector; vector k in column k of V).
+  if (t < r_eff) {
+    const int k = t;
+    const double lk = sm.lam[k];
+    const double tiny = 1e-14 * fmax(fabs(glo), fabs(ghi)) + pivmin;
+    double uu = sm.dg[0] - lk;
+    if (fabs(uu) < tiny) uu = tiny;
+    inv_slot<N>(sm, k, 0, 0) = 1.0 / uu;
+    for (int i = 1; i < N; ++i) {
+      const double l = sm.od[i - 1] / uu;
+      uu = (sm.dg[i] - lk) - l * sm.od[i - 1];
+      if (fabs(uu) < tiny) uu = tiny;
+      inv_slot<N>(sm, k, i, 0) = 1.0 / uu;
+      inv_slot<N>(sm, k, i, 1) = l;
+    }
+    for (int i = 0; i < N; ++i) sm.V[i][k] = 1.0 + static_cast<double>((i * 7 + k * 13) % 11) / 11.0;
+    for (int iter = 0; iter < 3; ++iter) {
+      double prev = sm.V[0][k];
+      for (int i = 1; i < N; ++i) {
+        prev = sm.V[i][k] - inv_slot<N>(sm, k, i, 1) * prev;
+        sm.V[i][k] = prev;
+      }
+      double next = 0.0, nrm = 0.0;
+      for (int i = N - 1; i >= 0; --i) {
+        const double vi = (i == N - 1 ? sm.V[i][k] : sm.V[i][k] - sm.od[i] * next) * inv_slot<N>(sm, k, i, 0);
+        sm.V[i][k] = vi;
+        next = vi;
+        nrm += vi * vi;
+      }
+      const double inv = 1.0 / sqrt(nrm);
+      for (int i = 0; i < N; ++i) sm.V[i][k] *= inv;
+    }
+  }
+  __syncthreads();
+  // Modified Gram-Schmidt in eigenvalue order (one wave, N/64 elements per lane).
+  if (t < 64) {
+    for (int k = 0; k < r_eff; ++k) {
+      for (int j = 0; j < k; ++j) {
+        double dp = 0.0;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) dp += sm.V[t + 64 * e][j] * sm.V[t + 64 * e][k];
+        const double dot = wave_sum_f64(dp);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) sm.V[t + 64 * e][k] -= dot * sm.V[t + 64 * e][j];
+      }
+      double np = 0.0;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) np += sm.V[t + 64 * e][k] * sm.V[t + 64 * e][k];
+      const double inv = 1.0 / sqrt(wave_sum_f64(np));
+#pragma unroll
+      for (int e = 0; e < EL; ++e) sm.V[t + 64 * e][k] *= inv;
+    }
+  }
+  __syncthreads();
+  // (4) Back-transformation, y <- H_s y for s = N-3 .. 0 (16-lane groups, one vector each);
+  // the reflector of step s is row s of G right of the diagonal.
+  {
+    const int k = t >> 4, q = t & 15;
+    if (k < r_eff) {
+      for (int s = N - 3; s >= 0; --s) {
+        double dot = 0.0;
+#pragma unroll
+        for (int c = 0; c < N / 16; ++c) {
+          const int i = q + 16 * c;
+          if (i > s) dot += sm.G[s][i] * sm.V[i][k];
+        }
+        dot = row16_sum(dot);
+#pragma unroll
+        for (int c = 0; c < N / 16; ++c) {
+          const int i = q + 16 * c;
+          if (i > s) sm.V[i][k] -= 2.0 * dot * sm.G[s][i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Y^T Y + lambda I and the right-hand sides Z = sum_m y_m (t_m^T V_r), one pass over the rows:
+  // each chunk stages y and t rows and the products z_m = t_m^T V_r.  Thread (wave q, lane)
+  // keeps Z[lane + 64 e][4 q + r], the layout of the solve below.
+  constexpr int kRhs = kMaxRank / (kFitThreads / 64);
+  double z[EL][kRhs];
+#pragma unroll
+  for (int e = 0; e < EL; ++e)
+#pragma unroll
+    for (int r = 0; r < kRhs; ++r) z[e][r] = 0.0;
+  {
+    double* sy = stage;
+    double* st = stage + kChunkRows * N;
+    double* sz = stage + 2 * kChunkRows * N;  // [kChunkRows][kMaxRank]
+    double acc[B][B];
+    auto fill = [&](int m0, int rows) {
+      row_y(sy, m0, rows);
+      row_t(st, m0, rows);
+      __syncthreads();
+      {  // z_m[k] for the chunk's rows: thread (m, k)
+        const int m = t / kMaxRank, k = t % kMaxRank;
+        if (m < rows) {
+          double s = 0.0;
+          if (k < r_eff)
+            for (int d = 0; d < D; ++d) s += st[m * N + d] * sm.V[d][k];
+          sz[m * kMaxRank + k] = s;
+        }
+      }
+      __syncthreads();
+      for (int m = 0; m < rows; ++m)
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          const double yv = sy[m * N + lane + 64 * e];
+#pragma unroll
+          for (int r = 0; r < kRhs; ++r) z[e][r] += yv * sz[m * kMaxRank + kRhs * wave + r];
+        }
+    };
+    static_assert(kChunkRows * kMaxRank == kFitThreads, "one z product per thread");
+    gram_stream<N>(M, sy, sy, fill, acc);
+#pragma unroll
+    for (int r = 0; r < B; ++r)
+#pragma unroll
+      for (int c = 0; c < B; ++c)
+        sm.G[i0 + r][j0 + c] = acc[r][c] + (i0 + r == j0 + c ? static_cast<double>(lambda) : 0.0);
+  }
+  __syncthreads();
+  // L D L^T of G (right-looking, both triangles; see the dual kernel), then the solve.
+  for (int k = 0; k < N - 1; ++k) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int j = lane + 64 * e;
+      if (j > k) {
+        const double rk = sm.G[k][j] / sm.G[k][k];
+        for (int i = k + 1 + wave; i < N; i += kFitThreads / 64) sm.G[i][j] -= sm.G[i][k] * rk;
+      }
+    }
+    __syncthreads();
+  }
+  {
+    double rdl[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) rdl[e] = 1.0 / sm.G[lane + 64 * e][lane + 64 * e];
+    for (int k = 0; k < N - 1; ++k) {
+      const double rk = lane_elem<EL>(rdl, k);
+      double zk[kRhs];
+#pragma unroll
+      for (int r = 0; r < kRhs; ++r) {
+        double col[EL];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) col[e] = z[e][r];
+        zk[r] = lane_elem<EL>(col, k);
+      }
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int j = lane + 64 * e;
+        const double g = j > k ? sm.G[k][j] * rk : 0.0;  // L[j][k]
+#pragma unroll
+        for (int r = 0; r < kRhs; ++r) z[e][r] -= g * zk[r];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e)
+#pragma unroll
+      for (int r = 0; r < kRhs; ++r) z[e][r] *= rdl[e];
+    for (int k = N - 1; k > 0; --k) {
+      double zk[kRhs];
+#pragma unroll
+      for (int r = 0; r < kRhs; ++r) {
+        double col[EL];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) col[e] = z[e][r];
+        zk[r] = lane_elem<EL>(col, k);
+      }
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int j = lane + 64 * e;
+        const double g = j < k ? sm.G[k][j] * rdl[e] : 0.0;  // L[k][j]
+#pragma unroll
+        for (int r = 0; r < kRhs; ++r) z[e][r] -= g * zk[r];
+      }
+    }
+  }
+  __syncthreads();  // the factor is read; its storage takes diag(1/sigma) W V_r
+  double (*WV)[kMaxRank + 1] = reinterpret_cast<double (*)[kMaxRank + 1]>(&sm.G[0][0]);
+#pragma unroll
+  for (int e = 0; e < EL; ++e)
+#pragma unroll
+    for (int r = 0; r < kRhs; ++r) {
+      const int d = lane + 64 * e, k = kRhs * wave + r;
+      WV[d][k] = k < r_eff ? z[e][r] / sm.sig[d] : 0.0;
+    }
+  __syncthreads();
+  if (t < r_eff) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += sm.mu[d] * WV[d][t];
+    sm.u[t] = s;
+  }
+  __syncthreads();
+  float* Ah = Aout + static_cast<size_t>(bh) * D * D;
+  {
+    const int j = t % D;
+    double vcol[kMaxRank];
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) vcol[k] = k < r_eff ? sm.V[j][k] : 0.0;
+    for (int i = t / D; i < D; i += kFitThreads / D) {
+      double a = 0.0;
+#pragma unroll
+      for (int k = 0; k < kMaxRank; ++k) a += WV[i][k] * vcol[k];
+      Ah[i * D + j] = static_cast<float>(a);
+    }
+  }
+  for (int j = t; j < D; j += kFitThreads) {
+    double cj = sm.rbar[j];
+    for (int k = 0; k < r_eff; ++k) cj -= sm.u[k] * sm.V[j][k];
+    cout[static_cast<size_t>(bh) * D + j] = static_cast<float>(cj);
+  }
+}
+
 // O <- O + O A + c for 128 rows per workgroup: (O A) on bf16 MFMA into LDS, then a
 // row-parallel pass adds O and c in float32 and rounds once.  O is exact in bfloat16; A is
 // split into high and low bfloat16 parts so the product keeps float32 accuracy.
@@ -740,10 +1241,22 @@ extern "C" bsa_status bsa_probe_fit(int B, int Hq, int Hkv, int D, const float* 
   if (n_layouts != 1 && static_cast<long long>(n_layouts) != static_cast<long long>(B) * Hkv) return BSA_E_ARG;
   if (D != 64 && D != 128) return BSA_E_UNSUPPORTED;
   if (M < 2) return BSA_E_ARG;
-  if (M > kMaxM) return BSA_E_UNSUPPORTED;
+  if (M > kMaxPrimalM) return BSA_E_UNSUPPORTED;
   if (!(lambda > 0.0f) || !(lambda < INFINITY)) return BSA_E_ARG;
   if (rank < 1 || rank > D) return BSA_E_ARG;
   if (rank > kMaxRank) return BSA_E_UNSUPPORTED;
+  if (M > kMaxM) {  // the primal form
+    auto launch = [&](auto kern, int smem) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      hipLaunchKernelGGL(kern, dim3(B * Hq), dim3(kFitThreads), smem, stream, O_sparse_probe, O_dense_probe, weights,
+                         M, Hq, Hkv, n_layouts, lambda, rank, A, c);
+    };
+    if (D == 128)
+      launch(probe_fit_primal_kernel<128>, static_cast<int>(sizeof(PrimalSmem<128>)));
+    else
+      launch(probe_fit_primal_kernel<64>, static_cast<int>(sizeof(PrimalSmem<64>)));
+    return launch_status();
+  }
   const int smem = static_cast<int>(sizeof(FitSmem));
   hipFuncSetAttribute(reinterpret_cast<const void*>(probe_fit_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   hipLaunchKernelGGL(probe_fit_kernel, dim3(B * Hq), dim3(kFitThreads), smem, stream, O_sparse_probe, O_dense_probe,

@@ -113,8 +113,9 @@ class SparseAttentionPath:
                 raise ValueError("scored masks need clusters of exactly `block` tokens (the last one may be "
                                  "shorter): cluster i must be score block i")
             self.tau = torch.as_tensor(np.asarray(cfg.tau, dtype=np.float32).reshape(-1)).to(self.device)
-        if cfg.probes and not 2 <= cfg.probes <= _lib.MAX_FIT_PROBES:
-            raise ValueError(f"probes must lie in [2, {_lib.MAX_FIT_PROBES}] (the ridge fit's range)")
+        max_probes = min(_lib.MAX_FIT_PROBES, _lib.MAX_PROBE_ROWS)
+        if cfg.probes and not 2 <= cfg.probes <= max_probes:
+            raise ValueError(f"probes must lie in [2, {max_probes}] (the probe rows' and the ridge fit's range)")
         if cfg.probes and cfg.mask_mode != "partitioned":
             idx, w = api.select_probe_rows(cfg.labels, cfg.C, cfg.probes)
             self.probe_idx = torch.as_tensor(idx).to(self.device)

@@ -304,7 +304,9 @@ bsa_status bsa_probe_attention_packed(int B, int Hq, int Hkv, int S, int D, int 
  *   1: one set for every head; B * Hkv: head (b, h) takes row b * Hkv + h / (Hq / Hkv), the
  *   weights of its layout's probes)
  *   A float [B, Hq, D, D] out (row-major: correction_j = sum_i o_i A[i][j] + c_j); c float [B, Hq, D] out
- * Needs 2 <= M <= 64, lambda > 0 and 1 <= rank <= 16 (rank <= D).
+ * Needs 2 <= M <= 65536, lambda > 0 and 1 <= rank <= 16 (rank <= D).  Up to 64 probes the fit
+ * runs in its M x M dual form (the probe rows held in LDS); with more, in the D x D primal form,
+ * the probe rows streamed from global memory.  Both give the map above.
  */
 bsa_status bsa_probe_fit(int B, int Hq, int Hkv, int D, const float* O_sparse_probe, const float* O_dense_probe,
                          const float* weights, int M, int n_layouts, float lambda, int rank, float* A, float* c,

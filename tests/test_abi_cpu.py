@@ -142,7 +142,7 @@ def test_host_validation_rejects_before_launch(lib):
     # workspace too small
     assert lib.bsa_cluster_layout(1, dummy, 100, 4, dummy, dummy, dummy, dummy, 0, None) == 5
     # too many probes for the fit; bad lambda
-    assert lib.bsa_probe_fit(1, 1, 1, 128, dummy, dummy, dummy, 65, 1, ctypes.c_float(0.1), 16, dummy, dummy, None) == 4
+    assert lib.bsa_probe_fit(1, 1, 1, 128, dummy, dummy, dummy, 65537, 1, ctypes.c_float(0.1), 16, dummy, dummy, None) == 4
     assert lib.bsa_probe_fit(1, 1, 1, 128, dummy, dummy, dummy, 64, 1, ctypes.c_float(0.0), 16, dummy, dummy, None) == 1
     assert lib.bsa_probe_fit(1, 1, 1, 128, dummy, dummy, dummy, 64, 1, ctypes.c_float(0.1), 17, dummy, dummy, None) == 4
     # tau count must be 1 or one per head

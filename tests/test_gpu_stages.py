@@ -472,7 +472,9 @@ def fit_inputs(M, D, H=3, seed=0):
     return xs.astype(np.float32), xd.astype(np.float32), w.astype(np.float32)
 
 
-@pytest.mark.parametrize("D,M,rank", [(128, 64, 16), (64, 16, 4), (128, 2, 16), (128, 33, 16), (64, 64, 16)])
+# M <= 64: the dual M x M form; M > 64: the primal D x D form (probe rows streamed).
+@pytest.mark.parametrize("D,M,rank", [(128, 64, 16), (64, 16, 4), (128, 2, 16), (128, 33, 16), (64, 64, 16),
+                                      (128, 65, 16), (64, 96, 16), (128, 300, 12), (64, 520, 16)])
 def test_probe_fit(bsa, D, M, rank):
     say(f"probe fit D={D} M={M} r={rank}")
     xs, xd, w = fit_inputs(M, D, seed=M + D)
@@ -481,6 +483,29 @@ def test_probe_fit(bsa, D, M, rank):
     A_h, c_h = host(A), host(c)
     for h in range(xs.shape[1]):
         fit = orep.ridge_fit(xs[0, h], xd[0, h], w, 0.1, rank)
+        scale = np.max(np.abs(fit["A"])) + 1e-30
+        assert np.max(np.abs(A_h[0, h] - fit["A"])) <= 1e-4 * scale + 1e-6, np.max(np.abs(A_h[0, h] - fit["A"]))
+        assert np.max(np.abs(c_h[0, h] - fit["c"])) <= 1e-4 * (np.max(np.abs(fit["c"])) + scale) + 1e-6
+
+
+@pytest.mark.parametrize("D,M", [(64, 100), (128, 40), (128, 200)])
+def test_probe_fit_low_rank(bsa, D, M):
+    """A residual of rank 3 (plus a constant): three directions pass the 1e-12 eigenvalue
+    threshold, so the rank-16 fit keeps 3; one feature has no spread (sigma taken as 1)."""
+    say(f"probe fit low-rank residual D={D} M={M}")
+    rng = np.random.default_rng(D + M)
+    xs = rng.standard_normal((1, 2, M, D)) * rng.uniform(0.3, 2.0, size=D)
+    xs[..., 5] = 0.75
+    U = rng.standard_normal((D, 3))
+    V = rng.standard_normal((3, D)) * 0.1
+    xd = xs + (xs @ U) @ V + 0.2
+    xs, xd = xs.astype(np.float32), xd.astype(np.float32)
+    w = rng.uniform(0.5, 2.0, size=M).astype(np.float32)
+    A, c = bsa.probe_fit(torch.from_numpy(xs).cuda(), torch.from_numpy(xd).cuda(), torch.from_numpy(w).cuda(), 0.1, 16)
+    A_h, c_h = host(A), host(c)
+    for h in range(2):
+        fit = orep.ridge_fit(xs[0, h], xd[0, h], w, 0.1, 16)
+        assert fit["r_eff"] == 3
         scale = np.max(np.abs(fit["A"])) + 1e-30
         assert np.max(np.abs(A_h[0, h] - fit["A"])) <= 1e-4 * scale + 1e-6, np.max(np.abs(A_h[0, h] - fit["A"]))
         assert np.max(np.abs(c_h[0, h] - fit["c"])) <= 1e-4 * (np.max(np.abs(fit["c"])) + scale) + 1e-6
