@@ -126,44 +126,70 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
 #pragma unroll
   for (int e = 0; e < EPC; ++e) ks[e] = vs[e] = 0.0f;
   const int ntiles = (n + kPackTile - 1) / kPackTile;
+  // Loads are issued in batches: the token indices of all of a thread's rows of a tile, then
+  // all their K and V chunks, so that each tile costs one round trip for the indices and one
+  // for the rows.  The rows of tile j+1 are requested before tile j is processed.
+  auto load_idx = [&](int j, int (&p)[kItems]) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int r = j * kPackTile + kg + i * kKeyGroups;
+      p[i] = r < n ? perm[lo + r] : -1;
+    }
+  };
+  // Rows past the cluster read token 0 (always present) and are replaced by zeros where they
+  // are used: the loads are unconditional, so none of them waits behind a branch.
+  auto load_rows = [&](const int (&p)[kItems], uint4 (&kv)[kItems], uint4 (&vv)[kItems]) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const size_t row = static_cast<size_t>(p[i] >= 0 ? p[i] : 0) * D + ch * EPC;
+      kv[i] = *reinterpret_cast<const uint4*>(Kh + row);
+      vv[i] = *reinterpret_cast<const uint4*>(Vh + row);
+    }
+  };
+  uint4 kv[kItems], vv[kItems];
+  if (ntiles > 0) {
+    int p0[kItems];
+    load_idx(0, p0);
+    load_rows(p0, kv, vv);
+  }
   for (int j = 0; j < ntiles; ++j) {
     const size_t tile = bh * tiles_per_head + tile_off[c] + j;
     uint32_t* emax_slot = &emax_s[j & 1];
     if (t == 0) *emax_slot = 0;
-    uint4 kv[kItems], vv[kItems];
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int r = j * kPackTile + kg + i * kKeyGroups;
-      kv[i] = vv[i] = make_uint4(0, 0, 0, 0);
-      if (r < n) {
-        const size_t row = static_cast<size_t>(perm[lo + r]) * D + ch * EPC;
-        kv[i] = *reinterpret_cast<const uint4*>(Kh + row);
-        vv[i] = *reinterpret_cast<const uint4*>(Vh + row);
-      }
+    uint4 kn[kItems], vn[kItems];
+    if (j + 1 < ntiles) {
+      int p1[kItems];
+      load_idx(j + 1, p1);
+      load_rows(p1, kn, vn);
     }
-    __syncthreads();  // the slot cleared; the previous tile's V^T reads are done
+    // LDS-only barriers in the loop: the compiler's barrier would also wait for the loads of
+    // tile j+1 (the registers of tile j are awaited where they are used).
+    pipe_barrier();  // the slot cleared; the previous tile's V^T reads are done
     uint32_t emax = 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int key = kg + i * kKeyGroups;
-      *reinterpret_cast<uint4*>(Kp + (tile * kPackTile + key) * D + ch * EPC) = kv[i];
-      const T* ke = reinterpret_cast<const T*>(&kv[i]);
-      const T* ve = reinterpret_cast<const T*>(&vv[i]);
+      const bool in = j * kPackTile + key < n;
+      const uint4 zero = make_uint4(0, 0, 0, 0);
+      const uint4 kq = in ? kv[i] : zero, vq = in ? vv[i] : zero;
+      *reinterpret_cast<uint4*>(Kp + (tile * kPackTile + key) * D + ch * EPC) = kq;
+      const T* ke = reinterpret_cast<const T*>(&kq);
+      const T* ve = reinterpret_cast<const T*>(&vq);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         ks[e] += to_f32(ke[e]);
         vs[e] += to_f32(ve[e]);
       }
       if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vv[i];
+        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vq;
 #pragma unroll
         for (int e = 0; e < EPC; ++e) emax = max(emax, bf16_exp(ve[e].bits));
       } else {
-        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vv[i];
+        *reinterpret_cast<uint4*>(vt + key * M::VROW + ch * EPC) = vq;
       }
     }
     if constexpr (sizeof(T) == 2) atomicMax(emax_slot, emax);
-    __syncthreads();
+    pipe_barrier();
     // V^T rows: [d][64 keys], 16-bit (8 keys per 16-byte chunk) or float32 (4 keys).  A wave
     // takes 32 (16) consecutive d and 2 (4) neighbouring chunks of keys: its LDS reads then
     // fall in distinct banks (key rows are D + 8 (D + 4) elements apart), and each V^T row
@@ -192,6 +218,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_cluster_kernel(
         *reinterpret_cast<f32x4*>(Vtp32 + (tile * D + d) * kPackTile + k0) =
             f32x4{vt[vt_key(k0) * M::VROW + d], vt[vt_key(k0 + 1) * M::VROW + d], vt[vt_key(k0 + 2) * M::VROW + d],
                   vt[vt_key(k0 + 3) * M::VROW + d]};
+      }
+    }
+    if (j + 1 < ntiles) {
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        kv[i] = kn[i];
+        vv[i] = vn[i];
       }
     }
   }
