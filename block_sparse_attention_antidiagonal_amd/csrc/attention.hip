@@ -1277,16 +1277,18 @@ __global__ __launch_bounds__(kThreads, (attn_occupancy<T, FAST>())) void sparse_
       const float v = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
       lse[bhq * S + qtok] = v;
     }
-    __syncthreads();
+    // Each wave stores its own 32 rows, 64 / ZCPR whole rows per instruction; a row's token
+    // comes from the lane that loaded its query (a lane shuffle, not a global load).
     constexpr int ZCPR = D / L::ZEPC;  // 16-byte chunks per output row
-#pragma unroll 2
-    for (int idx = threadIdx.x; idx < kRowsWG * ZCPR; idx += kThreads) {
-      const int row = idx / ZCPR, ch = idx % ZCPR;
-      if (row < nrows) {
-        const int tok = qperm_h[rt + row];
+    constexpr int RPI = 64 / ZCPR;     // rows per store instruction
+#pragma unroll 1
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int rw = k * RPI + lane / ZCPR, ch = lane % ZCPR;  // row within the wave
+      const int row = wave * 32 + rw;
+      const int tok = __shfl(qtok, rw);
+      if (row < nrows)
         *reinterpret_cast<uint4*>(Oh + static_cast<size_t>(tok) * D + ch * L::ZEPC) =
             *reinterpret_cast<const uint4*>(Z + row * L::ZROW + ch * L::ZEPC);
-      }
     }
     __syncthreads();
   }
