@@ -73,6 +73,11 @@ PROFILE_COMMANDS = {
           "--no-cpu-baseline",
     "l2": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
           "-d $R/gpurun_out/prof -o l2 -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    # where the waves' time goes: waiting to issue, waiting on memory/LDS, VALU beside MFMA
+    "issue": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+             "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+             "SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof -o issue -- python3 "
+             "$R/bench.py --profile-kernels 3 --no-cpu-baseline",
     # the partitioned (SparsePR) call alone
     "trace_partitioned": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
                          "csv -d $R/gpurun_out/prof -o trace_partitioned -- python3 $R/bench.py --steps 5 "
@@ -218,6 +223,37 @@ def _summarize_counters(d: str, out_path: str) -> None:
                           f"{mean('SQ_INSTS_VALU'):.3g} | {mean('SQ_INSTS_LDS'):.3g} | {100 * conf:.1f}% | "
                           f"{100 * hit / (hit + miss) if hit + miss > 0 else 0.0:.1f}% |"))
     lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    issue_csv = os.path.join(d, "issue_counter_collection.csv")
+    if os.path.exists(issue_csv):
+        iss = _counters_by_dispatch(issue_csv)
+        lines += ["", "## Issue and wait counters", "", "```", PROFILE_COMMANDS["issue"], "```", "",
+                  "Per kernel, the mean over its dispatches of at least 20 us.  Wave shares are over the waves' "
+                  "resident cycles (SQ_WAVE_CYCLES): waiting to issue (SQ_WAIT_INST_ANY: an instruction is ready "
+                  "but its unit is taken, e.g. by the other wave's MFMAs), waiting on a counter or barrier "
+                  "(SQ_WAIT_ANY), issuing VALU (SQ_ACTIVE_INST_VALU) and LDS (SQ_ACTIVE_INST_LDS) work; per SIMD "
+                  "over the cycles that elapsed at the seen clock: MFMA busy and cycles in which a VALU "
+                  "instruction issued while the MFMA unit was busy (SQ_VALU_MFMA_COEXEC_CYCLES).", "",
+                  "| kernel | us | clock GHz | waves per SIMD | wait to issue | wait on counter | VALU issue | "
+                  "LDS issue | MFMA busy | VALU beside MFMA |",
+                  "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        rows = []
+        for k, ds in iss.items():
+            ds = [e for e in ds if e["dur_ns"] >= 20000]
+            if not ds or k.startswith("__amd"):
+                continue
+            mean = lambda key: float(np.mean([e.get(key, 0.0) for e in ds]))
+            dur, grbm = mean("dur_ns"), mean("GRBM_GUI_ACTIVE")
+            elapsed = grbm / XCDS  # cycles at the seen clock
+            wave = 4.0 * mean("SQ_WAVE_CYCLES")  # the SQ wave counters count quad-cycles
+            if elapsed <= 0 or wave <= 0:
+                continue
+            share = lambda key: 100.0 * 4.0 * mean(key) / wave
+            rows.append((dur, f"| `{k}` | {dur / 1e3:.1f} | {elapsed / dur:.2f} | {wave / SIMDS / elapsed:.2f} | "
+                              f"{share('SQ_WAIT_INST_ANY'):.1f}% | {share('SQ_WAIT_ANY'):.1f}% | "
+                              f"{share('SQ_ACTIVE_INST_VALU'):.1f}% | {share('SQ_ACTIVE_INST_LDS'):.1f}% | "
+                              f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (SIMDS * elapsed):.1f}% | "
+                              f"{100 * mean('SQ_VALU_MFMA_COEXEC_CYCLES') / (SIMDS * elapsed):.1f}% |"))
+        lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
