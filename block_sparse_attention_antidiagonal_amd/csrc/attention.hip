@@ -1523,8 +1523,10 @@ __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
     t1 = comp ? first_ctile + ctiles : first_ctile;
   } else {
     const int ntiles = tile_off[C];
-    t0 = ci * tpc;
-    t1 = min(ntiles, t0 + tpc);
+    // tpc == 0: the head's tiles are split evenly over the chunks (at most 2 kNK each).
+    const int per = tpc > 0 ? tpc : (ntiles + nchunks - 1) / nchunks;
+    t0 = ci * per;
+    t1 = min(ntiles, t0 + per);
   }
   // Tile t belongs to cluster c with tile_off[c] <= t < tile_off[c + 1].
   if (!cen && static_cast<int>(threadIdx.x) < t1 - t0) {
@@ -2014,10 +2016,22 @@ bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void
                                int Cq = 1, bool comp = false, float* Os = nullptr) {
   const PackLayout PL = pack_layout(B, Hkv, S, D, C, sizeof(bf16_t), nl);
   const unsigned char* base = static_cast<const unsigned char*>(packed);
-  const int tpc = packed_probe_tpc(PL.first_centroid_tile);
-  const int nchunks = packed_probe_chunks(PL.first_centroid_tile);
   const bool sparse = Os != nullptr;
   const int nrows = sparse ? 2 * M : M;
+  int tpc = packed_probe_tpc(PL.first_centroid_tile);
+  int nchunks = packed_probe_chunks(PL.first_centroid_tile);  // the most chunks (sizes the workspace)
+  if (sparse && nrows <= kRowsWG) {
+    // The repair's pass (dense and sparse rows of up to 64 probes in one row tile): as many
+    // chunks per head as one round of the workgroups the device runs at once takes, each
+    // splitting the head's filled tiles (tile_off[C], read by the kernel) evenly.  Fixed
+    // chunks over the allocated tile range left a partial second round: on the video workload
+    // 32 tiles per chunk took 0.66 ms, 48 0.57 ms, 64 0.65 ms, 96 0.87 ms.
+    const int slots = device_cus() * 2 * 9 / 10;
+    const int want = max(1, slots / (B * Hq));
+    const int least = (PL.first_centroid_tile + 2 * kNK - 1) / (2 * kNK);  // chunks of at most 2 kNK tiles
+    nchunks = max(least, min(nchunks, want));
+    tpc = 0;
+  }
   const int nch = sparse ? nchunks + 1 : nchunks;
   const int qtiles = (nrows + kRowsWG - 1) / kRowsWG;
   const int words = sparse ? (C + 31) / 32 : 0;
