@@ -756,8 +756,8 @@ def main() -> int:
                     help="time the headline path only (no repair workloads or side measurements)")
     ap.add_argument("--partitioned-only", action="store_true",
                     help="time the partitioned (SparsePR) call alone and print its figures")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="run the K/V packing and probe rows on the caller's stream too")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the K/V packing on a second stream beside the scores (default: before them)")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
                     help="launch each kernel K times on its own, then one plain copy (for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -779,7 +779,7 @@ def main() -> int:
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     wl = make_config(2)
     cfg = bsa.PathConfig.from_workload(wl)
-    cfg.overlap = not args.no_overlap
+    cfg.overlap = args.overlap
     path = bsa.SparseAttentionPath(cfg)
     q = torch.from_numpy(wl.q).to(torch.bfloat16).cuda()
     k = torch.from_numpy(wl.k).to(torch.bfloat16).cuda()

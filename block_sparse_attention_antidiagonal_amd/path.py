@@ -11,9 +11,11 @@ attention runs and every row is corrected before its single rounding.  Every sta
 or a few kernel launches on the current stream; nothing is computed on the host except the
 probe selection, which depends only on the labels and is done once.
 
-Streams: the K/V packing depends only on the inputs and the layout, so it runs on a second
-stream (default priority) while the scores and the top-p masks run on the caller's stream;
-the probe rows and the attention wait for both.
+Streams: the K/V packing depends only on the inputs and the layout, so with
+``PathConfig.overlap`` it runs on a second stream (default priority) while the scores and the
+top-p masks run on the caller's stream, and the probe rows and the attention wait for both.
+The default runs it on the caller's stream before the scores: both kernels fill the chip, so
+side by side each slows down by about what the other takes, and the call is no faster.
 """
 
 from __future__ import annotations
@@ -51,7 +53,7 @@ class PathConfig:
     probes: int = 0
     lam: float = 0.1
     rank: int = 16
-    overlap: bool = True  # the pack on a second stream, beside scores and top-p
+    overlap: bool = False  # the pack on a second stream, beside scores and top-p (no faster)
     route_density: float = 0.2  # routed modes: executed-pair density (probe rows included), a fraction of S
     partition_iters: int = 4  # partitioned mode: Lloyd iterations of each grouping
 

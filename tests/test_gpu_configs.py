@@ -30,8 +30,10 @@ def bsa():
     return m
 
 
-def run_gpu(bsa, wl):
-    path = bsa.SparseAttentionPath(bsa.PathConfig.from_workload(wl))
+def run_gpu(bsa, wl, overlap=False):
+    cfg = bsa.PathConfig.from_workload(wl)
+    cfg.overlap = overlap  # the pack on a second stream (configs 1 and 3) or after the scores
+    path = bsa.SparseAttentionPath(cfg)
     q, k, v = dev(wl.q, wl.dtype), dev(wl.k, wl.dtype), dev(wl.v, wl.dtype)
     res = path(q, k, v, keep_sparse=True)
     torch.cuda.synchronize()
@@ -61,7 +63,7 @@ def check_masks(wl, res, pairs):
 def test_small_config_every_row(bsa, cfg):
     say(f"config {cfg} full")
     wl = make_config(cfg)
-    path, res = run_gpu(bsa, wl)
+    path, res = run_gpu(bsa, wl, overlap=cfg == 1)
     Hm = res.mask.Hm
     check_masks(wl, res, [(b, h) for b in range(wl.B) for h in range(Hm)])
     keep = res.mask.keep.cpu().numpy()
@@ -86,7 +88,7 @@ def test_video_config_sampled(bsa, cfg, heads):
     say(f"config {cfg} generate")
     wl = make_config(cfg)
     say(f"config {cfg} gpu path")
-    path, res = run_gpu(bsa, wl)
+    path, res = run_gpu(bsa, wl, overlap=cfg == 3)
     keep = res.mask.keep.cpu().numpy()
     if cfg in (2, 4):  # every mask head (40, and 2 x 8 pooled group masks)
         mask_pairs = [(b, hm) for b in range(wl.B) for hm in range(res.mask.Hm)]
