@@ -73,6 +73,12 @@ PROFILE_COMMANDS = {
           "--no-cpu-baseline",
     "l2": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
           "-d $R/gpurun_out/prof -o l2 -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    # the grouped-query workload's attention alone: HBM bytes, then L2 hits (its five query
+    # heads of a group share their K/V tiles through L2)
+    "gqa_fetch": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                 "-d $R/gpurun_out/prof -o gqa_fetch -- python3 $R/bench.py --profile-gqa 3",
+    "gqa_l2": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
+              "-d $R/gpurun_out/prof -o gqa_l2 -- python3 $R/bench.py --profile-gqa 3",
     # where the waves' time goes: waiting to issue, waiting on memory/LDS, VALU beside MFMA
     "issue": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
              "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
@@ -254,8 +260,48 @@ def _summarize_counters(d: str, out_path: str) -> None:
                               f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (SIMDS * elapsed):.1f}% | "
                               f"{100 * mean('SQ_VALU_MFMA_COEXEC_CYCLES') / (SIMDS * elapsed):.1f}% |"))
         lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    lines += _summarize_gqa(d)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def _summarize_gqa(d: str) -> list:
+    """The float16 attention kernel of the headline (one query head per K/V head) beside the
+    grouped-query workload's (five query heads per K/V head): fetched bytes per launch against
+    the packed K/V bytes they cover, and the L2 hit rate, from the fetch/l2 and gqa_fetch/gqa_l2
+    runs (each run's FETCH_SIZE scaled by its own closing copy)."""
+    runs = [("video, 40 query heads on 40 K/V heads", "fetch", "l2", 40, 1),
+            ("grouped-query, 2 x 40 query heads on 2 x 8 K/V heads", "gqa_fetch", "gqa_l2", 16, 5)]  # kv heads, group
+    copy = "__amd_rocclr_copyBuffer"
+    rows = []
+    for title, fname, lname, kv_heads, group in runs:
+        fcsv = os.path.join(d, f"{fname}_counter_collection.csv")
+        lcsv = os.path.join(d, f"{lname}_counter_collection.csv")
+        if not (os.path.exists(fcsv) and os.path.exists(lcsv)):
+            return []
+        fe, l2 = _counters_by_dispatch(fcsv), _counters_by_dispatch(lcsv)
+        scale = COPY_BYTES / (sum(e.get("FETCH_SIZE", 0.0) for e in fe.get(copy, [])) * 1024.0)
+        name = next((k for k in fe if k.startswith(ATTN_KERNEL) and k.endswith("true, false>")), None)
+        if name is None:
+            return []
+        fd = [e for e in fe[name] if e["dur_ns"] >= 20000]
+        ld = [e for e in l2.get(name, []) if e["dur_ns"] >= 20000]
+        fetch = float(np.mean([e["FETCH_SIZE"] for e in fd])) * 1024.0 * scale
+        hit = float(np.mean([e["TCC_HIT_sum"] for e in ld]))
+        miss = float(np.mean([e["TCC_MISS_sum"] for e in ld]))
+        dur = float(np.mean([e["dur_ns"] for e in ld]))
+        # packed K/V: the token tiles (ceil(S/64) when clusters fill their tiles) and the
+        # centroid tiles (256 clusters / 64), 64 keys x 128 features x 2 bytes x 2 (K and V)
+        packed = kv_heads * (math.ceil(32760 / 64) + 4) * 64 * 128 * 2 * 2
+        rows.append(f"| {title} | {group} | {dur / 1e3:.0f} | {packed / 1e9:.3f} | {fetch / 1e9:.2f} | "
+                    f"{fetch / (kv_heads * group) / 1e9:.3f} | {100 * hit / (hit + miss):.1f}% |")
+    return ["", "## K/V tiles shared by the query heads of a group", "", "```", PROFILE_COMMANDS["gqa_fetch"],
+            PROFILE_COMMANDS["gqa_l2"], "```", "",
+            "The float16 attention kernel, mean over its launches; the first row from the `fetch` and `l2` runs "
+            "above.  The units of a group's query heads (same mask row, same tiles) run next to each other on "
+            "one XCD, so their tile copies meet in its L2.", "",
+            "| workload | query heads per K/V head | us | packed K/V GB | fetched GB per launch | "
+            "fetched GB per query head | L2 hit |", "|---|---:|---:|---:|---:|---:|---:|"] + rows
 
 
 def summarize_profiles(d: str) -> int:
@@ -612,6 +658,38 @@ def profile_kernels(bsa, path, cfg, q, k, v, reps):
     return 0
 
 
+def profile_gqa(bsa, reps):
+    """The grouped-query workload (B=2, 40 query heads on 8 K/V heads, masks pooled per group):
+    one path call for its layout and masks, `reps` launches of its compensated attention alone,
+    then one plain device copy of COPY_BYTES."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+    from synthetic import make_config
+
+    wl4 = make_config(4)
+    cfg4 = bsa.PathConfig.from_workload(dataclasses.replace(wl4, probes=0))
+    path4 = bsa.SparseAttentionPath(cfg4)
+    q4 = torch.from_numpy(wl4.q).to(torch.bfloat16).cuda()
+    k4 = torch.from_numpy(wl4.k).to(torch.bfloat16).cuda()
+    v4 = torch.from_numpy(wl4.v).to(torch.bfloat16).cuda()
+    res = path4(q4, k4, v4)
+    torch.cuda.synchronize()
+    kv = api.kv_pack(k4, v4, res.layout)
+    ws = api.attention_workspace(q4, kv, res.layout, res.mask)
+    out = torch.empty_like(q4)
+    for i in range(reps):
+        api.block_sparse_attention(q4, kv, res.layout, res.mask, True, cfg4.scale, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"[profile] grouped-query attention {i}", flush=True)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=q4.device).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[profile] copy {COPY_BYTES} bytes", flush=True)
+    return 0
+
+
 def time_path(path, q, k, v, steps, warmup):
     """Warm up, then time `steps` whole path calls between two device synchronizations; per
     stage, the mean of the events each stage records on its own stream."""
@@ -760,6 +838,8 @@ def main() -> int:
                     help="run the K/V packing on a second stream beside the scores (default: before them)")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="K",
                     help="launch each kernel K times on its own, then one plain copy (for rocprofv3)")
+    ap.add_argument("--profile-gqa", type=int, default=0, metavar="K",
+                    help="launch the grouped-query workload's attention K times, then one plain copy (for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from the rocprofv3 csv files in DIR")
     args = ap.parse_args()
@@ -776,6 +856,8 @@ def main() -> int:
     import block_sparse_attention_antidiagonal_amd as bsa
     from synthetic import make_config
 
+    if args.profile_gqa:
+        return profile_gqa(bsa, args.profile_gqa)
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     wl = make_config(2)
     cfg = bsa.PathConfig.from_workload(wl)
