@@ -1483,9 +1483,12 @@ struct RowCentroids {
 // attention -- a token tile counts for a row only when the row's query cluster keeps the
 // tile's key cluster (keep bits in LDS) -- and one more chunk, index nchunks, holds the
 // centroid tiles, whose columns count for the sparse rows of the clusters that skipped them
-// (with compensation; the chunk is empty without).  Partial rows, running max and sum go to
-// probe_merge_kernel.  Chunks past the head's last tile write empty partials.
-template <int D, bool SPARSE>
+// (with compensation; the chunk is empty without).  That chunk is a launch of its own (CEN):
+// one kernel holding both kinds of tile step spilled registers inside its tile loop (0.55 ms
+// against 0.19 ms for the repair's probe pass on the video workload).  Partial rows, running
+// max and sum go to probe_merge_kernel.  Chunks past the head's last tile write empty
+// partials.
+template <int D, bool SPARSE, bool CEN = false>
 __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
     const bf16_t* __restrict__ Q, int Hq, int Hkv, int Sq, float c2, const int32_t* __restrict__ probe_idx, int M,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ k_off, int C, int nl,
@@ -1501,7 +1504,10 @@ __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
   int* clus = nv + 2 * kNK;                            // key cluster of each tile of the chunk
   float* cbias = reinterpret_cast<float*>(clus + 2 * kNK);  // log2 n_c of a centroid tile's columns
   uint32_t* bits = reinterpret_cast<uint32_t*>(cbias + kNK);  // [128 rows][words]: sparse rows' keep bits
-  const int ci = blockIdx.x, qt = blockIdx.y, bh = blockIdx.z;
+  static_assert(SPARSE || !CEN, "the centroid chunk belongs to the sparse rows");
+  // CEN: this launch takes the centroid chunk (index nchunks) alone, so that each kernel holds
+  // one kind of tile step.
+  const int ci = CEN ? nchunks : static_cast<int>(blockIdx.x), qt = blockIdx.y, bh = blockIdx.z;
   const int b = bh / Hq, hq = bh % Hq, kvh = hq / (Hq / Hkv);
   const size_t bkv = static_cast<size_t>(b) * Hkv + kvh;
   const unsigned char* Kph = reinterpret_cast<const unsigned char*>(Kp) + bkv * tiles_per_head * kTileBytes;
@@ -1514,7 +1520,7 @@ __global__ __launch_bounds__(kThreads, 2) void probe_packed_kernel(
   clog2n += lay * C;
   if (q_labels != nullptr) q_labels += lay * Sq;
   if (probe_idx != nullptr) probe_idx += lay * M;
-  const bool cen = SPARSE && ci == nchunks;  // the centroid chunk
+  constexpr bool cen = CEN;  // the centroid chunk
   const int nrows = SPARSE ? 2 * M : M;
   const int nch = SPARSE ? nchunks + 1 : nchunks;
   int t0, t1;
@@ -2023,9 +2029,9 @@ bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void
   if (sparse && nrows <= kRowsWG) {
     // The repair's pass (dense and sparse rows of up to 64 probes in one row tile): as many
     // chunks per head as one round of the workgroups the device runs at once takes, each
-    // splitting the head's filled tiles (tile_off[C], read by the kernel) evenly.  Fixed
-    // chunks over the allocated tile range left a partial second round: on the video workload
-    // 32 tiles per chunk took 0.66 ms, 48 0.57 ms, 64 0.65 ms, 96 0.87 ms.
+    // splitting the head's filled tiles (tile_off[C], read by the kernel) evenly.  On the
+    // video workload (40 heads): 11 chunks per head 0.19 ms; 12, which leaves a partial second
+    // round, 0.26 ms; 23 (two rounds) 0.23 ms.
     const int slots = device_cus() * 2 * 9 / 10;
     const int want = max(1, slots / (B * Hq));
     const int least = (PL.first_centroid_tile + 2 * kNK - 1) / (2 * kNK);  // chunks of at most 2 kNK tiles
@@ -2046,9 +2052,12 @@ bsa_status launch_probe_packed(int B, int Hq, int Hkv, int S, int Sq, const void
       Cq, reinterpret_cast<const float*>(base + PL.clog2n), PL.first_centroid_tile, PL.centroid_tiles, comp ? 1 : 0, \
       words, Opart, mpart, lpart
   if (sparse) {
-    auto kern = probe_packed_kernel<D, true>;
+    auto kern = probe_packed_kernel<D, true, false>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    hipLaunchKernelGGL(kern, dim3(nch, qtiles, B * Hq), dim3(kThreads), LDS, stream, BSA_PROBE_ARGS);
+    hipLaunchKernelGGL(kern, dim3(nchunks, qtiles, B * Hq), dim3(kThreads), LDS, stream, BSA_PROBE_ARGS);
+    auto kcen = probe_packed_kernel<D, true, true>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kcen), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    hipLaunchKernelGGL(kcen, dim3(1, qtiles, B * Hq), dim3(kThreads), LDS, stream, BSA_PROBE_ARGS);
   } else {
     auto kern = probe_packed_kernel<D, false>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
