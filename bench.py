@@ -61,7 +61,7 @@ TRACE_STEPS, TRACE_WARMUP = 5, 2  # the path calls of the "trace" command below
 PROFILE_COMMANDS = {
     "trace": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $R/gpurun_out/prof -o trace -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
-             "--path-only",
+             "--path-only > $R/gpurun_out/prof/trace_bench.json",
     "fetch": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
              "-d $R/gpurun_out/prof -o fetch -- python3 $R/bench.py --profile-kernels 3 --no-cpu-baseline",
     "write": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
@@ -347,6 +347,17 @@ def summarize_profiles(d: str) -> int:
                     ("tile_list_wave_kernel", "tile_list_kernel", "group_rank_kernel", "order_kernel"))
         lines += ["", f"Attention kernels (`{ATTN_KERNEL}`, all variants) per timed call: {attn:.1f} us; with the "
                   f"tile-list and work-order kernels of the attention stage: {stage:.1f} us."]
+        # The bench line the same run printed: its attention time from HIP events on the
+        # kernel's stream, against the trace's average above.
+        line_path = os.path.join(d, "trace_bench.json")
+        if os.path.exists(line_path):
+            with open(line_path) as f:
+                rows = [json.loads(x) for x in f if x.startswith("{")]
+            if rows:
+                rl = rows[-1]["roofline"]
+                lines += ["", f"The bench line of the same run (HIP events around the timed calls): attention "
+                          f"{rl['avg_launch_ms'] * 1e3:.1f} us per launch, {rl['achieved']:.1f} TFLOP/s, "
+                          f"frac {rl['frac']:.4f}."]
         with open(os.path.join(out_dir, f"path_kernels_{stem}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     fetch = os.path.join(d, "fetch_counter_collection.csv")
