@@ -36,6 +36,12 @@ struct FitSmem {
   union {
     double E[kN][kN + 1];          // eigenvectors of T T^T (columns)
     double WV[128][kMaxRank + 1];  // diag(1/sigma) W V_r, once the eigenvectors are consumed
+    struct {                       // exchange buffers of the reduction steps (by step parity)
+      double colH[2][kN];          // column k of T T^T
+      double colL[2][kN];          // column k of Y Y^T + lambda I
+      double p[2][kN];             // p = G v
+      double vp[2][kFitThreads / 64];  // per-wave partial sums of v^T p
+    } hh;
   } e;
   double Zr[kN][kMaxRank + 1];  // U_r Lambda_r^1/2, then (Y Y^T + lambda I)^-1 of it
   double mu[128], sig[128], rbar[128];
@@ -91,6 +97,31 @@ __device__ double block_sum(double v, double* part) {
 #pragma unroll
   for (int i = 0; i < kFitThreads / 64; ++i) s += part[i];
   return s;
+}
+
+// acc[r][c] = sum_d X[i0+r][d] X[j0+c][d] (i0 = 4 (t / 16), j0 = 4 (t % 16)): thread t's 4 x 4
+// block of the 64 x 64 Gram matrix of the rows of X (in LDS, float32), float64 sums, plus
+// diag_add on the diagonal.
+__device__ __forceinline__ void gram64_block(const float (*X)[128 + 1], int D, double (&acc)[4][4], double diag_add) {
+  const int i0 = (threadIdx.x / 16) * 4, j0 = (threadIdx.x % 16) * 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+  for (int d = 0; d < D; ++d) {
+    double a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = static_cast<double>(X[i0 + r][d]);
+      b[r] = static_cast<double>(X[j0 + r][d]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] += a[r] * b[c];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r][r] += i0 == j0 ? diag_add : 0.0;
 }
 
 // out[i][j] = sum_d X[i][d] X[j][d] over 64 x 64 (rows of X in LDS, float32), float64 sums;
@@ -174,8 +205,22 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     sm.t.T[m][d] = static_cast<float>(sm.sw[m] * (rres - sm.rbar[d]));
   }
   __syncthreads();
-  // G = T T^T (64 x 64).
-  gram64(sm.t.T, D, sm.G, 0.0);
+  // G = T T^T and G2 = Y Y^T + lambda I (64 x 64): thread t holds the 4 x 4 blocks of both at
+  // rows i0.., columns j0.. in registers.  G2 runs over all 64 rows: the zero rows past M give
+  // the block sqrt(lambda) I in its factor, which the zero right-hand sides there leave at zero.
+  const int i0 = (t / 16) * 4, j0 = (t % 16) * 4;
+  double g[4][4], g2[4][4];
+  gram64_block(sm.t.T, D, g, 0.0);
+  gram64_block(sm.Y, D, g2, static_cast<double>(lambda));
+  auto& hh = sm.e.hh;
+  // Column 0 of G and of G2 into the exchange buffers (by the threads holding it).
+  if (j0 == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hh.colH[0][i0 + r] = g[r][0];
+      hh.colL[0][i0 + r] = g2[r][0];
+    }
+  }
   __syncthreads();
 
   // Leading eigenpairs of G, in four steps: Householder reduction to tridiagonal form, the
@@ -184,55 +229,98 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   //
   // (1) Step k reflects rows and columns k+1.. so that column k has zeros below the
   // subdiagonal: H = I - 2 v v^T with |v| = 1; the trailing block becomes G - v w^T - w v^T with
-  // w = 2 G v - 2 (v^T G v) v.  v is kept in column k below the diagonal.  G stays symmetric,
-  // so every wave reads the column as row k (lane = element) and forms v itself; wave q
-  // handles rows k+1+q, k+5+q, ... of p = G v (partial sums over its rows, added after the
-  // first barrier) and of the update.  Lanes index columns, so LDS rows are read whole.
+  // w = 2 G v - 2 (v^T G v) v.  Every wave forms the reflector from column k (lane = element;
+  // wave 0 keeps v in column k of the LDS matrix below the diagonal, for the back-
+  // transformation); each thread then forms p = G v on its block, summed over the 16 lanes of
+  // its row block, and after one barrier (for v^T p and p by column) updates its block.  The
+  // same steps eliminate G2 = L D L^T (L unit lower triangular, D the pivots): step k subtracts
+  // G2[i][k] G2[k][j] / G2[k][k] from the trailing block, so G2 stays symmetric and afterwards
+  // G2[k][k] = d_k and G2[i][k] = G2[k][i] = L[i][k] d_k for i > k.  Two barriers per step.
   {
     const int wave = t >> 6, lane = t & 63;
     for (int k = 0; k < kN - 2; ++k) {
-      const bool act = lane > k;  // trailing column
-      const double x = act ? sm.G[k][lane] : 0.0;
-      const double s2 = wave_sum_f64(x * x);
-      const double x0 = readlane_f64(x, k + 1);
+      const int b = k & 1;
+      const double xl = lane > k ? hh.colH[b][lane] : 0.0;
+      const double s2 = wave_sum_f64(xl * xl);
+      const double x0 = hh.colH[b][k + 1];
       double alpha = 0.0, vn2 = 0.0;
       if (s2 > 0.0) {
         alpha = x0 >= 0.0 ? -sqrt(s2) : sqrt(s2);
         vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
       }
       const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
-      const double v = act ? (x - (lane == k + 1 ? alpha : 0.0)) * vinv : 0.0;
-      double acc = 0.0;  // sum over this wave's rows c of G[c][lane] v_c
-      for (int c = k + 1 + wave; c < kN; c += kFitThreads / 64) acc += sm.G[c][lane] * readlane_f64(v, c);
-      sm.pw[wave][lane] = acc;
-      __syncthreads();  // partial products complete; every wave has read row k
       if (wave == 0) {
-        if (act) sm.G[lane][k] = v;
+        if (lane > k) sm.G[lane][k] = (xl - (lane == k + 1 ? alpha : 0.0)) * vinv;
         if (lane == 0) {
-          sm.dg[k] = sm.G[k][k];
+          sm.dg[k] = hh.colH[b][k];
           sm.od[k] = alpha;
         }
       }
-      if (vn2 > 0.0) {  // else the column is already zero: H = I
-        double pl = 0.0;
-        if (act) {
+      double vr[4], vc[4], lr[4], lc[4];
 #pragma unroll
-          for (int q = 0; q < kFitThreads / 64; ++q) pl += sm.pw[q][lane];
-        }
-        const double vp = wave_sum_f64(v * pl);
-        const double w = 2.0 * pl - 2.0 * vp * v;
-        if (act)
-          for (int c = k + 1 + wave; c < kN; c += kFitThreads / 64)
-            sm.G[c][lane] -= readlane_f64(v, c) * w + readlane_f64(w, c) * v;
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r, j = j0 + r;
+        vr[r] = i > k ? (hh.colH[b][i] - (i == k + 1 ? alpha : 0.0)) * vinv : 0.0;
+        vc[r] = j > k ? (hh.colH[b][j] - (j == k + 1 ? alpha : 0.0)) * vinv : 0.0;
+        lr[r] = hh.colL[b][i];
+        lc[r] = hh.colL[b][j];
       }
-      __syncthreads();  // the trailing block is updated
+      const double rpiv = 1.0 / hh.colL[b][k];
+      double p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc += g[r][c] * vc[c];
+        p[r] = row16_sum(acc);
+      }
+      double part = (t & 15) == 0 ? (vr[0] * p[0] + vr[1] * p[1]) + (vr[2] * p[2] + vr[3] * p[3]) : 0.0;
+      part = (readlane_f64(part, 0) + readlane_f64(part, 16)) + (readlane_f64(part, 32) + readlane_f64(part, 48));
+      if (lane == 0) hh.vp[b][wave] = part;
+      if ((t & 15) == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hh.p[b][i0 + r] = p[r];
+      }
+      __syncthreads();  // v^T p partials and p are in LDS
+      const double vp = (hh.vp[b][0] + hh.vp[b][1]) + (hh.vp[b][2] + hh.vp[b][3]);
+      if (vn2 > 0.0) {  // else the column is already zero: H = I
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const double wc = 2.0 * hh.p[b][j0 + c] - 2.0 * vp * vc[c];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const double wr = 2.0 * p[r] - 2.0 * vp * vr[r];
+            if (i0 + r > k && j0 + c > k) g[r][c] -= vr[r] * wc + wr * vc[c];
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double rk = lc[c] * rpiv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i0 + r > k && j0 + c > k) g2[r][c] -= lr[r] * rk;
+      }
+      if (j0 == ((k + 1) & ~3)) {
+        const int c = (k + 1) & 3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hh.colH[b ^ 1][i0 + r] = c == 0 ? g[r][0] : c == 1 ? g[r][1] : c == 2 ? g[r][2] : g[r][3];
+          hh.colL[b ^ 1][i0 + r] = c == 0 ? g2[r][0] : c == 1 ? g2[r][1] : c == 2 ? g2[r][2] : g2[r][3];
+        }
+      }
+      __syncthreads();  // column k+1 is in LDS
     }
   }
+  // The last 2 x 2 block of the tridiagonal form, and the last elimination step of G2.
   if (t == 0) {
-    sm.dg[kN - 2] = sm.G[kN - 2][kN - 2];
-    sm.od[kN - 2] = sm.G[kN - 1][kN - 2];
-    sm.dg[kN - 1] = sm.G[kN - 1][kN - 1];
+    sm.dg[kN - 2] = hh.colH[0][kN - 2];
+    sm.od[kN - 2] = hh.colH[0][kN - 1];
     sm.od[kN - 1] = 0.0;
+  }
+  if (t == kFitThreads - 1) {
+    sm.dg[kN - 1] = g[3][3];
+    g2[3][3] -= hh.colL[0][kN - 1] * (hh.colL[0][kN - 1] * (1.0 / hh.colL[0][kN - 2]));
   }
   __syncthreads();
   if (t < kN) sm.e2[t] = sm.od[t] * sm.od[t];
@@ -414,9 +502,11 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     }
     vr[i] = v;
   }
-  // G <- Y Y^T + lambda I over all 64 rows: the zero rows past M give the block sqrt(lambda) I
-  // in the factor, which the zero right-hand sides there leave at zero.
-  gram64(sm.Y, D, sm.G, static_cast<double>(lambda));
+  // G <- the factor of Y Y^T + lambda I, from the registers that eliminated it.
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm.G[i0 + r][j0 + c] = g2[r][c];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kVrPer; ++i) {
@@ -424,20 +514,8 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     const int k = e / D, d = e % D;
     if (k < kMaxRank) sm.t.Vr[k][d] = vr[i];
   }
-  // G2 = L D L^T (L unit lower triangular, D the pivots) by right-looking elimination on the
-  // whole symmetric matrix: step k subtracts G[i][k] G[k][j] / G[k][k] from both triangles of
-  // the trailing block, so row k stays equal to column k and every access reads an LDS row
-  // whole (lane = column).  Wave q updates rows k+1+q, k+5+q, ...; one barrier per step.
-  // Afterwards G[k][k] = d_k and G[k][i] = G[i][k] = L[i][k] d_k for i > k.
   {
     const int wave = t >> 6, lane = t & 63;
-    for (int k = 0; k < kN - 1; ++k) {
-      if (lane > k) {
-        const double rk = sm.G[k][lane] / sm.G[k][k];
-        for (int i = k + 1 + wave; i < kN; i += kFitThreads / 64) sm.G[i][lane] -= sm.G[i][k] * rk;
-      }
-      __syncthreads();
-    }
     // z = G2^-1 Zr: wave q solves right-hand sides 4q .. 4q+3 with lane = row, in registers,
     // without barriers: L a = Zr (a_k broadcast from lane k), b = D^-1 a, then L^T z = b.
     constexpr int kRhsPerWave = kMaxRank / (kFitThreads / 64);
