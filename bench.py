@@ -464,6 +464,28 @@ def cpu_baseline(wl, seconds_hint=20.0):
     }
 
 
+def measure_centroids(bsa, k, v, layout, reps=20):
+    """The centroid sums on their own (bsa_centroids: read K and V once through the cluster
+    layout, write the float32 means), timed with events on the current stream; GB/s over the
+    K and V bytes it must read, the stage's algorithmic bytes."""
+    import torch
+    from block_sparse_attention_antidiagonal_amd import api
+
+    stream = torch.cuda.current_stream()
+    api.centroids(k, v, layout)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        api.centroids(k, v, layout)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = (k.numel() + v.numel()) * k.element_size()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4)}
+
+
 def measure_reuse(bsa, cfg, q, k, res, reps=10):
     """Head-wise mask reuse on the same inputs, timed with events on the current stream:
     the pooled Q/K pass (reads Q and K once), the drift/gate decision, and one cache step
@@ -947,6 +969,8 @@ def main() -> int:
             "scores_TFLOPs": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12, 2),
             "scores_mfma_frac": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
+        # the same sums by the standalone call (no tiles written), on the same K, V and layout
+        "centroids_standalone": measure_centroids(bsa, k, v, res.layout),
     }
     if not args.path_only:
         print("[bench] repair workloads", file=sys.stderr, flush=True)

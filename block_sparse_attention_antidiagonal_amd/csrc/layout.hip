@@ -24,27 +24,51 @@ __global__ __launch_bounds__(256) void centroid_kernel(const T* __restrict__ K, 
   const T* Kh = K + bh * static_cast<size_t>(S) * D;
   const T* Vh = V + bh * static_cast<size_t>(S) * D;
   float ka[8] = {}, va[8] = {};
-  for (int r = lo + rr; r < hi; r += kRowsPerPass) {
-    const int tok = perm[r];
-    if (tok < 0 || tok >= S) continue;
-    const T* kp = Kh + static_cast<size_t>(tok) * D + sub * 8;
-    const T* vp = Vh + static_cast<size_t>(tok) * D + sub * 8;
-    if constexpr (sizeof(T) == 2) {
-      const uint4 kq = *reinterpret_cast<const uint4*>(kp);
-      const uint4 vq = *reinterpret_cast<const uint4*>(vp);
-      const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w}, vw[4] = {vq.x, vq.y, vq.z, vq.w};
+  // Rows go kBatch passes at a time: their cluster-order token indices first, then all their
+  // K and V loads, so that 2 kBatch row loads per thread are in flight; the sums take the rows
+  // in the same order as one pass at a time would.
+  constexpr int kBatch = 4;
+  for (int r0 = lo + rr; r0 < hi; r0 += kBatch * kRowsPerPass) {
+    int tok[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ka[2 * i] += __uint_as_float(kw[i] << 16);
-        ka[2 * i + 1] += __uint_as_float(kw[i] & 0xffff0000u);
-        va[2 * i] += __uint_as_float(vw[i] << 16);
-        va[2 * i + 1] += __uint_as_float(vw[i] & 0xffff0000u);
+    for (int i = 0; i < kBatch; ++i) {
+      const int r = r0 + i * kRowsPerPass;
+      tok[i] = r < hi ? perm[r] : -1;
+    }
+    float kx[kBatch][8], vx[kBatch][8];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const bool ok = tok[i] >= 0 && tok[i] < S;
+      const size_t off = static_cast<size_t>(ok ? tok[i] : 0) * D + sub * 8;
+      if constexpr (sizeof(T) == 2) {
+        uint4 kq = make_uint4(0u, 0u, 0u, 0u), vq = make_uint4(0u, 0u, 0u, 0u);
+        if (ok) {
+          kq = *reinterpret_cast<const uint4*>(Kh + off);
+          vq = *reinterpret_cast<const uint4*>(Vh + off);
+        }
+        const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w}, vw[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[i][2 * j] = __uint_as_float(kw[j] << 16);
+          kx[i][2 * j + 1] = __uint_as_float(kw[j] & 0xffff0000u);
+          vx[i][2 * j] = __uint_as_float(vw[j] << 16);
+          vx[i][2 * j + 1] = __uint_as_float(vw[j] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kx[i][j] = ok ? to_f32(Kh[off + j]) : 0.0f;
+          vx[i][j] = ok ? to_f32(Vh[off + j]) : 0.0f;
+        }
       }
-    } else {
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ka[i] += to_f32(kp[i]);
-        va[i] += to_f32(vp[i]);
+    for (int i = 0; i < kBatch; ++i) {
+      if (tok[i] < 0 || tok[i] >= S) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ka[j] += kx[i][j];
+        va[j] += vx[i][j];
       }
     }
   }
