@@ -209,7 +209,11 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   // rows i0.., columns j0.. in registers.  G2 runs over all 64 rows: the zero rows past M give
   // the block sqrt(lambda) I in its factor, which the zero right-hand sides there leave at zero.
   const int i0 = (t / 16) * 4, j0 = (t % 16) * 4;
-  double g[4][4], g2[4][4];
+  double g[4][4], g2[4][4], qb[4][4];  // qb: this thread's block of Q = H_0 H_1 ... (starts at I)
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qb[r][c] = i0 + r == j0 + c ? 1.0 : 0.0;
   gram64_block(sm.t.T, D, g, 0.0);
   gram64_block(sm.Y, D, g2, static_cast<double>(lambda));
   auto& hh = sm.e.hh;
@@ -229,10 +233,11 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   //
   // (1) Step k reflects rows and columns k+1.. so that column k has zeros below the
   // subdiagonal: H = I - 2 v v^T with |v| = 1; the trailing block becomes G - v w^T - w v^T with
-  // w = 2 G v - 2 (v^T G v) v.  Every wave forms the reflector from column k (lane = element;
-  // wave 0 keeps v in column k of the LDS matrix below the diagonal, for the back-
-  // transformation); each thread then forms p = G v on its block, summed over the 16 lanes of
-  // its row block, and after one barrier (for v^T p and p by column) updates its block.  The
+  // w = 2 G v - 2 (v^T G v) v.  Every wave forms the reflector from column k (lane = element);
+  // each thread then forms p = G v on its block, summed over the 16 lanes of its row block, and
+  // after one barrier (for v^T p and p by column) updates its block.  The product of the
+  // reflectors, Q = H_0 H_1 ..., is accumulated on the same blocks (Q <- Q - 2 (Q v) v^T, no
+  // barrier of its own), so the eigenvectors of G are Q times those of the tridiagonal form.  The
   // same steps eliminate G2 = L D L^T (L unit lower triangular, D the pivots): step k subtracts
   // G2[i][k] G2[k][j] / G2[k][k] from the trailing block, so G2 stays symmetric and afterwards
   // G2[k][k] = d_k and G2[i][k] = G2[k][i] = L[i][k] d_k for i > k.  Two barriers per step.
@@ -249,12 +254,9 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
         vn2 = 2.0 * s2 - 2.0 * x0 * alpha;
       }
       const double vinv = vn2 > 0.0 ? 1.0 / sqrt(vn2) : 0.0;
-      if (wave == 0) {
-        if (lane > k) sm.G[lane][k] = (xl - (lane == k + 1 ? alpha : 0.0)) * vinv;
-        if (lane == 0) {
-          sm.dg[k] = hh.colH[b][k];
-          sm.od[k] = alpha;
-        }
+      if (t == 0) {
+        sm.dg[k] = hh.colH[b][k];
+        sm.od[k] = alpha;
       }
       double vr[4], vc[4], lr[4], lc[4];
 #pragma unroll
@@ -273,6 +275,15 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc += g[r][c] * vc[c];
         p[r] = row16_sum(acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc += qb[r][c] * vc[c];
+        const double qv2 = 2.0 * row16_sum(acc);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qb[r][c] -= qv2 * vc[c];
       }
       double part = (t & 15) == 0 ? (vr[0] * p[0] + vr[1] * p[1]) + (vr[2] * p[2] + vr[3] * p[3]) : 0.0;
       part = (readlane_f64(part, 0) + readlane_f64(part, 16)) + (readlane_f64(part, 32) + readlane_f64(part, 48));
@@ -322,6 +333,11 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     sm.dg[kN - 1] = g[3][3];
     g2[3][3] -= hh.colL[0][kN - 1] * (hh.colL[0][kN - 1] * (1.0 / hh.colL[0][kN - 2]));
   }
+  // Q into the LDS matrix, for the back-transformation.
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm.G[i0 + r][j0 + c] = qb[r][c];
   __syncthreads();
   if (t < kN) sm.e2[t] = sm.od[t] * sm.od[t];
   __syncthreads();
@@ -351,7 +367,10 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   {  // 16 eigenvalues at once: lanes of a 16-lane group probe 16 points of its interval
     const int k = t >> 4, j = t & 15;
     double a = glo - 1e-3 * span, b = ghi + 1e-3 * span;
-    for (int it = 0; it < 13; ++it) {  // 17^13 > 1e15: the interval shrinks to rounding level
+    // 17^10 > 2e12: each eigenvalue to about 1e-12 of the spectrum's span, close enough for
+    // the inverse iteration below (the fit itself uses only the eigenvectors: lambda^1/2 in
+    // Zr and lambda^-1/2 in V_r cancel in A).
+    for (int it = 0; it < 10; ++it) {
       const double x = a + (b - a) * static_cast<double>(j + 1) / 17.0;
       const bool ok = (kN - below(x)) <= k;  // at most k eigenvalues above x: lambda_k <= x
       const unsigned long long mask = __ballot(ok);
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
   const int nvec = sm.r_eff;
 
   // (3) Inverse iteration on T for each kept eigenvalue (one thread per vector): LU of
-  // T - lambda I without pivoting (tiny pivots replaced), three solves from a fixed start,
+  // T - lambda I without pivoting (tiny pivots replaced), two solves from a fixed start,
   // normalized each time.  The vector lives in registers (the loops are unrolled); column
   // 16+k of E holds the reciprocal pivots and column 32+k the multipliers; the result goes
   // to column k.
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     for (int i = 0; i < kN; ++i) x[i * RS] = 1.0 + static_cast<double>((i * 7 + k * 13) % 11) / 11.0;
     // The recurrences run through registers; elements and factors move in blocks of 8 so
     // their LDS accesses overlap.
-    for (int iter = 0; iter < 3; ++iter) {
+    for (int iter = 0; iter < 2; ++iter) {
       double prev = x[0];
       for (int i0 = 0; i0 < kN; i0 += 8) {
         double xb[8], lb[8];
@@ -451,24 +470,24 @@ __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __r
     }
   }
   __syncthreads();
-  // (4) Eigenvectors of G = H_0 H_1 ... H_61 y: 16-lane groups, one vector each.
+  // (4) Eigenvectors of G: Q y for each tridiagonal eigenvector y (16-lane groups, one vector
+  // each, four rows per lane), written over y once every group has read its vector.
   {
     const int k = t >> 4, q = t & 15;
+    double x[kN / 16];
+#pragma unroll
+    for (int c = 0; c < kN / 16; ++c) x[c] = 0.0;
     if (k < nvec) {
-      for (int s = kN - 3; s >= 0; --s) {
-        double dot = 0.0;
+      for (int j = 0; j < kN; ++j) {
+        const double y = sm.e.E[j][k];
 #pragma unroll
-        for (int c = 0; c < kN / 16; ++c) {
-          const int i = q + 16 * c;
-          if (i > s) dot += sm.G[i][s] * sm.e.E[i][k];
-        }
-        dot = row16_sum(dot);
-#pragma unroll
-        for (int c = 0; c < kN / 16; ++c) {
-          const int i = q + 16 * c;
-          if (i > s) sm.e.E[i][k] -= 2.0 * dot * sm.G[i][s];
-        }
+        for (int c = 0; c < kN / 16; ++c) x[c] += sm.G[q + 16 * c][j] * y;
       }
+    }
+    __syncthreads();
+    if (k < nvec) {
+#pragma unroll
+      for (int c = 0; c < kN / 16; ++c) sm.e.E[q + 16 * c][k] = x[c];
     }
   }
   if (t < kN) {
