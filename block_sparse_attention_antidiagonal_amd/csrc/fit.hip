@@ -49,7 +49,6 @@ struct FitSmem {
   double eval[kN];
   double u[kMaxRank];  // (mu / sigma)^T W V_r
   double dg[kN], od[kN], e2[kN];  // tridiagonal form: diagonal, off-diagonal, off-diagonal squared
-  double pw[kFitThreads / 64][kN];  // Householder step: partial sums of p = G v per wave
   double lam[kMaxRank];           // the largest eigenvalues, descending
   int order[kN];
   double wave_part[kFitThreads / 64];
@@ -122,29 +121,6 @@ __device__ __forceinline__ void gram64_block(const float (*X)[128 + 1], int D, d
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r][r] += i0 == j0 ? diag_add : 0.0;
-}
-
-// out[i][j] = sum_d X[i][d] X[j][d] over 64 x 64 (rows of X in LDS, float32), float64 sums;
-// each thread owns a 4 x 4 block.
-__device__ __forceinline__ void gram64(const float (*X)[128 + 1], int D, double (*out)[kN + 1], double diag_add) {
-  const int i0 = (threadIdx.x / 16) * 4, j0 = (threadIdx.x % 16) * 4;
-  double acc[4][4] = {};
-  for (int d = 0; d < D; ++d) {
-    double a[4], b[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      a[r] = static_cast<double>(X[i0 + r][d]);
-      b[r] = static_cast<double>(X[j0 + r][d]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] += a[r] * b[c];
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) out[i0 + r][j0 + c] = acc[r][c] + (i0 + r == j0 + c ? diag_add : 0.0);
 }
 
 __global__ __launch_bounds__(kFitThreads) void probe_fit_kernel(const float* __restrict__ Os,
