@@ -84,6 +84,14 @@ PROFILE_COMMANDS = {
              "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
              "SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof -o issue -- python3 "
              "$R/bench.py --profile-kernels 3 --no-cpu-baseline",
+    # LDS and vector-memory occupancy: LDS busy cycles and bytes read/written by LDS
+    # instructions, the address (TA) and data (TD) units of the vector memory path, and the
+    # cycles their queues were full
+    "lds": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+           "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_INSTS_LDS_STORE_BANDWIDTH SQ_LDS_DATA_FIFO_FULL SQ_VMEM_TA_ADDR_FIFO_FULL "
+           "SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE TA_BUSY_avr TA_BUFFER_TOTAL_CYCLES_sum TD_TD_BUSY_sum "
+           "--output-format csv -d $R/gpurun_out/prof -o lds -- python3 $R/bench.py --profile-kernels 3 "
+           "--no-cpu-baseline",
     # the partitioned (SparsePR) call alone
     "trace_partitioned": "R=$PWD; cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
                          "csv -d $R/gpurun_out/prof -o trace_partitioned -- python3 $R/bench.py --steps 5 "
@@ -260,9 +268,53 @@ def _summarize_counters(d: str, out_path: str) -> None:
                               f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (SIMDS * elapsed):.1f}% | "
                               f"{100 * mean('SQ_VALU_MFMA_COEXEC_CYCLES') / (SIMDS * elapsed):.1f}% |"))
         lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    lines += _summarize_lds(d)
     lines += _summarize_gqa(d)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def _summarize_lds(d: str) -> list:
+    """LDS and vector-memory occupancy per kernel from the "lds" run: the share of elapsed CU
+    cycles in which the LDS served indexed (ds_*) operations (rocprofv3's LdsUtil: the busy
+    cycles summed over the CUs over elapsed cycles x CUs), bytes read and written by ds_*
+    instructions per CU and elapsed cycle, the busy share of the vector memory path's address
+    (TA) and data (TD) units, and the share of cycles with their queues full."""
+    csv_path = os.path.join(d, "lds_counter_collection.csv")
+    if not os.path.exists(csv_path):
+        return []
+    cus = SIMDS // 4
+    rows = []
+    for k, ds in _counters_by_dispatch(csv_path).items():
+        ds = [e for e in ds if e["dur_ns"] >= 20000]
+        if not ds or k.startswith("__amd"):
+            continue
+        mean = lambda key: float(np.mean([e.get(key, 0.0) for e in ds]))
+        dur, elapsed = mean("dur_ns"), mean("GRBM_GUI_ACTIVE") / XCDS  # cycles at the seen clock
+        if elapsed <= 0:
+            continue
+        per_cu = lambda key: mean(key) / (cus * elapsed)
+        act = mean("SQ_LDS_IDX_ACTIVE")
+        rows.append((dur, f"| `{k}` | {dur / 1e3:.1f} | {elapsed / dur:.2f} | {100 * per_cu('SQ_LDS_IDX_ACTIVE'):.1f}% | "
+                          f"{64 * per_cu('SQ_INSTS_LDS_LOAD_BANDWIDTH'):.1f} | "
+                          f"{64 * per_cu('SQ_INSTS_LDS_STORE_BANDWIDTH'):.1f} | "
+                          f"{100 * mean('SQ_LDS_BANK_CONFLICT') / act if act > 0 else 0.0:.1f}% | "
+                          f"{100 * per_cu('SQ_LDS_DATA_FIFO_FULL'):.1f}% | "
+                          f"{100 * mean('TA_BUSY_avr') / elapsed:.1f}% | {100 * per_cu('TD_TD_BUSY_sum'):.1f}% | "
+                          f"{100 * per_cu('SQ_VMEM_TA_ADDR_FIFO_FULL'):.1f}% |"))
+    if not rows:
+        return []
+    return ["", "## LDS and vector-memory occupancy", "", "```", PROFILE_COMMANDS["lds"], "```", "",
+            "Per kernel, the mean over its dispatches of at least 20 us; shares are of the cycles that "
+            "elapsed at the seen clock (GRBM_GUI_ACTIVE / 8), per CU.  LDS busy: SQ_LDS_IDX_ACTIVE (cycles the "
+            "LDS serves ds_* operations; rocprofv3's LdsUtil); LDS read/written: 64 x "
+            "SQ_INSTS_LDS_LOAD/STORE_BANDWIDTH bytes per CU per cycle (ds_* instructions only: the copies "
+            "from global memory straight into LDS are not among them); TA and TD busy: TA_BUSY_avr (mean over "
+            "the TA instances) and TD_TD_BUSY_sum over the CUs; queue full: SQ_LDS_DATA_FIFO_FULL and "
+            "SQ_VMEM_TA_ADDR_FIFO_FULL over the CUs.", "",
+            "| kernel | us | clock GHz | LDS busy | LDS read B/clk | LDS written B/clk | LDS conflict | "
+            "LDS data queue full | TA busy | TD busy | TA address queue full |",
+            "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"] + [r for _, r in sorted(rows, key=lambda x: -x[0])]
 
 
 def _summarize_gqa(d: str) -> list:
@@ -969,10 +1021,10 @@ def main() -> int:
             "scores_TFLOPs": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12, 2),
             "scores_mfma_frac": round(score_flops / (stages_ms["scores"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
-        # the same sums by the standalone call (no tiles written), on the same K, V and layout
-        "centroids_standalone": measure_centroids(bsa, k, v, res.layout),
     }
     if not args.path_only:
+        # the same sums by the standalone call (no tiles written), on the same K, V and layout
+        line["centroids_standalone"] = measure_centroids(bsa, k, v, res.layout)
         print("[bench] repair workloads", file=sys.stderr, flush=True)
         line["repair_workloads"] = measure_repair_workloads(bsa, args.steps, args.warmup, wl, q, k, v)
         print("[bench] mask reuse", file=sys.stderr, flush=True)
